@@ -1,0 +1,130 @@
+"""fp64 CPU oracle for the GSPN four-direction line-scan propagation.
+
+TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the product library
+(``spatial_line_scan_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``gspn_oracle.c`` (plain C, compiled with gcc); this
+module only marshals numpy arrays into it.  Every input is widened exactly to
+float64 (fp32 and bf16 values are exactly representable), so the oracle sees
+the same numbers the GPU path sees.
+
+Functions
+---------
+normalize(w_raw, NL, L, eps)              -> normalised taps (one direction)
+scan_dir(x, lam, u, w, dir, w_is_raw, eps) -> u * h for one direction
+prop2d(x, lam, u, w4, eps)                -> sum over the four directions
+
+Layouts follow the C file's header: x, lam, u: [B][C][H][W]; the taps of one
+direction: [B][C][3][NL][L] indexed by (line, position) of that direction
+(TD/BU: NL=H, L=W; LR/RL: NL=W, L=H); w4: [4][B][C][3][..][..].
+
+Parity unpinned: none.  Each function is pinned by tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+TD, BU, LR, RL = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gspn_oracle.c")
+_LIB = os.path.join(_HERE, "libgspn_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile gspn_oracle.c with gcc into oracle/libgspn_oracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load(path: str | None = None):
+    """Load the compiled oracle (building it first), or a given build of it."""
+    global _lib
+    if path is not None or _lib is None:
+        if path is None:
+            path = build()
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        L = ctypes.c_long
+        lib.gspn_oracle_normalize.argtypes = [dp, dp, L, L, L, ctypes.c_double]
+        lib.gspn_oracle_normalize.restype = None
+        lib.gspn_oracle_scan_dir.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_double,
+                                             dp, L, L, L, L, ctypes.c_int]
+        lib.gspn_oracle_scan_dir.restype = ctypes.c_int
+        lib.gspn_oracle_prop2d.argtypes = [dp, dp, dp, dp, ctypes.c_double, dp, L, L, L, L]
+        lib.gspn_oracle_prop2d.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def use_library(path: str | None):
+    """Point this module at another build of gspn_oracle.c (None: the default).
+
+    Used by the mutation tests, which compile deliberately broken copies of
+    the oracle and check that the pins reject them.
+    """
+    global _lib
+    _lib = None
+    if path is not None:
+        _load(path)
+
+
+def _f64(a) -> np.ndarray:
+    """Exact widening to a contiguous float64 numpy array (torch tensors too)."""
+    if hasattr(a, "detach"):  # torch tensor: go through fp32 (exact for bf16/fp32)
+        import torch
+        a = a.detach().to("cpu", torch.float32).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def line_geometry(dir: int, H: int, W: int):
+    """(number of lines, line length) for a direction."""
+    return (H, W) if dir in (TD, BU) else (W, H)
+
+
+def normalize(w_raw, NL: int, L: int, eps: float = 1e-6) -> np.ndarray:
+    """Row-stochastic normalisation of taps laid out [..][3][NL][L]."""
+    w = _f64(w_raw)
+    assert w.size % (3 * NL * L) == 0
+    out = np.empty_like(w)
+    _load().gspn_oracle_normalize(_ptr(w), _ptr(out), w.size // (3 * NL * L), NL, L, float(eps))
+    return out
+
+
+def scan_dir(x, lam, u, w, dir: int, w_is_raw: bool = True, eps: float = 1e-6) -> np.ndarray:
+    """u * h for one direction; x, lam, u: [B][C][H][W], w: [B][C][3][NL][L]."""
+    x, lam, u, w = _f64(x), _f64(lam), _f64(u), _f64(w)
+    B, C, H, W = x.shape
+    assert lam.shape == x.shape and u.shape == x.shape and w.size == 3 * x.size
+    out = np.empty_like(x)
+    rc = _load().gspn_oracle_scan_dir(_ptr(x), _ptr(lam), _ptr(u), _ptr(w), int(bool(w_is_raw)),
+                                      float(eps), _ptr(out), B, C, H, W, int(dir))
+    if rc != 0:
+        raise MemoryError("oracle scan could not allocate scratch")
+    return out
+
+
+def prop2d(x, lam, u, w4, eps: float = 1e-6) -> np.ndarray:
+    """y = sum over TD, BU, LR, RL of u * h_d with normalised taps."""
+    x, lam, u, w4 = _f64(x), _f64(lam), _f64(u), _f64(w4)
+    B, C, H, W = x.shape
+    assert w4.size == 12 * x.size
+    y = np.empty_like(x)
+    rc = _load().gspn_oracle_prop2d(_ptr(x), _ptr(lam), _ptr(u), _ptr(w4), float(eps), _ptr(y),
+                                    B, C, H, W)
+    if rc != 0:
+        raise MemoryError("oracle propagation could not allocate scratch")
+    return y

@@ -1,0 +1,191 @@
+/*
+ * Reference oracle for the GSPN four-direction line-scan propagation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is a plain, slow, single-threaded
+ * fp64 restatement of what the operator computes.  It exists so the HIP
+ * kernels can be checked against something obviously correct.  Only the
+ * tests, the smoke check and the bench's CPU-baseline leg may load it; the
+ * product library never links or calls it, and it shares no code, header or
+ * table with the HIP path.
+ *
+ * Sources (the paper "Scaling Parallel Sequence Models to Foundation-Scale
+ * Vision Encoders", C-GSPN, and its reading notes):
+ *   - paper §3 "Background: 2D Spatial Propagation": feature map B x C x H x W,
+ *     line-scan recurrence (display lost in the extraction; the standard GSPN
+ *     form is used: h_i = w_i h_{i-1} + lambda_i * x_i, output u_i * h_i).
+ *   - reading notes, "method / overall framework": lines are scanned in
+ *     order, all positions of a line update in parallel from the previous
+ *     line through three coefficients (a tridiagonal neighbourhood); w must
+ *     be row-stochastic, made so by sigmoid followed by division by the
+ *     neighbourhood sum; four directions (top-down, bottom-up, left-right,
+ *     right-left) are each scanned once.
+ *   - paper §5.1 "Fused CUDA normalization": sigmoid, local reduction,
+ *     clamping, division.
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes of the repository):
+ *   - h before the first line is 0, so the first line in scan order is
+ *     lambda * x and its taps are unused.
+ *   - tap k (0,1,2) stored at destination position p weights position
+ *     p + k - 1 of the previous line, in absolute coordinates for every
+ *     direction; taps whose source falls outside the line are dropped from
+ *     both the numerator and the neighbourhood sum.
+ *   - the clamp bounds the neighbourhood sum from below by eps.
+ *   - lambda and u are shared by the four directions; the four directional
+ *     outputs u * h_d are summed in the order TD, BU, LR, RL.
+ *
+ * Memory layouts (row-major, innermost last):
+ *   x, lambda, u, y : [B][C][H][W]
+ *   taps of one direction : [B][C][3][NL][L], indexed by (line, position)
+ *       of that direction: TD/BU lines are rows (NL = H, L = W),
+ *       LR/RL lines are columns (NL = W, L = H), i.e. LR/RL tap planes are
+ *       stored transposed with respect to the pixel grid.
+ *   taps of all four directions : [4][B][C][3][...] in order TD, BU, LR, RL.
+ *
+ * Build: gcc -O2 -shared -fPIC gspn_oracle.c -o libgspn_oracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { DIR_TD = 0, DIR_BU = 1, DIR_LR = 2, DIR_RL = 3 };
+
+/* Logistic sigmoid 1 / (1 + e^-z) in fp64. */
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/*
+ * Row-stochastic normalisation of the three taps of one destination position
+ * (reading notes, normalisation formula; paper §5.1 fused normalisation):
+ *   s_k = sigmoid(raw_k) if position p + k - 1 lies on the line, else 0
+ *   S   = max(s_0 + s_1 + s_2, eps)          (the clamp)
+ *   w_k = s_k / S
+ */
+static void normalize_three(const double raw[3], long p, long L, double eps,
+                            double out[3]) {
+    double s[3];
+    double sum = 0.0;
+    for (int k = 0; k < 3; ++k) {
+        long q = p + k - 1;
+        s[k] = (q >= 0 && q < L) ? sigmoid(raw[k]) : 0.0;
+        sum += s[k];
+    }
+    double S = sum > eps ? sum : eps;
+    for (int k = 0; k < 3; ++k) out[k] = s[k] / S;
+}
+
+/*
+ * Normalise one direction's tap block w_raw [P][3][NL][L] into w_norm (same
+ * layout).  Every position is written, including the first line's, whose
+ * taps the scan never uses.
+ */
+void gspn_oracle_normalize(const double* w_raw, double* w_norm, long P,
+                           long NL, long L, double eps) {
+    long plane = NL * L;
+    for (long pl = 0; pl < P; ++pl) {
+        const double* src = w_raw + pl * 3 * plane;
+        double* dst = w_norm + pl * 3 * plane;
+        for (long i = 0; i < NL; ++i) {
+            for (long p = 0; p < L; ++p) {
+                double raw[3], out[3];
+                for (int k = 0; k < 3; ++k) raw[k] = src[k * plane + i * L + p];
+                normalize_three(raw, p, L, eps, out);
+                for (int k = 0; k < 3; ++k) dst[k * plane + i * L + p] = out[k];
+            }
+        }
+    }
+}
+
+/* Pixel (row, col) visited by direction dir at line i, position p. */
+static void pixel_of(int dir, long i, long p, long* row, long* col) {
+    if (dir == DIR_TD || dir == DIR_BU) { *row = i; *col = p; }
+    else                                { *row = p; *col = i; }
+}
+
+/*
+ * One directional scan over every (b, c) plane (paper §3 line-scan
+ * recurrence; reading notes, top-down example generalised to the other three
+ * directions).  For each plane, lines are visited in scan order (TD: rows
+ * 0..H-1, BU: rows H-1..0, LR: columns 0..W-1, RL: columns W-1..0):
+ *   first line:  h[p] = lambda * x
+ *   later lines: h[p] = sum_{in-line k} w_k(i, p) * h_prev[p + k - 1]
+ *                       + lambda * x
+ * and out = u * h at every pixel.  With w_is_raw the taps are normalised
+ * first; otherwise they are used as given (a tap whose source lies outside
+ * the line contributes nothing, whatever its value).
+ * Returns 0, or -1 if scratch memory could not be obtained.
+ */
+int gspn_oracle_scan_dir(const double* x, const double* lam, const double* u,
+                         const double* w, int w_is_raw, double eps,
+                         double* out, long B, long C, long H, long W,
+                         int dir) {
+    long NL = (dir == DIR_TD || dir == DIR_BU) ? H : W;
+    long L  = (dir == DIR_TD || dir == DIR_BU) ? W : H;
+    int forward = (dir == DIR_TD || dir == DIR_LR);
+    long npix = H * W;
+    double* hprev = (double*)malloc(sizeof(double) * (size_t)L);
+    double* hnew  = (double*)malloc(sizeof(double) * (size_t)L);
+    if (!hprev || !hnew) { free(hprev); free(hnew); return -1; }
+
+    for (long pl = 0; pl < B * C; ++pl) {
+        const double* xp = x + pl * npix;
+        const double* lp = lam + pl * npix;
+        const double* up = u + pl * npix;
+        const double* wp = w + pl * 3 * npix;   /* [3][NL][L] */
+        double* op = out + pl * npix;
+        for (long step = 0; step < NL; ++step) {
+            long i = forward ? step : NL - 1 - step;
+            for (long p = 0; p < L; ++p) {
+                long r, c;
+                pixel_of(dir, i, p, &r, &c);
+                double bx = lp[r * W + c] * xp[r * W + c];
+                double h = bx;
+                if (step > 0) {
+                    double raw[3], tap[3];
+                    for (int k = 0; k < 3; ++k) raw[k] = wp[k * npix + i * L + p];
+                    if (w_is_raw) normalize_three(raw, p, L, eps, tap);
+                    else memcpy(tap, raw, sizeof tap);
+                    double mix = 0.0;
+                    for (int k = 0; k < 3; ++k) {
+                        long q = p + k - 1;
+                        if (q < 0 || q >= L) continue;
+                        mix += tap[k] * hprev[q];
+                    }
+                    h = mix + bx;
+                }
+                hnew[p] = h;
+                op[r * W + c] = up[r * W + c] * h;
+            }
+            double* t = hprev; hprev = hnew; hnew = t;
+        }
+    }
+    free(hprev);
+    free(hnew);
+    return 0;
+}
+
+/*
+ * Four-direction propagation y = sum_d u * h_d, summed in fp64 in the order
+ * TD, BU, LR, RL, with the taps of every direction normalised (the operator
+ * the latent sublayer applies: y_c = Prop2D(x_c; u, lambda, w), reading
+ * notes, key design 1).  w4 is [4][B][C][3][...].
+ * Returns 0, or -1 if scratch memory could not be obtained.
+ */
+int gspn_oracle_prop2d(const double* x, const double* lam, const double* u,
+                       const double* w4, double eps, double* y, long B,
+                       long C, long H, long W) {
+    long n = B * C * H * W;
+    double* part = (double*)malloc(sizeof(double) * (size_t)n);
+    if (!part) return -1;
+    for (long e = 0; e < n; ++e) y[e] = 0.0;
+    for (int d = 0; d < 4; ++d) {
+        if (gspn_oracle_scan_dir(x, lam, u, w4 + (long)d * 3 * n, 1, eps, part,
+                                 B, C, H, W, d) != 0) {
+            free(part);
+            return -1;
+        }
+        for (long e = 0; e < n; ++e) y[e] += part[e];
+    }
+    free(part);
+    return 0;
+}

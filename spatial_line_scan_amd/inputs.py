@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module holds no arithmetic of the propagation operator; it only draws
+numbers.  Values are a pure function of (seed, tensor id, element index), so
+any slice of any tensor can be regenerated on its own and the result does not
+depend on draw order, chunking or platform.
+
+Generator: SplitMix64 (G. Steele, D. Lea, C. Flood, "Fast splittable
+pseudorandom number generators", OOPSLA 2014; finaliser constants as
+published) used as a counter-based hash, and the Box-Muller transform
+(G. Box, M. Muller, 1958) for standard normals:
+
+    key      = mix(mix(seed) ^ (GAMMA * (tensor_id + 1)))
+    bits(j)  = mix(key + GAMMA * (j + 1))
+    u(j)     = ((bits(j) >> 11) + 1) * 2^-53          in (0, 1]
+    z(e)     = sqrt(-2 ln u(2e)) * cos(2 pi u(2e+1))   float64
+
+Storage rounding: fp32 tensors hold float32(z) (round to nearest even);
+bf16 tensors hold bf16(float32(z)) (round to nearest even on the fp32 bits).
+
+Tensor ids: x = 0, lambda = 1, u = 2, taps of all four directions = 3.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+TENSOR_IDS = {"x": 0, "lam": 1, "u": 2, "w": 3}
+_CHUNK = 1 << 22
+
+
+def _mix(z: np.ndarray) -> np.ndarray:
+    z = (z ^ (z >> np.uint64(30))) * _M1
+    z = (z ^ (z >> np.uint64(27))) * _M2
+    return z ^ (z >> np.uint64(31))
+
+
+def _key(seed: int, tensor_id: int) -> np.uint64:
+    with np.errstate(over="ignore"):
+        s = _mix(np.array([seed & 0xFFFFFFFFFFFFFFFF], dtype=np.uint64))
+        t = GAMMA * np.uint64(tensor_id + 1)
+        return _mix(s ^ t)[0]
+
+
+def normal_f64(seed: int, tensor_id: int, start: int, count: int) -> np.ndarray:
+    """Standard normals z(start) .. z(start + count - 1) of one tensor stream."""
+    key = _key(seed, tensor_id)
+    out = np.empty(count, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        for lo in range(0, count, _CHUNK):
+            n = min(_CHUNK, count - lo)
+            e = np.arange(start + lo, start + lo + n, dtype=np.uint64)
+            j1 = np.uint64(2) * e + np.uint64(1)     # counter of u(2e), offset by one
+            b1 = _mix(key + GAMMA * j1)
+            b2 = _mix(key + GAMMA * (j1 + np.uint64(1)))
+            u1 = ((b1 >> np.uint64(11)) + np.uint64(1)).astype(np.float64) * 2.0 ** -53
+            u2 = ((b2 >> np.uint64(11)) + np.uint64(1)).astype(np.float64) * 2.0 ** -53
+            out[lo:lo + n] = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
+    return out
+
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest even); returns uint16 bit patterns."""
+    bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
+    return ((bits + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32 values."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def draw(seed: int, name: str, shape, dtype: str, start: int = 0) -> np.ndarray:
+    """Values of one tensor (or of the slice starting at element `start`).
+
+    Returns float32 values; for dtype 'bf16' they are already rounded to bf16.
+    """
+    count = int(np.prod(shape))
+    z = normal_f64(seed, TENSOR_IDS[name], start, count).astype(np.float32)
+    if dtype == "bf16":
+        z = f32_from_bf16_bits(bf16_bits_from_f32(z))
+    elif dtype != "fp32":
+        raise ValueError("dtype must be 'fp32' or 'bf16'")
+    return z.reshape(shape)
+
+
+def problem(B: int, C: int, H: int, W: int, seed: int, dtype: str) -> dict:
+    """All inputs of one propagation problem as float32 numpy arrays.
+
+    x, lam, u: [B][C][H][W]; w: [4][B][C][3][H*W] taps (per direction laid out
+    [3][lines][line length] of that direction).
+    """
+    shp = (B, C, H, W)
+    return {
+        "x": draw(seed, "x", shp, dtype),
+        "lam": draw(seed, "lam", shp, dtype),
+        "u": draw(seed, "u", shp, dtype),
+        "w": draw(seed, "w", (4, B, C, 3, H * W), dtype),
+    }
+
+
+def plane_slice(B: int, C: int, H: int, W: int, seed: int, dtype: str, b: int, c: int) -> dict:
+    """Inputs of the single (b, c) plane of the problem drawn by `problem`.
+
+    Same values as slicing the full tensors, computed without drawing them.
+    """
+    n = H * W
+    pl = b * C + c
+    out = {name: draw(seed, name, (1, 1, H, W), dtype, start=pl * n) for name in ("x", "lam", "u")}
+    w = np.empty((4, 1, 1, 3, n), dtype=np.float32)
+    for d in range(4):
+        w[d, 0, 0] = draw(seed, "w", (3, n), dtype, start=((d * B + b) * C + c) * 3 * n)
+    out["w"] = w
+    return out
+
+
+def to_torch(a: np.ndarray, dtype: str, device="cpu"):
+    """A torch tensor holding exactly the values of `a` in the storage dtype."""
+    import torch
+    if dtype == "bf16":
+        bits = bf16_bits_from_f32(a)
+        t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32).copy())
+    return t.reshape(a.shape).to(device)

@@ -1,0 +1,50 @@
+"""The seeded input generator: deterministic, sliceable, standard normal."""
+import numpy as np
+
+from spatial_line_scan_amd import inputs
+
+
+def test_deterministic_and_sliceable():
+    a = inputs.normal_f64(3, 1, 0, 5000)
+    b = inputs.normal_f64(3, 1, 0, 5000)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(inputs.normal_f64(3, 1, 1234, 100), a[1234:1334])
+    assert not np.array_equal(a, inputs.normal_f64(4, 1, 0, 5000))
+    assert not np.array_equal(a, inputs.normal_f64(3, 2, 0, 5000))
+
+
+def test_standard_normal_moments():
+    z = inputs.normal_f64(0, 0, 0, 400_000)
+    assert abs(z.mean()) < 0.01
+    assert abs(z.std() - 1.0) < 0.01
+    assert abs(np.mean(np.abs(z) < 1.0) - 0.6827) < 0.01
+
+
+def test_splitmix64_reference_values():
+    # SplitMix64 with state 0: the first outputs of the published generator
+    # (mix applied to 0 + GAMMA, 0 + 2 GAMMA, ...).
+    st = np.array([0x9E3779B97F4A7C15, 0x3C6EF372FE94F82A], dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        got = inputs._mix(st)
+    assert [int(v) for v in got] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4]
+
+
+def test_bf16_round_to_nearest_even():
+    f = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 3.0e38], dtype=np.float32)
+    bits = inputs.bf16_bits_from_f32(f)
+    back = inputs.f32_from_bf16_bits(bits)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: rounds to the even 1.0
+    assert back[0] == 1.0 and back[1] == 1.0
+    # 1 + 3*2^-8 is a tie between 1 + 2^-7 and 1 + 2^-6: rounds to even 1 + 2^-6
+    assert back[2] == np.float32(1.0 + 2 ** -6)
+    assert back[3] == 1.0 and back[4] == -2.5
+    assert np.isfinite(back[5])
+
+
+def test_plane_slice_matches_full_problem():
+    B, C, H, W = 2, 3, 5, 4
+    full = inputs.problem(B, C, H, W, seed=9, dtype="bf16")
+    one = inputs.plane_slice(B, C, H, W, seed=9, dtype="bf16", b=1, c=2)
+    for k in ("x", "lam", "u"):
+        np.testing.assert_array_equal(one[k][0, 0], full[k][1, 2])
+    np.testing.assert_array_equal(one["w"][:, 0, 0], full["w"][:, 1, 2])

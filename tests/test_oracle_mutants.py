@@ -1,0 +1,76 @@
+"""The pins must reject plausible mistakes in the oracle.
+
+Each case compiles a copy of oracle/gspn_oracle.c with one deliberate error
+(a dropped term, a wrong sign or index, a transposed operand, a wrong scan
+order), points the oracle module at it, and requires that at least one pin
+of tests/test_oracle_pins.py fails.  Everything runs on the CPU.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "gspn_oracle.c")
+
+MUTANTS = [
+    ("taps mirrored in the mix", "                        long q = p + k - 1;",
+     "                        long q = p - k + 1;"),
+    ("out-of-line taps kept in the sum", "? sigmoid(raw[k]) : 0.0", "? sigmoid(raw[k]) : sigmoid(raw[k])"),
+    ("eps added instead of clamping", "double S = sum > eps ? sum : eps;", "double S = sum + eps;"),
+    ("clamp missing", "double S = sum > eps ? sum : eps;", "double S = sum;"),
+    ("lambda dropped", "double bx = lp[r * W + c] * xp[r * W + c];", "double bx = xp[r * W + c];"),
+    ("u dropped", "op[r * W + c] = up[r * W + c] * h;", "op[r * W + c] = h;"),
+    ("BU scans downwards, LR leftwards", "int forward = (dir == DIR_TD || dir == DIR_LR);",
+     "int forward = (dir == DIR_TD || dir == DIR_BU);"),
+    ("propagation term dropped", "h = mix + bx;", "h = bx;"),
+    ("sigmoid sign flipped", "exp(-z)", "exp(z)"),
+    ("only three directions summed", "for (int d = 0; d < 4; ++d)", "for (int d = 0; d < 3; ++d)"),
+    ("taps read mirrored along the line", "raw[k] = wp[k * npix + i * L + p];",
+     "raw[k] = wp[k * npix + i * L + (L - 1 - p)];"),
+    ("taps read from the transposed plane", "raw[k] = wp[k * npix + i * L + p];",
+     "raw[k] = wp[k * npix + p * NL + i];"),
+]
+
+
+def _checks():
+    yield lambda: pins.test_normalize_closed_forms()
+    yield lambda: pins.test_normalize_invariants(5, 7)
+    yield lambda: pins.test_worked_2x2()
+    for d in range(4):
+        yield lambda d=d: pins.test_scan_matches_dense_map(3, 5, d)
+        yield lambda d=d: pins.test_single_position_lines_are_running_sums(d)
+        yield lambda d=d: pins.test_identity_and_shift_taps(d)
+        yield lambda d=d: pins.test_row_stochastic_constant_propagates(d, 6, 9)
+    yield lambda: pins.test_direction_symmetries(4, 7)
+    yield lambda: pins.test_prop2d_is_sum_of_directions()
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not unique: " + old
+    mut = tmp_path / "mutant.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-shared", "-fPIC", str(mut), "-o", str(lib), "-lm"])
+    oracle.use_library(str(lib))
+    failed = 0
+    try:
+        for check in _checks():
+            try:
+                check()
+            except AssertionError:
+                failed += 1
+    finally:
+        oracle.use_library(None)
+    assert failed > 0, "no pin rejects the mutant: " + name
+
+
+def test_unmutated_oracle_passes_every_check():
+    for check in _checks():
+        check()
