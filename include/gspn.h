@@ -1,0 +1,144 @@
+/*
+ * gspn.h - C ABI of the MI355X (gfx950) GSPN line-scan propagation library.
+ *
+ * The operator is the 2D line-scan propagation of GSPN as used inside the
+ * C-GSPN latent sublayer ("Scaling Parallel Sequence Models to
+ * Foundation-Scale Vision Encoders": §3 "Background: 2D Spatial
+ * Propagation", §4 "A Fast GSPN Kernel", §5.1 "Latent-space 2D
+ * propagation" and "Fused CUDA normalization"; reading notes of the same
+ * paper, method / overall framework and key designs 1-2).
+ *
+ * For every (b, c) plane of a B x C x H x W feature map and for each of the
+ * four scan directions d (top-down TD, bottom-up BU, left-right LR,
+ * right-left RL) the lines of the plane are visited in order and
+ *
+ *     h_first = lambda * x                       (state before the first line is 0)
+ *     h_i[p]  = sum_k wn_k(i, p) * h_{i-1}[p + k - 1] + lambda_i[p] * x_i[p]
+ *     out_d   = u * h
+ *
+ * with the three taps k = 0, 1, 2 of destination position p made
+ * row-stochastic from raw logits w~ by the fused normalisation
+ *
+ *     s_k = sigmoid(w~_k) if p + k - 1 lies on the line, else 0
+ *     S   = max(s_0 + s_1 + s_2, eps)
+ *     wn_k = s_k / S.
+ *
+ * gspn_prop2d_4dir returns y = sum_d u * h_d.  Readings taken where the pages
+ * are silent: zero initial state; tap offsets are absolute (not mirrored for
+ * BU or RL); out-of-line taps are dropped from numerator and sum; the clamp
+ * bounds the sum below by eps; lambda and u are shared by the directions;
+ * the directional outputs are summed.
+ *
+ * ------------------------------------------------------------------------
+ * Layouts (all row-major, innermost index last, densely packed):
+ *   x, lambda, u, y        [B][C][H][W]
+ *   taps of one direction  [B][C][3][NL][L], indexed by (line i, position p)
+ *                          of that direction:
+ *                            TD, BU: line = row,    NL = H, L = W
+ *                            LR, RL: line = column, NL = W, L = H
+ *                          i.e. the LR/RL tap planes are stored transposed
+ *                          relative to the pixel grid, so that every line's
+ *                          taps are contiguous in memory.
+ *   taps of all directions [4][B][C][3][..][..] in the order TD, BU, LR, RL.
+ * Element types: every tensor of one call has the same type (GSPN_FP32 or
+ * GSPN_BF16); arithmetic is fp32; bf16 results are rounded to nearest even.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller; the
+ * library keeps no pointer after a call returns and allocates no device
+ * memory.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without synchronising.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * enqueued; on any error the call returns a non-zero gspn_status, enqueues
+ * nothing and leaves every output untouched.  GSPN_ERR_HIP reports a failed
+ * launch.  The library never prints, aborts or throws, keeps no mutable
+ * global state other than one-time device attribute queries, and may be
+ * called from several host threads.  Non-finite inputs propagate by IEEE
+ * rules; the results of a plane holding a non-finite input are unspecified
+ * but confined to that plane.
+ * ------------------------------------------------------------------------
+ */
+#ifndef GSPN_H
+#define GSPN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GSPN_ABI_VERSION 1
+
+/* Longest line (H or W) any entry point accepts. */
+#define GSPN_MAX_LINE 8192
+
+typedef enum {
+    GSPN_OK = 0,
+    GSPN_ERR_NULL = 1,   /* a required pointer is NULL                          */
+    GSPN_ERR_SHAPE = 2,  /* a size < 1, a line > GSPN_MAX_LINE, an element count
+                            >= 2^31, or a plane too large for the entry point  */
+    GSPN_ERR_DTYPE = 3,  /* unknown element type                                */
+    GSPN_ERR_DIR = 4,    /* unknown direction (or GSPN_ALL4 where one is needed)*/
+    GSPN_ERR_ALIGN = 5,  /* a pointer is not 16-byte aligned                    */
+    GSPN_ERR_ALIAS = 6,  /* an output overlaps an input                         */
+    GSPN_ERR_VALUE = 7,  /* eps is not finite and > 0, or a flag is not 0/1     */
+    GSPN_ERR_HIP = 8     /* the HIP runtime reported an error                   */
+} gspn_status;
+
+typedef enum { GSPN_FP32 = 0, GSPN_BF16 = 1 } gspn_dtype;
+
+typedef enum { GSPN_TD = 0, GSPN_BU = 1, GSPN_LR = 2, GSPN_RL = 3, GSPN_ALL4 = 4 } gspn_dir;
+
+/* GSPN_ABI_VERSION of the built library. */
+int gspn_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* gspn_status_str(int status);
+
+/*
+ * Row-stochastic normalisation of raw taps (sigmoid -> neighbourhood sum ->
+ * clamp -> divide; paper §5.1 "Fused CUDA normalization", reading notes,
+ * normalisation formula).
+ *   w_raw, w_norm : taps of direction `dir` ([B][C][3][NL][L]), or of all four
+ *                   directions ([4][B][C][3][..][..]) when dir == GSPN_ALL4.
+ *   Every position is written, the first line of each scan included.
+ *   w_norm must not overlap w_raw.
+ */
+int gspn_normalize_weights(const void* w_raw, void* w_norm, int dtype,
+                           int64_t B, int64_t C, int64_t H, int64_t W,
+                           int dir, float eps, void* stream);
+
+/*
+ * One scan direction (paper §3 line-scan recurrence; §4.1 single-kernel
+ * design: every line step of the scan runs inside one launch).
+ *   x, lam, u, y : [B][C][H][W];  w : taps of direction `dir`.
+ *   w_is_raw = 1 : w holds logits, normalised on the fly (fused);
+ *   w_is_raw = 0 : w holds final weights, used as given (a tap whose source
+ *                  lies outside the line contributes nothing).
+ *   accumulate = 0 : y = u * h;   accumulate = 1 : y = y + u * h.
+ *   y must not overlap x, lam, u or w.
+ */
+int gspn_scan_dir(const void* x, const void* lam, const void* u, const void* w,
+                  int w_is_raw, float eps, void* y, int accumulate, int dtype,
+                  int64_t B, int64_t C, int64_t H, int64_t W, int dir,
+                  void* stream);
+
+/*
+ * All four directions with fused normalisation, in one launch:
+ *   y = u * (h_TD + h_BU + h_LR + h_RL)
+ * (the latent propagation y_c = Prop2D(x_c; u, lambda, w) of reading notes
+ * key design 1, run on whatever channel count the caller passes, e.g. the
+ * compressed latent C_c).
+ *   x, lam, u, y : [B][C][H][W];  w_raw4 : [4][B][C][3][..][..] logits.
+ *   y must not overlap any input.  The result is bitwise reproducible
+ *   from run to run.
+ */
+int gspn_prop2d_4dir(const void* x, const void* lam, const void* u,
+                     const void* w_raw4, float eps, void* y, int dtype,
+                     int64_t B, int64_t C, int64_t H, int64_t W, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSPN_H */

@@ -1,0 +1,119 @@
+// C-ABI entry points of libgspn: argument validation and dispatch.
+//
+// Every check runs on the host before anything touches the device, so a bad
+// call returns its status with nothing enqueued and every output untouched.
+#include "gspn.h"
+#include "gspn_internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+
+int64_t elem_size(int dtype) { return dtype == GSPN_FP32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) { return dtype == GSPN_FP32 || dtype == GSPN_BF16; }
+
+// Sizes of a B x C x H x W problem whose largest tensor holds `mult` values
+// per pixel-channel.
+int check_dims(int64_t B, int64_t C, int64_t H, int64_t W, int64_t mult) {
+    if (B < 1 || C < 1 || H < 1 || W < 1) return GSPN_ERR_SHAPE;
+    if (H > GSPN_MAX_LINE || W > GSPN_MAX_LINE) return GSPN_ERR_SHAPE;
+    if (B > kMaxElems || C > kMaxElems) return GSPN_ERR_SHAPE;
+    const int64_t plane = H * W;  // <= 2^26
+    if (B * C > kMaxElems / plane) return GSPN_ERR_SHAPE;
+    if (B * C * plane > kMaxElems / mult) return GSPN_ERR_SHAPE;
+    return GSPN_OK;
+}
+
+bool valid_eps(float eps) { return std::isfinite(eps) && eps > 0.0f; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? GSPN_OK : GSPN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int gspn_abi_version(void) { return GSPN_ABI_VERSION; }
+
+const char* gspn_status_str(int status) {
+    switch (status) {
+        case GSPN_OK: return "GSPN_OK";
+        case GSPN_ERR_NULL: return "GSPN_ERR_NULL: a required pointer is NULL";
+        case GSPN_ERR_SHAPE: return "GSPN_ERR_SHAPE: unsupported sizes";
+        case GSPN_ERR_DTYPE: return "GSPN_ERR_DTYPE: unknown element type";
+        case GSPN_ERR_DIR: return "GSPN_ERR_DIR: unknown direction";
+        case GSPN_ERR_ALIGN: return "GSPN_ERR_ALIGN: pointer not 16-byte aligned";
+        case GSPN_ERR_ALIAS: return "GSPN_ERR_ALIAS: output overlaps an input";
+        case GSPN_ERR_VALUE: return "GSPN_ERR_VALUE: eps must be finite and > 0, flags 0 or 1";
+        case GSPN_ERR_HIP: return "GSPN_ERR_HIP: HIP runtime error";
+        default: return "GSPN: unknown status";
+    }
+}
+
+int gspn_normalize_weights(const void* w_raw, void* w_norm, int dtype, int64_t B, int64_t C,
+                           int64_t H, int64_t W, int dir, float eps, void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
+    if (dir < GSPN_TD || dir > GSPN_ALL4) return GSPN_ERR_DIR;
+    const int ndir = dir == GSPN_ALL4 ? 4 : 1;
+    if (int s = check_dims(B, C, H, W, 3 * ndir)) return s;
+    if (!valid_eps(eps)) return GSPN_ERR_VALUE;
+    if (!w_raw || !w_norm) return GSPN_ERR_NULL;
+    if (!aligned16(w_raw) || !aligned16(w_norm)) return GSPN_ERR_ALIGN;
+    const int64_t bytes = B * C * H * W * 3 * ndir * elem_size(dtype);
+    if (overlap(w_raw, bytes, w_norm, bytes)) return GSPN_ERR_ALIAS;
+    return launch_status(gspn::launch_normalize(w_raw, w_norm, dtype, B * C, H, W,
+                                                dir == GSPN_ALL4 ? 0 : dir, ndir, eps,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int gspn_scan_dir(const void* x, const void* lam, const void* u, const void* w, int w_is_raw,
+                  float eps, void* y, int accumulate, int dtype, int64_t B, int64_t C,
+                  int64_t H, int64_t W, int dir, void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
+    if (dir < GSPN_TD || dir > GSPN_RL) return GSPN_ERR_DIR;
+    if (int s = check_dims(B, C, H, W, 3)) return s;
+    if ((w_is_raw != 0 && w_is_raw != 1) || (accumulate != 0 && accumulate != 1))
+        return GSPN_ERR_VALUE;
+    if (w_is_raw && !valid_eps(eps)) return GSPN_ERR_VALUE;
+    if (!x || !lam || !u || !w || !y) return GSPN_ERR_NULL;
+    if (!aligned16(x) || !aligned16(lam) || !aligned16(u) || !aligned16(w) || !aligned16(y))
+        return GSPN_ERR_ALIGN;
+    const int64_t n = B * C * H * W * elem_size(dtype);
+    if (overlap(y, n, x, n) || overlap(y, n, lam, n) || overlap(y, n, u, n) ||
+        overlap(y, n, w, 3 * n))
+        return GSPN_ERR_ALIAS;
+    return launch_status(gspn::launch_scan_dir(x, lam, u, w, w_is_raw, eps, y, accumulate, dtype,
+                                               B * C, H, W, dir,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int gspn_prop2d_4dir(const void* x, const void* lam, const void* u, const void* w_raw4,
+                     float eps, void* y, int dtype, int64_t B, int64_t C, int64_t H, int64_t W,
+                     void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
+    if (int s = check_dims(B, C, H, W, 12)) return s;
+    if (H * W > gspn::prop2d_max_plane(dtype, H, W)) return GSPN_ERR_SHAPE;
+    if (!valid_eps(eps)) return GSPN_ERR_VALUE;
+    if (!x || !lam || !u || !w_raw4 || !y) return GSPN_ERR_NULL;
+    if (!aligned16(x) || !aligned16(lam) || !aligned16(u) || !aligned16(w_raw4) ||
+        !aligned16(y))
+        return GSPN_ERR_ALIGN;
+    const int64_t n = B * C * H * W * elem_size(dtype);
+    if (overlap(y, n, x, n) || overlap(y, n, lam, n) || overlap(y, n, u, n) ||
+        overlap(y, n, w_raw4, 12 * n))
+        return GSPN_ERR_ALIAS;
+    return launch_status(gspn::launch_prop2d(x, lam, u, w_raw4, eps, y, dtype, B * C, H, W,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Internal interface between the C-ABI host layer (gspn_host.cpp) and the
+// gfx950 kernels (gspn_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gspn {
+
+// LDS a single workgroup may address on gfx950 (160 KiB per CU).
+constexpr int64_t kLdsBytes = 160 * 1024;
+
+// Launchers.  Arguments are already validated; each enqueues work on
+// `stream` and returns the launch status.
+hipError_t launch_normalize(const void* w_raw, void* w_norm, int dtype, int64_t planes,
+                            int64_t H, int64_t W, int dir0, int ndir, float eps,
+                            hipStream_t stream);
+
+hipError_t launch_scan_dir(const void* x, const void* lam, const void* u, const void* w,
+                           int w_is_raw, float eps, void* y, int accumulate, int dtype,
+                           int64_t planes, int64_t H, int64_t W, int dir, hipStream_t stream);
+
+hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const void* w4,
+                         float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
+                         hipStream_t stream);
+
+// Largest plane (H * W pixels) gspn_prop2d_4dir accepts for an element type.
+int64_t prop2d_max_plane(int dtype, int64_t H, int64_t W);
+
+}  // namespace gspn

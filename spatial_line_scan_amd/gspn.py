@@ -1,0 +1,148 @@
+"""ctypes binding of libgspn (include/gspn.h).  Argument marshalling only.
+
+Every function here checks torch-level facts (device, dtype, contiguity,
+element counts), allocates the output with torch when none is given, and
+calls the C ABI on torch's current HIP stream.  All arithmetic happens in the
+library's gfx950 kernels; there is no fallback.  If libgspn.so is missing the
+first call raises.
+
+Tensor layouts (see include/gspn.h):
+  x, lam, u, y   [B, C, H, W]
+  taps of a direction  B*C*3*H*W elements, laid out [B][C][3][lines][length]
+      (TD/BU: lines are rows; LR/RL: lines are columns, i.e. transposed)
+  w4             4*B*C*3*H*W elements, directions in the order TD, BU, LR, RL
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+TD, BU, LR, RL, ALL4 = 0, 1, 2, 3, 4
+FP32, BF16 = 0, 1
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgspn.so")
+_lib = None
+
+_STATUS_EXC = {1: ValueError, 2: ValueError, 3: TypeError, 4: ValueError, 5: ValueError,
+               6: ValueError, 7: ValueError, 8: RuntimeError}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libgspn (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libgspn.so is not built (%s); run `python -m "
+                               "spatial_line_scan_amd.build` or __graft_entry__.build()" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64, ci, cf = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        L.gspn_abi_version.argtypes = []
+        L.gspn_abi_version.restype = ci
+        L.gspn_status_str.argtypes = [ci]
+        L.gspn_status_str.restype = ctypes.c_char_p
+        L.gspn_normalize_weights.argtypes = [vp, vp, ci, i64, i64, i64, i64, ci, cf, vp]
+        L.gspn_normalize_weights.restype = ci
+        L.gspn_scan_dir.argtypes = [vp, vp, vp, vp, ci, cf, vp, ci, ci, i64, i64, i64, i64, ci, vp]
+        L.gspn_scan_dir.restype = ci
+        L.gspn_prop2d_4dir.argtypes = [vp, vp, vp, vp, cf, vp, ci, i64, i64, i64, i64, vp]
+        L.gspn_prop2d_4dir.restype = ci
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = lib().gspn_status_str(status).decode()
+        raise _STATUS_EXC.get(status, RuntimeError)(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FP32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("gspn tensors must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _same(ref: torch.Tensor, *ts: torch.Tensor):
+    for t in ts:
+        if t.device != ref.device or t.dtype != ref.dtype:
+            raise ValueError("all tensors must share device and dtype")
+        if not t.is_contiguous():
+            raise ValueError("gspn tensors must be contiguous")
+    if ref.device.type != "cuda":
+        raise ValueError("gspn tensors must be on a GPU device")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _p(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def normalize_weights(w: torch.Tensor, dir: int, B: int, C: int, H: int, W: int,
+                      eps: float = 1e-6, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-stochastic taps from raw logits (one direction, or ALL4)."""
+    _same(w, w)
+    n = 3 * B * C * H * W * (4 if dir == ALL4 else 1)
+    if w.numel() != n:
+        raise ValueError("w has %d elements, expected %d" % (w.numel(), n))
+    if out is None:
+        out = torch.empty_like(w)
+    _same(w, out)
+    with torch.cuda.device(w.device):
+        _check(lib().gspn_normalize_weights(_p(w), _p(out), _dtype_code(w), B, C, H, W, dir,
+                                            float(eps), _stream(w)))
+    return out
+
+
+def scan_dir(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w: torch.Tensor, dir: int,
+             w_is_raw: bool = True, out: torch.Tensor | None = None, accumulate: bool = False,
+             eps: float = 1e-6) -> torch.Tensor:
+    """u * h of one direction (accumulate: out += u * h)."""
+    _same(x, lam, u, w)
+    if x.dim() != 4 or lam.shape != x.shape or u.shape != x.shape:
+        raise ValueError("x, lam, u must share one [B, C, H, W] shape")
+    B, C, H, W = x.shape
+    if w.numel() != 3 * x.numel():
+        raise ValueError("w must hold 3*B*C*H*W elements")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an output tensor")
+        out = torch.empty_like(x)
+    _same(x, out)
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    with torch.cuda.device(x.device):
+        _check(lib().gspn_scan_dir(_p(x), _p(lam), _p(u), _p(w), int(bool(w_is_raw)), float(eps),
+                                   _p(out), int(bool(accumulate)), _dtype_code(x), B, C, H, W,
+                                   dir, _stream(x)))
+    return out
+
+
+def prop2d_4dir(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4: torch.Tensor,
+                eps: float = 1e-6, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = u * (h_TD + h_BU + h_LR + h_RL) with fused tap normalisation."""
+    _same(x, lam, u, w4)
+    if x.dim() != 4 or lam.shape != x.shape or u.shape != x.shape:
+        raise ValueError("x, lam, u must share one [B, C, H, W] shape")
+    B, C, H, W = x.shape
+    if w4.numel() != 12 * x.numel():
+        raise ValueError("w4 must hold 4*B*C*3*H*W elements")
+    if out is None:
+        out = torch.empty_like(x)
+    _same(x, out)
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    with torch.cuda.device(x.device):
+        _check(lib().gspn_prop2d_4dir(_p(x), _p(lam), _p(u), _p(w4), float(eps), _p(out),
+                                      _dtype_code(x), B, C, H, W, _stream(x)))
+    return out

@@ -118,6 +118,73 @@ def plane_slice(B: int, C: int, H: int, W: int, seed: int, dtype: str, b: int, c
     return out
 
 
+# ------------------------------------------------------------------ torch path
+#
+# The same generator written with torch int64 tensors (two's-complement
+# wrap-around equals arithmetic modulo 2^64; logical shifts are masked), so
+# large problems can be drawn on the device.  The integer stream is identical
+# bit for bit; the float64 log/cos may differ from numpy's in the last bit,
+# which changes a rounded fp32 value with probability about 2^-28.
+
+def _signed(v: int) -> int:
+    v &= 0xFFFFFFFFFFFFFFFF
+    return v - (1 << 64) if v >= (1 << 63) else v
+
+
+_GAMMA_S = _signed(int(GAMMA))
+_M1_S = _signed(int(_M1))
+_M2_S = _signed(int(_M2))
+
+
+def _srl(z, k: int):
+    return (z >> k) & ((1 << (64 - k)) - 1)
+
+
+def _mix_t(z):
+    z = (z ^ _srl(z, 30)) * _M1_S
+    z = (z ^ _srl(z, 27)) * _M2_S
+    return z ^ _srl(z, 31)
+
+
+def draw_torch(seed: int, name: str, shape, dtype: str, device, start: int = 0):
+    """Tensor of the values `draw` returns, generated on `device`.
+
+    dtype 'fp32' gives a float32 tensor, 'bf16' a bfloat16 tensor.
+    """
+    import torch
+    count = int(np.prod(shape))
+    key = _signed(int(_key(seed, TENSOR_IDS[name])))
+    out = torch.empty(count, dtype=torch.float32, device=device)
+    chunk = 1 << 24
+    for lo in range(0, count, chunk):
+        n = min(chunk, count - lo)
+        e = torch.arange(start + lo, start + lo + n, dtype=torch.int64, device=device)
+        j1 = e * 2 + 1
+        b1 = _mix_t(key + _GAMMA_S * j1)
+        b2 = _mix_t(key + _GAMMA_S * (j1 + 1))
+        u1 = (_srl(b1, 11) + 1).to(torch.float64) * 2.0 ** -53
+        u2 = (_srl(b2, 11) + 1).to(torch.float64) * 2.0 ** -53
+        z = torch.sqrt(-2.0 * torch.log(u1)) * torch.cos(2.0 * np.pi * u2)
+        out[lo:lo + n] = z.to(torch.float32)
+        del e, j1, b1, b2, u1, u2, z
+    if dtype == "bf16":
+        out = out.to(torch.bfloat16)
+    elif dtype != "fp32":
+        raise ValueError("dtype must be 'fp32' or 'bf16'")
+    return out.reshape(shape)
+
+
+def problem_torch(B: int, C: int, H: int, W: int, seed: int, dtype: str, device) -> dict:
+    """`problem` drawn directly as device tensors."""
+    shp = (B, C, H, W)
+    return {
+        "x": draw_torch(seed, "x", shp, dtype, device),
+        "lam": draw_torch(seed, "lam", shp, dtype, device),
+        "u": draw_torch(seed, "u", shp, dtype, device),
+        "w": draw_torch(seed, "w", (4, B, C, 3, H * W), dtype, device),
+    }
+
+
 def to_torch(a: np.ndarray, dtype: str, device="cpu"):
     """A torch tensor holding exactly the values of `a` in the storage dtype."""
     import torch

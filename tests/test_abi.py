@@ -1,0 +1,145 @@
+"""The C ABI: the library loads on any host, exports what include/gspn.h
+declares, and rejects every bad argument on the host before touching a device.
+
+No test here launches a kernel: each call has exactly one thing wrong, and
+validation returns before any HIP call.  Pointers are fake addresses that are
+never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from spatial_line_scan_amd import gspn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "gspn.h")
+
+OK, NULL, SHAPE, DTYPE, DIR, ALIGN, ALIAS, VALUE, HIP = range(9)
+A = 0x7F0000000000          # fake 16-byte-aligned device addresses, far apart
+STEP = 0x10000000000
+
+
+def P(i):
+    return ctypes.c_void_p(A + i * STEP)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gspn.library_path()):
+        pytest.skip("libgspn.so not built")
+    return gspn.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(gspn_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert set(syms) >= {"gspn_abi_version", "gspn_status_str", "gspn_normalize_weights",
+                         "gspn_scan_dir", "gspn_prop2d_4dir"}
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_version_and_status_strings(L):
+    assert L.gspn_abi_version() == 1
+    for s in range(9):
+        assert L.gspn_status_str(s).decode().startswith("GSPN")
+    assert L.gspn_status_str(12345)
+
+
+def prop(L, x=None, lam=None, u=None, w=None, eps=1e-6, y=None, dt=0, B=2, C=3, H=5, W=7):
+    return L.gspn_prop2d_4dir(x or P(0), lam or P(1), u or P(2), w or P(3), eps, y or P(5), dt,
+                              B, C, H, W, None)
+
+
+def scan(L, w_is_raw=1, eps=1e-6, acc=0, dt=0, B=2, C=3, H=5, W=7, d=0, x=None, y=None):
+    return L.gspn_scan_dir(x or P(0), P(1), P(2), P(3), w_is_raw, eps, y or P(5), acc, dt, B, C,
+                           H, W, d, None)
+
+
+def norm(L, dt=0, B=2, C=3, H=5, W=7, d=4, eps=1e-6, src=None, dst=None):
+    return L.gspn_normalize_weights(src or P(3), dst or P(6), dt, B, C, H, W, d, eps, None)
+
+
+def test_dtype_and_direction(L):
+    assert prop(L, dt=2) == DTYPE
+    assert scan(L, dt=-1) == DTYPE
+    assert norm(L, dt=7) == DTYPE
+    assert scan(L, d=4) == DIR           # scan needs a single direction
+    assert scan(L, d=-1) == DIR
+    assert norm(L, d=5) == DIR
+
+
+@pytest.mark.parametrize("dims", [(0, 3, 5, 7), (2, 0, 5, 7), (2, 3, 0, 7), (2, 3, 5, 0),
+                                  (-1, 3, 5, 7), (1, 1, 8193, 4), (1, 1, 4, 8193),
+                                  (1 << 20, 1 << 20, 2, 2), (1, 1 << 18, 64, 64)])
+def test_bad_sizes(L, dims):
+    B, C, H, W = dims
+    assert prop(L, B=B, C=C, H=H, W=W) == SHAPE
+    assert scan(L, B=B, C=C, H=H, W=W) == SHAPE
+    assert norm(L, B=B, C=C, H=H, W=W) == SHAPE
+
+
+def test_element_count_limit_counts_all_taps(L):
+    # 12 taps per pixel-channel must stay below 2^31 elements
+    assert prop(L, B=1, C=2048, H=512, W=512) == SHAPE      # 12 * 2^29 > 2^31
+    assert norm(L, B=1, C=4096, H=256, W=256, d=4) == SHAPE  # 12 * 2^28 > 2^31
+    # 12 * 2^26 = 805M < 2^31 is accepted: this call is rejected only by its
+    # overlapping (fake) pointers
+    assert norm(L, B=1, C=1024, H=256, W=256, d=4, dst=ctypes.c_void_p(A + 3 * STEP + 16)) == ALIAS
+
+
+def test_bf16_plane_limit(L):
+    assert prop(L, dt=1, B=1, C=1, H=256, W=256) == SHAPE   # accumulator does not fit on chip
+
+
+@pytest.mark.parametrize("eps", [0.0, -1e-6, float("nan"), float("inf")])
+def test_bad_eps(L, eps):
+    assert prop(L, eps=eps) == VALUE
+    assert scan(L, eps=eps) == VALUE
+    assert norm(L, eps=eps) == VALUE
+
+
+def test_eps_ignored_for_normalised_taps(L):
+    # with w_is_raw = 0 eps is unused; the call fails later, on the alias check
+    assert scan(L, w_is_raw=0, eps=float("nan"), y=P(0)) == ALIAS
+
+
+def test_bad_flags(L):
+    assert scan(L, w_is_raw=2) == VALUE
+    assert scan(L, acc=-1) == VALUE
+
+
+def test_null_pointers(L):
+    null = ctypes.c_void_p(0)
+    for i in range(5):
+        args = [P(0), P(1), P(2), P(3), P(5)]
+        args[i] = null
+        assert L.gspn_prop2d_4dir(args[0], args[1], args[2], args[3], 1e-6, args[4], 0, 2, 3, 5, 7,
+                                  None) == NULL
+        assert L.gspn_scan_dir(args[0], args[1], args[2], args[3], 1, 1e-6, args[4], 0, 0, 2, 3, 5,
+                               7, 0, None) == NULL
+    assert L.gspn_normalize_weights(null, P(6), 0, 2, 3, 5, 7, 4, 1e-6, None) == NULL
+    assert L.gspn_normalize_weights(P(3), null, 0, 2, 3, 5, 7, 4, 1e-6, None) == NULL
+
+
+def test_misaligned(L):
+    bad = ctypes.c_void_p(A + 8)
+    assert prop(L, x=bad) == ALIGN
+    assert prop(L, y=ctypes.c_void_p(A + 5 * STEP + 4)) == ALIGN
+    assert scan(L, x=bad) == ALIGN
+    assert norm(L, src=bad) == ALIGN
+
+
+def test_aliasing(L):
+    assert prop(L, y=P(0)) == ALIAS
+    assert prop(L, y=ctypes.c_void_p(A + 3 * STEP + 16)) == ALIAS          # inside w4
+    n = 2 * 3 * 5 * 7 * 4
+    assert prop(L, y=ctypes.c_void_p(A + 3 * STEP + 12 * n - 16)) == ALIAS  # tail of w4
+    assert scan(L, y=P(0)) == ALIAS
+    assert norm(L, dst=P(3)) == ALIAS

@@ -48,3 +48,11 @@ def test_plane_slice_matches_full_problem():
     for k in ("x", "lam", "u"):
         np.testing.assert_array_equal(one[k][0, 0], full[k][1, 2])
     np.testing.assert_array_equal(one["w"][:, 0, 0], full["w"][:, 1, 2])
+
+
+def test_torch_path_matches_numpy_path():
+    import torch
+    for dtype in ("fp32", "bf16"):
+        a = inputs.draw(5, "w", (3, 7, 1111), dtype, start=17)
+        t = inputs.draw_torch(5, "w", (3, 7, 1111), dtype, "cpu", start=17)
+        np.testing.assert_array_equal(t.to(torch.float32).numpy(), a)

@@ -1,0 +1,30 @@
+"""Agreement test between a GPU result and the fp64 oracle.
+
+Pass iff both hold, with r the oracle and g the GPU output widened to fp64:
+  elementwise  |g - r| <= rtol * max(|r|, rms(r))   (rms over the whole output)
+  normwise     ||g - r||_2 <= rtol * ||r||_2
+fp32 storage: rtol 1e-5; bf16 storage (fp32 arithmetic): rtol 2e-2.
+"""
+import numpy as np
+
+RTOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+def compare(g, r, rtol):
+    g = np.asarray(g, dtype=np.float64).reshape(-1)
+    r = np.asarray(r, dtype=np.float64).reshape(-1)
+    if r.size == 0:
+        return True, "empty"
+    err = np.abs(g - r)
+    rms = float(np.sqrt(np.mean(r * r)))
+    floor = np.maximum(np.abs(r), rms)
+    worst = float(np.max(err / np.where(floor > 0, floor, 1.0)))
+    nr = float(np.linalg.norm(r))
+    normwise = float(np.linalg.norm(g - r)) / (nr if nr > 0 else 1.0)
+    ok = bool(np.all(np.isfinite(g))) and worst <= rtol and normwise <= rtol
+    return ok, "worst elementwise %.3e, normwise %.3e (rtol %.1e)" % (worst, normwise, rtol)
+
+
+def assert_close(g, r, rtol, what=""):
+    ok, msg = compare(g, r, rtol)
+    assert ok, (what + ": " if what else "") + msg
