@@ -1,0 +1,238 @@
+"""Throughput of the four-direction GSPN propagation on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload latent1k]
+
+One step = one gspn_prop2d_4dir launch over the whole workload (normalise
+the 12 taps of every pixel-channel, scan all four directions, write y), on
+inputs already resident in HBM.  Input sets are rotated so that successive
+steps do not hit the 256 MB Infinity Cache.  Prints one JSON line.
+
+value     : algorithmic GB/s = 16 values per pixel-channel (read x, lambda, u
+            and 4 x 3 taps, write y) x bytes per value / wall time per step
+roofline  : the same bytes / average kernel duration (HIP events on the
+            launch stream), against the MI355X HBM peak of 8 TB/s; `traffic`
+            is the measured HBM bytes per launch from the committed rocprofv3
+            counter summary when it was taken on the current kernel source
+cpu_baseline : the fp64 C oracle on the host, single thread, on a bounded
+            sample of the same workload (whole planes)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "4-dir GSPN propagation GB/s & ms (B=32,C_c=64,74×74) + % of HBM peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prop2d_latent1k_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "spatial_line_scan_amd", "csrc", f)
+                  for f in ("gspn_kernels.hip", "gspn_host.cpp", "gspn_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
+    """Time the fp64 oracle on whole planes of the workload, single-threaded.
+
+    The planes are those of the first rotated input set, in order, until the
+    time budget is spent (the whole workload if it fits); the GPU output of
+    those planes from the timed steps is compared with the oracle's as a
+    by-product.
+    """
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle.tolerance import RTOL, compare
+
+    lib = oracle._load()
+    dp = ctypes.POINTER(ctypes.c_double)
+    n = wl.H * wl.W
+    f64 = lambda t: t.to("cpu", torch.float32).numpy().astype(np.float64)
+    X, LAM, U, Wt = (f64(gpu_inputs[k]) for k in ("x", "lam", "u", "w"))
+    Wt = Wt.reshape(4, wl.B, wl.C, 3 * n)
+    Y = f64(gpu_out)
+    planes, spent, all_ok, details = 0, 0.0, True, []
+    order = [(b, c) for b in range(wl.B) for c in range(wl.C)]
+    while spent < budget_s and planes < len(order):
+        b, c = order[planes]
+        arrs = [np.ascontiguousarray(a[b, c]) for a in (X, LAM, U)]
+        arrs.append(np.ascontiguousarray(Wt[:, b, c]))
+        y = np.empty_like(arrs[0])
+        t0 = time.perf_counter()
+        rc = lib.gspn_oracle_prop2d(*(a.ctypes.data_as(dp) for a in arrs), 1e-6,
+                                    y.ctypes.data_as(dp), 1, 1, wl.H, wl.W)
+        spent += time.perf_counter() - t0
+        if rc != 0:
+            raise MemoryError("oracle failed")
+        ok, msg = compare(Y[b, c], y, RTOL[wl.dtype])
+        all_ok &= ok
+        if len(details) < 2 or not ok:
+            details.append("(%d,%d): %s" % (b, c, msg))
+        planes += 1
+    bytes_done = 16 * wl.elem_bytes * n * planes
+    return {
+        "value": bytes_done / spent / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d of %d planes (%dx%d, %s values) of the timed inputs, fp64 C loop, %.1f s" % (
+            planes, wl.B * wl.C, wl.H, wl.W, wl.dtype, spent),
+        "seconds": spent,
+        "cpu": _cpu_model(),
+        "host_cores_visible": os.cpu_count(),
+        "gpu_output_matches_oracle_on_sample": bool(all_ok),
+        "parity_detail": details[:6],
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="latent1k")
+    ap.add_argument("--rotate-bytes", type=float, default=1.0e9,
+                    help="total bytes of rotated input sets (defeats the 256 MB cache)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the propagation shards over independent (b, c) "
+              "planes with no exchange, so there is no multi-GPU code path; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from spatial_line_scan_amd import gspn, inputs
+    from spatial_line_scan_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: drawing %s inputs" % wl.name, file=sys.stderr, flush=True)
+    base = inputs.problem_torch(wl.B, wl.C, wl.H, wl.W, 0, wl.dtype, dev)
+    nsets = max(1, int(np.ceil(args.rotate_bytes / wl.algorithmic_bytes)))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    outs = [torch.empty_like(base["x"]) for _ in range(nsets)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        s = sets[i % nsets]
+        gspn.prop2d_4dir(s["x"], s["lam"], s["u"], s["w"], out=outs[i % nsets])
+
+    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # wall time of exactly K steps
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-launch kernel durations, HIP events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg = float(np.mean(kern_ms))
+
+    # calibration: a plain device copy of ~1 GB through the same HBM
+    cal = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cal2 = torch.empty_like(cal)
+    cal2.copy_(cal)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        cal2.copy_(cal)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cal.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cal, cal2
+
+    nbytes = wl.algorithmic_bytes
+    ms_per_step = wall * 1e3 / args.steps
+    value = nbytes / (wall / args.steps) / 1e9
+    achieved = nbytes / (kern_avg * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W,
+                   "storage": wl.dtype, "arithmetic": "fp32", "rotated_input_sets": nsets,
+                   "algorithmic_bytes_per_step": nbytes},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel_ms_avg": round(kern_avg, 5),
+                     "kernel_ms_min": round(float(np.min(kern_ms)), 5)},
+        "calibration": {"torch_copy_GBps": round(copy_gbps, 1),
+                        "frac_of_copy": round(achieved / copy_gbps, 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, sets[0], outs[0])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

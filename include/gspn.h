@@ -79,7 +79,7 @@ typedef enum {
                             >= 2^31, or a plane too large for the entry point  */
     GSPN_ERR_DTYPE = 3,  /* unknown element type                                */
     GSPN_ERR_DIR = 4,    /* unknown direction (or GSPN_ALL4 where one is needed)*/
-    GSPN_ERR_ALIGN = 5,  /* a pointer is not 16-byte aligned                    */
+    GSPN_ERR_ALIGN = 5,  /* a pointer is not aligned to its element size        */
     GSPN_ERR_ALIAS = 6,  /* an output overlaps an input                         */
     GSPN_ERR_VALUE = 7,  /* eps is not finite and > 0, or a flag is not 0/1     */
     GSPN_ERR_HIP = 8     /* the HIP runtime reported an error                   */

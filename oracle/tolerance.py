@@ -1,4 +1,4 @@
-"""Agreement test between a GPU result and the fp64 oracle.
+"""Agreement test between a GPU result and the fp64 oracle (test infrastructure).
 
 Pass iff both hold, with r the oracle and g the GPU output widened to fp64:
   elementwise  |g - r| <= rtol * max(|r|, rms(r))   (rms over the whole output)

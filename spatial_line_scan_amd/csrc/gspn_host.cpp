@@ -30,7 +30,10 @@ int check_dims(int64_t B, int64_t C, int64_t H, int64_t W, int64_t mult) {
 
 bool valid_eps(float eps) { return std::isfinite(eps) && eps > 0.0f; }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// Natural alignment of the element type.
+bool aligned(const void* p, int dtype) {
+    return (reinterpret_cast<uintptr_t>(p) & static_cast<uintptr_t>(elem_size(dtype) - 1)) == 0;
+}
 
 bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -52,7 +55,7 @@ const char* gspn_status_str(int status) {
         case GSPN_ERR_SHAPE: return "GSPN_ERR_SHAPE: unsupported sizes";
         case GSPN_ERR_DTYPE: return "GSPN_ERR_DTYPE: unknown element type";
         case GSPN_ERR_DIR: return "GSPN_ERR_DIR: unknown direction";
-        case GSPN_ERR_ALIGN: return "GSPN_ERR_ALIGN: pointer not 16-byte aligned";
+        case GSPN_ERR_ALIGN: return "GSPN_ERR_ALIGN: pointer not aligned to its element size";
         case GSPN_ERR_ALIAS: return "GSPN_ERR_ALIAS: output overlaps an input";
         case GSPN_ERR_VALUE: return "GSPN_ERR_VALUE: eps must be finite and > 0, flags 0 or 1";
         case GSPN_ERR_HIP: return "GSPN_ERR_HIP: HIP runtime error";
@@ -68,7 +71,7 @@ int gspn_normalize_weights(const void* w_raw, void* w_norm, int dtype, int64_t B
     if (int s = check_dims(B, C, H, W, 3 * ndir)) return s;
     if (!valid_eps(eps)) return GSPN_ERR_VALUE;
     if (!w_raw || !w_norm) return GSPN_ERR_NULL;
-    if (!aligned16(w_raw) || !aligned16(w_norm)) return GSPN_ERR_ALIGN;
+    if (!aligned(w_raw, dtype) || !aligned(w_norm, dtype)) return GSPN_ERR_ALIGN;
     const int64_t bytes = B * C * H * W * 3 * ndir * elem_size(dtype);
     if (overlap(w_raw, bytes, w_norm, bytes)) return GSPN_ERR_ALIAS;
     return launch_status(gspn::launch_normalize(w_raw, w_norm, dtype, B * C, H, W,
@@ -86,7 +89,8 @@ int gspn_scan_dir(const void* x, const void* lam, const void* u, const void* w, 
         return GSPN_ERR_VALUE;
     if (w_is_raw && !valid_eps(eps)) return GSPN_ERR_VALUE;
     if (!x || !lam || !u || !w || !y) return GSPN_ERR_NULL;
-    if (!aligned16(x) || !aligned16(lam) || !aligned16(u) || !aligned16(w) || !aligned16(y))
+    if (!aligned(x, dtype) || !aligned(lam, dtype) || !aligned(u, dtype) || !aligned(w, dtype) ||
+        !aligned(y, dtype))
         return GSPN_ERR_ALIGN;
     const int64_t n = B * C * H * W * elem_size(dtype);
     if (overlap(y, n, x, n) || overlap(y, n, lam, n) || overlap(y, n, u, n) ||
@@ -105,8 +109,8 @@ int gspn_prop2d_4dir(const void* x, const void* lam, const void* u, const void* 
     if (H * W > gspn::prop2d_max_plane(dtype, H, W)) return GSPN_ERR_SHAPE;
     if (!valid_eps(eps)) return GSPN_ERR_VALUE;
     if (!x || !lam || !u || !w_raw4 || !y) return GSPN_ERR_NULL;
-    if (!aligned16(x) || !aligned16(lam) || !aligned16(u) || !aligned16(w_raw4) ||
-        !aligned16(y))
+    if (!aligned(x, dtype) || !aligned(lam, dtype) || !aligned(u, dtype) ||
+        !aligned(w_raw4, dtype) || !aligned(y, dtype))
         return GSPN_ERR_ALIGN;
     const int64_t n = B * C * H * W * elem_size(dtype);
     if (overlap(y, n, x, n) || overlap(y, n, lam, n) || overlap(y, n, u, n) ||

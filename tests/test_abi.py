@@ -129,11 +129,15 @@ def test_null_pointers(L):
 
 
 def test_misaligned(L):
-    bad = ctypes.c_void_p(A + 8)
+    bad = ctypes.c_void_p(A + 2)           # fp32 needs 4-byte alignment
     assert prop(L, x=bad) == ALIGN
-    assert prop(L, y=ctypes.c_void_p(A + 5 * STEP + 4)) == ALIGN
+    assert prop(L, y=ctypes.c_void_p(A + 5 * STEP + 1)) == ALIGN
     assert scan(L, x=bad) == ALIGN
     assert norm(L, src=bad) == ALIGN
+    odd = ctypes.c_void_p(A + 1)           # bf16 needs 2-byte alignment
+    assert prop(L, x=odd, dt=1) == ALIGN
+    # 8-byte offsets are fine for both types: rejected later by the alias check
+    assert prop(L, x=ctypes.c_void_p(A + 5 * STEP + 8), dt=1) == ALIAS
 
 
 def test_aliasing(L):

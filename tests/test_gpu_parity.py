@@ -2,7 +2,7 @@
 
 All calls go through the C ABI (spatial_line_scan_amd.gspn).  Inputs are the
 seeded N(0, 1) draws of spatial_line_scan_amd.inputs, rounded to the storage
-type; the oracle sees exactly the same values.  Tolerances: tests/tolerance.py.
+type; the oracle sees exactly the same values.  Tolerances: oracle/tolerance.py.
 """
 import sys
 
@@ -13,7 +13,7 @@ import torch
 import oracle
 from spatial_line_scan_amd import gspn, inputs
 from spatial_line_scan_amd.workloads import WORKLOADS
-from tolerance import RTOL, assert_close
+from oracle.tolerance import RTOL, assert_close
 
 pytestmark = pytest.mark.gpu
 
