@@ -32,7 +32,8 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "4-dir GSPN propagation GB/s & ms (B=32,C_c=64,74×74) + % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prop2d_latent1k_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "spatial_line_scan_amd", "csrc", f)
-                  for f in ("gspn_kernels.hip", "gspn_host.cpp", "gspn_internal.h")]
+                  for f in ("gspn_kernels.hip", "gspn_prop2d_pair.hip", "gspn_host.cpp",
+                            "gspn_internal.h", "gspn_device.h")]
 
 
 def kernel_source_hash() -> str:

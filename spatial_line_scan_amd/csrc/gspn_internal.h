@@ -24,6 +24,13 @@ hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const vo
                          float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                          hipStream_t stream);
 
+// Fast path of gspn_prop2d_4dir: two wavefronts per plane (gspn_prop2d_pair.hip).
+bool prop2d_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
+                          const void* lam, const void* u, const void* w4, const void* y);
+hipError_t launch_prop2d_pair(const void* x, const void* lam, const void* u, const void* w4,
+                              float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
+                              hipStream_t stream);
+
 // Largest plane (H * W pixels) gspn_prop2d_4dir accepts for an element type.
 int64_t prop2d_max_plane(int dtype, int64_t H, int64_t W);
 
