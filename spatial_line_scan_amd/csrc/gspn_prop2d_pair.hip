@@ -189,33 +189,34 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
             }
             lo += dlo;
         };
-        // Column-scan chunks: columns [s0, s0 + D) forward, [W - D - s0, W - s0)
-        // backward, for each of the lane's K rows; double-buffered per block.
+        // Column-scan chunks: the D columns a block of steps visits, for each
+        // of the lane's K rows, one dword per load.  Dword w holds the
+        // columns of steps EPD w .. EPD w + EPD - 1 in visiting order: forward
+        // scans read ascending addresses, backward scans descending ones, so
+        // both index a step's element by the same static position.  The last
+        // chunk of a backward scan reaches left of column 0; those dwords
+        // lie below the row (first row of the tensor: below its start, where
+        // the offset wraps and the load reads 0) and are never used.
+        constexpr int EPD = 4 / ES;            // elements per dword
         constexpr int KC = kRows ? 1 : K;     // chunk rows (unused by the row scans)
         uint32_t xc0[KC][CW], lc0[KC][CW], xc1[KC][CW], lc1[KC][CW];
+        const int cstep = fwd ? 4 : -4;
         auto load_chunk = [&](int s0, uint32_t (&cx)[KC][CW], uint32_t (&cl)[KC][CW]) {
-            const int cstart = fwd ? s0 : W - D - s0;
-    #pragma unroll
-            for (int j = 0; j < KC; ++j) {
-                const uint32_t off = xl_col_b[j] + static_cast<uint32_t>(cstart * ES);
-                if (cstart >= 0) {
-                    load_words<CW>(xs, off, cx[j]);
-                    load_words<CW>(ls, off, cl[j]);
-                } else {
-                    // The last chunk of a backward scan starts left of column 0.
-                    // Dwords left of the row get an offset past the end of the
-                    // buffer (read as 0) so that no load also covering in-row
-                    // dwords can be formed for the first row of the tensor.
+            const int cfirst = fwd ? s0 : W - EPD - s0;   // column of dword 0
 #pragma unroll
-                    for (int w = 0; w < CW; ++w) {
-                        const bool in_row = cstart + w * (4 / ES) >= 0;
-                        const uint32_t o = in_row ? off + 4 * w : 0xffffffffu;
-                        cx[j][w] = __builtin_amdgcn_raw_buffer_load_b32(xs, o, 0, 0);
-                        cl[j][w] = __builtin_amdgcn_raw_buffer_load_b32(ls, o, 0, 0);
-                    }
+            for (int j = 0; j < KC; ++j) {
+                const uint32_t off = xl_col_b[j] + static_cast<uint32_t>(cfirst * ES);
+#pragma unroll
+                for (int w = 0; w < CW; ++w) {
+                    const uint32_t o = off + static_cast<uint32_t>(cstep * w);
+                    cx[j][w] = __builtin_amdgcn_raw_buffer_load_b32(xs, o, 0, 0);
+                    cl[j][w] = __builtin_amdgcn_raw_buffer_load_b32(ls, o, 0, 0);
                 }
             }
         };
+        // bf16 half of a chunk dword visited at even / odd steps
+        const uint32_t csel_even = fwd ? 0x01000c0cu : 0x03020c0cu;
+        const uint32_t csel_odd = fwd ? 0x03020c0cu : 0x01000c0cu;
 
     #pragma unroll
         for (int d = 0; d < D; ++d) load_line(d);
@@ -257,14 +258,13 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
                         xv = window_elem<T, K, NW>(xbuf[d], j, sel_even, sel_odd);
                         lv = window_elem<T, K, NW>(lbuf[d], j, sel_even, sel_odd);
                     } else {
-                        const int e = fwd ? d : D - 1 - d;            // column inside the chunk
                         if constexpr (kBf16) {
-                            const uint32_t xw = cx[j][e >> 1], lw = cl[j][e >> 1];
-                            xv = __uint_as_float((e & 1) ? (xw & 0xffff0000u) : (xw << 16));
-                            lv = __uint_as_float((e & 1) ? (lw & 0xffff0000u) : (lw << 16));
+                            const uint32_t sel = (d & 1) ? csel_odd : csel_even;
+                            xv = __uint_as_float(__builtin_amdgcn_perm(cx[j][d >> 1], cx[j][d >> 1], sel));
+                            lv = __uint_as_float(__builtin_amdgcn_perm(cl[j][d >> 1], cl[j][d >> 1], sel));
                         } else {
-                            xv = __uint_as_float(cx[j][e]);
-                            lv = __uint_as_float(cl[j][e]);
+                            xv = __uint_as_float(cx[j][d]);
+                            lv = __uint_as_float(cl[j][d]);
                         }
                     }
                     b[j] = lv * xv;
