@@ -15,20 +15,25 @@
 // wave-wide DPP shift in each direction (across the boundary between the two
 // halves the shifted value meets a dropped tap of weight exactly 0).
 //
-// Sums.  LDS holds two fp32 planes: R (row-major) receives h_TD + h_BU and
-// C (column-major) receives h_LR + h_RL; each plane is written by one
-// wavefront only, and each of its lines is visited twice (once per
-// direction): the first visit writes, the second reads (issued one step
-// ahead), adds and writes.  Every pixel's sum therefore has a fixed order.
-// After both scans y = u * (R + C).
+// Sums.  LDS holds two fp32 planes, zeroed first: R (row-major) receives
+// h_TD + h_BU and C (column-major) receives h_LR + h_RL.  Each plane is
+// written by one wavefront only.  Every step adds h to the value of its line
+// that was read right after the previous step's writes, and writes it back;
+// the in-order LDS makes the other half's earlier writes visible to that
+// read, so a pixel's two terms are added in a fixed order and the step body
+// has no branches.  Padding lines before and after each plane keep the
+// look-ahead reads in bounds; slots past the end of a line use a dummy word
+// of their lane.  When a scan has an odd number of lines both halves reach
+// the middle line in the same step: the forward half writes first, then the
+// backward half adds.  After both scans y = u * (R + C).
 //
 // Streams.  Taps are line-major for every direction, so each half reads its
 // line's taps contiguously; x and lambda rows are contiguous for the row
-// scans; the column scans read x and lambda in chunks of D columns of their
-// K rows, which stay resident in L2 while the plane is being scanned.  All
-// streams are prefetched D steps ahead with buffer loads, which return 0
-// outside the tensor (offsets below its start wrap to large values and read
-// as 0 too).
+// scans; the column scans read x and lambda in chunks of D columns (16 bytes
+// or more) of each of their K rows, loaded a block ahead, which stay resident
+// in L2 while the plane is being scanned.  All streams are prefetched D steps
+// ahead with buffer loads, which return 0 for every dword outside the tensor
+// (offsets below its start wrap to large values and read as 0 too).
 //
 // Normalisation: s_k = 1 / (2^(-z_k log2 e) + c_k) with c_k = 1 for in-line
 // taps and +inf for dropped ones (s_k exactly 0), r = 1 / max(s_0 + s_1 + s_2,
@@ -53,24 +58,26 @@ __device__ __forceinline__ float from_next(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x130, 0xf, 0xf, true));
 }
 
+// NW (1..4) consecutive dwords as one value, so that a prefetched window
+// stays one register tuple from its load to its use.
+template <int NW> struct Words { using type = uint32_t __attribute__((ext_vector_type(NW))); };
+template <> struct Words<1> { using type = uint32_t; };
+template <int NW> using words_t = typename Words<NW>::type;
+
 // NW consecutive dwords at byte offset `off` of a buffer.
 template <int NW>
-__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* dst) {
-    int w = 0;
-#pragma unroll
-    for (; w + 4 <= NW; w += 4) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * w, 0, 0);
-        dst[w] = v[0]; dst[w + 1] = v[1]; dst[w + 2] = v[2]; dst[w + 3] = v[3];
-    }
-    if constexpr (NW % 4 == 3) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4 * w, 0, 0);
-        dst[w] = v[0]; dst[w + 1] = v[1]; dst[w + 2] = v[2];
-    } else if constexpr (NW % 4 == 2) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * w, 0, 0);
-        dst[w] = v[0]; dst[w + 1] = v[1];
-    } else if constexpr (NW % 4 == 1) {
-        dst[w] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * w, 0, 0);
-    }
+__device__ __forceinline__ words_t<NW> load_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    static_assert(NW >= 1 && NW <= 4, "one load per window");
+    if constexpr (NW == 1) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    else if constexpr (NW == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    else if constexpr (NW == 3) return __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+template <int NW>
+__device__ __forceinline__ uint32_t word(const words_t<NW>& w, int i) {
+    if constexpr (NW == 1) return w;
+    else return w[i];
 }
 
 // Dwords covering K consecutive elements starting at an element of parity
@@ -82,20 +89,38 @@ constexpr int window_words() {
 
 // Element j of a lane's window as fp32.
 template <typename T, int K, int NW>
-__device__ __forceinline__ float window_elem(const uint32_t (&w)[NW], int j, uint32_t sel_even,
+__device__ __forceinline__ float window_elem(const words_t<NW>& w, int j, uint32_t sel_even,
                                              uint32_t sel_odd) {
     if constexpr (sizeof(T) == 4) {
-        return __uint_as_float(w[j]);
+        return __uint_as_float(word<NW>(w, j));
     } else {
         const int a = j >> 1;
-        const uint32_t lo = w[a];
-        const uint32_t hi = (a + 1 < NW) ? w[a + 1] : lo;
+        const uint32_t lo = word<NW>(w, a);
+        const uint32_t hi = (a + 1 < NW) ? word<NW>(w, a + 1) : lo;
         return __uint_as_float(__builtin_amdgcn_perm(hi, lo, (j & 1) ? sel_odd : sel_even));
     }
 }
 
-template <typename T, int K, int D>
-__global__ void __launch_bounds__(128)
+__device__ __forceinline__ float& lds_at(float* lds, uint32_t byte_off) {
+    return *reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + byte_off);
+}
+
+// LDS layout in floats: [pad W][R: H x W][pad W][pad H][C: W x H][pad H]
+// [dummy: 2 x 64], one dummy word per lane of each wavefront.
+struct PairLayout {
+    int r0, c0, dummy, words;
+    __host__ __device__ PairLayout(int H, int W) {
+        r0 = W;
+        c0 = W + H * W + W + H;
+        dummy = c0 + W * H + H;
+        words = dummy + 128;
+    }
+};
+
+// OddH / OddW: the row / column scans have an odd number of lines.
+template <typename T, int K, int D, bool OddH, bool OddW>
+// Two wavefronts per SIMD: at most 256 VGPRs, so that three planes share a CU.
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
 prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __restrict__ u,
                    const T* __restrict__ w4, int w4_bytes, int xl_bytes, float eps,
                    T* __restrict__ y, int planes, int H, int W) {
@@ -103,13 +128,15 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
     constexpr int ES = sizeof(T);
     constexpr int NW = window_words<T, K>();
     constexpr int CW = D * ES / 4;        // dwords of one D-column chunk
-    static_assert(D % 2 == 0 && CW >= 1, "chunks are whole dwords");
+    static_assert(CW % 4 == 0, "chunks are whole 16-byte pieces");
     extern __shared__ float lds[];
     const int HW = H * W;
-    float* const R = lds;                // [H][W]
-    float* const Cp = lds + HW;          // [W][H]
+    const PairLayout lay(H, W);
+    float* const R = lds + lay.r0;       // [H][W]
+    float* const Cp = lds + lay.c0;      // [W][H]
 
-    const int wv = threadIdx.x >> 6;     // 0: rows, 1: columns
+    // 0: rows, 1: columns (read from lane 0, so that branches on it are uniform)
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;          // 0: forward (TD, LR), 1: backward (BU, RL)
     const int q = lane & 31;
@@ -130,6 +157,13 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
     for (int k = 0; k < kUPer; ++k) {
         const int f = static_cast<int>(threadIdx.x) + 128 * k;
         ureg[k] = f < u_words ? u32[f] : 0u;
+    }
+
+    // ------------------------------- zero this wavefront's plane and its pads
+    {
+        const int first = rows ? 0 : lay.c0 - H;
+        const int count = rows ? HW + 2 * W : HW + 2 * H;
+        for (int f = lane; f < count; f += 64) lds[first + f] = 0.0f;
     }
 
     // ------------------------------------------------------- per-lane constants
@@ -173,219 +207,302 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
 
     // The scan of one wavefront; the row and column scans differ only in
     // where x and lambda come from and in which sum plane they fill.
-    auto scan = [&](auto rows_tag) {
+    auto scan = [&](auto rows_tag, auto odd_tag) {
         constexpr bool kRows = decltype(rows_tag)::value;
+        constexpr bool kOdd = decltype(odd_tag)::value;   // odd number of lines
         // Tap and x/lambda streams for the line of step s (D steps ahead).
         uint32_t lo = fwd ? 0u : static_cast<uint32_t>(NL - 1) * line_b;
         const uint32_t dlo = fwd ? line_b : 0u - line_b;
-        uint32_t tbuf[D][3][NW];
-        uint32_t xbuf[kRows ? D : 1][NW], lbuf[kRows ? D : 1][NW];
+        words_t<NW> tbuf[D][3];
+        words_t<NW> xbuf[kRows ? D : 1], lbuf[kRows ? D : 1];
         auto load_line = [&](int d) {
-    #pragma unroll
-            for (int k = 0; k < 3; ++k) load_words<NW>(taps, tap_b[k] + lo, tbuf[d][k]);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps, tap_b[k] + lo);
             if constexpr (kRows) {
-                load_words<NW>(xs, xl_row_b + lo, xbuf[d]);
-                load_words<NW>(ls, xl_row_b + lo, lbuf[d]);
+                xbuf[d] = load_words<NW>(xs, xl_row_b + lo);
+                lbuf[d] = load_words<NW>(ls, xl_row_b + lo);
             }
             lo += dlo;
         };
-        // Column-scan chunks: the D columns a block of steps visits, for each
-        // of the lane's K rows, one dword per load.  Dword w holds the
-        // columns of steps EPD w .. EPD w + EPD - 1 in visiting order: forward
-        // scans read ascending addresses, backward scans descending ones, so
-        // both index a step's element by the same static position.  The last
-        // chunk of a backward scan reaches left of column 0; those dwords
-        // lie below the row (first row of the tensor: below its start, where
-        // the offset wraps and the load reads 0) and are never used.
-        constexpr int EPD = 4 / ES;            // elements per dword
-        constexpr int KC = kRows ? 1 : K;     // chunk rows (unused by the row scans)
-        uint32_t xc0[KC][CW], lc0[KC][CW], xc1[KC][CW], lc1[KC][CW];
-        const int cstep = fwd ? 4 : -4;
-        auto load_chunk = [&](int s0, uint32_t (&cx)[KC][CW], uint32_t (&cl)[KC][CW]) {
-            const int cfirst = fwd ? s0 : W - EPD - s0;   // column of dword 0
+        // Column scans: x and lambda of the lane's rows K q + j for the D
+        // columns of a block, as CW dwords in ascending address order (one
+        // 16-byte load per 4 dwords): forward lanes take a block's columns
+        // s0 .. s0+D-1, backward lanes W-D-s0 .. W-1-s0, and one byte permute
+        // of (forward word, backward word) decodes both.  Two chunk buffers
+        // alternate between blocks; a block's buffer is filled at the start
+        // of the previous block.  A backward chunk that would start left of
+        // column 0 (the partial last block) starts at column 0 instead; its
+        // words are moved into place before that block.
+        constexpr int KC = kRows ? 1 : K;
+        constexpr int CQ = CW / 4;             // 16-byte pieces per chunk
+        using chunk_t = words_t<4>[KC][CQ];
+        chunk_t xcA, lcA, xcB, lcB;
+        uint32_t xl_col_b[KC];
+#pragma unroll
+        for (int j = 0; j < KC; ++j)
+            xl_col_b[j] = static_cast<uint32_t>(pix0 + static_cast<size_t>(K * q + j) * W) * ES;
+        auto load_chunk = [&](int s0, chunk_t& cx, chunk_t& cl) {
+            int c0 = fwd ? s0 : W - D - s0;
+            c0 = c0 < 0 ? 0 : c0;
+            // an empty asm orders the load after the decodes of the previous
+            // block, which read the same registers
+            uint32_t cofs = static_cast<uint32_t>(c0 * ES);
+            asm volatile("" : "+v"(cofs));
 #pragma unroll
             for (int j = 0; j < KC; ++j) {
-                const uint32_t off = xl_col_b[j] + static_cast<uint32_t>(cfirst * ES);
+                const uint32_t o = xl_col_b[j] + cofs;
 #pragma unroll
-                for (int w = 0; w < CW; ++w) {
-                    const uint32_t o = off + static_cast<uint32_t>(cstep * w);
-                    cx[j][w] = __builtin_amdgcn_raw_buffer_load_b32(xs, o, 0, 0);
-                    cl[j][w] = __builtin_amdgcn_raw_buffer_load_b32(ls, o, 0, 0);
+                for (int i = 0; i < CQ; ++i) {
+                    cx[j][i] = load_words<4>(xs, o + 16 * i);
+                    cl[j][i] = load_words<4>(ls, o + 16 * i);
                 }
             }
         };
-        // bf16 half of a chunk dword visited at even / odd steps
-        const uint32_t csel_even = fwd ? 0x01000c0cu : 0x03020c0cu;
-        const uint32_t csel_odd = fwd ? 0x03020c0cu : 0x01000c0cu;
+        // chunk word holding the column of step d of a block
+        auto fwd_word = [](int d) { return (d * ES) / 4; };
+        auto bwd_word = [](int d) { return ((D - 1 - d) * ES) / 4; };
+        // byte selectors: forward word from the first operand, backward word
+        // (other half for bf16) from the second
+        const uint32_t csel_even = kBf16 ? (fwd ? 0x05040c0cu : 0x03020c0cu) : (fwd ? 0x07060504u : 0x03020100u);
+        const uint32_t csel_odd = kBf16 ? (fwd ? 0x07060c0cu : 0x01000c0cu) : csel_even;
 
-    #pragma unroll
-        for (int d = 0; d < D; ++d) load_line(d);
-        if constexpr (!kRows) load_chunk(0, xc0, lc0);
+        // Prologue: slots in step order, as the loop refills them (the wait
+        // counts inside the loop are derived from this order as well).
+        if constexpr (!kRows) load_chunk(0, xcA, lcA);
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_line(d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 
-        // This wave's sum plane, line-major in its own orientation.
-        float* const P = kRows ? R : Cp;
+        // LDS byte offset of each slot in this wavefront's sum plane (line-major
+        // in its own orientation) and its change per step; a slot past the
+        // line end stays on its lane's dummy word.
+        const int base = kRows ? lay.r0 : lay.c0;
         const int i0 = fwd ? 0 : NL - 1;
-        float* pl = P + i0 * L + K * q;                       // slot 0 of the current line
-        const int dpl = fwd ? L : -L;
-        float prev[K];                                        // second-visit reads, one step ahead
-
-        float h[K];
-    #pragma unroll
+        uint32_t addr[K];
+        uint32_t dstep[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            addr[j] = 4u * static_cast<uint32_t>(valid[j] ? base + i0 * L + K * q + j
+                                                          : lay.dummy + 64 * wv + lane);
+            dstep[j] = valid[j] ? (fwd ? 4u * L : 0u - 4u * L) : 0u;
+        }
+        float h[K], acc[K];
+#pragma unroll
         for (int j = 0; j < K; ++j) {
             h[j] = 0.0f;
-            prev[j] = 0.0f;
+            acc[j] = lds_at(lds, addr[j]);      // the zeroes stored above
         }
+        // Odd scans: both halves reach the middle line in step mid; there the
+        // backward half's slots are moved by mid_off to the padding line after
+        // the plane, which starts zeroed.
+        const int mid = (NL - 1) / 2;
+        uint32_t mid_off[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            mid_off[j] = (valid[j] && !fwd) ? 4u * static_cast<uint32_t>((NL - mid) * L) : 0u;
 
-        // One block of D steps; cx/cl hold this block's column chunks and the
-        // next block's are loaded into nx/nl.
-        auto run_block = [&](int s0, const uint32_t (&cx)[KC][CW], const uint32_t (&cl)[KC][CW],
-                             uint32_t (&nx)[KC][CW], uint32_t (&nl)[KC][CW]) {
-            if constexpr (!kRows) {
-                if (s0 + D < NL) load_chunk(s0 + D, nx, nl);
+        // Step s with its streams in slot d: decode them, refill slot d for
+        // step s + D, advance h and add it into the sum plane.
+        auto step = [&](int s, int d, chunk_t& cx, chunk_t& cl) {
+            // The slot's words pass through an empty asm here, so that no
+            // decode of them is scheduled before this step (it would wait for
+            // the most recent loads).
+            asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
+            if constexpr (kRows) {
+                asm volatile("" : "+v"(xbuf[d]), "+v"(lbuf[d]));
+            } else {
+#pragma unroll
+                for (int j = 0; j < KC; ++j) {
+                    asm volatile("" : "+v"(cx[j][fwd_word(d) / 4]), "+v"(cl[j][fwd_word(d) / 4]));
+                    if (bwd_word(d) / 4 != fwd_word(d) / 4)
+                        asm volatile("" : "+v"(cx[j][bwd_word(d) / 4]), "+v"(cl[j][bwd_word(d) / 4]));
+                }
             }
-    #pragma unroll
-            for (int d = 0; d < D; ++d) {
-                const int s = s0 + d;
-                if (s >= NL) break;
-                float z[3][K], b[K];
-    #pragma unroll
-                for (int j = 0; j < K; ++j) {
-    #pragma unroll
-                    for (int k = 0; k < 3; ++k)
-                        z[k][j] = window_elem<T, K, NW>(tbuf[d][k], j, sel_even, sel_odd);
-                    float xv, lv;
-                    if constexpr (kRows) {
-                        xv = window_elem<T, K, NW>(xbuf[d], j, sel_even, sel_odd);
-                        lv = window_elem<T, K, NW>(lbuf[d], j, sel_even, sel_odd);
-                    } else {
-                        if constexpr (kBf16) {
-                            const uint32_t sel = (d & 1) ? csel_odd : csel_even;
-                            xv = __uint_as_float(__builtin_amdgcn_perm(cx[j][d >> 1], cx[j][d >> 1], sel));
-                            lv = __uint_as_float(__builtin_amdgcn_perm(cl[j][d >> 1], cl[j][d >> 1], sel));
-                        } else {
-                            xv = __uint_as_float(cx[j][d]);
-                            lv = __uint_as_float(cl[j][d]);
-                        }
-                    }
-                    b[j] = lv * xv;
-                }
-                load_line(d);
-
-                const float hl0 = from_prev(h[K - 1]);
-                const float hrK = from_next(h[0]);
-                float hn[K];
-    #pragma unroll
-                for (int j = 0; j < K; ++j) {
-                    const float hl = j > 0 ? h[j - 1] : hl0;
-                    const float hr = j < K - 1 ? h[j + 1] : hrK;
-                    const float s0v = __builtin_amdgcn_rcpf(
-                        __builtin_amdgcn_exp2f(z[0][j] * kNegLog2e) + c0[j]);
-                    const float s1v = __builtin_amdgcn_rcpf(
-                        __builtin_amdgcn_exp2f(z[1][j] * kNegLog2e) + c1[j]);
-                    const float s2v = __builtin_amdgcn_rcpf(
-                        __builtin_amdgcn_exp2f(z[2][j] * kNegLog2e) + c2[j]);
-                    const float r = __builtin_amdgcn_rcpf(fmaxf((s0v + s1v) + s2v, eps));
-                    float m = s1v * h[j];
-                    m = fmaf(s0v, hl, m);
-                    m = fmaf(s2v, hr, m);
-                    hn[j] = fmaf(m, r, b[j]);
-                }
-    #pragma unroll
-                for (int j = 0; j < K; ++j) h[j] = hn[j];
-
-                // Visits of this line: first (2s < NL-1) write, second (2s > NL-1)
-                // add to the value read one step ahead; the middle line of an odd
-                // scan is visited by both halves in this step: forward writes,
-                // then backward reads it back and adds.
-                const int twice = 2 * s;
-                if (twice < NL - 1) {
-    #pragma unroll
-                    for (int j = 0; j < K; ++j)
-                        if (valid[j]) pl[j] = h[j];
-                } else if (twice > NL - 1) {
-    #pragma unroll
-                    for (int j = 0; j < K; ++j)
-                        if (valid[j]) pl[j] = prev[j] + h[j];
+            // Everything that does not depend on h: normalised taps and lambda x.
+            float s0v[K], s1v[K], s2v[K], r[K], b[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const float z0 = window_elem<T, K, NW>(tbuf[d][0], j, sel_even, sel_odd);
+                const float z1 = window_elem<T, K, NW>(tbuf[d][1], j, sel_even, sel_odd);
+                const float z2 = window_elem<T, K, NW>(tbuf[d][2], j, sel_even, sel_odd);
+                float xv, lv;
+                if constexpr (kRows) {
+                    xv = window_elem<T, K, NW>(xbuf[d], j, sel_even, sel_odd);
+                    lv = window_elem<T, K, NW>(lbuf[d], j, sel_even, sel_odd);
                 } else {
-                    if (fwd) {
-    #pragma unroll
-                        for (int j = 0; j < K; ++j)
-                            if (valid[j]) pl[j] = h[j];
-                    }
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                    if (!fwd) {
-    #pragma unroll
-                        for (int j = 0; j < K; ++j)
-                            if (valid[j]) pl[j] = pl[j] + h[j];
-                    }
+                    const int fw = fwd_word(d), bw = bwd_word(d);
+                    const uint32_t sel = (d & 1) ? csel_odd : csel_even;
+                    xv = __uint_as_float(__builtin_amdgcn_perm(cx[j][fw / 4][fw % 4], cx[j][bw / 4][bw % 4], sel));
+                    lv = __uint_as_float(__builtin_amdgcn_perm(cl[j][fw / 4][fw % 4], cl[j][bw / 4][bw % 4], sel));
                 }
-                pl += dpl;
-                if (2 * (s + 1) > NL - 1 && s + 1 < NL) {
-    #pragma unroll
-                    for (int j = 0; j < K; ++j) prev[j] = valid[j] ? pl[j] : 0.0f;
-                }
+                b[j] = lv * xv;
+                s0v[j] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z0 * kNegLog2e) + c0[j]);
+                s1v[j] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z1 * kNegLog2e) + c1[j]);
+                s2v[j] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z2 * kNegLog2e) + c2[j]);
+                r[j] = __builtin_amdgcn_rcpf(fmaxf((s0v[j] + s1v[j]) + s2v[j], eps));
+            }
+            // Slot d is refilled only after it has been decoded: the refill
+            // offsets pass through an empty asm that takes the decoded values,
+            // so no load can move above the decode (two live copies of a slot
+            // would need register copies that wait for the load).
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                asm volatile("" : "+v"(lo)
+                             : "v"(s0v[j]), "v"(s1v[j]), "v"(s2v[j]), "v"(r[j]), "v"(b[j]));
+            load_line(d);
+
+            const float hl0 = from_prev(h[K - 1]);
+            const float hrK = from_next(h[0]);
+            float hn[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const float hl = j > 0 ? h[j - 1] : hl0;
+                const float hr = j < K - 1 ? h[j + 1] : hrK;
+                float m = s1v[j] * h[j];
+                m = fmaf(s0v[j], hl, m);
+                m = fmaf(s2v[j], hr, m);
+                hn[j] = fmaf(m, r[j], b[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) h[j] = hn[j];
+
+            // On the middle line of an odd scan the backward half writes to
+            // the padding line after the plane instead (added in afterwards).
+            const bool at_mid = kOdd && s == mid;
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                lds_at(lds, at_mid ? addr[j] + mid_off[j] : addr[j]) = acc[j] + h[j];
+            // the next line, read after this step's writes
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                addr[j] += dstep[j];
+                acc[j] = lds_at(lds, addr[j]);
             }
         };
-        for (int s0 = 0; s0 < NL; s0 += 2 * D) {
-            run_block(s0, xc0, lc0, xc1, lc1);
-            if (s0 + D < NL) run_block(s0 + D, xc1, lc1, xc0, lc0);
+
+        // Whole blocks of D steps, two per iteration so that the chunk buffers
+        // alternate; the streams are refilled unconditionally (past the end
+        // they read unused data or 0), so that no branch drains the prefetch
+        // queue.  Then the partial last block.
+        auto block = [&](int s0, chunk_t& cx, chunk_t& cl, chunk_t& nx, chunk_t& nl) {
+            if constexpr (!kRows) load_chunk(s0 + D, nx, nl);
+#pragma unroll
+            for (int d = 0; d < D; ++d) step(s0 + d, d, cx, cl);
+        };
+        int s0 = 0;
+        for (; s0 + 2 * D <= NL; s0 += 2 * D) {
+            block(s0, xcA, lcA, xcB, lcB);
+            block(s0 + D, xcB, lcB, xcA, lcA);
+        }
+        if (s0 + D <= NL) {
+            block(s0, xcA, lcA, xcB, lcB);
+            s0 += D;
+            if constexpr (!kRows) {
+#pragma unroll
+                for (int j = 0; j < KC; ++j)
+#pragma unroll
+                    for (int i = 0; i < CQ; ++i) {
+                        xcA[j][i] = xcB[j][i];
+                        lcA[j][i] = lcB[j][i];
+                    }
+            }
+        }
+        if (s0 < NL) {
+            if constexpr (!kRows) {
+                // The backward chunk of this block starts at column 0 rather
+                // than D - T columns to its left (T steps remain): move its words
+                // up by that many columns.
+                const int sh = ((D - (NL - s0)) * ES) / 4;
+                for (int i = 0; i < sh; ++i) {
+#pragma unroll
+                    for (int j = 0; j < KC; ++j)
+#pragma unroll
+                        for (int w = CW - 1; w >= 1; --w) {
+                            const uint32_t xp = xcA[j][(w - 1) / 4][(w - 1) % 4];
+                            const uint32_t lp = lcA[j][(w - 1) / 4][(w - 1) % 4];
+                            if (!fwd) {
+                                xcA[j][w / 4][w % 4] = xp;
+                                lcA[j][w / 4][w % 4] = lp;
+                            }
+                        }
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                if (s0 + d < NL) step(s0 + d, d, xcA, lcA);
+        }
+        if constexpr (kOdd) {
+            // the middle line receives the backward half's term last
+            if (!fwd) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    const uint32_t a = 4u * static_cast<uint32_t>(base + mid * L + K * q + j);
+                    if (valid[j]) lds_at(lds, a) = lds_at(lds, a) + lds_at(lds, a + mid_off[j]);
+                }
+            }
         }
     };
-    if (rows) scan(std::true_type{});
-    else scan(std::false_type{});
+    if (rows) scan(std::true_type{}, std::bool_constant<OddH>{});
+    else scan(std::false_type{}, std::bool_constant<OddW>{});
     __syncthreads();
 
     // ------------------------------------------------------- y = u * (R + C)
+    // Thread slot f walks the plane in strides of 128 words; its pixel
+    // position advances by whole rows and a remainder instead of a division.
     if constexpr (kBf16) {
         uint32_t* y32 = reinterpret_cast<uint32_t*>(y + pix0);
-#pragma unroll
-        for (int k = 0; k < kUPer; ++k) {
-            const int f = static_cast<int>(threadIdx.x) + 128 * k;
-            if (f < u_words) {
-                const int p0 = 2 * f;                         // even pixel, same row as p0 + 1
-                const int r0 = p0 / W, c0i = p0 - r0 * W;
-                const float a0 = R[p0] + Cp[c0i * H + r0];
-                const float a1 = R[p0 + 1] + Cp[(c0i + 1) * H + r0];
-                const uint32_t uv = ureg[k];
-                const uint32_t lo16 = bf16_rne(__uint_as_float(uv << 16) * a0);
-                const uint32_t hi16 = bf16_rne(__uint_as_float(uv & 0xffff0000u) * a1);
-                y32[f] = lo16 | (hi16 << 16);
-            }
-        }
-        for (int f = static_cast<int>(threadIdx.x) + 128 * kUPer; f < u_words; f += 128) {
-            const int p0 = 2 * f;
-            const int r0 = p0 / W, c0i = p0 - r0 * W;
-            const float a0 = R[p0] + Cp[c0i * H + r0];
-            const float a1 = R[p0 + 1] + Cp[(c0i + 1) * H + r0];
-            const uint32_t uv = u32[f];
+        const int dq = 256 / W, dr = 256 - dq * W;   // 128 pixel pairs
+        int f = threadIdx.x;
+        int r0 = (2 * f) / W, c0i = 2 * f - r0 * W;
+        auto emit = [&](uint32_t uv) {
+            // W is even: the pair (r0, c0i), (r0, c0i + 1) lies in one row
+            const float a0 = R[r0 * W + c0i] + Cp[c0i * H + r0];
+            const float a1 = R[r0 * W + c0i + 1] + Cp[(c0i + 1) * H + r0];
             y32[f] = bf16_rne(__uint_as_float(uv << 16) * a0) |
                      (static_cast<uint32_t>(bf16_rne(__uint_as_float(uv & 0xffff0000u) * a1)) << 16);
-        }
-    } else {
-        float* yp = reinterpret_cast<float*>(y + pix0);
+        };
+        auto advance = [&]() {
+            f += 128;
+            c0i += dr;
+            r0 += dq;
+            if (c0i >= W) { c0i -= W; ++r0; }
+        };
 #pragma unroll
         for (int k = 0; k < kUPer; ++k) {
-            const int f = static_cast<int>(threadIdx.x) + 128 * k;
-            if (f < u_words) {
-                const int r0 = f / W, c0i = f - r0 * W;
-                yp[f] = __uint_as_float(ureg[k]) * (R[f] + Cp[c0i * H + r0]);
-            }
+            if (f < u_words) emit(ureg[k]);
+            advance();
         }
-        for (int f = static_cast<int>(threadIdx.x) + 128 * kUPer; f < u_words; f += 128) {
-            const int r0 = f / W, c0i = f - r0 * W;
-            yp[f] = __uint_as_float(u32[f]) * (R[f] + Cp[c0i * H + r0]);
+        for (; f < u_words; advance()) emit(u32[f]);
+    } else {
+        float* yp = reinterpret_cast<float*>(y + pix0);
+        const int dq = 128 / W, dr = 128 - dq * W;
+        int f = threadIdx.x;
+        int r0 = f / W, c0i = f - r0 * W;
+        auto advance = [&]() {
+            f += 128;
+            c0i += dr;
+            r0 += dq;
+            if (c0i >= W) { c0i -= W; ++r0; }
+        };
+#pragma unroll
+        for (int k = 0; k < kUPer; ++k) {
+            if (f < u_words) yp[f] = __uint_as_float(ureg[k]) * (R[f] + Cp[c0i * H + r0]);
+            advance();
         }
+        for (; f < u_words; advance()) yp[f] = __uint_as_float(u32[f]) * (R[f] + Cp[c0i * H + r0]);
     }
 }
 
-template <typename T, int K>
+template <typename T, int K, bool OddH, bool OddW>
 hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, float eps,
                     void* y, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
-    constexpr int D = 8;
-    const size_t lds = static_cast<size_t>(2 * H * W) * sizeof(float);
-    auto kern = prop2d_pair_kernel<T, K, D>;
+    // prefetch depth: D steps of every stream in registers
+    constexpr int D = (sizeof(T) == 4 && K == 3) ? 4 : 8;
+    const size_t lds =
+        static_cast<size_t>(PairLayout(static_cast<int>(H), static_cast<int>(W)).words) * sizeof(float);
+    auto kern = prop2d_pair_kernel<T, K, D, OddH, OddW>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -401,13 +518,27 @@ hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w
     return hipGetLastError();
 }
 
+template <typename T, int K>
+hipError_t launch_parity(const void* x, const void* lam, const void* u, const void* w4, float eps,
+                         void* y, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
+    if constexpr (sizeof(T) == 2) {  // bf16 shapes are even (eligibility)
+        return launch_k<T, K, false, false>(x, lam, u, w4, eps, y, planes, H, W, stream);
+    } else {
+        const bool oh = H & 1, ow = W & 1;
+        if (!oh && !ow) return launch_k<T, K, false, false>(x, lam, u, w4, eps, y, planes, H, W, stream);
+        if (oh && ow) return launch_k<T, K, true, true>(x, lam, u, w4, eps, y, planes, H, W, stream);
+        if (oh) return launch_k<T, K, true, false>(x, lam, u, w4, eps, y, planes, H, W, stream);
+        return launch_k<T, K, false, true>(x, lam, u, w4, eps, y, planes, H, W, stream);
+    }
+}
+
 template <typename T>
 hipError_t launch_t(const void* x, const void* lam, const void* u, const void* w4, float eps,
                     void* y, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
     const int64_t Lmax = H > W ? H : W;
-    if (Lmax <= 32) return launch_k<T, 1>(x, lam, u, w4, eps, y, planes, H, W, stream);
-    if (Lmax <= 64) return launch_k<T, 2>(x, lam, u, w4, eps, y, planes, H, W, stream);
-    return launch_k<T, 3>(x, lam, u, w4, eps, y, planes, H, W, stream);
+    if (Lmax <= 32) return launch_parity<T, 1>(x, lam, u, w4, eps, y, planes, H, W, stream);
+    if (Lmax <= 64) return launch_parity<T, 2>(x, lam, u, w4, eps, y, planes, H, W, stream);
+    return launch_parity<T, 3>(x, lam, u, w4, eps, y, planes, H, W, stream);
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -417,7 +548,9 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool prop2d_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
                           const void* lam, const void* u, const void* w4, const void* y) {
     if (H > 96 || W > 96) return false;
-    if (2 * H * W * 4 > kLdsBytes) return false;
+    if (4 * static_cast<int64_t>(PairLayout(static_cast<int>(H), static_cast<int>(W)).words) >
+        kLdsBytes)
+        return false;
     // all stream offsets are 32-bit byte offsets into one buffer resource
     const int64_t es = dtype == 0 ? 4 : 2;
     if (12 * planes * H * W * es > 0x7fffffff) return false;
