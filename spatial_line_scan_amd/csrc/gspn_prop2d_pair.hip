@@ -101,18 +101,29 @@ __device__ __forceinline__ float window_elem(const words_t<NW>& w, int j, uint32
     }
 }
 
+// Two floats to packed bf16 (low, high), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ float& lds_at(float* lds, uint32_t byte_off) {
     return *reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + byte_off);
 }
 
-// LDS layout in floats: [pad W][R: H x W][pad W][pad H][C: W x H][pad H]
-// [dummy: 2 x 64], one dummy word per lane of each wavefront.
+// LDS layout in floats: [pad W][R: H x W][pad W] [pad H][C: W x H][pad H]
+// [dummy: 2 x 64] (one dummy word per lane of each wavefront); the row and
+// column regions each start at a multiple of 4 floats.
 struct PairLayout {
-    int r0, c0, dummy, words;
+    int rows_end, r0, c0, cols_end, dummy, words;
     __host__ __device__ PairLayout(int H, int W) {
         r0 = W;
-        c0 = W + H * W + W + H;
-        dummy = c0 + W * H + H;
+        rows_end = (H * W + 2 * W + 3) & ~3;
+        c0 = rows_end + H;
+        cols_end = (rows_end + H * W + 2 * H + 3) & ~3;
+        dummy = cols_end;
         words = dummy + 128;
     }
 };
@@ -161,9 +172,10 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
 
     // ------------------------------- zero this wavefront's plane and its pads
     {
-        const int first = rows ? 0 : lay.c0 - H;
-        const int count = rows ? HW + 2 * W : HW + 2 * H;
-        for (int f = lane; f < count; f += 64) lds[first + f] = 0.0f;
+        const int first = rows ? 0 : lay.rows_end;
+        const int count = rows ? lay.rows_end : lay.cols_end - lay.rows_end;
+        float4* z4 = reinterpret_cast<float4*>(lds + first);
+        for (int f = lane; f < count / 4; f += 64) z4[f] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 
     // ------------------------------------------------------- per-lane constants
@@ -179,8 +191,13 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
         c2[j] = (valid[j] && p < L - 1) ? 1.0f : inf;
     }
 
-    const __amdgpu_buffer_rsrc_t taps =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4), 0, w4_bytes, kBufFlags);
+    // one resource per tap plane k, based k planes into the tap tensor, so
+    // that the three tap loads of a step share one offset register
+    __amdgpu_buffer_rsrc_t taps[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + static_cast<size_t>(k) * HW), 0,
+                                                    w4_bytes - k * HW * ES, kBufFlags);
     const __amdgpu_buffer_rsrc_t xs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(x), 0, xl_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t ls =
@@ -193,10 +210,8 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
     const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
     const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
     const uint32_t line_b = static_cast<uint32_t>(L) * ES;
-    uint32_t tap_b[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-        tap_b[k] = static_cast<uint32_t>((((g * planes + plane) * 3 + k) * HW)) * ES + win_b;
+    // offset of this lane's window in tap plane 0 of its direction
+    const uint32_t tap_b = static_cast<uint32_t>(((g * planes + plane) * 3) * HW) * ES + win_b;
     // Row scans: x and lambda of the current row, same window.
     const uint32_t xl_row_b = static_cast<uint32_t>(pix0) * ES + win_b;
     // Column scans: x and lambda of rows K q + j, D columns per chunk.
@@ -211,18 +226,21 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
         constexpr bool kRows = decltype(rows_tag)::value;
         constexpr bool kOdd = decltype(odd_tag)::value;   // odd number of lines
         // Tap and x/lambda streams for the line of step s (D steps ahead).
-        uint32_t lo = fwd ? 0u : static_cast<uint32_t>(NL - 1) * line_b;
+        const uint32_t lo0 = fwd ? 0u : static_cast<uint32_t>(NL - 1) * line_b;
         const uint32_t dlo = fwd ? line_b : 0u - line_b;
+        uint32_t lo = tap_b + lo0;                  // taps of the line loaded next
+        uint32_t xo = xl_row_b + lo0;               // x and lambda (row scans)
         words_t<NW> tbuf[D][3];
         words_t<NW> xbuf[kRows ? D : 1], lbuf[kRows ? D : 1];
         auto load_line = [&](int d) {
 #pragma unroll
-            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps, tap_b[k] + lo);
-            if constexpr (kRows) {
-                xbuf[d] = load_words<NW>(xs, xl_row_b + lo);
-                lbuf[d] = load_words<NW>(ls, xl_row_b + lo);
-            }
+            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
             lo += dlo;
+            if constexpr (kRows) {
+                xbuf[d] = load_words<NW>(xs, xo);
+                lbuf[d] = load_words<NW>(ls, xo);
+                xo += dlo;
+            }
         };
         // Column scans: x and lambda of the lane's rows K q + j for the D
         // columns of a block, as CW dwords in ascending address order (one
@@ -348,9 +366,14 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
             // so no load can move above the decode (two live copies of a slot
             // would need register copies that wait for the load).
 #pragma unroll
-            for (int j = 0; j < K; ++j)
-                asm volatile("" : "+v"(lo)
-                             : "v"(s0v[j]), "v"(s1v[j]), "v"(s2v[j]), "v"(r[j]), "v"(b[j]));
+            for (int j = 0; j < K; ++j) {
+                if constexpr (kRows)
+                    asm volatile("" : "+v"(lo), "+v"(xo)
+                                 : "v"(s0v[j]), "v"(s1v[j]), "v"(s2v[j]), "v"(r[j]), "v"(b[j]));
+                else
+                    asm volatile("" : "+v"(lo)
+                                 : "v"(s0v[j]), "v"(s1v[j]), "v"(s2v[j]), "v"(r[j]), "v"(b[j]));
+            }
             load_line(d);
 
             const float hl0 = from_prev(h[K - 1]);
@@ -458,10 +481,10 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
         int r0 = (2 * f) / W, c0i = 2 * f - r0 * W;
         auto emit = [&](uint32_t uv) {
             // W is even: the pair (r0, c0i), (r0, c0i + 1) lies in one row
-            const float a0 = R[r0 * W + c0i] + Cp[c0i * H + r0];
-            const float a1 = R[r0 * W + c0i + 1] + Cp[(c0i + 1) * H + r0];
-            y32[f] = bf16_rne(__uint_as_float(uv << 16) * a0) |
-                     (static_cast<uint32_t>(bf16_rne(__uint_as_float(uv & 0xffff0000u) * a1)) << 16);
+            const float2 rr = *reinterpret_cast<const float2*>(R + r0 * W + c0i);
+            const float a0 = rr.x + Cp[c0i * H + r0];
+            const float a1 = rr.y + Cp[(c0i + 1) * H + r0];
+            y32[f] = pack_bf16x2(__uint_as_float(uv << 16) * a0, __uint_as_float(uv & 0xffff0000u) * a1);
         };
         auto advance = [&]() {
             f += 128;
