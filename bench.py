@@ -134,6 +134,10 @@ def main():
                     help="total bytes of rotated input sets (defeats the 256 MB cache)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="run only the device copy used for calibration (--steps copies of "
+                         "256 Mi fp32 = 1 GiB read + 1 GiB written), e.g. under rocprofv3 --pmc "
+                         "to scale FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -151,6 +155,15 @@ def main():
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_only:
+        src = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_launches": args.steps, "bytes_read_per_launch": src.numel() * 4,
+                          "bytes_written_per_launch": dst.numel() * 4}), flush=True)
+        return
     print("bench: drawing %s inputs" % wl.name, file=sys.stderr, flush=True)
     base = inputs.problem_torch(wl.B, wl.C, wl.H, wl.W, 0, wl.dtype, dev)
     nsets = max(1, int(np.ceil(args.rotate_bytes / wl.algorithmic_bytes)))
