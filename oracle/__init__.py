@@ -14,6 +14,8 @@ Functions
 normalize(w_raw, NL, L, eps)              -> normalised taps (one direction)
 scan_dir(x, lam, u, w, dir, w_is_raw, eps) -> u * h for one direction
 prop2d(x, lam, u, w4, eps)                -> sum over the four directions
+prop2d_backward(x, lam, u, w4, gy, eps)   -> (gx, glam, gu, gw4), the gradient
+                                             of <gy, prop2d(x, lam, u, w4)>
 
 Layouts follow the C file's header: x, lam, u: [B][C][H][W]; the taps of one
 direction: [B][C][3][NL][L] indexed by (line, position) of that direction
@@ -62,6 +64,10 @@ def _load(path: str | None = None):
         lib.gspn_oracle_scan_dir.restype = ctypes.c_int
         lib.gspn_oracle_prop2d.argtypes = [dp, dp, dp, dp, ctypes.c_double, dp, L, L, L, L]
         lib.gspn_oracle_prop2d.restype = ctypes.c_int
+        if hasattr(lib, "gspn_oracle_prop2d_backward"):
+            lib.gspn_oracle_prop2d_backward.argtypes = [dp, dp, dp, dp, dp, ctypes.c_double,
+                                                        dp, dp, dp, dp, L, L, L, L]
+            lib.gspn_oracle_prop2d_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -128,3 +134,18 @@ def prop2d(x, lam, u, w4, eps: float = 1e-6) -> np.ndarray:
     if rc != 0:
         raise MemoryError("oracle propagation could not allocate scratch")
     return y
+
+
+def prop2d_backward(x, lam, u, w4, gy, eps: float = 1e-6):
+    """Gradient of <gy, prop2d(x, lam, u, w4)> with respect to x, lam, u and w4."""
+    x, lam, u, w4, gy = _f64(x), _f64(lam), _f64(u), _f64(w4), _f64(gy)
+    B, C, H, W = x.shape
+    assert w4.size == 12 * x.size and gy.shape == x.shape
+    gx, glam, gu = np.empty_like(x), np.empty_like(x), np.empty_like(x)
+    gw4 = np.empty_like(w4)
+    rc = _load().gspn_oracle_prop2d_backward(_ptr(x), _ptr(lam), _ptr(u), _ptr(w4), _ptr(gy),
+                                             float(eps), _ptr(gx), _ptr(glam), _ptr(gu), _ptr(gw4),
+                                             B, C, H, W)
+    if rc != 0:
+        raise MemoryError("oracle backward could not allocate scratch")
+    return gx, glam, gu, gw4

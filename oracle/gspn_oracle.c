@@ -189,3 +189,143 @@ int gspn_oracle_prop2d(const double* x, const double* lam, const double* u,
     free(part);
     return 0;
 }
+
+/*
+ * Gradient of the four-direction propagation (paper §6.1 reports forward and
+ * backward kernels; the backward itself is not described on the pages, so
+ * this is the exact derivative of the forward definition above).
+ *
+ * Given gy = dL/dy for y = sum_d u * h_d, per plane and direction d, with
+ * scan-order lines i = 0 .. NL-1, normalised taps wn(i, p, k) and
+ * b_i = lambda_i * x_i:
+ *   adjoint, in reverse scan order:
+ *     g_{NL-1} = u * gy
+ *     g_i      = u * gy + sum_k wn(i+1, q, k) g_{i+1}[q]   over q = p - k + 1
+ *                (the transposed tridiagonal map of line i + 1)
+ *   gx     = lambda * sum_d g_d       glambda = x * sum_d g_d
+ *   gu     = gy * sum_d h_d
+ *   gwn(i, p, k) = g_i[p] * h_{i-1}[p + k - 1]  for i >= 1 and in-line k,
+ *                  0 otherwise (the first line's taps are unused)
+ *   normalisation: s_k = sigmoid(z_k) (in-line), T = s_0 + s_1 + s_2,
+ *     T > eps : gs_m = (gwn_m - sum_k gwn_k wn_k) / T
+ *     T <= eps: gs_m = gwn_m / eps        (the clamp holds S at eps)
+ *     gz_m = gs_m s_m (1 - s_m) for in-line m, 0 for dropped taps.
+ * The branch follows the forward's: the sum is used when it exceeds eps.
+ * All outputs are fp64, in the layouts of the corresponding inputs.
+ * Returns 0, or -1 if scratch memory could not be obtained.
+ */
+int gspn_oracle_prop2d_backward(const double* x, const double* lam, const double* u,
+                                const double* w4, const double* gy, double eps,
+                                double* gx, double* glam, double* gu, double* gw4,
+                                long B, long C, long H, long W) {
+    long npix = H * W;
+    long n = B * C * npix;
+    long Lmax = H > W ? H : W;
+    double* hs = (double*)malloc(sizeof(double) * (size_t)npix);     /* sum_d h_d */
+    double* gs = (double*)malloc(sizeof(double) * (size_t)npix);     /* sum_d g_d */
+    double* hl = (double*)malloc(sizeof(double) * (size_t)npix);     /* h_d by (line, pos) */
+    double* g  = (double*)malloc(sizeof(double) * (size_t)Lmax);
+    double* gn = (double*)malloc(sizeof(double) * (size_t)Lmax);
+    double* wn = (double*)malloc(sizeof(double) * (size_t)npix * 3); /* wn by (line, pos, k) */
+    if (!hs || !gs || !hl || !g || !gn || !wn) {
+        free(hs); free(gs); free(hl); free(g); free(gn); free(wn);
+        return -1;
+    }
+    for (long pl = 0; pl < B * C; ++pl) {
+        const double* xp = x + pl * npix;
+        const double* lp = lam + pl * npix;
+        const double* up = u + pl * npix;
+        const double* gyp = gy + pl * npix;
+        for (long e = 0; e < npix; ++e) { hs[e] = 0.0; gs[e] = 0.0; }
+        for (int d = 0; d < 4; d++) {
+            long NL = (d == DIR_TD || d == DIR_BU) ? H : W;
+            long L  = (d == DIR_TD || d == DIR_BU) ? W : H;
+            int forward = (d == DIR_TD || d == DIR_LR);
+            const double* wp = w4 + ((long)d * n + pl * npix) * 3;   /* [3][NL][L] */
+            double* gwp = gw4 + ((long)d * n + pl * npix) * 3;
+            /* normalised taps of every line */
+            for (long i = 0; i < NL; ++i)
+                for (long p = 0; p < L; ++p) {
+                    double raw[3], t[3];
+                    for (int k = 0; k < 3; ++k) raw[k] = wp[k * npix + (i * L + p)];
+                    normalize_three(raw, p, L, eps, t);
+                    for (int k = 0; k < 3; ++k) wn[(i * L + p) * 3 + k] = t[k];
+                }
+            /* forward scan, keeping every line of h (indexed by line i) */
+            for (long step = 0; step < NL; ++step) {
+                long i = forward ? step : NL - 1 - step;
+                long iprev = forward ? i - 1 : i + 1;
+                for (long p = 0; p < L; ++p) {
+                    long r, c;
+                    pixel_of(d, i, p, &r, &c);
+                    double h = lp[r * W + c] * xp[r * W + c];
+                    if (step > 0) {
+                        for (int k = 0; k < 3; ++k) {
+                            const long q = p + k - 1;
+                            if (q < 0 || q >= L) continue;
+                            h += wn[(i * L + p) * 3 + k] * hl[iprev * L + q];
+                        }
+                    }
+                    hl[i * L + p] = h;
+                    hs[r * W + c] += h;
+                }
+            }
+            /* adjoint scan in reverse order */
+            for (long step = NL - 1; step >= 0; --step) {
+                long i = forward ? step : NL - 1 - step;
+                long inext = forward ? i + 1 : i - 1;      /* the line scanned after i */
+                long iprev = forward ? i - 1 : i + 1;      /* the line scanned before i */
+                for (long p = 0; p < L; ++p) {
+                    long r, c;
+                    pixel_of(d, i, p, &r, &c);
+                    double v = up[r * W + c] * gyp[r * W + c];
+                    if (step < NL - 1) {
+                        /* destinations q of line inext whose tap k reads position p */
+                        for (int k = 0; k < 3; ++k) {
+                            long q = p - k + 1;
+                            if (q < 0 || q >= L) continue;
+                            v += wn[(inext * L + q) * 3 + k] * g[q];
+                        }
+                    }
+                    gn[p] = v;
+                    gs[r * W + c] += v;
+                }
+                /* tap gradients of line i */
+                for (long p = 0; p < L; ++p) {
+                    double gwn[3] = {0.0, 0.0, 0.0};
+                    if (step > 0) {
+                        for (int k = 0; k < 3; ++k) {
+                            const long q = p + k - 1;
+                            if (q < 0 || q >= L) continue;
+                            gwn[k] = gn[p] * hl[iprev * L + q];
+                        }
+                    }
+                    double s[3], T = 0.0, dot = 0.0;
+                    for (int k = 0; k < 3; ++k) {
+                        const long q = p + k - 1;
+                        s[k] = (q >= 0 && q < L) ? sigmoid(wp[k * npix + i * L + p]) : 0.0;
+                        T += s[k];
+                    }
+                    for (int k = 0; k < 3; ++k) dot += gwn[k] * wn[(i * L + p) * 3 + k];
+                    for (int k = 0; k < 3; ++k) {
+                        const long q = p + k - 1;
+                        double gz = 0.0;
+                        if (q >= 0 && q < L) {
+                            double gsk = T > eps ? (gwn[k] - dot) / T : gwn[k] / eps;
+                            gz = gsk * s[k] * (1.0 - s[k]);
+                        }
+                        gwp[k * npix + i * L + p] = gz;
+                    }
+                }
+                double* t = g; g = gn; gn = t;
+            }
+        }
+        for (long e = 0; e < npix; ++e) {
+            gx[pl * npix + e] = lp[e] * gs[e];
+            glam[pl * npix + e] = xp[e] * gs[e];
+            gu[pl * npix + e] = gyp[e] * hs[e];
+        }
+    }
+    free(hs); free(gs); free(hl); free(g); free(gn); free(wn);
+    return 0;
+}

@@ -12,6 +12,7 @@ import subprocess
 import pytest
 
 import oracle
+import test_oracle_backward as bpins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gspn_oracle.c")
@@ -33,6 +34,17 @@ MUTANTS = [
      "raw[k] = wp[k * npix + i * L + (L - 1 - p)];"),
     ("taps read from the transposed plane", "raw[k] = wp[k * npix + i * L + p];",
      "raw[k] = wp[k * npix + p * NL + i];"),
+    # gradient (oracle.prop2d_backward)
+    ("adjoint uses the forward tap map", "long q = p - k + 1;", "long q = p + k - 1;"),
+    ("adjoint seed without u", "double v = up[r * W + c] * gyp[r * W + c];",
+     "double v = gyp[r * W + c];"),
+    ("normalisation Jacobian without the mean term", "(gwn[k] - dot) / T", "gwn[k] / T"),
+    ("clamp branch differentiated as unclamped", "gwn[k] / eps;", "(gwn[k] - dot) / eps;"),
+    ("sigmoid derivative dropped", "gz = gsk * s[k] * (1.0 - s[k]);", "gz = gsk * s[k];"),
+    ("tap gradient paired with the older adjoint line", "gwn[k] = gn[p] * hl[iprev * L + q];",
+     "gwn[k] = g[p] * hl[iprev * L + q];"),
+    ("gu without gy", "gu[pl * npix + e] = gyp[e] * hs[e];", "gu[pl * npix + e] = hs[e];"),
+    ("gx scaled by x", "gx[pl * npix + e] = lp[e] * gs[e];", "gx[pl * npix + e] = xp[e] * gs[e];"),
 ]
 
 
@@ -47,6 +59,10 @@ def _checks():
         yield lambda d=d: pins.test_row_stochastic_constant_propagates(d, 6, 9)
     yield lambda: pins.test_direction_symmetries(4, 7)
     yield lambda: pins.test_prop2d_is_sum_of_directions()
+    yield lambda: bpins.test_backward_matches_directional_finite_differences(3, 5, 0)
+    yield lambda: bpins.test_backward_adjoint_identities(3, 4)
+    yield lambda: bpins.test_backward_clamp_branch()
+    yield lambda: bpins.test_backward_first_line_and_dropped_taps_have_zero_gradient()
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
