@@ -15,6 +15,11 @@ roofline  : the same bytes / average kernel duration (HIP events on the
             counter summary when it was taken on the current kernel source
 cpu_baseline : the fp64 C oracle on the host, single thread, on a bounded
             sample of the same workload (whole planes)
+backward  : the gradient entry point (gspn_prop2d_4dir_backward) on the same
+            workload and rotated sets, timed the same way (not part of
+            `value`); algorithmic bytes = 31 values per pixel-channel (read x,
+            lambda, u, gy and 12 taps, write gx, glambda, gu and 12 tap
+            gradients)
 """
 from __future__ import annotations
 
@@ -32,8 +37,9 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "4-dir GSPN propagation GB/s & ms (B=32,C_c=64,74×74) + % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prop2d_latent1k_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "spatial_line_scan_amd", "csrc", f)
-                  for f in ("gspn_kernels.hip", "gspn_prop2d_pair.hip", "gspn_host.cpp",
-                            "gspn_internal.h", "gspn_device.h")]
+                  for f in ("gspn_kernels.hip", "gspn_prop2d_pair.hip", "gspn_internal.h",
+                            "gspn_device.h")]
+BWD_VALUES_PER_PIXEL = 31
 
 
 def kernel_source_hash() -> str:
@@ -113,6 +119,65 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
     }
 
 
+def backward_leg(wl, sets, args, dev):
+    """Warmup + K backward launches over the rotated sets: wall time and
+    per-launch HIP-event durations on the launch stream."""
+    import numpy as np
+    import torch
+
+    from spatial_line_scan_amd import gspn
+
+    nsets = len(sets)
+    need = gspn.prop2d_4dir_backward_workspace_bytes(wl.B, wl.C, wl.H, wl.W)
+    ws = torch.empty(max(1, need // 4), dtype=torch.float32, device=dev) if need else None
+    grads = []
+    for s in sets:
+        grads.append([torch.empty_like(s["x"]) for _ in range(3)] + [torch.empty_like(s["w"])])
+    lib = gspn.lib()
+    code = gspn.FP32 if wl.dtype == "fp32" else gspn.BF16
+    stream = torch.cuda.current_stream(dev)
+    sp = gspn.ctypes.c_void_p(stream.cuda_stream)
+    wsp = gspn.ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
+    wsb = ws.numel() * 4 if ws is not None else 0
+
+    def bstep(i):
+        s, g = sets[i % nsets], grads[i % nsets]
+        st = lib.gspn_prop2d_4dir_backward(
+            *(gspn.ctypes.c_void_p(t.data_ptr()) for t in (s["x"], s["lam"], s["u"], s["w"], s["gy"])),
+            1e-6, *(gspn.ctypes.c_void_p(t.data_ptr()) for t in g), wsp, wsb, code,
+            wl.B, wl.C, wl.H, wl.W, sp)
+        if st != 0:
+            raise RuntimeError(lib.gspn_status_str(st).decode())
+
+    for i in range(args.warmup):
+        bstep(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        bstep(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        bstep(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern = [a.elapsed_time(b) for a, b in ev]
+    kavg = float(np.mean(kern))
+    nbytes = BWD_VALUES_PER_PIXEL * wl.elem_bytes * wl.pixels
+    achieved = nbytes / (kavg * 1e-3) / 1e9
+    del grads, ws
+    return {"ms_per_step": round(wall * 1e3 / args.steps, 5),
+            "value": round(nbytes / (wall / args.steps) / 1e9, 2), "unit": "GB/s",
+            "algorithmic_bytes_per_step": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                         "kernel_ms_avg": round(kavg, 5),
+                         "kernel_ms_min": round(float(np.min(kern)), 5)}}
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -134,6 +199,10 @@ def main():
                     help="total bytes of rotated input sets (defeats the 256 MB cache)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="run only warmup + K backward launches and print their timing "
+                         "(for profiling the backward kernel on its own)")
     ap.add_argument("--copy-only", action="store_true",
                     help="run only the device copy used for calibration (--steps copies of "
                          "256 Mi fp32 = 1 GiB read + 1 GiB written), e.g. under rocprofv3 --pmc "
@@ -166,8 +235,13 @@ def main():
         return
     print("bench: drawing %s inputs" % wl.name, file=sys.stderr, flush=True)
     base = inputs.problem_torch(wl.B, wl.C, wl.H, wl.W, 0, wl.dtype, dev)
+    if not args.no_backward:
+        base["gy"] = inputs.draw_torch(0, "gy", (wl.B, wl.C, wl.H, wl.W), wl.dtype, dev)
     nsets = max(1, int(np.ceil(args.rotate_bytes / wl.algorithmic_bytes)))
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    if args.backward_only:
+        print(json.dumps({"backward": backward_leg(wl, sets, args, dev)}), flush=True)
+        return
     outs = [torch.empty_like(base["x"]) for _ in range(nsets)]
     torch.cuda.synchronize()
 
@@ -242,6 +316,9 @@ def main():
         "calibration": {"torch_copy_GBps": round(copy_gbps, 1),
                         "frac_of_copy": round(achieved / copy_gbps, 4)},
     }
+    if not args.no_backward:
+        print("bench: backward", file=sys.stderr, flush=True)
+        out["backward"] = backward_leg(wl, sets, args, dev)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, sets[0], outs[0])

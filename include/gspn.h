@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 1
+#define GSPN_ABI_VERSION 2
 
 /* Longest line (H or W) any entry point accepts. */
 #define GSPN_MAX_LINE 8192
@@ -136,6 +136,40 @@ int gspn_scan_dir(const void* x, const void* lam, const void* u, const void* w,
 int gspn_prop2d_4dir(const void* x, const void* lam, const void* u,
                      const void* w_raw4, float eps, void* y, int dtype,
                      int64_t B, int64_t C, int64_t H, int64_t W, void* stream);
+
+/*
+ * Gradient of gspn_prop2d_4dir (the pages report backward kernels, paper text
+ * §6.1, without describing them; this is the exact derivative of the
+ * operator above).  Given gy = dL/dy:
+ *   gx = lambda * G,  glam = x * G,  gu = gy * sum_d h_d,  G = sum_d g_d,
+ * where g_d is the adjoint of direction d, run in reverse scan order with
+ * the transposed tridiagonal tap map:
+ *   g_last = u * gy,   g_i[p] = u * gy + sum_k wn_k(i+1, p-k+1) g_{i+1}[p-k+1];
+ * and gw4 (layout of w_raw4) is the gradient with respect to the logits:
+ *   gwn_k(i, p) = g_i[p] h_{i-1}[p+k-1]  (0 on the first line of the scan
+ *                 and for out-of-line taps),
+ *   T = sum of the in-line sigmoids s_k;
+ *   T > eps : gs_m = (gwn_m - sum_k gwn_k wn_k) / T,  else gs_m = gwn_m / eps
+ *   gz_m = gs_m s_m (1 - s_m).
+ *   x, lam, u, gy, gx, glam, gu : [B][C][H][W];  w_raw4, gw4 : [4][B][C][3][..][..].
+ *   workspace : fp32 scratch of at least
+ *               gspn_prop2d_4dir_backward_workspace(B, C, H, W) bytes (NULL
+ *               allowed when that is 0, which holds while a plane's three
+ *               fp32 planes fit in LDS, e.g. up to 74 x 74 and beyond);
+ *               4-byte aligned; contents on return are unspecified.
+ *   Outputs must not overlap inputs, each other or the workspace.  Lines up
+ *   to 5851 (H and W).  bf16 gradients are rounded to nearest even.  The
+ *   result is bitwise reproducible from run to run.
+ */
+int gspn_prop2d_4dir_backward(const void* x, const void* lam, const void* u,
+                              const void* w_raw4, const void* gy, float eps, void* gx,
+                              void* glam, void* gu, void* gw4, void* workspace,
+                              int64_t workspace_bytes, int dtype, int64_t B, int64_t C,
+                              int64_t H, int64_t W, void* stream);
+
+/* Workspace bytes gspn_prop2d_4dir_backward needs for these sizes (0 if
+ * none), or -1 if it does not accept them. */
+int64_t gspn_prop2d_4dir_backward_workspace(int64_t B, int64_t C, int64_t H, int64_t W);
 
 #ifdef __cplusplus
 }

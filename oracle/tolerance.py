@@ -4,10 +4,20 @@ Pass iff both hold, with r the oracle and g the GPU output widened to fp64:
   elementwise  |g - r| <= rtol * max(|r|, rms(r))   (rms over the whole output)
   normwise     ||g - r||_2 <= rtol * ||r||_2
 fp32 storage: rtol 1e-5; bf16 storage (fp32 arithmetic): rtol 2e-2.
+
+Gradients (backward of the four-direction propagation; the pages give no
+tolerance for them): gx, glambda and gu are a sum of adjoint or forward scans
+and keep the output's rtol.  The tap gradient is a product of an adjoint value
+and a forward value, g_i[p] * h_{i-1}[p+k-1], each carrying a scan's rounding
+error of the size the output's rtol allows, so its relative error is the sum
+of the two: 2e-5 for fp32 storage.  bf16 storage keeps 2e-2 (its 2^-9 output
+rounding is far below it).
 """
 import numpy as np
 
 RTOL = {"fp32": 1e-5, "bf16": 2e-2}
+GRAD_RTOL = {"fp32": {"gx": 1e-5, "glam": 1e-5, "gu": 1e-5, "gw4": 2e-5},
+             "bf16": {"gx": 2e-2, "glam": 2e-2, "gu": 2e-2, "gw4": 2e-2}}
 
 
 def compare(g, r, rtol):

@@ -1,0 +1,246 @@
+// Gradient of the four-direction propagation (gfx950).
+//
+// Operator: "Scaling Parallel Sequence Models to Foundation-Scale Vision
+// Encoders", §3 line-scan recurrence and §5.1 fused normalisation (forward);
+// §6.1 reports backward kernels without describing them, so this is the exact
+// derivative of the forward definition:
+//
+//   adjoint of direction d, lines in reverse scan order:
+//     g_last = u * gy,   g_i = u * gy + (W_{i+1})^T g_{i+1}
+//   where (W^T g)[p] = sum_k wn_k(q) g[q] over the destinations q = p - k + 1
+//   of the next line whose tap k reads position p;
+//   gx = lambda * sum_d g_d,  glambda = x * sum_d g_d,  gu = gy * sum_d h_d;
+//   gwn_k(i, p) = g_i[p] h_{i-1}[p + k - 1] (0 on the first line and for
+//   dropped taps); through the normalisation s = sigmoid(z), T = sum s:
+//     T > eps : gs_m = (gwn_m - sum_k gwn_k wn_k) / T,   else gs_m = gwn_m / eps
+//     (evaluated as sum_{k != m} wn_k (gwn_m - gwn_k) / T, equal since the
+//     unclamped taps sum to one)
+//     gz_m = gs_m s_m (1 - s_m) for in-line taps.
+//
+// One workgroup owns one (b, c) plane and runs the four directions in turn:
+// a forward pass that keeps every line of h (in the line-major order of the
+// direction), then the adjoint pass.  The three fp32 planes (h of the current
+// direction, sum_d h, sum_d g) live in LDS when they fit, else in a workspace
+// the caller passes; the current, previous and next lines and the next line's
+// normalised taps are LDS lines.
+#include "gspn_device.h"
+#include "gspn_internal.h"
+
+namespace gspn {
+namespace {
+
+constexpr int kBwdThreads = 256;
+
+// Sigmoids, sum and normalised taps of one destination position (forward
+// normalisation, kept for the Jacobian).
+struct TapNorm {
+    float s[3], wn[3], T;
+};
+
+__device__ __forceinline__ TapNorm tap_norm(float z0, float z1, float z2, bool has_left,
+                                            bool has_right, float eps) {
+    TapNorm t;
+    t.s[0] = has_left ? sigmoid_hw(z0) : 0.0f;
+    t.s[1] = sigmoid_hw(z1);
+    t.s[2] = has_right ? sigmoid_hw(z2) : 0.0f;
+    t.T = (t.s[0] + t.s[1]) + t.s[2];
+    const float r = __builtin_amdgcn_rcpf(fmaxf(t.T, eps));
+    for (int k = 0; k < 3; ++k) t.wn[k] = t.s[k] * r;
+    return t;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_f(T* p, size_t i, float v) {
+    store_elem(p, i, v);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kBwdThreads)
+prop2d_backward_kernel(const T* __restrict__ x, const T* __restrict__ lam,
+                       const T* __restrict__ u, const T* __restrict__ w4,
+                       const T* __restrict__ gy, float eps, T* __restrict__ gx,
+                       T* __restrict__ glam, T* __restrict__ gu, T* __restrict__ gw4,
+                       float* __restrict__ ws, int64_t planes, int H, int W) {
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x;
+    const int Lmax = H > W ? H : W;
+    const size_t npix = static_cast<size_t>(H) * W;
+    const size_t plane = blockIdx.x;
+    // LDS lines: h (2), g (2), normalised taps of the next line (3)
+    float* hline = lds;                  // [2][Lmax]
+    float* gline = hline + 2 * Lmax;     // [2][Lmax]
+    float* wnext = gline + 2 * Lmax;     // [3][Lmax]
+    float* planes3;
+    if (ws == nullptr) planes3 = wnext + 3 * Lmax;   // [3][npix] in LDS
+    else planes3 = ws + plane * 3 * npix;
+    float* hd = planes3;                 // h of the current direction, [NL][L]
+    float* hs = planes3 + npix;          // sum_d h, pixel order
+    float* gs = planes3 + 2 * npix;      // sum_d g, pixel order
+
+    const T* xp = x + plane * npix;
+    const T* lp = lam + plane * npix;
+    const T* up = u + plane * npix;
+    const T* gyp = gy + plane * npix;
+    for (size_t e = tid; e < npix; e += kBwdThreads) {
+        hs[e] = 0.0f;
+        gs[e] = 0.0f;
+    }
+    __syncthreads();
+
+    for (int dir = 0; dir < 4; ++dir) {
+        const bool rows = dir < 2;
+        const bool fwd = dir == 0 || dir == 2;
+        const int NL = rows ? H : W;
+        const int L = rows ? W : H;
+        const size_t tap_base = (static_cast<size_t>(dir) * planes + plane) * 3 * npix;
+        const T* wp = w4 + tap_base;
+        T* gwp = gw4 + tap_base;
+        auto pix = [&](int i, int p) -> size_t {
+            return rows ? static_cast<size_t>(i) * W + p : static_cast<size_t>(p) * W + i;
+        };
+        auto line_of = [&](int step) { return fwd ? step : NL - 1 - step; };
+
+        // ---------------------------------------------- forward, keeping h
+        for (int step = 0; step < NL; ++step) {
+            const int i = line_of(step);
+            const float* hprev = hline + ((step + 1) & 1) * Lmax;
+            float* hnew = hline + (step & 1) * Lmax;
+            for (int p = tid; p < L; p += kBwdThreads) {
+                const size_t px = pix(i, p);
+                float h = load_elem(lp, px) * load_elem(xp, px);
+                if (step > 0) {
+                    const size_t t = static_cast<size_t>(i) * L + p;
+                    const TapNorm tn = tap_norm(load_elem(wp, t), load_elem(wp, t + npix),
+                                                load_elem(wp, t + 2 * npix), p > 0, p < L - 1, eps);
+                    float m = tn.wn[1] * hprev[p];
+                    if (p > 0) m = fmaf(tn.wn[0], hprev[p - 1], m);
+                    if (p < L - 1) m = fmaf(tn.wn[2], hprev[p + 1], m);
+                    h += m;
+                }
+                hnew[p] = h;
+                hd[static_cast<size_t>(i) * L + p] = h;
+                hs[px] += h;
+            }
+            __syncthreads();
+        }
+
+        // ---------------------------------------------- adjoint, reverse order
+        for (int step = NL - 1; step >= 0; --step) {
+            const int i = line_of(step);
+            const int iprev = step > 0 ? line_of(step - 1) : i;
+            const float* gold = gline + ((step + 1) & 1) * Lmax;   // line scanned after i
+            float* gnew = gline + (step & 1) * Lmax;
+            float wcur[3][4];   // normalised taps of line i for this thread's positions
+            int slot = 0;
+            for (int p = tid; p < L; p += kBwdThreads, ++slot) {
+                const size_t px = pix(i, p);
+                float v = load_elem(up, px) * load_elem(gyp, px);
+                if (step < NL - 1) {
+                    // destinations q = p + 1, p, p - 1 of the next line read p
+                    // through their taps 0, 1, 2
+                    v = fmaf(wnext[Lmax + p], gold[p], v);
+                    if (p + 1 < L) v = fmaf(wnext[p + 1], gold[p + 1], v);
+                    if (p > 0) v = fmaf(wnext[2 * Lmax + p - 1], gold[p - 1], v);
+                }
+                gnew[p] = v;
+                gs[px] += v;
+
+                const size_t t = static_cast<size_t>(i) * L + p;
+                const TapNorm tn = tap_norm(load_elem(wp, t), load_elem(wp, t + npix),
+                                            load_elem(wp, t + 2 * npix), p > 0, p < L - 1, eps);
+                if (slot < 4)
+                    for (int k = 0; k < 3; ++k) wcur[k][slot] = tn.wn[k];
+                float gz[3] = {0.0f, 0.0f, 0.0f};
+                if (step > 0) {
+                    const float* hp = hd + static_cast<size_t>(iprev) * L;
+                    float gwn[3];
+                    gwn[0] = p > 0 ? v * hp[p - 1] : 0.0f;
+                    gwn[1] = v * hp[p];
+                    gwn[2] = p < L - 1 ? v * hp[p + 1] : 0.0f;
+                    // Unclamped, the taps sum to one, so gwn_m - sum_k gwn_k wn_k
+                    // = sum_{k != m} wn_k (gwn_m - gwn_k): the same value without
+                    // the cancellation (a lone in-line tap gets exactly 0).
+                    const bool unclamped = tn.T > eps;
+                    const float rT = __builtin_amdgcn_rcpf(unclamped ? tn.T : eps);
+                    for (int m = 0; m < 3; ++m) {
+                        float num = gwn[m];
+                        if (unclamped) {
+                            num = 0.0f;
+                            for (int k = 0; k < 3; ++k)
+                                if (k != m) num = fmaf(tn.wn[k], gwn[m] - gwn[k], num);
+                        }
+                        gz[m] = num * rT * tn.s[m] * (1.0f - tn.s[m]);
+                    }
+                    if (p == 0) gz[0] = 0.0f;
+                    if (p == L - 1) gz[2] = 0.0f;
+                }
+                store_f(gwp, t, gz[0]);
+                store_f(gwp, t + npix, gz[1]);
+                store_f(gwp, t + 2 * npix, gz[2]);
+            }
+            __syncthreads();   // every read of wnext and gold of this step is done
+            slot = 0;
+            for (int p = tid; p < L; p += kBwdThreads, ++slot) {
+                if (slot < 4) {
+                    for (int k = 0; k < 3; ++k) wnext[k * Lmax + p] = wcur[k][slot];
+                } else {
+                    const size_t t = static_cast<size_t>(i) * L + p;
+                    const TapNorm tn = tap_norm(load_elem(wp, t), load_elem(wp, t + npix),
+                                                load_elem(wp, t + 2 * npix), p > 0, p < L - 1, eps);
+                    for (int k = 0; k < 3; ++k) wnext[k * Lmax + p] = tn.wn[k];
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    for (size_t e = tid; e < npix; e += kBwdThreads) {
+        const float g = gs[e];
+        store_f(gx + plane * npix, e, load_elem(lp, e) * g);
+        store_f(glam + plane * npix, e, load_elem(xp, e) * g);
+        store_f(gu + plane * npix, e, load_elem(gyp, e) * hs[e]);
+    }
+}
+
+size_t bwd_line_floats(int64_t H, int64_t W) { return 7 * static_cast<size_t>(H > W ? H : W); }
+
+template <typename T>
+hipError_t backward_t(const void* x, const void* lam, const void* u, const void* w4,
+                      const void* gy, float eps, void* gx, void* glam, void* gu, void* gw4,
+                      void* ws, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
+    const size_t lines = bwd_line_floats(H, W) * sizeof(float);
+    const size_t lds = ws ? lines : lines + 3 * static_cast<size_t>(H * W) * sizeof(float);
+    auto kern = prop2d_backward_kernel<T>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    kern<<<dim3(static_cast<unsigned>(planes)), dim3(kBwdThreads), lds, stream>>>(
+        static_cast<const T*>(x), static_cast<const T*>(lam), static_cast<const T*>(u),
+        static_cast<const T*>(w4), static_cast<const T*>(gy), eps, static_cast<T*>(gx),
+        static_cast<T*>(glam), static_cast<T*>(gu), static_cast<T*>(gw4),
+        static_cast<float*>(ws), planes, static_cast<int>(H), static_cast<int>(W));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W) {
+    const int64_t lds = static_cast<int64_t>(bwd_line_floats(H, W) + 3 * H * W) * 4;
+    return lds <= kLdsBytes ? 0 : planes * 3 * H * W * 4;
+}
+
+int64_t prop2d_backward_max_line() { return kLdsBytes / 4 / 7; }
+
+hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u, const void* w4,
+                                  const void* gy, float eps, void* gx, void* glam, void* gu,
+                                  void* gw4, void* ws, int dtype, int64_t planes, int64_t H,
+                                  int64_t W, hipStream_t stream) {
+    return dtype == 0 ? backward_t<float>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W, stream)
+                      : backward_t<uint16_t>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W,
+                                             stream);
+}
+
+}  // namespace gspn

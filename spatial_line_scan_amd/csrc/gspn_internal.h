@@ -31,6 +31,16 @@ hipError_t launch_prop2d_pair(const void* x, const void* lam, const void* u, con
                               float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                               hipStream_t stream);
 
+// Gradient of gspn_prop2d_4dir (gspn_backward.hip).  ws is NULL when the
+// three fp32 planes of a workgroup fit in LDS, else planes * 3 * H * W floats.
+hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u, const void* w4,
+                                  const void* gy, float eps, void* gx, void* glam, void* gu,
+                                  void* gw4, void* ws, int dtype, int64_t planes, int64_t H,
+                                  int64_t W, hipStream_t stream);
+int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W);
+// Longest line the backward's LDS lines allow.
+int64_t prop2d_backward_max_line();
+
 // Largest plane (H * W pixels) gspn_prop2d_4dir accepts for an element type.
 int64_t prop2d_max_plane(int dtype, int64_t H, int64_t W);
 

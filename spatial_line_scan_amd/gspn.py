@@ -52,6 +52,11 @@ def lib():
         L.gspn_scan_dir.restype = ci
         L.gspn_prop2d_4dir.argtypes = [vp, vp, vp, vp, cf, vp, ci, i64, i64, i64, i64, vp]
         L.gspn_prop2d_4dir.restype = ci
+        L.gspn_prop2d_4dir_backward.argtypes = [vp, vp, vp, vp, vp, cf, vp, vp, vp, vp, vp, i64,
+                                                ci, i64, i64, i64, i64, vp]
+        L.gspn_prop2d_4dir_backward.restype = ci
+        L.gspn_prop2d_4dir_backward_workspace.argtypes = [i64, i64, i64, i64]
+        L.gspn_prop2d_4dir_backward_workspace.restype = i64
         _lib = L
     return _lib
 
@@ -146,3 +151,55 @@ def prop2d_4dir(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4: torch.T
         _check(lib().gspn_prop2d_4dir(_p(x), _p(lam), _p(u), _p(w4), float(eps), _p(out),
                                       _dtype_code(x), B, C, H, W, _stream(x)))
     return out
+
+
+def prop2d_4dir_backward_workspace_bytes(B: int, C: int, H: int, W: int) -> int:
+    """Scratch bytes prop2d_4dir_backward needs for these sizes (0: none)."""
+    n = lib().gspn_prop2d_4dir_backward_workspace(B, C, H, W)
+    if n < 0:
+        raise ValueError("sizes not accepted by gspn_prop2d_4dir_backward")
+    return n
+
+
+def prop2d_4dir_backward(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4: torch.Tensor,
+                         gy: torch.Tensor, eps: float = 1e-6, workspace: torch.Tensor | None = None):
+    """Gradients (gx, glam, gu, gw4) of prop2d_4dir given gy = dL/dy.
+
+    The workspace (fp32 scratch, only needed for planes too large for on-chip
+    memory) is allocated here with torch when none is given."""
+    _same(x, lam, u, w4, gy)
+    if x.dim() != 4 or lam.shape != x.shape or u.shape != x.shape or gy.shape != x.shape:
+        raise ValueError("x, lam, u, gy must share one [B, C, H, W] shape")
+    B, C, H, W = x.shape
+    if w4.numel() != 12 * x.numel():
+        raise ValueError("w4 must hold 4*B*C*3*H*W elements")
+    need = prop2d_4dir_backward_workspace_bytes(B, C, H, W)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=x.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if workspace is not None and (workspace.device != x.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on x's device")
+    gx, glam, gu = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    gw4 = torch.empty_like(w4)
+    with torch.cuda.device(x.device):
+        _check(lib().gspn_prop2d_4dir_backward(_p(x), _p(lam), _p(u), _p(w4), _p(gy), float(eps),
+                                               _p(gx), _p(glam), _p(gu), _p(gw4), ws_ptr, ws_bytes,
+                                               _dtype_code(x), B, C, H, W, _stream(x)))
+    return gx, glam, gu, gw4
+
+
+class Prop2d4Dir(torch.autograd.Function):
+    """Autograd wrapper: forward prop2d_4dir, backward prop2d_4dir_backward."""
+
+    @staticmethod
+    def forward(ctx, x, lam, u, w4, eps=1e-6):
+        ctx.eps = float(eps)
+        ctx.save_for_backward(x, lam, u, w4)
+        return prop2d_4dir(x, lam, u, w4, eps)
+
+    @staticmethod
+    def backward(ctx, gy):
+        x, lam, u, w4 = ctx.saved_tensors
+        gx, glam, gu, gw4 = prop2d_4dir_backward(x, lam, u, w4, gy.contiguous(), ctx.eps)
+        return gx, glam, gu, gw4, None

@@ -18,7 +18,8 @@ published) used as a counter-based hash, and the Box-Muller transform
 Storage rounding: fp32 tensors hold float32(z) (round to nearest even);
 bf16 tensors hold bf16(float32(z)) (round to nearest even on the fp32 bits).
 
-Tensor ids: x = 0, lambda = 1, u = 2, taps of all four directions = 3.
+Tensor ids: x = 0, lambda = 1, u = 2, taps of all four directions = 3,
+upstream gradient gy (dL/dy, for the backward) = 4.
 """
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-TENSOR_IDS = {"x": 0, "lam": 1, "u": 2, "w": 3}
+TENSOR_IDS = {"x": 0, "lam": 1, "u": 2, "w": 3, "gy": 4}
 _CHUNK = 1 << 22
 
 

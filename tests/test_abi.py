@@ -34,19 +34,20 @@ def L():
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(gspn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|int64_t|const char\*)\s+(gspn_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
     assert set(syms) >= {"gspn_abi_version", "gspn_status_str", "gspn_normalize_weights",
-                         "gspn_scan_dir", "gspn_prop2d_4dir"}
+                         "gspn_scan_dir", "gspn_prop2d_4dir",
+                         "gspn_prop2d_4dir_backward", "gspn_prop2d_4dir_backward_workspace"}
     for s in syms:
         assert hasattr(L, s), s
 
 
 def test_version_and_status_strings(L):
-    assert L.gspn_abi_version() == 1
+    assert L.gspn_abi_version() == 2
     for s in range(9):
         assert L.gspn_status_str(s).decode().startswith("GSPN")
     assert L.gspn_status_str(12345)
@@ -147,3 +148,61 @@ def test_aliasing(L):
     assert prop(L, y=ctypes.c_void_p(A + 3 * STEP + 12 * n - 16)) == ALIAS  # tail of w4
     assert scan(L, y=P(0)) == ALIAS
     assert norm(L, dst=P(3)) == ALIAS
+
+
+def bwd(L, ptrs=None, eps=1e-6, ws=None, ws_bytes=0, dt=0, B=2, C=3, H=5, W=7):
+    p = list(ptrs) if ptrs else [P(i) for i in range(9)]
+    return L.gspn_prop2d_4dir_backward(p[0], p[1], p[2], p[3], p[4], eps, p[5], p[6], p[7], p[8],
+                                       ws, ws_bytes, dt, B, C, H, W, None)
+
+
+def test_backward_workspace_query(L):
+    # 7 LDS lines plus three fp32 planes fit in 160 KiB up to about 115 x 115
+    assert L.gspn_prop2d_4dir_backward_workspace(32, 64, 74, 74) == 0
+    assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 115, 115) == 0
+    assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 120, 120) == 2 * 3 * 3 * 120 * 120 * 4
+    assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 5852, 2) == -1      # line too long
+    assert L.gspn_prop2d_4dir_backward_workspace(0, 1, 4, 4) == -1
+    assert L.gspn_prop2d_4dir_backward_workspace(1, 1 << 18, 64, 64) == -1
+
+
+def test_backward_rejects_bad_arguments(L):
+    assert bwd(L, dt=2) == DTYPE
+    assert bwd(L, B=0) == SHAPE
+    assert bwd(L, H=5852, W=2) == SHAPE
+    assert bwd(L, eps=0.0) == VALUE
+    assert bwd(L, eps=float("nan")) == VALUE
+    null = ctypes.c_void_p(0)
+    for i in range(9):
+        ptrs = [P(j) for j in range(9)]
+        ptrs[i] = null
+        assert bwd(L, ptrs) == NULL
+    ptrs = [P(j) for j in range(9)]
+    ptrs[0] = ctypes.c_void_p(A + 2)
+    assert bwd(L, ptrs) == ALIGN
+    ptrs = [P(j) for j in range(9)]
+    ptrs[8] = ctypes.c_void_p(A + 8 * STEP + 1)
+    assert bwd(L, ptrs, dt=1) == ALIGN
+
+
+def test_backward_aliasing(L):
+    for o in range(5, 9):
+        for other in range(9):
+            if other == o:
+                continue
+            ptrs = [P(j) for j in range(9)]
+            ptrs[o] = P(other)
+            assert bwd(L, ptrs) == ALIAS, (o, other)
+    ptrs = [P(j) for j in range(9)]
+    ptrs[5] = ctypes.c_void_p(A + 3 * STEP + 16)            # gx inside w4
+    assert bwd(L, ptrs) == ALIAS
+
+
+def test_backward_workspace_checks(L):
+    need = 2 * 3 * 3 * 120 * 120 * 4
+    assert bwd(L, H=120, W=120) == NULL                      # workspace needed, none given
+    assert bwd(L, ws=P(10), ws_bytes=need - 4, H=120, W=120) == SHAPE
+    assert bwd(L, ws=ctypes.c_void_p(A + 10 * STEP + 2), ws_bytes=need, H=120, W=120) == ALIGN
+    assert bwd(L, ws=P(0), ws_bytes=need, H=120, W=120) == ALIAS        # over x
+    assert bwd(L, ws=P(7), ws_bytes=need, H=120, W=120) == ALIAS        # over gu
+    assert bwd(L, ws_bytes=-1) == SHAPE
