@@ -16,12 +16,17 @@ scan_dir(x, lam, u, w, dir, w_is_raw, eps) -> u * h for one direction
 prop2d(x, lam, u, w4, eps)                -> sum over the four directions
 prop2d_backward(x, lam, u, w4, gy, eps)   -> (gx, glam, gu, gw4), the gradient
                                              of <gy, prop2d(x, lam, u, w4)>
+prop2d_ex(x, lam, u, w4g, groups, k_chunk, eps)
+                                          -> prop2d with taps shared by groups of
+                                             channels and/or chunked scans
 
 Layouts follow the C file's header: x, lam, u: [B][C][H][W]; the taps of one
 direction: [B][C][3][NL][L] indexed by (line, position) of that direction
-(TD/BU: NL=H, L=W; LR/RL: NL=W, L=H); w4: [4][B][C][3][..][..].
+(TD/BU: NL=H, L=W; LR/RL: NL=W, L=H); w4: [4][B][C][3][..][..]; grouped
+taps w4g: [4][B][G][3][..][..].
 
-Parity unpinned: none.  Each function is pinned by tests/test_oracle_pins.py.
+Parity unpinned: none.  Each function is pinned: tests/test_oracle_pins.py,
+tests/test_oracle_backward.py, tests/test_oracle_ex.py.
 """
 from __future__ import annotations
 
@@ -68,6 +73,10 @@ def _load(path: str | None = None):
             lib.gspn_oracle_prop2d_backward.argtypes = [dp, dp, dp, dp, dp, ctypes.c_double,
                                                         dp, dp, dp, dp, L, L, L, L]
             lib.gspn_oracle_prop2d_backward.restype = ctypes.c_int
+        if hasattr(lib, "gspn_oracle_prop2d_ex"):
+            lib.gspn_oracle_prop2d_ex.argtypes = [dp, dp, dp, dp, L, L, ctypes.c_double, dp,
+                                                  L, L, L, L]
+            lib.gspn_oracle_prop2d_ex.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -149,3 +158,19 @@ def prop2d_backward(x, lam, u, w4, gy, eps: float = 1e-6):
     if rc != 0:
         raise MemoryError("oracle backward could not allocate scratch")
     return gx, glam, gu, gw4
+
+
+def prop2d_ex(x, lam, u, w4g, groups: int, k_chunk: int = 1, eps: float = 1e-6) -> np.ndarray:
+    """prop2d with taps shared by `groups` contiguous channel groups (w4g:
+    [4][B][groups][3][..][..]) and each scan cut into k_chunk segments."""
+    x, lam, u, w4g = _f64(x), _f64(lam), _f64(u), _f64(w4g)
+    B, C, H, W = x.shape
+    assert w4g.size == 12 * B * groups * H * W
+    y = np.empty_like(x)
+    rc = _load().gspn_oracle_prop2d_ex(_ptr(x), _ptr(lam), _ptr(u), _ptr(w4g), int(groups),
+                                       int(k_chunk), float(eps), _ptr(y), B, C, H, W)
+    if rc == -2:
+        raise ValueError("groups must divide C and k_chunk must be >= 1")
+    if rc != 0:
+        raise MemoryError("oracle propagation could not allocate scratch")
+    return y

@@ -329,3 +329,84 @@ int gspn_oracle_prop2d_backward(const double* x, const double* lam, const double
     free(hs); free(gs); free(hl); free(g); free(gn); free(wn);
     return 0;
 }
+
+/*
+ * Extended operator: tap groups and chunked (local) scans.
+ *
+ * Tap groups (paper §4.2, channel-shared weights; §6.2 shares the weights
+ * across channels in every module): the C channels form G contiguous groups
+ * of C / G channels, and channel c reads the taps of group c / (C / G).  The
+ * taps are then [4][B][G][3][..][..].  G = C is the per-channel operator
+ * above; G = 1 shares one set of taps among all channels of an image.
+ *
+ * Chunked scan (paper §4.1: the grid is indexed by (chunk, b, c), k_chunk
+ * chunks per plane): each direction's NL lines are cut into k_chunk
+ * contiguous segments of Lc = ceil(NL / k_chunk) lines (the last one may be
+ * shorter; with k_chunk > NL some are empty), the same segments for both
+ * scan orders of an axis.  Each segment is scanned on its own: the first
+ * line of a segment in the direction's scan order restarts from
+ * h = lambda * x.  k_chunk = 1 is the global scan above.
+ *
+ * y = sum over TD, BU, LR, RL of u * h_d, accumulated in that order.
+ * Returns 0, -1 if scratch memory could not be obtained, -2 for a bad G or
+ * k_chunk.
+ */
+static int restarts_segment(long i, long NL, long Lc, int fwd) {
+    if (fwd) return i % Lc == 0;                 /* top (left) line of its segment */
+    return i == NL - 1 || (i + 1) % Lc == 0;     /* bottom (right) line of its segment */
+}
+
+int gspn_oracle_prop2d_ex(const double* x, const double* lam, const double* u,
+                          const double* w4, long G, long k_chunk, double eps,
+                          double* y, long B, long C, long H, long W) {
+    if (G < 1 || C % G != 0 || k_chunk < 1) return -2;
+    long npix = H * W;
+    long cpg = C / G;                              /* channels per group */
+    long Lmax = H > W ? H : W;
+    double* prev = (double*)malloc(sizeof(double) * (size_t)Lmax);
+    double* cur = (double*)malloc(sizeof(double) * (size_t)Lmax);
+    if (!prev || !cur) { free(prev); free(cur); return -1; }
+    for (long b = 0; b < B; ++b) {
+        for (long ch = 0; ch < C; ++ch) {
+            long pl = b * C + ch;
+            const double* xs = x + pl * npix;
+            const double* ls = lam + pl * npix;
+            const double* us = u + pl * npix;
+            double* ys = y + pl * npix;
+            for (long e = 0; e < npix; ++e) ys[e] = 0.0;
+            for (int dir = DIR_TD; dir <= DIR_RL; dir++) {
+                int along_rows = (dir == DIR_TD || dir == DIR_BU);
+                long NL = along_rows ? H : W;
+                long L = along_rows ? W : H;
+                int fwd = (dir == DIR_TD) || (dir == DIR_LR);
+                long Lc = (NL + k_chunk - 1) / k_chunk;
+                const double* tg = w4 + (((long)dir * B + b) * G + ch / cpg) * 3 * npix;
+                for (long step = 0; step < NL; ++step) {
+                    long i = fwd ? step : NL - 1 - step;
+                    int restart = restarts_segment(i, NL, Lc, fwd);
+                    for (long p = 0; p < L; ++p) {
+                        long r, c;
+                        pixel_of(dir, i, p, &r, &c);
+                        long e = r * W + c;
+                        double hv = ls[e] * xs[e];
+                        if (!restart) {
+                            double z[3], wn[3];
+                            for (int k = 0; k < 3; ++k) z[k] = tg[(long)k * npix + i * L + p];
+                            normalize_three(z, p, L, eps, wn);
+                            for (int k = 0; k < 3; ++k) {
+                                long src = p + k - 1;
+                                if (src >= 0 && src < L) hv += wn[k] * prev[src];
+                            }
+                        }
+                        cur[p] = hv;
+                        ys[e] += us[e] * hv;
+                    }
+                    double* t = prev; prev = cur; cur = t;
+                }
+            }
+        }
+    }
+    free(prev);
+    free(cur);
+    return 0;
+}

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 import test_oracle_backward as bpins
+import test_oracle_ex as xpins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gspn_oracle.c")
@@ -45,6 +46,15 @@ MUTANTS = [
      "gwn[k] = g[p] * hl[iprev * L + q];"),
     ("gu without gy", "gu[pl * npix + e] = gyp[e] * hs[e];", "gu[pl * npix + e] = hs[e];"),
     ("gx scaled by x", "gx[pl * npix + e] = lp[e] * gs[e];", "gx[pl * npix + e] = xp[e] * gs[e];"),
+    # tap groups and chunked scans (oracle.prop2d_ex)
+    ("reverse segments restart at their first spatial line",
+     "return i == NL - 1 || (i + 1) % Lc == 0;", "return i == NL - 1 || i % Lc == 0;"),
+    ("forward segments restart one line late", "if (fwd) return i % Lc == 0;",
+     "if (fwd) return i == 0 || i % Lc == 1;"),
+    ("segment length rounded down", "long Lc = (NL + k_chunk - 1) / k_chunk;",
+     "long Lc = NL > k_chunk ? NL / k_chunk : 1;"),
+    ("channel groups interleaved", "ch / cpg) * 3 * npix;", "ch % G) * 3 * npix;"),
+    ("segments never restart", "if (!restart) {", "if (step > 0) {"),
 ]
 
 
@@ -63,6 +73,11 @@ def _checks():
     yield lambda: bpins.test_backward_adjoint_identities(3, 4)
     yield lambda: bpins.test_backward_clamp_branch()
     yield lambda: bpins.test_backward_first_line_and_dropped_taps_have_zero_gradient()
+    yield lambda: xpins.test_ex_reduces_to_prop2d(3, 5)
+    yield lambda: xpins.test_grouped_taps_equal_expanded_per_channel_taps(6, 2)
+    yield lambda: xpins.test_groups_are_contiguous_channel_blocks()
+    yield lambda: xpins.test_chunked_scan_equals_global_scans_of_segments(7, 9, 3)
+    yield lambda: xpins.test_one_line_segments_reduce_to_4_u_lambda_x(7)
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
