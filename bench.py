@@ -15,6 +15,10 @@ roofline  : the same bytes / average kernel duration (HIP events on the
             counter summary when it was taken on the current kernel source
 cpu_baseline : the fp64 C oracle on the host, single thread, on a bounded
             sample of the same workload (whole planes)
+variants  : gspn_prop2d_4dir_ex on the same workload shape, timed the same
+            way (not part of `value`): taps shared by all channels of an image
+            (groups = 1; algorithmic bytes 4 + 12 G / C values per
+            pixel-channel) and a chunked scan (k_chunk = 4, per-channel taps)
 backward  : the gradient entry point (gspn_prop2d_4dir_backward) on the same
             workload and rotated sets, timed the same way (not part of
             `value`); algorithmic bytes = 31 values per pixel-channel (read x,
@@ -119,6 +123,62 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
     }
 
 
+def _timed(fn, steps, warmup, stream):
+    """Wall time of `steps` calls and their per-call HIP-event durations."""
+    import numpy as np
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern = [a.elapsed_time(b) for a, b in ev]
+    return wall, float(np.mean(kern)), float(np.min(kern))
+
+
+def variant_leg(wl, args, dev, G, k):
+    """gspn_prop2d_4dir_ex with `G` tap groups and k-chunk scans on the
+    workload's shape, over rotated input sets of at least --rotate-bytes."""
+    import numpy as np
+    import torch
+
+    from spatial_line_scan_amd import gspn, inputs
+
+    shp = (wl.B, wl.C, wl.H, wl.W)
+    base = {n: inputs.draw_torch(0, n, shp, wl.dtype, dev) for n in ("x", "lam", "u")}
+    base["w"] = inputs.draw_torch(0, "w", (4, wl.B, G, 3, wl.H * wl.W), wl.dtype, dev)
+    nbytes = int(round((4 + 12.0 * G / wl.C) * wl.elem_bytes * wl.pixels))
+    nsets = max(1, int(np.ceil(args.rotate_bytes / nbytes)))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(nsets - 1)]
+    outs = [torch.empty_like(base["x"]) for _ in range(nsets)]
+    torch.cuda.synchronize()
+
+    def fn(i):
+        s = sets[i % nsets]
+        gspn.prop2d_4dir_ex(s["x"], s["lam"], s["u"], s["w"], G, k, out=outs[i % nsets])
+
+    wall, kavg, kmin = _timed(fn, args.steps, args.warmup, torch.cuda.current_stream(dev))
+    achieved = nbytes / (kavg * 1e-3) / 1e9
+    del sets, outs
+    torch.cuda.empty_cache()
+    return {"groups": G, "k_chunk": k, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+            "value": round(nbytes / (wall / args.steps) / 1e9, 2), "unit": "GB/s",
+            "algorithmic_bytes_per_step": nbytes, "rotated_input_sets": nsets,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                         "kernel_ms_avg": round(kavg, 5), "kernel_ms_min": round(kmin, 5)}}
+
+
 def backward_leg(wl, sets, args, dev):
     """Warmup + K backward launches over the rotated sets: wall time and
     per-launch HIP-event durations on the launch stream."""
@@ -200,6 +260,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-variants", action="store_true", help="skip the grouped / chunked legs")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only warmup + K backward launches and print their timing "
                          "(for profiling the backward kernel on its own)")
@@ -316,6 +377,9 @@ def main():
         "calibration": {"torch_copy_GBps": round(copy_gbps, 1),
                         "frac_of_copy": round(achieved / copy_gbps, 4)},
     }
+    if not args.no_variants:
+        print("bench: variants", file=sys.stderr, flush=True)
+        out["variants"] = [variant_leg(wl, args, dev, G, k) for G, k in ((1, 1), (wl.C, 4))]
     if not args.no_backward:
         print("bench: backward", file=sys.stderr, flush=True)
         out["backward"] = backward_leg(wl, sets, args, dev)

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 2
+#define GSPN_ABI_VERSION 3
 
 /* Longest line (H or W) any entry point accepts. */
 #define GSPN_MAX_LINE 8192
@@ -136,6 +136,30 @@ int gspn_scan_dir(const void* x, const void* lam, const void* u, const void* w,
 int gspn_prop2d_4dir(const void* x, const void* lam, const void* u,
                      const void* w_raw4, float eps, void* y, int dtype,
                      int64_t B, int64_t C, int64_t H, int64_t W, void* stream);
+
+/*
+ * gspn_prop2d_4dir with two options of the operator:
+ *   groups  : taps shared by channel groups (paper §4.2 channel-shared
+ *             weights; §6.2 shares them across channels in every module).
+ *             The C channels form `groups` contiguous groups of C / groups
+ *             channels; channel c reads the taps of group c / (C / groups).
+ *             w_raw4 is [4][B][groups][3][..][..].  groups = C is
+ *             gspn_prop2d_4dir; groups = 1 shares one set of taps per image.
+ *             Must divide C (else GSPN_ERR_SHAPE).
+ *   k_chunk : chunked (local) scan (paper §4.1: the grid is indexed by
+ *             (chunk, b, c)).  Each direction's NL lines are cut into
+ *             k_chunk segments of ceil(NL / k_chunk) lines (the last may be
+ *             shorter), the same segments for both scan orders of an axis;
+ *             each segment is scanned on its own and its first line in scan
+ *             order is lambda * x.  k_chunk = 1 is the global scan; values at
+ *             or above a scan's line count give single-line segments.  Must
+ *             be >= 1 (else GSPN_ERR_VALUE).
+ * Other arguments, layouts, errors and determinism as gspn_prop2d_4dir.
+ */
+int gspn_prop2d_4dir_ex(const void* x, const void* lam, const void* u,
+                        const void* w_raw4, int64_t groups, int64_t k_chunk,
+                        float eps, void* y, int dtype, int64_t B, int64_t C,
+                        int64_t H, int64_t W, void* stream);
 
 /*
  * Gradient of gspn_prop2d_4dir (the pages report backward kernels, paper text

@@ -5,6 +5,7 @@
 #include "gspn.h"
 #include "gspn_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -104,19 +105,32 @@ int gspn_scan_dir(const void* x, const void* lam, const void* u, const void* w, 
 int gspn_prop2d_4dir(const void* x, const void* lam, const void* u, const void* w_raw4,
                      float eps, void* y, int dtype, int64_t B, int64_t C, int64_t H, int64_t W,
                      void* stream) {
+    return gspn_prop2d_4dir_ex(x, lam, u, w_raw4, C, 1, eps, y, dtype, B, C, H, W, stream);
+}
+
+int gspn_prop2d_4dir_ex(const void* x, const void* lam, const void* u, const void* w_raw4,
+                        int64_t groups, int64_t k_chunk, float eps, void* y, int dtype,
+                        int64_t B, int64_t C, int64_t H, int64_t W, void* stream) {
     if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
     if (int s = check_dims(B, C, H, W, 12)) return s;
     if (H * W > gspn::prop2d_max_plane(dtype, H, W)) return GSPN_ERR_SHAPE;
+    if (groups < 1 || groups > C || C % groups != 0) return GSPN_ERR_SHAPE;
+    if (k_chunk < 1) return GSPN_ERR_VALUE;
     if (!valid_eps(eps)) return GSPN_ERR_VALUE;
     if (!x || !lam || !u || !w_raw4 || !y) return GSPN_ERR_NULL;
     if (!aligned(x, dtype) || !aligned(lam, dtype) || !aligned(u, dtype) ||
         !aligned(w_raw4, dtype) || !aligned(y, dtype))
         return GSPN_ERR_ALIGN;
     const int64_t n = B * C * H * W * elem_size(dtype);
+    const int64_t taps = 12 * B * groups * H * W * elem_size(dtype);
     if (overlap(y, n, x, n) || overlap(y, n, lam, n) || overlap(y, n, u, n) ||
-        overlap(y, n, w_raw4, 12 * n))
+        overlap(y, n, w_raw4, taps))
         return GSPN_ERR_ALIAS;
-    return launch_status(gspn::launch_prop2d(x, lam, u, w_raw4, eps, y, dtype, B * C, H, W,
+    gspn::PropOpts opts;
+    opts.cpg = C / groups;
+    // any count at or above a scan's line count cuts it into single lines
+    opts.k_chunk = std::min<int64_t>(k_chunk, std::max(H, W));
+    return launch_status(gspn::launch_prop2d(x, lam, u, w_raw4, eps, y, dtype, B * C, H, W, opts,
                                              static_cast<hipStream_t>(stream)));
 }
 

@@ -10,6 +10,14 @@ namespace gspn {
 // LDS a single workgroup may address on gfx950 (160 KiB per CU).
 constexpr int64_t kLdsBytes = 160 * 1024;
 
+// Options of the four-direction propagation: channels per tap group (taps
+// are [4][planes / cpg][3][..][..]; tap plane of plane p is p / cpg) and the
+// number of segments each scan is cut into.
+struct PropOpts {
+    int64_t cpg = 1;
+    int64_t k_chunk = 1;
+};
+
 // Launchers.  Arguments are already validated; each enqueues work on
 // `stream` and returns the launch status.
 hipError_t launch_normalize(const void* w_raw, void* w_norm, int dtype, int64_t planes,
@@ -22,14 +30,14 @@ hipError_t launch_scan_dir(const void* x, const void* lam, const void* u, const 
 
 hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const void* w4,
                          float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
-                         hipStream_t stream);
+                         const PropOpts& opts, hipStream_t stream);
 
 // Fast path of gspn_prop2d_4dir: two wavefronts per plane (gspn_prop2d_pair.hip).
 bool prop2d_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
                           const void* lam, const void* u, const void* w4, const void* y);
 hipError_t launch_prop2d_pair(const void* x, const void* lam, const void* u, const void* w4,
                               float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
-                              hipStream_t stream);
+                              const PropOpts& opts, hipStream_t stream);
 
 // Gradient of gspn_prop2d_4dir (gspn_backward.hip).  ws is NULL when the
 // three fp32 planes of a workgroup fit in LDS, else planes * 3 * H * W floats.

@@ -52,11 +52,13 @@ normalize_kernel(const T* __restrict__ w_raw, T* __restrict__ w_norm, int64_t pl
 // Scans direction `dir` of the plane whose inputs start at xp/lp/up/wp.  For
 // every produced value h at pixel `pix`, calls sink(pix, h).  h_prev and
 // h_next are LDS lines of at least L floats.  Ends with a barrier.
+// The lines are scanned in segments of `seg` lines (seg = NL: one global
+// scan); the first line of a segment in scan order is lambda x.
 template <typename T, typename Sink>
 __device__ __forceinline__ void scan_plane(const T* __restrict__ xp, const T* __restrict__ lp,
                                            const T* __restrict__ wp, bool w_is_raw, float eps,
-                                           int H, int W, int dir, float* h_prev, float* h_next,
-                                           Sink sink) {
+                                           int H, int W, int dir, int seg, float* h_prev,
+                                           float* h_next, Sink sink) {
     const bool rows = dir < 2;
     const int NL = rows ? H : W;
     const int L = rows ? W : H;
@@ -64,13 +66,14 @@ __device__ __forceinline__ void scan_plane(const T* __restrict__ xp, const T* __
     const size_t npix = static_cast<size_t>(H) * W;
     for (int step = 0; step < NL; ++step) {
         const int i = forward ? step : NL - 1 - step;
+        const bool restart = forward ? i % seg == 0 : (i == NL - 1 || (i + 1) % seg == 0);
         for (int p = threadIdx.x; p < L; p += kThreads) {
             const int r = rows ? i : p;
             const int c = rows ? p : i;
             const size_t pix = static_cast<size_t>(r) * W + c;
             const float bx = load_elem(lp, pix) * load_elem(xp, pix);
             float h = bx;
-            if (step > 0) {
+            if (!restart) {
                 const size_t ti = static_cast<size_t>(i) * L + p;
                 const bool has_left = p > 0;
                 const bool has_right = p < L - 1;
@@ -105,7 +108,7 @@ scan_dir_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __r
     const T* up = u + plane * npix;
     T* yp = y + plane * npix;
     scan_plane(x + plane * npix, lam + plane * npix, w + plane * 3 * npix, w_is_raw != 0, eps, H,
-               W, dir, lds, lds + L, [&](size_t pix, float h) {
+               W, dir, dir < 2 ? H : W, lds, lds + L, [&](size_t pix, float h) {
                    float o = load_elem(up, pix) * h;
                    if (accumulate) o = load_elem(yp, pix) + o;
                    store_elem(yp, pix, o);
@@ -118,7 +121,7 @@ template <typename T, bool kAccInLds>
 __global__ void __launch_bounds__(kThreads)
 prop2d_plane_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __restrict__ u,
                     const T* __restrict__ w4, float eps, T* __restrict__ y, int64_t planes, int H,
-                    int W) {
+                    int W, int64_t cpg, int k_chunk) {
     extern __shared__ float lds[];
     const int Lmax = H > W ? H : W;
     const size_t npix = static_cast<size_t>(H) * W;
@@ -130,13 +133,19 @@ prop2d_plane_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
         static_assert(sizeof(T) == sizeof(float), "global accumulation needs fp32 output");
         acc = reinterpret_cast<float*>(y + plane * npix);
     }
+    // tap plane of this plane: its channel group's
+    const size_t tap_planes = static_cast<size_t>(planes / cpg);
+    const size_t tplane = plane / static_cast<size_t>(cpg);
+    const int seg_rows = (H + k_chunk - 1) / k_chunk;
+    const int seg_cols = (W + k_chunk - 1) / k_chunk;
     for (int dir = 0; dir < 4; ++dir) {
-        const T* wp = w4 + (static_cast<size_t>(dir) * planes + plane) * 3 * npix;
+        const T* wp = w4 + (static_cast<size_t>(dir) * tap_planes + tplane) * 3 * npix;
+        const int seg = dir < 2 ? seg_rows : seg_cols;
         if (dir == 0) {
-            scan_plane(x + plane * npix, lam + plane * npix, wp, true, eps, H, W, dir, lds,
+            scan_plane(x + plane * npix, lam + plane * npix, wp, true, eps, H, W, dir, seg, lds,
                        lds + Lmax, [&](size_t pix, float h) { acc[pix] = h; });
         } else {
-            scan_plane(x + plane * npix, lam + plane * npix, wp, true, eps, H, W, dir, lds,
+            scan_plane(x + plane * npix, lam + plane * npix, wp, true, eps, H, W, dir, seg, lds,
                        lds + Lmax, [&](size_t pix, float h) { acc[pix] += h; });
         }
     }
@@ -188,7 +197,8 @@ size_t prop2d_lds_bytes(int64_t H, int64_t W) {
 
 template <typename T>
 hipError_t prop2d_t(const void* x, const void* lam, const void* u, const void* w4, float eps,
-                    void* y, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
+                    void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                    hipStream_t stream) {
     const size_t lds_acc = prop2d_lds_bytes(H, W);
     const bool in_lds = static_cast<int64_t>(lds_acc) <= kLdsBytes;
     const dim3 grid(static_cast<unsigned>(planes));
@@ -198,7 +208,7 @@ hipError_t prop2d_t(const void* x, const void* lam, const void* u, const void* w
         prop2d_plane_kernel<T, true><<<grid, dim3(kThreads), lds_acc, stream>>>(
             static_cast<const T*>(x), static_cast<const T*>(lam), static_cast<const T*>(u),
             static_cast<const T*>(w4), eps, static_cast<T*>(y), planes, static_cast<int>(H),
-            static_cast<int>(W));
+            static_cast<int>(W), o.cpg, static_cast<int>(o.k_chunk));
     } else {
         if constexpr (sizeof(T) != sizeof(float)) {
             return hipErrorInvalidValue;  // rejected earlier by prop2d_max_plane
@@ -209,7 +219,7 @@ hipError_t prop2d_t(const void* x, const void* lam, const void* u, const void* w
             prop2d_plane_kernel<T, false><<<grid, dim3(kThreads), lds, stream>>>(
                 static_cast<const T*>(x), static_cast<const T*>(lam), static_cast<const T*>(u),
                 static_cast<const T*>(w4), eps, static_cast<T*>(y), planes,
-                static_cast<int>(H), static_cast<int>(W));
+                static_cast<int>(H), static_cast<int>(W), o.cpg, static_cast<int>(o.k_chunk));
         }
     }
     return hipGetLastError();
@@ -236,11 +246,11 @@ hipError_t launch_scan_dir(const void* x, const void* lam, const void* u, const 
 
 hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const void* w4,
                          float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
-                         hipStream_t stream) {
+                         const PropOpts& o, hipStream_t stream) {
     if (prop2d_pair_eligible(dtype, planes, H, W, x, lam, u, w4, y))
-        return launch_prop2d_pair(x, lam, u, w4, eps, y, dtype, planes, H, W, stream);
-    return dtype == 0 ? prop2d_t<float>(x, lam, u, w4, eps, y, planes, H, W, stream)
-                      : prop2d_t<uint16_t>(x, lam, u, w4, eps, y, planes, H, W, stream);
+        return launch_prop2d_pair(x, lam, u, w4, eps, y, dtype, planes, H, W, o, stream);
+    return dtype == 0 ? prop2d_t<float>(x, lam, u, w4, eps, y, planes, H, W, o, stream)
+                      : prop2d_t<uint16_t>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 int64_t prop2d_max_plane(int dtype, int64_t H, int64_t W) {

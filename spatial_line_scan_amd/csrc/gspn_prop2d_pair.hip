@@ -35,6 +35,12 @@
 // ahead with buffer loads, which return 0 for every dword outside the tensor
 // (offsets below its start wrap to large values and read as 0 too).
 //
+// Tap groups: plane p = b C + c reads the taps of tap plane p / (C / G) =
+// b G + c / (C / G) (channel-shared weights, paper text §4.2).  Chunked
+// scans (Chunked): the lines of a scan restart from h = 0 at the first line
+// of each segment of ceil(NL / k_chunk) lines in scan order, so that line is
+// lambda x (paper text §4.1, chunk index of the grid).
+//
 // Normalisation: s_k = 1 / (2^(-z_k log2 e) + c_k) with c_k = 1 for in-line
 // taps and +inf for dropped ones (s_k exactly 0), r = 1 / max(s_0 + s_1 + s_2,
 // eps), h = r (s_0 h_l + s_1 h_c + s_2 h_r) + lambda x.
@@ -129,12 +135,13 @@ struct PairLayout {
 };
 
 // OddH / OddW: the row / column scans have an odd number of lines.
-template <typename T, int K, int D, bool OddH, bool OddW>
+// Chunked: k_chunk > 1.
+template <typename T, int K, int D, bool OddH, bool OddW, bool Chunked>
 // Two wavefronts per SIMD: at most 256 VGPRs, so that three planes share a CU.
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
 prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __restrict__ u,
                    const T* __restrict__ w4, int w4_bytes, int xl_bytes, float eps,
-                   T* __restrict__ y, int planes, int H, int W) {
+                   T* __restrict__ y, int planes, int H, int W, int cpg, int k_chunk) {
     constexpr bool kBf16 = sizeof(T) == 2;
     constexpr int ES = sizeof(T);
     constexpr int NW = window_words<T, K>();
@@ -211,7 +218,9 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
     const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
     const uint32_t line_b = static_cast<uint32_t>(L) * ES;
     // offset of this lane's window in tap plane 0 of its direction
-    const uint32_t tap_b = static_cast<uint32_t>(((g * planes + plane) * 3) * HW) * ES + win_b;
+    const int tap_planes = planes / cpg;
+    const uint32_t tap_b =
+        static_cast<uint32_t>(((g * tap_planes + plane / cpg) * 3) * HW) * ES + win_b;
     // Row scans: x and lambda of the current row, same window.
     const uint32_t xl_row_b = static_cast<uint32_t>(pix0) * ES + win_b;
     // Column scans: x and lambda of rows K q + j, D columns per chunk.
@@ -316,6 +325,14 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
         // backward half's slots are moved by mid_off to the padding line after
         // the plane, which starts zeroed.
         const int mid = (NL - 1) / 2;
+        // Chunked scans: step of the next restart after step 0 (where h is
+        // still 0).  Forward lines restart at multiples of the segment
+        // length; backward ones at s = 0 and where NL - s is a multiple of it.
+        int seg = NL, next_restart = NL;
+        if constexpr (Chunked) {
+            seg = (NL + k_chunk - 1) / k_chunk;
+            next_restart = fwd ? seg : NL - ((NL - 1) / seg) * seg;
+        }
         uint32_t mid_off[K];
 #pragma unroll
         for (int j = 0; j < K; ++j)
@@ -376,6 +393,14 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
             }
             load_line(d);
 
+            if constexpr (Chunked) {
+                // lanes at a segment start go on from h = 0 (values that
+                // cross between the two halves meet dropped taps of weight 0)
+                const bool restart = s == next_restart;
+                next_restart = restart ? next_restart + seg : next_restart;
+#pragma unroll
+                for (int j = 0; j < K; ++j) h[j] = restart ? 0.0f : h[j];
+            }
             const float hl0 = from_prev(h[K - 1]);
             const float hrK = from_next(h[0]);
             float hn[K];
@@ -518,14 +543,15 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
     }
 }
 
-template <typename T, int K, bool OddH, bool OddW>
+template <typename T, int K, bool OddH, bool OddW, bool Chunked>
 hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, float eps,
-                    void* y, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
+                    void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                    hipStream_t stream) {
     // prefetch depth: D steps of every stream in registers
     constexpr int D = (sizeof(T) == 4 && K == 3) ? 4 : 8;
     const size_t lds =
         static_cast<size_t>(PairLayout(static_cast<int>(H), static_cast<int>(W)).words) * sizeof(float);
-    auto kern = prop2d_pair_kernel<T, K, D, OddH, OddW>;
+    auto kern = prop2d_pair_kernel<T, K, D, OddH, OddW, Chunked>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -535,33 +561,47 @@ hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w
     const int64_t n = planes * H * W;
     kern<<<dim3(static_cast<unsigned>(planes)), dim3(128), lds, stream>>>(
         static_cast<const T*>(x), static_cast<const T*>(lam), static_cast<const T*>(u),
-        static_cast<const T*>(w4), static_cast<int>(12 * n * sizeof(T)),
+        static_cast<const T*>(w4), static_cast<int>(12 * (n / o.cpg) * sizeof(T)),
         static_cast<int>(n * sizeof(T)), eps, static_cast<T*>(y), static_cast<int>(planes),
-        static_cast<int>(H), static_cast<int>(W));
+        static_cast<int>(H), static_cast<int>(W), static_cast<int>(o.cpg),
+        static_cast<int>(o.k_chunk));
     return hipGetLastError();
 }
 
-template <typename T, int K>
+template <typename T, int K, bool Chunked>
 hipError_t launch_parity(const void* x, const void* lam, const void* u, const void* w4, float eps,
-                         void* y, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
+                         void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                         hipStream_t stream) {
     if constexpr (sizeof(T) == 2) {  // bf16 shapes are even (eligibility)
-        return launch_k<T, K, false, false>(x, lam, u, w4, eps, y, planes, H, W, stream);
+        return launch_k<T, K, false, false, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
     } else {
         const bool oh = H & 1, ow = W & 1;
-        if (!oh && !ow) return launch_k<T, K, false, false>(x, lam, u, w4, eps, y, planes, H, W, stream);
-        if (oh && ow) return launch_k<T, K, true, true>(x, lam, u, w4, eps, y, planes, H, W, stream);
-        if (oh) return launch_k<T, K, true, false>(x, lam, u, w4, eps, y, planes, H, W, stream);
-        return launch_k<T, K, false, true>(x, lam, u, w4, eps, y, planes, H, W, stream);
+        if (!oh && !ow)
+            return launch_k<T, K, false, false, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        if (oh && ow)
+            return launch_k<T, K, true, true, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        if (oh)
+            return launch_k<T, K, true, false, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        return launch_k<T, K, false, true, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
     }
+}
+
+template <typename T, bool Chunked>
+hipError_t launch_c(const void* x, const void* lam, const void* u, const void* w4, float eps,
+                    void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                    hipStream_t stream) {
+    const int64_t Lmax = H > W ? H : W;
+    if (Lmax <= 32) return launch_parity<T, 1, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (Lmax <= 64) return launch_parity<T, 2, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    return launch_parity<T, 3, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 template <typename T>
 hipError_t launch_t(const void* x, const void* lam, const void* u, const void* w4, float eps,
-                    void* y, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
-    const int64_t Lmax = H > W ? H : W;
-    if (Lmax <= 32) return launch_parity<T, 1>(x, lam, u, w4, eps, y, planes, H, W, stream);
-    if (Lmax <= 64) return launch_parity<T, 2>(x, lam, u, w4, eps, y, planes, H, W, stream);
-    return launch_parity<T, 3>(x, lam, u, w4, eps, y, planes, H, W, stream);
+                    void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                    hipStream_t stream) {
+    return o.k_chunk > 1 ? launch_c<T, true>(x, lam, u, w4, eps, y, planes, H, W, o, stream)
+                         : launch_c<T, false>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -587,9 +627,9 @@ bool prop2d_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const
 
 hipError_t launch_prop2d_pair(const void* x, const void* lam, const void* u, const void* w4,
                               float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
-                              hipStream_t stream) {
-    return dtype == 0 ? launch_t<float>(x, lam, u, w4, eps, y, planes, H, W, stream)
-                      : launch_t<uint16_t>(x, lam, u, w4, eps, y, planes, H, W, stream);
+                              const PropOpts& o, hipStream_t stream) {
+    return dtype == 0 ? launch_t<float>(x, lam, u, w4, eps, y, planes, H, W, o, stream)
+                      : launch_t<uint16_t>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 }  // namespace gspn

@@ -11,6 +11,8 @@ Tensor layouts (see include/gspn.h):
   taps of a direction  B*C*3*H*W elements, laid out [B][C][3][lines][length]
       (TD/BU: lines are rows; LR/RL: lines are columns, i.e. transposed)
   w4             4*B*C*3*H*W elements, directions in the order TD, BU, LR, RL
+  grouped taps   4*B*G*3*H*W elements ([4][B][G][3][..][..]); channel c reads
+                 group c // (C // G)
 """
 from __future__ import annotations
 
@@ -52,6 +54,9 @@ def lib():
         L.gspn_scan_dir.restype = ci
         L.gspn_prop2d_4dir.argtypes = [vp, vp, vp, vp, cf, vp, ci, i64, i64, i64, i64, vp]
         L.gspn_prop2d_4dir.restype = ci
+        L.gspn_prop2d_4dir_ex.argtypes = [vp, vp, vp, vp, i64, i64, cf, vp, ci, i64, i64, i64,
+                                          i64, vp]
+        L.gspn_prop2d_4dir_ex.restype = ci
         L.gspn_prop2d_4dir_backward.argtypes = [vp, vp, vp, vp, vp, cf, vp, vp, vp, vp, vp, i64,
                                                 ci, i64, i64, i64, i64, vp]
         L.gspn_prop2d_4dir_backward.restype = ci
@@ -150,6 +155,31 @@ def prop2d_4dir(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4: torch.T
     with torch.cuda.device(x.device):
         _check(lib().gspn_prop2d_4dir(_p(x), _p(lam), _p(u), _p(w4), float(eps), _p(out),
                                       _dtype_code(x), B, C, H, W, _stream(x)))
+    return out
+
+
+def prop2d_4dir_ex(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4: torch.Tensor,
+                   groups: int, k_chunk: int = 1, eps: float = 1e-6,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """prop2d_4dir with taps shared by `groups` contiguous channel groups and
+    each scan cut into k_chunk segments (include/gspn.h)."""
+    _same(x, lam, u, w4)
+    if x.dim() != 4 or lam.shape != x.shape or u.shape != x.shape:
+        raise ValueError("x, lam, u must share one [B, C, H, W] shape")
+    B, C, H, W = x.shape
+    if groups < 1 or C % groups:
+        raise ValueError("groups must divide C")
+    if w4.numel() != 12 * B * groups * H * W:
+        raise ValueError("w4 must hold 4*B*groups*3*H*W elements")
+    if out is None:
+        out = torch.empty_like(x)
+    _same(x, out)
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    with torch.cuda.device(x.device):
+        _check(lib().gspn_prop2d_4dir_ex(_p(x), _p(lam), _p(u), _p(w4), int(groups), int(k_chunk),
+                                         float(eps), _p(out), _dtype_code(x), B, C, H, W,
+                                         _stream(x)))
     return out
 
 

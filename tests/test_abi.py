@@ -41,13 +41,14 @@ def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
     assert set(syms) >= {"gspn_abi_version", "gspn_status_str", "gspn_normalize_weights",
                          "gspn_scan_dir", "gspn_prop2d_4dir",
-                         "gspn_prop2d_4dir_backward", "gspn_prop2d_4dir_backward_workspace"}
+                         "gspn_prop2d_4dir_backward", "gspn_prop2d_4dir_backward_workspace",
+                         "gspn_prop2d_4dir_ex"}
     for s in syms:
         assert hasattr(L, s), s
 
 
 def test_version_and_status_strings(L):
-    assert L.gspn_abi_version() == 2
+    assert L.gspn_abi_version() == 3
     for s in range(9):
         assert L.gspn_status_str(s).decode().startswith("GSPN")
     assert L.gspn_status_str(12345)
@@ -206,3 +207,30 @@ def test_backward_workspace_checks(L):
     assert bwd(L, ws=P(0), ws_bytes=need, H=120, W=120) == ALIAS        # over x
     assert bwd(L, ws=P(7), ws_bytes=need, H=120, W=120) == ALIAS        # over gu
     assert bwd(L, ws_bytes=-1) == SHAPE
+
+
+def ex(L, groups=3, k=1, eps=1e-6, dt=0, B=2, C=3, H=5, W=7, y=None):
+    return L.gspn_prop2d_4dir_ex(P(0), P(1), P(2), P(3), groups, k, eps, y or P(5), dt, B, C, H, W,
+                                 None)
+
+
+def test_ex_rejects_bad_groups_and_chunks(L):
+    assert ex(L, groups=2) == SHAPE          # 2 does not divide 3
+    assert ex(L, groups=0) == SHAPE
+    assert ex(L, groups=6) == SHAPE
+    assert ex(L, groups=-3) == SHAPE
+    assert ex(L, k=0) == VALUE
+    assert ex(L, k=-2) == VALUE
+    assert ex(L, dt=2) == DTYPE
+    assert ex(L, eps=0.0) == VALUE
+    assert ex(L, B=0) == SHAPE
+
+
+def test_ex_alias_extent_follows_groups(L):
+    # groups = 1: the taps take 12 * B * H * W elements and an output starting
+    # on their last element is an alias; with groups = C the tap tensor is
+    # three times larger and the address just past the grouped one is inside
+    taps = 12 * 2 * 1 * 5 * 7 * 4
+    assert ex(L, groups=1, y=ctypes.c_void_p(A + 3 * STEP + taps - 4)) == ALIAS
+    assert ex(L, groups=3, y=ctypes.c_void_p(A + 3 * STEP + taps)) == ALIAS
+    assert ex(L, y=P(0)) == ALIAS
