@@ -19,6 +19,9 @@ prop2d_backward(x, lam, u, w4, gy, eps)   -> (gx, glam, gu, gw4), the gradient
 prop2d_ex(x, lam, u, w4g, groups, k_chunk, eps)
                                           -> prop2d with taps shared by groups of
                                              channels and/or chunked scans
+latent_sublayer(x_tok, p_down, w_param, p_up, H, W, groups, k_chunk, eps)
+                                          -> the latent propagation sublayer:
+                                             1x1 projections around prop2d_ex
 
 Layouts follow the C file's header: x, lam, u: [B][C][H][W]; the taps of one
 direction: [B][C][3][NL][L] indexed by (line, position) of that direction
@@ -174,3 +177,36 @@ def prop2d_ex(x, lam, u, w4g, groups: int, k_chunk: int = 1, eps: float = 1e-6) 
     if rc != 0:
         raise MemoryError("oracle propagation could not allocate scratch")
     return y
+
+
+def latent_sublayer(x_tok, p_down, w_param, p_up, H: int, W: int, groups: int, k_chunk: int = 1,
+                    eps: float = 1e-6) -> np.ndarray:
+    """Latent-space propagation sublayer (paper text §5.1; reading notes, key
+    design 1): tokens x_tok [B][H*W][C] are projected to Cc latent channels
+    by the 1x1 convolution p_down [Cc][C]; per-position propagation
+    parameters come from the 1x1 convolution w_param [2 Cc + 12 G][Cc] of
+    the latent (rows: lambda for the Cc channels, u for the Cc channels,
+    then the raw taps in [direction TD, BU, LR, RL][group][tap] order); the
+    latent is propagated in four directions (prop2d_ex, G tap groups,
+    k_chunk segments) and projected back by p_up [C][Cc].  Returns
+    y_tok [B][H*W][C] in fp64.  Every matrix product is a plain numpy
+    matmul in fp64."""
+    x_tok, p_down, w_param, p_up = _f64(x_tok), _f64(p_down), _f64(w_param), _f64(p_up)
+    B, N, C = x_tok.shape
+    Cc = p_down.shape[0]
+    G = groups
+    assert N == H * W and p_down.shape == (Cc, C) and p_up.shape == (C, Cc)
+    assert w_param.shape == (2 * Cc + 12 * G, Cc)
+    z = np.matmul(p_down, np.transpose(x_tok, (0, 2, 1)))          # [B][Cc][N]
+    par = np.matmul(w_param, z)                                      # [B][2Cc+12G][N]
+    lam = par[:, :Cc].reshape(B, Cc, H, W)
+    u = par[:, Cc:2 * Cc].reshape(B, Cc, H, W)
+    taps = par[:, 2 * Cc:].reshape(B, 4, G, 3, H, W)
+    w4 = np.empty((4, B, G, 3, H * W))
+    for d in range(4):
+        t = taps[:, d]
+        if d in (LR, RL):             # column-major lines: [3][W][H]
+            t = np.transpose(t, (0, 1, 2, 4, 3))
+        w4[d] = t.reshape(B, G, 3, H * W)
+    yc = prop2d_ex(z.reshape(B, Cc, H, W), lam, u, w4, G, k_chunk, eps)
+    return np.matmul(yc.reshape(B, Cc, N).transpose(0, 2, 1), p_up.T)  # [B][N][C]
