@@ -19,6 +19,11 @@ variants  : gspn_prop2d_4dir_ex on the same workload shape, timed the same
             way (not part of `value`): taps shared by all channels of an image
             (groups = 1; algorithmic bytes 4 + 12 G / C values per
             pixel-channel) and a chunked scan (k_chunk = 4, per-channel taps)
+sublayer  : gspn_latent_sublayer (P_down, parameter 1x1 convolutions, scan,
+            P_up) on the pages' 1K shape: B=32 images of 74 x 74 tokens, C=1152
+            compressed to Cc=64, bf16; per-channel taps (G = 64) and shared taps
+            (G = 1).  Bytes: tokens in + tokens out (the least any
+            implementation moves)
 backward  : the gradient entry point (gspn_prop2d_4dir_backward) on the same
             workload and rotated sets, timed the same way (not part of
             `value`); algorithmic bytes = 31 values per pixel-channel (read x,
@@ -179,6 +184,37 @@ def variant_leg(wl, args, dev, G, k):
                          "kernel_ms_avg": round(kavg, 5), "kernel_ms_min": round(kmin, 5)}}
 
 
+def sublayer_leg(args, dev, G, B=32, C=1152, Cc=64, H=74, W=74):
+    """gspn_latent_sublayer at the pages' 1K shape (bf16), over rotated token sets."""
+    import numpy as np
+    import torch
+
+    from spatial_line_scan_amd import gspn, inputs
+
+    base = inputs.sublayer_problem_torch(B, C, Cc, G, H, W, 0, "bf16", dev)
+    tok_bytes = B * H * W * C * 2
+    nbytes = 2 * tok_bytes
+    nsets = max(1, int(np.ceil(args.rotate_bytes / nbytes)))
+    toks = [base["x_tok"]] + [base["x_tok"].clone() for _ in range(nsets - 1)]
+    outs = [torch.empty_like(base["x_tok"]) for _ in range(nsets)]
+    need = gspn.latent_sublayer_workspace_bytes(torch.bfloat16, B, C, Cc, G, H, W)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def fn(i):
+        gspn.latent_sublayer(toks[i % nsets], base["p_down"], base["w_param"], base["p_up"], H, W,
+                             G, 1, workspace=ws, out=outs[i % nsets])
+
+    wall, kavg, kmin = _timed(fn, args.steps, args.warmup, torch.cuda.current_stream(dev))
+    del toks, outs, ws
+    torch.cuda.empty_cache()
+    return {"groups": G, "B": B, "C": C, "Cc": Cc, "H": H, "W": W, "dtype": "bf16",
+            "ms_per_step": round(wall * 1e3 / args.steps, 5), "event_ms_avg": round(kavg, 5),
+            "event_ms_min": round(kmin, 5), "token_bytes_per_step": nbytes,
+            "token_GBps": round(nbytes / (kavg * 1e-3) / 1e9, 2), "rotated_token_sets": nsets,
+            "pages_sublayer_ms_A100": 0.18}
+
+
 def backward_leg(wl, sets, args, dev):
     """Warmup + K backward launches over the rotated sets: wall time and
     per-launch HIP-event durations on the launch stream."""
@@ -261,6 +297,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-variants", action="store_true", help="skip the grouped / chunked legs")
+    ap.add_argument("--no-sublayer", action="store_true", help="skip the latent sublayer legs")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only warmup + K backward launches and print their timing "
                          "(for profiling the backward kernel on its own)")
@@ -380,6 +417,9 @@ def main():
     if not args.no_variants:
         print("bench: variants", file=sys.stderr, flush=True)
         out["variants"] = [variant_leg(wl, args, dev, G, k) for G, k in ((1, 1), (wl.C, 4))]
+    if not args.no_sublayer and wl.name == "latent1k":
+        print("bench: sublayer", file=sys.stderr, flush=True)
+        out["sublayer"] = [sublayer_leg(args, dev, G) for G in (64, 1)]
     if not args.no_backward:
         print("bench: backward", file=sys.stderr, flush=True)
         out["backward"] = backward_leg(wl, sets, args, dev)

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 3
+#define GSPN_ABI_VERSION 4
 
 /* Longest line (H or W) any entry point accepts. */
 #define GSPN_MAX_LINE 8192
@@ -194,6 +194,40 @@ int gspn_prop2d_4dir_backward(const void* x, const void* lam, const void* u,
 /* Workspace bytes gspn_prop2d_4dir_backward needs for these sizes (0 if
  * none), or -1 if it does not accept them. */
 int64_t gspn_prop2d_4dir_backward_workspace(int64_t B, int64_t C, int64_t H, int64_t W);
+
+/*
+ * Latent-space propagation sublayer (paper §5.1, a more efficient ViT block:
+ * propagation in a compressed latent; reading notes, key design 1): the
+ * four-direction propagation wrapped in its 1x1 projections.
+ *   z      = P_down x            per token: Cc latent channels from C
+ *   lambda = W_lambda z,  u = W_u z,  w_raw = W_taps z   (1x1 convolutions
+ *            of the latent: the propagation parameters are per-position)
+ *   y_c    = gspn_prop2d_4dir_ex(z, lambda, u, w_raw, groups, k_chunk)
+ *   y      = P_up y_c            per token: C channels from Cc
+ *   x_tok, y_tok : [B][H*W][C] tokens (row-major grid, channels last).
+ *   p_down  : [Cc][C];   p_up : [C][Cc];
+ *   w_param : [2 Cc + 12 groups][Cc], rows lambda (Cc), u (Cc), then the raw
+ *             taps in [direction TD, BU, LR, RL][group][tap k] order.
+ *   workspace : at least gspn_latent_sublayer_workspace(...) bytes; holds the
+ *             latent, its parameters, the scan output and the GEMM library's
+ *             scratch; contents on return are unspecified.
+ *   All pointers 16-byte aligned; y_tok and workspace must not overlap any
+ *   input or each other.  The projections run in hipBLASLt (fp32
+ *   accumulation; bf16 storage rounds every intermediate to bf16), one
+ *   algorithm per shape chosen on first use, so repeated calls give
+ *   bitwise equal results.  Errors as gspn_prop2d_4dir_ex, plus
+ *   GSPN_ERR_SHAPE for a workspace that is too small or C outside
+ *   [1, 65536].
+ */
+int gspn_latent_sublayer(const void* x_tok, const void* p_down, const void* w_param,
+                         const void* p_up, int64_t groups, int64_t k_chunk, float eps,
+                         void* y_tok, void* workspace, int64_t workspace_bytes, int dtype,
+                         int64_t B, int64_t C, int64_t Cc, int64_t H, int64_t W, void* stream);
+
+/* Workspace bytes gspn_latent_sublayer needs, or -1 if it does not accept
+ * these sizes. */
+int64_t gspn_latent_sublayer_workspace(int dtype, int64_t B, int64_t C, int64_t Cc,
+                                       int64_t groups, int64_t H, int64_t W);
 
 #ifdef __cplusplus
 }

@@ -179,8 +179,24 @@ def prop2d_ex(x, lam, u, w4g, groups: int, k_chunk: int = 1, eps: float = 1e-6) 
     return y
 
 
+def _to_storage(a: np.ndarray, storage: str | None) -> np.ndarray:
+    """Values of `a` once stored as `storage` (None: kept in fp64).  fp32:
+    round to nearest even; bf16: to fp32, then to the nearest even bf16 (the
+    upper 16 bits of the fp32 pattern after adding 0x7fff plus the lowest kept
+    bit), as a tensor of that type written from an fp32 result holds."""
+    if storage is None:
+        return a
+    f = np.ascontiguousarray(a, dtype=np.float32)
+    if storage == "fp32":
+        return f.astype(np.float64)
+    assert storage == "bf16"
+    bits = f.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
 def latent_sublayer(x_tok, p_down, w_param, p_up, H: int, W: int, groups: int, k_chunk: int = 1,
-                    eps: float = 1e-6) -> np.ndarray:
+                    eps: float = 1e-6, storage: str | None = None, with_scale: bool = False):
     """Latent-space propagation sublayer (paper text §5.1; reading notes, key
     design 1): tokens x_tok [B][H*W][C] are projected to Cc latent channels
     by the 1x1 convolution p_down [Cc][C]; per-position propagation
@@ -190,15 +206,19 @@ def latent_sublayer(x_tok, p_down, w_param, p_up, H: int, W: int, groups: int, k
     latent is propagated in four directions (prop2d_ex, G tap groups,
     k_chunk segments) and projected back by p_up [C][Cc].  Returns
     y_tok [B][H*W][C] in fp64.  Every matrix product is a plain numpy
-    matmul in fp64."""
+    matmul in fp64.  With `storage` ("fp32" or "bf16") the latent, the
+    parameters and the scan output are rounded to that type where a layer
+    storing its activations in it writes them (the inputs are taken as
+    given).  with_scale: also return |y_c^T| |p_up^T|, the componentwise
+    magnitudes of the output projection's terms."""
     x_tok, p_down, w_param, p_up = _f64(x_tok), _f64(p_down), _f64(w_param), _f64(p_up)
     B, N, C = x_tok.shape
     Cc = p_down.shape[0]
     G = groups
     assert N == H * W and p_down.shape == (Cc, C) and p_up.shape == (C, Cc)
     assert w_param.shape == (2 * Cc + 12 * G, Cc)
-    z = np.matmul(p_down, np.transpose(x_tok, (0, 2, 1)))          # [B][Cc][N]
-    par = np.matmul(w_param, z)                                      # [B][2Cc+12G][N]
+    z = _to_storage(np.matmul(p_down, np.transpose(x_tok, (0, 2, 1))), storage)   # [B][Cc][N]
+    par = _to_storage(np.matmul(w_param, z), storage)                # [B][2Cc+12G][N]
     lam = par[:, :Cc].reshape(B, Cc, H, W)
     u = par[:, Cc:2 * Cc].reshape(B, Cc, H, W)
     taps = par[:, 2 * Cc:].reshape(B, 4, G, 3, H, W)
@@ -208,5 +228,9 @@ def latent_sublayer(x_tok, p_down, w_param, p_up, H: int, W: int, groups: int, k
         if d in (LR, RL):             # column-major lines: [3][W][H]
             t = np.transpose(t, (0, 1, 2, 4, 3))
         w4[d] = t.reshape(B, G, 3, H * W)
-    yc = prop2d_ex(z.reshape(B, Cc, H, W), lam, u, w4, G, k_chunk, eps)
-    return np.matmul(yc.reshape(B, Cc, N).transpose(0, 2, 1), p_up.T)  # [B][N][C]
+    yc = _to_storage(prop2d_ex(z.reshape(B, Cc, H, W), lam, u, w4, G, k_chunk, eps), storage)
+    yt = yc.reshape(B, Cc, N).transpose(0, 2, 1)
+    y = np.matmul(yt, p_up.T)                                        # [B][N][C]
+    if with_scale:
+        return y, np.matmul(np.abs(yt), np.abs(p_up.T))
+    return y

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgspn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["gspn_host.cpp", "gspn_kernels.hip", "gspn_prop2d_pair.hip", "gspn_backward.hip"]
+SOURCES = ["gspn_host.cpp", "gspn_kernels.hip", "gspn_prop2d_pair.hip", "gspn_backward.hip",
+           "gspn_sublayer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -40,7 +41,8 @@ def build(verbose: bool = False) -> str:
         subprocess.check_call(cmd)
         objs.append(obj)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp,
+           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)

@@ -12,6 +12,8 @@
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+// token channels of the latent sublayer (1x1 projections C <-> Cc)
+constexpr int64_t kMaxTokenChannels = int64_t{1} << 16;
 
 int64_t elem_size(int dtype) { return dtype == GSPN_FP32 ? 4 : 2; }
 
@@ -176,6 +178,44 @@ int gspn_prop2d_4dir_backward(const void* x, const void* lam, const void* u,
     return launch_status(gspn::launch_prop2d_backward(
         x, lam, u, w_raw4, gy, eps, gx, glam, gu, gw4, need > 0 ? workspace : nullptr, dtype,
         B * C, H, W, static_cast<hipStream_t>(stream)));
+}
+
+int64_t gspn_latent_sublayer_workspace(int dtype, int64_t B, int64_t C, int64_t Cc,
+                                       int64_t groups, int64_t H, int64_t W) {
+    if (!valid_dtype(dtype)) return -1;
+    if (check_dims(B, Cc, H, W, 12) != GSPN_OK || C < 1 || C > kMaxTokenChannels) return -1;
+    if (groups < 1 || groups > Cc || Cc % groups != 0) return -1;
+    return gspn::latent_sublayer_workspace_bytes(dtype, B, Cc, groups, H, W);
+}
+
+int gspn_latent_sublayer(const void* x_tok, const void* p_down, const void* w_param,
+                         const void* p_up, int64_t groups, int64_t k_chunk, float eps,
+                         void* y_tok, void* workspace, int64_t workspace_bytes, int dtype,
+                         int64_t B, int64_t C, int64_t Cc, int64_t H, int64_t W, void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
+    if (int s = check_dims(B, Cc, H, W, 12)) return s;
+    if (C < 1 || C > kMaxTokenChannels) return GSPN_ERR_SHAPE;
+    if (H * W > gspn::prop2d_max_plane(dtype, H, W)) return GSPN_ERR_SHAPE;
+    if (groups < 1 || groups > Cc || Cc % groups != 0) return GSPN_ERR_SHAPE;
+    if (k_chunk < 1) return GSPN_ERR_VALUE;
+    if (!valid_eps(eps)) return GSPN_ERR_VALUE;
+    if (!x_tok || !p_down || !w_param || !p_up || !y_tok || !workspace) return GSPN_ERR_NULL;
+    const int64_t need = gspn::latent_sublayer_workspace_bytes(dtype, B, Cc, groups, H, W);
+    if (workspace_bytes < need) return GSPN_ERR_SHAPE;
+    const void* ptrs[] = {x_tok, p_down, w_param, p_up, y_tok, workspace};
+    for (const void* p : ptrs)
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return GSPN_ERR_ALIGN;
+    const int64_t es = elem_size(dtype);
+    const int64_t tok = B * H * W * C * es;
+    const void* ins[] = {x_tok, p_down, w_param, p_up};
+    const int64_t in_bytes[] = {tok, Cc * C * es, (2 * Cc + 12 * groups) * Cc * es, C * Cc * es};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(y_tok, tok, ins[i], in_bytes[i]) || overlap(workspace, need, ins[i], in_bytes[i]))
+            return GSPN_ERR_ALIAS;
+    if (overlap(y_tok, tok, workspace, need)) return GSPN_ERR_ALIAS;
+    return launch_status(gspn::launch_latent_sublayer(
+        x_tok, p_down, w_param, p_up, groups, std::min<int64_t>(k_chunk, std::max(H, W)), eps,
+        y_tok, workspace, dtype, B, C, Cc, H, W, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

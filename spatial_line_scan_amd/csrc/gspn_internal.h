@@ -49,6 +49,15 @@ int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W);
 // Longest line the backward's LDS lines allow.
 int64_t prop2d_backward_max_line();
 
+// Latent propagation sublayer (gspn_sublayer.hip): hipBLASLt 1x1 projections
+// around launch_prop2d.  ws holds latent_sublayer_workspace_bytes bytes.
+hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const void* w_param,
+                                  const void* p_up, int64_t G, int64_t k_chunk, float eps,
+                                  void* y_tok, void* ws, int dtype, int64_t B, int64_t C,
+                                  int64_t Cc, int64_t H, int64_t W, hipStream_t stream);
+int64_t latent_sublayer_workspace_bytes(int dtype, int64_t B, int64_t Cc, int64_t G, int64_t H,
+                                        int64_t W);
+
 // Largest plane (H * W pixels) gspn_prop2d_4dir accepts for an element type.
 int64_t prop2d_max_plane(int dtype, int64_t H, int64_t W);
 

@@ -57,6 +57,11 @@ def lib():
         L.gspn_prop2d_4dir_ex.argtypes = [vp, vp, vp, vp, i64, i64, cf, vp, ci, i64, i64, i64,
                                           i64, vp]
         L.gspn_prop2d_4dir_ex.restype = ci
+        L.gspn_latent_sublayer.argtypes = [vp, vp, vp, vp, i64, i64, cf, vp, vp, i64, ci, i64,
+                                           i64, i64, i64, i64, vp]
+        L.gspn_latent_sublayer.restype = ci
+        L.gspn_latent_sublayer_workspace.argtypes = [ci, i64, i64, i64, i64, i64, i64]
+        L.gspn_latent_sublayer_workspace.restype = i64
         L.gspn_prop2d_4dir_backward.argtypes = [vp, vp, vp, vp, vp, cf, vp, vp, vp, vp, vp, i64,
                                                 ci, i64, i64, i64, i64, vp]
         L.gspn_prop2d_4dir_backward.restype = ci
@@ -233,3 +238,43 @@ class Prop2d4Dir(torch.autograd.Function):
         x, lam, u, w4 = ctx.saved_tensors
         gx, glam, gu, gw4 = prop2d_4dir_backward(x, lam, u, w4, gy.contiguous(), ctx.eps)
         return gx, glam, gu, gw4, None
+
+
+def latent_sublayer_workspace_bytes(dtype: torch.dtype, B: int, C: int, Cc: int, groups: int,
+                                    H: int, W: int) -> int:
+    code = FP32 if dtype == torch.float32 else BF16
+    n = lib().gspn_latent_sublayer_workspace(code, B, C, Cc, groups, H, W)
+    if n < 0:
+        raise ValueError("sizes not accepted by gspn_latent_sublayer")
+    return n
+
+
+def latent_sublayer(x_tok: torch.Tensor, p_down: torch.Tensor, w_param: torch.Tensor,
+                    p_up: torch.Tensor, H: int, W: int, groups: int, k_chunk: int = 1,
+                    eps: float = 1e-6, workspace: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """Latent propagation sublayer on tokens [B][H*W][C] (include/gspn.h):
+    P_down, the 1x1 parameter convolutions, the four-direction scan and P_up.
+    The workspace (bytes) is allocated here with torch when none is given."""
+    _same(x_tok, p_down, w_param, p_up)
+    if x_tok.dim() != 3 or x_tok.shape[1] != H * W:
+        raise ValueError("x_tok must be [B, H*W, C]")
+    B, _, C = x_tok.shape
+    Cc = p_down.shape[0]
+    if p_down.shape != (Cc, C) or p_up.shape != (C, Cc) or \
+            w_param.shape != (2 * Cc + 12 * groups, Cc):
+        raise ValueError("weights must be p_down [Cc, C], w_param [2Cc+12G, Cc], p_up [C, Cc]")
+    need = latent_sublayer_workspace_bytes(x_tok.dtype, B, C, Cc, groups, H, W)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_tok.device)
+    if workspace.device != x_tok.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on x_tok's device")
+    if out is None:
+        out = torch.empty_like(x_tok)
+    _same(x_tok, out)
+    with torch.cuda.device(x_tok.device):
+        _check(lib().gspn_latent_sublayer(
+            _p(x_tok), _p(p_down), _p(w_param), _p(p_up), int(groups), int(k_chunk), float(eps),
+            _p(out), _p(workspace), workspace.numel() * workspace.element_size(),
+            _dtype_code(x_tok), B, C, Cc, H, W, _stream(x_tok)))
+    return out

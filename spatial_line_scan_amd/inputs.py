@@ -19,7 +19,10 @@ Storage rounding: fp32 tensors hold float32(z) (round to nearest even);
 bf16 tensors hold bf16(float32(z)) (round to nearest even on the fp32 bits).
 
 Tensor ids: x = 0, lambda = 1, u = 2, taps of all four directions = 3,
-upstream gradient gy (dL/dy, for the backward) = 4.
+upstream gradient gy (dL/dy, for the backward) = 4; latent sublayer: tokens
+x_tok = 5, p_down = 6, w_param = 7, p_up = 8 (each weight matrix is drawn
+N(0, 1), scaled by 1 / sqrt(its fan-in) in float32, then rounded to the
+storage type).
 """
 from __future__ import annotations
 
@@ -29,7 +32,8 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-TENSOR_IDS = {"x": 0, "lam": 1, "u": 2, "w": 3, "gy": 4}
+TENSOR_IDS = {"x": 0, "lam": 1, "u": 2, "w": 3, "gy": 4, "x_tok": 5, "p_down": 6, "w_param": 7,
+              "p_up": 8}
 _CHUNK = 1 << 22
 
 
@@ -195,3 +199,16 @@ def to_torch(a: np.ndarray, dtype: str, device="cpu"):
     else:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32).copy())
     return t.reshape(a.shape).to(device)
+
+
+def sublayer_problem_torch(B: int, C: int, Cc: int, G: int, H: int, W: int, seed: int, dtype: str,
+                           device) -> dict:
+    """Inputs of one latent sublayer call: tokens [B][H*W][C] and the three
+    weight matrices, drawn on `device`."""
+    import torch
+    out = {"x_tok": draw_torch(seed, "x_tok", (B, H * W, C), dtype, device)}
+    for name, shape, fan_in in (("p_down", (Cc, C), C), ("w_param", (2 * Cc + 12 * G, Cc), Cc),
+                                ("p_up", (C, Cc), Cc)):
+        w = draw_torch(seed, name, shape, "fp32", device) * np.float32(1.0 / np.sqrt(fan_in))
+        out[name] = w.to(torch.bfloat16) if dtype == "bf16" else w
+    return out

@@ -42,13 +42,14 @@ def test_exports_every_declared_symbol(L):
     assert set(syms) >= {"gspn_abi_version", "gspn_status_str", "gspn_normalize_weights",
                          "gspn_scan_dir", "gspn_prop2d_4dir",
                          "gspn_prop2d_4dir_backward", "gspn_prop2d_4dir_backward_workspace",
-                         "gspn_prop2d_4dir_ex"}
+                         "gspn_prop2d_4dir_ex", "gspn_latent_sublayer",
+                         "gspn_latent_sublayer_workspace"}
     for s in syms:
         assert hasattr(L, s), s
 
 
 def test_version_and_status_strings(L):
-    assert L.gspn_abi_version() == 3
+    assert L.gspn_abi_version() == 4
     for s in range(9):
         assert L.gspn_status_str(s).decode().startswith("GSPN")
     assert L.gspn_status_str(12345)
@@ -234,3 +235,46 @@ def test_ex_alias_extent_follows_groups(L):
     assert ex(L, groups=1, y=ctypes.c_void_p(A + 3 * STEP + taps - 4)) == ALIAS
     assert ex(L, groups=3, y=ctypes.c_void_p(A + 3 * STEP + taps)) == ALIAS
     assert ex(L, y=P(0)) == ALIAS
+
+
+def sub(L, ptrs=None, groups=4, k=1, eps=1e-6, ws_bytes=None, dt=0, B=2, C=12, Cc=4, H=5, W=7):
+    p = list(ptrs) if ptrs else [P(i) for i in range(6)]
+    if ws_bytes is None:
+        ws_bytes = L.gspn_latent_sublayer_workspace(dt, B, C, Cc, groups, H, W)
+    return L.gspn_latent_sublayer(p[0], p[1], p[2], p[3], groups, k, eps, p[4], p[5], ws_bytes, dt,
+                                  B, C, Cc, H, W, None)
+
+
+def test_sublayer_workspace_query(L):
+    n = L.gspn_latent_sublayer_workspace(1, 32, 1152, 64, 64, 74, 74)
+    plane = 32 * 64 * 74 * 74 * 2
+    assert n >= (5 + 12) * plane and n <= (5 + 12) * plane + (64 << 20)
+    assert L.gspn_latent_sublayer_workspace(1, 32, 1152, 64, 1, 74, 74) < n
+    assert L.gspn_latent_sublayer_workspace(2, 1, 8, 4, 4, 5, 5) == -1
+    assert L.gspn_latent_sublayer_workspace(0, 1, 8, 4, 3, 5, 5) == -1      # 3 does not divide 4
+    assert L.gspn_latent_sublayer_workspace(0, 1, 1 << 17, 4, 4, 5, 5) == -1
+
+
+def test_sublayer_rejects_bad_arguments(L):
+    assert sub(L, dt=2) == DTYPE
+    assert sub(L, groups=3) == SHAPE
+    assert sub(L, C=0) == SHAPE
+    assert sub(L, k=0) == VALUE
+    assert sub(L, eps=float("inf")) == VALUE
+    need = L.gspn_latent_sublayer_workspace(0, 2, 12, 4, 4, 5, 7)
+    assert sub(L, ws_bytes=need - 1) == SHAPE
+    for i in range(6):
+        ptrs = [P(j) for j in range(6)]
+        ptrs[i] = ctypes.c_void_p(0)
+        assert sub(L, ptrs) == NULL
+        ptrs[i] = ctypes.c_void_p(A + i * STEP + 8)        # 16-byte alignment required
+        assert sub(L, ptrs) == ALIGN
+    ptrs = [P(j) for j in range(6)]
+    ptrs[4] = P(0)                                          # output over the tokens
+    assert sub(L, ptrs) == ALIAS
+    ptrs = [P(j) for j in range(6)]
+    ptrs[5] = P(2)                                          # workspace over w_param
+    assert sub(L, ptrs) == ALIAS
+    ptrs = [P(j) for j in range(6)]
+    ptrs[4] = P(5)                                          # output over the workspace
+    assert sub(L, ptrs) == ALIAS

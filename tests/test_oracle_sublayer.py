@@ -8,7 +8,9 @@ properties the definition fixes:
     (this pins the column-major tap planes of LR / RL);
   - with every scan cut into single lines (k_chunk >= H, W) each direction
     returns lambda * z, so y = p_up (4 u lambda z) per token;
-  - linearity in p_up.
+  - linearity in p_up;
+  - storage rounding: exact on values the storage type holds, round to
+    nearest even on halfway cases, and within half an ulp otherwise.
 """
 import numpy as np
 import pytest
@@ -62,7 +64,8 @@ SUBLAYER_MUTANTS = [
     ("tap rows read group-major", "taps = par[:, 2 * Cc:].reshape(B, 4, G, 3, H, W)",
      "taps = par[:, 2 * Cc:].reshape(B, G, 4, 3, H, W).transpose(0, 2, 1, 3, 4, 5)"),
     ("u taken from the lambda rows", "u = par[:, Cc:2 * Cc]", "u = par[:, :Cc]"),
-    ("output projected with p_up untransposed", "p_up.T)", "p_up[:, ::-1].T)"),
+    ("output projected with reordered latent channels", "y = np.matmul(yt, p_up.T)",
+     "y = np.matmul(yt, p_up[:, ::-1].T)"),
 ]
 
 
@@ -82,3 +85,22 @@ def test_sublayer_pins_reject_mutant(monkeypatch, name, old, new):
         except AssertionError:
             failed += 1
     assert failed > 0, name
+
+
+def test_storage_rounding():
+    to = oracle._to_storage
+    # bf16 keeps 8 significand bits: 1 + 2^-8 is a halfway case between 1 and
+    # 1 + 2^-7 and rounds to the even one (1); 1 + 3 * 2^-8 rounds up to 1 + 2^-6
+    a = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -2.5, 0.0, 1 + 2.0 ** -7])
+    assert np.array_equal(to(a, "bf16"), [1.0, 1.0, 1 + 2.0 ** -6, -2.5, 0.0, 1 + 2.0 ** -7])
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal(10000)
+    r = to(v, "bf16")
+    # half an ulp of an 8-bit significand: at most 2^-8 relative (plus the
+    # first rounding to fp32)
+    assert np.all(np.abs(r - v) <= (2.0 ** -8 + 2.0 ** -24) * np.abs(v))
+    assert np.max(np.abs(r - v) / np.abs(v)) > 2.0 ** -9      # not a finer type
+    assert np.array_equal(to(r, "bf16"), r)
+    f = to(v, "fp32")
+    assert np.array_equal(f, v.astype(np.float32).astype(np.float64))
+    assert to(v, None) is v
