@@ -298,6 +298,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-variants", action="store_true", help="skip the grouped / chunked legs")
     ap.add_argument("--no-sublayer", action="store_true", help="skip the latent sublayer legs")
+    ap.add_argument("--sublayer-only", type=int, default=None, metavar="G",
+                    help="run only the latent sublayer leg with G tap groups and print it "
+                         "(for profiling its kernels on their own)")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only warmup + K backward launches and print their timing "
                          "(for profiling the backward kernel on its own)")
@@ -330,6 +333,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_launches": args.steps, "bytes_read_per_launch": src.numel() * 4,
                           "bytes_written_per_launch": dst.numel() * 4}), flush=True)
+        return
+    if args.sublayer_only is not None:
+        print(json.dumps({"sublayer": sublayer_leg(args, dev, args.sublayer_only)}), flush=True)
         return
     print("bench: drawing %s inputs" % wl.name, file=sys.stderr, flush=True)
     base = inputs.problem_torch(wl.B, wl.C, wl.H, wl.W, 0, wl.dtype, dev)

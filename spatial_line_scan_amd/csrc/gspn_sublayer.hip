@@ -147,8 +147,11 @@ hipError_t gemm(int dtype, const GemmShape& g, const void* A, const void* B, voi
         cleanup();
         return blas_error(s);
     }
-    // one algorithm per shape, chosen once: the same shape always runs the
-    // same kernel, so results repeat bitwise
+    // One algorithm per shape, chosen on first use: the library's best
+    // candidates are each timed on this call's operands (a few runs, HIP
+    // events on `stream`) and the fastest is kept, so that later calls with
+    // the same shape run the same kernel and results repeat bitwise.
+    const float one = 1.0f, zero = 0.0f;
     hipblasLtMatmulAlgo_t algo;
     {
         std::lock_guard<std::mutex> lock(g_mu);
@@ -159,19 +162,59 @@ hipError_t gemm(int dtype, const GemmShape& g, const void* A, const void* B, voi
             if (s == HIPBLAS_STATUS_SUCCESS)
                 s = hipblasLtMatmulPreferenceSetAttribute(
                     pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb));
-            hipblasLtMatmulHeuristicResult_t res[1];
+            constexpr int kCandidates = 12;
+            hipblasLtMatmulHeuristicResult_t res[kCandidates];
             int found = 0;
             if (s == HIPBLAS_STATUS_SUCCESS)
-                s = hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, ld, ld, pref, 1, res, &found);
+                s = hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, ld, ld, pref, kCandidates,
+                                                    res, &found);
             if (s != HIPBLAS_STATUS_SUCCESS || found < 1) {
                 cleanup();
                 return s != HIPBLAS_STATUS_SUCCESS ? blas_error(s) : hipErrorNotSupported;
             }
-            it = g_algos.emplace(g.key(dtype), res[0].algo).first;
+            int best = 0;
+            if (found > 1) {
+                hipEvent_t e0, e1;
+                if ((he = hipEventCreate(&e0)) != hipSuccess) {
+                    cleanup();
+                    return he;
+                }
+                if ((he = hipEventCreate(&e1)) != hipSuccess) {
+                    (void)hipEventDestroy(e0);
+                    cleanup();
+                    return he;
+                }
+                float best_ms = 0.0f;
+                for (int a = 0; a < found; ++a) {
+                    if (res[a].state != HIPBLAS_STATUS_SUCCESS ||
+                        res[a].workspaceSize > static_cast<size_t>(kBlasWorkspace))
+                        continue;
+                    // one untimed run (first-use costs), then three timed
+                    hipblasStatus_t r = hipblasLtMatmul(h, desc, &one, A, la, B, lb, &zero, D, ld,
+                                                        D, ld, &res[a].algo, ws, kBlasWorkspace,
+                                                        stream);
+                    if (r != HIPBLAS_STATUS_SUCCESS) continue;
+                    if (hipEventRecord(e0, stream) != hipSuccess) continue;
+                    for (int rep = 0; rep < 3 && r == HIPBLAS_STATUS_SUCCESS; ++rep)
+                        r = hipblasLtMatmul(h, desc, &one, A, la, B, lb, &zero, D, ld, D, ld,
+                                            &res[a].algo, ws, kBlasWorkspace, stream);
+                    if (r != HIPBLAS_STATUS_SUCCESS || hipEventRecord(e1, stream) != hipSuccess ||
+                        hipEventSynchronize(e1) != hipSuccess)
+                        continue;
+                    float ms = 0.0f;
+                    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) continue;
+                    if (best_ms == 0.0f || ms < best_ms) {
+                        best_ms = ms;
+                        best = a;
+                    }
+                }
+                (void)hipEventDestroy(e0);
+                (void)hipEventDestroy(e1);
+            }
+            it = g_algos.emplace(g.key(dtype), res[best].algo).first;
         }
         algo = it->second;
     }
-    const float one = 1.0f, zero = 0.0f;
     s = hipblasLtMatmul(h, desc, &one, A, la, B, lb, &zero, D, ld, D, ld, &algo, ws,
                         static_cast<size_t>(kBlasWorkspace), stream);
     cleanup();
