@@ -39,6 +39,14 @@ hipError_t launch_prop2d_pair(const void* x, const void* lam, const void* u, con
                               float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                               const PropOpts& opts, hipStream_t stream);
 
+// Fast path for bf16 planes: one wavefront per plane, rows then columns,
+// lambda x and the direction sum on chip (gspn_prop2d_phase.hip).
+bool prop2d_phase_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
+                           const void* lam, const void* u, const void* w4, const void* y);
+hipError_t launch_prop2d_phase(const void* x, const void* lam, const void* u, const void* w4,
+                               float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
+                               const PropOpts& opts, hipStream_t stream);
+
 // Gradient of gspn_prop2d_4dir (gspn_backward.hip).  ws is NULL when the
 // three fp32 planes of a workgroup fit in LDS, else planes * 3 * H * W floats.
 hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u, const void* w4,

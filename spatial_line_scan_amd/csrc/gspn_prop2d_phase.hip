@@ -1,0 +1,477 @@
+// Four-direction propagation, one wavefront per (b, c) plane in two phases
+// (gfx950).
+//
+// Operator: "Scaling Parallel Sequence Models to Foundation-Scale Vision
+// Encoders", §3 line-scan recurrence (standard GSPN form), §4.1 single-kernel
+// design, §4.3 hidden state kept on chip, §5.1 fused normalisation (sigmoid,
+// local sum, clamp, divide); reading notes, method / overall framework.
+//
+// Work split.  One wavefront owns one plane and scans it twice: first the
+// rows (lanes 0-31 top-down, lanes 32-63 bottom-up), then the columns (lanes
+// 0-31 left-right, lanes 32-63 right-left).  Within a 32-lane half, lane q
+// holds positions Kq .. Kq+K-1 of the current line in registers and the
+// neighbour exchange is one wave-wide DPP shift each way (across the halves
+// the shifted value meets a dropped tap of weight 0).
+//
+// On-chip data.  LDS holds, per plane:
+//   S  fp32 [H][W]: the sum of the four directional states, zeroed first;
+//      every step adds h into the value of its line read one step earlier.
+//      One wavefront does all the adds, in program order, so the four terms
+//      of a pixel are summed in a fixed order (TD or BU first, then LR or
+//      RL) and no two lanes ever update one word in the same instruction.
+//   b = lambda x of every pixel, computed once from coalesced loads of x and
+//      lambda: fp32 for fp32 storage; for bf16 storage the exact product of
+//      two bf16 values has at most 16 significant bits, so its fp32 pattern
+//      ends in 8 zero bits and it is kept as 24 bits, the upper 16 in one
+//      array and the next 8 in another (3 bytes a pixel instead of 4).
+// With b on chip, the scans stream only the taps (line-major for every
+// direction, one coalesced window load per tap and step); x and lambda are
+// read once, whole, and never along a column.  At 74 x 74 bf16 a plane takes
+// 39 KB, so four planes share a CU, one wavefront per SIMD.
+//
+// Padding.  S and the b arrays are surrounded by pads of one longest line,
+// so that the one-step-ahead reads past either end of a scan stay inside the
+// allocation; slots past the end of a line all read and write dummy words at
+// LDS address 0 (zeroed; such a slot's taps are all dropped, so its state
+// and everything it writes stay 0).
+// When a scan has an odd number of lines both halves reach the middle line
+// in the same step: the backward half writes its state to the pad after S
+// and adds it in after the phase.
+//
+// Tap groups and chunked scans as in the two-wavefront kernel: the tap plane
+// of plane p is p / cpg, and a chunked scan restarts h at the first line of
+// each segment of ceil(NL / k_chunk) lines.
+#include "gspn_device.h"
+#include "gspn_internal.h"
+#include "gspn_lane.h"
+
+#include <type_traits>
+
+namespace gspn {
+namespace {
+
+using namespace lane;
+
+// LDS layout in bytes (all offsets multiples of 16):
+//   [S dummy: 16][b dummy: 16][pad Lmax][S: H W][pad Lmax] fp32,
+//   bf16: [pad][b_hi: H W][pad] u16, [pad][b_lo: H W][pad] u8
+//   fp32: [pad][b: H W][pad] fp32
+// Slots past a line end all use the dummies: their S reads and writes go to
+// the S dummy, their b reads in the column scan to the b dummy (zero, never
+// written) and their b writes in the row scan to the pads before the b
+// arrays.  Their taps are all dropped, so no in-line position ever weighs
+// their (finite) states.
+struct PhaseLayout {
+    int s, s_pad, bh, bl, bytes;
+    static constexpr int dum = 0, bdum = 16;
+    __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
+    __host__ __device__ PhaseLayout(int H, int W, bool bf16) {
+        const int lmax = H > W ? H : W;
+        const int hw = H * W;
+        s = a16(32 + 4 * lmax);
+        s_pad = s + 4 * hw;                          // pad line after S (odd middle lines)
+        const int es_hi = bf16 ? 2 : 4;
+        bh = a16(s_pad + 4 * lmax + es_hi * lmax);
+        if (bf16) {
+            bl = a16(bh + es_hi * (hw + lmax) + lmax);
+            bytes = a16(bl + hw + lmax);
+        } else {
+            bl = 0;
+            bytes = a16(bh + es_hi * (hw + lmax));
+        }
+    }
+};
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <typename V> using lds_t = __attribute__((address_space(3))) V;
+
+// Orders this wavefront's LDS accesses before the fence against those after
+// it (one wavefront per workgroup: no barrier, and global loads in flight
+// are not waited for).
+__device__ __forceinline__ void lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+}
+
+template <typename V>
+__device__ __forceinline__ lds_t<V>& lds_ref(uint32_t byte_off) {
+    // the kernel's only LDS is its dynamic array, which starts at address 0
+    return *reinterpret_cast<lds_t<V>*>(static_cast<uintptr_t>(byte_off));
+}
+
+// OddH / OddW: the row / column scans have an odd number of lines.
+// Chunked: k_chunk > 1.
+template <typename T, int K, int D, bool OddH, bool OddW, bool Chunked>
+__global__ void __launch_bounds__(64)
+prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __restrict__ u,
+                    const T* __restrict__ w4, int w4_bytes, float eps, T* __restrict__ y,
+                    int planes, int H, int W, int cpg, int k_chunk) {
+    constexpr bool kBf16 = sizeof(T) == 2;
+    constexpr int ES = sizeof(T);
+    constexpr int NW = window_words<T, K>();
+    const int HW = H * W;
+    const PhaseLayout lay(H, W, kBf16);
+    const int lane = threadIdx.x;
+    const int half = lane >> 5;          // 0: forward (TD, LR), 1: backward (BU, RL)
+    const int q = lane & 31;
+    const bool fwd = half == 0;
+    const int plane = blockIdx.x;
+    const size_t pix0 = static_cast<size_t>(plane) * HW;
+
+    // ---------------------------------------- zero S, its pads and dummies
+    // [0, bh): the dummy words, S with its pads, and the pad before b_hi
+    for (int f = lane; f < lay.bh / 16; f += 64) lds_ref<u32x4_t>(16u * f) = u32x4_t{0u, 0u, 0u, 0u};
+
+    const int words = kBf16 ? HW / 2 : HW;     // bf16: HW is even, two pixels a dword
+    // u for the end, in dword pairs, loaded now so that it arrives during
+    // the scans (a trailing odd dword is loaded at the end)
+    constexpr int kUPer = 24;
+    const int pairs = words / 2;
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t* u64p = reinterpret_cast<const u32x2_t*>(u + pix0);
+    u32x2_t ureg[kUPer];
+#pragma unroll
+    for (int k = 0; k < kUPer; ++k) {
+        const int f = lane + 64 * k;
+        ureg[k] = f < pairs ? u64p[f] : u32x2_t{0u, 0u};
+    }
+    lds_order();
+
+    // LDS address of b at element index e
+    auto b_addr_hi = [&](int e) { return static_cast<uint32_t>(lay.bh + (kBf16 ? 2 : 4) * e); };
+    auto b_addr_lo = [&](int e) { return static_cast<uint32_t>(lay.bl + e); };
+
+    // one resource per tap plane k, based k planes into the tap tensor
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(x), 0, static_cast<int>(static_cast<int64_t>(planes) * HW * ES), kBufFlags);
+    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(lam), 0, static_cast<int>(static_cast<int64_t>(planes) * HW * ES), kBufFlags);
+    __amdgpu_buffer_rsrc_t taps[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + static_cast<size_t>(k) * HW), 0,
+                                                    w4_bytes - k * HW * ES, kBufFlags);
+    const int tap_planes = planes / cpg;
+    const int par = kBf16 ? ((K * q) & 1) : 0;
+    const uint32_t win_b = static_cast<uint32_t>(K * q - par) * ES;
+    const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
+    const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
+
+    auto phase = [&](auto rows_tag, auto odd_tag) {
+        constexpr bool kRows = decltype(rows_tag)::value;
+        constexpr bool kOdd = decltype(odd_tag)::value;
+        const int L = kRows ? W : H;
+        const int NL = kRows ? H : W;
+        const int g = (kRows ? 0 : 2) + half;        // direction TD, BU, LR, RL
+        float c0[K], c1[K], c2[K];
+        bool valid[K];
+        const float inf = __builtin_inff();
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int p = K * q + j;
+            valid[j] = p < L;
+            c0[j] = (valid[j] && p > 0) ? 1.0f : inf;
+            c1[j] = valid[j] ? 1.0f : inf;
+            c2[j] = (valid[j] && p < L - 1) ? 1.0f : inf;
+        }
+        const uint32_t line_b = static_cast<uint32_t>(L) * ES;
+        const uint32_t lo0 = fwd ? 0u : static_cast<uint32_t>(NL - 1) * line_b;
+        const uint32_t dlo = fwd ? line_b : 0u - line_b;
+        uint32_t lo = static_cast<uint32_t>(((g * tap_planes + plane / cpg) * 3) * HW) * ES + win_b + lo0;
+        // row scan: x and lambda of the current row, same window as the taps
+        uint32_t xo = static_cast<uint32_t>(pix0) * ES + win_b + lo0;
+        words_t<NW> tbuf[D][3];
+        words_t<NW> xbuf[kRows ? D : 1], lbuf[kRows ? D : 1];
+        auto load_line = [&](int d) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
+            lo += dlo;
+            if constexpr (kRows) {
+                xbuf[d] = load_words<NW>(xs, xo);
+                lbuf[d] = load_words<NW>(ls, xo);
+                xo += dlo;
+            }
+        };
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_line(d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // Per slot: element index of its pixel on the current line, and its
+        // change per step (0 for slots past the line end, which stay on the
+        // lane's dummy words).
+        const int i0 = fwd ? 0 : NL - 1;
+        const int de = kRows ? (fwd ? W : -W) : (fwd ? 1 : -1);
+        uint32_t aS[K], aH[K], aL[K];
+        const int dS = 4 * de, dH = (kBf16 ? 2 : 4) * de, dL = de;
+        int dSj[K], dHj[K], dLj[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int p = K * q + j;
+            const int e = kRows ? i0 * W + p : p * W + i0;
+            if (valid[j]) {
+                aS[j] = static_cast<uint32_t>(lay.s + 4 * e);
+                aH[j] = b_addr_hi(e);
+                aL[j] = b_addr_lo(e);
+            } else if (kRows) {
+                // b writes of the row scan land in the pads before the b arrays
+                aS[j] = PhaseLayout::dum;
+                aH[j] = static_cast<uint32_t>(lay.bh - (kBf16 ? 2 : 4) * (j + 1));
+                aL[j] = static_cast<uint32_t>(lay.bl - (j + 1));
+            } else {
+                aS[j] = PhaseLayout::dum;
+                aH[j] = aL[j] = PhaseLayout::bdum;
+            }
+            dSj[j] = valid[j] ? dS : 0;
+            dHj[j] = valid[j] ? dH : 0;
+            dLj[j] = valid[j] ? dL : 0;
+        }
+        auto read_b = [&](int j) -> float {
+            if constexpr (kBf16) {
+                const uint32_t hi = lds_ref<uint16_t>(aH[j]);
+                const uint32_t lo8 = lds_ref<uint8_t>(aL[j]);
+                return __uint_as_float((hi << 16) | (lo8 << 8));
+            } else {
+                return lds_ref<float>(aH[j]);
+            }
+        };
+        float h[K], acc[K], bv[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            h[j] = 0.0f;
+            acc[j] = lds_ref<float>(aS[j]);
+            if constexpr (!kRows) bv[j] = read_b(j);
+        }
+        // odd scans: the backward half's middle-line states go to the pad
+        // line after S (indexed by position) and are added in afterwards
+        const int mid = (NL - 1) / 2;
+        uint32_t mid_pad[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            mid_pad[j] = static_cast<uint32_t>(valid[j] ? lay.s_pad + 4 * (K * q + j) : PhaseLayout::dum);
+        int seg = NL, next_restart = NL;
+        if constexpr (Chunked) {
+            seg = (NL + k_chunk - 1) / k_chunk;
+            next_restart = fwd ? seg : NL - ((NL - 1) / seg) * seg;
+        }
+
+        auto step = [&](int s, int d) {
+            asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
+            if constexpr (kRows) asm volatile("" : "+v"(xbuf[d]), "+v"(lbuf[d]));
+            float s0v[K], s1v[K], s2v[K], r[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                if constexpr (kRows) {
+                    // b = lambda x from the row's windows, also kept for the column scan
+                    bv[j] = window_elem<T, K, NW>(lbuf[d], j, sel_even, sel_odd) *
+                            window_elem<T, K, NW>(xbuf[d], j, sel_even, sel_odd);
+                }
+                const float z0 = window_elem<T, K, NW>(tbuf[d][0], j, sel_even, sel_odd);
+                const float z1 = window_elem<T, K, NW>(tbuf[d][1], j, sel_even, sel_odd);
+                const float z2 = window_elem<T, K, NW>(tbuf[d][2], j, sel_even, sel_odd);
+                s0v[j] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z0 * kNegLog2e) + c0[j]);
+                s1v[j] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z1 * kNegLog2e) + c1[j]);
+                s2v[j] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z2 * kNegLog2e) + c2[j]);
+                r[j] = __builtin_amdgcn_rcpf(fmaxf((s0v[j] + s1v[j]) + s2v[j], eps));
+            }
+            // refill slot d only after it has been decoded
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                if constexpr (kRows)
+                    asm volatile("" : "+v"(lo), "+v"(xo)
+                                 : "v"(s0v[j]), "v"(s1v[j]), "v"(s2v[j]), "v"(r[j]), "v"(bv[j]));
+                else
+                    asm volatile("" : "+v"(lo) : "v"(s0v[j]), "v"(s1v[j]), "v"(s2v[j]), "v"(r[j]));
+            }
+            load_line(d);
+            if constexpr (kRows) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    const uint32_t bb = __float_as_uint(bv[j]);
+                    if constexpr (kBf16) {
+                        lds_ref<uint16_t>(aH[j]) = static_cast<uint16_t>(bb >> 16);
+                        lds_ref<uint8_t>(aL[j]) = static_cast<uint8_t>(bb >> 8);
+                    } else {
+                        lds_ref<float>(aH[j]) = bv[j];
+                    }
+                }
+            }
+
+            if constexpr (Chunked) {
+                const bool restart = s == next_restart;
+                next_restart = restart ? next_restart + seg : next_restart;
+#pragma unroll
+                for (int j = 0; j < K; ++j) h[j] = restart ? 0.0f : h[j];
+            }
+            const float hl0 = from_prev(h[K - 1]);
+            const float hrK = from_next(h[0]);
+            float hn[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const float hl = j > 0 ? h[j - 1] : hl0;
+                const float hr = j < K - 1 ? h[j + 1] : hrK;
+                float m = s1v[j] * h[j];
+                m = fmaf(s0v[j], hl, m);
+                m = fmaf(s2v[j], hr, m);
+                hn[j] = fmaf(m, r[j], bv[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) h[j] = hn[j];
+
+            const bool at_mid = kOdd && !fwd && s == mid;
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                if (at_mid) lds_ref<float>(mid_pad[j]) = h[j];
+                else lds_ref<float>(aS[j]) = acc[j] + h[j];
+            }
+            // the next line, read after this step's writes
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                aS[j] += dSj[j];
+                aH[j] += dHj[j];
+                aL[j] += dLj[j];
+                acc[j] = lds_ref<float>(aS[j]);
+                if constexpr (!kRows) bv[j] = read_b(j);
+            }
+        };
+
+        int s0 = 0;
+        for (; s0 + D <= NL; s0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) step(s0 + d, d);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (s0 + d < NL) step(s0 + d, d);
+        if constexpr (kOdd) {
+            // the middle line receives the backward half's term last
+            if (!fwd) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    if (!valid[j]) continue;
+                    const int p = K * q + j;
+                    const int e = kRows ? mid * W + p : p * W + mid;
+                    const uint32_t a = static_cast<uint32_t>(lay.s + 4 * e);
+                    lds_ref<float>(a) = lds_ref<float>(a) + lds_ref<float>(mid_pad[j]);
+                }
+            }
+        }
+    };
+    phase(std::true_type{}, std::bool_constant<OddH>{});
+    lds_order();
+    phase(std::false_type{}, std::bool_constant<OddW>{});
+    lds_order();
+
+    // --------------------------------------------------------- y = u * S
+    // (bf16: S is read as four floats per dword pair, 16-byte aligned since
+    // the pair starts at an even dword)
+    uint32_t* y32 = reinterpret_cast<uint32_t*>(y + pix0);
+    const uint32_t* u32 = reinterpret_cast<const uint32_t*>(u + pix0);
+    u32x2_t* y64p = reinterpret_cast<u32x2_t*>(y + pix0);
+    auto emit_word = [&](int f, uint32_t uv) -> uint32_t {
+        if constexpr (kBf16) {
+            const f32x2_t sv = lds_ref<f32x2_t>(lay.s + 8u * f);
+            return pack_bf16x2(__uint_as_float(uv << 16) * sv.x,
+                               __uint_as_float(uv & 0xffff0000u) * sv.y);
+        } else {
+            return __float_as_uint(__uint_as_float(uv) * lds_ref<float>(lay.s + 4u * f));
+        }
+    };
+    auto emit_pair = [&](int f, u32x2_t uv) {
+        y64p[f] = u32x2_t{emit_word(2 * f, uv.x), emit_word(2 * f + 1, uv.y)};
+    };
+#pragma unroll
+    for (int k = 0; k < kUPer; ++k) {
+        const int f = lane + 64 * k;
+        if (f < pairs) emit_pair(f, ureg[k]);
+    }
+    for (int f = lane + 64 * kUPer; f < pairs; f += 64) emit_pair(f, u64p[f]);
+    if ((words & 1) && lane == 0) y32[words - 1] = emit_word(words - 1, u32[words - 1]);
+}
+
+template <typename T, int K, bool OddH, bool OddW, bool Chunked>
+hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, float eps,
+                    void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                    hipStream_t stream) {
+    constexpr int D = 8;   // taps prefetched D steps ahead
+    const size_t lds = PhaseLayout(static_cast<int>(H), static_cast<int>(W), sizeof(T) == 2).bytes;
+    auto kern = prop2d_phase_kernel<T, K, D, OddH, OddW, Chunked>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    const int64_t n = planes * H * W;
+    kern<<<dim3(static_cast<unsigned>(planes)), dim3(64), lds, stream>>>(
+        static_cast<const T*>(x), static_cast<const T*>(lam), static_cast<const T*>(u),
+        static_cast<const T*>(w4), static_cast<int>(12 * (n / o.cpg) * sizeof(T)), eps,
+        static_cast<T*>(y), static_cast<int>(planes), static_cast<int>(H), static_cast<int>(W),
+        static_cast<int>(o.cpg), static_cast<int>(o.k_chunk));
+    return hipGetLastError();
+}
+
+template <typename T, int K, bool Chunked>
+hipError_t launch_parity(const void* x, const void* lam, const void* u, const void* w4, float eps,
+                         void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                         hipStream_t stream) {
+    if constexpr (sizeof(T) == 2) {  // bf16 shapes are even (eligibility)
+        return launch_k<T, K, false, false, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    } else {
+        const bool oh = H & 1, ow = W & 1;
+        if (!oh && !ow)
+            return launch_k<T, K, false, false, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        if (oh && ow)
+            return launch_k<T, K, true, true, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        if (oh)
+            return launch_k<T, K, true, false, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        return launch_k<T, K, false, true, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    }
+}
+
+template <typename T, bool Chunked>
+hipError_t launch_c(const void* x, const void* lam, const void* u, const void* w4, float eps,
+                    void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                    hipStream_t stream) {
+    const int64_t Lmax = H > W ? H : W;
+    if (Lmax <= 32) return launch_parity<T, 1, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (Lmax <= 64) return launch_parity<T, 2, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    return launch_parity<T, 3, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+}
+
+template <typename T>
+hipError_t launch_t(const void* x, const void* lam, const void* u, const void* w4, float eps,
+                    void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                    hipStream_t stream) {
+    return o.k_chunk > 1 ? launch_c<T, true>(x, lam, u, w4, eps, y, planes, H, W, o, stream)
+                         : launch_c<T, false>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+bool prop2d_phase_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
+                           const void* lam, const void* u, const void* w4, const void* y) {
+    if (H > 96 || W > 96) return false;
+    if (PhaseLayout(static_cast<int>(H), static_cast<int>(W), dtype == 1).bytes > kLdsBytes)
+        return false;
+    const int64_t es = dtype == 0 ? 4 : 2;
+    if (12 * planes * H * W * es > 0x7fffffff) return false;
+    if (dtype == 1) {  // bf16: whole dwords per line and per plane
+        if ((H & 1) || (W & 1)) return false;
+        if (!aligned4(x) || !aligned4(lam) || !aligned4(u) || !aligned4(w4) || !aligned4(y))
+            return false;
+    }
+    return true;
+}
+
+hipError_t launch_prop2d_phase(const void* x, const void* lam, const void* u, const void* w4,
+                               float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
+                               const PropOpts& o, hipStream_t stream) {
+    return dtype == 0 ? launch_t<float>(x, lam, u, w4, eps, y, planes, H, W, o, stream)
+                      : launch_t<uint16_t>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+}
+
+}  // namespace gspn
