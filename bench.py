@@ -46,8 +46,8 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "4-dir GSPN propagation GB/s & ms (B=32,C_c=64,74×74) + % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prop2d_latent1k_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "spatial_line_scan_amd", "csrc", f)
-                  for f in ("gspn_kernels.hip", "gspn_prop2d_pair.hip", "gspn_internal.h",
-                            "gspn_device.h")]
+                  for f in ("gspn_kernels.hip", "gspn_prop2d_phase.hip", "gspn_prop2d_pair.hip",
+                            "gspn_internal.h", "gspn_device.h", "gspn_lane.h")]
 BWD_VALUES_PER_PIXEL = 31
 
 
@@ -75,9 +75,10 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
     """Time the fp64 oracle on whole planes of the workload, single-threaded.
 
     The planes are those of the first rotated input set, in order, until the
-    time budget is spent (the whole workload if it fits); the GPU output of
-    those planes from the timed steps is compared with the oracle's as a
-    by-product.
+    time budget is spent; when the whole workload takes less than the budget
+    it is run again (whole passes) until the budget is reached.  The GPU
+    output of the first pass's planes from the timed steps is compared with
+    the oracle's as a by-product.
     """
     import ctypes
 
@@ -96,8 +97,8 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
     Y = f64(gpu_out)
     planes, spent, all_ok, details = 0, 0.0, True, []
     order = [(b, c) for b in range(wl.B) for c in range(wl.C)]
-    while spent < budget_s and planes < len(order):
-        b, c = order[planes]
+    while spent < budget_s:
+        b, c = order[planes % len(order)]
         arrs = [np.ascontiguousarray(a[b, c]) for a in (X, LAM, U)]
         arrs.append(np.ascontiguousarray(Wt[:, b, c]))
         y = np.empty_like(arrs[0])
@@ -107,10 +108,11 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
         spent += time.perf_counter() - t0
         if rc != 0:
             raise MemoryError("oracle failed")
-        ok, msg = compare(Y[b, c], y, RTOL[wl.dtype])
-        all_ok &= ok
-        if len(details) < 2 or not ok:
-            details.append("(%d,%d): %s" % (b, c, msg))
+        if planes < len(order):
+            ok, msg = compare(Y[b, c], y, RTOL[wl.dtype])
+            all_ok &= ok
+            if len(details) < 2 or not ok:
+                details.append("(%d,%d): %s" % (b, c, msg))
         planes += 1
     bytes_done = 16 * wl.elem_bytes * n * planes
     return {
@@ -118,8 +120,8 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": "%d of %d planes (%dx%d, %s values) of the timed inputs, fp64 C loop, %.1f s" % (
-            planes, wl.B * wl.C, wl.H, wl.W, wl.dtype, spent),
+        "sample": "%d plane passes over the %d planes (%dx%d, %s values) of the timed inputs, "
+                  "fp64 C loop, %.1f s" % (planes, wl.B * wl.C, wl.H, wl.W, wl.dtype, spent),
         "seconds": spent,
         "cpu": _cpu_model(),
         "host_cores_visible": os.cpu_count(),
@@ -293,7 +295,7 @@ def main():
     ap.add_argument("--workload", default="latent1k")
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9,
                     help="total bytes of rotated input sets (defeats the 256 MB cache)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-variants", action="store_true", help="skip the grouped / chunked legs")

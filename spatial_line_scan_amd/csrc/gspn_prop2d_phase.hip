@@ -231,7 +231,8 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
             if constexpr (kBf16) {
                 const uint32_t hi = lds_ref<uint16_t>(aH[j]);
                 const uint32_t lo8 = lds_ref<uint8_t>(aL[j]);
-                return __uint_as_float((hi << 16) | (lo8 << 8));
+                // bytes (hi.1, hi.0, lo.0, 0)
+                return __uint_as_float(__builtin_amdgcn_perm(hi, lo8, 0x0504000cu));
             } else {
                 return lds_ref<float>(aH[j]);
             }
@@ -267,14 +268,36 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
                     bv[j] = window_elem<T, K, NW>(lbuf[d], j, sel_even, sel_odd) *
                             window_elem<T, K, NW>(xbuf[d], j, sel_even, sel_odd);
                 }
-                const float z0 = window_elem<T, K, NW>(tbuf[d][0], j, sel_even, sel_odd);
-                const float z1 = window_elem<T, K, NW>(tbuf[d][1], j, sel_even, sel_odd);
-                const float z2 = window_elem<T, K, NW>(tbuf[d][2], j, sel_even, sel_odd);
-                s0v[j] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z0 * kNegLog2e) + c0[j]);
-                s1v[j] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z1 * kNegLog2e) + c1[j]);
-                s2v[j] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z2 * kNegLog2e) + c2[j]);
-                r[j] = __builtin_amdgcn_rcpf(fmaxf((s0v[j] + s1v[j]) + s2v[j], eps));
+                s0v[j] = window_elem<T, K, NW>(tbuf[d][0], j, sel_even, sel_odd) * kNegLog2e;
+                s1v[j] = window_elem<T, K, NW>(tbuf[d][1], j, sel_even, sel_odd) * kNegLog2e;
+                s2v[j] = window_elem<T, K, NW>(tbuf[d][2], j, sel_even, sel_odd) * kNegLog2e;
             }
+            // breadth first over the 3 K taps: each dependent operation finds
+            // its operand several instructions back
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                s0v[j] = __builtin_amdgcn_exp2f(s0v[j]);
+                s1v[j] = __builtin_amdgcn_exp2f(s1v[j]);
+                s2v[j] = __builtin_amdgcn_exp2f(s2v[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                s0v[j] += c0[j];
+                s1v[j] += c1[j];
+                s2v[j] += c2[j];
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                s0v[j] = __builtin_amdgcn_rcpf(s0v[j]);
+                s1v[j] = __builtin_amdgcn_rcpf(s1v[j]);
+                s2v[j] = __builtin_amdgcn_rcpf(s2v[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) r[j] = s0v[j] + s1v[j];
+#pragma unroll
+            for (int j = 0; j < K; ++j) r[j] = fmaxf(r[j] + s2v[j], eps);
+#pragma unroll
+            for (int j = 0; j < K; ++j) r[j] = __builtin_amdgcn_rcpf(r[j]);
             // refill slot d only after it has been decoded
 #pragma unroll
             for (int j = 0; j < K; ++j) {
