@@ -176,11 +176,16 @@ int gspn_prop2d_4dir_ex(const void* x, const void* lam, const void* u,
  *   T > eps : gs_m = (gwn_m - sum_k gwn_k wn_k) / T,  else gs_m = gwn_m / eps
  *   gz_m = gs_m s_m (1 - s_m).
  *   x, lam, u, gy, gx, glam, gu : [B][C][H][W];  w_raw4, gw4 : [4][B][C][3][..][..].
- *   workspace : fp32 scratch of at least
- *               gspn_prop2d_4dir_backward_workspace(B, C, H, W) bytes (NULL
- *               allowed when that is 0, which holds while a plane's three
- *               fp32 planes fit in LDS, e.g. up to 74 x 74 and beyond);
- *               4-byte aligned; contents on return are unspecified.
+ *   workspace : scratch of at least
+ *               gspn_prop2d_4dir_backward_workspace(B, C, H, W) bytes, 4-byte
+ *               aligned (16-byte alignment lets even-sided planes up to 96
+ *               take the fast kernels); contents on return are unspecified.
+ *               Planes with even H and W up to 96 need it for transposed
+ *               copies of x, lam, u, gy and two fp32 partial sums per
+ *               pixel-channel (sized for fp32 storage).  Otherwise it holds
+ *               three fp32 planes per (b, c) once they no longer fit in LDS
+ *               (above about 115 x 115); below that the size is 0 and NULL is
+ *               allowed.
  *   Outputs must not overlap inputs, each other or the workspace.  Lines up
  *   to 5851 (H and W).  bf16 gradients are rounded to nearest even.  The
  *   result is bitwise reproducible from run to run.

@@ -225,11 +225,19 @@ hipError_t backward_t(const void* x, const void* lam, const void* u, const void*
     return hipGetLastError();
 }
 
+// Workspace of this kernel: its three fp32 planes when they do not fit in LDS.
+int64_t plane_kernel_workspace_bytes(int64_t planes, int64_t H, int64_t W) {
+    const int64_t lds = static_cast<int64_t>(bwd_line_floats(H, W) + 3 * H * W) * 4;
+    return lds <= kLdsBytes ? 0 : planes * 3 * H * W * 4;
+}
+
 }  // namespace
 
 int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W) {
-    const int64_t lds = static_cast<int64_t>(bwd_line_floats(H, W) + 3 * H * W) * 4;
-    return lds <= kLdsBytes ? 0 : planes * 3 * H * W * 4;
+    const int64_t general = plane_kernel_workspace_bytes(planes, H, W);
+    const int64_t pair = prop2d_backward_pair_shape(planes, H, W)
+                             ? prop2d_backward_pair_workspace_bytes(planes, H, W) : 0;
+    return general > pair ? general : pair;
 }
 
 int64_t prop2d_backward_max_line() { return kLdsBytes / 4 / 7; }
@@ -238,6 +246,12 @@ hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u,
                                   const void* gy, float eps, void* gx, void* glam, void* gu,
                                   void* gw4, void* ws, int dtype, int64_t planes, int64_t H,
                                   int64_t W, hipStream_t stream) {
+    const void* ptrs[] = {x, lam, u, w4, gy, gx, glam, gu, gw4};
+    if (prop2d_backward_pair_eligible(dtype, planes, H, W, ptrs, 9, ws))
+        return launch_prop2d_backward_pair(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, dtype,
+                                           planes, H, W, stream);
+    // this kernel takes a workspace only when its planes leave LDS
+    if (plane_kernel_workspace_bytes(planes, H, W) == 0) ws = nullptr;
     return dtype == 0 ? backward_t<float>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W, stream)
                       : backward_t<uint16_t>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W,
                                              stream);

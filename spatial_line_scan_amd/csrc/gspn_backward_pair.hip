@@ -1,0 +1,624 @@
+// Gradient of the four-direction propagation, one wavefront per (b, c) plane
+// and direction pair (gfx950), for planes of even sides up to 96.
+//
+// Operator: the exact derivative of the forward definition ("Scaling Parallel
+// Sequence Models to Foundation-Scale Vision Encoders", §3 line-scan
+// recurrence, §5.1 fused normalisation; §6.1 reports backward kernels without
+// describing them), with the same formulas as the general backward kernel:
+//   adjoint, lines in reverse scan order: g_last = u gy,
+//     g_i[p] = u gy + sum_k wn_k(i+1, p-k+1) g_{i+1}[p-k+1];
+//   gx = lambda G, glambda = x G, gu = gy S with G = sum_d g_d, S = sum_d h_d;
+//   tap gradient gwn_k(i, p) = g_i[p] h_{i-1}[p+k-1] (0 on a scan's first
+//   line), then through s = sigmoid(z), T = sum s, r = 1 / max(T, eps):
+//     T > eps: gs_m = r sum_{k != m} wn_k (gwn_m - gwn_k), else gs_m = r gwn_m;
+//     gz_m = gs_m s_m (1 - s_m); dropped taps have s = 0 and get 0.
+//
+// Work split.  The row pair (top-down, bottom-up) and the column pair
+// (left-right, right-left) are two launches of one kernel that sees the lines
+// of its pair as the rows of a line-major plane: the row launch reads x,
+// lambda, u and gy as they are, the column launch reads copies transposed by
+// transpose4_kernel.  Every direction's taps are line-major already.  Lanes
+// 0-31 take the direction that scans lines 0 .. NL-1, lanes 32-63 the other;
+// lane q holds positions Kq .. Kq+K-1 of its line, and the three-tap
+// neighbourhood is one DPP lane shift each way, as in the forward kernels.
+//   1. Forward: h line by line (taps normalised in registers, b = lambda x
+//      from the line's windows); every line of h goes to an fp32 LDS plane of
+//      the half.
+//   2. S pass: S = h_a + h_b per pixel.  Row launch: to the workspace.
+//      Column launch: added to the row launch's S, and gu = gy S written.
+//   3. Adjoint, in reverse scan order.  The transposed products of line i+1
+//      (wn_k g per destination) stay in registers from the previous step and
+//      reach their source positions by lane shifts; the tap gradients of line
+//      i take h_{i-1} from the LDS plane, read one step ahead, and go to gw4
+//      as they are produced.  g_i overwrites h_i, which was last read one step
+//      earlier.
+//   4. G pass: G = g_a + g_b per pixel.  Row launch: to the workspace.
+//      Column launch: added to the row launch's G, and gx, glambda written.
+// Sums run in a fixed order (row pair before column pair, first half before
+// second), so the result is the same on every run.
+#include "gspn_device.h"
+#include "gspn_internal.h"
+#include "gspn_lane.h"
+
+namespace gspn {
+namespace {
+
+using namespace lane;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <typename V> using lds_t = __attribute__((address_space(3))) V;
+
+template <typename V>
+__device__ __forceinline__ lds_t<V>& lds_at(uint32_t byte_off) {
+    // the kernel's only LDS is its dynamic array, which starts at address 0
+    return *reinterpret_cast<lds_t<V>*>(static_cast<uintptr_t>(byte_off));
+}
+
+// Orders this wavefront's LDS accesses before the fence against those after it.
+__device__ __forceinline__ void lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+}
+
+// LDS layout in bytes (offsets multiples of 16):
+//   [dummy: 16][2 lines][A: NL x L][B: NL x L][2 lines]   fp32
+// A is the plane of lanes 0-31, B that of lanes 32-63.  The line before A
+// and the line after B are zero: the h before a scan's first line.  The
+// outer lines only absorb the read-ahead past the last adjoint step.  Slots
+// past a line's end read and write the dummy words.
+struct PairBwdLayout {
+    int a, b, bytes;
+    static constexpr int dum = 0;
+    __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
+    __host__ __device__ PairBwdLayout(int NL, int L) {
+        a = a16(16 + 8 * L);
+        b = a16(a + 4 * NL * L);
+        bytes = a16(b + 4 * (NL + 2) * L);
+    }
+};
+
+// Stores of the K tap gradients of a lane's slots into one tap line, with
+// buffer stores whose offsets are pushed past the tensor for positions past
+// the line's end (the hardware drops them).
+constexpr uint32_t kDrop = 0x80000000u;
+
+template <typename T, int K>
+struct TapStore {
+    uint32_t o32, o16, oe[K];   // byte offsets within a line (kDrop for dropped stores)
+    bool even;
+    __device__ TapStore(int q, int L) {
+        even = (q & 1) == 0;
+        if constexpr (sizeof(T) == 4) {
+            for (int j = 0; j < K; ++j) oe[j] = K * q + j < L ? 4u * (K * q + j) : kDrop;
+        } else if constexpr (K == 1) {
+            o16 = q < L ? 2u * q : kDrop;
+        } else if constexpr (K == 2) {
+            o32 = 2 * q < L ? 4u * q : kDrop;   // L is even: 2q < L implies 2q + 1 < L
+        } else {
+            // even q: dword (3q, 3q+1), short 3q+2; odd q: short 3q, dword (3q+1, 3q+2)
+            const int p32 = even ? 3 * q : 3 * q + 1;
+            const int p16 = even ? 3 * q + 2 : 3 * q;
+            o32 = p32 < L ? 2u * p32 : kDrop;
+            o16 = p16 < L ? 2u * p16 : kDrop;
+        }
+    }
+    __device__ __forceinline__ void put(__amdgpu_buffer_rsrc_t r, uint32_t line_off, const float (&v)[K]) const {
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), r, oe[j] + line_off, 0, 0);
+        } else if constexpr (K == 1) {
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(pack_bf16x2(v[0], v[0])), r,
+                                                  o16 + line_off, 0, 0);
+        } else if constexpr (K == 2) {
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[0], v[1]), r, o32 + line_off, 0, 0);
+        } else {
+            const float a = even ? v[0] : v[1];
+            const float b = even ? v[1] : v[2];
+            const float c = even ? v[2] : v[0];
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a, b), r, o32 + line_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(pack_bf16x2(c, c)), r,
+                                                  o16 + line_off, 0, 0);
+        }
+    }
+};
+
+// Two consecutive pixels of an output plane.
+template <typename T>
+__device__ __forceinline__ void store_pair(T* p, size_t e, float v0, float v1) {
+    if constexpr (sizeof(T) == 4) *reinterpret_cast<f32x2_t*>(p + e) = f32x2_t{v0, v1};
+    else *reinterpret_cast<uint32_t*>(p + e) = pack_bf16x2(v0, v1);
+}
+template <typename T>
+__device__ __forceinline__ f32x2_t load_pair(const T* p, size_t e) {
+    if constexpr (sizeof(T) == 4) {
+        return *reinterpret_cast<const f32x2_t*>(p + e);
+    } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(p + e);
+        return f32x2_t{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+    }
+}
+
+// Cols = false: the row pair (NL = H, L = W), inputs as they are; writes S and
+// G of the pair to s_ws, g_ws ([planes][H][W] fp32).
+// Cols = true: the column pair (NL = W, L = H), inputs transposed; adds the
+// row pair's S and G and writes gu, gx, glam.
+template <typename T, int K, int D, bool Cols>
+__global__ void __launch_bounds__(64)
+prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml,
+                            const T* __restrict__ ul, const T* __restrict__ gyl,
+                            const T* __restrict__ w4, T* __restrict__ gw4, int w4_bytes,
+                            float eps, int planes, int NL, int L, int dir0,
+                            float* __restrict__ s_ws, float* __restrict__ g_ws,
+                            const T* __restrict__ x, const T* __restrict__ lam,
+                            const T* __restrict__ gy, T* __restrict__ gx, T* __restrict__ glam,
+                            T* __restrict__ gu) {
+    constexpr int ES = sizeof(T);
+    constexpr int NW = window_words<T, K>();
+    const int HW = NL * L;
+    const PairBwdLayout lay(NL, L);
+    const int lane = threadIdx.x;
+    const int half = lane >> 5;
+    const int q = lane & 31;
+    const bool fwd = half == 0;
+    const int plane = blockIdx.x;
+    const size_t pix0 = static_cast<size_t>(plane) * HW;
+
+    // zero lines (h before a scan's first line) and the dummy words
+    if (lane < 4) lds_at<float>(4u * lane) = 0.0f;
+    for (int f = lane; f < L; f += 64) {
+        lds_at<float>(lay.a - 4 * L + 4 * f) = 0.0f;
+        lds_at<float>(lay.b + 4 * HW + 4 * f) = 0.0f;
+    }
+
+    const int in_bytes = planes * HW * ES;
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xl), 0, in_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(laml), 0, in_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t us = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(ul), 0, in_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t gs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(gyl), 0, in_bytes, kBufFlags);
+    __amdgpu_buffer_rsrc_t taps[3], gws[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + static_cast<size_t>(k) * HW), 0,
+                                                    w4_bytes - k * HW * ES, kBufFlags);
+        gws[k] = __builtin_amdgcn_make_buffer_rsrc(gw4 + static_cast<size_t>(k) * HW, 0,
+                                                   w4_bytes - k * HW * ES, kBufFlags);
+    }
+    const int par = ES == 2 ? ((K * q) & 1) : 0;
+    const uint32_t win_b = static_cast<uint32_t>(K * q - par) * ES;
+    const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
+    const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
+    const uint32_t tap_b = static_cast<uint32_t>(((dir0 + half) * planes + plane) * 3 * HW) * ES;
+    const uint32_t line_b = static_cast<uint32_t>(L) * ES;
+    const uint32_t plane_base = half ? lay.b : lay.a;
+
+    float c0[K], c1[K], c2[K];
+    bool valid[K];
+    const float inf = __builtin_inff();
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int p = K * q + j;
+        valid[j] = p < L;
+        c0[j] = (valid[j] && p > 0) ? 1.0f : inf;
+        c1[j] = valid[j] ? 1.0f : inf;
+        c2[j] = (valid[j] && p < L - 1) ? 1.0f : inf;
+    }
+    // s_k = sigmoid(z_k) (0 for dropped taps) and r = 1 / max(sum s, eps)
+    auto normalise = [&](const words_t<NW> (&tw)[3], float (&s0)[K], float (&s1)[K], float (&s2)[K],
+                         float (&t)[K], float (&r)[K]) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            s0[j] = window_elem<T, K, NW>(tw[0], j, sel_even, sel_odd) * kNegLog2e;
+            s1[j] = window_elem<T, K, NW>(tw[1], j, sel_even, sel_odd) * kNegLog2e;
+            s2[j] = window_elem<T, K, NW>(tw[2], j, sel_even, sel_odd) * kNegLog2e;
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            s0[j] = __builtin_amdgcn_exp2f(s0[j]);
+            s1[j] = __builtin_amdgcn_exp2f(s1[j]);
+            s2[j] = __builtin_amdgcn_exp2f(s2[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            s0[j] = __builtin_amdgcn_rcpf(s0[j] + c0[j]);
+            s1[j] = __builtin_amdgcn_rcpf(s1[j] + c1[j]);
+            s2[j] = __builtin_amdgcn_rcpf(s2[j] + c2[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            t[j] = (s0[j] + s1[j]) + s2[j];
+            r[j] = __builtin_amdgcn_rcpf(fmaxf(t[j], eps));
+        }
+    };
+
+    // ------------------------------------------------------------ forward
+    {
+        const uint32_t lo0 = fwd ? 0u : static_cast<uint32_t>(NL - 1) * line_b;
+        const uint32_t dlo = fwd ? line_b : 0u - line_b;
+        uint32_t lo = tap_b + win_b + lo0;
+        uint32_t xo = static_cast<uint32_t>(pix0) * ES + win_b + lo0;
+        words_t<NW> tbuf[D][3], xbuf[D], lbuf[D];
+        auto load_line = [&](int d) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
+            xbuf[d] = load_words<NW>(xs, xo);
+            lbuf[d] = load_words<NW>(ls, xo);
+            lo += dlo;
+            xo += dlo;
+        };
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_line(d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int i0 = fwd ? 0 : NL - 1;
+        const int dl = fwd ? 4 * L : -4 * L;
+        uint32_t aH[K];
+        int dH[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            aH[j] = valid[j] ? plane_base + 4u * (i0 * L + K * q + j) : PairBwdLayout::dum + 4u * j;
+            dH[j] = valid[j] ? dl : 0;
+        }
+        float h[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) h[j] = 0.0f;
+
+        auto step = [&](int d) {
+            asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
+            asm volatile("" : "+v"(xbuf[d]), "+v"(lbuf[d]));
+            float s0[K], s1[K], s2[K], t[K], r[K], b[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                b[j] = window_elem<T, K, NW>(lbuf[d], j, sel_even, sel_odd) *
+                       window_elem<T, K, NW>(xbuf[d], j, sel_even, sel_odd);
+            normalise(tbuf[d], s0, s1, s2, t, r);
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                asm volatile("" : "+v"(lo), "+v"(xo) : "v"(s0[j]), "v"(s1[j]), "v"(s2[j]), "v"(r[j]), "v"(b[j]));
+            load_line(d);
+            const float hl0 = from_prev(h[K - 1]);
+            const float hrK = from_next(h[0]);
+            float hn[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const float hl = j > 0 ? h[j - 1] : hl0;
+                const float hr = j < K - 1 ? h[j + 1] : hrK;
+                float m = s1[j] * h[j];
+                m = fmaf(s0[j], hl, m);
+                m = fmaf(s2[j], hr, m);
+                hn[j] = fmaf(m, r[j], b[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                h[j] = hn[j];
+                lds_at<float>(aH[j]) = hn[j];
+                aH[j] += dH[j];
+            }
+        };
+        int s0 = 0;
+        for (; s0 + D <= NL; s0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) step(d);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (s0 + d < NL) step(d);
+    }
+    lds_order();
+
+    // --------------------------------------------------------- S = h_a + h_b
+    // (line-major order is pixel order for the row pair; for the column pair
+    // pixel (r, c) is position r of line c)
+    if constexpr (!Cols) {
+        f32x4_t* sp = reinterpret_cast<f32x4_t*>(s_ws + pix0);
+        for (int e = lane; e < HW / 4; e += 64)
+            sp[e] = lds_at<f32x4_t>(lay.a + 16u * e) + lds_at<f32x4_t>(lay.b + 16u * e);
+    } else {
+        const int W = NL, H = L;
+        const float invW = 1.0f / static_cast<float>(W);
+        for (int e2 = lane; e2 < HW / 2; e2 += 64) {
+            const int e = 2 * e2;
+            const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
+            const int c = e - r * W;
+            const uint32_t o0 = 4u * (c * H + r), o1 = o0 + 4u * H;
+            const f32x2_t sr = reinterpret_cast<const f32x2_t*>(s_ws + pix0)[e2];
+            const float v0 = sr.x + (lds_at<float>(lay.a + o0) + lds_at<float>(lay.b + o0));
+            const float v1 = sr.y + (lds_at<float>(lay.a + o1) + lds_at<float>(lay.b + o1));
+            const f32x2_t g2 = load_pair(gy, pix0 + e);
+            store_pair(gu, pix0 + e, g2.x * v0, g2.y * v1);
+        }
+    }
+    lds_order();
+
+    // ------------------------------------------------------------ adjoint
+    {
+        // lanes 0-31 walk their lines NL-1 .. 0, lanes 32-63 walk 0 .. NL-1
+        const int i0 = fwd ? NL - 1 : 0;
+        const uint32_t lo0 = static_cast<uint32_t>(i0) * line_b;
+        const uint32_t dlo = fwd ? 0u - line_b : line_b;
+        uint32_t lo = tap_b + win_b + lo0;
+        uint32_t uo = static_cast<uint32_t>(pix0) * ES + win_b + lo0;
+        uint32_t so = tap_b + lo0;          // line offset of the tap-gradient stores
+        words_t<NW> tbuf[D][3], ubuf[D], gbuf[D];
+        auto load_line = [&](int d) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
+            ubuf[d] = load_words<NW>(us, uo);
+            gbuf[d] = load_words<NW>(gs, uo);
+            lo += dlo;
+            uo += dlo;
+        };
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_line(d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const TapStore<T, K> st(q, L);
+        // LDS: g_i goes to line i; h_{i-1} (lanes 0-31) or h_{i+1} (32-63)
+        // is read one step ahead
+        const int dl = fwd ? -4 * L : 4 * L;
+        uint32_t aG[K], aP[K];
+        int dG[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            aG[j] = valid[j] ? plane_base + 4u * (i0 * L + K * q + j) : PairBwdLayout::dum + 4u * j;
+            aP[j] = valid[j] ? aG[j] + dl : aG[j];
+            dG[j] = valid[j] ? dl : 0;
+        }
+        float hp[K], gp[K], w0p[K], w1p[K], w2p[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            hp[j] = lds_at<float>(aP[j]);
+            gp[j] = w0p[j] = w1p[j] = w2p[j] = 0.0f;
+        }
+
+        auto step = [&](int d) {
+            asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
+            asm volatile("" : "+v"(ubuf[d]), "+v"(gbuf[d]));
+            float s0[K], s1[K], s2[K], t[K], r[K], ugy[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                ugy[j] = window_elem<T, K, NW>(ubuf[d], j, sel_even, sel_odd) *
+                         window_elem<T, K, NW>(gbuf[d], j, sel_even, sel_odd);
+            normalise(tbuf[d], s0, s1, s2, t, r);
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                asm volatile("" : "+v"(lo), "+v"(uo) : "v"(s0[j]), "v"(s1[j]), "v"(s2[j]), "v"(r[j]), "v"(ugy[j]));
+            load_line(d);
+
+            // g_i from the next line's transposed products
+            float P0[K], P2[K], g[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                P0[j] = w0p[j] * gp[j];
+                P2[j] = w2p[j] * gp[j];
+                g[j] = fmaf(w1p[j], gp[j], ugy[j]);
+            }
+            const float P0n = from_next(P0[0]);
+            const float P2p = from_prev(P2[K - 1]);
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                g[j] += j < K - 1 ? P0[j + 1] : P0n;
+                g[j] += j > 0 ? P2[j - 1] : P2p;
+            }
+
+            // tap gradients of line i
+            const float hl0 = from_prev(hp[K - 1]);
+            const float hrK = from_next(hp[0]);
+            float gz0[K], gz1[K], gz2[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const float hl = j > 0 ? hp[j - 1] : hl0;
+                const float hr = j < K - 1 ? hp[j + 1] : hrK;
+                const float e0 = g[j] * hl, e1 = g[j] * hp[j], e2 = g[j] * hr;
+                const float wn0 = s0[j] * r[j], wn1 = s1[j] * r[j], wn2 = s2[j] * r[j];
+                float n0 = e0, n1 = e1, n2 = e2;
+                if (t[j] > eps) {
+                    const float d01 = e0 - e1, d02 = e0 - e2, d12 = e1 - e2;
+                    n0 = fmaf(wn1, d01, wn2 * d02);
+                    n1 = fmaf(wn2, d12, -(wn0 * d01));
+                    n2 = -fmaf(wn0, d02, wn1 * d12);
+                }
+                // s (1 - s) is 0 for a dropped tap, so its gradient is 0
+                gz0[j] = n0 * (r[j] * fmaf(-s0[j], s0[j], s0[j]));
+                gz1[j] = n1 * (r[j] * fmaf(-s1[j], s1[j], s1[j]));
+                gz2[j] = n2 * (r[j] * fmaf(-s2[j], s2[j], s2[j]));
+                w0p[j] = wn0;
+                w1p[j] = wn1;
+                w2p[j] = wn2;
+            }
+            st.put(gws[0], so, gz0);
+            st.put(gws[1], so, gz1);
+            st.put(gws[2], so, gz2);
+            so += dlo;
+
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                gp[j] = g[j];
+                lds_at<float>(aG[j]) = g[j];
+                aG[j] += dG[j];
+                aP[j] += dG[j];
+                hp[j] = lds_at<float>(aP[j]);
+            }
+        };
+        int s0 = 0;
+        for (; s0 + D <= NL; s0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) step(d);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (s0 + d < NL) step(d);
+    }
+    lds_order();
+
+    // --------------------------------------------------------- G = g_a + g_b
+    if constexpr (!Cols) {
+        f32x4_t* gp4 = reinterpret_cast<f32x4_t*>(g_ws + pix0);
+        for (int e = lane; e < HW / 4; e += 64)
+            gp4[e] = lds_at<f32x4_t>(lay.a + 16u * e) + lds_at<f32x4_t>(lay.b + 16u * e);
+    } else {
+        const int W = NL, H = L;
+        const float invW = 1.0f / static_cast<float>(W);
+        for (int e2 = lane; e2 < HW / 2; e2 += 64) {
+            const int e = 2 * e2;
+            const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
+            const int c = e - r * W;
+            const uint32_t o0 = 4u * (c * H + r), o1 = o0 + 4u * H;
+            const f32x2_t gr = reinterpret_cast<const f32x2_t*>(g_ws + pix0)[e2];
+            const float v0 = gr.x + (lds_at<float>(lay.a + o0) + lds_at<float>(lay.b + o0));
+            const float v1 = gr.y + (lds_at<float>(lay.a + o1) + lds_at<float>(lay.b + o1));
+            const f32x2_t l2 = load_pair(lam, pix0 + e);
+            const f32x2_t x2 = load_pair(x, pix0 + e);
+            store_pair(gx, pix0 + e, l2.x * v0, l2.y * v1);
+            store_pair(glam, pix0 + e, x2.x * v0, x2.y * v1);
+        }
+    }
+}
+
+// x, lambda, u, gy of every plane transposed ([H][W] -> [W][H]); one
+// workgroup per (plane, tensor), the plane staged in LDS.
+template <typename T>
+__global__ void __launch_bounds__(256)
+transpose4_kernel(const T* __restrict__ a0, const T* __restrict__ a1, const T* __restrict__ a2,
+                  const T* __restrict__ a3, T* __restrict__ t0, T* __restrict__ t1,
+                  T* __restrict__ t2, T* __restrict__ t3, int H, int W) {
+    extern __shared__ float tile[];
+    const int which = blockIdx.y;
+    const T* src = which == 0 ? a0 : which == 1 ? a1 : which == 2 ? a2 : a3;
+    T* dst = which == 0 ? t0 : which == 1 ? t1 : which == 2 ? t2 : t3;
+    const int HW = H * W;
+    const size_t base = static_cast<size_t>(blockIdx.x) * HW;
+    for (int e = threadIdx.x; e < HW; e += 256) tile[e] = load_elem(src, base + e);
+    __syncthreads();
+    for (int e = threadIdx.x; e < HW; e += 256) {
+        const int c = e / H, r = e - c * H;
+        store_elem(dst, base + e, tile[r * W + c]);
+    }
+}
+
+// Workspace regions (bytes, 256-aligned): x, lambda, u, gy transposed, then
+// S and G of the row pair in fp32.
+struct PairBwdWs {
+    int64_t xt, lt, ut, gt, s, g, bytes;
+    PairBwdWs(int64_t planes, int64_t H, int64_t W, int64_t es) {
+        auto a256 = [](int64_t v) { return (v + 255) & ~static_cast<int64_t>(255); };
+        const int64_t n = planes * H * W;
+        xt = 0;
+        lt = a256(xt + n * es);
+        ut = a256(lt + n * es);
+        gt = a256(ut + n * es);
+        s = a256(gt + n * es);
+        g = a256(s + n * 4);
+        bytes = a256(g + n * 4);
+    }
+};
+
+template <typename T, int K, bool Cols>
+hipError_t launch_pass(const T* xl, const T* ll, const T* ul, const T* gl, const T* w4, T* gw4,
+                       float eps, int64_t planes, int64_t NL, int64_t L, int dir0, float* s_ws,
+                       float* g_ws, const T* x, const T* lam, const T* gy, T* gx, T* glam, T* gu,
+                       hipStream_t stream) {
+    constexpr int D = 8;
+    const size_t lds = PairBwdLayout(static_cast<int>(NL), static_cast<int>(L)).bytes;
+    auto kern = prop2d_backward_pair_kernel<T, K, D, Cols>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    const int64_t n = planes * NL * L;
+    kern<<<dim3(static_cast<unsigned>(planes)), dim3(64), lds, stream>>>(
+        xl, ll, ul, gl, w4, gw4, static_cast<int>(12 * n * sizeof(T)), eps, static_cast<int>(planes),
+        static_cast<int>(NL), static_cast<int>(L), dir0, s_ws, g_ws, x, lam, gy, gx, glam, gu);
+    return hipGetLastError();
+}
+
+template <typename T, bool Cols>
+hipError_t launch_pass_k(const T* xl, const T* ll, const T* ul, const T* gl, const T* w4, T* gw4,
+                         float eps, int64_t planes, int64_t NL, int64_t L, int dir0, float* s_ws,
+                         float* g_ws, const T* x, const T* lam, const T* gy, T* gx, T* glam, T* gu,
+                         hipStream_t stream) {
+    if (L <= 32)
+        return launch_pass<T, 1, Cols>(xl, ll, ul, gl, w4, gw4, eps, planes, NL, L, dir0, s_ws, g_ws,
+                                       x, lam, gy, gx, glam, gu, stream);
+    if (L <= 64)
+        return launch_pass<T, 2, Cols>(xl, ll, ul, gl, w4, gw4, eps, planes, NL, L, dir0, s_ws, g_ws,
+                                       x, lam, gy, gx, glam, gu, stream);
+    return launch_pass<T, 3, Cols>(xl, ll, ul, gl, w4, gw4, eps, planes, NL, L, dir0, s_ws, g_ws,
+                                   x, lam, gy, gx, glam, gu, stream);
+}
+
+template <typename T>
+hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, const void* w4_,
+                           const void* gy_, float eps, void* gx_, void* glam_, void* gu_, void* gw4_,
+                           void* ws_, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
+    const T* x = static_cast<const T*>(x_);
+    const T* lam = static_cast<const T*>(lam_);
+    const T* u = static_cast<const T*>(u_);
+    const T* w4 = static_cast<const T*>(w4_);
+    const T* gy = static_cast<const T*>(gy_);
+    T* gx = static_cast<T*>(gx_);
+    T* glam = static_cast<T*>(glam_);
+    T* gu = static_cast<T*>(gu_);
+    T* gw4 = static_cast<T*>(gw4_);
+    char* ws = static_cast<char*>(ws_);
+    const PairBwdWs lay(planes, H, W, sizeof(T));
+    T* xt = reinterpret_cast<T*>(ws + lay.xt);
+    T* lt = reinterpret_cast<T*>(ws + lay.lt);
+    T* ut = reinterpret_cast<T*>(ws + lay.ut);
+    T* gt = reinterpret_cast<T*>(ws + lay.gt);
+    float* s_ws = reinterpret_cast<float*>(ws + lay.s);
+    float* g_ws = reinterpret_cast<float*>(ws + lay.g);
+
+    // row pair on the inputs as they are: taps and gradients of directions 0, 1
+    hipError_t e = launch_pass_k<T, false>(x, lam, u, gy, w4, gw4, eps, planes, H, W, 0, s_ws, g_ws,
+                                           x, lam, gy, gx, glam, gu, stream);
+    if (e != hipSuccess) return e;
+    transpose4_kernel<T><<<dim3(static_cast<unsigned>(planes), 4), dim3(256),
+                           static_cast<size_t>(H * W) * sizeof(float), stream>>>(
+        x, lam, u, gy, xt, lt, ut, gt, static_cast<int>(H), static_cast<int>(W));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // column pair on the transposed copies: directions 2, 3, then the outputs
+    return launch_pass_k<T, true>(xt, lt, ut, gt, w4, gw4, eps, planes, W, H, 2, s_ws, g_ws, x, lam,
+                                  gy, gx, glam, gu, stream);
+}
+
+}  // namespace
+
+bool prop2d_backward_pair_shape(int64_t planes, int64_t H, int64_t W) {
+    if (H < 2 || W < 2 || H > 96 || W > 96 || (H & 1) || (W & 1)) return false;
+    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W)).bytes > kLdsBytes ||
+        PairBwdLayout(static_cast<int>(W), static_cast<int>(H)).bytes > kLdsBytes)
+        return false;
+    // every stream offset is a 32-bit byte offset into one buffer resource
+    return 12 * planes * H * W * 4 <= 0x7fffffff;
+}
+
+int64_t prop2d_backward_pair_workspace_bytes(int64_t planes, int64_t H, int64_t W) {
+    return PairBwdWs(planes, H, W, 4).bytes;   // fp32 storage needs the most
+}
+
+bool prop2d_backward_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t W,
+                                   const void* const* ptrs, int nptrs, const void* ws) {
+    if (ws == nullptr || !prop2d_backward_pair_shape(planes, H, W)) return false;
+    // pixel pairs are read and written whole: 8 bytes in fp32, 4 in bf16
+    const uintptr_t mask = dtype == 0 ? 7u : 3u;
+    for (int i = 0; i < nptrs; ++i)
+        if (reinterpret_cast<uintptr_t>(ptrs[i]) & mask) return false;
+    return (reinterpret_cast<uintptr_t>(ws) & 15u) == 0;
+}
+
+hipError_t launch_prop2d_backward_pair(const void* x, const void* lam, const void* u,
+                                       const void* w4, const void* gy, float eps, void* gx,
+                                       void* glam, void* gu, void* gw4, void* ws, int dtype,
+                                       int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
+    return dtype == 0
+               ? backward_pair_t<float>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W, stream)
+               : backward_pair_t<uint16_t>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W,
+                                           stream);
+}
+
+}  // namespace gspn

@@ -54,6 +54,18 @@ hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u,
                                   void* gw4, void* ws, int dtype, int64_t planes, int64_t H,
                                   int64_t W, hipStream_t stream);
 int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W);
+
+// Fast path of the gradient for planes of even sides up to 96: one wavefront
+// per plane and direction pair (gspn_backward_pair.hip).  Needs a workspace of
+// prop2d_backward_pair_workspace_bytes bytes, 16-byte aligned.
+bool prop2d_backward_pair_shape(int64_t planes, int64_t H, int64_t W);
+int64_t prop2d_backward_pair_workspace_bytes(int64_t planes, int64_t H, int64_t W);
+bool prop2d_backward_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t W,
+                                   const void* const* ptrs, int nptrs, const void* ws);
+hipError_t launch_prop2d_backward_pair(const void* x, const void* lam, const void* u,
+                                       const void* w4, const void* gy, float eps, void* gx,
+                                       void* glam, void* gu, void* gw4, void* ws, int dtype,
+                                       int64_t planes, int64_t H, int64_t W, hipStream_t stream);
 // Longest line the backward's LDS lines allow.
 int64_t prop2d_backward_max_line();
 

@@ -65,9 +65,13 @@ def test_backward_small_workloads(name):
         _check(_run(p), _oracle(p), wl.dtype, "%s seed %d" % (name, seed))
 
 
-# (148, 148) and (120, 120) exceed on-chip memory: the workspace path
+# Even sides up to 96 take the one-wavefront-per-direction-pair kernel (its
+# lines cover 1, 2 or 3 positions per lane; the two launches of a plane can
+# differ); the rest the general kernel, whose planes leave LDS at (148, 148)
+# and (120, 120).
 BWD_SHAPES = [(1, 1), (1, 2), (2, 1), (3, 5), (5, 3), (1, 74), (74, 1), (63, 64), (74, 74),
-              (127, 33), (13, 148), (120, 120), (148, 148), (300, 5), (5, 300)]
+              (127, 33), (13, 148), (120, 120), (148, 148), (300, 5), (5, 300),
+              (2, 2), (2, 96), (96, 2), (32, 34), (34, 32), (64, 66), (96, 96), (30, 66), (8, 74)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -112,9 +116,10 @@ def test_backward_deterministic(H, W, dtype):
         assert torch.equal(x.view(iv), y.view(iv))
 
 
-def test_backward_clamp_and_saturated_logits():
-    say("backward clamp")
-    B, C, H, W = 1, 4, 9, 11
+@pytest.mark.parametrize("H,W", [(9, 11), (10, 12)])
+def test_backward_clamp_and_saturated_logits(H, W):
+    say("backward clamp", H, W)
+    B, C = 1, 4
     p = _problem(B, C, H, W, 3, "fp32")
     w = p["w"].clone().view(4, B, C, 3, H * W)
     w[:, :, 0] = -20.0 + 0.3 * w[:, :, 0]
