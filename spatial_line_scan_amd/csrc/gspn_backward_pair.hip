@@ -40,6 +40,8 @@
 #include "gspn_internal.h"
 #include "gspn_lane.h"
 
+#include <type_traits>
+
 namespace gspn {
 namespace {
 
@@ -231,6 +233,46 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         }
     };
 
+    // Column launch, after each phase: for every pixel pair (r, c), (r, c+1)
+    // in row-major order, v = part (the row pair's sum, workspace) + the
+    // column pair's sum (LDS, position r of lines c and c+1); out0 = m0 * v
+    // and, with Two, out1 = m1 * v.  The global loads of U pairs per lane are
+    // issued before any of them is used (these loads, not the arithmetic,
+    // set the time of the pass).
+    auto column_pass = [&](const float* part, const T* m0, const T* m1, T* out0, T* out1,
+                           auto two_tag) {
+        constexpr bool kTwo = decltype(two_tag)::value;
+        constexpr int U = 24;
+        const int W = NL, H = L, npairs = HW / 2;
+        const float invW = 1.0f / static_cast<float>(W);
+        const f32x2_t* pp = reinterpret_cast<const f32x2_t*>(part + pix0);
+        for (int base = 0; base < npairs; base += 64 * U) {
+            f32x2_t pv[U], a[U], b[U];
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                // clamped to the last pair: in bounds, the value is not used
+                const int e2 = min(base + 64 * k + lane, npairs - 1);
+                pv[k] = pp[e2];
+                a[k] = load_pair(m0, pix0 + 2 * e2);
+                if constexpr (kTwo) b[k] = load_pair(m1, pix0 + 2 * e2);
+            }
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const int e2 = base + 64 * k + lane;
+                if (e2 < npairs) {
+                    const int e = 2 * e2;
+                    const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
+                    const int c = e - r * W;
+                    const uint32_t o0 = 4u * (c * H + r), o1 = o0 + 4u * H;
+                    const float v0 = pv[k].x + (lds_at<float>(lay.a + o0) + lds_at<float>(lay.b + o0));
+                    const float v1 = pv[k].y + (lds_at<float>(lay.a + o1) + lds_at<float>(lay.b + o1));
+                    store_pair(out0, pix0 + e, a[k].x * v0, a[k].y * v1);
+                    if constexpr (kTwo) store_pair(out1, pix0 + e, b[k].x * v0, b[k].y * v1);
+                }
+            }
+        }
+    };
+
     // ------------------------------------------------------------ forward
     {
         const uint32_t lo0 = fwd ? 0u : static_cast<uint32_t>(NL - 1) * line_b;
@@ -315,19 +357,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         for (int e = lane; e < HW / 4; e += 64)
             sp[e] = lds_at<f32x4_t>(lay.a + 16u * e) + lds_at<f32x4_t>(lay.b + 16u * e);
     } else {
-        const int W = NL, H = L;
-        const float invW = 1.0f / static_cast<float>(W);
-        for (int e2 = lane; e2 < HW / 2; e2 += 64) {
-            const int e = 2 * e2;
-            const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
-            const int c = e - r * W;
-            const uint32_t o0 = 4u * (c * H + r), o1 = o0 + 4u * H;
-            const f32x2_t sr = reinterpret_cast<const f32x2_t*>(s_ws + pix0)[e2];
-            const float v0 = sr.x + (lds_at<float>(lay.a + o0) + lds_at<float>(lay.b + o0));
-            const float v1 = sr.y + (lds_at<float>(lay.a + o1) + lds_at<float>(lay.b + o1));
-            const f32x2_t g2 = load_pair(gy, pix0 + e);
-            store_pair(gu, pix0 + e, g2.x * v0, g2.y * v1);
-        }
+        column_pass(s_ws, gy, gy, gu, gu, std::false_type{});
     }
     lds_order();
 
@@ -459,42 +489,54 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         for (int e = lane; e < HW / 4; e += 64)
             gp4[e] = lds_at<f32x4_t>(lay.a + 16u * e) + lds_at<f32x4_t>(lay.b + 16u * e);
     } else {
-        const int W = NL, H = L;
-        const float invW = 1.0f / static_cast<float>(W);
-        for (int e2 = lane; e2 < HW / 2; e2 += 64) {
-            const int e = 2 * e2;
-            const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
-            const int c = e - r * W;
-            const uint32_t o0 = 4u * (c * H + r), o1 = o0 + 4u * H;
-            const f32x2_t gr = reinterpret_cast<const f32x2_t*>(g_ws + pix0)[e2];
-            const float v0 = gr.x + (lds_at<float>(lay.a + o0) + lds_at<float>(lay.b + o0));
-            const float v1 = gr.y + (lds_at<float>(lay.a + o1) + lds_at<float>(lay.b + o1));
-            const f32x2_t l2 = load_pair(lam, pix0 + e);
-            const f32x2_t x2 = load_pair(x, pix0 + e);
-            store_pair(gx, pix0 + e, l2.x * v0, l2.y * v1);
-            store_pair(glam, pix0 + e, x2.x * v0, x2.y * v1);
-        }
+        column_pass(g_ws, lam, x, gx, glam, std::true_type{});
     }
 }
 
-// x, lambda, u, gy of every plane transposed ([H][W] -> [W][H]); one
-// workgroup per (plane, tensor), the plane staged in LDS.
+// x, lambda, u, gy of every plane transposed ([H][W] -> [W][H], H and W
+// even); one workgroup per (plane, tensor).  The plane is staged in LDS as
+// 32-bit words with a row pitch of W + 1 (odd, so the column reads of
+// consecutive rows fall in different banks); global reads and writes move
+// element pairs.
 template <typename T>
 __global__ void __launch_bounds__(256)
 transpose4_kernel(const T* __restrict__ a0, const T* __restrict__ a1, const T* __restrict__ a2,
                   const T* __restrict__ a3, T* __restrict__ t0, T* __restrict__ t1,
                   T* __restrict__ t2, T* __restrict__ t3, int H, int W) {
-    extern __shared__ float tile[];
+    extern __shared__ uint32_t tile[];
     const int which = blockIdx.y;
     const T* src = which == 0 ? a0 : which == 1 ? a1 : which == 2 ? a2 : a3;
     T* dst = which == 0 ? t0 : which == 1 ? t1 : which == 2 ? t2 : t3;
-    const int HW = H * W;
+    const int HW = H * W, pitch = W + 1, npairs = HW / 2;
     const size_t base = static_cast<size_t>(blockIdx.x) * HW;
-    for (int e = threadIdx.x; e < HW; e += 256) tile[e] = load_elem(src, base + e);
+    const float invW = 1.0f / static_cast<float>(W), invH = 1.0f / static_cast<float>(H);
+    // with e < 96 * 96 and n <= 96, (e + 0.5) / n in fp32 stays within 6e-4 of
+    // its value, whose distance to an integer is at least 0.5 / n: the quotient is exact
+    for (int t = threadIdx.x; t < npairs; t += 256) {
+        const int e = 2 * t;
+        const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
+        const int c = e - r * W;
+        uint32_t v0, v1;
+        if constexpr (sizeof(T) == 4) {
+            const uint2 w = *reinterpret_cast<const uint2*>(src + base + e);
+            v0 = w.x;
+            v1 = w.y;
+        } else {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(src + base + e);
+            v0 = w & 0xffffu;
+            v1 = w >> 16;
+        }
+        tile[r * pitch + c] = v0;
+        tile[r * pitch + c + 1] = v1;
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < HW; e += 256) {
-        const int c = e / H, r = e - c * H;
-        store_elem(dst, base + e, tile[r * W + c]);
+    for (int t = threadIdx.x; t < npairs; t += 256) {
+        const int e = 2 * t;                 // output element (c, r), (c, r + 1)
+        const int c = static_cast<int>((static_cast<float>(e) + 0.5f) * invH);
+        const int r = e - c * H;
+        const uint32_t v0 = tile[r * pitch + c], v1 = tile[(r + 1) * pitch + c];
+        if constexpr (sizeof(T) == 4) *reinterpret_cast<uint2*>(dst + base + e) = make_uint2(v0, v1);
+        else *reinterpret_cast<uint32_t*>(dst + base + e) = v0 | (v1 << 16);
     }
 }
 
@@ -578,7 +620,7 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
                                            x, lam, gy, gx, glam, gu, stream);
     if (e != hipSuccess) return e;
     transpose4_kernel<T><<<dim3(static_cast<unsigned>(planes), 4), dim3(256),
-                           static_cast<size_t>(H * W) * sizeof(float), stream>>>(
+                           static_cast<size_t>(H * (W + 1)) * sizeof(uint32_t), stream>>>(
         x, lam, u, gy, xt, lt, ut, gt, static_cast<int>(H), static_cast<int>(W));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // column pair on the transposed copies: directions 2, 3, then the outputs
