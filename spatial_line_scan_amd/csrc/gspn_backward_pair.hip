@@ -63,67 +63,70 @@ __device__ __forceinline__ void lds_order() {
 }
 
 // LDS layout in bytes (offsets multiples of 16):
-//   [dummy: 16][2 lines][A: NL x L][B: NL x L][2 lines]   fp32
+//   [dummy: 16][2 lines][A: NL x L][B: NL x L][2 lines] ... [staging: 6 x 96]
 // A is the plane of lanes 0-31, B that of lanes 32-63.  The line before A
 // and the line after B are zero: the h before a scan's first line.  The
 // outer lines only absorb the read-ahead past the last adjoint step.  Slots
 // past a line's end read and write the dummy words.
+// fp32 data: one array of fp32 values.  bf16 data (narrow): two arrays laid
+// out this way, the upper 16 bits and the next 8 bits of each fp32 value
+// rounded to nearest even at bit 8 (a 16-bit significand; the gradients are
+// rounded to bf16's 8 bits in the end), so that four planes share a CU at
+// 74 x 74.
 struct PairBwdLayout {
-    int a, b, bytes;
-    static constexpr int dum = 0;
+    int a, b, la, lb, stage, bytes;   // line 0 of A and B: fp32 or upper-16-bit array; low-8-bit
+                                      // array; tap-gradient staging lines
+    static constexpr int dum = 0, ldum = 8;
     __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
-    __host__ __device__ PairBwdLayout(int NL, int L) {
-        a = a16(16 + 8 * L);
-        b = a16(a + 4 * NL * L);
-        bytes = a16(b + 4 * (NL + 2) * L);
+    __host__ __device__ PairBwdLayout(int NL, int L, bool narrow) {
+        const int w = narrow ? 2 : 4;
+        a = a16(16 + 2 * w * L);
+        b = a16(a + w * NL * L);
+        int end = b + w * (NL + 2) * L;
+        la = lb = 0;
+        if (narrow) {
+            la = a16(end + 2 * L);
+            lb = a16(la + NL * L);
+            end = lb + (NL + 2) * L;
+        }
+        stage = a16(end);
+        bytes = stage + 6 * 96 * (narrow ? 2 : 4);
     }
 };
 
-// Stores of the K tap gradients of a lane's slots into one tap line, with
-// buffer stores whose offsets are pushed past the tensor for positions past
-// the line's end (the hardware drops them).
+// Tap gradients of one adjoint step go out through LDS: each lane puts the
+// values of its K slots into a staging line per (half, tap), 96 elements
+// apart so that slots past a line's end land in the padding, and the
+// wavefront then writes the six lines as whole dwords (stores of a few bytes
+// at a 6-byte stride cost far more).  kDrop pushes the offset of an unused
+// dword store past the tensor; the hardware drops it.
 constexpr uint32_t kDrop = 0x80000000u;
 
 template <typename T, int K>
-struct TapStore {
-    uint32_t o32, o16, oe[K];   // byte offsets within a line (kDrop for dropped stores)
-    bool even;
-    __device__ TapStore(int q, int L) {
-        even = (q & 1) == 0;
-        if constexpr (sizeof(T) == 4) {
-            for (int j = 0; j < K; ++j) oe[j] = K * q + j < L ? 4u * (K * q + j) : kDrop;
-        } else if constexpr (K == 1) {
-            o16 = q < L ? 2u * q : kDrop;
-        } else if constexpr (K == 2) {
-            o32 = 2 * q < L ? 4u * q : kDrop;   // L is even: 2q < L implies 2q + 1 < L
-        } else {
-            // even q: dword (3q, 3q+1), short 3q+2; odd q: short 3q, dword (3q+1, 3q+2)
-            const int p32 = even ? 3 * q : 3 * q + 1;
-            const int p16 = even ? 3 * q + 2 : 3 * q;
-            o32 = p32 < L ? 2u * p32 : kDrop;
-            o16 = p16 < L ? 2u * p16 : kDrop;
-        }
-    }
-    __device__ __forceinline__ void put(__amdgpu_buffer_rsrc_t r, uint32_t line_off, const float (&v)[K]) const {
-        if constexpr (sizeof(T) == 4) {
+__device__ __forceinline__ void stage_put(uint32_t line, int q, const float (&v)[K]) {
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    auto w32 = [](uint32_t a, uint32_t x) { *reinterpret_cast<lds_u32*>(static_cast<uintptr_t>(a)) = x; };
+    auto w16 = [](uint32_t a, uint32_t x) {
+        *reinterpret_cast<lds_u16*>(static_cast<uintptr_t>(a)) = static_cast<uint16_t>(x);
+    };
+    if constexpr (sizeof(T) == 4) {
 #pragma unroll
-            for (int j = 0; j < K; ++j)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), r, oe[j] + line_off, 0, 0);
-        } else if constexpr (K == 1) {
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(pack_bf16x2(v[0], v[0])), r,
-                                                  o16 + line_off, 0, 0);
-        } else if constexpr (K == 2) {
-            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[0], v[1]), r, o32 + line_off, 0, 0);
-        } else {
-            const float a = even ? v[0] : v[1];
-            const float b = even ? v[1] : v[2];
-            const float c = even ? v[2] : v[0];
-            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a, b), r, o32 + line_off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(pack_bf16x2(c, c)), r,
-                                                  o16 + line_off, 0, 0);
-        }
+        for (int j = 0; j < K; ++j) w32(line + 4u * (K * q + j), __float_as_uint(v[j]));
+    } else if constexpr (K == 1) {
+        w16(line + 2u * q, pack_bf16x2(v[0], v[0]));
+    } else if constexpr (K == 2) {
+        w32(line + 4u * q, pack_bf16x2(v[0], v[1]));
+    } else {
+        // even q: dword (3q, 3q+1), short 3q+2; odd q: short 3q, dword (3q+1, 3q+2)
+        const bool even = (q & 1) == 0;
+        const float a = even ? v[0] : v[1];
+        const float b = even ? v[1] : v[2];
+        const float c = even ? v[2] : v[0];
+        w32(line + (even ? 6u * q : 6u * q + 2u), pack_bf16x2(a, b));
+        w16(line + (even ? 6u * q + 4u : 6u * q), pack_bf16x2(c, c));
     }
-};
+}
 
 // Two consecutive pixels of an output plane.
 template <typename T>
@@ -157,8 +160,10 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                             T* __restrict__ gu) {
     constexpr int ES = sizeof(T);
     constexpr int NW = window_words<T, K>();
+    constexpr bool kNarrow = ES == 2;
+    constexpr int VW = kNarrow ? 2 : 4;     // bytes of a value in the A / B array
     const int HW = NL * L;
-    const PairBwdLayout lay(NL, L);
+    const PairBwdLayout lay(NL, L, kNarrow);
     const int lane = threadIdx.x;
     const int half = lane >> 5;
     const int q = lane & 31;
@@ -169,22 +174,62 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     // zero lines (h before a scan's first line) and the dummy words
     if (lane < 4) lds_at<float>(4u * lane) = 0.0f;
     for (int f = lane; f < L; f += 64) {
-        lds_at<float>(lay.a - 4 * L + 4 * f) = 0.0f;
-        lds_at<float>(lay.b + 4 * HW + 4 * f) = 0.0f;
+        if constexpr (kNarrow) {
+            lds_at<uint16_t>(lay.a - 2 * L + 2 * f) = 0;
+            lds_at<uint16_t>(lay.b + 2 * HW + 2 * f) = 0;
+            lds_at<uint8_t>(lay.la - L + f) = 0;
+            lds_at<uint8_t>(lay.lb + HW + f) = 0;
+        } else {
+            lds_at<float>(lay.a - 4 * L + 4 * f) = 0.0f;
+            lds_at<float>(lay.b + 4 * HW + 4 * f) = 0.0f;
+        }
     }
+    // one value of a plane: fp32, or its upper 24 bits (rounded to nearest
+    // even) in the two narrow arrays
+    auto put = [&](uint32_t ah, uint32_t al, float v) {
+        if constexpr (kNarrow) {
+            uint32_t w = __float_as_uint(v);
+            w += 0x7fu + ((w >> 8) & 1u);
+            lds_at<uint16_t>(ah) = static_cast<uint16_t>(w >> 16);
+            lds_at<uint8_t>(al) = static_cast<uint8_t>(w >> 8);
+        } else {
+            lds_at<float>(ah) = v;
+        }
+    };
+    auto get = [&](uint32_t ah, uint32_t al) -> float {
+        if constexpr (kNarrow)
+            return __uint_as_float(__builtin_amdgcn_perm(static_cast<uint32_t>(lds_at<uint16_t>(ah)),
+                                                         static_cast<uint32_t>(lds_at<uint8_t>(al)),
+                                                         0x0504000cu));
+        else
+            return lds_at<float>(ah);
+    };
+    // four consecutive values from array offset (in values) e4 * 4
+    auto get4 = [&](int base, int lbase, int e4) -> f32x4_t {
+        if constexpr (kNarrow) {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t hi = lds_at<u32x2_t>(base + 8u * e4);
+            const uint32_t lo = lds_at<uint32_t>(lbase + 4u * e4);
+            return f32x4_t{__uint_as_float(__builtin_amdgcn_perm(hi.x, lo, 0x0504000cu)),
+                           __uint_as_float(__builtin_amdgcn_perm(hi.x, lo, 0x0706010cu)),
+                           __uint_as_float(__builtin_amdgcn_perm(hi.y, lo, 0x0504020cu)),
+                           __uint_as_float(__builtin_amdgcn_perm(hi.y, lo, 0x0706030cu))};
+        } else {
+            return lds_at<f32x4_t>(base + 16u * e4);
+        }
+    };
 
     const int in_bytes = planes * HW * ES;
     const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xl), 0, in_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(laml), 0, in_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t us = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(ul), 0, in_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t gs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(gyl), 0, in_bytes, kBufFlags);
-    __amdgpu_buffer_rsrc_t taps[3], gws[3];
+    __amdgpu_buffer_rsrc_t taps[3];
+    const __amdgpu_buffer_rsrc_t gws = __builtin_amdgcn_make_buffer_rsrc(gw4, 0, w4_bytes, kBufFlags);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + static_cast<size_t>(k) * HW), 0,
                                                     w4_bytes - k * HW * ES, kBufFlags);
-        gws[k] = __builtin_amdgcn_make_buffer_rsrc(gw4 + static_cast<size_t>(k) * HW, 0,
-                                                   w4_bytes - k * HW * ES, kBufFlags);
     }
     const int par = ES == 2 ? ((K * q) & 1) : 0;
     const uint32_t win_b = static_cast<uint32_t>(K * q - par) * ES;
@@ -193,6 +238,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     const uint32_t tap_b = static_cast<uint32_t>(((dir0 + half) * planes + plane) * 3 * HW) * ES;
     const uint32_t line_b = static_cast<uint32_t>(L) * ES;
     const uint32_t plane_base = half ? lay.b : lay.a;
+    const uint32_t lplane_base = half ? lay.lb : lay.la;
 
     float c0[K], c1[K], c2[K];
     bool valid[K];
@@ -263,9 +309,9 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                     const int e = 2 * e2;
                     const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
                     const int c = e - r * W;
-                    const uint32_t o0 = 4u * (c * H + r), o1 = o0 + 4u * H;
-                    const float v0 = pv[k].x + (lds_at<float>(lay.a + o0) + lds_at<float>(lay.b + o0));
-                    const float v1 = pv[k].y + (lds_at<float>(lay.a + o1) + lds_at<float>(lay.b + o1));
+                    const uint32_t i0 = c * H + r, i1 = i0 + H;
+                    const float v0 = pv[k].x + (get(lay.a + VW * i0, lay.la + i0) + get(lay.b + VW * i0, lay.lb + i0));
+                    const float v1 = pv[k].y + (get(lay.a + VW * i1, lay.la + i1) + get(lay.b + VW * i1, lay.lb + i1));
                     store_pair(out0, pix0 + e, a[k].x * v0, a[k].y * v1);
                     if constexpr (kTwo) store_pair(out1, pix0 + e, b[k].x * v0, b[k].y * v1);
                 }
@@ -294,13 +340,16 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             __builtin_amdgcn_sched_barrier(0);
         }
         const int i0 = fwd ? 0 : NL - 1;
-        const int dl = fwd ? 4 * L : -4 * L;
-        uint32_t aH[K];
-        int dH[K];
+        const int dl = fwd ? L : -L;       // values per line step
+        uint32_t aH[K], aL[K];
+        int dH[K], dL[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            aH[j] = valid[j] ? plane_base + 4u * (i0 * L + K * q + j) : PairBwdLayout::dum + 4u * j;
-            dH[j] = valid[j] ? dl : 0;
+            const int v = i0 * L + K * q + j;
+            aH[j] = valid[j] ? plane_base + VW * v : PairBwdLayout::dum + VW * j;
+            aL[j] = valid[j] ? lplane_base + v : PairBwdLayout::ldum + j;
+            dH[j] = valid[j] ? VW * dl : 0;
+            dL[j] = valid[j] ? dl : 0;
         }
         float h[K];
 #pragma unroll
@@ -334,8 +383,9 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
 #pragma unroll
             for (int j = 0; j < K; ++j) {
                 h[j] = hn[j];
-                lds_at<float>(aH[j]) = hn[j];
+                put(aH[j], aL[j], hn[j]);
                 aH[j] += dH[j];
+                aL[j] += dL[j];
             }
         };
         int s0 = 0;
@@ -354,8 +404,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     // pixel (r, c) is position r of line c)
     if constexpr (!Cols) {
         f32x4_t* sp = reinterpret_cast<f32x4_t*>(s_ws + pix0);
-        for (int e = lane; e < HW / 4; e += 64)
-            sp[e] = lds_at<f32x4_t>(lay.a + 16u * e) + lds_at<f32x4_t>(lay.b + 16u * e);
+        for (int e = lane; e < HW / 4; e += 64) sp[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
     } else {
         column_pass(s_ws, gy, gy, gu, gu, std::false_type{});
     }
@@ -369,7 +418,6 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         const uint32_t dlo = fwd ? 0u - line_b : line_b;
         uint32_t lo = tap_b + win_b + lo0;
         uint32_t uo = static_cast<uint32_t>(pix0) * ES + win_b + lo0;
-        uint32_t so = tap_b + lo0;          // line offset of the tap-gradient stores
         words_t<NW> tbuf[D][3], ubuf[D], gbuf[D];
         auto load_line = [&](int d) {
 #pragma unroll
@@ -384,22 +432,48 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             load_line(d);
             __builtin_amdgcn_sched_barrier(0);
         }
-        const TapStore<T, K> st(q, L);
-        // LDS: g_i goes to line i; h_{i-1} (lanes 0-31) or h_{i+1} (32-63)
-        // is read one step ahead
-        const int dl = fwd ? -4 * L : 4 * L;
-        uint32_t aG[K], aP[K];
-        int dG[K];
+        // read-back of the staging lines: dword f = lane + 64 t of the six
+        // lines of L ES / 4 dwords, stored at its place on the current line of
+        // its half's tap plane
+        constexpr int NT = ES == 2 ? 5 : 9;     // ceil(6 * 96 * ES / 4 / 64)
+        const int per_line = L * ES / 4;
+        uint32_t rd[NT], go[NT], gd[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int f = lane + 64 * t;
+            rd[t] = lay.stage;
+            go[t] = kDrop;
+            gd[t] = 0;
+            if (f < 6 * per_line) {
+                const int hk = f / per_line, m = f - hk * per_line;
+                const int h = hk / 3, k = hk - 3 * h;
+                const int start = h == 0 ? NL - 1 : 0;      // first adjoint line of that half
+                rd[t] = lay.stage + hk * 96 * ES + 4 * m;
+                go[t] = static_cast<uint32_t>((((dir0 + h) * planes + plane) * 3 + k) * HW * ES +
+                                              start * L * ES + 4 * m);
+                gd[t] = h == 0 ? 0u - line_b : line_b;
+            }
+        }
+        const uint32_t my_stage = lay.stage + 3 * half * 96 * ES;
+        // LDS: g_i goes to line i (G); h_{i-1} (lanes 0-31) or h_{i+1}
+        // (32-63) is read one step ahead (P), and P of one step is G of the next
+        const int dl = fwd ? -L : L;       // values per step
+        uint32_t aGH[K], aGL[K], aPH[K], aPL[K];
+        int dH[K], dL[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            aG[j] = valid[j] ? plane_base + 4u * (i0 * L + K * q + j) : PairBwdLayout::dum + 4u * j;
-            aP[j] = valid[j] ? aG[j] + dl : aG[j];
-            dG[j] = valid[j] ? dl : 0;
+            const int v = i0 * L + K * q + j;
+            aGH[j] = valid[j] ? plane_base + VW * v : PairBwdLayout::dum + VW * j;
+            aGL[j] = valid[j] ? lplane_base + v : PairBwdLayout::ldum + j;
+            dH[j] = valid[j] ? VW * dl : 0;
+            dL[j] = valid[j] ? dl : 0;
+            aPH[j] = aGH[j] + dH[j];
+            aPL[j] = aGL[j] + dL[j];
         }
         float hp[K], gp[K], w0p[K], w1p[K], w2p[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            hp[j] = lds_at<float>(aP[j]);
+            hp[j] = get(aPH[j], aPL[j]);
             gp[j] = w0p[j] = w1p[j] = w2p[j] = 0.0f;
         }
 
@@ -458,18 +532,28 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 w1p[j] = wn1;
                 w2p[j] = wn2;
             }
-            st.put(gws[0], so, gz0);
-            st.put(gws[1], so, gz1);
-            st.put(gws[2], so, gz2);
-            so += dlo;
+            stage_put<T, K>(my_stage, q, gz0);
+            stage_put<T, K>(my_stage + 96 * ES, q, gz1);
+            stage_put<T, K>(my_stage + 2 * 96 * ES, q, gz2);
+            // the staging lines are written with 16- and 32-bit stores and read
+            // back as dwords: keep the compiler from moving the reads above
+            // the writes (the LDS then executes them in program order)
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                __builtin_amdgcn_raw_buffer_store_b32(lds_at<uint32_t>(rd[t]), gws, go[t], 0, 0);
+                go[t] += gd[t];
+            }
 
 #pragma unroll
             for (int j = 0; j < K; ++j) {
                 gp[j] = g[j];
-                lds_at<float>(aG[j]) = g[j];
-                aG[j] += dG[j];
-                aP[j] += dG[j];
-                hp[j] = lds_at<float>(aP[j]);
+                put(aGH[j], aGL[j], g[j]);
+                aGH[j] = aPH[j];
+                aGL[j] = aPL[j];
+                aPH[j] += dH[j];
+                aPL[j] += dL[j];
+                hp[j] = get(aPH[j], aPL[j]);
             }
         };
         int s0 = 0;
@@ -486,8 +570,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     // --------------------------------------------------------- G = g_a + g_b
     if constexpr (!Cols) {
         f32x4_t* gp4 = reinterpret_cast<f32x4_t*>(g_ws + pix0);
-        for (int e = lane; e < HW / 4; e += 64)
-            gp4[e] = lds_at<f32x4_t>(lay.a + 16u * e) + lds_at<f32x4_t>(lay.b + 16u * e);
+        for (int e = lane; e < HW / 4; e += 64) gp4[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
     } else {
         column_pass(g_ws, lam, x, gx, glam, std::true_type{});
     }
@@ -562,8 +645,8 @@ hipError_t launch_pass(const T* xl, const T* ll, const T* ul, const T* gl, const
                        float eps, int64_t planes, int64_t NL, int64_t L, int dir0, float* s_ws,
                        float* g_ws, const T* x, const T* lam, const T* gy, T* gx, T* glam, T* gu,
                        hipStream_t stream) {
-    constexpr int D = 8;
-    const size_t lds = PairBwdLayout(static_cast<int>(NL), static_cast<int>(L)).bytes;
+    constexpr int D = 4;   // lines prefetched ahead (the steps are long; a deeper unroll outgrows the instruction cache)
+    const size_t lds = PairBwdLayout(static_cast<int>(NL), static_cast<int>(L), sizeof(T) == 2).bytes;
     auto kern = prop2d_backward_pair_kernel<T, K, D, Cols>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -632,8 +715,9 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
 
 bool prop2d_backward_pair_shape(int64_t planes, int64_t H, int64_t W) {
     if (H < 2 || W < 2 || H > 96 || W > 96 || (H & 1) || (W & 1)) return false;
-    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W)).bytes > kLdsBytes ||
-        PairBwdLayout(static_cast<int>(W), static_cast<int>(H)).bytes > kLdsBytes)
+    // the fp32 layout is the larger
+    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), false).bytes > kLdsBytes ||
+        PairBwdLayout(static_cast<int>(W), static_cast<int>(H), false).bytes > kLdsBytes)
         return false;
     // every stream offset is a 32-bit byte offset into one buffer resource
     return 12 * planes * H * W * 4 <= 0x7fffffff;
