@@ -247,7 +247,7 @@ hipError_t launch_scan_dir(const void* x, const void* lam, const void* u, const 
 hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const void* w4,
                          float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                          const PropOpts& o, hipStream_t stream) {
-    if (dtype == 1 && prop2d_phase_eligible(dtype, planes, H, W, x, lam, u, w4, y))
+    if (prop2d_phase_eligible(dtype, planes, H, W, x, lam, u, w4, y))
         return launch_prop2d_phase(x, lam, u, w4, eps, y, dtype, planes, H, W, o, stream);
     if (prop2d_pair_eligible(dtype, planes, H, W, x, lam, u, w4, y))
         return launch_prop2d_pair(x, lam, u, w4, eps, y, dtype, planes, H, W, o, stream);

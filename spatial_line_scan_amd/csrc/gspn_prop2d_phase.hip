@@ -1,5 +1,7 @@
-// Four-direction propagation, one wavefront per (b, c) plane in two phases
-// (gfx950).
+// Four-direction propagation of bf16 planes with even sides up to 96, one
+// wavefront per (b, c) plane in two phases (gfx950).  fp32 planes take the
+// two-wavefront kernel: their 4-byte lambda x would not leave room for four
+// planes per CU.
 //
 // Operator: "Scaling Parallel Sequence Models to Foundation-Scale Vision
 // Encoders", §3 line-scan recurrence (standard GSPN form), §4.1 single-kernel
@@ -20,10 +22,10 @@
 //      of a pixel are summed in a fixed order (TD or BU first, then LR or
 //      RL) and no two lanes ever update one word in the same instruction.
 //   b = lambda x of every pixel, computed once from coalesced loads of x and
-//      lambda: fp32 for fp32 storage; for bf16 storage the exact product of
-//      two bf16 values has at most 16 significant bits, so its fp32 pattern
-//      ends in 8 zero bits and it is kept as 24 bits, the upper 16 in one
-//      array and the next 8 in another (3 bytes a pixel instead of 4).
+//      lambda: the exact product of two bf16 values has at most 16
+//      significant bits, so its fp32 pattern ends in 8 zero bits and it is
+//      kept as 24 bits, the upper 16 in one array and the next 8 in another
+//      (3 bytes a pixel instead of 4).
 // With b on chip, the scans stream only the taps (line-major for every
 // direction, one coalesced window load per tap and step); x and lambda are
 // read once, whole, and never along a column.  At 74 x 74 bf16 a plane takes
@@ -32,11 +34,9 @@
 // Padding.  S and the b arrays are surrounded by pads of one longest line,
 // so that the one-step-ahead reads past either end of a scan stay inside the
 // allocation; slots past the end of a line all read and write dummy words at
-// LDS address 0 (zeroed; such a slot's taps are all dropped, so its state
-// and everything it writes stay 0).
-// When a scan has an odd number of lines both halves reach the middle line
-// in the same step: the backward half writes its state to the pad after S
-// and adds it in after the phase.
+// LDS address 0 (zeroed; such a slot's taps are all dropped, so no
+// in-line position ever weighs its state).  With an even number of lines the
+// two halves of a scan never meet on one line in the same step.
 //
 // Tap groups and chunked scans as in the two-wavefront kernel: the tap plane
 // of plane p is p / cpg, and a chunked scan restarts h at the first line of
@@ -54,31 +54,23 @@ using namespace lane;
 
 // LDS layout in bytes (all offsets multiples of 16):
 //   [S dummy: 16][b dummy: 16][pad Lmax][S: H W][pad Lmax] fp32,
-//   bf16: [pad][b_hi: H W][pad] u16, [pad][b_lo: H W][pad] u8
-//   fp32: [pad][b: H W][pad] fp32
+//   [pad][b_hi: H W][pad] u16, [pad][b_lo: H W][pad] u8
 // Slots past a line end all use the dummies: their S reads and writes go to
 // the S dummy, their b reads in the column scan to the b dummy (zero, never
 // written) and their b writes in the row scan to the pads before the b
 // arrays.  Their taps are all dropped, so no in-line position ever weighs
 // their (finite) states.
 struct PhaseLayout {
-    int s, s_pad, bh, bl, bytes;
+    int s, bh, bl, bytes;
     static constexpr int dum = 0, bdum = 16;
     __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
-    __host__ __device__ PhaseLayout(int H, int W, bool bf16) {
+    __host__ __device__ PhaseLayout(int H, int W) {
         const int lmax = H > W ? H : W;
         const int hw = H * W;
         s = a16(32 + 4 * lmax);
-        s_pad = s + 4 * hw;                          // pad line after S (odd middle lines)
-        const int es_hi = bf16 ? 2 : 4;
-        bh = a16(s_pad + 4 * lmax + es_hi * lmax);
-        if (bf16) {
-            bl = a16(bh + es_hi * (hw + lmax) + lmax);
-            bytes = a16(bl + hw + lmax);
-        } else {
-            bl = 0;
-            bytes = a16(bh + es_hi * (hw + lmax));
-        }
+        bh = a16(s + 4 * hw + 4 * lmax + 2 * lmax);
+        bl = a16(bh + 2 * (hw + lmax) + lmax);
+        bytes = a16(bl + hw + lmax);
     }
 };
 
@@ -99,18 +91,17 @@ __device__ __forceinline__ lds_t<V>& lds_ref(uint32_t byte_off) {
     return *reinterpret_cast<lds_t<V>*>(static_cast<uintptr_t>(byte_off));
 }
 
-// OddH / OddW: the row / column scans have an odd number of lines.
-// Chunked: k_chunk > 1.
-template <typename T, int K, int D, bool OddH, bool OddW, bool Chunked>
+// T: bf16 bits (uint16_t).  Chunked: k_chunk > 1.
+template <typename T, int K, int D, bool Chunked>
 __global__ void __launch_bounds__(64)
 prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __restrict__ u,
                     const T* __restrict__ w4, int w4_bytes, float eps, T* __restrict__ y,
                     int planes, int H, int W, int cpg, int k_chunk) {
-    constexpr bool kBf16 = sizeof(T) == 2;
+    static_assert(sizeof(T) == 2, "bf16 planes only");
     constexpr int ES = sizeof(T);
     constexpr int NW = window_words<T, K>();
     const int HW = H * W;
-    const PhaseLayout lay(H, W, kBf16);
+    const PhaseLayout lay(H, W);
     const int lane = threadIdx.x;
     const int half = lane >> 5;          // 0: forward (TD, LR), 1: backward (BU, RL)
     const int q = lane & 31;
@@ -122,7 +113,7 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
     // [0, bh): the dummy words, S with its pads, and the pad before b_hi
     for (int f = lane; f < lay.bh / 16; f += 64) lds_ref<u32x4_t>(16u * f) = u32x4_t{0u, 0u, 0u, 0u};
 
-    const int words = kBf16 ? HW / 2 : HW;     // bf16: HW is even, two pixels a dword
+    const int words = HW / 2;     // HW is even: two pixels a dword
     // u for the end, in dword pairs, loaded now so that it arrives during
     // the scans (a trailing odd dword is loaded at the end)
     constexpr int kUPer = 24;
@@ -138,7 +129,7 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
     lds_order();
 
     // LDS address of b at element index e
-    auto b_addr_hi = [&](int e) { return static_cast<uint32_t>(lay.bh + (kBf16 ? 2 : 4) * e); };
+    auto b_addr_hi = [&](int e) { return static_cast<uint32_t>(lay.bh + 2 * e); };
     auto b_addr_lo = [&](int e) { return static_cast<uint32_t>(lay.bl + e); };
 
     // one resource per tap plane k, based k planes into the tap tensor
@@ -152,14 +143,13 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
         taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + static_cast<size_t>(k) * HW), 0,
                                                     w4_bytes - k * HW * ES, kBufFlags);
     const int tap_planes = planes / cpg;
-    const int par = kBf16 ? ((K * q) & 1) : 0;
+    const int par = (K * q) & 1;
     const uint32_t win_b = static_cast<uint32_t>(K * q - par) * ES;
     const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
     const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
 
-    auto phase = [&](auto rows_tag, auto odd_tag) {
+    auto phase = [&](auto rows_tag) {
         constexpr bool kRows = decltype(rows_tag)::value;
-        constexpr bool kOdd = decltype(odd_tag)::value;
         const int L = kRows ? W : H;
         const int NL = kRows ? H : W;
         const int g = (kRows ? 0 : 2) + half;        // direction TD, BU, LR, RL
@@ -204,7 +194,7 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
         const int i0 = fwd ? 0 : NL - 1;
         const int de = kRows ? (fwd ? W : -W) : (fwd ? 1 : -1);
         uint32_t aS[K], aH[K], aL[K];
-        const int dS = 4 * de, dH = (kBf16 ? 2 : 4) * de, dL = de;
+        const int dS = 4 * de, dH = 2 * de, dL = de;
         int dSj[K], dHj[K], dLj[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -217,7 +207,7 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
             } else if (kRows) {
                 // b writes of the row scan land in the pads before the b arrays
                 aS[j] = PhaseLayout::dum;
-                aH[j] = static_cast<uint32_t>(lay.bh - (kBf16 ? 2 : 4) * (j + 1));
+                aH[j] = static_cast<uint32_t>(lay.bh - 2 * (j + 1));
                 aL[j] = static_cast<uint32_t>(lay.bl - (j + 1));
             } else {
                 aS[j] = PhaseLayout::dum;
@@ -228,14 +218,10 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
             dLj[j] = valid[j] ? dL : 0;
         }
         auto read_b = [&](int j) -> float {
-            if constexpr (kBf16) {
-                const uint32_t hi = lds_ref<uint16_t>(aH[j]);
-                const uint32_t lo8 = lds_ref<uint8_t>(aL[j]);
-                // bytes (hi.1, hi.0, lo.0, 0)
-                return __uint_as_float(__builtin_amdgcn_perm(hi, lo8, 0x0504000cu));
-            } else {
-                return lds_ref<float>(aH[j]);
-            }
+            const uint32_t hi = lds_ref<uint16_t>(aH[j]);
+            const uint32_t lo8 = lds_ref<uint8_t>(aL[j]);
+            // bytes (hi.1, hi.0, lo.0, 0)
+            return __uint_as_float(__builtin_amdgcn_perm(hi, lo8, 0x0504000cu));
         };
         float h[K], acc[K], bv[K];
 #pragma unroll
@@ -244,13 +230,6 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
             acc[j] = lds_ref<float>(aS[j]);
             if constexpr (!kRows) bv[j] = read_b(j);
         }
-        // odd scans: the backward half's middle-line states go to the pad
-        // line after S (indexed by position) and are added in afterwards
-        const int mid = (NL - 1) / 2;
-        uint32_t mid_pad[K];
-#pragma unroll
-        for (int j = 0; j < K; ++j)
-            mid_pad[j] = static_cast<uint32_t>(valid[j] ? lay.s_pad + 4 * (K * q + j) : PhaseLayout::dum);
         int seg = NL, next_restart = NL;
         if constexpr (Chunked) {
             seg = (NL + k_chunk - 1) / k_chunk;
@@ -312,12 +291,8 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
                     const uint32_t bb = __float_as_uint(bv[j]);
-                    if constexpr (kBf16) {
-                        lds_ref<uint16_t>(aH[j]) = static_cast<uint16_t>(bb >> 16);
-                        lds_ref<uint8_t>(aL[j]) = static_cast<uint8_t>(bb >> 8);
-                    } else {
-                        lds_ref<float>(aH[j]) = bv[j];
-                    }
+                    lds_ref<uint16_t>(aH[j]) = static_cast<uint16_t>(bb >> 16);
+                    lds_ref<uint8_t>(aL[j]) = static_cast<uint8_t>(bb >> 8);
                 }
             }
 
@@ -342,12 +317,8 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
 #pragma unroll
             for (int j = 0; j < K; ++j) h[j] = hn[j];
 
-            const bool at_mid = kOdd && !fwd && s == mid;
 #pragma unroll
-            for (int j = 0; j < K; ++j) {
-                if (at_mid) lds_ref<float>(mid_pad[j]) = h[j];
-                else lds_ref<float>(aS[j]) = acc[j] + h[j];
-            }
+            for (int j = 0; j < K; ++j) lds_ref<float>(aS[j]) = acc[j] + h[j];
             // the next line, read after this step's writes
 #pragma unroll
             for (int j = 0; j < K; ++j) {
@@ -367,39 +338,21 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
 #pragma unroll
         for (int d = 0; d < D; ++d)
             if (s0 + d < NL) step(s0 + d, d);
-        if constexpr (kOdd) {
-            // the middle line receives the backward half's term last
-            if (!fwd) {
-#pragma unroll
-                for (int j = 0; j < K; ++j) {
-                    if (!valid[j]) continue;
-                    const int p = K * q + j;
-                    const int e = kRows ? mid * W + p : p * W + mid;
-                    const uint32_t a = static_cast<uint32_t>(lay.s + 4 * e);
-                    lds_ref<float>(a) = lds_ref<float>(a) + lds_ref<float>(mid_pad[j]);
-                }
-            }
-        }
     };
-    phase(std::true_type{}, std::bool_constant<OddH>{});
+    phase(std::true_type{});
     lds_order();
-    phase(std::false_type{}, std::bool_constant<OddW>{});
+    phase(std::false_type{});
     lds_order();
 
     // --------------------------------------------------------- y = u * S
-    // (bf16: S is read as four floats per dword pair, 16-byte aligned since
-    // the pair starts at an even dword)
+    // (S is read as four floats per dword pair, 16-byte aligned since the
+    // pair starts at an even dword)
     uint32_t* y32 = reinterpret_cast<uint32_t*>(y + pix0);
     const uint32_t* u32 = reinterpret_cast<const uint32_t*>(u + pix0);
     u32x2_t* y64p = reinterpret_cast<u32x2_t*>(y + pix0);
     auto emit_word = [&](int f, uint32_t uv) -> uint32_t {
-        if constexpr (kBf16) {
-            const f32x2_t sv = lds_ref<f32x2_t>(lay.s + 8u * f);
-            return pack_bf16x2(__uint_as_float(uv << 16) * sv.x,
-                               __uint_as_float(uv & 0xffff0000u) * sv.y);
-        } else {
-            return __float_as_uint(__uint_as_float(uv) * lds_ref<float>(lay.s + 4u * f));
-        }
+        const f32x2_t sv = lds_ref<f32x2_t>(lay.s + 8u * f);
+        return pack_bf16x2(__uint_as_float(uv << 16) * sv.x, __uint_as_float(uv & 0xffff0000u) * sv.y);
     };
     auto emit_pair = [&](int f, u32x2_t uv) {
         y64p[f] = u32x2_t{emit_word(2 * f, uv.x), emit_word(2 * f + 1, uv.y)};
@@ -413,13 +366,14 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
     if ((words & 1) && lane == 0) y32[words - 1] = emit_word(words - 1, u32[words - 1]);
 }
 
-template <typename T, int K, bool OddH, bool OddW, bool Chunked>
+template <int K, bool Chunked>
 hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, float eps,
                     void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                     hipStream_t stream) {
+    using T = uint16_t;
     constexpr int D = 8;   // taps prefetched D steps ahead
-    const size_t lds = PhaseLayout(static_cast<int>(H), static_cast<int>(W), sizeof(T) == 2).bytes;
-    auto kern = prop2d_phase_kernel<T, K, D, OddH, OddW, Chunked>;
+    const size_t lds = PhaseLayout(static_cast<int>(H), static_cast<int>(W)).bytes;
+    auto kern = prop2d_phase_kernel<T, K, D, Chunked>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -435,40 +389,14 @@ hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w
     return hipGetLastError();
 }
 
-template <typename T, int K, bool Chunked>
-hipError_t launch_parity(const void* x, const void* lam, const void* u, const void* w4, float eps,
-                         void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
-                         hipStream_t stream) {
-    if constexpr (sizeof(T) == 2) {  // bf16 shapes are even (eligibility)
-        return launch_k<T, K, false, false, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    } else {
-        const bool oh = H & 1, ow = W & 1;
-        if (!oh && !ow)
-            return launch_k<T, K, false, false, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-        if (oh && ow)
-            return launch_k<T, K, true, true, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-        if (oh)
-            return launch_k<T, K, true, false, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-        return launch_k<T, K, false, true, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    }
-}
-
-template <typename T, bool Chunked>
+template <bool Chunked>
 hipError_t launch_c(const void* x, const void* lam, const void* u, const void* w4, float eps,
                     void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                     hipStream_t stream) {
     const int64_t Lmax = H > W ? H : W;
-    if (Lmax <= 32) return launch_parity<T, 1, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    if (Lmax <= 64) return launch_parity<T, 2, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    return launch_parity<T, 3, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-}
-
-template <typename T>
-hipError_t launch_t(const void* x, const void* lam, const void* u, const void* w4, float eps,
-                    void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
-                    hipStream_t stream) {
-    return o.k_chunk > 1 ? launch_c<T, true>(x, lam, u, w4, eps, y, planes, H, W, o, stream)
-                         : launch_c<T, false>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (Lmax <= 32) return launch_k<1, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (Lmax <= 64) return launch_k<2, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    return launch_k<3, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -477,24 +405,19 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 bool prop2d_phase_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
                            const void* lam, const void* u, const void* w4, const void* y) {
-    if (H > 96 || W > 96) return false;
-    if (PhaseLayout(static_cast<int>(H), static_cast<int>(W), dtype == 1).bytes > kLdsBytes)
-        return false;
-    const int64_t es = dtype == 0 ? 4 : 2;
-    if (12 * planes * H * W * es > 0x7fffffff) return false;
-    if (dtype == 1) {  // bf16: whole dwords per line and per plane
-        if ((H & 1) || (W & 1)) return false;
-        if (!aligned4(x) || !aligned4(lam) || !aligned4(u) || !aligned4(w4) || !aligned4(y))
-            return false;
-    }
-    return true;
+    if (dtype != 1) return false;                         // bf16 planes only
+    if (H > 96 || W > 96 || (H & 1) || (W & 1)) return false;   // whole dwords per line
+    if (PhaseLayout(static_cast<int>(H), static_cast<int>(W)).bytes > kLdsBytes) return false;
+    if (12 * planes * H * W * 2 > 0x7fffffff) return false;
+    return aligned4(x) && aligned4(lam) && aligned4(u) && aligned4(w4) && aligned4(y);
 }
 
 hipError_t launch_prop2d_phase(const void* x, const void* lam, const void* u, const void* w4,
                                float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                                const PropOpts& o, hipStream_t stream) {
-    return dtype == 0 ? launch_t<float>(x, lam, u, w4, eps, y, planes, H, W, o, stream)
-                      : launch_t<uint16_t>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (dtype != 1) return hipErrorInvalidValue;
+    return o.k_chunk > 1 ? launch_c<true>(x, lam, u, w4, eps, y, planes, H, W, o, stream)
+                         : launch_c<false>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 }  // namespace gspn
