@@ -120,8 +120,9 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": "%d plane passes over the %d planes (%dx%d, %s values) of the timed inputs, "
-                  "fp64 C loop, %.1f s" % (planes, wl.B * wl.C, wl.H, wl.W, wl.dtype, spent),
+        "sample": "%d planes (%.1f passes over the %d planes, %dx%d, %s values, of the timed "
+                  "inputs), fp64 C loop, %.1f s" % (planes, planes / len(order), len(order), wl.H,
+                                                  wl.W, wl.dtype, spent),
         "seconds": spent,
         "cpu": _cpu_model(),
         "host_cores_visible": os.cpu_count(),
