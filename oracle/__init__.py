@@ -80,6 +80,10 @@ def _load(path: str | None = None):
             lib.gspn_oracle_prop2d_ex.argtypes = [dp, dp, dp, dp, L, L, ctypes.c_double, dp,
                                                   L, L, L, L]
             lib.gspn_oracle_prop2d_ex.restype = ctypes.c_int
+        if hasattr(lib, "gspn_oracle_prop2d_ex_backward"):
+            lib.gspn_oracle_prop2d_ex_backward.argtypes = [dp, dp, dp, dp, dp, L, L, ctypes.c_double,
+                                                           dp, dp, dp, dp, L, L, L, L]
+            lib.gspn_oracle_prop2d_ex_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -177,6 +181,24 @@ def prop2d_ex(x, lam, u, w4g, groups: int, k_chunk: int = 1, eps: float = 1e-6) 
     if rc != 0:
         raise MemoryError("oracle propagation could not allocate scratch")
     return y
+
+
+def prop2d_ex_backward(x, lam, u, w4g, gy, groups: int, k_chunk: int = 1, eps: float = 1e-6):
+    """Gradient of <gy, prop2d_ex(x, lam, u, w4g, groups, k_chunk)> with respect
+    to x, lam, u and w4g (the tap gradient has the grouped layout of w4g)."""
+    x, lam, u, w4g, gy = _f64(x), _f64(lam), _f64(u), _f64(w4g), _f64(gy)
+    B, C, H, W = x.shape
+    assert w4g.size == 12 * B * groups * H * W and gy.shape == x.shape
+    gx, glam, gu = np.empty_like(x), np.empty_like(x), np.empty_like(x)
+    gw4 = np.empty_like(w4g)
+    rc = _load().gspn_oracle_prop2d_ex_backward(_ptr(x), _ptr(lam), _ptr(u), _ptr(w4g), _ptr(gy),
+                                                int(groups), int(k_chunk), float(eps), _ptr(gx),
+                                                _ptr(glam), _ptr(gu), _ptr(gw4), B, C, H, W)
+    if rc == -2:
+        raise ValueError("groups must divide C and k_chunk must be >= 1")
+    if rc != 0:
+        raise MemoryError("oracle backward could not allocate scratch")
+    return gx, glam, gu, gw4
 
 
 def _to_storage(a: np.ndarray, storage: str | None) -> np.ndarray:

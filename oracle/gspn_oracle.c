@@ -410,3 +410,129 @@ int gspn_oracle_prop2d_ex(const double* x, const double* lam, const double* u,
     free(cur);
     return 0;
 }
+
+/*
+ * Gradient of the extended operator above (tap groups and chunked scans): the
+ * exact derivative of gspn_oracle_prop2d_ex, with the formulas of
+ * gspn_oracle_prop2d_backward and two changes that follow from the forward:
+ *   - a line that restarts its segment does not read the line before it: its
+ *     taps get gradient 0, and the line before it (in scan order) receives no
+ *     adjoint term from it, so its g is u * gy alone;
+ *   - channel c reads the taps of group c / (C / G), so the tap gradient of a
+ *     group is the sum over its channels, accumulated in channel order.
+ * gw4 has the layout of w4, [4][B][G][3][..][..].
+ * Returns 0, -1 if scratch memory could not be obtained, -2 for a bad G or
+ * k_chunk.
+ */
+int gspn_oracle_prop2d_ex_backward(const double* x, const double* lam, const double* u,
+                                   const double* w4, const double* gy, long G, long k_chunk,
+                                   double eps, double* gx, double* glam, double* gu,
+                                   double* gw4, long B, long C, long H, long W) {
+    if (G < 1 || C % G != 0 || k_chunk < 1) return -2;
+    long npix = H * W;
+    long cpg = C / G;
+    long Lmax = H > W ? H : W;
+    double* hsum = (double*)malloc(sizeof(double) * (size_t)npix);
+    double* gsum = (double*)malloc(sizeof(double) * (size_t)npix);
+    double* hline = (double*)malloc(sizeof(double) * (size_t)npix);   /* h by (line, pos) */
+    double* wnorm = (double*)malloc(sizeof(double) * (size_t)npix * 3);
+    double* gnext = (double*)malloc(sizeof(double) * (size_t)Lmax);   /* g of the line after */
+    double* gcur = (double*)malloc(sizeof(double) * (size_t)Lmax);
+    if (!hsum || !gsum || !hline || !wnorm || !gnext || !gcur) {
+        free(hsum); free(gsum); free(hline); free(wnorm); free(gnext); free(gcur);
+        return -1;
+    }
+    for (long e = 0; e < 4 * B * G * 3 * npix; ++e) gw4[e] = 0.0;
+    for (long b = 0; b < B; ++b) {
+        for (long ch = 0; ch < C; ++ch) {
+            long pl = b * C + ch;
+            const double* xs = x + pl * npix;
+            const double* ls = lam + pl * npix;
+            const double* us = u + pl * npix;
+            const double* gys = gy + pl * npix;
+            for (long e = 0; e < npix; ++e) { hsum[e] = 0.0; gsum[e] = 0.0; }
+            for (int dir = DIR_TD; dir <= DIR_RL; dir++) {
+                int along_rows = (dir == DIR_TD || dir == DIR_BU);
+                long NL = along_rows ? H : W;
+                long L = along_rows ? W : H;
+                int fwd = (dir == DIR_TD) || (dir == DIR_LR);
+                long seg = (NL + k_chunk - 1) / k_chunk;
+                long grp = ch / cpg;                        /* the channel's tap group */
+                long tap_off = (((long)dir * B + b) * G + grp) * 3 * npix;
+                const double* tg = w4 + tap_off;
+                double* gtg = gw4 + tap_off;
+                for (long i = 0; i < NL; ++i)
+                    for (long p = 0; p < L; ++p) {
+                        double z[3], wn[3];
+                        for (int k = 0; k < 3; ++k) z[k] = tg[(long)k * npix + i * L + p];
+                        normalize_three(z, p, L, eps, wn);
+                        for (int k = 0; k < 3; ++k) wnorm[(i * L + p) * 3 + k] = wn[k];
+                    }
+                /* forward, keeping every line */
+                for (long step = 0; step < NL; ++step) {
+                    long i = fwd ? step : NL - 1 - step;
+                    long before = fwd ? i - 1 : i + 1;
+                    int restart = restarts_segment(i, NL, seg, fwd);
+                    for (long p = 0; p < L; ++p) {
+                        long r, c;
+                        pixel_of(dir, i, p, &r, &c);
+                        double hv = ls[r * W + c] * xs[r * W + c];
+                        if (!restart)
+                            for (int k = 0; k < 3; ++k) {
+                                long src = p + k - 1;
+                                if (src >= 0 && src < L)
+                                    hv += wnorm[(i * L + p) * 3 + k] * hline[before * L + src];
+                            }
+                        hline[i * L + p] = hv;
+                        hsum[r * W + c] += hv;
+                    }
+                }
+                /* adjoint, lines in reverse scan order */
+                for (long step = NL - 1; step >= 0; --step) {
+                    long i = fwd ? step : NL - 1 - step;
+                    long after = fwd ? i + 1 : i - 1;
+                    long before = fwd ? i - 1 : i + 1;
+                    int after_reads_i = step < NL - 1 && !restarts_segment(after, NL, seg, fwd);
+                    for (long p = 0; p < L; ++p) {
+                        long r, c;
+                        pixel_of(dir, i, p, &r, &c);
+                        double v = us[r * W + c] * gys[r * W + c];
+                        if (after_reads_i)
+                            for (int k = 0; k < 3; ++k) {
+                                long dst = p - k + 1;   /* position of line `after` whose tap k reads p */
+                                if (dst >= 0 && dst < L) v += wnorm[(after * L + dst) * 3 + k] * gnext[dst];
+                            }
+                        gcur[p] = v;
+                        gsum[r * W + c] += v;
+                    }
+                    int reads_before = !restarts_segment(i, NL, seg, fwd);
+                    for (long p = 0; p < L; ++p) {
+                        double dwn[3] = {0.0, 0.0, 0.0}, s[3], T = 0.0, wdot = 0.0;
+                        for (int k = 0; k < 3; ++k) {
+                            long src = p + k - 1;
+                            int inl = src >= 0 && src < L;
+                            if (reads_before && inl) dwn[k] = gcur[p] * hline[before * L + src];
+                            s[k] = inl ? sigmoid(tg[(long)k * npix + i * L + p]) : 0.0;
+                            T += s[k];
+                        }
+                        for (int k = 0; k < 3; ++k) wdot += dwn[k] * wnorm[(i * L + p) * 3 + k];
+                        for (int k = 0; k < 3; ++k) {
+                            long src = p + k - 1;
+                            if (src < 0 || src >= L) continue;
+                            double gs_k = T > eps ? (dwn[k] - wdot) / T : dwn[k] / eps;
+                            gtg[(long)k * npix + i * L + p] += gs_k * s[k] * (1.0 - s[k]);
+                        }
+                    }
+                    double* t = gnext; gnext = gcur; gcur = t;
+                }
+            }
+            for (long e = 0; e < npix; ++e) {
+                gx[pl * npix + e] = ls[e] * gsum[e];
+                glam[pl * npix + e] = xs[e] * gsum[e];
+                gu[pl * npix + e] = gys[e] * hsum[e];
+            }
+        }
+    }
+    free(hsum); free(gsum); free(hline); free(wnorm); free(gnext); free(gcur);
+    return 0;
+}

@@ -3,7 +3,7 @@
 Each case compiles a copy of oracle/gspn_oracle.c with one deliberate error
 (a dropped term, a wrong sign or index, a transposed operand, a wrong scan
 order), points the oracle module at it, and requires that at least one pin
-of tests/test_oracle_pins.py fails.  Everything runs on the CPU.
+of the oracle's pin tests fails.  Everything runs on the CPU.
 """
 import os
 import shutil
@@ -14,6 +14,7 @@ import pytest
 import oracle
 import test_oracle_backward as bpins
 import test_oracle_ex as xpins
+import test_oracle_ex_backward as xbpins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gspn_oracle.c")
@@ -55,6 +56,21 @@ MUTANTS = [
      "long Lc = NL > k_chunk ? NL / k_chunk : 1;"),
     ("channel groups interleaved", "ch / cpg) * 3 * npix;", "ch % G) * 3 * npix;"),
     ("segments never restart", "if (!restart) {", "if (step > 0) {"),
+    # gradient of the extended operator (oracle.prop2d_ex_backward)
+    ("restart lines keep tap gradients", "int reads_before = !restarts_segment(i, NL, seg, fwd);",
+     "int reads_before = step > 0;"),
+    ("adjoint flows back across segment starts",
+     "int after_reads_i = step < NL - 1 && !restarts_segment(after, NL, seg, fwd);",
+     "int after_reads_i = step < NL - 1;"),
+    ("adjoint cut at the wrong line",
+     "step < NL - 1 && !restarts_segment(after, NL, seg, fwd);",
+     "step < NL - 1 && !restarts_segment(i, NL, seg, fwd);"),
+    ("group tap gradient overwritten, not summed", "gtg[(long)k * npix + i * L + p] += gs_k",
+     "gtg[(long)k * npix + i * L + p] = gs_k"),
+    ("gradient's forward ignores restarts", "int restart = restarts_segment(i, NL, seg, fwd);",
+     "int restart = step == 0;"),
+    ("grouped gu from the adjoint sum", "gu[pl * npix + e] = gys[e] * hsum[e];",
+     "gu[pl * npix + e] = gys[e] * gsum[e];"),
 ]
 
 
@@ -78,6 +94,10 @@ def _checks():
     yield lambda: xpins.test_groups_are_contiguous_channel_blocks()
     yield lambda: xpins.test_chunked_scan_equals_global_scans_of_segments(7, 9, 3)
     yield lambda: xpins.test_one_line_segments_reduce_to_4_u_lambda_x(7)
+    yield lambda: xbpins.test_ex_backward_reduces_to_per_channel_backward()
+    yield lambda: xbpins.test_ex_backward_matches_finite_differences(2, 3)
+    yield lambda: xbpins.test_ex_backward_shared_taps_sum_the_replicated_gradients(2, 3)
+    yield lambda: xbpins.test_ex_backward_one_line_segments_closed_form()
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
