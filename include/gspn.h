@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 4
+#define GSPN_ABI_VERSION 5
 
 /* Longest line (H or W) any entry point accepts. */
 #define GSPN_MAX_LINE 8192
@@ -199,6 +199,37 @@ int gspn_prop2d_4dir_backward(const void* x, const void* lam, const void* u,
 /* Workspace bytes gspn_prop2d_4dir_backward needs for these sizes (0 if
  * none), or -1 if it does not accept them. */
 int64_t gspn_prop2d_4dir_backward_workspace(int64_t B, int64_t C, int64_t H, int64_t W);
+
+/*
+ * Gradient of gspn_prop2d_4dir_ex (tap groups and chunked scans): the exact
+ * derivative of that operator, with the formulas of gspn_prop2d_4dir_backward
+ * and two changes that follow from the forward:
+ *   - the first line of each segment (in its scan order) reads no line before
+ *     it, so its taps get gradient 0 and the line before it receives no
+ *     adjoint term from it;
+ *   - channel c reads the taps of group c / (C / groups), so the gradient of
+ *     a group's taps is the sum over its channels, taken in channel order.
+ *   groups, k_chunk : as gspn_prop2d_4dir_ex (groups must divide C, else
+ *               GSPN_ERR_SHAPE; k_chunk >= 1, else GSPN_ERR_VALUE).
+ *   w_raw4, gw4 : [4][B][groups][3][..][..] (gw4 has the layout of w_raw4).
+ *   workspace : at least gspn_prop2d_4dir_ex_backward_workspace(B, C, groups,
+ *               H, W) bytes, 4-byte aligned (16 for the fast kernels).  On top
+ *               of what gspn_prop2d_4dir_backward needs, channels that share
+ *               taps (groups < C) keep their fp32 tap gradients there before
+ *               they are summed: 48 bytes per pixel-channel.
+ * Other arguments, layouts, errors and determinism as
+ * gspn_prop2d_4dir_backward, which is this call with groups = C, k_chunk = 1.
+ */
+int gspn_prop2d_4dir_ex_backward(const void* x, const void* lam, const void* u,
+                                 const void* w_raw4, int64_t groups, int64_t k_chunk,
+                                 const void* gy, float eps, void* gx, void* glam, void* gu,
+                                 void* gw4, void* workspace, int64_t workspace_bytes, int dtype,
+                                 int64_t B, int64_t C, int64_t H, int64_t W, void* stream);
+
+/* Workspace bytes gspn_prop2d_4dir_ex_backward needs for these sizes (0 if
+ * none), or -1 if it does not accept them. */
+int64_t gspn_prop2d_4dir_ex_backward_workspace(int64_t B, int64_t C, int64_t groups, int64_t H,
+                                               int64_t W);
 
 /*
  * Latent-space propagation sublayer (paper §5.1, a more efficient ViT block:

@@ -24,6 +24,7 @@
 // the caller passes; the current, previous and next lines and the next line's
 // normalised taps are LDS lines.
 #include "gspn_device.h"
+#include <algorithm>
 #include "gspn_internal.h"
 
 namespace gspn {
@@ -54,13 +55,17 @@ __device__ __forceinline__ void store_f(T* p, size_t i, float v) {
     store_elem(p, i, v);
 }
 
-template <typename T>
+// GT: type of the tap gradients written, per channel ([4][planes][3][..][..]):
+// T straight into gw4 when every channel has its own taps, fp32 into a
+// workspace that a group reduction then sums when channels share them.
+// cpg: channels per tap group; k_chunk: segments per scan.
+template <typename T, typename GT>
 __global__ void __launch_bounds__(kBwdThreads)
 prop2d_backward_kernel(const T* __restrict__ x, const T* __restrict__ lam,
                        const T* __restrict__ u, const T* __restrict__ w4,
                        const T* __restrict__ gy, float eps, T* __restrict__ gx,
-                       T* __restrict__ glam, T* __restrict__ gu, T* __restrict__ gw4,
-                       float* __restrict__ ws, int64_t planes, int H, int W) {
+                       T* __restrict__ glam, T* __restrict__ gu, GT* __restrict__ gwd,
+                       float* __restrict__ ws, int64_t planes, int H, int W, int cpg, int k_chunk) {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int Lmax = H > W ? H : W;
@@ -92,13 +97,15 @@ prop2d_backward_kernel(const T* __restrict__ x, const T* __restrict__ lam,
         const bool fwd = dir == 0 || dir == 2;
         const int NL = rows ? H : W;
         const int L = rows ? W : H;
-        const size_t tap_base = (static_cast<size_t>(dir) * planes + plane) * 3 * npix;
-        const T* wp = w4 + tap_base;
-        T* gwp = gw4 + tap_base;
+        const T* wp = w4 + (static_cast<size_t>(dir) * (planes / cpg) + plane / cpg) * 3 * npix;
+        GT* gwp = gwd + (static_cast<size_t>(dir) * planes + plane) * 3 * npix;
         auto pix = [&](int i, int p) -> size_t {
             return rows ? static_cast<size_t>(i) * W + p : static_cast<size_t>(p) * W + i;
         };
         auto line_of = [&](int step) { return fwd ? step : NL - 1 - step; };
+        // the first line of each segment in scan order reads no line before it
+        const int seg = (NL + k_chunk - 1) / k_chunk;
+        auto restarts = [&](int i) { return fwd ? i % seg == 0 : (i == NL - 1 || (i + 1) % seg == 0); };
 
         // ---------------------------------------------- forward, keeping h
         for (int step = 0; step < NL; ++step) {
@@ -108,7 +115,7 @@ prop2d_backward_kernel(const T* __restrict__ x, const T* __restrict__ lam,
             for (int p = tid; p < L; p += kBwdThreads) {
                 const size_t px = pix(i, p);
                 float h = load_elem(lp, px) * load_elem(xp, px);
-                if (step > 0) {
+                if (!restarts(i)) {
                     const size_t t = static_cast<size_t>(i) * L + p;
                     const TapNorm tn = tap_norm(load_elem(wp, t), load_elem(wp, t + npix),
                                                 load_elem(wp, t + 2 * npix), p > 0, p < L - 1, eps);
@@ -130,12 +137,14 @@ prop2d_backward_kernel(const T* __restrict__ x, const T* __restrict__ lam,
             const int iprev = step > 0 ? line_of(step - 1) : i;
             const float* gold = gline + ((step + 1) & 1) * Lmax;   // line scanned after i
             float* gnew = gline + (step & 1) * Lmax;
+            const bool next_reads_i = step < NL - 1 && !restarts(line_of(step + 1));
+            const bool reads_prev = !restarts(i);
             float wcur[3][4];   // normalised taps of line i for this thread's positions
             int slot = 0;
             for (int p = tid; p < L; p += kBwdThreads, ++slot) {
                 const size_t px = pix(i, p);
                 float v = load_elem(up, px) * load_elem(gyp, px);
-                if (step < NL - 1) {
+                if (next_reads_i) {
                     // destinations q = p + 1, p, p - 1 of the next line read p
                     // through their taps 0, 1, 2
                     v = fmaf(wnext[Lmax + p], gold[p], v);
@@ -151,7 +160,7 @@ prop2d_backward_kernel(const T* __restrict__ x, const T* __restrict__ lam,
                 if (slot < 4)
                     for (int k = 0; k < 3; ++k) wcur[k][slot] = tn.wn[k];
                 float gz[3] = {0.0f, 0.0f, 0.0f};
-                if (step > 0) {
+                if (reads_prev) {
                     const float* hp = hd + static_cast<size_t>(iprev) * L;
                     float gwn[3];
                     gwn[0] = p > 0 ? v * hp[p - 1] : 0.0f;
@@ -204,13 +213,14 @@ prop2d_backward_kernel(const T* __restrict__ x, const T* __restrict__ lam,
 
 size_t bwd_line_floats(int64_t H, int64_t W) { return 7 * static_cast<size_t>(H > W ? H : W); }
 
-template <typename T>
+template <typename T, typename GT>
 hipError_t backward_t(const void* x, const void* lam, const void* u, const void* w4,
-                      const void* gy, float eps, void* gx, void* glam, void* gu, void* gw4,
-                      void* ws, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
+                      const void* gy, float eps, void* gx, void* glam, void* gu, void* gwd,
+                      void* ws, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                      hipStream_t stream) {
     const size_t lines = bwd_line_floats(H, W) * sizeof(float);
     const size_t lds = ws ? lines : lines + 3 * static_cast<size_t>(H * W) * sizeof(float);
-    auto kern = prop2d_backward_kernel<T>;
+    auto kern = prop2d_backward_kernel<T, GT>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -220,8 +230,9 @@ hipError_t backward_t(const void* x, const void* lam, const void* u, const void*
     kern<<<dim3(static_cast<unsigned>(planes)), dim3(kBwdThreads), lds, stream>>>(
         static_cast<const T*>(x), static_cast<const T*>(lam), static_cast<const T*>(u),
         static_cast<const T*>(w4), static_cast<const T*>(gy), eps, static_cast<T*>(gx),
-        static_cast<T*>(glam), static_cast<T*>(gu), static_cast<T*>(gw4),
-        static_cast<float*>(ws), planes, static_cast<int>(H), static_cast<int>(W));
+        static_cast<T*>(glam), static_cast<T*>(gu), static_cast<GT*>(gwd),
+        static_cast<float*>(ws), planes, static_cast<int>(H), static_cast<int>(W),
+        static_cast<int>(o.cpg), static_cast<int>(o.k_chunk));
     return hipGetLastError();
 }
 
@@ -231,13 +242,34 @@ int64_t plane_kernel_workspace_bytes(int64_t planes, int64_t H, int64_t W) {
     return lds <= kLdsBytes ? 0 : planes * 3 * H * W * 4;
 }
 
+// Per-channel fp32 tap gradients of channels that share taps, [4][planes][3][H W].
+int64_t group_grad_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg) {
+    return cpg > 1 ? (12 * planes * H * W * 4 + 255) & ~static_cast<int64_t>(255) : 0;
+}
+
+// Tap gradient of each group: the sum over its channels, in channel order.
+// gwc is [4][B][G][cpg][3 HW] read as [..][cpg][plane3]; gw4 is [4][B][G][3 HW].
+template <typename T>
+__global__ void __launch_bounds__(256)
+group_sum_kernel(const float* __restrict__ gwc, T* __restrict__ gw4, int64_t n_out, int64_t plane3,
+                 int cpg) {
+    for (int64_t o = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; o < n_out;
+         o += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t grp = o / plane3, r = o - grp * plane3;
+        const float* src = gwc + grp * cpg * plane3 + r;
+        float acc = 0.0f;
+        for (int c = 0; c < cpg; ++c) acc += src[c * plane3];
+        store_elem(gw4, static_cast<size_t>(o), acc);
+    }
+}
+
 }  // namespace
 
-int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W) {
+int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg) {
     const int64_t general = plane_kernel_workspace_bytes(planes, H, W);
     const int64_t pair = prop2d_backward_pair_shape(planes, H, W)
                              ? prop2d_backward_pair_workspace_bytes(planes, H, W) : 0;
-    return general > pair ? general : pair;
+    return group_grad_bytes(planes, H, W, cpg) + (general > pair ? general : pair);
 }
 
 int64_t prop2d_backward_max_line() { return kLdsBytes / 4 / 7; }
@@ -245,16 +277,41 @@ int64_t prop2d_backward_max_line() { return kLdsBytes / 4 / 7; }
 hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u, const void* w4,
                                   const void* gy, float eps, void* gx, void* glam, void* gu,
                                   void* gw4, void* ws, int dtype, int64_t planes, int64_t H,
-                                  int64_t W, hipStream_t stream) {
+                                  int64_t W, const PropOpts& o, hipStream_t stream) {
+    // channels that share taps write their own fp32 tap gradients first, at
+    // the start of the workspace; the kernels' own scratch follows
+    const bool grouped = o.cpg > 1;
+    void* gdst = grouped ? ws : gw4;
+    void* rest = ws ? static_cast<char*>(ws) + group_grad_bytes(planes, H, W, o.cpg) : nullptr;
     const void* ptrs[] = {x, lam, u, w4, gy, gx, glam, gu, gw4};
-    if (prop2d_backward_pair_eligible(dtype, planes, H, W, ptrs, 9, ws))
-        return launch_prop2d_backward_pair(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, dtype,
-                                           planes, H, W, stream);
-    // this kernel takes a workspace only when its planes leave LDS
-    if (plane_kernel_workspace_bytes(planes, H, W) == 0) ws = nullptr;
-    return dtype == 0 ? backward_t<float>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W, stream)
-                      : backward_t<uint16_t>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W,
-                                             stream);
+    hipError_t e;
+    if (prop2d_backward_pair_eligible(dtype, planes, H, W, ptrs, 9, rest)) {
+        e = launch_prop2d_backward_pair(x, lam, u, w4, gy, eps, gx, glam, gu, gdst, grouped, rest,
+                                        dtype, planes, H, W, o, stream);
+    } else {
+        // this kernel takes a workspace only when its planes leave LDS
+        void* pws = plane_kernel_workspace_bytes(planes, H, W) == 0 ? nullptr : rest;
+        if (dtype == 0)
+            e = backward_t<float, float>(x, lam, u, w4, gy, eps, gx, glam, gu, gdst, pws, planes, H, W, o,
+                                         stream);
+        else if (grouped)
+            e = backward_t<uint16_t, float>(x, lam, u, w4, gy, eps, gx, glam, gu, gdst, pws, planes, H, W,
+                                            o, stream);
+        else
+            e = backward_t<uint16_t, uint16_t>(x, lam, u, w4, gy, eps, gx, glam, gu, gdst, pws, planes, H,
+                                               W, o, stream);
+    }
+    if (e != hipSuccess || !grouped) return e;
+    const int64_t plane3 = 3 * H * W;
+    const int64_t n_out = 4 * (planes / o.cpg) * plane3;
+    const int64_t blocks = std::min<int64_t>((n_out + 255) / 256, 16384);
+    if (dtype == 0)
+        group_sum_kernel<float><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
+            static_cast<const float*>(ws), static_cast<float*>(gw4), n_out, plane3, static_cast<int>(o.cpg));
+    else
+        group_sum_kernel<uint16_t><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
+            static_cast<const float*>(ws), static_cast<uint16_t*>(gw4), n_out, plane3, static_cast<int>(o.cpg));
+    return hipGetLastError();
 }
 
 }  // namespace gspn

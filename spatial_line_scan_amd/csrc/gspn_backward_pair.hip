@@ -78,7 +78,8 @@ struct PairBwdLayout {
                                       // array; tap-gradient staging lines
     static constexpr int dum = 0, ldum = 8;
     __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
-    __host__ __device__ PairBwdLayout(int NL, int L, bool narrow) {
+    // gsize: bytes of a staged tap gradient
+    __host__ __device__ PairBwdLayout(int NL, int L, bool narrow, int gsize) {
         const int w = narrow ? 2 : 4;
         a = a16(16 + 2 * w * L);
         b = a16(a + w * NL * L);
@@ -90,7 +91,7 @@ struct PairBwdLayout {
             end = lb + (NL + 2) * L;
         }
         stage = a16(end);
-        bytes = stage + 6 * 96 * (narrow ? 2 : 4);
+        bytes = stage + 6 * 96 * gsize;
     }
 };
 
@@ -148,11 +149,15 @@ __device__ __forceinline__ f32x2_t load_pair(const T* p, size_t e) {
 // G of the pair to s_ws, g_ws ([planes][H][W] fp32).
 // Cols = true: the column pair (NL = W, L = H), inputs transposed; adds the
 // row pair's S and G and writes gu, gx, glam.
-template <typename T, int K, int D, bool Cols>
+// Taps are read from group plane p / cpg (w4: w4_bytes); the tap gradients
+// are written per channel, as GT, to gwd ([4][planes][3][..][..], gw_bytes).
+// Chunked: k_chunk > 1.
+template <typename T, typename GT, int K, int D, bool Cols, bool Chunked>
 __global__ void __launch_bounds__(64)
 prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml,
                             const T* __restrict__ ul, const T* __restrict__ gyl,
-                            const T* __restrict__ w4, T* __restrict__ gw4, int w4_bytes,
+                            const T* __restrict__ w4, int w4_bytes, GT* __restrict__ gwd,
+                            int gw_bytes, int cpg, int k_chunk,
                             float eps, int planes, int NL, int L, int dir0,
                             float* __restrict__ s_ws, float* __restrict__ g_ws,
                             const T* __restrict__ x, const T* __restrict__ lam,
@@ -163,7 +168,8 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     constexpr bool kNarrow = ES == 2;
     constexpr int VW = kNarrow ? 2 : 4;     // bytes of a value in the A / B array
     const int HW = NL * L;
-    const PairBwdLayout lay(NL, L, kNarrow);
+    constexpr int GS = sizeof(GT);
+    const PairBwdLayout lay(NL, L, kNarrow, GS);
     const int lane = threadIdx.x;
     const int half = lane >> 5;
     const int q = lane & 31;
@@ -225,7 +231,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     const __amdgpu_buffer_rsrc_t us = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(ul), 0, in_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t gs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(gyl), 0, in_bytes, kBufFlags);
     __amdgpu_buffer_rsrc_t taps[3];
-    const __amdgpu_buffer_rsrc_t gws = __builtin_amdgcn_make_buffer_rsrc(gw4, 0, w4_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t gws = __builtin_amdgcn_make_buffer_rsrc(gwd, 0, gw_bytes, kBufFlags);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + static_cast<size_t>(k) * HW), 0,
@@ -235,7 +241,9 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     const uint32_t win_b = static_cast<uint32_t>(K * q - par) * ES;
     const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
     const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
-    const uint32_t tap_b = static_cast<uint32_t>(((dir0 + half) * planes + plane) * 3 * HW) * ES;
+    const uint32_t tap_b = static_cast<uint32_t>(((dir0 + half) * (planes / cpg) + plane / cpg) * 3 * HW) * ES;
+    // segments of a chunked scan; a segment's first line reads no line before it
+    const int seg = Chunked ? (NL + k_chunk - 1) / k_chunk : NL;
     const uint32_t line_b = static_cast<uint32_t>(L) * ES;
     const uint32_t plane_base = half ? lay.b : lay.a;
     const uint32_t lplane_base = half ? lay.lb : lay.la;
@@ -354,8 +362,11 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         float h[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) h[j] = 0.0f;
+        // step of the next restart (scan order: lines seg, 2 seg, .. from the
+        // top; NL - 1 - (seg - 1), .. from the bottom)
+        int next_restart = fwd ? seg : NL - ((NL - 1) / seg) * seg;
 
-        auto step = [&](int d) {
+        auto step = [&](int s, int d) {
             asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
             asm volatile("" : "+v"(xbuf[d]), "+v"(lbuf[d]));
             float s0[K], s1[K], s2[K], t[K], r[K], b[K];
@@ -368,6 +379,12 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             for (int j = 0; j < K; ++j)
                 asm volatile("" : "+v"(lo), "+v"(xo) : "v"(s0[j]), "v"(s1[j]), "v"(s2[j]), "v"(r[j]), "v"(b[j]));
             load_line(d);
+            if constexpr (Chunked) {
+                const bool restart = s == next_restart;
+                next_restart = restart ? next_restart + seg : next_restart;
+#pragma unroll
+                for (int j = 0; j < K; ++j) h[j] = restart ? 0.0f : h[j];
+            }
             const float hl0 = from_prev(h[K - 1]);
             const float hrK = from_next(h[0]);
             float hn[K];
@@ -391,11 +408,11 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         int s0 = 0;
         for (; s0 + D <= NL; s0 += D) {
 #pragma unroll
-            for (int d = 0; d < D; ++d) step(d);
+            for (int d = 0; d < D; ++d) step(s0 + d, d);
         }
 #pragma unroll
         for (int d = 0; d < D; ++d)
-            if (s0 + d < NL) step(d);
+            if (s0 + d < NL) step(s0 + d, d);
     }
     lds_order();
 
@@ -435,8 +452,8 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         // read-back of the staging lines: dword f = lane + 64 t of the six
         // lines of L ES / 4 dwords, stored at its place on the current line of
         // its half's tap plane
-        constexpr int NT = ES == 2 ? 5 : 9;     // ceil(6 * 96 * ES / 4 / 64)
-        const int per_line = L * ES / 4;
+        constexpr int NT = GS == 2 ? 5 : 9;     // ceil(6 * 96 * GS / 4 / 64)
+        const int per_line = L * GS / 4;
         uint32_t rd[NT], go[NT], gd[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -448,13 +465,16 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 const int hk = f / per_line, m = f - hk * per_line;
                 const int h = hk / 3, k = hk - 3 * h;
                 const int start = h == 0 ? NL - 1 : 0;      // first adjoint line of that half
-                rd[t] = lay.stage + hk * 96 * ES + 4 * m;
-                go[t] = static_cast<uint32_t>((((dir0 + h) * planes + plane) * 3 + k) * HW * ES +
-                                              start * L * ES + 4 * m);
-                gd[t] = h == 0 ? 0u - line_b : line_b;
+                rd[t] = lay.stage + hk * 96 * GS + 4 * m;
+                go[t] = static_cast<uint32_t>((((dir0 + h) * planes + plane) * 3 + k) * HW * GS +
+                                              start * L * GS + 4 * m);
+                gd[t] = h == 0 ? 0u - static_cast<uint32_t>(L * GS) : static_cast<uint32_t>(L * GS);
             }
         }
-        const uint32_t my_stage = lay.stage + 3 * half * 96 * ES;
+        const uint32_t my_stage = lay.stage + 3 * half * 96 * GS;
+        // adjoint step of the next restart line: its taps read nothing (tap
+        // gradient 0) and the line before it receives no adjoint term from it
+        int next_restart = fwd ? (NL - 1) - ((NL - 1) / seg) * seg : seg - 1;
         // LDS: g_i goes to line i (G); h_{i-1} (lanes 0-31) or h_{i+1}
         // (32-63) is read one step ahead (P), and P of one step is G of the next
         const int dl = fwd ? -L : L;       // values per step
@@ -477,7 +497,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             gp[j] = w0p[j] = w1p[j] = w2p[j] = 0.0f;
         }
 
-        auto step = [&](int d) {
+        auto step = [&](int s, int d) {
             asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
             asm volatile("" : "+v"(ubuf[d]), "+v"(gbuf[d]));
             float s0[K], s1[K], s2[K], t[K], r[K], ugy[K];
@@ -508,6 +528,13 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             }
 
             // tap gradients of line i
+            bool restart = false;
+            if constexpr (Chunked) {
+                restart = s == next_restart;
+                next_restart = restart ? next_restart + seg : next_restart;
+#pragma unroll
+                for (int j = 0; j < K; ++j) hp[j] = restart ? 0.0f : hp[j];
+            }
             const float hl0 = from_prev(hp[K - 1]);
             const float hrK = from_next(hp[0]);
             float gz0[K], gz1[K], gz2[K];
@@ -532,9 +559,9 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 w1p[j] = wn1;
                 w2p[j] = wn2;
             }
-            stage_put<T, K>(my_stage, q, gz0);
-            stage_put<T, K>(my_stage + 96 * ES, q, gz1);
-            stage_put<T, K>(my_stage + 2 * 96 * ES, q, gz2);
+            stage_put<GT, K>(my_stage, q, gz0);
+            stage_put<GT, K>(my_stage + 96 * GS, q, gz1);
+            stage_put<GT, K>(my_stage + 2 * 96 * GS, q, gz2);
             // the staging lines are written with 16- and 32-bit stores and read
             // back as dwords: keep the compiler from moving the reads above
             // the writes (the LDS then executes them in program order)
@@ -547,7 +574,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
 
 #pragma unroll
             for (int j = 0; j < K; ++j) {
-                gp[j] = g[j];
+                gp[j] = restart ? 0.0f : g[j];
                 put(aGH[j], aGL[j], g[j]);
                 aGH[j] = aPH[j];
                 aGL[j] = aPL[j];
@@ -559,11 +586,11 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         int s0 = 0;
         for (; s0 + D <= NL; s0 += D) {
 #pragma unroll
-            for (int d = 0; d < D; ++d) step(d);
+            for (int d = 0; d < D; ++d) step(s0 + d, d);
         }
 #pragma unroll
         for (int d = 0; d < D; ++d)
-            if (s0 + d < NL) step(d);
+            if (s0 + d < NL) step(s0 + d, d);
     }
     lds_order();
 
@@ -640,75 +667,104 @@ struct PairBwdWs {
     }
 };
 
-template <typename T, int K, bool Cols>
-hipError_t launch_pass(const T* xl, const T* ll, const T* ul, const T* gl, const T* w4, T* gw4,
-                       float eps, int64_t planes, int64_t NL, int64_t L, int dir0, float* s_ws,
-                       float* g_ws, const T* x, const T* lam, const T* gy, T* gx, T* glam, T* gu,
-                       hipStream_t stream) {
+// Arguments of one launch of the pair kernel.
+template <typename T, typename GT>
+struct PassArgs {
+    const T *xl, *ll, *ul, *gl;     // line-major inputs of the pair
+    const T* w4;
+    int w4_bytes;
+    GT* gwd;                        // per-channel tap gradients
+    int gw_bytes;
+    int cpg, k_chunk;
+    float eps;
+    int64_t planes, NL, L;
+    int dir0;
+    float *s_ws, *g_ws;
+    const T *x, *lam, *gy;          // pixel order (column pair's outputs)
+    T *gx, *glam, *gu;
+};
+
+template <typename T, typename GT, int K, bool Cols, bool Chunked>
+hipError_t launch_pass(const PassArgs<T, GT>& a, hipStream_t stream) {
     constexpr int D = 4;   // lines prefetched ahead (the steps are long; a deeper unroll outgrows the instruction cache)
-    const size_t lds = PairBwdLayout(static_cast<int>(NL), static_cast<int>(L), sizeof(T) == 2).bytes;
-    auto kern = prop2d_backward_pair_kernel<T, K, D, Cols>;
+    const size_t lds = PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L), sizeof(T) == 2,
+                                     sizeof(GT)).bytes;
+    auto kern = prop2d_backward_pair_kernel<T, GT, K, D, Cols, Chunked>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    const int64_t n = planes * NL * L;
-    kern<<<dim3(static_cast<unsigned>(planes)), dim3(64), lds, stream>>>(
-        xl, ll, ul, gl, w4, gw4, static_cast<int>(12 * n * sizeof(T)), eps, static_cast<int>(planes),
-        static_cast<int>(NL), static_cast<int>(L), dir0, s_ws, g_ws, x, lam, gy, gx, glam, gu);
+    kern<<<dim3(static_cast<unsigned>(a.planes)), dim3(64), lds, stream>>>(
+        a.xl, a.ll, a.ul, a.gl, a.w4, a.w4_bytes, a.gwd, a.gw_bytes, a.cpg, a.k_chunk, a.eps,
+        static_cast<int>(a.planes), static_cast<int>(a.NL), static_cast<int>(a.L), a.dir0, a.s_ws,
+        a.g_ws, a.x, a.lam, a.gy, a.gx, a.glam, a.gu);
     return hipGetLastError();
 }
 
-template <typename T, bool Cols>
-hipError_t launch_pass_k(const T* xl, const T* ll, const T* ul, const T* gl, const T* w4, T* gw4,
-                         float eps, int64_t planes, int64_t NL, int64_t L, int dir0, float* s_ws,
-                         float* g_ws, const T* x, const T* lam, const T* gy, T* gx, T* glam, T* gu,
-                         hipStream_t stream) {
-    if (L <= 32)
-        return launch_pass<T, 1, Cols>(xl, ll, ul, gl, w4, gw4, eps, planes, NL, L, dir0, s_ws, g_ws,
-                                       x, lam, gy, gx, glam, gu, stream);
-    if (L <= 64)
-        return launch_pass<T, 2, Cols>(xl, ll, ul, gl, w4, gw4, eps, planes, NL, L, dir0, s_ws, g_ws,
-                                       x, lam, gy, gx, glam, gu, stream);
-    return launch_pass<T, 3, Cols>(xl, ll, ul, gl, w4, gw4, eps, planes, NL, L, dir0, s_ws, g_ws,
-                                   x, lam, gy, gx, glam, gu, stream);
+template <typename T, typename GT, bool Cols>
+hipError_t launch_pass_k(const PassArgs<T, GT>& a, hipStream_t stream) {
+    const bool ch = a.k_chunk > 1;
+    if (a.L <= 32)
+        return ch ? launch_pass<T, GT, 1, Cols, true>(a, stream) : launch_pass<T, GT, 1, Cols, false>(a, stream);
+    if (a.L <= 64)
+        return ch ? launch_pass<T, GT, 2, Cols, true>(a, stream) : launch_pass<T, GT, 2, Cols, false>(a, stream);
+    return ch ? launch_pass<T, GT, 3, Cols, true>(a, stream) : launch_pass<T, GT, 3, Cols, false>(a, stream);
 }
 
-template <typename T>
+template <typename T, typename GT>
 hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, const void* w4_,
-                           const void* gy_, float eps, void* gx_, void* glam_, void* gu_, void* gw4_,
-                           void* ws_, int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
-    const T* x = static_cast<const T*>(x_);
-    const T* lam = static_cast<const T*>(lam_);
-    const T* u = static_cast<const T*>(u_);
-    const T* w4 = static_cast<const T*>(w4_);
-    const T* gy = static_cast<const T*>(gy_);
-    T* gx = static_cast<T*>(gx_);
-    T* glam = static_cast<T*>(glam_);
-    T* gu = static_cast<T*>(gu_);
-    T* gw4 = static_cast<T*>(gw4_);
+                           const void* gy_, float eps, void* gx_, void* glam_, void* gu_, void* gwd_,
+                           void* ws_, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                           hipStream_t stream) {
     char* ws = static_cast<char*>(ws_);
     const PairBwdWs lay(planes, H, W, sizeof(T));
     T* xt = reinterpret_cast<T*>(ws + lay.xt);
     T* lt = reinterpret_cast<T*>(ws + lay.lt);
     T* ut = reinterpret_cast<T*>(ws + lay.ut);
     T* gt = reinterpret_cast<T*>(ws + lay.gt);
-    float* s_ws = reinterpret_cast<float*>(ws + lay.s);
-    float* g_ws = reinterpret_cast<float*>(ws + lay.g);
+    PassArgs<T, GT> a;
+    a.xl = static_cast<const T*>(x_);
+    a.ll = static_cast<const T*>(lam_);
+    a.ul = static_cast<const T*>(u_);
+    a.gl = static_cast<const T*>(gy_);
+    a.w4 = static_cast<const T*>(w4_);
+    a.w4_bytes = static_cast<int>(12 * (planes / o.cpg) * H * W * sizeof(T));
+    a.gwd = static_cast<GT*>(gwd_);
+    a.gw_bytes = static_cast<int>(12 * planes * H * W * sizeof(GT));
+    a.cpg = static_cast<int>(o.cpg);
+    a.k_chunk = static_cast<int>(o.k_chunk);
+    a.eps = eps;
+    a.planes = planes;
+    a.NL = H;
+    a.L = W;
+    a.dir0 = 0;
+    a.s_ws = reinterpret_cast<float*>(ws + lay.s);
+    a.g_ws = reinterpret_cast<float*>(ws + lay.g);
+    a.x = a.xl;
+    a.lam = a.ll;
+    a.gy = a.gl;
+    a.gx = static_cast<T*>(gx_);
+    a.glam = static_cast<T*>(glam_);
+    a.gu = static_cast<T*>(gu_);
 
     // row pair on the inputs as they are: taps and gradients of directions 0, 1
-    hipError_t e = launch_pass_k<T, false>(x, lam, u, gy, w4, gw4, eps, planes, H, W, 0, s_ws, g_ws,
-                                           x, lam, gy, gx, glam, gu, stream);
+    hipError_t e = launch_pass_k<T, GT, false>(a, stream);
     if (e != hipSuccess) return e;
     transpose4_kernel<T><<<dim3(static_cast<unsigned>(planes), 4), dim3(256),
                            static_cast<size_t>(H * (W + 1)) * sizeof(uint32_t), stream>>>(
-        x, lam, u, gy, xt, lt, ut, gt, static_cast<int>(H), static_cast<int>(W));
+        a.x, a.lam, a.ul, a.gy, xt, lt, ut, gt, static_cast<int>(H), static_cast<int>(W));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // column pair on the transposed copies: directions 2, 3, then the outputs
-    return launch_pass_k<T, true>(xt, lt, ut, gt, w4, gw4, eps, planes, W, H, 2, s_ws, g_ws, x, lam,
-                                  gy, gx, glam, gu, stream);
+    a.xl = xt;
+    a.ll = lt;
+    a.ul = ut;
+    a.gl = gt;
+    a.NL = W;
+    a.L = H;
+    a.dir0 = 2;
+    return launch_pass_k<T, GT, true>(a, stream);
 }
 
 }  // namespace
@@ -716,8 +772,8 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
 bool prop2d_backward_pair_shape(int64_t planes, int64_t H, int64_t W) {
     if (H < 2 || W < 2 || H > 96 || W > 96 || (H & 1) || (W & 1)) return false;
     // the fp32 layout is the larger
-    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), false).bytes > kLdsBytes ||
-        PairBwdLayout(static_cast<int>(W), static_cast<int>(H), false).bytes > kLdsBytes)
+    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), false, 4).bytes > kLdsBytes ||
+        PairBwdLayout(static_cast<int>(W), static_cast<int>(H), false, 4).bytes > kLdsBytes)
         return false;
     // every stream offset is a 32-bit byte offset into one buffer resource
     return 12 * planes * H * W * 4 <= 0x7fffffff;
@@ -739,12 +795,17 @@ bool prop2d_backward_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t
 
 hipError_t launch_prop2d_backward_pair(const void* x, const void* lam, const void* u,
                                        const void* w4, const void* gy, float eps, void* gx,
-                                       void* glam, void* gu, void* gw4, void* ws, int dtype,
-                                       int64_t planes, int64_t H, int64_t W, hipStream_t stream) {
-    return dtype == 0
-               ? backward_pair_t<float>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W, stream)
-               : backward_pair_t<uint16_t>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, planes, H, W,
-                                           stream);
+                                       void* glam, void* gu, void* gwd, bool gw_fp32, void* ws,
+                                       int dtype, int64_t planes, int64_t H, int64_t W,
+                                       const PropOpts& o, hipStream_t stream) {
+    if (dtype == 0)
+        return backward_pair_t<float, float>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes, H, W,
+                                             o, stream);
+    if (gw_fp32)
+        return backward_pair_t<uint16_t, float>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes, H,
+                                                W, o, stream);
+    return backward_pair_t<uint16_t, uint16_t>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes, H,
+                                               W, o, stream);
 }
 
 }  // namespace gspn

@@ -136,24 +136,32 @@ int gspn_prop2d_4dir_ex(const void* x, const void* lam, const void* u, const voi
                                              static_cast<hipStream_t>(stream)));
 }
 
-int64_t gspn_prop2d_4dir_backward_workspace(int64_t B, int64_t C, int64_t H, int64_t W) {
+int64_t gspn_prop2d_4dir_ex_backward_workspace(int64_t B, int64_t C, int64_t groups, int64_t H,
+                                               int64_t W) {
     if (check_dims(B, C, H, W, 12) != GSPN_OK) return -1;
     if (H > gspn::prop2d_backward_max_line() || W > gspn::prop2d_backward_max_line()) return -1;
-    return gspn::prop2d_backward_workspace_bytes(B * C, H, W);
+    if (groups < 1 || groups > C || C % groups != 0) return -1;
+    return gspn::prop2d_backward_workspace_bytes(B * C, H, W, C / groups);
 }
 
-int gspn_prop2d_4dir_backward(const void* x, const void* lam, const void* u,
-                              const void* w_raw4, const void* gy, float eps, void* gx,
-                              void* glam, void* gu, void* gw4, void* workspace,
-                              int64_t workspace_bytes, int dtype, int64_t B, int64_t C,
-                              int64_t H, int64_t W, void* stream) {
+int64_t gspn_prop2d_4dir_backward_workspace(int64_t B, int64_t C, int64_t H, int64_t W) {
+    return gspn_prop2d_4dir_ex_backward_workspace(B, C, C, H, W);
+}
+
+int gspn_prop2d_4dir_ex_backward(const void* x, const void* lam, const void* u,
+                                 const void* w_raw4, int64_t groups, int64_t k_chunk,
+                                 const void* gy, float eps, void* gx, void* glam, void* gu,
+                                 void* gw4, void* workspace, int64_t workspace_bytes, int dtype,
+                                 int64_t B, int64_t C, int64_t H, int64_t W, void* stream) {
     if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
     if (int s = check_dims(B, C, H, W, 12)) return s;
     if (H > gspn::prop2d_backward_max_line() || W > gspn::prop2d_backward_max_line())
         return GSPN_ERR_SHAPE;
+    if (groups < 1 || groups > C || C % groups != 0) return GSPN_ERR_SHAPE;
+    if (k_chunk < 1) return GSPN_ERR_VALUE;
     if (!valid_eps(eps)) return GSPN_ERR_VALUE;
     if (!x || !lam || !u || !w_raw4 || !gy || !gx || !glam || !gu || !gw4) return GSPN_ERR_NULL;
-    const int64_t need = gspn::prop2d_backward_workspace_bytes(B * C, H, W);
+    const int64_t need = gspn::prop2d_backward_workspace_bytes(B * C, H, W, C / groups);
     if (need > 0 && !workspace) return GSPN_ERR_NULL;
     if (workspace_bytes < 0 || (need > 0 && workspace_bytes < need)) return GSPN_ERR_SHAPE;
     const void* ptrs[] = {x, lam, u, w_raw4, gy, gx, glam, gu, gw4};
@@ -161,10 +169,11 @@ int gspn_prop2d_4dir_backward(const void* x, const void* lam, const void* u,
         if (!aligned(p, dtype)) return GSPN_ERR_ALIGN;
     if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u)) return GSPN_ERR_ALIGN;
     const int64_t n = B * C * H * W * elem_size(dtype);
+    const int64_t taps = 12 * B * groups * H * W * elem_size(dtype);
     const void* ins[] = {x, lam, u, w_raw4, gy};
-    const int64_t in_bytes[] = {n, n, n, 12 * n, n};
+    const int64_t in_bytes[] = {n, n, n, taps, n};
     void* outs[] = {gx, glam, gu, gw4};
-    const int64_t out_bytes[] = {n, n, n, 12 * n};
+    const int64_t out_bytes[] = {n, n, n, taps};
     for (int o = 0; o < 4; ++o) {
         for (int i = 0; i < 5; ++i)
             if (overlap(outs[o], out_bytes[o], ins[i], in_bytes[i])) return GSPN_ERR_ALIAS;
@@ -175,9 +184,21 @@ int gspn_prop2d_4dir_backward(const void* x, const void* lam, const void* u,
     if (need > 0)
         for (int i = 0; i < 5; ++i)
             if (overlap(workspace, need, ins[i], in_bytes[i])) return GSPN_ERR_ALIAS;
+    gspn::PropOpts opts;
+    opts.cpg = C / groups;
+    opts.k_chunk = std::min<int64_t>(k_chunk, std::max(H, W));
     return launch_status(gspn::launch_prop2d_backward(
         x, lam, u, w_raw4, gy, eps, gx, glam, gu, gw4, need > 0 ? workspace : nullptr, dtype,
-        B * C, H, W, static_cast<hipStream_t>(stream)));
+        B * C, H, W, opts, static_cast<hipStream_t>(stream)));
+}
+
+int gspn_prop2d_4dir_backward(const void* x, const void* lam, const void* u,
+                              const void* w_raw4, const void* gy, float eps, void* gx,
+                              void* glam, void* gu, void* gw4, void* workspace,
+                              int64_t workspace_bytes, int dtype, int64_t B, int64_t C,
+                              int64_t H, int64_t W, void* stream) {
+    return gspn_prop2d_4dir_ex_backward(x, lam, u, w_raw4, C, 1, gy, eps, gx, glam, gu, gw4,
+                                        workspace, workspace_bytes, dtype, B, C, H, W, stream);
 }
 
 int64_t gspn_latent_sublayer_workspace(int dtype, int64_t B, int64_t C, int64_t Cc,

@@ -47,13 +47,15 @@ hipError_t launch_prop2d_phase(const void* x, const void* lam, const void* u, co
                                float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                                const PropOpts& opts, hipStream_t stream);
 
-// Gradient of gspn_prop2d_4dir (gspn_backward.hip).  ws is NULL when the
-// three fp32 planes of a workgroup fit in LDS, else planes * 3 * H * W floats.
+// Gradient of gspn_prop2d_4dir_ex (gspn_backward.hip): taps of plane p read
+// from group plane p / cpg, scans cut into k_chunk segments.  ws holds
+// prop2d_backward_workspace_bytes(planes, H, W, cpg) bytes (NULL when that
+// is 0).
 hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u, const void* w4,
                                   const void* gy, float eps, void* gx, void* glam, void* gu,
                                   void* gw4, void* ws, int dtype, int64_t planes, int64_t H,
-                                  int64_t W, hipStream_t stream);
-int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W);
+                                  int64_t W, const PropOpts& opts, hipStream_t stream);
+int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg);
 
 // Fast path of the gradient for planes of even sides up to 96: one wavefront
 // per plane and direction pair (gspn_backward_pair.hip).  Needs a workspace of
@@ -62,10 +64,13 @@ bool prop2d_backward_pair_shape(int64_t planes, int64_t H, int64_t W);
 int64_t prop2d_backward_pair_workspace_bytes(int64_t planes, int64_t H, int64_t W);
 bool prop2d_backward_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t W,
                                    const void* const* ptrs, int nptrs, const void* ws);
+// gwd receives the per-channel tap gradients: gw4 itself (storage type), or
+// with gw_fp32 an fp32 buffer [4][planes][3][H W] for channels sharing taps.
 hipError_t launch_prop2d_backward_pair(const void* x, const void* lam, const void* u,
                                        const void* w4, const void* gy, float eps, void* gx,
-                                       void* glam, void* gu, void* gw4, void* ws, int dtype,
-                                       int64_t planes, int64_t H, int64_t W, hipStream_t stream);
+                                       void* glam, void* gu, void* gwd, bool gw_fp32, void* ws,
+                                       int dtype, int64_t planes, int64_t H, int64_t W,
+                                       const PropOpts& opts, hipStream_t stream);
 // Longest line the backward's LDS lines allow.
 int64_t prop2d_backward_max_line();
 

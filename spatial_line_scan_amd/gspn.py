@@ -67,6 +67,11 @@ def lib():
         L.gspn_prop2d_4dir_backward.restype = ci
         L.gspn_prop2d_4dir_backward_workspace.argtypes = [i64, i64, i64, i64]
         L.gspn_prop2d_4dir_backward_workspace.restype = i64
+        L.gspn_prop2d_4dir_ex_backward.argtypes = [vp, vp, vp, vp, i64, i64, vp, cf, vp, vp, vp, vp,
+                                                   vp, i64, ci, i64, i64, i64, i64, vp]
+        L.gspn_prop2d_4dir_ex_backward.restype = ci
+        L.gspn_prop2d_4dir_ex_backward_workspace.argtypes = [i64, i64, i64, i64, i64]
+        L.gspn_prop2d_4dir_ex_backward_workspace.restype = i64
         _lib = L
     return _lib
 
@@ -221,6 +226,45 @@ def prop2d_4dir_backward(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4
         _check(lib().gspn_prop2d_4dir_backward(_p(x), _p(lam), _p(u), _p(w4), _p(gy), float(eps),
                                                _p(gx), _p(glam), _p(gu), _p(gw4), ws_ptr, ws_bytes,
                                                _dtype_code(x), B, C, H, W, _stream(x)))
+    return gx, glam, gu, gw4
+
+
+def prop2d_4dir_ex_backward_workspace_bytes(B: int, C: int, groups: int, H: int, W: int) -> int:
+    """Scratch bytes prop2d_4dir_ex_backward needs for these sizes (0: none)."""
+    n = lib().gspn_prop2d_4dir_ex_backward_workspace(B, C, groups, H, W)
+    if n < 0:
+        raise ValueError("sizes not accepted by gspn_prop2d_4dir_ex_backward")
+    return n
+
+
+def prop2d_4dir_ex_backward(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4: torch.Tensor,
+                            gy: torch.Tensor, groups: int, k_chunk: int = 1, eps: float = 1e-6,
+                            workspace: torch.Tensor | None = None):
+    """Gradients (gx, glam, gu, gw4) of prop2d_4dir_ex given gy = dL/dy; gw4
+    has w4's grouped layout.  The workspace is allocated here with torch when
+    none is given."""
+    _same(x, lam, u, w4, gy)
+    if x.dim() != 4 or lam.shape != x.shape or u.shape != x.shape or gy.shape != x.shape:
+        raise ValueError("x, lam, u, gy must share one [B, C, H, W] shape")
+    B, C, H, W = x.shape
+    if groups < 1 or C % groups:
+        raise ValueError("groups must divide C")
+    if w4.numel() != 12 * B * groups * H * W:
+        raise ValueError("w4 must hold 4*B*groups*3*H*W elements")
+    need = prop2d_4dir_ex_backward_workspace_bytes(B, C, groups, H, W)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=x.device)
+    if workspace is not None and (workspace.device != x.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on x's device")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    gx, glam, gu = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    gw4 = torch.empty_like(w4)
+    with torch.cuda.device(x.device):
+        _check(lib().gspn_prop2d_4dir_ex_backward(_p(x), _p(lam), _p(u), _p(w4), int(groups),
+                                                  int(k_chunk), _p(gy), float(eps), _p(gx), _p(glam),
+                                                  _p(gu), _p(gw4), ws_ptr, ws_bytes, _dtype_code(x),
+                                                  B, C, H, W, _stream(x)))
     return gx, glam, gu, gw4
 
 

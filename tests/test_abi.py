@@ -43,13 +43,14 @@ def test_exports_every_declared_symbol(L):
                          "gspn_scan_dir", "gspn_prop2d_4dir",
                          "gspn_prop2d_4dir_backward", "gspn_prop2d_4dir_backward_workspace",
                          "gspn_prop2d_4dir_ex", "gspn_latent_sublayer",
-                         "gspn_latent_sublayer_workspace"}
+                         "gspn_latent_sublayer_workspace", "gspn_prop2d_4dir_ex_backward",
+                         "gspn_prop2d_4dir_ex_backward_workspace"}
     for s in syms:
         assert hasattr(L, s), s
 
 
 def test_version_and_status_strings(L):
-    assert L.gspn_abi_version() == 4
+    assert L.gspn_abi_version() == 5
     for s in range(9):
         assert L.gspn_status_str(s).decode().startswith("GSPN")
     assert L.gspn_status_str(12345)
@@ -214,6 +215,40 @@ def test_backward_workspace_checks(L):
     assert bwd(L, ws=P(0), ws_bytes=need, H=120, W=120) == ALIAS        # over x
     assert bwd(L, ws=P(7), ws_bytes=need, H=120, W=120) == ALIAS        # over gu
     assert bwd(L, ws_bytes=-1) == SHAPE
+
+
+def exb(L, groups=3, k=1, ws=None, ws_bytes=0, dt=0, B=2, C=3, H=5, W=7, ptrs=None):
+    p = list(ptrs) if ptrs else [P(i) for i in range(9)]
+    return L.gspn_prop2d_4dir_ex_backward(p[0], p[1], p[2], p[3], groups, k, p[4], 1e-6, p[5], p[6],
+                                          p[7], p[8], ws, ws_bytes, dt, B, C, H, W, None)
+
+
+def test_ex_backward_workspace_query(L):
+    # shared taps add 48 bytes of fp32 tap gradients per pixel-channel
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 3, 5, 7) == 0
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 1, 5, 7) == (12 * 2 * 3 * 35 * 4 + 255) // 256 * 256
+    n = 32 * 64 * 74 * 74
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(32, 64, 64, 74, 74) == 6 * 4 * n
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(32, 64, 1, 74, 74) == 6 * 4 * n + 48 * n
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 2, 5, 7) == -1       # 2 does not divide 3
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 0, 5, 7) == -1
+
+
+def test_ex_backward_rejects_bad_arguments(L):
+    assert exb(L, groups=2) == SHAPE
+    assert exb(L, groups=0) == SHAPE
+    assert exb(L, k=0) == VALUE
+    assert exb(L, dt=2) == DTYPE
+    assert exb(L, groups=1) == NULL                          # shared taps need a workspace
+    need = L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 1, 5, 7)
+    assert exb(L, groups=1, ws=P(10), ws_bytes=need - 4) == SHAPE
+    assert exb(L, groups=1, ws=P(0), ws_bytes=need) == ALIAS      # over x
+    ptrs = [P(j) for j in range(9)]
+    ptrs[8] = P(3)
+    assert exb(L, ptrs=ptrs) == ALIAS                        # gw4 over w_raw4
+    ptrs = [P(j) for j in range(9)]
+    ptrs[8] = ctypes.c_void_p(A + 3 * STEP + 12 * 2 * 1 * 35 * 4 - 4)
+    assert exb(L, groups=1, ptrs=ptrs, ws=P(10), ws_bytes=need) == ALIAS   # last word of 1-group taps
 
 
 def ex(L, groups=3, k=1, eps=1e-6, dt=0, B=2, C=3, H=5, W=7, y=None):
