@@ -83,6 +83,21 @@ hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const v
 int64_t latent_sublayer_workspace_bytes(int dtype, int64_t B, int64_t Cc, int64_t G, int64_t H,
                                         int64_t W);
 
+// Matrix-core 1x1 convolutions of the latent sublayer (bf16 storage).
+// conv1x1_eligible: shapes the kernels take (K = Cc a multiple of 8 up to
+// 64, H W a multiple of 4, H and W at most 96, C a multiple of 4).
+bool conv1x1_eligible(int dtype, int64_t B, int64_t K, int64_t H, int64_t W, int64_t C);
+// lambda, u ([B][Cc][H W]) and the four directions' raw taps (taps4[d]:
+// [B][G][3][..], row-major for TD and BU, column-major for LR and RL) from
+// the latent z [B][Cc][H W] and w_param [2 Cc + 12 G][Cc]; zt receives the
+// transposed latent ([B][Cc][W][H]).
+hipError_t launch_conv1x1_params(const void* z, void* zt, const void* w_param, int64_t B,
+                                 int64_t Cc, int64_t G, int64_t H, int64_t W, void* lam, void* u,
+                                 void* const* taps4, hipStream_t stream);
+// y_tok [B][H W][C] = P_up applied to the planar latent yc [B][Cc][H W].
+hipError_t launch_conv1x1_up(const void* yc, const void* p_up, int64_t B, int64_t Cc, int64_t C,
+                             int64_t H, int64_t W, void* y_tok, hipStream_t stream);
+
 // Largest plane (H * W pixels) gspn_prop2d_4dir accepts for an element type.
 int64_t prop2d_max_plane(int dtype, int64_t H, int64_t W);
 

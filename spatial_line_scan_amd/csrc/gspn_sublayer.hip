@@ -267,6 +267,21 @@ hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const v
     e = gemm(dtype, {HIPBLAS_OP_T, HIPBLAS_OP_N, N, Cc, C, C, C, N, N * C, 0, Cc * N, bt}, x_tok,
              p_down, z, bws, stream);
     if (e != hipSuccess) return e;
+    PropOpts opts;
+    opts.cpg = Cc / G;
+    opts.k_chunk = k_chunk;
+    if (conv1x1_eligible(dtype, B, Cc, H, W, C)) {
+        // the parameter convolutions and P_up on the matrix cores: one launch
+        // writes lambda, u and the row scans' taps from z, one the column
+        // scans' taps from the transposed latent zt
+        void* taps4[4];
+        for (int d = 0; d < 4; ++d) taps4[d] = taps + d * B * 3 * G * N * es;
+        e = launch_conv1x1_params(z, zt, w_param, B, Cc, G, H, W, lam, u, taps4, stream);
+        if (e != hipSuccess) return e;
+        e = launch_prop2d(z, lam, u, taps, eps, yc, dtype, B * Cc, H, W, opts, stream);
+        if (e != hipSuccess) return e;
+        return launch_conv1x1_up(yc, p_up, B, Cc, C, H, W, y_tok, stream);
+    }
     // column-major copy of every latent plane, for the column scans' taps
     {
         const int tiles_w = static_cast<int>((W + kTile - 1) / kTile);
@@ -297,9 +312,6 @@ hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const v
                    3 * G * N);
         if (e != hipSuccess) return e;
     }
-    PropOpts opts;
-    opts.cpg = Cc / G;
-    opts.k_chunk = k_chunk;
     e = launch_prop2d(z, lam, u, taps, eps, yc, dtype, B * Cc, H, W, opts, stream);
     if (e != hipSuccess) return e;
     // y[b] (N x C, row-major) = yc[b]^T P_up^T: column-major y^T = P_up yc[b]
