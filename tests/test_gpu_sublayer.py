@@ -48,7 +48,12 @@ def _run(B, C, Cc, G, H, W, k, dtype, seed, batches=None):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("B,C,Cc,G,H,W,k", [
     (2, 24, 8, 8, 10, 10, 1), (2, 24, 8, 1, 10, 12, 1), (1, 40, 8, 2, 9, 14, 3),
-    (3, 16, 4, 4, 27, 27, 1), (2, 64, 16, 16, 74, 74, 1), (1, 32, 8, 1, 100, 36, 2)])
+    (3, 16, 4, 4, 27, 27, 1), (2, 64, 16, 16, 74, 74, 1), (1, 32, 8, 1, 100, 36, 2),
+    # matrix-core path edges: C % 8 == 4 (8-byte token stores), Cc = 24 (a
+    # zero-padded 16-k step), a rectangular plane through the transpose, the
+    # largest side it takes (96), and a shape just past it (97: hipBLASLt)
+    (1, 20, 8, 2, 10, 12, 1), (2, 36, 24, 3, 12, 20, 2), (1, 64, 64, 1, 96, 96, 1),
+    (1, 24, 8, 8, 4, 97, 1)])
 def test_sublayer_small(B, C, Cc, G, H, W, k, dtype):
     say("sublayer", B, C, Cc, G, H, W, k, dtype)
     _run(B, C, Cc, G, H, W, k, dtype, 5 + B + C + G + k)
