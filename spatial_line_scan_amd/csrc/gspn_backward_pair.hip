@@ -604,49 +604,56 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
 }
 
 // x, lambda, u, gy of every plane transposed ([H][W] -> [W][H], H and W
-// even); one workgroup per (plane, tensor).  The plane is staged in LDS as
-// 32-bit words with a row pitch of W + 1 (odd, so the column reads of
-// consecutive rows fall in different banks); global reads and writes move
-// element pairs.
+// even); one workgroup per (plane, tensor).  The plane is staged in LDS in
+// its own layout and element type; global reads, LDS writes and global
+// writes move four consecutive elements (H W % 4 == 0), and each thread
+// issues up to eight reads before its LDS writes, so the plane's loads
+// overlap.
 template <typename T>
 __global__ void __launch_bounds__(256)
 transpose4_kernel(const T* __restrict__ a0, const T* __restrict__ a1, const T* __restrict__ a2,
                   const T* __restrict__ a3, T* __restrict__ t0, T* __restrict__ t1,
                   T* __restrict__ t2, T* __restrict__ t3, int H, int W) {
-    extern __shared__ uint32_t tile[];
+    extern __shared__ __attribute__((aligned(16))) uint32_t tile_words[];
+    T* tile = reinterpret_cast<T*>(tile_words);
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    typedef typename std::conditional<sizeof(T) == 4, u32x4_t, u32x2_t>::type quad_t;
     const int which = blockIdx.y;
     const T* src = which == 0 ? a0 : which == 1 ? a1 : which == 2 ? a2 : a3;
     T* dst = which == 0 ? t0 : which == 1 ? t1 : which == 2 ? t2 : t3;
-    const int HW = H * W, pitch = W + 1, npairs = HW / 2;
+    const int HW = H * W, nq = HW / 4;
     const size_t base = static_cast<size_t>(blockIdx.x) * HW;
-    const float invW = 1.0f / static_cast<float>(W), invH = 1.0f / static_cast<float>(H);
-    // with e < 96 * 96 and n <= 96, (e + 0.5) / n in fp32 stays within 6e-4 of
-    // its value, whose distance to an integer is at least 0.5 / n: the quotient is exact
-    for (int t = threadIdx.x; t < npairs; t += 256) {
-        const int e = 2 * t;
-        const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
-        const int c = e - r * W;
-        uint32_t v0, v1;
-        if constexpr (sizeof(T) == 4) {
-            const uint2 w = *reinterpret_cast<const uint2*>(src + base + e);
-            v0 = w.x;
-            v1 = w.y;
-        } else {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(src + base + e);
-            v0 = w & 0xffffu;
-            v1 = w >> 16;
+    const quad_t* sq = reinterpret_cast<const quad_t*>(src + base);
+    quad_t* dq = reinterpret_cast<quad_t*>(dst + base);
+    quad_t* tq = reinterpret_cast<quad_t*>(tile);
+    for (int q0 = 0; q0 < nq; q0 += 8 * 256) {
+        quad_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = q0 + 256 * j + static_cast<int>(threadIdx.x);
+            if (t < nq) v[j] = sq[t];
         }
-        tile[r * pitch + c] = v0;
-        tile[r * pitch + c + 1] = v1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = q0 + 256 * j + static_cast<int>(threadIdx.x);
+            if (t < nq) tq[t] = v[j];
+        }
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < npairs; t += 256) {
-        const int e = 2 * t;                 // output element (c, r), (c, r + 1)
-        const int c = static_cast<int>((static_cast<float>(e) + 0.5f) * invH);
-        const int r = e - c * H;
-        const uint32_t v0 = tile[r * pitch + c], v1 = tile[(r + 1) * pitch + c];
-        if constexpr (sizeof(T) == 4) *reinterpret_cast<uint2*>(dst + base + e) = make_uint2(v0, v1);
-        else *reinterpret_cast<uint32_t*>(dst + base + e) = v0 | (v1 << 16);
+    for (int t = threadIdx.x; t < nq; t += 256) {
+        int c = (4 * t) / H, r = 4 * t - c * H;               // output element (c, r), then down the column
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (sizeof(T) == 4) w[i] = __float_as_uint(tile[r * W + c]);
+            else w[i] = tile[r * W + c];
+            const bool wrap = r + 1 == H;
+            r = wrap ? 0 : r + 1;
+            c = wrap ? c + 1 : c;
+        }
+        if constexpr (sizeof(T) == 4) dq[t] = u32x4_t{w[0], w[1], w[2], w[3]};
+        else dq[t] = u32x2_t{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
     }
 }
 
@@ -753,7 +760,7 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
     hipError_t e = launch_pass_k<T, GT, false>(a, stream);
     if (e != hipSuccess) return e;
     transpose4_kernel<T><<<dim3(static_cast<unsigned>(planes), 4), dim3(256),
-                           static_cast<size_t>(H * (W + 1)) * sizeof(uint32_t), stream>>>(
+                           static_cast<size_t>(H * W) * sizeof(T), stream>>>(
         a.x, a.lam, a.ul, a.gy, xt, lt, ut, gt, static_cast<int>(H), static_cast<int>(W));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // column pair on the transposed copies: directions 2, 3, then the outputs
