@@ -29,6 +29,10 @@ backward  : the gradient entry point (gspn_prop2d_4dir_backward) on the same
             `value`); algorithmic bytes = 31 values per pixel-channel (read x,
             lambda, u, gy and 12 taps, write gx, glambda, gu and 12 tap
             gradients)
+backward_variants : gspn_prop2d_4dir_ex_backward on the same shape: shared
+            taps (groups = 1) and per-channel taps, each with four-segment
+            scans (k_chunk = 4); algorithmic bytes 7 + 24 G / C values per
+            pixel-channel
 """
 from __future__ import annotations
 
@@ -178,6 +182,41 @@ def variant_leg(wl, args, dev, G, k):
     wall, kavg, kmin = _timed(fn, args.steps, args.warmup, torch.cuda.current_stream(dev))
     achieved = nbytes / (kavg * 1e-3) / 1e9
     del sets, outs
+    torch.cuda.empty_cache()
+    return {"groups": G, "k_chunk": k, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+            "value": round(nbytes / (wall / args.steps) / 1e9, 2), "unit": "GB/s",
+            "algorithmic_bytes_per_step": nbytes, "rotated_input_sets": nsets,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                         "kernel_ms_avg": round(kavg, 5), "kernel_ms_min": round(kmin, 5)}}
+
+
+def ex_backward_leg(wl, args, dev, G, k):
+    """gspn_prop2d_4dir_ex_backward (tap groups, chunked scans) on the
+    workload's shape over rotated input sets: reads x, lambda, u, gy and the
+    grouped taps, writes gx, glambda, gu and the grouped tap gradients."""
+    import numpy as np
+    import torch
+
+    from spatial_line_scan_amd import gspn, inputs
+
+    shp = (wl.B, wl.C, wl.H, wl.W)
+    base = {n: inputs.draw_torch(0, n, shp, wl.dtype, dev) for n in ("x", "lam", "u", "gy")}
+    base["w"] = inputs.draw_torch(0, "w", (4, wl.B, G, 3, wl.H * wl.W), wl.dtype, dev)
+    nbytes = int(round((7 + 24.0 * G / wl.C) * wl.elem_bytes * wl.pixels))
+    nsets = max(1, int(np.ceil(args.rotate_bytes / nbytes)))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(nsets - 1)]
+    need = gspn.prop2d_4dir_ex_backward_workspace_bytes(wl.B, wl.C, G, wl.H, wl.W)
+    ws = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def fn(i):
+        s = sets[i % nsets]
+        gspn.prop2d_4dir_ex_backward(s["x"], s["lam"], s["u"], s["w"], s["gy"], G, k, workspace=ws)
+
+    wall, kavg, kmin = _timed(fn, args.steps, args.warmup, torch.cuda.current_stream(dev))
+    achieved = nbytes / (kavg * 1e-3) / 1e9
+    del sets, ws
     torch.cuda.empty_cache()
     return {"groups": G, "k_chunk": k, "ms_per_step": round(wall * 1e3 / args.steps, 5),
             "value": round(nbytes / (wall / args.steps) / 1e9, 2), "unit": "GB/s",
@@ -432,6 +471,9 @@ def main():
     if not args.no_backward:
         print("bench: backward", file=sys.stderr, flush=True)
         out["backward"] = backward_leg(wl, sets, args, dev)
+        if not args.no_variants:
+            print("bench: grouped / chunked backward", file=sys.stderr, flush=True)
+            out["backward_variants"] = [ex_backward_leg(wl, args, dev, G, k) for G, k in ((1, 4), (wl.C, 4))]
     if not args.no_cpu_baseline:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, sets[0], outs[0])
