@@ -1,4 +1,4 @@
-// Four-direction propagation of bf16 planes with even sides up to 96, one
+// Four-direction propagation of bf16 planes with even sides up to 160, one
 // wavefront per (b, c) plane in two phases (gfx950).  fp32 planes take the
 // two-wavefront kernel: their 4-byte lambda x would not leave room for four
 // planes per CU.
@@ -13,7 +13,9 @@
 // 0-31 left-right, lanes 32-63 right-left).  Within a 32-lane half, lane q
 // holds positions Kq .. Kq+K-1 of the current line in registers and the
 // neighbour exchange is one wave-wide DPP shift each way (across the halves
-// the shifted value meets a dropped tap of weight 0).
+// the shifted value meets a dropped tap of weight 0).  K = 1 .. 5 for lines
+// up to 32, 64, 96, 128, 160 positions; a 148 x 148 plane takes 155 KB of
+// LDS, one plane per CU.
 //
 // On-chip data.  LDS holds, per plane:
 //   S  fp32 [H][W]: the sum of the four directional states, zeroed first;
@@ -362,7 +364,16 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
         const int f = lane + 64 * k;
         if (f < pairs) emit_pair(f, ureg[k]);
     }
-    for (int f = lane + 64 * kUPer; f < pairs; f += 64) emit_pair(f, u64p[f]);
+    // the rest of u (planes over 6144 pixels), eight loads in flight at a time
+    for (int f0 = lane + 64 * kUPer; f0 < pairs; f0 += 64 * 8) {
+        u32x2_t uv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (f0 + 64 * j < pairs) uv[j] = u64p[f0 + 64 * j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (f0 + 64 * j < pairs) emit_pair(f0 + 64 * j, uv[j]);
+    }
     if ((words & 1) && lane == 0) y32[words - 1] = emit_word(words - 1, u32[words - 1]);
 }
 
@@ -396,7 +407,9 @@ hipError_t launch_c(const void* x, const void* lam, const void* u, const void* w
     const int64_t Lmax = H > W ? H : W;
     if (Lmax <= 32) return launch_k<1, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
     if (Lmax <= 64) return launch_k<2, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    return launch_k<3, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (Lmax <= 96) return launch_k<3, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (Lmax <= 128) return launch_k<4, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    return launch_k<5, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -406,7 +419,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool prop2d_phase_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
                            const void* lam, const void* u, const void* w4, const void* y) {
     if (dtype != 1) return false;                         // bf16 planes only
-    if (H > 96 || W > 96 || (H & 1) || (W & 1)) return false;   // whole dwords per line
+    if (H > 160 || W > 160 || (H & 1) || (W & 1)) return false;  // K <= 5 positions a lane; whole dwords per line
     if (PhaseLayout(static_cast<int>(H), static_cast<int>(W)).bytes > kLdsBytes) return false;
     if (12 * planes * H * W * 2 > 0x7fffffff) return false;
     return aligned4(x) && aligned4(lam) && aligned4(u) && aligned4(w4) && aligned4(y);

@@ -47,8 +47,12 @@ def test_prop2d_small_workloads_all_seeds(name):
         assert_close(_np(y), r, RTOL[wl.dtype], "%s seed %d" % (name, seed))
 
 
+# bf16 planes with even sides up to 160 take the one-wavefront phase kernel
+# (K = 1..5 positions a lane: sides up to 32, 64, 96, 128, 160), fp32 ones up
+# to 96 the two-wavefront kernel, the rest the general kernel.
 EDGE_SHAPES = [(1, 1), (1, 2), (2, 1), (2, 2), (3, 5), (5, 3), (1, 74), (74, 1), (63, 64), (64, 65),
-               (65, 63), (74, 74), (127, 33), (13, 148), (148, 148), (256, 7)]
+               (65, 63), (74, 74), (127, 33), (13, 148), (148, 148), (256, 7),
+               (98, 98), (128, 128), (130, 160), (160, 2), (2, 160), (158, 126), (96, 128), (162, 40)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -89,7 +93,7 @@ def test_prop2d_full_size_sampled_planes(name):
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["latent1k", "base378"])
+@pytest.mark.parametrize("name", ["latent1k", "base378", "latent2k"])
 def test_prop2d_deterministic(name):
     wl = WORKLOADS[name]
     say("determinism", name)
