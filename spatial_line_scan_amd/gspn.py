@@ -284,6 +284,25 @@ class Prop2d4Dir(torch.autograd.Function):
         return gx, glam, gu, gw4, None
 
 
+class Prop2d4DirEx(torch.autograd.Function):
+    """Autograd wrapper of the grouped / chunked operator: forward
+    prop2d_4dir_ex, backward prop2d_4dir_ex_backward (w4 has the grouped
+    layout [4][B][groups][3][H*W])."""
+
+    @staticmethod
+    def forward(ctx, x, lam, u, w4, groups, k_chunk=1, eps=1e-6):
+        ctx.groups, ctx.k_chunk, ctx.eps = int(groups), int(k_chunk), float(eps)
+        ctx.save_for_backward(x, lam, u, w4)
+        return prop2d_4dir_ex(x, lam, u, w4, groups, k_chunk, eps)
+
+    @staticmethod
+    def backward(ctx, gy):
+        x, lam, u, w4 = ctx.saved_tensors
+        gx, glam, gu, gw4 = prop2d_4dir_ex_backward(x, lam, u, w4, gy.contiguous(), ctx.groups,
+                                                    ctx.k_chunk, ctx.eps)
+        return gx, glam, gu, gw4, None, None, None
+
+
 def latent_sublayer_workspace_bytes(dtype: torch.dtype, B: int, C: int, Cc: int, groups: int,
                                     H: int, W: int) -> int:
     code = FP32 if dtype == torch.float32 else BF16

@@ -138,3 +138,17 @@ def test_ex_backward_caller_workspace_and_eps():
     need = gspn.prop2d_4dir_ex_backward_workspace_bytes(B, C, G, H, W)
     ws = torch.full((need // 4 + 1000,), float("nan"), device=DEV)
     _check(_run(p, G, 3, 1e-3, workspace=ws), _oracle(p, G, 3, 1e-3), "fp32", "workspace")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_ex_autograd_function_matches_entry_point(dtype):
+    say("ex autograd", dtype)
+    G, k = 2, 3
+    p = _problem(2, 4, 10, 12, G, 6, dtype)
+    leaves = [p[n].clone().requires_grad_(True) for n in ("x", "lam", "u", "w")]
+    y = gspn.Prop2d4DirEx.apply(*leaves, G, k)
+    y.backward(p["gy"])
+    direct = _run(p, G, k)
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    for leaf, g in zip(leaves, direct):
+        assert torch.equal(leaf.grad.reshape(-1).view(iv), g.reshape(-1).view(iv))
