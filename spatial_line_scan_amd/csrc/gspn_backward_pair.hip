@@ -1,5 +1,6 @@
 // Gradient of the four-direction propagation, one wavefront per (b, c) plane
-// and direction pair (gfx950), for planes of even sides up to 96.
+// and direction pair (gfx950), for planes of even sides up to 160 (bf16; fp32
+// while its wider layout fits in LDS).
 //
 // Operator: the exact derivative of the forward definition ("Scaling Parallel
 // Sequence Models to Foundation-Scale Vision Encoders", §3 line-scan
@@ -63,7 +64,7 @@ __device__ __forceinline__ void lds_order() {
 }
 
 // LDS layout in bytes (offsets multiples of 16):
-//   [dummy: 16][2 lines][A: NL x L][B: NL x L][2 lines] ... [staging: 6 x 96]
+//   [dummy: 16][2 lines][A: NL x L][B: NL x L][2 lines] ... [staging: 6 x 32 K]
 // A is the plane of lanes 0-31, B that of lanes 32-63.  The line before A
 // and the line after B are zero: the h before a scan's first line.  The
 // outer lines only absorb the read-ahead past the last adjoint step.  Slots
@@ -91,12 +92,12 @@ struct PairBwdLayout {
             end = lb + (NL + 2) * L;
         }
         stage = a16(end);
-        bytes = stage + 6 * 96 * gsize;
+        bytes = stage + 6 * 32 * ((L + 31) / 32) * gsize;   // K = ceil(L / 32) slots a lane
     }
 };
 
 // Tap gradients of one adjoint step go out through LDS: each lane puts the
-// values of its K slots into a staging line per (half, tap), 96 elements
+// values of its K slots into a staging line per (half, tap), 32 K elements
 // apart so that slots past a line's end land in the padding, and the
 // wavefront then writes the six lines as whole dwords (stores of a few bytes
 // at a 6-byte stride cost far more).  kDrop pushes the offset of an unused
@@ -118,7 +119,19 @@ __device__ __forceinline__ void stage_put(uint32_t line, int q, const float (&v)
         w16(line + 2u * q, pack_bf16x2(v[0], v[0]));
     } else if constexpr (K == 2) {
         w32(line + 4u * q, pack_bf16x2(v[0], v[1]));
+    } else if constexpr (K == 4) {
+        w32(line + 8u * q, pack_bf16x2(v[0], v[1]));
+        w32(line + 8u * q + 4u, pack_bf16x2(v[2], v[3]));
+    } else if constexpr (K == 5) {
+        // even q: dwords (5q, 5q+1), (5q+2, 5q+3), short 5q+4; odd q: short 5q,
+        // dwords (5q+1, 5q+2), (5q+3, 5q+4)
+        const bool even = (q & 1) == 0;
+        const uint32_t b0 = 10u * q;
+        w32(b0 + (even ? 0u : 2u) + line, even ? pack_bf16x2(v[0], v[1]) : pack_bf16x2(v[1], v[2]));
+        w32(b0 + (even ? 4u : 6u) + line, even ? pack_bf16x2(v[2], v[3]) : pack_bf16x2(v[3], v[4]));
+        w16(b0 + (even ? 8u : 0u) + line, even ? pack_bf16x2(v[4], v[4]) : pack_bf16x2(v[0], v[0]));
     } else {
+        static_assert(K == 3, "one to five slots a lane");
         // even q: dword (3q, 3q+1), short 3q+2; odd q: short 3q, dword (3q+1, 3q+2)
         const bool even = (q & 1) == 0;
         const float a = even ? v[0] : v[1];
@@ -452,7 +465,8 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         // read-back of the staging lines: dword f = lane + 64 t of the six
         // lines of L ES / 4 dwords, stored at its place on the current line of
         // its half's tap plane
-        constexpr int NT = GS == 2 ? 5 : 9;     // ceil(6 * 96 * GS / 4 / 64)
+        constexpr int SL = 32 * K;               // staging line length
+        constexpr int NT = (3 * K * GS + 3) / 4; // ceil(6 * SL * GS / 4 / 64)
         const int per_line = L * GS / 4;
         uint32_t rd[NT], go[NT], gd[NT];
 #pragma unroll
@@ -465,13 +479,13 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 const int hk = f / per_line, m = f - hk * per_line;
                 const int h = hk / 3, k = hk - 3 * h;
                 const int start = h == 0 ? NL - 1 : 0;      // first adjoint line of that half
-                rd[t] = lay.stage + hk * 96 * GS + 4 * m;
+                rd[t] = lay.stage + hk * SL * GS + 4 * m;
                 go[t] = static_cast<uint32_t>((((dir0 + h) * planes + plane) * 3 + k) * HW * GS +
                                               start * L * GS + 4 * m);
                 gd[t] = h == 0 ? 0u - static_cast<uint32_t>(L * GS) : static_cast<uint32_t>(L * GS);
             }
         }
-        const uint32_t my_stage = lay.stage + 3 * half * 96 * GS;
+        const uint32_t my_stage = lay.stage + 3 * half * SL * GS;
         // adjoint step of the next restart line: its taps read nothing (tap
         // gradient 0) and the line before it receives no adjoint term from it
         int next_restart = fwd ? (NL - 1) - ((NL - 1) / seg) * seg : seg - 1;
@@ -560,8 +574,8 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 w2p[j] = wn2;
             }
             stage_put<GT, K>(my_stage, q, gz0);
-            stage_put<GT, K>(my_stage + 96 * GS, q, gz1);
-            stage_put<GT, K>(my_stage + 2 * 96 * GS, q, gz2);
+            stage_put<GT, K>(my_stage + SL * GS, q, gz1);
+            stage_put<GT, K>(my_stage + 2 * SL * GS, q, gz2);
             // the staging lines are written with 16- and 32-bit stores and read
             // back as dwords: keep the compiler from moving the reads above
             // the writes (the LDS then executes them in program order)
@@ -717,7 +731,15 @@ hipError_t launch_pass_k(const PassArgs<T, GT>& a, hipStream_t stream) {
         return ch ? launch_pass<T, GT, 1, Cols, true>(a, stream) : launch_pass<T, GT, 1, Cols, false>(a, stream);
     if (a.L <= 64)
         return ch ? launch_pass<T, GT, 2, Cols, true>(a, stream) : launch_pass<T, GT, 2, Cols, false>(a, stream);
-    return ch ? launch_pass<T, GT, 3, Cols, true>(a, stream) : launch_pass<T, GT, 3, Cols, false>(a, stream);
+    if (a.L <= 96)
+        return ch ? launch_pass<T, GT, 3, Cols, true>(a, stream) : launch_pass<T, GT, 3, Cols, false>(a, stream);
+    if (a.L <= 128)
+        return ch ? launch_pass<T, GT, 4, Cols, true>(a, stream) : launch_pass<T, GT, 4, Cols, false>(a, stream);
+    if constexpr (sizeof(T) == 4) {
+        return hipErrorInvalidValue;   // fp32 lines take at most four dwords a lane (pair_fits)
+    } else {
+        return ch ? launch_pass<T, GT, 5, Cols, true>(a, stream) : launch_pass<T, GT, 5, Cols, false>(a, stream);
+    }
 }
 
 template <typename T, typename GT>
@@ -759,8 +781,12 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
     // row pair on the inputs as they are: taps and gradients of directions 0, 1
     hipError_t e = launch_pass_k<T, GT, false>(a, stream);
     if (e != hipSuccess) return e;
-    transpose4_kernel<T><<<dim3(static_cast<unsigned>(planes), 4), dim3(256),
-                           static_cast<size_t>(H * W) * sizeof(T), stream>>>(
+    const size_t tlds = static_cast<size_t>(H * W) * sizeof(T);
+    if (tlds > 64 * 1024 &&
+        (e = hipFuncSetAttribute(reinterpret_cast<const void*>(transpose4_kernel<T>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(tlds))) != hipSuccess)
+        return e;
+    transpose4_kernel<T><<<dim3(static_cast<unsigned>(planes), 4), dim3(256), tlds, stream>>>(
         a.x, a.lam, a.ul, a.gy, xt, lt, ut, gt, static_cast<int>(H), static_cast<int>(W));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // column pair on the transposed copies: directions 2, 3, then the outputs
@@ -776,14 +802,28 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
 
 }  // namespace
 
-bool prop2d_backward_pair_shape(int64_t planes, int64_t H, int64_t W) {
-    if (H < 2 || W < 2 || H > 96 || W > 96 || (H & 1) || (W & 1)) return false;
-    // the fp32 layout is the larger
-    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), false, 4).bytes > kLdsBytes ||
-        PairBwdLayout(static_cast<int>(W), static_cast<int>(H), false, 4).bytes > kLdsBytes)
+namespace {
+
+// Even sides up to 160 for bf16 (five slots a lane) and 128 for fp32 (four
+// slots: a lane's window of a line is one load of at most four dwords) whose
+// layout, for the storage width (narrow: bf16) and fp32 staged tap gradients
+// (the larger staging), fits in LDS for both the row and the column launch.
+bool pair_fits(int64_t planes, int64_t H, int64_t W, bool narrow) {
+    const int64_t side = narrow ? 160 : 128;
+    if (H < 2 || W < 2 || H > side || W > side || (H & 1) || (W & 1)) return false;
+    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), narrow, 4).bytes > kLdsBytes ||
+        PairBwdLayout(static_cast<int>(W), static_cast<int>(H), narrow, 4).bytes > kLdsBytes)
         return false;
     // every stream offset is a 32-bit byte offset into one buffer resource
     return 12 * planes * H * W * 4 <= 0x7fffffff;
+}
+
+}  // namespace
+
+// Whether some storage type takes the pair kernel (the narrow bf16 layout is
+// the smaller); sizes the workspace.
+bool prop2d_backward_pair_shape(int64_t planes, int64_t H, int64_t W) {
+    return pair_fits(planes, H, W, true);
 }
 
 int64_t prop2d_backward_pair_workspace_bytes(int64_t planes, int64_t H, int64_t W) {
@@ -792,7 +832,7 @@ int64_t prop2d_backward_pair_workspace_bytes(int64_t planes, int64_t H, int64_t 
 
 bool prop2d_backward_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t W,
                                    const void* const* ptrs, int nptrs, const void* ws) {
-    if (ws == nullptr || !prop2d_backward_pair_shape(planes, H, W)) return false;
+    if (ws == nullptr || !pair_fits(planes, H, W, dtype == 1)) return false;
     // pixel pairs are read and written whole: 8 bytes in fp32, 4 in bf16
     const uintptr_t mask = dtype == 0 ? 7u : 3u;
     for (int i = 0; i < nptrs; ++i)

@@ -160,15 +160,19 @@ def bwd(L, ptrs=None, eps=1e-6, ws=None, ws_bytes=0, dt=0, B=2, C=3, H=5, W=7):
 
 
 def test_backward_workspace_query(L):
-    # even sides up to 96: transposed x, lambda, u, gy and two fp32 planes per
-    # pixel-channel, sized for fp32 storage
+    # even sides up to 160 (the pair kernel's bf16 limit): transposed x,
+    # lambda, u, gy and two fp32 planes per pixel-channel, sized for fp32
+    # storage
     n = 32 * 64 * 74 * 74
     assert L.gspn_prop2d_4dir_backward_workspace(32, 64, 74, 74) == 6 * 4 * n
     assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 2, 96) == 6 * 768    # 256-byte regions
+    assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 120, 120) == 6 * 4 * 2 * 3 * 120 * 120
+    assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 148, 148) == 6 * ((148 * 148 * 4 + 255) // 256 * 256)
     # otherwise 7 LDS lines plus three fp32 planes fit in 160 KiB up to about 115 x 115
     assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 115, 115) == 0
     assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 95, 96) == 0
-    assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 120, 120) == 2 * 3 * 3 * 120 * 120 * 4
+    assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 170, 170) == 2 * 3 * 3 * 170 * 170 * 4
+    assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 121, 121) == 2 * 3 * 3 * 121 * 121 * 4
     assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 5852, 2) == -1      # line too long
     assert L.gspn_prop2d_4dir_backward_workspace(0, 1, 4, 4) == -1
     assert L.gspn_prop2d_4dir_backward_workspace(1, 1 << 18, 64, 64) == -1
@@ -207,13 +211,13 @@ def test_backward_aliasing(L):
 
 
 def test_backward_workspace_checks(L):
-    need = 2 * 3 * 3 * 120 * 120 * 4
-    assert bwd(L, H=120, W=120) == NULL                      # workspace needed, none given
+    need = 2 * 3 * 3 * 170 * 170 * 4
+    assert bwd(L, H=170, W=170) == NULL                      # workspace needed, none given
     assert bwd(L, H=6, W=8) == NULL                          # the even-sided path needs one too
-    assert bwd(L, ws=P(10), ws_bytes=need - 4, H=120, W=120) == SHAPE
-    assert bwd(L, ws=ctypes.c_void_p(A + 10 * STEP + 2), ws_bytes=need, H=120, W=120) == ALIGN
-    assert bwd(L, ws=P(0), ws_bytes=need, H=120, W=120) == ALIAS        # over x
-    assert bwd(L, ws=P(7), ws_bytes=need, H=120, W=120) == ALIAS        # over gu
+    assert bwd(L, ws=P(10), ws_bytes=need - 4, H=170, W=170) == SHAPE
+    assert bwd(L, ws=ctypes.c_void_p(A + 10 * STEP + 2), ws_bytes=need, H=170, W=170) == ALIGN
+    assert bwd(L, ws=P(0), ws_bytes=need, H=170, W=170) == ALIAS        # over x
+    assert bwd(L, ws=P(7), ws_bytes=need, H=170, W=170) == ALIAS        # over gu
     assert bwd(L, ws_bytes=-1) == SHAPE
 
 

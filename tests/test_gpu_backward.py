@@ -65,13 +65,14 @@ def test_backward_small_workloads(name):
         _check(_run(p), _oracle(p), wl.dtype, "%s seed %d" % (name, seed))
 
 
-# Even sides up to 96 take the one-wavefront-per-direction-pair kernel (its
-# lines cover 1, 2 or 3 positions per lane; the two launches of a plane can
-# differ); the rest the general kernel, whose planes leave LDS at (148, 148)
-# and (120, 120).
+# Even sides take the one-wavefront-per-direction-pair kernel up to 160 in
+# bf16 and 128 in fp32 (its lines cover 1 to 5 positions per lane; the two
+# launches of a plane can differ); the rest the general kernel, whose planes
+# leave LDS at (148, 148) and (120, 120) (fp32: (148, 148) is general).
 BWD_SHAPES = [(1, 1), (1, 2), (2, 1), (3, 5), (5, 3), (1, 74), (74, 1), (63, 64), (74, 74),
               (127, 33), (13, 148), (120, 120), (148, 148), (300, 5), (5, 300),
-              (2, 2), (2, 96), (96, 2), (32, 34), (34, 32), (64, 66), (96, 96), (30, 66), (8, 74)]
+              (2, 2), (2, 96), (96, 2), (32, 34), (34, 32), (64, 66), (96, 96), (30, 66), (8, 74),
+              (98, 98), (128, 128), (130, 160), (160, 2), (2, 160), (158, 126), (96, 128), (162, 40)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -132,7 +133,7 @@ def test_backward_clamp_and_saturated_logits(H, W):
 def test_backward_caller_workspace_and_eps():
     """A caller-provided (oversized) workspace and a non-default eps."""
     say("backward workspace")
-    B, C, H, W = 1, 2, 160, 90
+    B, C, H, W = 1, 2, 170, 90
     p = _problem(B, C, H, W, 4, "fp32")
     need = gspn.prop2d_4dir_backward_workspace_bytes(B, C, H, W)
     assert need == B * C * 3 * H * W * 4

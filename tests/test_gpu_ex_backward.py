@@ -7,8 +7,9 @@ taps are the "w" stream drawn at the grouped shape, gy its own stream),
 rounded to the storage type; the oracle sees exactly the same values.  Each
 gradient is compared with oracle/tolerance.py's GRAD_RTOL rule; a grouped tap
 gradient is a sum over the channels of its group, which that rule's rms floor
-covers.  Shapes cover both kernels: even sides up to 96 take the
-one-wavefront-per-direction-pair kernel, the rest the general one.
+covers.  Shapes cover both kernels: even sides up to 160 (bf16) or 128
+(fp32) take the one-wavefront-per-direction-pair kernel, the rest the
+general one.
 """
 import sys
 
@@ -63,7 +64,7 @@ def _check(got, ref, dtype, what):
 
 
 SHAPES = [(1, 1), (3, 5), (2, 96), (16, 16), (27, 27), (32, 34), (74, 74), (96, 96), (97, 40),
-          (130, 20)]
+          (130, 20), (148, 148)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -133,7 +134,7 @@ def test_ex_backward_caller_workspace_and_eps():
     eps, on a plane the general kernel takes with its tap gradients reduced
     across the group."""
     say("ex backward workspace")
-    B, C, G, H, W = 1, 4, 2, 160, 90
+    B, C, G, H, W = 1, 4, 2, 170, 90
     p = _problem(B, C, H, W, G, 4, "fp32")
     need = gspn.prop2d_4dir_ex_backward_workspace_bytes(B, C, G, H, W)
     ws = torch.full((need // 4 + 1000,), float("nan"), device=DEV)
