@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libgspn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["gspn_host.cpp", "gspn_kernels.hip", "gspn_prop2d_pair.hip", "gspn_prop2d_phase.hip",
-           "gspn_backward.hip", "gspn_backward_pair.hip", "gspn_sublayer.hip", "gspn_conv1x1.hip"]
+           "gspn_backward.hip", "gspn_backward_pair.hip", "gspn_sublayer.hip", "gspn_conv1x1.hip",
+           "gspn_prop2d_wide.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

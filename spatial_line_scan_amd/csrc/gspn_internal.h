@@ -39,6 +39,14 @@ hipError_t launch_prop2d_pair(const void* x, const void* lam, const void* u, con
                               float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                               const PropOpts& opts, hipStream_t stream);
 
+// Large fp32 planes (sides up to 256, multiples of 4): one launch per
+// direction with y as the accumulator (gspn_prop2d_wide.hip).
+bool prop2d_wide_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
+                          const void* lam, const void* u, const void* w4, const void* y);
+hipError_t launch_prop2d_wide(const void* x, const void* lam, const void* u, const void* w4,
+                              float eps, void* y, int64_t planes, int64_t H, int64_t W,
+                              const PropOpts& opts, hipStream_t stream);
+
 // Fast path for bf16 planes: one wavefront per plane, rows then columns,
 // lambda x and the direction sum on chip (gspn_prop2d_phase.hip).
 bool prop2d_phase_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,

@@ -251,6 +251,8 @@ hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const vo
         return launch_prop2d_phase(x, lam, u, w4, eps, y, dtype, planes, H, W, o, stream);
     if (prop2d_pair_eligible(dtype, planes, H, W, x, lam, u, w4, y))
         return launch_prop2d_pair(x, lam, u, w4, eps, y, dtype, planes, H, W, o, stream);
+    if (prop2d_wide_eligible(dtype, planes, H, W, x, lam, u, w4, y))
+        return launch_prop2d_wide(x, lam, u, w4, eps, y, planes, H, W, o, stream);
     return dtype == 0 ? prop2d_t<float>(x, lam, u, w4, eps, y, planes, H, W, o, stream)
                       : prop2d_t<uint16_t>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }

@@ -1,0 +1,328 @@
+// Four-direction propagation of large fp32 planes (sides up to 256, a
+// multiple of 4), gfx950.
+//
+// Operator: "Scaling Parallel Sequence Models to Foundation-Scale Vision
+// Encoders", §3 line-scan recurrence, §4.1 all steps of a scan in one launch,
+// §5.1 fused normalisation (sigmoid, local sum, clamp, divide); reading
+// notes, method / overall framework.
+//
+// A plane's direction sum does not fit in LDS, so the fp32 output y is the
+// accumulator.  Four launches, one per direction, each one wavefront per
+// (b, c) plane; lane l holds positions K l .. K l + K - 1 of the current
+// line (K = ceil(L / 64)), and the neighbour exchange is one wave-wide DPP
+// shift each way:
+//   TD  y = h_TD            rows top-down
+//   BU  y = y + h_BU        rows bottom-up
+//   LR  y = y + h_LR        columns left-right
+//   RL  y = u (y + h_RL)    columns right-left
+// so the four terms of a pixel are summed in the fixed order TD, BU, LR, RL.
+// Every direction's taps are line-major, so a tap window is contiguous in
+// both kinds of pass, and taps are prefetched D lines ahead.
+//   Row passes read x, lambda (and y) as row windows, prefetched with the
+//   taps, and write y rows.
+//   Column passes walk the plane in strips of 16 columns.  A strip's
+//   b = lambda x and its slice of y are read with row-contiguous 16-byte
+//   loads and staged in LDS transposed ([column][row], 33 KB at 256 rows);
+//   the strip's columns are then scanned from LDS and the y slice written
+//   back (with the factor u in the last pass).  Reading x, lambda and y
+//   along columns straight from memory would fetch a cache line per element.
+// Chunked scans restart h at the first line of each segment of
+// ceil(NL / k_chunk) lines; the tap plane of plane p is p / cpg.
+#include "gspn_device.h"
+#include "gspn_internal.h"
+#include "gspn_lane.h"
+
+namespace gspn {
+namespace {
+
+using namespace lane;
+
+constexpr int kSW = 16;           // columns per strip
+constexpr int kMaxSideWide = 256;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+template <typename V> using lds_t = __attribute__((address_space(3))) V;
+
+// LDS row pitch of a strip (floats): a column of H rows plus a pad that
+// spreads the transposed writes of one row over the banks.
+__host__ __device__ inline int strip_pitch(int H) { return ((H + 3) & ~3) + 4; }
+
+// Orders this wavefront's LDS accesses before the fence against those after
+// it (one wavefront per workgroup: no barrier).
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
+}
+
+template <int K, int D, int Dir, bool Chunked>
+__global__ void __launch_bounds__(64)
+wide_pass_kernel(const float* __restrict__ x, const float* __restrict__ lam,
+                 const float* __restrict__ u, const float* __restrict__ w4, float eps,
+                 float* __restrict__ y, int planes, int H, int W, int cpg, int k_chunk) {
+    constexpr bool kRows = Dir < 2;
+    constexpr bool kFwd = Dir == 0 || Dir == 2;
+    static_assert(kSW % D == 0 && 4 % D == 0, "strip steps stay aligned to the prefetch ring");
+    extern __shared__ __attribute__((aligned(16))) float strip[];
+    const int HW = H * W;
+    const int NL = kRows ? H : W;
+    const int L = kRows ? W : H;
+    const int lane = threadIdx.x;
+    const int plane = blockIdx.x;
+    const size_t pix0 = static_cast<size_t>(plane) * HW;
+    // one buffer resource per plane (offsets within a plane; loads past its
+    // end return 0), so the tensors themselves may exceed 2 GiB
+    const int plane_bytes = HW * 4;
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(x + pix0), 0, plane_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lam + pix0), 0, plane_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(y + pix0, 0, plane_bytes, kBufFlags);
+    __amdgpu_buffer_rsrc_t taps[3];
+    const int tap_planes = planes / cpg;
+    const size_t tap0 = (static_cast<size_t>(Dir) * tap_planes + plane / cpg) * 3 * HW;
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w4 + tap0 + static_cast<size_t>(k) * HW), 0,
+                                                    plane_bytes, kBufFlags);
+
+    float c0[K], c1[K], c2[K];
+    bool valid[K];
+    const float inf = __builtin_inff();
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int p = K * lane + j;
+        valid[j] = p < L;
+        c0[j] = (valid[j] && p > 0) ? 1.0f : inf;
+        c1[j] = valid[j] ? 1.0f : inf;
+        c2[j] = (valid[j] && p < L - 1) ? 1.0f : inf;
+    }
+    const int seg = Chunked ? (NL + k_chunk - 1) / k_chunk : NL;
+    auto line_of = [&](int s) { return kFwd ? s : NL - 1 - s; };
+    auto restarts = [&](int i) {
+        return kFwd ? i % seg == 0 : (i == NL - 1 || (i + 1) % seg == 0);
+    };
+    const uint32_t win = static_cast<uint32_t>(K * lane) * 4;   // byte offset of the lane's window
+
+    // ---- prefetch ring: taps (and for rows x, lambda, y) of line line_of(s)
+    words_t<K> tbuf[D][3], xbuf[kRows ? D : 1], lbuf[kRows ? D : 1], ybuf[kRows ? D : 1];
+    auto load_line = [&](int s, int d) {
+        const int i = line_of(s < NL ? s : NL - 1);
+        const uint32_t lo = static_cast<uint32_t>(i * L) * 4 + win;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<K>(taps[k], lo);
+        if constexpr (kRows) {
+            const uint32_t xo = static_cast<uint32_t>(i * W) * 4 + win;
+            xbuf[d] = load_words<K>(xs, xo);
+            lbuf[d] = load_words<K>(ls, xo);
+            if constexpr (Dir == 1) ybuf[d] = load_words<K>(ys, xo);
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_line(d, d);
+
+    float h[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) h[j] = 0.0f;
+
+    // one step of the scan: line line_of(s), prefetch slot d; b[] is lambda x
+    // of the lane's positions, out[] receives the new states
+    auto advance = [&](int s, int d, const float (&b)[K], float (&hn)[K]) {
+        float s0[K], s1[K], s2[K], r[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            s0[j] = __builtin_amdgcn_exp2f(__uint_as_float(word<K>(tbuf[d][0], j)) * kNegLog2e);
+            s1[j] = __builtin_amdgcn_exp2f(__uint_as_float(word<K>(tbuf[d][1], j)) * kNegLog2e);
+            s2[j] = __builtin_amdgcn_exp2f(__uint_as_float(word<K>(tbuf[d][2], j)) * kNegLog2e);
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            s0[j] = __builtin_amdgcn_rcpf(s0[j] + c0[j]);
+            s1[j] = __builtin_amdgcn_rcpf(s1[j] + c1[j]);
+            s2[j] = __builtin_amdgcn_rcpf(s2[j] + c2[j]);
+            r[j] = __builtin_amdgcn_rcpf(fmaxf((s0[j] + s1[j]) + s2[j], eps));
+        }
+        const bool restart = restarts(line_of(s));
+#pragma unroll
+        for (int j = 0; j < K; ++j) h[j] = restart ? 0.0f : h[j];
+        const float hl0 = from_prev(h[K - 1]);
+        const float hrK = from_next(h[0]);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const float hl = j > 0 ? h[j - 1] : hl0;
+            const float hr = j < K - 1 ? h[j + 1] : hrK;
+            float m = s1[j] * h[j];
+            m = fmaf(s0[j], hl, m);
+            m = fmaf(s2[j], hr, m);
+            hn[j] = fmaf(m, r[j], b[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) h[j] = hn[j];
+    };
+
+    if constexpr (kRows) {
+        for (int s0 = 0; s0 < NL; s0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int s = s0 + d;
+                if (s < NL) {
+                    float b[K], hn[K];
+#pragma unroll
+                    for (int j = 0; j < K; ++j)
+                        b[j] = __uint_as_float(word<K>(lbuf[d], j)) * __uint_as_float(word<K>(xbuf[d], j));
+                    float yv[K];
+                    if constexpr (Dir == 1) {
+#pragma unroll
+                        for (int j = 0; j < K; ++j) yv[j] = __uint_as_float(word<K>(ybuf[d], j));
+                    }
+                    advance(s, d, b, hn);
+                    const int i = line_of(s);
+                    float* yr = y + pix0 + static_cast<size_t>(i) * W + K * lane;
+                    load_line(s + D, d);
+#pragma unroll
+                    for (int j = 0; j < K; ++j)
+                        if (valid[j]) yr[j] = Dir == 0 ? hn[j] : yv[j] + hn[j];
+                }
+            }
+        }
+    } else {
+        // strips of kSW columns: LR takes them left to right, RL right to left
+        const int pitch = strip_pitch(H);
+        float* bs = strip;                          // b = lambda x, [column][row]
+        float* yst = strip + kSW * pitch;           // y slice, [column][row]
+        const int T = (W + kSW - 1) / kSW;
+        const int units = H * (kSW / 4);            // (row, 4-column chunk) pairs of a strip
+        int s = 0;                                  // scan step
+        for (int tt = 0; tt < T; ++tt) {
+            const int t = kFwd ? tt : T - 1 - tt;
+            const int cb = t * kSW;                 // first column of the strip
+            const int width = W - cb < kSW ? W - cb : kSW;   // a multiple of 4
+            // load the strip: unit f = row f / 4, columns cb + 4 (f % 4) ..
+            for (int f0 = 0; f0 < units; f0 += 64 * 4) {
+                f32x4_t xv[4], lv[4], yv[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int f = f0 + 64 * a + lane;
+                    const int row = f >> 2, cq = 4 * (f & 3);
+                    xv[a] = lv[a] = yv[a] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    if (f < units && cq < width) {
+                        const uint32_t o = static_cast<uint32_t>(row * W + cb + cq) * 4;
+                        xv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0));
+                        lv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ls, o, 0, 0));
+                        yv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ys, o, 0, 0));
+                    }
+                }
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int f = f0 + 64 * a + lane;
+                    const int row = f >> 2, cq = 4 * (f & 3);
+                    if (f < units) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            bs[(cq + e) * pitch + row] = lv[a][e] * xv[a][e];
+                            yst[(cq + e) * pitch + row] = yv[a][e];
+                        }
+                    }
+                }
+            }
+            lds_sync();
+            // scan the strip's columns
+            for (int q0 = 0; q0 < kSW; q0 += D) {
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    const int q = q0 + d;                    // step within the strip
+                    if (q < width) {
+                        const int cl = kFwd ? q : width - 1 - q;   // column within the strip
+                        // strips start at multiples of D steps (widths are
+                        // multiples of 4), so this step's ring slot is d
+                        // positions past H (their taps are dropped) take b = 0
+                        // and touch no LDS: they would reach the next column
+                        float b[K], hn[K];
+#pragma unroll
+                        for (int j = 0; j < K; ++j) b[j] = valid[j] ? bs[cl * pitch + K * lane + j] : 0.0f;
+                        advance(s, d, b, hn);
+                        load_line(s + D, d);
+#pragma unroll
+                        for (int j = 0; j < K; ++j)
+                            if (valid[j]) yst[cl * pitch + K * lane + j] += hn[j];
+                        ++s;
+                    }
+                }
+            }
+            lds_sync();
+            // write the y slice back (the last pass applies u)
+            for (int f = lane; f < units; f += 64) {
+                const int row = f >> 2, cq = 4 * (f & 3);
+                if (cq < width) {
+                    const size_t e = pix0 + static_cast<size_t>(row) * W + cb + cq;
+                    f32x4_t v;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) v[k] = yst[(cq + k) * pitch + row];
+                    if constexpr (Dir == 3) {
+                        const f32x4_t uv = *reinterpret_cast<const f32x4_t*>(u + e);
+                        v = v * uv;
+                    }
+                    *reinterpret_cast<f32x4_t*>(y + e) = v;
+                }
+            }
+            lds_sync();
+        }
+    }
+}
+
+template <int K, int Dir>
+hipError_t launch_dir(const float* x, const float* lam, const float* u, const float* w4, float eps,
+                      float* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                      hipStream_t stream) {
+    constexpr int D = 4;
+    const size_t lds = Dir < 2 ? 0 : 2 * kSW * static_cast<size_t>(strip_pitch(static_cast<int>(H))) * 4;
+    auto run = [&](auto kern) -> hipError_t {
+        if (lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+            if (e != hipSuccess) return e;
+        }
+        kern<<<dim3(static_cast<unsigned>(planes)), dim3(64), lds, stream>>>(
+            x, lam, u, w4, eps, y, static_cast<int>(planes), static_cast<int>(H),
+            static_cast<int>(W), static_cast<int>(o.cpg), static_cast<int>(o.k_chunk));
+        return hipGetLastError();
+    };
+    return o.k_chunk > 1 ? run(wide_pass_kernel<K, D, Dir, true>) : run(wide_pass_kernel<K, D, Dir, false>);
+}
+
+template <int Dir>
+hipError_t launch_dir_k(const float* x, const float* lam, const float* u, const float* w4, float eps,
+                        float* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                        hipStream_t stream) {
+    const int64_t L = Dir < 2 ? W : H;
+    if (L <= 64) return launch_dir<1, Dir>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (L <= 128) return launch_dir<2, Dir>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (L <= 192) return launch_dir<3, Dir>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    return launch_dir<4, Dir>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+bool prop2d_wide_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
+                          const void* lam, const void* u, const void* w4, const void* y) {
+    if (dtype != 0) return false;                                   // fp32: y is the accumulator
+    if (H > kMaxSideWide || W > kMaxSideWide || (H & 3) || (W & 3)) return false;
+    if (planes > 0x7fffffff) return false;                          // one workgroup a plane
+    return aligned16(x) && aligned16(lam) && aligned16(u) && aligned16(w4) && aligned16(y);
+}
+
+hipError_t launch_prop2d_wide(const void* x_, const void* lam_, const void* u_, const void* w4_,
+                              float eps, void* y_, int64_t planes, int64_t H, int64_t W,
+                              const PropOpts& o, hipStream_t stream) {
+    const float* x = static_cast<const float*>(x_);
+    const float* lam = static_cast<const float*>(lam_);
+    const float* u = static_cast<const float*>(u_);
+    const float* w4 = static_cast<const float*>(w4_);
+    float* y = static_cast<float*>(y_);
+    hipError_t e;
+    if ((e = launch_dir_k<0>(x, lam, u, w4, eps, y, planes, H, W, o, stream)) != hipSuccess) return e;
+    if ((e = launch_dir_k<1>(x, lam, u, w4, eps, y, planes, H, W, o, stream)) != hipSuccess) return e;
+    if ((e = launch_dir_k<2>(x, lam, u, w4, eps, y, planes, H, W, o, stream)) != hipSuccess) return e;
+    return launch_dir_k<3>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+}
+
+}  // namespace gspn

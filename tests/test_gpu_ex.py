@@ -48,7 +48,8 @@ def _run_check(p, G, k, dtype, what):
     return y
 
 
-SHAPES = [(1, 1), (3, 5), (16, 16), (27, 27), (33, 70), (74, 74), (96, 96), (97, 40), (130, 20)]
+SHAPES = [(1, 1), (3, 5), (16, 16), (27, 27), (33, 70), (74, 74), (96, 96), (97, 40), (130, 20),
+          (148, 100), (200, 36)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])

@@ -48,11 +48,18 @@ def test_prop2d_small_workloads_all_seeds(name):
 
 
 # bf16 planes with even sides up to 160 take the one-wavefront phase kernel
-# (K = 1..5 positions a lane: sides up to 32, 64, 96, 128, 160), fp32 ones up
-# to 96 the two-wavefront kernel, the rest the general kernel.
+# (K = 1..5 positions a lane: sides up to 32, 64, 96, 128, 160); fp32 ones up
+# to 96 the two-wavefront kernel, and fp32 ones with sides up to 256 that are
+# multiples of 4 the one-launch-per-direction kernel (y accumulates; K = 1..4
+# positions a lane over 64 lanes; columns in strips of 16); the rest the
+# general kernel.
 EDGE_SHAPES = [(1, 1), (1, 2), (2, 1), (2, 2), (3, 5), (5, 3), (1, 74), (74, 1), (63, 64), (64, 65),
                (65, 63), (74, 74), (127, 33), (13, 148), (148, 148), (256, 7),
                (98, 98), (128, 128), (130, 160), (160, 2), (2, 160), (158, 126), (96, 128), (162, 40)]
+# fp32 only: the one-launch-per-direction kernel (bf16 planes this large are
+# rejected: no bf16 kernel holds their direction sum)
+WIDE_SHAPES = [(100, 100), (4, 256), (256, 4), (200, 100), (100, 196), (148, 152), (256, 256),
+               (252, 68), (120, 120)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -73,6 +80,16 @@ def _sampled_planes(B, C, k=6):
     while len(planes) < min(k, B * C):
         planes.add((int(rng.integers(B)), int(rng.integers(C))))
     return sorted(planes)
+
+
+@pytest.mark.parametrize("H,W", WIDE_SHAPES)
+def test_prop2d_wide_fp32_shapes(H, W):
+    say("prop2d wide", H, W)
+    p = _problem(2, 3, H, W, 31 + H + 7 * W, "fp32")
+    y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
+    torch.cuda.synchronize()
+    assert_close(_np(y), oracle.prop2d(p["x"], p["lam"], p["u"], p["w"]), RTOL["fp32"],
+                 "%dx%d fp32" % (H, W))
 
 
 @pytest.mark.parametrize("name", ["latent1k", "latent2k", "wide256"])
