@@ -20,12 +20,15 @@
 // both kinds of pass, and taps are prefetched D lines ahead.
 //   Row passes read x, lambda (and y) as row windows, prefetched with the
 //   taps, and write y rows.
-//   Column passes walk the plane in strips of 16 columns.  A strip's
-//   b = lambda x and its slice of y are read with row-contiguous 16-byte
+//   Column passes walk the plane in strips of 32 columns, so that each row
+//   of a strip is one whole 128-byte line of x, lambda, y and u (narrower
+//   strips fetch every line twice: its other half is evicted before the
+//   next strip).  A strip's b = lambda x is read with row-contiguous 16-byte
 //   loads and staged in LDS transposed ([column][row], 33 KB at 256 rows);
-//   the strip's columns are then scanned from LDS and the y slice written
-//   back (with the factor u in the last pass).  Reading x, lambda and y
-//   along columns straight from memory would fetch a cache line per element.
+//   the strip's columns are then scanned from LDS, each column's h taking
+//   the place of its b, and the strip's y is read, added to (and in the last
+//   pass multiplied by u) and written back in rows.  Reading along columns
+//   straight from memory would fetch a cache line per element.
 // Chunked scans restart h at the first line of each segment of
 // ceil(NL / k_chunk) lines; the tap plane of plane p is p / cpg.
 #include "gspn_device.h"
@@ -37,16 +40,19 @@ namespace {
 
 using namespace lane;
 
-constexpr int kSW = 16;           // columns per strip
+constexpr int kSW = 32;           // columns per strip: 128-byte rows of x, lambda, y, u
+constexpr int kCQ = kSW / 4;      // 16-byte chunks per strip row
+constexpr int kBatch = 16;        // strip chunks a lane loads per batch
 constexpr int kMaxSideWide = 256;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <typename V> using lds_t = __attribute__((address_space(3))) V;
 
-// LDS row pitch of a strip (floats): a column of H rows plus a pad that
-// spreads the transposed writes of one row over the banks.
-__host__ __device__ inline int strip_pitch(int H) { return ((H + 3) & ~3) + 4; }
+// LDS row pitch of a strip (floats): a column of H rows plus a pad, with
+// pitch = 2 mod 16 so that the transposed accesses of one batch (8 rows x 8
+// chunks of 4 columns) fall on distinct banks.
+__host__ __device__ inline int strip_pitch(int H) { return ((H + 13) & ~15) + 2; }
 
 // Orders this wavefront's LDS accesses before the fence against those after
 // it (one wavefront per workgroup: no barrier).
@@ -185,45 +191,42 @@ wide_pass_kernel(const float* __restrict__ x, const float* __restrict__ lam,
     } else {
         // strips of kSW columns: LR takes them left to right, RL right to left
         const int pitch = strip_pitch(H);
-        float* bs = strip;                          // b = lambda x, [column][row]
-        float* yst = strip + kSW * pitch;           // y slice, [column][row]
+        float* bs = strip;                          // [column][row]: b = lambda x, then h
         const int T = (W + kSW - 1) / kSW;
-        const int units = H * (kSW / 4);            // (row, 4-column chunk) pairs of a strip
+        const int units = H * kCQ;                  // (row, 4-column chunk) pairs of a strip
+        const __amdgpu_buffer_rsrc_t us =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(u + pix0), 0, plane_bytes, kBufFlags);
         int s = 0;                                  // scan step
         for (int tt = 0; tt < T; ++tt) {
             const int t = kFwd ? tt : T - 1 - tt;
             const int cb = t * kSW;                 // first column of the strip
             const int width = W - cb < kSW ? W - cb : kSW;   // a multiple of 4
-            // load the strip: unit f = row f / 4, columns cb + 4 (f % 4) ..
-            for (int f0 = 0; f0 < units; f0 += 64 * 4) {
-                f32x4_t xv[4], lv[4], yv[4];
+            // b of the strip: unit f = row f / kCQ, columns cb + 4 (f % kCQ) ..
+            for (int f0 = 0; f0 < units; f0 += 64 * kBatch) {
+                f32x4_t xv[kBatch], lv[kBatch];
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
+                for (int a = 0; a < kBatch; ++a) {
                     const int f = f0 + 64 * a + lane;
-                    const int row = f >> 2, cq = 4 * (f & 3);
-                    xv[a] = lv[a] = yv[a] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    const int row = f / kCQ, cq = 4 * (f % kCQ);
+                    xv[a] = lv[a] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
                     if (f < units && cq < width) {
                         const uint32_t o = static_cast<uint32_t>(row * W + cb + cq) * 4;
                         xv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0));
                         lv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ls, o, 0, 0));
-                        yv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ys, o, 0, 0));
                     }
                 }
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
+                for (int a = 0; a < kBatch; ++a) {
                     const int f = f0 + 64 * a + lane;
-                    const int row = f >> 2, cq = 4 * (f & 3);
+                    const int row = f / kCQ, cq = 4 * (f % kCQ);
                     if (f < units) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            bs[(cq + e) * pitch + row] = lv[a][e] * xv[a][e];
-                            yst[(cq + e) * pitch + row] = yv[a][e];
-                        }
+                        for (int e = 0; e < 4; ++e) bs[(cq + e) * pitch + row] = lv[a][e] * xv[a][e];
                     }
                 }
             }
             lds_sync();
-            // scan the strip's columns
+            // scan the strip's columns; each column's h replaces its b
             for (int q0 = 0; q0 < kSW; q0 += D) {
 #pragma unroll
                 for (int d = 0; d < D; ++d) {
@@ -231,7 +234,7 @@ wide_pass_kernel(const float* __restrict__ x, const float* __restrict__ lam,
                     if (q < width) {
                         const int cl = kFwd ? q : width - 1 - q;   // column within the strip
                         // strips start at multiples of D steps (widths are
-                        // multiples of 4), so this step's ring slot is d
+                        // multiples of 4), so this step's ring slot is d;
                         // positions past H (their taps are dropped) take b = 0
                         // and touch no LDS: they would reach the next column
                         float b[K], hn[K];
@@ -241,25 +244,37 @@ wide_pass_kernel(const float* __restrict__ x, const float* __restrict__ lam,
                         load_line(s + D, d);
 #pragma unroll
                         for (int j = 0; j < K; ++j)
-                            if (valid[j]) yst[cl * pitch + K * lane + j] += hn[j];
+                            if (valid[j]) bs[cl * pitch + K * lane + j] = hn[j];
                         ++s;
                     }
                 }
             }
             lds_sync();
-            // write the y slice back (the last pass applies u)
-            for (int f = lane; f < units; f += 64) {
-                const int row = f >> 2, cq = 4 * (f & 3);
-                if (cq < width) {
-                    const size_t e = pix0 + static_cast<size_t>(row) * W + cb + cq;
-                    f32x4_t v;
+            // y of the strip = y + h (times u in the last pass), written back in rows
+            for (int f0 = 0; f0 < units; f0 += 64 * kBatch) {
+                f32x4_t yv[kBatch], uv[kBatch];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) v[k] = yst[(cq + k) * pitch + row];
-                    if constexpr (Dir == 3) {
-                        const f32x4_t uv = *reinterpret_cast<const f32x4_t*>(u + e);
-                        v = v * uv;
+                for (int a = 0; a < kBatch; ++a) {
+                    const int f = f0 + 64 * a + lane;
+                    const int row = f / kCQ, cq = 4 * (f % kCQ);
+                    if (f < units && cq < width) {
+                        const uint32_t o = static_cast<uint32_t>(row * W + cb + cq) * 4;
+                        yv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ys, o, 0, 0));
+                        if constexpr (Dir == 3)
+                            uv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(us, o, 0, 0));
                     }
-                    *reinterpret_cast<f32x4_t*>(y + e) = v;
+                }
+#pragma unroll
+                for (int a = 0; a < kBatch; ++a) {
+                    const int f = f0 + 64 * a + lane;
+                    const int row = f / kCQ, cq = 4 * (f % kCQ);
+                    if (f < units && cq < width) {
+                        f32x4_t v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = yv[a][e] + bs[(cq + e) * pitch + row];
+                        if constexpr (Dir == 3) v = v * uv[a];
+                        *reinterpret_cast<f32x4_t*>(y + pix0 + static_cast<size_t>(row) * W + cb + cq) = v;
+                    }
                 }
             }
             lds_sync();
@@ -272,7 +287,7 @@ hipError_t launch_dir(const float* x, const float* lam, const float* u, const fl
                       float* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                       hipStream_t stream) {
     constexpr int D = 4;
-    const size_t lds = Dir < 2 ? 0 : 2 * kSW * static_cast<size_t>(strip_pitch(static_cast<int>(H))) * 4;
+    const size_t lds = Dir < 2 ? 0 : kSW * static_cast<size_t>(strip_pitch(static_cast<int>(H))) * 4;
     auto run = [&](auto kern) -> hipError_t {
         if (lds > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
