@@ -7,10 +7,11 @@
 // notes, method / overall framework.
 //
 // A plane's direction sum does not fit in LDS, so the fp32 output y is the
-// accumulator.  Four launches, one per direction, each one wavefront per
-// (b, c) plane; lane l holds positions K l .. K l + K - 1 of the current
-// line (K = ceil(L / 64)), and the neighbour exchange is one wave-wide DPP
-// shift each way:
+// accumulator.  One launch, one wavefront per (b, c) plane, which runs four
+// passes over its plane in turn (ordered by workgroup-scope fences: a pass
+// reads y that other lanes wrote in the previous one); lane l holds
+// positions K l .. K l + K - 1 of the current line (K = ceil(L / 64)), and
+// the neighbour exchange is one wave-wide DPP shift each way:
 //   TD  y = h_TD            rows top-down
 //   BU  y = y + h_BU        rows bottom-up
 //   LR  y = y + h_LR        columns left-right
@@ -60,15 +61,22 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
 }
 
+// Orders this wavefront's global stores of one pass before the next pass's
+// loads, which other lanes of the wavefront issue.
+__device__ __forceinline__ void pass_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// One direction's pass over plane blockIdx.x; strip is the column passes' LDS.
 template <int K, int D, int Dir, bool Chunked>
-__global__ void __launch_bounds__(64)
-wide_pass_kernel(const float* __restrict__ x, const float* __restrict__ lam,
-                 const float* __restrict__ u, const float* __restrict__ w4, float eps,
-                 float* __restrict__ y, int planes, int H, int W, int cpg, int k_chunk) {
+__device__ __forceinline__ void wide_pass(const float* __restrict__ x, const float* __restrict__ lam,
+                                          const float* __restrict__ u, const float* __restrict__ w4,
+                                          float eps, float* __restrict__ y, int planes, int H, int W,
+                                          int cpg, int k_chunk, float* strip) {
     constexpr bool kRows = Dir < 2;
     constexpr bool kFwd = Dir == 0 || Dir == 2;
     static_assert(kSW % D == 0 && 4 % D == 0, "strip steps stay aligned to the prefetch ring");
-    extern __shared__ __attribute__((aligned(16))) float strip[];
     const int HW = H * W;
     const int NL = kRows ? H : W;
     const int L = kRows ? W : H;
@@ -282,12 +290,29 @@ wide_pass_kernel(const float* __restrict__ x, const float* __restrict__ lam,
     }
 }
 
-template <int K, int Dir>
-hipError_t launch_dir(const float* x, const float* lam, const float* u, const float* w4, float eps,
-                      float* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
-                      hipStream_t stream) {
+// The four passes of one plane, in the summation order TD, BU, LR, RL; KR
+// and KC are the positions a lane holds on a row and on a column.
+template <int KR, int KC, bool Chunked>
+__global__ void __launch_bounds__(64)
+prop2d_wide_kernel(const float* __restrict__ x, const float* __restrict__ lam,
+                   const float* __restrict__ u, const float* __restrict__ w4, float eps,
+                   float* __restrict__ y, int planes, int H, int W, int cpg, int k_chunk) {
+    extern __shared__ __attribute__((aligned(16))) float strip[];
     constexpr int D = 4;
-    const size_t lds = Dir < 2 ? 0 : kSW * static_cast<size_t>(strip_pitch(static_cast<int>(H))) * 4;
+    wide_pass<KR, D, 0, Chunked>(x, lam, u, w4, eps, y, planes, H, W, cpg, k_chunk, strip);
+    pass_sync();
+    wide_pass<KR, D, 1, Chunked>(x, lam, u, w4, eps, y, planes, H, W, cpg, k_chunk, strip);
+    pass_sync();
+    wide_pass<KC, D, 2, Chunked>(x, lam, u, w4, eps, y, planes, H, W, cpg, k_chunk, strip);
+    pass_sync();
+    wide_pass<KC, D, 3, Chunked>(x, lam, u, w4, eps, y, planes, H, W, cpg, k_chunk, strip);
+}
+
+template <int KR, int KC>
+hipError_t launch_k(const float* x, const float* lam, const float* u, const float* w4, float eps,
+                    float* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                    hipStream_t stream) {
+    const size_t lds = kSW * static_cast<size_t>(strip_pitch(static_cast<int>(H))) * 4;
     auto run = [&](auto kern) -> hipError_t {
         if (lds > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -299,18 +324,18 @@ hipError_t launch_dir(const float* x, const float* lam, const float* u, const fl
             static_cast<int>(W), static_cast<int>(o.cpg), static_cast<int>(o.k_chunk));
         return hipGetLastError();
     };
-    return o.k_chunk > 1 ? run(wide_pass_kernel<K, D, Dir, true>) : run(wide_pass_kernel<K, D, Dir, false>);
+    return o.k_chunk > 1 ? run(prop2d_wide_kernel<KR, KC, true>) : run(prop2d_wide_kernel<KR, KC, false>);
 }
 
-template <int Dir>
-hipError_t launch_dir_k(const float* x, const float* lam, const float* u, const float* w4, float eps,
-                        float* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
-                        hipStream_t stream) {
-    const int64_t L = Dir < 2 ? W : H;
-    if (L <= 64) return launch_dir<1, Dir>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    if (L <= 128) return launch_dir<2, Dir>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    if (L <= 192) return launch_dir<3, Dir>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    return launch_dir<4, Dir>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+// K = ceil(L / 64) positions a lane, L up to 256
+template <int KR>
+hipError_t launch_kc(const float* x, const float* lam, const float* u, const float* w4, float eps,
+                     float* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                     hipStream_t stream) {
+    if (H <= 64) return launch_k<KR, 1>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (H <= 128) return launch_k<KR, 2>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (H <= 192) return launch_k<KR, 3>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    return launch_k<KR, 4>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -333,11 +358,10 @@ hipError_t launch_prop2d_wide(const void* x_, const void* lam_, const void* u_, 
     const float* u = static_cast<const float*>(u_);
     const float* w4 = static_cast<const float*>(w4_);
     float* y = static_cast<float*>(y_);
-    hipError_t e;
-    if ((e = launch_dir_k<0>(x, lam, u, w4, eps, y, planes, H, W, o, stream)) != hipSuccess) return e;
-    if ((e = launch_dir_k<1>(x, lam, u, w4, eps, y, planes, H, W, o, stream)) != hipSuccess) return e;
-    if ((e = launch_dir_k<2>(x, lam, u, w4, eps, y, planes, H, W, o, stream)) != hipSuccess) return e;
-    return launch_dir_k<3>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (W <= 64) return launch_kc<1>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (W <= 128) return launch_kc<2>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (W <= 192) return launch_kc<3>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    return launch_kc<4>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 }  // namespace gspn
