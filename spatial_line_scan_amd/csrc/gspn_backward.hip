@@ -285,9 +285,17 @@ hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u,
     void* rest = ws ? static_cast<char*>(ws) + group_grad_bytes(planes, H, W, o.cpg) : nullptr;
     const void* ptrs[] = {x, lam, u, w4, gy, gx, glam, gu, gw4};
     hipError_t e;
+    // bytes the workspace query reserved after the tap gradients
+    const int64_t general = plane_kernel_workspace_bytes(planes, H, W);
+    const int64_t pair = prop2d_backward_pair_shape(planes, H, W)
+                             ? prop2d_backward_pair_workspace_bytes(planes, H, W) : 0;
+    const int64_t avail = ws ? (general > pair ? general : pair) : 0;
     if (prop2d_backward_pair_eligible(dtype, planes, H, W, ptrs, 9, rest)) {
         e = launch_prop2d_backward_pair(x, lam, u, w4, gy, eps, gx, glam, gu, gdst, grouped, rest,
                                         dtype, planes, H, W, o, stream);
+    } else if (prop2d_backward_wide_eligible(dtype, planes, H, W, ptrs, 9, rest, avail)) {
+        e = launch_prop2d_backward_wide(x, lam, u, w4, gy, eps, gx, glam, gu, gdst, rest, planes, H, W, o,
+                                        stream);
     } else {
         // this kernel takes a workspace only when its planes leave LDS
         void* pws = plane_kernel_workspace_bytes(planes, H, W) == 0 ? nullptr : rest;

@@ -82,6 +82,19 @@ hipError_t launch_prop2d_backward_pair(const void* x, const void* lam, const voi
 // Longest line the backward's LDS lines allow.
 int64_t prop2d_backward_max_line();
 
+// Gradient for large fp32 planes (sides up to 256, multiples of 4): one
+// wavefront per plane, h kept in ws (prop2d_backward_wide_workspace_bytes,
+// 16-byte aligned; ws_bytes is what is available there), gx and gu used as
+// the accumulators (gspn_backward_wide.hip).  gwd as for the pair kernel.
+int64_t prop2d_backward_wide_workspace_bytes(int64_t planes, int64_t H, int64_t W);
+bool prop2d_backward_wide_eligible(int dtype, int64_t planes, int64_t H, int64_t W,
+                                   const void* const* ptrs, int nptrs, const void* ws,
+                                   int64_t ws_bytes);
+hipError_t launch_prop2d_backward_wide(const void* x, const void* lam, const void* u, const void* w4,
+                                       const void* gy, float eps, void* gx, void* glam, void* gu,
+                                       void* gwd, void* ws, int64_t planes, int64_t H, int64_t W,
+                                       const PropOpts& opts, hipStream_t stream);
+
 // Latent propagation sublayer (gspn_sublayer.hip): hipBLASLt 1x1 projections
 // around launch_prop2d.  ws holds latent_sublayer_workspace_bytes bytes.
 hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const void* w_param,

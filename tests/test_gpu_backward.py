@@ -67,8 +67,9 @@ def test_backward_small_workloads(name):
 
 # Even sides take the one-wavefront-per-direction-pair kernel up to 160 in
 # bf16 and 128 in fp32 (its lines cover 1 to 5 positions per lane; the two
-# launches of a plane can differ); the rest the general kernel, whose planes
-# leave LDS at (148, 148) and (120, 120) (fp32: (148, 148) is general).
+# launches of a plane can differ); fp32 planes whose sums leave LDS (above
+# about 13K pixels) with sides up to 256, multiples of 4, the wide kernel
+# ((120, 120) and (148, 148) in fp32); the rest the general kernel.
 BWD_SHAPES = [(1, 1), (1, 2), (2, 1), (3, 5), (5, 3), (1, 74), (74, 1), (63, 64), (74, 74),
               (127, 33), (13, 148), (120, 120), (148, 148), (300, 5), (5, 300),
               (2, 2), (2, 96), (96, 2), (32, 34), (34, 32), (64, 66), (96, 96), (30, 66), (8, 74),
@@ -81,6 +82,39 @@ def test_backward_edge_shapes(H, W, dtype):
     say("backward edge", H, W, dtype)
     p = _problem(2, 3, H, W, 21 + H + 5 * W, dtype)
     _check(_run(p), _oracle(p), dtype, "%dx%d %s" % (H, W, dtype))
+
+
+# fp32 only: the one-wavefront-per-plane kernel for planes whose sums leave
+# LDS (K = 2, 3, 4 positions a lane; strips of 32 columns with a partial last
+# one; row and column lines of different lengths)
+WIDE_BWD_SHAPES = [(116, 116), (120, 124), (148, 152), (200, 100), (100, 200), (252, 68),
+                   (68, 252), (124, 256), (256, 256)]
+
+
+@pytest.mark.parametrize("H,W", WIDE_BWD_SHAPES)
+def test_backward_wide_fp32_shapes(H, W):
+    say("backward wide", H, W)
+    p = _problem(1, 2, H, W, 61 + H + 3 * W, "fp32")
+    _check(_run(p), _oracle(p), "fp32", "%dx%d fp32" % (H, W))
+
+
+def test_backward_wide256_sampled_planes():
+    """Full wide256 launch (fp32, 1024 planes of 256 x 256); the oracle
+    recomputes a sample of whole planes."""
+    wl = WORKLOADS["wide256"]
+    say("backward wide256")
+    p = _problem(wl.B, wl.C, wl.H, wl.W, 0, wl.dtype)
+    got = _run(p)
+    for t in got:
+        assert bool(torch.isfinite(t).all())
+    w = p["w"].view(4, wl.B, wl.C, 3, -1)
+    gw = got[3].view(4, wl.B, wl.C, 3, -1)
+    for c in (0, 517, wl.C - 1):
+        sl = lambda t: t[0:1, c:c + 1]
+        ref = oracle.prop2d_backward(sl(p["x"]), sl(p["lam"]), sl(p["u"]), w[:, 0:1, c:c + 1],
+                                     sl(p["gy"]))
+        mine = (sl(got[0]), sl(got[1]), sl(got[2]), gw[:, 0:1, c:c + 1])
+        _check(mine, ref, wl.dtype, "wide256 plane %d" % c)
 
 
 def test_backward_latent1k_sampled_planes():

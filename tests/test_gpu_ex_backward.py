@@ -7,9 +7,10 @@ taps are the "w" stream drawn at the grouped shape, gy its own stream),
 rounded to the storage type; the oracle sees exactly the same values.  Each
 gradient is compared with oracle/tolerance.py's GRAD_RTOL rule; a grouped tap
 gradient is a sum over the channels of its group, which that rule's rms floor
-covers.  Shapes cover both kernels: even sides up to 160 (bf16) or 128
-(fp32) take the one-wavefront-per-direction-pair kernel, the rest the
-general one.
+covers.  Shapes cover the three kernels: even sides up to 160 (bf16) or 128
+(fp32) take the one-wavefront-per-direction-pair kernel, fp32 planes above
+about 13K pixels with sides multiples of 4 up to 256 the one-wavefront-per-
+plane kernel, the rest the general one.
 """
 import sys
 
@@ -64,7 +65,7 @@ def _check(got, ref, dtype, what):
 
 
 SHAPES = [(1, 1), (3, 5), (2, 96), (16, 16), (27, 27), (32, 34), (74, 74), (96, 96), (97, 40),
-          (130, 20), (148, 148)]
+          (130, 20), (148, 148), (200, 100)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
