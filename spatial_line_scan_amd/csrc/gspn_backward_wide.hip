@@ -17,9 +17,10 @@
 // order TD, BU, LR, RL, a forward pass recomputes h and keeps every line of it
 // in a workspace plane (line-major), then the adjoint pass runs in reverse
 // scan order, reading h of the line before.  sum_d h and sum_d g accumulate in
-// gu and gx themselves, in that direction order, and a last pass turns them
-// into the three gradients.  Passes are ordered by workgroup-scope fences: a
-// pass reads what other lanes of the wavefront wrote in an earlier one.
+// gu and gx themselves, in that direction order, and the last direction's
+// passes turn them into the three gradients as they complete them.  Passes
+// are ordered by workgroup-scope fences: a pass reads what other lanes of the
+// wavefront wrote in an earlier one.
 // As in the wide forward kernel, lane l holds positions K l .. K l + K - 1 of
 // a line (neighbours through one DPP shift each way), row passes stream row
 // windows, and column passes walk strips of 32 columns (whole 128-byte lines)
@@ -96,7 +97,7 @@ __device__ __forceinline__ float wf(const words_t<K>& w, int j) {
 
 // What every pass of a plane needs.
 struct Ctx {
-    __amdgpu_buffer_rsrc_t xs, ls, us, gys, hs, gxs, gus;   // plane-sized, pixel order (hs: line-major h)
+    __amdgpu_buffer_rsrc_t xs, ls, us, gys, hs, gxs, gus, gls;   // plane-sized, pixel order (hs: line-major h)
     const float* w4;
     float* gwd;
     int planes, tap_planes, cpg, k_chunk, plane, H, W;
@@ -361,8 +362,11 @@ __device__ __forceinline__ void bwd_pass(const Ctx& c, float* strip) {
                 }
             }
             lds_sync();
+            // acc += the strip; the last direction completes the sums, so
+            // its passes write the gradients instead: gu = gy sum h, and
+            // gx = lambda sum g, glambda = x sum g
             for (int f0 = 0; f0 < units; f0 += 64 * kBatch) {
-                f32x4_t yv[kBatch];
+                f32x4_t yv[kBatch], m0[kBatch], m1[kBatch];
 #pragma unroll
                 for (int a = 0; a < kBatch; ++a) {
                     const int f = f0 + 64 * a + lane;
@@ -370,6 +374,12 @@ __device__ __forceinline__ void bwd_pass(const Ctx& c, float* strip) {
                     if (f < units && cq < width) {
                         const uint32_t o = static_cast<uint32_t>(row * W + cb + cq) * 4;
                         yv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(acc, o, 0, 0));
+                        if constexpr (Dir == 3) {
+                            m0[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                    Adj ? c.ls : c.gys, o, 0, 0));
+                            if constexpr (Adj)
+                                m1[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(c.xs, o, 0, 0));
+                        }
                     }
                 }
 #pragma unroll
@@ -377,11 +387,18 @@ __device__ __forceinline__ void bwd_pass(const Ctx& c, float* strip) {
                     const int f = f0 + 64 * a + lane;
                     const int row = f / kCQ, cq = 4 * (f % kCQ);
                     if (f < units && cq < width) {
-                        u32x4_t v;
+                        f32x4_t v;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(yv[a][e] + bs[(cq + e) * pitch + row]);
+                        for (int e = 0; e < 4; ++e) v[e] = yv[a][e] + bs[(cq + e) * pitch + row];
                         const uint32_t o = static_cast<uint32_t>(row * W + cb + cq) * 4;
-                        __builtin_amdgcn_raw_buffer_store_b128(v, acc, o, 0, 0);
+                        if constexpr (Dir == 3) {
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, m0[a] * v), acc, o, 0, 0);
+                            if constexpr (Adj)
+                                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, m1[a] * v), c.gls, o, 0,
+                                                                       0);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), acc, o, 0, 0);
+                        }
                     }
                 }
             }
@@ -409,6 +426,7 @@ prop2d_backward_wide_kernel(const float* __restrict__ x, const float* __restrict
     c.hs = rsrc(hws + pix0, pb);
     c.gxs = rsrc(gx + pix0, pb);
     c.gus = rsrc(gu + pix0, pb);
+    c.gls = rsrc(glam + pix0, pb);
     c.w4 = w4;
     c.gwd = gwd;
     c.planes = planes;
@@ -434,34 +452,6 @@ prop2d_backward_wide_kernel(const float* __restrict__ x, const float* __restrict
     bwd_pass<K, 3, false, Chunked>(c, strip);
     pass_sync();
     bwd_pass<K, 3, true, Chunked>(c, strip);
-    pass_sync();
-    // gx = lambda sum g, glambda = x sum g, gu = gy sum h
-    const int nq = HW / 4;
-    for (int e0 = 0; e0 < nq; e0 += 64 * 8) {
-        f32x4_t G[8], S[8], lv[8], xv[8], gv[8];
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            const int e = e0 + 64 * a + static_cast<int>(threadIdx.x);
-            if (e < nq) {
-                const uint32_t o = static_cast<uint32_t>(e) * 16;
-                G[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(c.gxs, o, 0, 0));
-                S[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(c.gus, o, 0, 0));
-                lv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(c.ls, o, 0, 0));
-                xv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(c.xs, o, 0, 0));
-                gv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(c.gys, o, 0, 0));
-            }
-        }
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            const int e = e0 + 64 * a + static_cast<int>(threadIdx.x);
-            if (e < nq) {
-                const size_t q = pix0 + 4 * static_cast<size_t>(e);
-                *reinterpret_cast<f32x4_t*>(gx + q) = lv[a] * G[a];
-                *reinterpret_cast<f32x4_t*>(glam + q) = xv[a] * G[a];
-                *reinterpret_cast<f32x4_t*>(gu + q) = gv[a] * S[a];
-            }
-        }
-    }
 }
 
 template <int K>
