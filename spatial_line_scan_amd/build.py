@@ -10,6 +10,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -29,18 +30,32 @@ FLAGS = [
 ]
 
 
+def _jobs() -> int:
+    """Parallel compiles: MAX_JOBS if set, else the CPUs this process may use."""
+    env = os.environ.get("MAX_JOBS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libgspn.so; returns its path."""
+    """Compile every source (in parallel) and link libgspn.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
+        cmds.append([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    with ThreadPoolExecutor(max_workers=min(_jobs(), len(cmds))) as pool:
+        for cmd in cmds:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+        # check_call raises on the first failed compile, after the others end
+        list(pool.map(subprocess.check_call, cmds))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp,
            "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
