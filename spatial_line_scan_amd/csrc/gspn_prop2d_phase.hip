@@ -8,21 +8,26 @@
 // design, §4.3 hidden state kept on chip, §5.1 fused normalisation (sigmoid,
 // local sum, clamp, divide); reading notes, method / overall framework.
 //
-// Work split.  One wavefront owns one plane and scans it twice: first the
-// rows (lanes 0-31 top-down, lanes 32-63 bottom-up), then the columns (lanes
-// 0-31 left-right, lanes 32-63 right-left).  Within a 32-lane half, lane q
-// holds positions Kq .. Kq+K-1 of the current line in registers and the
-// neighbour exchange is one wave-wide DPP shift each way (across the halves
-// the shifted value meets a dropped tap of weight 0).  K = 1 .. 5 for lines
-// up to 32, 64, 96, 128, 160 positions; a 148 x 148 plane takes 155 KB of
-// LDS, one plane per CU.
+// Work split.  One workgroup owns one plane and scans it twice: first the
+// rows (one half of its lanes top-down, the other bottom-up), then the
+// columns (left-right, right-left).  The halves are either the two 32-lane
+// halves of one wavefront or two whole wavefronts (when fewer than four
+// planes per CU are resident, or there are fewer planes than SIMDs): within
+// a half, lane q holds positions Kq .. Kq+K-1 of the current line in
+// registers and the neighbour exchange is one wave-wide DPP shift each way
+// (across the 32-lane halves the shifted value meets a dropped tap of weight
+// 0).  K = 1 .. 5 for lines up to 32, 64, 96, 128, 160 positions (32-lane
+// halves) or 1 .. 3 for lines up to 64, 128, 192 (64-lane halves); a 148 x
+// 148 plane takes 155 KB of LDS, one plane per CU.
 //
 // On-chip data.  LDS holds, per plane:
 //   S  fp32 [H][W]: the sum of the four directional states, zeroed first;
 //      every step adds h into the value of its line read one step earlier.
-//      One wavefront does all the adds, in program order, so the four terms
-//      of a pixel are summed in a fixed order (TD or BU first, then LR or
-//      RL) and no two lanes ever update one word in the same instruction.
+//      With one wavefront all the adds run in program order; two wavefronts
+//      meet at a barrier between every step's adds and its read of the next
+//      line.  Either way the four terms of a pixel are summed in a fixed
+//      order (TD or BU first, then LR or RL) and no two lanes ever update
+//      one word in the same step.
 //   b = lambda x of every pixel, computed once from coalesced loads of x and
 //      lambda: the exact product of two bf16 values has at most 16
 //      significant bits, so its fp32 pattern ends in 8 zero bits and it is
@@ -87,15 +92,24 @@ __device__ __forceinline__ void lds_order() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
 }
 
+// Two wavefronts: their LDS accesses before this point complete before
+// either wavefront's after it (LDS only: global loads in flight stay so).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename V>
 __device__ __forceinline__ lds_t<V>& lds_ref(uint32_t byte_off) {
     // the kernel's only LDS is its dynamic array, which starts at address 0
     return *reinterpret_cast<lds_t<V>*>(static_cast<uintptr_t>(byte_off));
 }
 
-// T: bf16 bits (uint16_t).  Chunked: k_chunk > 1.
-template <typename T, int K, int D, bool Chunked>
-__global__ void __launch_bounds__(64)
+// T: bf16 bits (uint16_t).  Chunked: k_chunk > 1.  NH: lanes a scan order
+// takes: 32 (the two halves of one wavefront) or 64 (one wavefront each).
+template <typename T, int K, int D, bool Chunked, int NH>
+__global__ void __launch_bounds__(2 * NH)
 prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __restrict__ u,
                     const T* __restrict__ w4, int w4_bytes, float eps, T* __restrict__ y,
                     int planes, int H, int W, int cpg, int k_chunk) {
@@ -104,31 +118,38 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
     constexpr int NW = window_words<T, K>();
     const int HW = H * W;
     const PhaseLayout lay(H, W);
-    const int lane = threadIdx.x;
-    const int half = lane >> 5;          // 0: forward (TD, LR), 1: backward (BU, RL)
-    const int q = lane & 31;
+    constexpr int NT = 2 * NH;           // threads of the workgroup
+    constexpr bool kTwo = NH == 64;
+    const int tid = threadIdx.x;
+    const int half = tid / NH;           // 0: forward (TD, LR), 1: backward (BU, RL)
+    const int q = tid % NH;
     const bool fwd = half == 0;
+    // orders the LDS accesses of the scan orders' lanes
+    auto sync = [&]() {
+        if constexpr (kTwo) lds_barrier();
+        else lds_order();
+    };
     const int plane = blockIdx.x;
     const size_t pix0 = static_cast<size_t>(plane) * HW;
 
     // ---------------------------------------- zero S, its pads and dummies
     // [0, bh): the dummy words, S with its pads, and the pad before b_hi
-    for (int f = lane; f < lay.bh / 16; f += 64) lds_ref<u32x4_t>(16u * f) = u32x4_t{0u, 0u, 0u, 0u};
+    for (int f = tid; f < lay.bh / 16; f += NT) lds_ref<u32x4_t>(16u * f) = u32x4_t{0u, 0u, 0u, 0u};
 
     const int words = HW / 2;     // HW is even: two pixels a dword
     // u for the end, in dword pairs, loaded now so that it arrives during
     // the scans (a trailing odd dword is loaded at the end)
-    constexpr int kUPer = 24;
+    constexpr int kUPer = kTwo ? 12 : 24;
     const int pairs = words / 2;
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     const u32x2_t* u64p = reinterpret_cast<const u32x2_t*>(u + pix0);
     u32x2_t ureg[kUPer];
 #pragma unroll
     for (int k = 0; k < kUPer; ++k) {
-        const int f = lane + 64 * k;
+        const int f = tid + NT * k;
         ureg[k] = f < pairs ? u64p[f] : u32x2_t{0u, 0u};
     }
-    lds_order();
+    sync();
 
     // LDS address of b at element index e
     auto b_addr_hi = [&](int e) { return static_cast<uint32_t>(lay.bh + 2 * e); };
@@ -321,6 +342,8 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
 
 #pragma unroll
             for (int j = 0; j < K; ++j) lds_ref<float>(aS[j]) = acc[j] + h[j];
+            // the other scan order's next line may be this one
+            if constexpr (kTwo) lds_barrier();
             // the next line, read after this step's writes
 #pragma unroll
             for (int j = 0; j < K; ++j) {
@@ -342,9 +365,9 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
             if (s0 + d < NL) step(s0 + d, d);
     };
     phase(std::true_type{});
-    lds_order();
+    sync();
     phase(std::false_type{});
-    lds_order();
+    sync();
 
     // --------------------------------------------------------- y = u * S
     // (S is read as four floats per dword pair, 16-byte aligned since the
@@ -361,30 +384,30 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
     };
 #pragma unroll
     for (int k = 0; k < kUPer; ++k) {
-        const int f = lane + 64 * k;
+        const int f = tid + NT * k;
         if (f < pairs) emit_pair(f, ureg[k]);
     }
     // the rest of u (planes over 6144 pixels), eight loads in flight at a time
-    for (int f0 = lane + 64 * kUPer; f0 < pairs; f0 += 64 * 8) {
+    for (int f0 = tid + NT * kUPer; f0 < pairs; f0 += NT * 8) {
         u32x2_t uv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            if (f0 + 64 * j < pairs) uv[j] = u64p[f0 + 64 * j];
+            if (f0 + NT * j < pairs) uv[j] = u64p[f0 + NT * j];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            if (f0 + 64 * j < pairs) emit_pair(f0 + 64 * j, uv[j]);
+            if (f0 + NT * j < pairs) emit_pair(f0 + NT * j, uv[j]);
     }
-    if ((words & 1) && lane == 0) y32[words - 1] = emit_word(words - 1, u32[words - 1]);
+    if ((words & 1) && tid == 0) y32[words - 1] = emit_word(words - 1, u32[words - 1]);
 }
 
-template <int K, bool Chunked>
+template <int K, bool Chunked, int NH>
 hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, float eps,
                     void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                     hipStream_t stream) {
     using T = uint16_t;
     constexpr int D = 8;   // taps prefetched D steps ahead
     const size_t lds = PhaseLayout(static_cast<int>(H), static_cast<int>(W)).bytes;
-    auto kern = prop2d_phase_kernel<T, K, D, Chunked>;
+    auto kern = prop2d_phase_kernel<T, K, D, Chunked, NH>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -392,7 +415,7 @@ hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w
         if (e != hipSuccess) return e;
     }
     const int64_t n = planes * H * W;
-    kern<<<dim3(static_cast<unsigned>(planes)), dim3(64), lds, stream>>>(
+    kern<<<dim3(static_cast<unsigned>(planes)), dim3(2 * NH), lds, stream>>>(
         static_cast<const T*>(x), static_cast<const T*>(lam), static_cast<const T*>(u),
         static_cast<const T*>(w4), static_cast<int>(12 * (n / o.cpg) * sizeof(T)), eps,
         static_cast<T*>(y), static_cast<int>(planes), static_cast<int>(H), static_cast<int>(W),
@@ -400,16 +423,36 @@ hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w
     return hipGetLastError();
 }
 
+// gfx950 (MI355X): compute units, four SIMDs each.
+constexpr int64_t kComputeUnits = 256;
+
+// Two wavefronts a plane (one per scan order, K = ceil(L / 64)) or one (32
+// lanes a scan order, K = ceil(L / 32)).  One wavefront a plane keeps every
+// SIMD busy once LDS holds four planes per CU and there is a plane for every
+// SIMD (latent1k: 0.115 ms against 0.135 with two, whose 64-lane lines leave
+// more slots idle and which meet at a barrier every step); with fewer planes
+// resident two wavefronts keep twice the SIMDs busy (148 x 148: one plane per
+// CU, 0.108 ms against 0.164).
+bool phase_two_waves(int64_t planes, int64_t H, int64_t W) {
+    const int64_t per_cu = kLdsBytes / PhaseLayout(static_cast<int>(H), static_cast<int>(W)).bytes;
+    return per_cu < 4 || planes < 4 * kComputeUnits;
+}
+
 template <bool Chunked>
 hipError_t launch_c(const void* x, const void* lam, const void* u, const void* w4, float eps,
                     void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                     hipStream_t stream) {
     const int64_t Lmax = H > W ? H : W;
-    if (Lmax <= 32) return launch_k<1, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    if (Lmax <= 64) return launch_k<2, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    if (Lmax <= 96) return launch_k<3, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    if (Lmax <= 128) return launch_k<4, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    return launch_k<5, Chunked>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (phase_two_waves(planes, H, W)) {
+        if (Lmax <= 64) return launch_k<1, Chunked, 64>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        if (Lmax <= 128) return launch_k<2, Chunked, 64>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        return launch_k<3, Chunked, 64>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    }
+    if (Lmax <= 32) return launch_k<1, Chunked, 32>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (Lmax <= 64) return launch_k<2, Chunked, 32>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (Lmax <= 96) return launch_k<3, Chunked, 32>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (Lmax <= 128) return launch_k<4, Chunked, 32>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    return launch_k<5, Chunked, 32>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }

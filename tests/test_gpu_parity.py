@@ -82,6 +82,22 @@ def _sampled_planes(B, C, k=6):
     return sorted(planes)
 
 
+# bf16 planes that the one-wavefront form of the phase kernel takes (LDS for
+# four planes a CU, a plane for every SIMD: 1024 planes here) with K = 1 .. 5
+# positions a lane; fewer planes take its two-wavefront form
+ONE_WAVE_SHAPES = [(16, 16), (64, 64), (30, 66), (74, 74), (20, 120), (8, 150)]
+
+
+@pytest.mark.parametrize("H,W", ONE_WAVE_SHAPES)
+def test_prop2d_phase_one_wave_form(H, W):
+    say("prop2d one-wave", H, W)
+    p = _problem(8, 128, H, W, 77 + H + 5 * W, "bf16")
+    y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
+    torch.cuda.synchronize()
+    assert_close(_np(y), oracle.prop2d(p["x"], p["lam"], p["u"], p["w"]), RTOL["bf16"],
+                 "%dx%d bf16, 1024 planes" % (H, W))
+
+
 @pytest.mark.parametrize("H,W", WIDE_SHAPES)
 def test_prop2d_wide_fp32_shapes(H, W):
     say("prop2d wide", H, W)
