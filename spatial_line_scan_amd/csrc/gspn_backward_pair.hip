@@ -63,12 +63,21 @@ __device__ __forceinline__ void lds_order() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
 }
 
+// Two wavefronts: their LDS accesses before this point complete before
+// either wavefront's after it (LDS only: global loads in flight stay so).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // LDS layout in bytes (offsets multiples of 16):
-//   [dummy: 16][2 lines][A: NL x L][B: NL x L][2 lines] ... [staging: 6 x 32 K]
-// A is the plane of lanes 0-31, B that of lanes 32-63.  The line before A
-// and the line after B are zero: the h before a scan's first line.  The
-// outer lines only absorb the read-ahead past the last adjoint step.  Slots
-// past a line's end read and write the dummy words.
+//   [dummy: 16 per wavefront][2 lines][A: NL x L][B: NL x L][2 lines] ... [staging: 6 x NH K]
+// A is the plane of the first direction's lanes, B that of the second's.
+// The line before A and the line after B are zero: the h before a scan's
+// first line.  The outer lines only absorb the read-ahead past the last
+// adjoint step.  Slots past a line's end read and write the dummy words (16
+// bytes, one set per wavefront).
 // fp32 data: one array of fp32 values.  bf16 data (narrow): two arrays laid
 // out this way, the upper 16 bits and the next 8 bits of each fp32 value
 // rounded to nearest even at bit 8 (a 16-bit significand; the gradients are
@@ -79,10 +88,10 @@ struct PairBwdLayout {
                                       // array; tap-gradient staging lines
     static constexpr int dum = 0, ldum = 8;
     __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
-    // gsize: bytes of a staged tap gradient
-    __host__ __device__ PairBwdLayout(int NL, int L, bool narrow, int gsize) {
+    // gsize: bytes of a staged tap gradient; nh: lanes a direction takes
+    __host__ __device__ PairBwdLayout(int NL, int L, bool narrow, int gsize, int nh = 32) {
         const int w = narrow ? 2 : 4;
-        a = a16(16 + 2 * w * L);
+        a = a16(16 * (nh / 32) + 2 * w * L);   // 16 dummy bytes per wavefront
         b = a16(a + w * NL * L);
         int end = b + w * (NL + 2) * L;
         la = lb = 0;
@@ -92,7 +101,7 @@ struct PairBwdLayout {
             end = lb + (NL + 2) * L;
         }
         stage = a16(end);
-        bytes = stage + 6 * 32 * ((L + 31) / 32) * gsize;   // K = ceil(L / 32) slots a lane
+        bytes = stage + 6 * nh * ((L + nh - 1) / nh) * gsize;   // K = ceil(L / nh) slots a lane
     }
 };
 
@@ -164,9 +173,10 @@ __device__ __forceinline__ f32x2_t load_pair(const T* p, size_t e) {
 // row pair's S and G and writes gu, gx, glam.
 // Taps are read from group plane p / cpg (w4: w4_bytes); the tap gradients
 // are written per channel, as GT, to gwd ([4][planes][3][..][..], gw_bytes).
-// Chunked: k_chunk > 1.
-template <typename T, typename GT, int K, int D, bool Cols, bool Chunked>
-__global__ void __launch_bounds__(64)
+// Chunked: k_chunk > 1.  NH: lanes a direction takes, 32 (the halves of one
+// wavefront) or 64 (a wavefront each; they meet only between passes).
+template <typename T, typename GT, int K, int D, bool Cols, bool Chunked, int NH>
+__global__ void __launch_bounds__(2 * NH)
 prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml,
                             const T* __restrict__ ul, const T* __restrict__ gyl,
                             const T* __restrict__ w4, int w4_bytes, GT* __restrict__ gwd,
@@ -182,17 +192,30 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     constexpr int VW = kNarrow ? 2 : 4;     // bytes of a value in the A / B array
     const int HW = NL * L;
     constexpr int GS = sizeof(GT);
-    const PairBwdLayout lay(NL, L, kNarrow, GS);
-    const int lane = threadIdx.x;
-    const int half = lane >> 5;
-    const int q = lane & 31;
+    const PairBwdLayout lay(NL, L, kNarrow, GS, NH);
+    constexpr int NT = 2 * NH;              // threads of the workgroup
+    constexpr bool kTwo = NH == 64;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int half = tid / NH;
+    const int q = tid % NH;
     const bool fwd = half == 0;
+    // orders the LDS accesses of the two directions' lanes
+    auto sync = [&]() {
+        if constexpr (kTwo) lds_barrier();
+        else lds_order();
+    };
     const int plane = blockIdx.x;
     const size_t pix0 = static_cast<size_t>(plane) * HW;
 
     // zero lines (h before a scan's first line) and the dummy words
-    if (lane < 4) lds_at<float>(4u * lane) = 0.0f;
-    for (int f = lane; f < L; f += 64) {
+    if (tid < 4 * (NH / 32)) lds_at<float>(4u * tid) = 0.0f;
+    // each wavefront's own dummy words: the values that slots past a line's
+    // end leave there (finite, and weighed only by dropped taps) then follow
+    // that wavefront's program order, so even the signs of the zero tap
+    // gradients they touch are the same from run to run
+    const uint32_t dum0 = kTwo ? 16u * half : 0u;
+    for (int f = tid; f < L; f += NT) {
         if constexpr (kNarrow) {
             lds_at<uint16_t>(lay.a - 2 * L + 2 * f) = 0;
             lds_at<uint16_t>(lay.b + 2 * HW + 2 * f) = 0;
@@ -313,19 +336,19 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         const int W = NL, H = L, npairs = HW / 2;
         const float invW = 1.0f / static_cast<float>(W);
         const f32x2_t* pp = reinterpret_cast<const f32x2_t*>(part + pix0);
-        for (int base = 0; base < npairs; base += 64 * U) {
+        for (int base = 0; base < npairs; base += NT * U) {
             f32x2_t pv[U], a[U], b[U];
 #pragma unroll
             for (int k = 0; k < U; ++k) {
                 // clamped to the last pair: in bounds, the value is not used
-                const int e2 = min(base + 64 * k + lane, npairs - 1);
+                const int e2 = min(base + NT * k + tid, npairs - 1);
                 pv[k] = pp[e2];
                 a[k] = load_pair(m0, pix0 + 2 * e2);
                 if constexpr (kTwo) b[k] = load_pair(m1, pix0 + 2 * e2);
             }
 #pragma unroll
             for (int k = 0; k < U; ++k) {
-                const int e2 = base + 64 * k + lane;
+                const int e2 = base + NT * k + tid;
                 if (e2 < npairs) {
                     const int e = 2 * e2;
                     const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
@@ -367,8 +390,8 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const int v = i0 * L + K * q + j;
-            aH[j] = valid[j] ? plane_base + VW * v : PairBwdLayout::dum + VW * j;
-            aL[j] = valid[j] ? lplane_base + v : PairBwdLayout::ldum + j;
+            aH[j] = valid[j] ? plane_base + VW * v : dum0 + PairBwdLayout::dum + VW * j;
+            aL[j] = valid[j] ? lplane_base + v : dum0 + PairBwdLayout::ldum + j;
             dH[j] = valid[j] ? VW * dl : 0;
             dL[j] = valid[j] ? dl : 0;
         }
@@ -427,18 +450,18 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         for (int d = 0; d < D; ++d)
             if (s0 + d < NL) step(s0 + d, d);
     }
-    lds_order();
+    sync();
 
     // --------------------------------------------------------- S = h_a + h_b
     // (line-major order is pixel order for the row pair; for the column pair
     // pixel (r, c) is position r of line c)
     if constexpr (!Cols) {
         f32x4_t* sp = reinterpret_cast<f32x4_t*>(s_ws + pix0);
-        for (int e = lane; e < HW / 4; e += 64) sp[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
+        for (int e = tid; e < HW / 4; e += NT) sp[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
     } else {
         column_pass(s_ws, gy, gy, gu, gu, std::false_type{});
     }
-    lds_order();
+    sync();
 
     // ------------------------------------------------------------ adjoint
     {
@@ -462,21 +485,24 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             load_line(d);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // read-back of the staging lines: dword f = lane + 64 t of the six
-        // lines of L ES / 4 dwords, stored at its place on the current line of
-        // its half's tap plane
-        constexpr int SL = 32 * K;               // staging line length
-        constexpr int NT = (3 * K * GS + 3) / 4; // ceil(6 * SL * GS / 4 / 64)
+        // read-back of the staging lines: dword f = lane + 64 t of the
+        // wavefront's lines (six, or its half's three with two wavefronts)
+        // of L ES / 4 dwords, stored at its place on the current line of its
+        // half's tap plane
+        constexpr int SL = NH * K;               // staging line length
+        constexpr int NR = (3 * K * GS + 3) / 4; // ceil(6 * 32 K GS / 4 / 64) = ceil(3 * 64 K GS / 4 / 64)
+        constexpr int kLines = kTwo ? 3 : 6;
         const int per_line = L * GS / 4;
-        uint32_t rd[NT], go[NT], gd[NT];
+        uint32_t rd[NR], go[NR], gd[NR];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < NR; ++t) {
             const int f = lane + 64 * t;
             rd[t] = lay.stage;
             go[t] = kDrop;
             gd[t] = 0;
-            if (f < 6 * per_line) {
-                const int hk = f / per_line, m = f - hk * per_line;
+            if (f < kLines * per_line) {
+                const int hk = (kTwo ? 3 * half : 0) + f / per_line;
+                const int m = f - (f / per_line) * per_line;
                 const int h = hk / 3, k = hk - 3 * h;
                 const int start = h == 0 ? NL - 1 : 0;      // first adjoint line of that half
                 rd[t] = lay.stage + hk * SL * GS + 4 * m;
@@ -497,8 +523,8 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const int v = i0 * L + K * q + j;
-            aGH[j] = valid[j] ? plane_base + VW * v : PairBwdLayout::dum + VW * j;
-            aGL[j] = valid[j] ? lplane_base + v : PairBwdLayout::ldum + j;
+            aGH[j] = valid[j] ? plane_base + VW * v : dum0 + PairBwdLayout::dum + VW * j;
+            aGL[j] = valid[j] ? lplane_base + v : dum0 + PairBwdLayout::ldum + j;
             dH[j] = valid[j] ? VW * dl : 0;
             dL[j] = valid[j] ? dl : 0;
             aPH[j] = aGH[j] + dH[j];
@@ -581,7 +607,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             // the writes (the LDS then executes them in program order)
             asm volatile("" ::: "memory");
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
+            for (int t = 0; t < NR; ++t) {
                 __builtin_amdgcn_raw_buffer_store_b32(lds_at<uint32_t>(rd[t]), gws, go[t], 0, 0);
                 go[t] += gd[t];
             }
@@ -606,12 +632,12 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         for (int d = 0; d < D; ++d)
             if (s0 + d < NL) step(s0 + d, d);
     }
-    lds_order();
+    sync();
 
     // --------------------------------------------------------- G = g_a + g_b
     if constexpr (!Cols) {
         f32x4_t* gp4 = reinterpret_cast<f32x4_t*>(g_ws + pix0);
-        for (int e = lane; e < HW / 4; e += 64) gp4[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
+        for (int e = tid; e < HW / 4; e += NT) gp4[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
     } else {
         column_pass(g_ws, lam, x, gx, glam, std::true_type{});
     }
@@ -705,40 +731,67 @@ struct PassArgs {
     T *gx, *glam, *gu;
 };
 
-template <typename T, typename GT, int K, bool Cols, bool Chunked>
+template <typename T, typename GT, int K, bool Cols, bool Chunked, int NH>
 hipError_t launch_pass(const PassArgs<T, GT>& a, hipStream_t stream) {
     constexpr int D = 4;   // lines prefetched ahead (the steps are long; a deeper unroll outgrows the instruction cache)
     const size_t lds = PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L), sizeof(T) == 2,
-                                     sizeof(GT)).bytes;
-    auto kern = prop2d_backward_pair_kernel<T, GT, K, D, Cols, Chunked>;
+                                     sizeof(GT), NH).bytes;
+    auto kern = prop2d_backward_pair_kernel<T, GT, K, D, Cols, Chunked, NH>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    kern<<<dim3(static_cast<unsigned>(a.planes)), dim3(64), lds, stream>>>(
+    kern<<<dim3(static_cast<unsigned>(a.planes)), dim3(2 * NH), lds, stream>>>(
         a.xl, a.ll, a.ul, a.gl, a.w4, a.w4_bytes, a.gwd, a.gw_bytes, a.cpg, a.k_chunk, a.eps,
         static_cast<int>(a.planes), static_cast<int>(a.NL), static_cast<int>(a.L), a.dir0, a.s_ws,
         a.g_ws, a.x, a.lam, a.gy, a.gx, a.glam, a.gu);
     return hipGetLastError();
 }
 
+// gfx950 (MI355X): compute units, four SIMDs each.
+constexpr int64_t kComputeUnits = 256;
+
+// A wavefront per direction (NH = 64) when fewer than four planes per CU
+// are resident or there are fewer planes than SIMDs, and its layout fits;
+// else the halves of one wavefront (NH = 32), which keep every SIMD busy
+// with fewer idle slots a line.
+template <typename T, typename GT>
+bool pair_two_waves(const PassArgs<T, GT>& a) {
+    const int lay32 = PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L), sizeof(T) == 2,
+                                    sizeof(GT), 32).bytes;
+    const int lay64 = PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L), sizeof(T) == 2,
+                                    sizeof(GT), 64).bytes;
+    if (lay64 > kLdsBytes) return false;
+    return kLdsBytes / lay32 < 4 || a.planes < 4 * kComputeUnits;
+}
+
 template <typename T, typename GT, bool Cols>
 hipError_t launch_pass_k(const PassArgs<T, GT>& a, hipStream_t stream) {
     const bool ch = a.k_chunk > 1;
+    if (pair_two_waves(a)) {
+        if (a.L <= 64)
+            return ch ? launch_pass<T, GT, 1, Cols, true, 64>(a, stream)
+                      : launch_pass<T, GT, 1, Cols, false, 64>(a, stream);
+        if (a.L <= 128)
+            return ch ? launch_pass<T, GT, 2, Cols, true, 64>(a, stream)
+                      : launch_pass<T, GT, 2, Cols, false, 64>(a, stream);
+        return ch ? launch_pass<T, GT, 3, Cols, true, 64>(a, stream)
+                  : launch_pass<T, GT, 3, Cols, false, 64>(a, stream);
+    }
     if (a.L <= 32)
-        return ch ? launch_pass<T, GT, 1, Cols, true>(a, stream) : launch_pass<T, GT, 1, Cols, false>(a, stream);
+        return ch ? launch_pass<T, GT, 1, Cols, true, 32>(a, stream) : launch_pass<T, GT, 1, Cols, false, 32>(a, stream);
     if (a.L <= 64)
-        return ch ? launch_pass<T, GT, 2, Cols, true>(a, stream) : launch_pass<T, GT, 2, Cols, false>(a, stream);
+        return ch ? launch_pass<T, GT, 2, Cols, true, 32>(a, stream) : launch_pass<T, GT, 2, Cols, false, 32>(a, stream);
     if (a.L <= 96)
-        return ch ? launch_pass<T, GT, 3, Cols, true>(a, stream) : launch_pass<T, GT, 3, Cols, false>(a, stream);
+        return ch ? launch_pass<T, GT, 3, Cols, true, 32>(a, stream) : launch_pass<T, GT, 3, Cols, false, 32>(a, stream);
     if (a.L <= 128)
-        return ch ? launch_pass<T, GT, 4, Cols, true>(a, stream) : launch_pass<T, GT, 4, Cols, false>(a, stream);
+        return ch ? launch_pass<T, GT, 4, Cols, true, 32>(a, stream) : launch_pass<T, GT, 4, Cols, false, 32>(a, stream);
     if constexpr (sizeof(T) == 4) {
         return hipErrorInvalidValue;   // fp32 lines take at most four dwords a lane (pair_fits)
     } else {
-        return ch ? launch_pass<T, GT, 5, Cols, true>(a, stream) : launch_pass<T, GT, 5, Cols, false>(a, stream);
+        return ch ? launch_pass<T, GT, 5, Cols, true, 32>(a, stream) : launch_pass<T, GT, 5, Cols, false, 32>(a, stream);
     }
 }
 
