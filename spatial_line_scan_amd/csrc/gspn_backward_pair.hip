@@ -1,6 +1,6 @@
-// Gradient of the four-direction propagation, one wavefront per (b, c) plane
-// and direction pair (gfx950), for planes of even sides up to 160 (bf16; fp32
-// while its wider layout fits in LDS).
+// Gradient of the four-direction propagation, one workgroup per (b, c) plane
+// and direction pair, a wavefront per direction (gfx950), for planes of even
+// sides up to 160 (bf16; fp32 up to 128, while its wider layout fits in LDS).
 //
 // Operator: the exact derivative of the forward definition ("Scaling Parallel
 // Sequence Models to Foundation-Scale Vision Encoders", §3 line-scan
@@ -18,10 +18,14 @@
 // (left-right, right-left) are two launches of one kernel that sees the lines
 // of its pair as the rows of a line-major plane: the row launch reads x,
 // lambda, u and gy as they are, the column launch reads copies transposed by
-// transpose4_kernel.  Every direction's taps are line-major already.  Lanes
-// 0-31 take the direction that scans lines 0 .. NL-1, lanes 32-63 the other;
-// lane q holds positions Kq .. Kq+K-1 of its line, and the three-tap
-// neighbourhood is one DPP lane shift each way, as in the forward kernels.
+// transpose4_kernel.  Every direction's taps are line-major already.  The
+// first wavefront takes the direction that scans lines 0 .. NL-1, the second
+// the other; lane q holds positions Kq .. Kq+K-1 of its line (K = ceil(L /
+// 64)), and the three-tap neighbourhood is one DPP lane shift each way, as in
+// the forward kernels.  The wavefronts meet only between passes (LDS-only
+// barriers).  The kernel also has the form that gives each direction one
+// 32-lane half of a single wavefront (NH = 32); it measured slower (latent1k
+// 0.505 ms against 0.480) and is not launched.
 //   1. Forward: h line by line (taps normalised in registers, b = lambda x
 //      from the line's windows); every line of h goes to an fp32 LDS plane of
 //      the half.
@@ -750,49 +754,19 @@ hipError_t launch_pass(const PassArgs<T, GT>& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// gfx950 (MI355X): compute units, four SIMDs each.
-constexpr int64_t kComputeUnits = 256;
-
-// A wavefront per direction (NH = 64) when fewer than four planes per CU
-// are resident or there are fewer planes than SIMDs, and its layout fits;
-// else the halves of one wavefront (NH = 32), which keep every SIMD busy
-// with fewer idle slots a line.
-template <typename T, typename GT>
-bool pair_two_waves(const PassArgs<T, GT>& a) {
-    const int lay32 = PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L), sizeof(T) == 2,
-                                    sizeof(GT), 32).bytes;
-    const int lay64 = PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L), sizeof(T) == 2,
-                                    sizeof(GT), 64).bytes;
-    if (lay64 > kLdsBytes) return false;
-    return kLdsBytes / lay32 < 4 || a.planes < 4 * kComputeUnits;
-}
-
+// A wavefront per direction (NH = 64, K = ceil(L / 64)).  The directions
+// meet only between passes, so this needs no barrier a step, and two
+// wavefronts a SIMD hide more of each other's latency than the halves of
+// one wavefront (NH = 32, K = ceil(L / 32)) save in idle slots: latent1k
+// 0.480 ms against 0.505, 148 x 148 (one plane per CU) 0.42 against 0.58.
 template <typename T, typename GT, bool Cols>
 hipError_t launch_pass_k(const PassArgs<T, GT>& a, hipStream_t stream) {
     const bool ch = a.k_chunk > 1;
-    if (pair_two_waves(a)) {
-        if (a.L <= 64)
-            return ch ? launch_pass<T, GT, 1, Cols, true, 64>(a, stream)
-                      : launch_pass<T, GT, 1, Cols, false, 64>(a, stream);
-        if (a.L <= 128)
-            return ch ? launch_pass<T, GT, 2, Cols, true, 64>(a, stream)
-                      : launch_pass<T, GT, 2, Cols, false, 64>(a, stream);
-        return ch ? launch_pass<T, GT, 3, Cols, true, 64>(a, stream)
-                  : launch_pass<T, GT, 3, Cols, false, 64>(a, stream);
-    }
-    if (a.L <= 32)
-        return ch ? launch_pass<T, GT, 1, Cols, true, 32>(a, stream) : launch_pass<T, GT, 1, Cols, false, 32>(a, stream);
     if (a.L <= 64)
-        return ch ? launch_pass<T, GT, 2, Cols, true, 32>(a, stream) : launch_pass<T, GT, 2, Cols, false, 32>(a, stream);
-    if (a.L <= 96)
-        return ch ? launch_pass<T, GT, 3, Cols, true, 32>(a, stream) : launch_pass<T, GT, 3, Cols, false, 32>(a, stream);
+        return ch ? launch_pass<T, GT, 1, Cols, true, 64>(a, stream) : launch_pass<T, GT, 1, Cols, false, 64>(a, stream);
     if (a.L <= 128)
-        return ch ? launch_pass<T, GT, 4, Cols, true, 32>(a, stream) : launch_pass<T, GT, 4, Cols, false, 32>(a, stream);
-    if constexpr (sizeof(T) == 4) {
-        return hipErrorInvalidValue;   // fp32 lines take at most four dwords a lane (pair_fits)
-    } else {
-        return ch ? launch_pass<T, GT, 5, Cols, true, 32>(a, stream) : launch_pass<T, GT, 5, Cols, false, 32>(a, stream);
-    }
+        return ch ? launch_pass<T, GT, 2, Cols, true, 64>(a, stream) : launch_pass<T, GT, 2, Cols, false, 64>(a, stream);
+    return ch ? launch_pass<T, GT, 3, Cols, true, 64>(a, stream) : launch_pass<T, GT, 3, Cols, false, 64>(a, stream);
 }
 
 template <typename T, typename GT>
@@ -857,15 +831,15 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
 
 namespace {
 
-// Even sides up to 160 for bf16 (five slots a lane) and 128 for fp32 (four
-// slots: a lane's window of a line is one load of at most four dwords) whose
-// layout, for the storage width (narrow: bf16) and fp32 staged tap gradients
-// (the larger staging), fits in LDS for both the row and the column launch.
+// Even sides up to 160 for bf16 (three slots a lane) and 128 for fp32 (two
+// slots) whose layout, for the storage width (narrow: bf16), fp32 staged tap
+// gradients (the larger staging) and a wavefront per direction, fits in LDS
+// for both the row and the column launch.
 bool pair_fits(int64_t planes, int64_t H, int64_t W, bool narrow) {
     const int64_t side = narrow ? 160 : 128;
     if (H < 2 || W < 2 || H > side || W > side || (H & 1) || (W & 1)) return false;
-    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), narrow, 4).bytes > kLdsBytes ||
-        PairBwdLayout(static_cast<int>(W), static_cast<int>(H), narrow, 4).bytes > kLdsBytes)
+    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), narrow, 4, 64).bytes > kLdsBytes ||
+        PairBwdLayout(static_cast<int>(W), static_cast<int>(H), narrow, 4, 64).bytes > kLdsBytes)
         return false;
     // every stream offset is a 32-bit byte offset into one buffer resource
     return 12 * planes * H * W * 4 <= 0x7fffffff;
