@@ -24,10 +24,10 @@
 //   S  fp32 [H][W]: the sum of the four directional states, zeroed first;
 //      every step adds h into the value of its line read one step earlier.
 //      With one wavefront all the adds run in program order; two wavefronts
-//      meet at a barrier between every step's adds and its read of the next
-//      line.  Either way the four terms of a pixel are summed in a fixed
-//      order (TD or BU first, then LR or RL) and no two lanes ever update
-//      one word in the same step.
+//      meet at one barrier a phase, at its middle step, which separates the
+//      two updates every pixel gets in the phase.  Either way the four terms
+//      of a pixel are summed in a fixed order (TD or BU first, then LR or
+//      RL) and no two lanes ever update one word at once.
 //   b = lambda x of every pixel, computed once from coalesced loads of x and
 //      lambda: the exact product of two bf16 values has at most 16
 //      significant bits, so its fp32 pattern ends in 8 zero bits and it is
@@ -342,8 +342,13 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
 
 #pragma unroll
             for (int j = 0; j < K; ++j) lds_ref<float>(aS[j]) = acc[j] + h[j];
-            // the other scan order's next line may be this one
-            if constexpr (kTwo) lds_barrier();
+            // Each pixel of the phase is updated once per scan order.  The
+            // order that reaches it first does so by step NL / 2 - 1; the
+            // other reads it one step ahead, at step NL / 2 - 1 or later.  So
+            // one barrier there, between this step's writes and its
+            // read-ahead, orders every pair of updates (NL is even).
+            if constexpr (kTwo)
+                if (s == NL / 2 - 1) lds_barrier();
             // the next line, read after this step's writes
 #pragma unroll
             for (int j = 0; j < K; ++j) {
@@ -429,10 +434,9 @@ constexpr int64_t kComputeUnits = 256;
 // Two wavefronts a plane (one per scan order, K = ceil(L / 64)) or one (32
 // lanes a scan order, K = ceil(L / 32)).  One wavefront a plane keeps every
 // SIMD busy once LDS holds four planes per CU and there is a plane for every
-// SIMD (latent1k: 0.115 ms against 0.135 with two, whose 64-lane lines leave
-// more slots idle and which meet at a barrier every step); with fewer planes
-// resident two wavefronts keep twice the SIMDs busy (148 x 148: one plane per
-// CU, 0.108 ms against 0.164).
+// SIMD (latent1k: 0.115 ms against 0.129 with two, whose 64-lane lines leave
+// more slots idle); with fewer planes resident two wavefronts keep twice the
+// SIMDs busy (148 x 148: one plane per CU, 0.099 ms against 0.164).
 bool phase_two_waves(int64_t planes, int64_t H, int64_t W) {
     const int64_t per_cu = kLdsBytes / PhaseLayout(static_cast<int>(H), static_cast<int>(W)).bytes;
     return per_cu < 4 || planes < 4 * kComputeUnits;
