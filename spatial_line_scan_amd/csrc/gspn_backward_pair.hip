@@ -23,9 +23,7 @@
 // the other; lane q holds positions Kq .. Kq+K-1 of its line (K = ceil(L /
 // 64)), and the three-tap neighbourhood is one DPP lane shift each way, as in
 // the forward kernels.  The wavefronts meet only between passes (LDS-only
-// barriers).  The kernel also has the form that gives each direction one
-// 32-lane half of a single wavefront (NH = 32); it measured slower (latent1k
-// 0.505 ms against 0.480) and is not launched.
+// barriers).
 //   1. Forward: h line by line (taps normalised in registers, b = lambda x
 //      from the line's windows); every line of h goes to an fp32 LDS plane of
 //      the half.
@@ -62,11 +60,6 @@ __device__ __forceinline__ lds_t<V>& lds_at(uint32_t byte_off) {
     return *reinterpret_cast<lds_t<V>*>(static_cast<uintptr_t>(byte_off));
 }
 
-// Orders this wavefront's LDS accesses before the fence against those after it.
-__device__ __forceinline__ void lds_order() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-}
-
 // Two wavefronts: their LDS accesses before this point complete before
 // either wavefront's after it (LDS only: global loads in flight stay so).
 __device__ __forceinline__ void lds_barrier() {
@@ -76,7 +69,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // LDS layout in bytes (offsets multiples of 16):
-//   [dummy: 16 per wavefront][2 lines][A: NL x L][B: NL x L][2 lines] ... [staging: 6 x NH K]
+//   [dummy: 16 per wavefront][2 lines][A: NL x L][B: NL x L][2 lines] ... [staging: 6 x 64 K]
 // A is the plane of the first direction's lanes, B that of the second's.
 // The line before A and the line after B are zero: the h before a scan's
 // first line.  The outer lines only absorb the read-ahead past the last
@@ -92,10 +85,11 @@ struct PairBwdLayout {
                                       // array; tap-gradient staging lines
     static constexpr int dum = 0, ldum = 8;
     __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
-    // gsize: bytes of a staged tap gradient; nh: lanes a direction takes
-    __host__ __device__ PairBwdLayout(int NL, int L, bool narrow, int gsize, int nh = 32) {
+    // gsize: bytes of a staged tap gradient
+    __host__ __device__ PairBwdLayout(int NL, int L, bool narrow, int gsize) {
+        constexpr int nh = 64;   // lanes a direction takes
         const int w = narrow ? 2 : 4;
-        a = a16(16 * (nh / 32) + 2 * w * L);   // 16 dummy bytes per wavefront
+        a = a16(32 + 2 * w * L);   // 16 dummy bytes per wavefront
         b = a16(a + w * NL * L);
         int end = b + w * (NL + 2) * L;
         la = lb = 0;
@@ -177,10 +171,10 @@ __device__ __forceinline__ f32x2_t load_pair(const T* p, size_t e) {
 // row pair's S and G and writes gu, gx, glam.
 // Taps are read from group plane p / cpg (w4: w4_bytes); the tap gradients
 // are written per channel, as GT, to gwd ([4][planes][3][..][..], gw_bytes).
-// Chunked: k_chunk > 1.  NH: lanes a direction takes, 32 (the halves of one
-// wavefront) or 64 (a wavefront each; they meet only between passes).
-template <typename T, typename GT, int K, int D, bool Cols, bool Chunked, int NH>
-__global__ void __launch_bounds__(2 * NH)
+// Chunked: k_chunk > 1.  A wavefront per direction; they meet only between
+// passes.
+template <typename T, typename GT, int K, int D, bool Cols, bool Chunked>
+__global__ void __launch_bounds__(128)
 prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml,
                             const T* __restrict__ ul, const T* __restrict__ gyl,
                             const T* __restrict__ w4, int w4_bytes, GT* __restrict__ gwd,
@@ -196,29 +190,25 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     constexpr int VW = kNarrow ? 2 : 4;     // bytes of a value in the A / B array
     const int HW = NL * L;
     constexpr int GS = sizeof(GT);
-    const PairBwdLayout lay(NL, L, kNarrow, GS, NH);
-    constexpr int NT = 2 * NH;              // threads of the workgroup
-    constexpr bool kTwo = NH == 64;
+    const PairBwdLayout lay(NL, L, kNarrow, GS);
+    constexpr int NT = 128;                 // threads of the workgroup
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int half = tid / NH;
-    const int q = tid % NH;
+    const int half = tid >> 6;              // the wavefront: its direction
+    const int q = lane;
     const bool fwd = half == 0;
-    // orders the LDS accesses of the two directions' lanes
-    auto sync = [&]() {
-        if constexpr (kTwo) lds_barrier();
-        else lds_order();
-    };
+    // orders the LDS accesses of the two wavefronts
+    auto sync = [&]() { lds_barrier(); };
     const int plane = blockIdx.x;
     const size_t pix0 = static_cast<size_t>(plane) * HW;
 
     // zero lines (h before a scan's first line) and the dummy words
-    if (tid < 4 * (NH / 32)) lds_at<float>(4u * tid) = 0.0f;
+    if (tid < 8) lds_at<float>(4u * tid) = 0.0f;
     // each wavefront's own dummy words: the values that slots past a line's
     // end leave there (finite, and weighed only by dropped taps) then follow
     // that wavefront's program order, so even the signs of the zero tap
     // gradients they touch are the same from run to run
-    const uint32_t dum0 = kTwo ? 16u * half : 0u;
+    const uint32_t dum0 = 16u * half;
     for (int f = tid; f < L; f += NT) {
         if constexpr (kNarrow) {
             lds_at<uint16_t>(lay.a - 2 * L + 2 * f) = 0;
@@ -490,12 +480,11 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             __builtin_amdgcn_sched_barrier(0);
         }
         // read-back of the staging lines: dword f = lane + 64 t of the
-        // wavefront's lines (six, or its half's three with two wavefronts)
-        // of L ES / 4 dwords, stored at its place on the current line of its
-        // half's tap plane
-        constexpr int SL = NH * K;               // staging line length
-        constexpr int NR = (3 * K * GS + 3) / 4; // ceil(6 * 32 K GS / 4 / 64) = ceil(3 * 64 K GS / 4 / 64)
-        constexpr int kLines = kTwo ? 3 : 6;
+        // wavefront's three lines of L ES / 4 dwords, stored at its place on
+        // the current line of its direction's tap plane
+        constexpr int SL = 64 * K;               // staging line length
+        constexpr int NR = (3 * K * GS + 3) / 4; // ceil(3 * SL * GS / 4 / 64)
+        constexpr int kLines = 3;
         const int per_line = L * GS / 4;
         uint32_t rd[NR], go[NR], gd[NR];
 #pragma unroll
@@ -505,7 +494,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             go[t] = kDrop;
             gd[t] = 0;
             if (f < kLines * per_line) {
-                const int hk = (kTwo ? 3 * half : 0) + f / per_line;
+                const int hk = 3 * half + f / per_line;
                 const int m = f - (f / per_line) * per_line;
                 const int h = hk / 3, k = hk - 3 * h;
                 const int start = h == 0 ? NL - 1 : 0;      // first adjoint line of that half
@@ -735,38 +724,38 @@ struct PassArgs {
     T *gx, *glam, *gu;
 };
 
-template <typename T, typename GT, int K, bool Cols, bool Chunked, int NH>
+template <typename T, typename GT, int K, bool Cols, bool Chunked>
 hipError_t launch_pass(const PassArgs<T, GT>& a, hipStream_t stream) {
     constexpr int D = 4;   // lines prefetched ahead (the steps are long; a deeper unroll outgrows the instruction cache)
     const size_t lds = PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L), sizeof(T) == 2,
-                                     sizeof(GT), NH).bytes;
-    auto kern = prop2d_backward_pair_kernel<T, GT, K, D, Cols, Chunked, NH>;
+                                     sizeof(GT)).bytes;
+    auto kern = prop2d_backward_pair_kernel<T, GT, K, D, Cols, Chunked>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    kern<<<dim3(static_cast<unsigned>(a.planes)), dim3(2 * NH), lds, stream>>>(
+    kern<<<dim3(static_cast<unsigned>(a.planes)), dim3(128), lds, stream>>>(
         a.xl, a.ll, a.ul, a.gl, a.w4, a.w4_bytes, a.gwd, a.gw_bytes, a.cpg, a.k_chunk, a.eps,
         static_cast<int>(a.planes), static_cast<int>(a.NL), static_cast<int>(a.L), a.dir0, a.s_ws,
         a.g_ws, a.x, a.lam, a.gy, a.gx, a.glam, a.gu);
     return hipGetLastError();
 }
 
-// A wavefront per direction (NH = 64, K = ceil(L / 64)).  The directions
-// meet only between passes, so this needs no barrier a step, and two
+// K = ceil(L / 64) positions a lane.  A wavefront per direction needs no
+// barrier a step (the directions meet only between passes), and two
 // wavefronts a SIMD hide more of each other's latency than the halves of
-// one wavefront (NH = 32, K = ceil(L / 32)) save in idle slots: latent1k
-// 0.480 ms against 0.505, 148 x 148 (one plane per CU) 0.42 against 0.58.
+// one wavefront (K = ceil(L / 32)) saved in idle slots: latent1k 0.480 ms
+// against 0.505, 148 x 148 (one plane per CU) 0.42 against 0.58.
 template <typename T, typename GT, bool Cols>
 hipError_t launch_pass_k(const PassArgs<T, GT>& a, hipStream_t stream) {
     const bool ch = a.k_chunk > 1;
     if (a.L <= 64)
-        return ch ? launch_pass<T, GT, 1, Cols, true, 64>(a, stream) : launch_pass<T, GT, 1, Cols, false, 64>(a, stream);
+        return ch ? launch_pass<T, GT, 1, Cols, true>(a, stream) : launch_pass<T, GT, 1, Cols, false>(a, stream);
     if (a.L <= 128)
-        return ch ? launch_pass<T, GT, 2, Cols, true, 64>(a, stream) : launch_pass<T, GT, 2, Cols, false, 64>(a, stream);
-    return ch ? launch_pass<T, GT, 3, Cols, true, 64>(a, stream) : launch_pass<T, GT, 3, Cols, false, 64>(a, stream);
+        return ch ? launch_pass<T, GT, 2, Cols, true>(a, stream) : launch_pass<T, GT, 2, Cols, false>(a, stream);
+    return ch ? launch_pass<T, GT, 3, Cols, true>(a, stream) : launch_pass<T, GT, 3, Cols, false>(a, stream);
 }
 
 template <typename T, typename GT>
@@ -838,8 +827,8 @@ namespace {
 bool pair_fits(int64_t planes, int64_t H, int64_t W, bool narrow) {
     const int64_t side = narrow ? 160 : 128;
     if (H < 2 || W < 2 || H > side || W > side || (H & 1) || (W & 1)) return false;
-    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), narrow, 4, 64).bytes > kLdsBytes ||
-        PairBwdLayout(static_cast<int>(W), static_cast<int>(H), narrow, 4, 64).bytes > kLdsBytes)
+    if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), narrow, 4).bytes > kLdsBytes ||
+        PairBwdLayout(static_cast<int>(W), static_cast<int>(H), narrow, 4).bytes > kLdsBytes)
         return false;
     // every stream offset is a 32-bit byte offset into one buffer resource
     return 12 * planes * H * W * 4 <= 0x7fffffff;
