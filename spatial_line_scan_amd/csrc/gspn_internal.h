@@ -55,6 +55,15 @@ hipError_t launch_prop2d_phase(const void* x, const void* lam, const void* u, co
                                float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                                const PropOpts& opts, hipStream_t stream);
 
+// Fast path for square bf16 planes with even sides up to 80: one wavefront
+// per plane scans all four directions at once (gspn_prop2d_quad.hip).
+bool prop2d_quad_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                          const void* x, const void* lam, const void* u, const void* w4,
+                          const void* y);
+hipError_t launch_prop2d_quad(const void* x, const void* lam, const void* u, const void* w4,
+                              float eps, void* y, int64_t planes, int64_t L, const PropOpts& o,
+                              hipStream_t stream);
+
 // Gradient of gspn_prop2d_4dir_ex (gspn_backward.hip): taps of plane p read
 // from group plane p / cpg, scans cut into k_chunk segments.  ws holds
 // prop2d_backward_workspace_bytes(planes, H, W, cpg) bytes (NULL when that

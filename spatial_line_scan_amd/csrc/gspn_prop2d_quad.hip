@@ -1,0 +1,475 @@
+// Four-direction propagation of square bf16 planes with even sides up to 80,
+// all four scan orders at once: one wavefront per (b, c) plane, one 16-lane
+// row of the wavefront per direction (gfx950).
+//
+// Operator: "Scaling Parallel Sequence Models to Foundation-Scale Vision
+// Encoders", §3 line-scan recurrence (standard GSPN form), §4.1 single-kernel
+// design, §4.3 hidden state kept on chip, §5.1 fused normalisation (sigmoid,
+// local sum, clamp, divide); reading notes, method / overall framework.
+//
+// Work split.  Lanes 16 g .. 16 g + 15 scan direction g (0 top-down, 1
+// bottom-up, 2 left-right, 3 right-left) of the same plane, all in the same
+// step: at step s, TD is on row s, BU on row L-1-s, LR on column s and RL on
+// column L-1-s.  Lane q of a row holds positions Kq .. Kq+K-1 of its line in
+// registers (K = 1..5 for sides up to 16, 32, 48, 64, 80), and the
+// neighbour exchange is one DPP shift each way inside the 16-lane row (its
+// first and last lanes receive 0, which only dropped taps weigh).  Compared
+// with scanning rows and then columns with two directions a wavefront, a
+// 74-position line fills 74 of 80 slots instead of 74 of 96, and the plane
+// takes one pass of L steps instead of two.
+//
+// On-chip data, per plane:
+//   S   fp32 [L][L]: the sum of the four directional states.  Every step
+//       adds h into the value of its pixel read one step earlier.
+//   b = lambda x of every pixel, computed before the scan from coalesced
+//       loads of x and lambda.  The exact product of two bf16 values has at
+//       most 16 significant bits, so its fp32 pattern ends in 8 zero bits:
+//       it is kept as 24 bits, the upper 16 in one array and the next 8 in
+//       another (3 bytes a pixel).
+//   side fp32 [4][L]: the column scans' terms of the pixels where a row scan
+//       and a column scan meet in the same step.
+// At 74 x 74 a plane takes 39.5 KB, so four planes share a CU.
+//
+// Meeting pixels.  Any row line and column line cross, so in every step the
+// column scans reach four pixels that a row scan updates in the same step:
+// (s, s), (s, L-1-s), (L-1-s, s), (L-1-s, L-1-s).  There the column scan
+// adds its state into a side word indexed by the step instead of into S (a
+// column slot's row is Kq + j, so the meeting rows s and L-1-s fall in slots
+// s mod K and (L-1-s) mod K, both fixed for each step of a block of
+// K-aligned steps once (L-1) mod K is a template constant).  After the scan
+// the side words are added into the diagonal and anti-diagonal pixels.  Row
+// scans never meet each other (L even), nor do column scans; every other
+// pair of updates of one pixel falls in different steps, and each step reads
+// its pixels' sums after the previous step's writes.  One wavefront does all
+// adds in program order, so every pixel's four terms are summed in a fixed
+// order and the result is bitwise reproducible.
+//
+// Slots past the end of a line (positions >= L) read and write dummy words,
+// decode every tap to -2^127 (weight exactly 0) and hold h = 0; lanes whose
+// whole window lies past the line load nothing (an offset past the buffer).
+// So no value outside the plane enters it.
+#include "gspn_device.h"
+#include "gspn_internal.h"
+#include "gspn_lane.h"
+
+#include <type_traits>
+
+namespace gspn {
+namespace {
+
+using namespace lane;
+
+// LDS layout in bytes (offsets multiples of 16):
+//   [S dummy: 16][b dummy: 16][pad: 4 L][S: L L fp32][side: 4 L fp32]
+//   [b_hi: L L + 8 u16][b_lo: L L + L + 8 u8]
+// The last step's read-ahead goes one line past every scan: one row before S
+// (the pad), one row after it (side), and for b the neighbouring arrays or
+// b_lo's spare row.
+// b_hi and b_lo have 8 spare entries for the second half of the plane's last
+// 16-byte chunk when L L is not a multiple of 8.
+struct QuadLayout {
+    int s, side, bh, bl, bytes;
+    static constexpr int sdum = 0, bdum = 16;
+    __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
+    __host__ __device__ explicit QuadLayout(int L) {
+        const int n = L * L;
+        s = a16(32 + 4 * L);
+        side = a16(s + 4 * n);
+        bh = a16(side + 16 * L);
+        bl = a16(bh + 2 * (n + 8));
+        bytes = a16(bl + n + L + 8);
+    }
+};
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+template <typename V> using lds_t = __attribute__((address_space(3))) V;
+
+template <typename V>
+__device__ __forceinline__ lds_t<V>& lds_ref(uint32_t byte_off) {
+    // the kernel's only LDS is its dynamic array, which starts at address 0
+    return *reinterpret_cast<lds_t<V>*>(static_cast<uintptr_t>(byte_off));
+}
+
+// Orders this wavefront's LDS accesses before the fence against those after
+// it (one wavefront per workgroup; global loads in flight are not waited for).
+__device__ __forceinline__ void lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+}
+
+// Shifts inside each 16-lane row: lane l receives lane l - 1 (from_prev) or
+// l + 1 (from_next) of its row; a row's first (last) lane receives 0.
+__device__ __forceinline__ float row_prev(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_next(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xf, 0xf, true));
+}
+
+// bf16 of the low / high half of a dword as fp32
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Selector of v_perm that yields 0xff000000 = -2^127: the logit of a dropped
+// tap or of a slot past the line end (sigmoid exactly 0).
+constexpr uint32_t kSelDropped = 0x0d0c0c0cu;
+
+// K: positions a lane; R = (L - 1) mod K; D: steps a block (a multiple of K),
+// also the number of lines of taps prefetched ahead.
+template <int K, int R, int D>
+__global__ void __launch_bounds__(64)
+prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
+                   const uint16_t* __restrict__ u, const uint16_t* __restrict__ w4, int w4_bytes,
+                   float eps, uint16_t* __restrict__ y, int planes, int L, int cpg) {
+    static_assert(D % K == 0, "blocks of whole slot cycles");
+    constexpr int NW = window_words<uint16_t, K>();
+    const int n = L * L;
+    const QuadLayout lay(L);
+    const int lane = threadIdx.x;
+    const int g = lane >> 4;             // 0 TD, 1 BU, 2 LR, 3 RL
+    const int q = lane & 15;
+    const bool rows = g < 2;
+    const bool fwd = (g & 1) == 0;
+    const int plane = blockIdx.x;
+    const uint32_t plane_b = static_cast<uint32_t>(plane) * static_cast<uint32_t>(n) * 2u;
+    const int nchunk = (2 * n + 15) / 16;  // 16-byte chunks of a plane's bf16 values
+
+    // ------------------------------------------------ u, prefetched for the end
+    // (it arrives while the plane is scanned; kU 16-byte chunks a lane)
+    constexpr int kU = (2 * 80 * 80 / 16 + 63) / 64;
+    const __amdgpu_buffer_rsrc_t us = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(u), 0, static_cast<int>(static_cast<int64_t>(planes) * n * 2), kBufFlags);
+    u32x4_t uv[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        const int f = lane + 64 * k;
+        uv[k] = f < nchunk ? __builtin_amdgcn_raw_buffer_load_b128(us, plane_b + 16u * static_cast<uint32_t>(f), 0, 0)
+                           : u32x4_t{0u, 0u, 0u, 0u};
+    }
+
+    // ------------------------------------------------ x and lambda, all at once
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), 0, static_cast<int>(static_cast<int64_t>(planes) * n * 2), kBufFlags);
+    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(lam), 0, static_cast<int>(static_cast<int64_t>(planes) * n * 2), kBufFlags);
+    u32x4_t xv[kU], lv[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        const int f = lane + 64 * k;
+        const uint32_t off = plane_b + 16u * static_cast<uint32_t>(f);
+        xv[k] = f < nchunk ? __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0) : u32x4_t{0u, 0u, 0u, 0u};
+        lv[k] = f < nchunk ? __builtin_amdgcn_raw_buffer_load_b128(ls, off, 0, 0) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+
+    // ------------------------------------------------ taps: first D lines
+    const int tap_planes = planes / cpg;
+    __amdgpu_buffer_rsrc_t taps[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w4) + static_cast<size_t>(k) * n,
+                                                    0, w4_bytes - k * n * 2, kBufFlags);
+    const int par = (K * q) & 1;
+    const bool lane_live = K * q < L;
+    const uint32_t line_b = static_cast<uint32_t>(L) * 2u;
+    const uint32_t tap_base =
+        static_cast<uint32_t>((g * tap_planes + plane / cpg) * 3) * static_cast<uint32_t>(n) * 2u +
+        static_cast<uint32_t>(K * q - par) * 2u;
+    const uint32_t lo_min = lane_live ? tap_base : 0x80000000u;
+    const uint32_t lo_max = lane_live ? tap_base + static_cast<uint32_t>(L - 1) * line_b : 0x80000000u;
+    uint32_t lo = fwd ? lo_min : lo_max;
+    const uint32_t dlo = lane_live ? (fwd ? line_b : 0u - line_b) : 0u;
+    words_t<NW> tbuf[D][3];
+    auto load_line = [&](int d) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
+        const uint32_t nx = lo + dlo;
+        lo = nx < lo_min ? lo_min : (nx > lo_max ? lo_max : nx);
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        load_line(d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ------------------------------------------------ zero S, side, dummies
+    for (int f = lane; f < lay.bh / 16; f += 64) lds_ref<u32x4_t>(16u * f) = u32x4_t{0u, 0u, 0u, 0u};
+
+    // ------------------------------------------------ b = lambda x into LDS
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        const int f = lane + 64 * k;
+        if (f < nchunk) {
+            uint32_t bb[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                bb[2 * m] = __float_as_uint(bf_lo(lv[k][m]) * bf_lo(xv[k][m]));
+                bb[2 * m + 1] = __float_as_uint(bf_hi(lv[k][m]) * bf_hi(xv[k][m]));
+            }
+            u32x4_t hi;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) hi[m] = __builtin_amdgcn_perm(bb[2 * m + 1], bb[2 * m], 0x07060302u);
+            u32x2_t lo8;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const uint32_t t01 = __builtin_amdgcn_perm(bb[4 * m + 1], bb[4 * m], 0x0c0c0501u);
+                const uint32_t t23 = __builtin_amdgcn_perm(bb[4 * m + 3], bb[4 * m + 2], 0x05010c0cu);
+                lo8[m] = t01 | t23;
+            }
+            lds_ref<u32x4_t>(lay.bh + 16u * f) = hi;
+            lds_ref<u32x2_t>(lay.bl + 8u * f) = lo8;
+        }
+    }
+    lds_order();
+
+    // ------------------------------------------------ per-slot constants
+    const int i0 = fwd ? 0 : L - 1;
+    const int de = rows ? (fwd ? L : -L) : (fwd ? 1 : -1);
+    uint32_t aS[K], aH[K], aL[K];
+    int dSj[K], dHj[K], dLj[K];
+    uint32_t sel[3][K];
+    const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
+    const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int p = K * q + j;
+        const bool valid = p < L;
+        const int e = rows ? i0 * L + p : p * L + i0;
+        aS[j] = valid ? static_cast<uint32_t>(lay.s + 4 * e) : QuadLayout::sdum;
+        aH[j] = valid ? static_cast<uint32_t>(lay.bh + 2 * e) : QuadLayout::bdum;
+        aL[j] = valid ? static_cast<uint32_t>(lay.bl + e) : QuadLayout::bdum;
+        dSj[j] = valid ? 4 * de : 0;
+        dHj[j] = valid ? 2 * de : 0;
+        dLj[j] = valid ? de : 0;
+        const uint32_t s_in = (j & 1) ? sel_odd : sel_even;
+        sel[0][j] = (valid && p > 0) ? s_in : kSelDropped;
+        sel[1][j] = valid ? s_in : kSelDropped;
+        sel[2][j] = (valid && p < L - 1) ? s_in : kSelDropped;
+    }
+    // column slots that meet a row scan: key q for the column rows, none else
+    const uint32_t key = rows ? 0xffu : static_cast<uint32_t>(q);
+    const uint32_t side1 = static_cast<uint32_t>(lay.side + 4 * L * (g == 3 ? 1 : 0));
+    const uint32_t side2 = static_cast<uint32_t>(lay.side + 4 * L * (g == 3 ? 3 : 2));
+
+    float h[K], acc[K];
+    uint32_t bhr[K], blr[K];
+    uint32_t ra1 = 0, ra2 = 0;   // addresses of this step's two meeting slots
+
+    // S address of slot j at step s, for a step whose meeting slots are j1
+    // (row s, lanes q1) and j2 (row L-1-s, lanes q2)
+    auto meet_addr = [&](int j, int j1, int j2, uint32_t q1, uint32_t q2, int s) -> uint32_t {
+        uint32_t a = aS[j];
+        if (j == j1) a = key == q1 ? side1 + 4u * s : a;
+        if (j == j2) a = key == q2 ? side2 + 4u * s : a;
+        return a;
+    };
+    // Meeting slots of step s = s0 + t of a block starting at s0 (a multiple
+    // of K; t a compile-time value): rows s (slot t mod K, lanes q1) and
+    // L-1-s (slot (R - t) mod K, lanes q2), with q1 = s0 / K + t / K and q2 =
+    // (L-1-R-s0) / K + floor((R - t) / K).
+    auto read_ahead = [&](int t, int s, int qb1, int qb2) {
+        const int j1 = t % K;
+        const int j2 = ((R - t) % K + K) % K;
+        const uint32_t q1 = static_cast<uint32_t>(qb1 + t / K);
+        const uint32_t q2 = static_cast<uint32_t>(qb2 + (R - t >= 0 ? (R - t) / K : -((t - R + K - 1) / K)));
+        ra1 = meet_addr(j1, j1, j2, q1, q2, s);
+        ra2 = meet_addr(j2, j1, j2, q1, q2, s);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const uint32_t a = j == j1 ? ra1 : (j == j2 ? ra2 : aS[j]);
+            acc[j] = lds_ref<float>(a);
+            bhr[j] = lds_ref<uint16_t>(aH[j]);
+            blr[j] = lds_ref<uint8_t>(aL[j]);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < K; ++j) h[j] = 0.0f;
+    read_ahead(0, 0, 0, (L - 1 - R) / K);
+
+    auto step = [&](int s, int d, int qb1, int qb2) {
+        asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
+        float s0v[K], s1v[K], s2v[K], r[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            s0v[j] = window_elem<uint16_t, K, NW>(tbuf[d][0], j, sel[0][j], sel[0][j]) * kNegLog2e;
+            s1v[j] = window_elem<uint16_t, K, NW>(tbuf[d][1], j, sel[1][j], sel[1][j]) * kNegLog2e;
+            s2v[j] = window_elem<uint16_t, K, NW>(tbuf[d][2], j, sel[2][j], sel[2][j]) * kNegLog2e;
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            s0v[j] = __builtin_amdgcn_exp2f(s0v[j]);
+            s1v[j] = __builtin_amdgcn_exp2f(s1v[j]);
+            s2v[j] = __builtin_amdgcn_exp2f(s2v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            s0v[j] = __builtin_amdgcn_rcpf(s0v[j] + 1.0f);
+            s1v[j] = __builtin_amdgcn_rcpf(s1v[j] + 1.0f);
+            s2v[j] = __builtin_amdgcn_rcpf(s2v[j] + 1.0f);
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) r[j] = s0v[j] + s1v[j];
+#pragma unroll
+        for (int j = 0; j < K; ++j) r[j] = fmaxf(r[j] + s2v[j], eps);
+#pragma unroll
+        for (int j = 0; j < K; ++j) r[j] = __builtin_amdgcn_rcpf(r[j]);
+        // refill slot d only after it has been decoded
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            asm volatile("" : "+v"(lo) : "v"(s0v[j]), "v"(s1v[j]), "v"(s2v[j]), "v"(r[j]));
+        load_line(d);
+
+        float bv[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) bv[j] = __uint_as_float(__builtin_amdgcn_perm(bhr[j], blr[j], 0x0504000cu));
+        const float hl0 = row_prev(h[K - 1]);
+        const float hrK = row_next(h[0]);
+        float hn[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const float hl = j > 0 ? h[j - 1] : hl0;
+            const float hr = j < K - 1 ? h[j + 1] : hrK;
+            float m = s1v[j] * h[j];
+            m = fmaf(s0v[j], hl, m);
+            m = fmaf(s2v[j], hr, m);
+            hn[j] = fmaf(m, r[j], bv[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) h[j] = hn[j];
+
+        const int t = d % K;
+        const int j1 = t;
+        const int j2 = ((R - t) % K + K) % K;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const uint32_t a = j == j1 ? ra1 : (j == j2 ? ra2 : aS[j]);
+            lds_ref<float>(a) = acc[j] + h[j];
+        }
+        // the next step's pixels, read after this step's writes (the pins keep
+        // each address one add a step instead of base + multiple of the step)
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            aS[j] += dSj[j];
+            aH[j] += dHj[j];
+            aL[j] += dLj[j];
+            asm volatile("" : "+v"(aS[j]), "+v"(aH[j]), "+v"(aL[j]));
+        }
+        read_ahead(d + 1, s + 1, qb1, qb2);
+    };
+
+    int s0 = 0;
+    for (; s0 + D <= L; s0 += D) {
+        const int qb1 = s0 / K, qb2 = (L - 1 - R - s0) / K;
+#pragma unroll
+        for (int d = 0; d < D; ++d) step(s0 + d, d, qb1, qb2);
+    }
+    {
+        const int qb1 = s0 / K, qb2 = (L - 1 - R - s0) / K;
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (s0 + d < L) step(s0 + d, d, qb1, qb2);
+    }
+    lds_order();
+
+    // ------------------------------------------------ meeting pixels
+    // (t, t) += LR's side word of step t + RL's of step L-1-t;
+    // (t, L-1-t) += RL's of step t + LR's of step L-1-t
+    for (int t = lane; t < L; t += 64) {
+        const uint32_t sd = static_cast<uint32_t>(lay.s + 4 * (t * L + t));
+        const uint32_t sa = static_cast<uint32_t>(lay.s + 4 * (t * L + L - 1 - t));
+        const float d0 = lds_ref<float>(lay.side + 4 * t);                    // LR, row = col = t
+        const float d1 = lds_ref<float>(lay.side + 4 * (3 * L + L - 1 - t));  // RL at step L-1-t
+        const float a0 = lds_ref<float>(lay.side + 4 * (L + t));              // RL, (t, L-1-t)
+        const float a1 = lds_ref<float>(lay.side + 4 * (2 * L + L - 1 - t));  // LR at step L-1-t
+        lds_ref<float>(sd) = (lds_ref<float>(sd) + d0) + d1;
+        lds_ref<float>(sa) = (lds_ref<float>(sa) + a0) + a1;
+    }
+    lds_order();
+
+    // ------------------------------------------------ y = u * S
+    {
+        const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
+            y, 0, static_cast<int>(static_cast<int64_t>(planes) * n * 2), kBufFlags);
+        const int nfull = (2 * n) / 16;   // whole chunks of the plane
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+            const int f = lane + 64 * k;
+            if (f < nchunk) {
+                const f32x4_t sa = lds_ref<f32x4_t>(lay.s + 32u * f);
+                const f32x4_t sb = lds_ref<f32x4_t>(lay.s + 32u * f + 16u);
+                u32x4_t o;
+                o[0] = pack_bf16x2(bf_lo(uv[k][0]) * sa[0], bf_hi(uv[k][0]) * sa[1]);
+                o[1] = pack_bf16x2(bf_lo(uv[k][1]) * sa[2], bf_hi(uv[k][1]) * sa[3]);
+                o[2] = pack_bf16x2(bf_lo(uv[k][2]) * sb[0], bf_hi(uv[k][2]) * sb[1]);
+                o[3] = pack_bf16x2(bf_lo(uv[k][3]) * sb[2], bf_hi(uv[k][3]) * sb[3]);
+                const uint32_t yo = plane_b + 16u * static_cast<uint32_t>(f);
+                if (f < nfull)
+                    __builtin_amdgcn_raw_buffer_store_b128(o, ys, yo, 0, 0);
+                else  // a plane of L L = 4 mod 8 values ends half way into its last chunk
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{o[0], o[1]}, ys, yo, 0, 0);
+            }
+        }
+    }
+}
+
+template <int K, int R>
+hipError_t launch_kr(const void* x, const void* lam, const void* u, const void* w4, float eps,
+                     void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
+    constexpr int D = K * ((8 + K - 1) / K);
+    const size_t lds = QuadLayout(static_cast<int>(L)).bytes;
+    auto kern = prop2d_quad_kernel<K, R, D>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    const int64_t n = planes * L * L;
+    kern<<<dim3(static_cast<unsigned>(planes)), dim3(64), lds, stream>>>(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(lam), static_cast<const uint16_t*>(u),
+        static_cast<const uint16_t*>(w4), static_cast<int>(12 * (n / o.cpg) * 2), eps,
+        static_cast<uint16_t*>(y), static_cast<int>(planes), static_cast<int>(L), static_cast<int>(o.cpg));
+    return hipGetLastError();
+}
+
+template <int K>
+hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, float eps,
+                    void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
+    switch ((L - 1) % K) {
+        case 0: return launch_kr<K, 0>(x, lam, u, w4, eps, y, planes, L, o, stream);
+        case 1: if constexpr (K > 1) return launch_kr<K, 1 % K>(x, lam, u, w4, eps, y, planes, L, o, stream);
+                [[fallthrough]];
+        case 2: if constexpr (K > 2) return launch_kr<K, 2 % K>(x, lam, u, w4, eps, y, planes, L, o, stream);
+                [[fallthrough]];
+        case 3: if constexpr (K > 3) return launch_kr<K, 3 % K>(x, lam, u, w4, eps, y, planes, L, o, stream);
+                [[fallthrough]];
+        default: if constexpr (K > 4) return launch_kr<K, 4 % K>(x, lam, u, w4, eps, y, planes, L, o, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+bool prop2d_quad_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                          const void* x, const void* lam, const void* u, const void* w4,
+                          const void* y) {
+    if (dtype != 1 || H != W || (H & 1) || H > 80) return false;
+    if (o.k_chunk != 1) return false;
+    if (QuadLayout(static_cast<int>(H)).bytes > kLdsBytes) return false;
+    if (12 * planes * H * W * 2 > 0x7fffffff) return false;
+    return aligned4(x) && aligned4(lam) && aligned4(u) && aligned4(w4) && aligned4(y);
+}
+
+hipError_t launch_prop2d_quad(const void* x, const void* lam, const void* u, const void* w4,
+                              float eps, void* y, int64_t planes, int64_t L, const PropOpts& o,
+                              hipStream_t stream) {
+    if (L <= 16) return launch_k<1>(x, lam, u, w4, eps, y, planes, L, o, stream);
+    if (L <= 32) return launch_k<2>(x, lam, u, w4, eps, y, planes, L, o, stream);
+    if (L <= 48) return launch_k<3>(x, lam, u, w4, eps, y, planes, L, o, stream);
+    if (L <= 64) return launch_k<4>(x, lam, u, w4, eps, y, planes, L, o, stream);
+    return launch_k<5>(x, lam, u, w4, eps, y, planes, L, o, stream);
+}
+
+}  // namespace gspn

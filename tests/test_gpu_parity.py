@@ -98,6 +98,23 @@ def test_prop2d_phase_one_wave_form(H, W):
                  "%dx%d bf16, 1024 planes" % (H, W))
 
 
+# square bf16 planes with even sides up to 80 take the kernel that scans the
+# four directions at once (16 lanes a direction, K = 1 .. 5 positions a lane);
+# sides cover every K and every value of (L - 1) mod K it is built for
+QUAD_SIDES = [2, 4, 6, 14, 16, 18, 30, 32, 34, 36, 38, 46, 48, 50, 52, 62, 64, 66, 68, 70, 72, 74,
+              76, 78, 80]
+
+
+@pytest.mark.parametrize("L", QUAD_SIDES)
+def test_prop2d_quad_sides(L):
+    say("prop2d quad", L)
+    p = _problem(3, 5, L, L, 101 + L, "bf16")
+    y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
+    torch.cuda.synchronize()
+    assert_close(_np(y), oracle.prop2d(p["x"], p["lam"], p["u"], p["w"]), RTOL["bf16"],
+                 "%dx%d bf16" % (L, L))
+
+
 @pytest.mark.parametrize("H,W", WIDE_SHAPES)
 def test_prop2d_wide_fp32_shapes(H, W):
     say("prop2d wide", H, W)
