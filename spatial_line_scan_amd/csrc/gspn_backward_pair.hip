@@ -278,25 +278,36 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     const uint32_t plane_base = half ? lay.b : lay.a;
     const uint32_t lplane_base = half ? lay.lb : lay.la;
 
+    // Dropped taps.  bf16: the slot's byte selector decodes a dropped tap (or
+    // any tap of a slot past the line end) to -2^127, whose sigmoid is exactly
+    // 0 whatever the memory holds, and the values of a slot past the line end
+    // to 0.  fp32 (no selector): 1 / (e + inf) = 0.
+    constexpr bool kB16 = ES == 2;
     float c0[K], c1[K], c2[K];
+    uint32_t st[3][K], sx[K];
     bool valid[K];
     const float inf = __builtin_inff();
 #pragma unroll
     for (int j = 0; j < K; ++j) {
         const int p = K * q + j;
         valid[j] = p < L;
-        c0[j] = (valid[j] && p > 0) ? 1.0f : inf;
-        c1[j] = valid[j] ? 1.0f : inf;
-        c2[j] = (valid[j] && p < L - 1) ? 1.0f : inf;
+        c0[j] = (kB16 || (valid[j] && p > 0)) ? 1.0f : inf;
+        c1[j] = (kB16 || valid[j]) ? 1.0f : inf;
+        c2[j] = (kB16 || (valid[j] && p < L - 1)) ? 1.0f : inf;
+        const uint32_t s_in = (j & 1) ? sel_odd : sel_even;
+        st[0][j] = (valid[j] && p > 0) ? s_in : kSelDropped;
+        st[1][j] = valid[j] ? s_in : kSelDropped;
+        st[2][j] = (valid[j] && p < L - 1) ? s_in : kSelDropped;
+        sx[j] = valid[j] ? s_in : kSelZero;
     }
     // s_k = sigmoid(z_k) (0 for dropped taps) and r = 1 / max(sum s, eps)
     auto normalise = [&](const words_t<NW> (&tw)[3], float (&s0)[K], float (&s1)[K], float (&s2)[K],
                          float (&t)[K], float (&r)[K]) {
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            s0[j] = window_elem<T, K, NW>(tw[0], j, sel_even, sel_odd) * kNegLog2e;
-            s1[j] = window_elem<T, K, NW>(tw[1], j, sel_even, sel_odd) * kNegLog2e;
-            s2[j] = window_elem<T, K, NW>(tw[2], j, sel_even, sel_odd) * kNegLog2e;
+            s0[j] = window_elem<T, K, NW>(tw[0], j, st[0][j], st[0][j]) * kNegLog2e;
+            s1[j] = window_elem<T, K, NW>(tw[1], j, st[1][j], st[1][j]) * kNegLog2e;
+            s2[j] = window_elem<T, K, NW>(tw[2], j, st[2][j], st[2][j]) * kNegLog2e;
         }
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -402,8 +413,8 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             float s0[K], s1[K], s2[K], t[K], r[K], b[K];
 #pragma unroll
             for (int j = 0; j < K; ++j)
-                b[j] = window_elem<T, K, NW>(lbuf[d], j, sel_even, sel_odd) *
-                       window_elem<T, K, NW>(xbuf[d], j, sel_even, sel_odd);
+                b[j] = window_elem<T, K, NW>(lbuf[d], j, sx[j], sx[j]) *
+                       window_elem<T, K, NW>(xbuf[d], j, sx[j], sx[j]);
             normalise(tbuf[d], s0, s1, s2, t, r);
 #pragma unroll
             for (int j = 0; j < K; ++j)
@@ -427,8 +438,11 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 m = fmaf(s2[j], hr, m);
                 hn[j] = fmaf(m, r[j], b[j]);
             }
+            // fp32 slots past the line end hold 0 (their windows read the next
+            // line or plane; bf16 ones decode to 0 and stay 0)
 #pragma unroll
             for (int j = 0; j < K; ++j) {
+                if constexpr (!kB16) hn[j] = valid[j] ? hn[j] : 0.0f;
                 h[j] = hn[j];
                 put(aH[j], aL[j], hn[j]);
                 aH[j] += dH[j];
@@ -536,8 +550,8 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             float s0[K], s1[K], s2[K], t[K], r[K], ugy[K];
 #pragma unroll
             for (int j = 0; j < K; ++j)
-                ugy[j] = window_elem<T, K, NW>(ubuf[d], j, sel_even, sel_odd) *
-                         window_elem<T, K, NW>(gbuf[d], j, sel_even, sel_odd);
+                ugy[j] = window_elem<T, K, NW>(ubuf[d], j, sx[j], sx[j]) *
+                         window_elem<T, K, NW>(gbuf[d], j, sx[j], sx[j]);
             normalise(tbuf[d], s0, s1, s2, t, r);
 #pragma unroll
             for (int j = 0; j < K; ++j)
@@ -558,6 +572,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             for (int j = 0; j < K; ++j) {
                 g[j] += j < K - 1 ? P0[j + 1] : P0n;
                 g[j] += j > 0 ? P2[j - 1] : P2p;
+                if constexpr (!kB16) g[j] = valid[j] ? g[j] : 0.0f;
             }
 
             // tap gradients of line i

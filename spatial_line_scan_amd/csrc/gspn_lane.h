@@ -64,6 +64,12 @@ __device__ __forceinline__ float window_elem(const words_t<NW>& w, int j, uint32
     }
 }
 
+// v_perm selectors for a bf16 window element that ignore the memory: 0xff000000
+// (-2^127, a logit whose sigmoid is exactly 0) and 0 (a value that adds
+// nothing).
+constexpr uint32_t kSelDropped = 0x0d0c0c0cu;
+constexpr uint32_t kSelZero = 0x0c0c0c0cu;
+
 // Two floats to packed bf16 (low, high), round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -353,8 +353,11 @@ prop2d_pair_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* 
                 m = fmaf(s2v[j], hr, m);
                 hn[j] = fmaf(m, r[j], b[j]);
             }
+            // slots past the line end hold 0: their windows read the next
+            // line, or the next plane, whose values may not be finite, and
+            // dropped taps weigh them by 0
 #pragma unroll
-            for (int j = 0; j < K; ++j) h[j] = hn[j];
+            for (int j = 0; j < K; ++j) h[j] = valid[j] ? hn[j] : 0.0f;
 
             // On the middle line of an odd scan the backward half writes to
             // the padding line after the plane instead (added in afterwards).

@@ -176,16 +176,21 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
         const int L = kRows ? W : H;
         const int NL = kRows ? H : W;
         const int g = (kRows ? 0 : 2) + half;        // direction TD, BU, LR, RL
-        float c0[K], c1[K], c2[K];
+        // per slot and tap, the byte selector of its element in the window;
+        // a dropped tap (or any tap of a slot past the line end) decodes to
+        // -2^127, whose sigmoid is exactly 0 whatever the memory holds, and x
+        // and lambda of a slot past the line end decode to 0
+        uint32_t st[3][K], sx[K];
         bool valid[K];
-        const float inf = __builtin_inff();
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const int p = K * q + j;
             valid[j] = p < L;
-            c0[j] = (valid[j] && p > 0) ? 1.0f : inf;
-            c1[j] = valid[j] ? 1.0f : inf;
-            c2[j] = (valid[j] && p < L - 1) ? 1.0f : inf;
+            const uint32_t s_in = (j & 1) ? sel_odd : sel_even;
+            st[0][j] = (valid[j] && p > 0) ? s_in : kSelDropped;
+            st[1][j] = valid[j] ? s_in : kSelDropped;
+            st[2][j] = (valid[j] && p < L - 1) ? s_in : kSelDropped;
+            sx[j] = valid[j] ? s_in : kSelZero;
         }
         const uint32_t line_b = static_cast<uint32_t>(L) * ES;
         const uint32_t lo0 = fwd ? 0u : static_cast<uint32_t>(NL - 1) * line_b;
@@ -267,12 +272,12 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
             for (int j = 0; j < K; ++j) {
                 if constexpr (kRows) {
                     // b = lambda x from the row's windows, also kept for the column scan
-                    bv[j] = window_elem<T, K, NW>(lbuf[d], j, sel_even, sel_odd) *
-                            window_elem<T, K, NW>(xbuf[d], j, sel_even, sel_odd);
+                    bv[j] = window_elem<T, K, NW>(lbuf[d], j, sx[j], sx[j]) *
+                            window_elem<T, K, NW>(xbuf[d], j, sx[j], sx[j]);
                 }
-                s0v[j] = window_elem<T, K, NW>(tbuf[d][0], j, sel_even, sel_odd) * kNegLog2e;
-                s1v[j] = window_elem<T, K, NW>(tbuf[d][1], j, sel_even, sel_odd) * kNegLog2e;
-                s2v[j] = window_elem<T, K, NW>(tbuf[d][2], j, sel_even, sel_odd) * kNegLog2e;
+                s0v[j] = window_elem<T, K, NW>(tbuf[d][0], j, st[0][j], st[0][j]) * kNegLog2e;
+                s1v[j] = window_elem<T, K, NW>(tbuf[d][1], j, st[1][j], st[1][j]) * kNegLog2e;
+                s2v[j] = window_elem<T, K, NW>(tbuf[d][2], j, st[2][j], st[2][j]) * kNegLog2e;
             }
             // breadth first over the 3 K taps: each dependent operation finds
             // its operand several instructions back
@@ -284,9 +289,9 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
             }
 #pragma unroll
             for (int j = 0; j < K; ++j) {
-                s0v[j] += c0[j];
-                s1v[j] += c1[j];
-                s2v[j] += c2[j];
+                s0v[j] += 1.0f;
+                s1v[j] += 1.0f;
+                s2v[j] += 1.0f;
             }
 #pragma unroll
             for (int j = 0; j < K; ++j) {

@@ -111,10 +111,6 @@ __device__ __forceinline__ float row_next(float v) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Selector of v_perm that yields 0xff000000 = -2^127: the logit of a dropped
-// tap or of a slot past the line end (sigmoid exactly 0).
-constexpr uint32_t kSelDropped = 0x0d0c0c0cu;
-
 // K: positions a lane; R = (L - 1) mod K; D: steps a block (a multiple of K),
 // also the number of lines of taps prefetched ahead.
 template <int K, int R, int D>

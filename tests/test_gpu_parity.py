@@ -115,6 +115,26 @@ def test_prop2d_quad_sides(L):
                  "%dx%d bf16" % (L, L))
 
 
+# The quad kernel is persistent: it launches as many workgroups as LDS lets
+# reside at once (one plane each) and each takes every G-th plane after its
+# first.  Plane counts above that limit give some workgroups two planes and
+# others one; the oracle checks sampled planes of both rounds.
+PERSISTENT_CASES = [(16, 19, 1000), (34, 5, 1000), (50, 3, 700), (64, 2, 650), (74, 3, 370), (80, 2, 410)]
+
+
+@pytest.mark.parametrize("L,B,C", PERSISTENT_CASES)
+def test_prop2d_quad_planes_beyond_one_round(L, B, C):
+    say("prop2d quad persistent", L, B, C)
+    p = _problem(B, C, L, L, 7 + L, "bf16")
+    y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    for (b, c) in _sampled_planes(B, C, k=10):
+        sl = lambda t: t[b:b + 1, c:c + 1]
+        r = oracle.prop2d(sl(p["x"]), sl(p["lam"]), sl(p["u"]), p["w"][:, b:b + 1, c:c + 1])
+        assert_close(_np(sl(y)), r, RTOL["bf16"], "%dx%d plane (%d,%d)" % (L, L, b, c))
+
+
 @pytest.mark.parametrize("H,W", WIDE_SHAPES)
 def test_prop2d_wide_fp32_shapes(H, W):
     say("prop2d wide", H, W)
