@@ -45,15 +45,18 @@
  *
  * Ownership: every pointer is a device pointer owned by the caller; the
  * library keeps no pointer after a call returns and allocates no device
- * memory.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * memory at call time (its one static device buffer, 64 MiB per GPU, exists
+ * from library load and serves gspn_prop2d_4dir_ex_backward_noalloc only).
+ * Work is enqueued on `stream` (a hipStream_t; NULL = the null
  * stream) and the call returns without synchronising.
  *
  * Errors: every argument is validated on the host before anything is
  * enqueued; on any error the call returns a non-zero gspn_status, enqueues
  * nothing and leaves every output untouched.  GSPN_ERR_HIP reports a failed
  * launch.  The library never prints, aborts or throws, keeps no mutable
- * global state other than one-time device attribute queries, and may be
- * called from several host threads.  Non-finite inputs propagate by IEEE
+ * global state other than one-time device attribute and symbol-address
+ * queries (and the static scratch buffer's contents), and may be called from
+ * several host threads.  Non-finite inputs propagate by IEEE
  * rules; the results of a plane holding a non-finite input are unspecified
  * but confined to that plane.
  * ------------------------------------------------------------------------
@@ -67,7 +70,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 5
+#define GSPN_ABI_VERSION 6
 
 /* Longest line (H or W) any entry point accepts. */
 #define GSPN_MAX_LINE 8192
@@ -82,7 +85,9 @@ typedef enum {
     GSPN_ERR_ALIGN = 5,  /* a pointer is not aligned to its element size        */
     GSPN_ERR_ALIAS = 6,  /* an output overlaps an input                         */
     GSPN_ERR_VALUE = 7,  /* eps is not finite and > 0, or a flag is not 0/1     */
-    GSPN_ERR_HIP = 8     /* the HIP runtime reported an error                   */
+    GSPN_ERR_HIP = 8,    /* the HIP runtime reported an error                   */
+    GSPN_ERR_SCRATCH = 9 /* the problem needs more than the static scratch
+                            buffer (gspn_prop2d_4dir_ex_backward_noalloc)      */
 } gspn_status;
 
 typedef enum { GSPN_FP32 = 0, GSPN_BF16 = 1 } gspn_dtype;
@@ -230,6 +235,32 @@ int gspn_prop2d_4dir_ex_backward(const void* x, const void* lam, const void* u,
  * none), or -1 if it does not accept them. */
 int64_t gspn_prop2d_4dir_ex_backward_workspace(int64_t B, int64_t C, int64_t groups, int64_t H,
                                                int64_t W);
+
+/*
+ * gspn_prop2d_4dir_ex_backward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results, layouts and errors, minus the
+ * workspace: the kernels use the library's static device buffer instead
+ * (gspn_noalloc_scratch_bytes() = 64 MiB on each GPU, held from library load
+ * until the process ends).  A problem whose workspace
+ * (gspn_prop2d_4dir_ex_backward_workspace) exceeds that returns
+ * GSPN_ERR_SCRATCH and enqueues nothing.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); its first call on a
+ * device looks up that device's buffer address once.
+ * Every call on one GPU shares that GPU's buffer: calls whose work overlaps
+ * in time on one GPU (two streams, or two host threads without ordering)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * The buffer keeps the last call's contents; nothing reads them before
+ * writing them.
+ */
+int gspn_prop2d_4dir_ex_backward_noalloc(const void* x, const void* lam, const void* u,
+                                         const void* w_raw4, int64_t groups, int64_t k_chunk,
+                                         const void* gy, float eps, void* gx, void* glam,
+                                         void* gu, void* gw4, int dtype, int64_t B, int64_t C,
+                                         int64_t H, int64_t W, void* stream);
+
+/* Size of the static scratch buffer (bytes per GPU). */
+int64_t gspn_noalloc_scratch_bytes(void);
 
 /*
  * Latent-space propagation sublayer (paper §5.1, a more efficient ViT block:

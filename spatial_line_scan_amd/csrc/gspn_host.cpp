@@ -45,6 +45,62 @@ bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GSPN_OK : GSPN_ERR_HIP; }
 
+// Shared by gspn_prop2d_4dir_ex_backward (caller's workspace) and its
+// _noalloc variant (scratch: the library's static buffer, looked up after
+// validation).
+int ex_backward(const void* x, const void* lam, const void* u, const void* w_raw4,
+                int64_t groups, int64_t k_chunk, const void* gy, float eps, void* gx,
+                void* glam, void* gu, void* gw4, void* workspace, int64_t workspace_bytes,
+                bool scratch, int dtype, int64_t B, int64_t C, int64_t H, int64_t W,
+                void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
+    if (int s = check_dims(B, C, H, W, 12)) return s;
+    if (H > gspn::prop2d_backward_max_line() || W > gspn::prop2d_backward_max_line())
+        return GSPN_ERR_SHAPE;
+    if (groups < 1 || groups > C || C % groups != 0) return GSPN_ERR_SHAPE;
+    if (k_chunk < 1) return GSPN_ERR_VALUE;
+    if (!valid_eps(eps)) return GSPN_ERR_VALUE;
+    if (!x || !lam || !u || !w_raw4 || !gy || !gx || !glam || !gu || !gw4) return GSPN_ERR_NULL;
+    const int64_t need = gspn::prop2d_backward_workspace_bytes(B * C, H, W, C / groups);
+    if (scratch) {
+        if (need > gspn::noalloc_scratch_bytes()) return GSPN_ERR_SCRATCH;
+    } else {
+        if (need > 0 && !workspace) return GSPN_ERR_NULL;
+        if (workspace_bytes < 0 || (need > 0 && workspace_bytes < need)) return GSPN_ERR_SHAPE;
+    }
+    const void* ptrs[] = {x, lam, u, w_raw4, gy, gx, glam, gu, gw4};
+    for (const void* p : ptrs)
+        if (!aligned(p, dtype)) return GSPN_ERR_ALIGN;
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u)) return GSPN_ERR_ALIGN;
+    const int64_t n = B * C * H * W * elem_size(dtype);
+    const int64_t taps = 12 * B * groups * H * W * elem_size(dtype);
+    const void* ins[] = {x, lam, u, w_raw4, gy};
+    const int64_t in_bytes[] = {n, n, n, taps, n};
+    void* outs[] = {gx, glam, gu, gw4};
+    const int64_t out_bytes[] = {n, n, n, taps};
+    // the static scratch buffer cannot overlap a caller's buffer: only a
+    // caller's workspace is checked
+    const bool check_ws = !scratch && need > 0;
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 5; ++i)
+            if (overlap(outs[o], out_bytes[o], ins[i], in_bytes[i])) return GSPN_ERR_ALIAS;
+        for (int o2 = 0; o2 < o; ++o2)
+            if (overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return GSPN_ERR_ALIAS;
+        if (check_ws && overlap(outs[o], out_bytes[o], workspace, need)) return GSPN_ERR_ALIAS;
+    }
+    if (check_ws)
+        for (int i = 0; i < 5; ++i)
+            if (overlap(workspace, need, ins[i], in_bytes[i])) return GSPN_ERR_ALIAS;
+    if (scratch && need > 0 && gspn::noalloc_scratch(&workspace) != hipSuccess)
+        return GSPN_ERR_HIP;
+    gspn::PropOpts opts;
+    opts.cpg = C / groups;
+    opts.k_chunk = std::min<int64_t>(k_chunk, std::max(H, W));
+    return launch_status(gspn::launch_prop2d_backward(
+        x, lam, u, w_raw4, gy, eps, gx, glam, gu, gw4, need > 0 ? workspace : nullptr, dtype,
+        B * C, H, W, opts, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -62,6 +118,8 @@ const char* gspn_status_str(int status) {
         case GSPN_ERR_ALIAS: return "GSPN_ERR_ALIAS: output overlaps an input";
         case GSPN_ERR_VALUE: return "GSPN_ERR_VALUE: eps must be finite and > 0, flags 0 or 1";
         case GSPN_ERR_HIP: return "GSPN_ERR_HIP: HIP runtime error";
+        case GSPN_ERR_SCRATCH:
+            return "GSPN_ERR_SCRATCH: the problem needs more scratch than the library's static buffer";
         default: return "GSPN: unknown status";
     }
 }
@@ -153,44 +211,20 @@ int gspn_prop2d_4dir_ex_backward(const void* x, const void* lam, const void* u,
                                  const void* gy, float eps, void* gx, void* glam, void* gu,
                                  void* gw4, void* workspace, int64_t workspace_bytes, int dtype,
                                  int64_t B, int64_t C, int64_t H, int64_t W, void* stream) {
-    if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
-    if (int s = check_dims(B, C, H, W, 12)) return s;
-    if (H > gspn::prop2d_backward_max_line() || W > gspn::prop2d_backward_max_line())
-        return GSPN_ERR_SHAPE;
-    if (groups < 1 || groups > C || C % groups != 0) return GSPN_ERR_SHAPE;
-    if (k_chunk < 1) return GSPN_ERR_VALUE;
-    if (!valid_eps(eps)) return GSPN_ERR_VALUE;
-    if (!x || !lam || !u || !w_raw4 || !gy || !gx || !glam || !gu || !gw4) return GSPN_ERR_NULL;
-    const int64_t need = gspn::prop2d_backward_workspace_bytes(B * C, H, W, C / groups);
-    if (need > 0 && !workspace) return GSPN_ERR_NULL;
-    if (workspace_bytes < 0 || (need > 0 && workspace_bytes < need)) return GSPN_ERR_SHAPE;
-    const void* ptrs[] = {x, lam, u, w_raw4, gy, gx, glam, gu, gw4};
-    for (const void* p : ptrs)
-        if (!aligned(p, dtype)) return GSPN_ERR_ALIGN;
-    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u)) return GSPN_ERR_ALIGN;
-    const int64_t n = B * C * H * W * elem_size(dtype);
-    const int64_t taps = 12 * B * groups * H * W * elem_size(dtype);
-    const void* ins[] = {x, lam, u, w_raw4, gy};
-    const int64_t in_bytes[] = {n, n, n, taps, n};
-    void* outs[] = {gx, glam, gu, gw4};
-    const int64_t out_bytes[] = {n, n, n, taps};
-    for (int o = 0; o < 4; ++o) {
-        for (int i = 0; i < 5; ++i)
-            if (overlap(outs[o], out_bytes[o], ins[i], in_bytes[i])) return GSPN_ERR_ALIAS;
-        for (int o2 = 0; o2 < o; ++o2)
-            if (overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return GSPN_ERR_ALIAS;
-        if (need > 0 && overlap(outs[o], out_bytes[o], workspace, need)) return GSPN_ERR_ALIAS;
-    }
-    if (need > 0)
-        for (int i = 0; i < 5; ++i)
-            if (overlap(workspace, need, ins[i], in_bytes[i])) return GSPN_ERR_ALIAS;
-    gspn::PropOpts opts;
-    opts.cpg = C / groups;
-    opts.k_chunk = std::min<int64_t>(k_chunk, std::max(H, W));
-    return launch_status(gspn::launch_prop2d_backward(
-        x, lam, u, w_raw4, gy, eps, gx, glam, gu, gw4, need > 0 ? workspace : nullptr, dtype,
-        B * C, H, W, opts, static_cast<hipStream_t>(stream)));
+    return ex_backward(x, lam, u, w_raw4, groups, k_chunk, gy, eps, gx, glam, gu, gw4, workspace,
+                       workspace_bytes, false, dtype, B, C, H, W, stream);
 }
+
+int gspn_prop2d_4dir_ex_backward_noalloc(const void* x, const void* lam, const void* u,
+                                         const void* w_raw4, int64_t groups, int64_t k_chunk,
+                                         const void* gy, float eps, void* gx, void* glam,
+                                         void* gu, void* gw4, int dtype, int64_t B, int64_t C,
+                                         int64_t H, int64_t W, void* stream) {
+    return ex_backward(x, lam, u, w_raw4, groups, k_chunk, gy, eps, gx, glam, gu, gw4, nullptr, 0,
+                       true, dtype, B, C, H, W, stream);
+}
+
+int64_t gspn_noalloc_scratch_bytes(void) { return gspn::noalloc_scratch_bytes(); }
 
 int gspn_prop2d_4dir_backward(const void* x, const void* lam, const void* u,
                               const void* w_raw4, const void* gy, float eps, void* gx,

@@ -128,6 +128,11 @@ hipError_t launch_conv1x1_params(const void* z, void* zt, const void* w_param, i
 hipError_t launch_conv1x1_up(const void* yc, const void* p_up, int64_t B, int64_t Cc, int64_t C,
                              int64_t H, int64_t W, void* y_tok, hipStream_t stream);
 
+// The library's static device scratch (gspn_noalloc.hip): its size, and its
+// address on the current device (looked up once per device).
+int64_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
+
 // Largest plane (H * W pixels) gspn_prop2d_4dir accepts for an element type.
 int64_t prop2d_max_plane(int dtype, int64_t H, int64_t W);
 

@@ -28,7 +28,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgspn.so
 _lib = None
 
 _STATUS_EXC = {1: ValueError, 2: ValueError, 3: TypeError, 4: ValueError, 5: ValueError,
-               6: ValueError, 7: ValueError, 8: RuntimeError}
+               6: ValueError, 7: ValueError, 8: RuntimeError, 9: ValueError}
 
 
 def library_path() -> str:
@@ -72,6 +72,11 @@ def lib():
         L.gspn_prop2d_4dir_ex_backward.restype = ci
         L.gspn_prop2d_4dir_ex_backward_workspace.argtypes = [i64, i64, i64, i64, i64]
         L.gspn_prop2d_4dir_ex_backward_workspace.restype = i64
+        L.gspn_prop2d_4dir_ex_backward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, vp, cf, vp,
+                                                           vp, vp, vp, ci, i64, i64, i64, i64, vp]
+        L.gspn_prop2d_4dir_ex_backward_noalloc.restype = ci
+        L.gspn_noalloc_scratch_bytes.argtypes = []
+        L.gspn_noalloc_scratch_bytes.restype = i64
         _lib = L
     return _lib
 
@@ -266,6 +271,42 @@ def prop2d_4dir_ex_backward(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor,
                                                   _p(gu), _p(gw4), ws_ptr, ws_bytes, _dtype_code(x),
                                                   B, C, H, W, _stream(x)))
     return gx, glam, gu, gw4
+
+
+def prop2d_4dir_ex_backward_noalloc(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor,
+                                    w4: torch.Tensor, gy: torch.Tensor, groups: int,
+                                    k_chunk: int = 1, eps: float = 1e-6, out=None):
+    """prop2d_4dir_ex_backward through the library's allocation-free entry
+    point: its kernels use the library's static device scratch (at most
+    noalloc_scratch_bytes() of workspace, else ValueError).  `out` =
+    (gx, glam, gu, gw4) preallocated by the caller; allocated here with torch
+    when None (the library call itself allocates nothing).  Calls overlapping
+    in time on one GPU race on the shared scratch."""
+    _same(x, lam, u, w4, gy)
+    if x.dim() != 4 or lam.shape != x.shape or u.shape != x.shape or gy.shape != x.shape:
+        raise ValueError("x, lam, u, gy must share one [B, C, H, W] shape")
+    B, C, H, W = x.shape
+    if groups < 1 or C % groups:
+        raise ValueError("groups must divide C")
+    if w4.numel() != 12 * B * groups * H * W:
+        raise ValueError("w4 must hold 4*B*groups*3*H*W elements")
+    if out is None:
+        out = (torch.empty_like(x), torch.empty_like(x), torch.empty_like(x), torch.empty_like(w4))
+    gx, glam, gu, gw4 = out
+    _same(x, gx, glam, gu, gw4)
+    if gx.shape != x.shape or glam.shape != x.shape or gu.shape != x.shape or \
+            gw4.numel() != w4.numel():
+        raise ValueError("out tensors must have the shapes of x, x, x, w4")
+    with torch.cuda.device(x.device):
+        _check(lib().gspn_prop2d_4dir_ex_backward_noalloc(
+            _p(x), _p(lam), _p(u), _p(w4), int(groups), int(k_chunk), _p(gy), float(eps), _p(gx),
+            _p(glam), _p(gu), _p(gw4), _dtype_code(x), B, C, H, W, _stream(x)))
+    return gx, glam, gu, gw4
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the library's static device scratch (per GPU)."""
+    return lib().gspn_noalloc_scratch_bytes()
 
 
 class Prop2d4Dir(torch.autograd.Function):

@@ -16,7 +16,7 @@ from spatial_line_scan_amd import gspn
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                       "gspn.h")
 
-OK, NULL, SHAPE, DTYPE, DIR, ALIGN, ALIAS, VALUE, HIP = range(9)
+OK, NULL, SHAPE, DTYPE, DIR, ALIGN, ALIAS, VALUE, HIP, SCRATCH = range(10)
 A = 0x7F0000000000          # fake 16-byte-aligned device addresses, far apart
 STEP = 0x10000000000
 
@@ -44,15 +44,17 @@ def test_exports_every_declared_symbol(L):
                          "gspn_prop2d_4dir_backward", "gspn_prop2d_4dir_backward_workspace",
                          "gspn_prop2d_4dir_ex", "gspn_latent_sublayer",
                          "gspn_latent_sublayer_workspace", "gspn_prop2d_4dir_ex_backward",
-                         "gspn_prop2d_4dir_ex_backward_workspace"}
+                         "gspn_prop2d_4dir_ex_backward_workspace",
+                         "gspn_prop2d_4dir_ex_backward_noalloc", "gspn_noalloc_scratch_bytes"}
     for s in syms:
         assert hasattr(L, s), s
 
 
 def test_version_and_status_strings(L):
-    assert L.gspn_abi_version() == 5
-    for s in range(9):
+    assert L.gspn_abi_version() == 6
+    for s in range(10):
         assert L.gspn_status_str(s).decode().startswith("GSPN")
+    assert "scratch" in L.gspn_status_str(SCRATCH).decode()
     assert L.gspn_status_str(12345)
 
 
@@ -253,6 +255,44 @@ def test_ex_backward_rejects_bad_arguments(L):
     ptrs = [P(j) for j in range(9)]
     ptrs[8] = ctypes.c_void_p(A + 3 * STEP + 12 * 2 * 1 * 35 * 4 - 4)
     assert exb(L, groups=1, ptrs=ptrs, ws=P(10), ws_bytes=need) == ALIAS   # last word of 1-group taps
+
+
+def exb_noalloc(L, groups=3, k=1, dt=0, B=2, C=3, H=5, W=7, ptrs=None):
+    p = list(ptrs) if ptrs else [P(i) for i in range(9)]
+    return L.gspn_prop2d_4dir_ex_backward_noalloc(p[0], p[1], p[2], p[3], groups, k, p[4], 1e-6,
+                                                  p[5], p[6], p[7], p[8], dt, B, C, H, W, None)
+
+
+def test_noalloc_scratch_limit(L):
+    # the static scratch is 64 MiB per GPU; a problem whose workspace exceeds
+    # it is rejected before anything is enqueued, one that fits is not
+    # rejected for its size (not called here: it would launch)
+    cap = L.gspn_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(32, 64, 64, 74, 74) > cap   # latent1k batch
+    assert exb_noalloc(L, B=32, C=64, groups=64, H=74, W=74) == SCRATCH
+    assert exb_noalloc(L, B=32, C=64, groups=1, H=74, W=74) == SCRATCH
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 64, 64, 74, 74) <= cap
+
+
+def test_noalloc_rejects_bad_arguments(L):
+    # same validation as gspn_prop2d_4dir_ex_backward, minus the workspace
+    assert exb_noalloc(L, groups=2) == SHAPE
+    assert exb_noalloc(L, k=0) == VALUE
+    assert exb_noalloc(L, dt=2) == DTYPE
+    assert exb_noalloc(L, B=0) == SHAPE
+    ptrs = [P(j) for j in range(9)]
+    ptrs[2] = None
+    assert exb_noalloc(L, ptrs=ptrs) == NULL
+    ptrs = [P(j) for j in range(9)]
+    ptrs[6] = ctypes.c_void_p(A + 6 * STEP + 2)
+    assert exb_noalloc(L, ptrs=ptrs) == ALIGN
+    ptrs = [P(j) for j in range(9)]
+    ptrs[8] = P(3)
+    assert exb_noalloc(L, ptrs=ptrs) == ALIAS                # gw4 over w_raw4
+    ptrs = [P(j) for j in range(9)]
+    ptrs[5] = P(4)
+    assert exb_noalloc(L, ptrs=ptrs) == ALIAS                # gx over gy
 
 
 def ex(L, groups=3, k=1, eps=1e-6, dt=0, B=2, C=3, H=5, W=7, y=None):
