@@ -9,6 +9,9 @@ namespace gspn {
 
 // LDS a single workgroup may address on gfx950 (160 KiB per CU).
 constexpr int64_t kLdsBytes = 160 * 1024;
+// Plane count up to which a launch of one workgroup a plane leaves CUs idle
+// (MI355X: 256 CUs).
+constexpr int64_t kFewPlanes = 256;
 
 // Options of the four-direction propagation: channels per tap group (taps
 // are [4][planes / cpg][3][..][..]; tap plane of plane p is p / cpg) and the
@@ -57,6 +60,12 @@ hipError_t launch_prop2d_phase(const void* x, const void* lam, const void* u, co
 
 // Fast path for square bf16 planes with even sides up to 80: one wavefront
 // per plane scans all four directions at once (gspn_prop2d_quad.hip).
+bool prop2d_duo_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                         const void* x, const void* lam, const void* u, const void* w4,
+                         const void* y);
+hipError_t launch_prop2d_duo(const void* x, const void* lam, const void* u, const void* w4,
+                             float eps, void* y, int64_t planes, int64_t L, const PropOpts& o,
+                             hipStream_t stream);
 bool prop2d_quad_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                           const void* x, const void* lam, const void* u, const void* w4,
                           const void* y);

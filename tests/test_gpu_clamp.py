@@ -90,7 +90,7 @@ EPS = {"deep": 1e-6, "eps": 1e-3}
 FWD_CASES = [(74, 74, "bf16", 8, 128), (30, 66, "bf16", 8, 128), (148, 148, "bf16", 1, 8),
              (40, 30, "bf16", 2, 4), (74, 74, "fp32", 1, 8), (9, 11, "fp32", 1, 4),
              (120, 120, "fp32", 1, 4), (256, 252, "fp32", 1, 4), (27, 27, "bf16", 2, 4),
-             (37, 35, "bf16", 1, 4)]
+             (37, 35, "bf16", 1, 4), (74, 74, "bf16", 2, 4), (90, 90, "bf16", 1, 4)]
 
 
 def _sampled(B, C):
@@ -190,7 +190,8 @@ def test_scan_dir_edge_logits_and_accumulate(dtype, mode):
 # A non-finite value in plane p + 1 (its first row of x and lambda, and its
 # taps) must leave plane p exactly as the oracle computes it.
 CONFINE_CASES = [(74, 74, "bf16", 8, 128), (30, 66, "bf16", 8, 128), (40, 30, "bf16", 1, 4),
-                 (74, 74, "fp32", 1, 4), (120, 120, "fp32", 1, 4), (27, 27, "bf16", 1, 4)]
+                 (74, 74, "fp32", 1, 4), (120, 120, "fp32", 1, 4), (27, 27, "bf16", 1, 4),
+                 (74, 74, "bf16", 1, 4), (90, 90, "bf16", 1, 4)]
 
 
 @pytest.mark.parametrize("H,W,dtype,B,C", CONFINE_CASES)

@@ -47,12 +47,14 @@ def test_prop2d_small_workloads_all_seeds(name):
         assert_close(_np(y), r, RTOL[wl.dtype], "%s seed %d" % (name, seed))
 
 
-# bf16 planes with even sides up to 160 take the one-wavefront phase kernel
-# (K = 1..5 positions a lane: sides up to 32, 64, 96, 128, 160); fp32 ones up
-# to 96 the two-wavefront kernel, and fp32 ones with sides up to 256 that are
-# multiples of 4 the one-launch-per-direction kernel (y accumulates; K = 1..4
-# positions a lane over 64 lanes; columns in strips of 16); the rest the
-# general kernel.
+# Forward dispatch.  bf16: square planes with even sides up to 80 take the
+# four-directions-a-wavefront kernel (K = 1..5 positions a lane in 16-lane
+# rows), except that sides 66..80 with at most 256 planes, and sides 82..96,
+# take the two-wavefronts-a-plane kernel (K = 1..3 over 32 lanes); other
+# planes with even sides up to 160 take the rows-then-columns phase kernel.
+# fp32: planes up to 96 the two-wavefront pair kernel, planes with sides up
+# to 256 that are multiples of 4 the one-launch-per-direction kernel (y
+# accumulates; columns in strips of 32).  The rest take the general kernel.
 EDGE_SHAPES = [(1, 1), (1, 2), (2, 1), (2, 2), (3, 5), (5, 3), (1, 74), (74, 1), (63, 64), (64, 65),
                (65, 63), (74, 74), (127, 33), (13, 148), (148, 148), (256, 7),
                (98, 98), (128, 128), (130, 160), (160, 2), (2, 160), (158, 126), (96, 128), (162, 40)]
@@ -100,7 +102,8 @@ def test_prop2d_phase_one_wave_form(H, W):
 
 # square bf16 planes with even sides up to 80 take the kernel that scans the
 # four directions at once (16 lanes a direction, K = 1 .. 5 positions a lane);
-# sides cover every K and every value of (L - 1) mod K it is built for
+# sides cover every K and every value of (L - 1) mod K it is built for.  Sides
+# above 64 take it only with more than 256 planes.
 QUAD_SIDES = [2, 4, 6, 14, 16, 18, 30, 32, 34, 36, 38, 46, 48, 50, 52, 62, 64, 66, 68, 70, 72, 74,
               76, 78, 80]
 
@@ -108,23 +111,53 @@ QUAD_SIDES = [2, 4, 6, 14, 16, 18, 30, 32, 34, 36, 38, 46, 48, 50, 52, 62, 64, 6
 @pytest.mark.parametrize("L", QUAD_SIDES)
 def test_prop2d_quad_sides(L):
     say("prop2d quad", L)
-    p = _problem(3, 5, L, L, 101 + L, "bf16")
+    B, C = (3, 5) if L <= 64 else (3, 90)
+    p = _problem(B, C, L, L, 101 + L, "bf16")
     y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
     torch.cuda.synchronize()
     assert_close(_np(y), oracle.prop2d(p["x"], p["lam"], p["u"], p["w"]), RTOL["bf16"],
                  "%dx%d bf16" % (L, L))
 
 
-# The quad kernel is persistent: it launches as many workgroups as LDS lets
-# reside at once (one plane each) and each takes every G-th plane after its
-# first.  Plane counts above that limit give some workgroups two planes and
-# others one; the oracle checks sampled planes of both rounds.
+# square bf16 planes with even sides 66..80 and at most 256 planes, and sides
+# 82..96, take the kernel with two wavefronts a plane (rows in one, columns in
+# the other, 32 lanes a direction, K = 3); the sides cover every (L - 1) mod 3
+DUO_SIDES = [66, 68, 70, 74, 80, 82, 84, 86, 90, 94, 96]
+
+
+@pytest.mark.parametrize("L", DUO_SIDES)
+def test_prop2d_duo_sides(L):
+    say("prop2d duo", L)
+    p = _problem(2, 5, L, L, 301 + L, "bf16")
+    y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
+    torch.cuda.synchronize()
+    assert_close(_np(y), oracle.prop2d(p["x"], p["lam"], p["u"], p["w"]), RTOL["bf16"],
+                 "%dx%d bf16" % (L, L))
+
+
+def test_prop2d_duo_and_quad_agree_bitwise():
+    # both kernels add each pixel's four directional terms in step order (the
+    # terms of a step's meeting pixels after the scan), so the plane a small
+    # launch computes with two wavefronts equals the one a full launch computes
+    # with one
+    say("prop2d duo vs quad 74x74")
+    p = _problem(4, 80, 74, 74, 77, "bf16")            # 320 planes: the quad kernel
+    y_all = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
+    sl = lambda t: t[1:2].contiguous()                   # 80 planes: the duo kernel
+    y_one = gspn.prop2d_4dir(sl(p["x"]), sl(p["lam"]), sl(p["u"]), p["w"][:, 1:2].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y_all[1:2], y_one)
+
+
+# Plane counts above what the CUs hold at once (LDS allows four 74 x 74
+# planes a CU) run in several rounds of workgroups; the oracle checks sampled
+# planes of every round.
 PERSISTENT_CASES = [(16, 19, 1000), (34, 5, 1000), (50, 3, 700), (64, 2, 650), (74, 3, 370), (80, 2, 410)]
 
 
 @pytest.mark.parametrize("L,B,C", PERSISTENT_CASES)
 def test_prop2d_quad_planes_beyond_one_round(L, B, C):
-    say("prop2d quad persistent", L, B, C)
+    say("prop2d quad rounds", L, B, C)
     p = _problem(B, C, L, L, 7 + L, "bf16")
     y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
     torch.cuda.synchronize()
