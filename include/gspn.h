@@ -53,10 +53,11 @@
  * Errors: every argument is validated on the host before anything is
  * enqueued; on any error the call returns a non-zero gspn_status, enqueues
  * nothing and leaves every output untouched.  GSPN_ERR_HIP reports a failed
- * launch.  The library never prints, aborts or throws, keeps no mutable
- * global state other than one-time device attribute and symbol-address
- * queries (and the static scratch buffer's contents), and may be called from
- * several host threads.  Non-finite inputs propagate by IEEE
+ * launch.  The library never prints, aborts or throws, and may be called
+ * from several host threads.  Its only global state is remembered results
+ * of one-time queries (device attributes, the static scratch buffer's
+ * address, the sublayer's hipBLASLt handle and algorithm per shape) and the
+ * static scratch buffer's contents; none of it changes a result.  Non-finite inputs propagate by IEEE
  * rules; the results of a plane holding a non-finite input are unspecified
  * but confined to that plane.
  * ------------------------------------------------------------------------
@@ -280,9 +281,14 @@ int64_t gspn_noalloc_scratch_bytes(void);
  *             scratch; contents on return are unspecified.
  *   All pointers 16-byte aligned; y_tok and workspace must not overlap any
  *   input or each other.  The projections run in hipBLASLt (fp32
- *   accumulation; bf16 storage rounds every intermediate to bf16), one
- *   algorithm per shape chosen on first use, so repeated calls give
- *   bitwise equal results.  Errors as gspn_prop2d_4dir_ex, plus
+ *   accumulation; bf16 storage rounds every intermediate to bf16).  Per
+ *   shape the GEMM algorithm is the library heuristic's first candidate that
+ *   succeeds and fits the scratch: nothing is timed, the call never waits
+ *   on the stream, and every process runs the same kernels, so results
+ *   repeat bitwise.  The first call on a device creates that device's
+ *   hipBLASLt handle, and the first call for a shape queries the heuristic;
+ *   both are remembered for the process (so make those first calls outside
+ *   stream capture).  Errors as gspn_prop2d_4dir_ex, plus
  *   GSPN_ERR_SHAPE for a workspace that is too small or C outside
  *   [1, 65536].
  */

@@ -147,10 +147,11 @@ hipError_t gemm(int dtype, const GemmShape& g, const void* A, const void* B, voi
         cleanup();
         return blas_error(s);
     }
-    // One algorithm per shape, chosen on first use: the library's best
-    // candidates are each timed on this call's operands (a few runs, HIP
-    // events on `stream`) and the fastest is kept, so that later calls with
-    // the same shape run the same kernel and results repeat bitwise.
+    // One algorithm per shape: the heuristic's first candidate that reports
+    // success and fits the workspace.  The heuristic is a function of the
+    // device, the shape and the library version, so every process runs the
+    // same kernel for a shape and results repeat bitwise; nothing is timed and
+    // nothing waits on the stream.  The choice is remembered per shape.
     const float one = 1.0f, zero = 0.0f;
     hipblasLtMatmulAlgo_t algo;
     {
@@ -162,56 +163,26 @@ hipError_t gemm(int dtype, const GemmShape& g, const void* A, const void* B, voi
             if (s == HIPBLAS_STATUS_SUCCESS)
                 s = hipblasLtMatmulPreferenceSetAttribute(
                     pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb));
-            constexpr int kCandidates = 12;
+            constexpr int kCandidates = 8;
             hipblasLtMatmulHeuristicResult_t res[kCandidates];
             int found = 0;
             if (s == HIPBLAS_STATUS_SUCCESS)
                 s = hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, ld, ld, pref, kCandidates,
                                                     res, &found);
-            if (s != HIPBLAS_STATUS_SUCCESS || found < 1) {
+            if (s != HIPBLAS_STATUS_SUCCESS) {
                 cleanup();
-                return s != HIPBLAS_STATUS_SUCCESS ? blas_error(s) : hipErrorNotSupported;
+                return blas_error(s);
             }
-            int best = 0;
-            if (found > 1) {
-                hipEvent_t e0, e1;
-                if ((he = hipEventCreate(&e0)) != hipSuccess) {
-                    cleanup();
-                    return he;
-                }
-                if ((he = hipEventCreate(&e1)) != hipSuccess) {
-                    (void)hipEventDestroy(e0);
-                    cleanup();
-                    return he;
-                }
-                float best_ms = 0.0f;
-                for (int a = 0; a < found; ++a) {
-                    if (res[a].state != HIPBLAS_STATUS_SUCCESS ||
-                        res[a].workspaceSize > static_cast<size_t>(kBlasWorkspace))
-                        continue;
-                    // one untimed run (first-use costs), then three timed
-                    hipblasStatus_t r = hipblasLtMatmul(h, desc, &one, A, la, B, lb, &zero, D, ld,
-                                                        D, ld, &res[a].algo, ws, kBlasWorkspace,
-                                                        stream);
-                    if (r != HIPBLAS_STATUS_SUCCESS) continue;
-                    if (hipEventRecord(e0, stream) != hipSuccess) continue;
-                    for (int rep = 0; rep < 3 && r == HIPBLAS_STATUS_SUCCESS; ++rep)
-                        r = hipblasLtMatmul(h, desc, &one, A, la, B, lb, &zero, D, ld, D, ld,
-                                            &res[a].algo, ws, kBlasWorkspace, stream);
-                    if (r != HIPBLAS_STATUS_SUCCESS || hipEventRecord(e1, stream) != hipSuccess ||
-                        hipEventSynchronize(e1) != hipSuccess)
-                        continue;
-                    float ms = 0.0f;
-                    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) continue;
-                    if (best_ms == 0.0f || ms < best_ms) {
-                        best_ms = ms;
-                        best = a;
-                    }
-                }
-                (void)hipEventDestroy(e0);
-                (void)hipEventDestroy(e1);
+            int pick = -1;
+            for (int a = 0; a < found && pick < 0; ++a)
+                if (res[a].state == HIPBLAS_STATUS_SUCCESS &&
+                    res[a].workspaceSize <= static_cast<size_t>(kBlasWorkspace))
+                    pick = a;
+            if (pick < 0) {
+                cleanup();
+                return hipErrorNotSupported;
             }
-            it = g_algos.emplace(g.key(dtype), res[best].algo).first;
+            it = g_algos.emplace(g.key(dtype), res[pick].algo).first;
         }
         algo = it->second;
     }
