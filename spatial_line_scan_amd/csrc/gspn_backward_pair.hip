@@ -26,7 +26,7 @@
 // barriers).
 //   1. Forward: h line by line (taps normalised in registers, b = lambda x
 //      from the line's windows); every line of h goes to an fp32 LDS plane of
-//      the half.
+//      the wavefront.
 //   2. S pass: S = h_a + h_b per pixel.  Row launch: to the workspace.
 //      Column launch: added to the row launch's S, and gu = gy S written.
 //   3. Adjoint, in reverse scan order.  The transposed products of line i+1
@@ -37,8 +37,8 @@
 //      earlier.
 //   4. G pass: G = g_a + g_b per pixel.  Row launch: to the workspace.
 //      Column launch: added to the row launch's G, and gx, glambda written.
-// Sums run in a fixed order (row pair before column pair, first half before
-// second), so the result is the same on every run.
+// Sums run in a fixed order (row pair before column pair, wavefront 0's
+// direction before wavefront 1's), so the result is the same on every run.
 #include "gspn_device.h"
 #include "gspn_internal.h"
 #include "gspn_lane.h"
@@ -104,8 +104,8 @@ struct PairBwdLayout {
 };
 
 // Tap gradients of one adjoint step go out through LDS: each lane puts the
-// values of its K slots into a staging line per (half, tap), 32 K elements
-// apart so that slots past a line's end land in the padding, and the
+// values of its K slots into a staging line per (wavefront, tap), 64 K
+// elements long so that slots past a line's end land in the padding, and the
 // wavefront then writes the six lines as whole dwords (stores of a few bytes
 // at a 6-byte stride cost far more).  kDrop pushes the offset of an unused
 // dword store past the tensor; the hardware drops it.
@@ -202,13 +202,14 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     const int plane = blockIdx.x;
     const size_t pix0 = static_cast<size_t>(plane) * HW;
 
-    // zero lines (h before a scan's first line) and the dummy words
-    if (tid < 8) lds_at<float>(4u * tid) = 0.0f;
-    // each wavefront's own dummy words: the values that slots past a line's
-    // end leave there (finite, and weighed only by dropped taps) then follow
-    // that wavefront's program order, so even the signs of the zero tap
-    // gradients they touch are the same from run to run
+    // each wavefront zeroes its own dummy words before it uses them: the
+    // values that slots past a line's end leave there (finite, and weighed
+    // only by dropped taps) then follow that wavefront's program order alone,
+    // so even the signs of the zero tap gradients they touch are the same
+    // from run to run
     const uint32_t dum0 = 16u * half;
+    if (lane < 4) lds_at<float>(dum0 + 4u * lane) = 0.0f;
+    // zero lines: h before a scan's first line
     for (int f = tid; f < L; f += NT) {
         if constexpr (kNarrow) {
             lds_at<uint16_t>(lay.a - 2 * L + 2 * f) = 0;
@@ -473,7 +474,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
 
     // ------------------------------------------------------------ adjoint
     {
-        // lanes 0-31 walk their lines NL-1 .. 0, lanes 32-63 walk 0 .. NL-1
+        // wavefront 0 walks its lines NL-1 .. 0, wavefront 1 walks 0 .. NL-1
         const int i0 = fwd ? NL - 1 : 0;
         const uint32_t lo0 = static_cast<uint32_t>(i0) * line_b;
         const uint32_t dlo = fwd ? 0u - line_b : line_b;
@@ -511,7 +512,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 const int hk = 3 * half + f / per_line;
                 const int m = f - (f / per_line) * per_line;
                 const int h = hk / 3, k = hk - 3 * h;
-                const int start = h == 0 ? NL - 1 : 0;      // first adjoint line of that half
+                const int start = h == 0 ? NL - 1 : 0;      // first adjoint line of that wavefront
                 rd[t] = lay.stage + hk * SL * GS + 4 * m;
                 go[t] = static_cast<uint32_t>((((dir0 + h) * planes + plane) * 3 + k) * HW * GS +
                                               start * L * GS + 4 * m);
@@ -522,8 +523,9 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         // adjoint step of the next restart line: its taps read nothing (tap
         // gradient 0) and the line before it receives no adjoint term from it
         int next_restart = fwd ? (NL - 1) - ((NL - 1) / seg) * seg : seg - 1;
-        // LDS: g_i goes to line i (G); h_{i-1} (lanes 0-31) or h_{i+1}
-        // (32-63) is read one step ahead (P), and P of one step is G of the next
+        // LDS: g_i goes to line i (G); h_{i-1} (wavefront 0) or h_{i+1}
+        // (wavefront 1) is read one step ahead (P), and P of one step is G of
+        // the next
         const int dl = fwd ? -L : L;       // values per step
         uint32_t aGH[K], aGL[K], aPH[K], aPL[K];
         int dH[K], dL[K];
