@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 6
+#define GSPN_ABI_VERSION 7
 
 /* Longest line (H or W) any entry point accepts. */
 #define GSPN_MAX_LINE 8192
@@ -166,6 +166,34 @@ int gspn_prop2d_4dir_ex(const void* x, const void* lam, const void* u,
                         const void* w_raw4, int64_t groups, int64_t k_chunk,
                         float eps, void* y, int dtype, int64_t B, int64_t C,
                         int64_t H, int64_t W, void* stream);
+
+/*
+ * gspn_prop2d_4dir_ex with a workspace that lets channels sharing taps share
+ * their normalisation (paper §4.2, channel-shared weights): where the
+ * workspace is used, a first kernel normalises each group's taps once into
+ * it (fp32 weights, the fused sigmoid / sum / clamp / divide with the same
+ * arithmetic) and the scan reads them, instead of every channel normalising
+ * its group's taps again.  Results agree with gspn_prop2d_4dir_ex within
+ * rounding (the weight is formed as s_k * (1 / S) before the products, not
+ * after); each path is deterministic.
+ *   workspace : at least gspn_prop2d_4dir_ex_workspace(...) bytes, 16-byte
+ *               aligned, not overlapping any argument; contents on return
+ *               unspecified.  When that size is 0 the workspace is not used
+ *               (may be NULL) and the call is gspn_prop2d_4dir_ex.
+ * Other arguments, layouts and errors as gspn_prop2d_4dir_ex, plus
+ * GSPN_ERR_SHAPE for a workspace smaller than needed.
+ */
+int gspn_prop2d_4dir_ex_ws(const void* x, const void* lam, const void* u, const void* w_raw4,
+                           int64_t groups, int64_t k_chunk, float eps, void* y, void* workspace,
+                           int64_t workspace_bytes, int dtype, int64_t B, int64_t C, int64_t H,
+                           int64_t W, void* stream);
+
+/* Workspace bytes gspn_prop2d_4dir_ex_ws uses for these sizes: 0 where it
+ * runs as gspn_prop2d_4dir_ex (today: all but bf16 square planes with even
+ * sides up to 80, one segment a scan and at least 2 channels a group), or -1
+ * if the sizes are not accepted. */
+int64_t gspn_prop2d_4dir_ex_workspace(int dtype, int64_t B, int64_t C, int64_t groups, int64_t H,
+                                      int64_t W);
 
 /*
  * Gradient of gspn_prop2d_4dir (the pages report backward kernels, paper text

@@ -45,6 +45,62 @@ bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GSPN_OK : GSPN_ERR_HIP; }
 
+// Workspace the grouped forward uses to normalise each group's taps once
+// (0: the taps are normalised by every channel as it scans).
+int64_t shared_workspace(int dtype, int64_t B, int64_t C, int64_t groups, int64_t H, int64_t W) {
+    gspn::PropOpts o;
+    o.cpg = C / groups;
+    // the eligibility test reads only alignment from these
+    const void* a = reinterpret_cast<const void*>(uintptr_t{256});
+    if (!gspn::prop2d_quad_shared_eligible(dtype, B * C, H, W, o, a, a, a, a, a)) return 0;
+    return gspn::prop2d_quad_shared_workspace_bytes(B * C, H, o.cpg);
+}
+
+// Shared by gspn_prop2d_4dir_ex and gspn_prop2d_4dir_ex_ws (with_ws).
+int ex_forward(const void* x, const void* lam, const void* u, const void* w_raw4, int64_t groups,
+               int64_t k_chunk, float eps, void* y, void* workspace, int64_t workspace_bytes,
+               bool with_ws, int dtype, int64_t B, int64_t C, int64_t H, int64_t W, void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
+    if (int s = check_dims(B, C, H, W, 12)) return s;
+    if (H * W > gspn::prop2d_max_plane(dtype, H, W)) return GSPN_ERR_SHAPE;
+    if (groups < 1 || groups > C || C % groups != 0) return GSPN_ERR_SHAPE;
+    if (k_chunk < 1) return GSPN_ERR_VALUE;
+    if (!valid_eps(eps)) return GSPN_ERR_VALUE;
+    if (!x || !lam || !u || !w_raw4 || !y) return GSPN_ERR_NULL;
+    if (!aligned(x, dtype) || !aligned(lam, dtype) || !aligned(u, dtype) ||
+        !aligned(w_raw4, dtype) || !aligned(y, dtype))
+        return GSPN_ERR_ALIGN;
+    const int64_t n = B * C * H * W * elem_size(dtype);
+    const int64_t taps = 12 * B * groups * H * W * elem_size(dtype);
+    if (overlap(y, n, x, n) || overlap(y, n, lam, n) || overlap(y, n, u, n) ||
+        overlap(y, n, w_raw4, taps))
+        return GSPN_ERR_ALIAS;
+    gspn::PropOpts opts;
+    opts.cpg = C / groups;
+    // any count at or above a scan's line count cuts it into single lines
+    opts.k_chunk = std::min<int64_t>(k_chunk, std::max(H, W));
+    const int64_t need = with_ws ? shared_workspace(dtype, B, C, groups, H, W) : 0;
+    if (need > 0) {
+        if (!workspace) return GSPN_ERR_NULL;
+        if (workspace_bytes < need) return GSPN_ERR_SHAPE;
+        if (reinterpret_cast<uintptr_t>(workspace) & 15u) return GSPN_ERR_ALIGN;
+        if (overlap(workspace, need, x, n) || overlap(workspace, need, lam, n) ||
+            overlap(workspace, need, u, n) || overlap(workspace, need, w_raw4, taps) ||
+            overlap(workspace, need, y, n))
+            return GSPN_ERR_ALIAS;
+        // buffers the fast kernels cannot address (2-byte aligned) take the
+        // path that normalises per channel
+        if (gspn::prop2d_quad_shared_eligible(dtype, B * C, H, W, opts, x, lam, u, w_raw4, y))
+            return launch_status(gspn::launch_prop2d_quad_shared(x, lam, u, w_raw4, eps, y, B * C,
+                                                                 H, opts, workspace,
+                                                                 static_cast<hipStream_t>(stream)));
+    } else if (with_ws && workspace_bytes < 0) {
+        return GSPN_ERR_SHAPE;
+    }
+    return launch_status(gspn::launch_prop2d(x, lam, u, w_raw4, eps, y, dtype, B * C, H, W, opts,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 // Shared by gspn_prop2d_4dir_ex_backward (caller's workspace) and its
 // _noalloc variant (scratch: the library's static buffer, looked up after
 // validation).
@@ -171,27 +227,24 @@ int gspn_prop2d_4dir(const void* x, const void* lam, const void* u, const void* 
 int gspn_prop2d_4dir_ex(const void* x, const void* lam, const void* u, const void* w_raw4,
                         int64_t groups, int64_t k_chunk, float eps, void* y, int dtype,
                         int64_t B, int64_t C, int64_t H, int64_t W, void* stream) {
-    if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
-    if (int s = check_dims(B, C, H, W, 12)) return s;
-    if (H * W > gspn::prop2d_max_plane(dtype, H, W)) return GSPN_ERR_SHAPE;
-    if (groups < 1 || groups > C || C % groups != 0) return GSPN_ERR_SHAPE;
-    if (k_chunk < 1) return GSPN_ERR_VALUE;
-    if (!valid_eps(eps)) return GSPN_ERR_VALUE;
-    if (!x || !lam || !u || !w_raw4 || !y) return GSPN_ERR_NULL;
-    if (!aligned(x, dtype) || !aligned(lam, dtype) || !aligned(u, dtype) ||
-        !aligned(w_raw4, dtype) || !aligned(y, dtype))
-        return GSPN_ERR_ALIGN;
-    const int64_t n = B * C * H * W * elem_size(dtype);
-    const int64_t taps = 12 * B * groups * H * W * elem_size(dtype);
-    if (overlap(y, n, x, n) || overlap(y, n, lam, n) || overlap(y, n, u, n) ||
-        overlap(y, n, w_raw4, taps))
-        return GSPN_ERR_ALIAS;
-    gspn::PropOpts opts;
-    opts.cpg = C / groups;
-    // any count at or above a scan's line count cuts it into single lines
-    opts.k_chunk = std::min<int64_t>(k_chunk, std::max(H, W));
-    return launch_status(gspn::launch_prop2d(x, lam, u, w_raw4, eps, y, dtype, B * C, H, W, opts,
-                                             static_cast<hipStream_t>(stream)));
+    return ex_forward(x, lam, u, w_raw4, groups, k_chunk, eps, y, nullptr, 0, false, dtype, B, C, H,
+                      W, stream);
+}
+
+int gspn_prop2d_4dir_ex_ws(const void* x, const void* lam, const void* u, const void* w_raw4,
+                           int64_t groups, int64_t k_chunk, float eps, void* y, void* workspace,
+                           int64_t workspace_bytes, int dtype, int64_t B, int64_t C, int64_t H,
+                           int64_t W, void* stream) {
+    return ex_forward(x, lam, u, w_raw4, groups, k_chunk, eps, y, workspace, workspace_bytes, true,
+                      dtype, B, C, H, W, stream);
+}
+
+int64_t gspn_prop2d_4dir_ex_workspace(int dtype, int64_t B, int64_t C, int64_t groups, int64_t H,
+                                      int64_t W) {
+    if (!valid_dtype(dtype) || check_dims(B, C, H, W, 12) != GSPN_OK) return -1;
+    if (H * W > gspn::prop2d_max_plane(dtype, H, W)) return -1;
+    if (groups < 1 || groups > C || C % groups != 0) return -1;
+    return shared_workspace(dtype, B, C, groups, H, W);
 }
 
 int64_t gspn_prop2d_4dir_ex_backward_workspace(int64_t B, int64_t C, int64_t groups, int64_t H,

@@ -72,6 +72,15 @@ bool prop2d_quad_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const
 hipError_t launch_prop2d_quad(const void* x, const void* lam, const void* u, const void* w4,
                               float eps, void* y, int64_t planes, int64_t L, const PropOpts& o,
                               hipStream_t stream);
+// Taps shared by cpg >= 2 channels: normalised once per tap plane into ws
+// (fp32, prop2d_quad_shared_workspace_bytes), then the scan reads them.
+int64_t prop2d_quad_shared_workspace_bytes(int64_t planes, int64_t L, int64_t cpg);
+bool prop2d_quad_shared_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                                 const void* x, const void* lam, const void* u, const void* w4,
+                                 const void* y);
+hipError_t launch_prop2d_quad_shared(const void* x, const void* lam, const void* u, const void* w4,
+                                     float eps, void* y, int64_t planes, int64_t L,
+                                     const PropOpts& o, void* ws, hipStream_t stream);
 
 // Gradient of gspn_prop2d_4dir_ex (gspn_backward.hip): taps of plane p read
 // from group plane p / cpg, scans cut into k_chunk segments.  ws holds

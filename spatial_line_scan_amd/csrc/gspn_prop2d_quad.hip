@@ -113,13 +113,72 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 
 // K: positions a lane; R = (L - 1) mod K; D: steps a block (a multiple of K),
 // also the number of lines of taps prefetched ahead.
-template <int K, int R, int D>
+// Floats of prepared weights a lane keeps a line: three a position, padded
+// to whole 16-byte loads.
+constexpr int prepared_floats(int K) { return (3 * K + 3) / 4 * 4; }
+
+// Weights of taps shared by a group of channels, normalised once for all of
+// them (paper §4.2, channel-shared weights; §5.1 fused normalisation: sigmoid,
+// local sum, clamp, divide).  For position p = Kq + j of the line the scan
+// reaches at a step (lane q of the 16 a direction takes, slot j), w_k =
+// s_k / max(s_0 + s_1 + s_2, eps) with
+// s_k the sigmoid of raw tap k, 0 for taps whose source lies outside the line
+// and for positions past its end.  Output [4][tap planes][L steps][16][KP]
+// fp32, position j's taps at 3 j .. 3 j + 2; the same arithmetic as the
+// fused kernels (hardware exp2 and reciprocal).
+template <int K>
+__global__ void __launch_bounds__(256)
+quad_prepare_kernel(const uint16_t* __restrict__ w4, float* __restrict__ wp, float eps, int tap_planes,
+                    int L) {
+    // one thread per (direction and tap plane, step, slot Kq + j of the 16 K
+    // a line has): its three weights, and the lane's padding after its last
+    // slot
+    constexpr int KP = prepared_floats(K);
+    constexpr int NS = 16 * K;
+    const int64_t total = static_cast<int64_t>(4) * tap_planes * L * NS;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (t >= total) return;
+    const int p = static_cast<int>(t % NS);
+    const int64_t ls = t / NS;                              // (direction, tap plane, step)
+    const int step = static_cast<int>(ls % L);
+    const int64_t dp = ls / L;                              // direction * tap_planes + tap plane
+    const int dir = static_cast<int>(dp / tap_planes);
+    const int line = (dir & 1) == 0 ? step : L - 1 - step;
+    const int q = p / K, j = p - q * K;
+    float* dst = wp + (ls * 16 + q) * KP + 3 * j;
+    if (j == K - 1) {
+#pragma unroll
+        for (int e = 3 * K; e < KP; ++e) wp[(ls * 16 + q) * KP + e] = 0.0f;
+    }
+    if (p >= L) {
+        dst[0] = dst[1] = dst[2] = 0.0f;
+        return;
+    }
+    const int64_t n = static_cast<int64_t>(L) * L;
+    const uint16_t* src = w4 + dp * 3 * n + static_cast<int64_t>(line) * L + p;
+    float sv[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const bool dropped = (k == 0 && p == 0) || (k == 2 && p == L - 1);
+        const float z = __uint_as_float(static_cast<uint32_t>(src[k * n]) << 16);
+        sv[k] = dropped ? 0.0f : __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z * kNegLog2e) + 1.0f);
+    }
+    const float r = __builtin_amdgcn_rcpf(fmaxf((sv[0] + sv[1]) + sv[2], eps));
+#pragma unroll
+    for (int k = 0; k < 3; ++k) dst[k] = sv[k] * r;
+}
+
+// PRE: w4 holds the weights quad_prepare_kernel wrote (fp32, normalised, in
+// scan order, KP a lane a line) instead of raw bf16 taps.
+template <int K, int R, int D, bool PRE>
 __global__ void __launch_bounds__(64)
 prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
                    const uint16_t* __restrict__ u, const uint16_t* __restrict__ w4, int w4_bytes,
                    float eps, uint16_t* __restrict__ y, int planes, int L, int cpg) {
     static_assert(D % K == 0, "blocks of whole slot cycles");
     constexpr int NW = window_words<uint16_t, K>();
+    constexpr int KP = prepared_floats(K);
+    constexpr int NV = KP / 4;
     const int n = L * L;
     const QuadLayout lay(L);
     const int lane = threadIdx.x;
@@ -127,13 +186,23 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     const int q = lane & 15;
     const bool rows = g < 2;
     const bool fwd = (g & 1) == 0;
-    const int plane = blockIdx.x;
+    // With shared taps, consecutive workgroups go to the 8 XCDs in turn;
+    // the plane of workgroup i is chosen so that XCD x walks tap planes x,
+    // x + 8, ... and every channel of a tap group reads its weights through
+    // one L2.  Any plane order gives the same results.
+    int plane = blockIdx.x;
+    if constexpr (PRE) {
+        if (planes % (8 * cpg) == 0) {
+            const int x8 = plane & 7, sl = plane >> 3;
+            plane = ((sl / cpg) * 8 + x8) * cpg + sl % cpg;
+        }
+    }
     const uint32_t plane_b = static_cast<uint32_t>(plane) * static_cast<uint32_t>(n) * 2u;
     const int nchunk = (2 * n + 15) / 16;  // 16-byte chunks of a plane's bf16 values
 
     // ------------------------------------------------ u, prefetched for the end
     // (it arrives while the plane is scanned; kU 16-byte chunks a lane)
-    constexpr int kU = (2 * 80 * 80 / 16 + 63) / 64;
+    constexpr int kU = (2 * (16 * K) * (16 * K) / 16 + 63) / 64;   // sides up to 16 K
     const __amdgpu_buffer_rsrc_t us = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(u), 0, static_cast<int>(static_cast<int64_t>(planes) * n * 2), kBufFlags);
     u32x4_t uv[kU];
@@ -161,26 +230,47 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     // ------------------------------------------------ taps: first D lines
     const int tap_planes = planes / cpg;
     __amdgpu_buffer_rsrc_t taps[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w4) + static_cast<size_t>(k) * n,
-                                                    0, w4_bytes - k * n * 2, kBufFlags);
     const int par = (K * q) & 1;
     const bool lane_live = K * q < L;
     const uint32_t line_b = static_cast<uint32_t>(L) * 2u;
-    const uint32_t tap_base =
-        static_cast<uint32_t>((g * tap_planes + plane / cpg) * 3) * static_cast<uint32_t>(n) * 2u +
-        static_cast<uint32_t>(K * q - par) * 2u;
-    const uint32_t lo_min = lane_live ? tap_base : 0x80000000u;
-    const uint32_t lo_max = lane_live ? tap_base + static_cast<uint32_t>(L - 1) * line_b : 0x80000000u;
-    uint32_t lo = fwd ? lo_min : lo_max;
-    const uint32_t dlo = lane_live ? (fwd ? line_b : 0u - line_b) : 0u;
-    words_t<NW> tbuf[D][3];
-    auto load_line = [&](int d) {
+    uint32_t lo = 0, lo_min = 0, lo_max = 0, dlo = 0;
+    words_t<NW> tbuf[PRE ? 1 : D][3];
+    // prepared weights: this lane's KP floats of the direction's step 0, then
+    // one line of 16 lanes a step
+    u32x4_t pbuf[PRE ? D : 1][NV];
+    const __amdgpu_buffer_rsrc_t wpr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w4), 0, w4_bytes, kBufFlags);
+    uint32_t po = 0;
+    constexpr uint32_t dpo = 16u * KP * 4u;
+    if constexpr (PRE) {
+        po = (static_cast<uint32_t>(g * tap_planes + plane / cpg) * static_cast<uint32_t>(L) * 16u +
+              static_cast<uint32_t>(q)) * (KP * 4u);
+    } else {
 #pragma unroll
-        for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
-        const uint32_t nx = lo + dlo;
-        lo = nx < lo_min ? lo_min : (nx > lo_max ? lo_max : nx);
+        for (int k = 0; k < 3; ++k)
+            taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w4) + static_cast<size_t>(k) * n,
+                                                        0, w4_bytes - k * n * 2, kBufFlags);
+        const uint32_t tap_base =
+            static_cast<uint32_t>((g * tap_planes + plane / cpg) * 3) * static_cast<uint32_t>(n) * 2u +
+            static_cast<uint32_t>(K * q - par) * 2u;
+        lo_min = lane_live ? tap_base : 0x80000000u;
+        lo_max = lane_live ? tap_base + static_cast<uint32_t>(L - 1) * line_b : 0x80000000u;
+        lo = fwd ? lo_min : lo_max;
+        dlo = lane_live ? (fwd ? line_b : 0u - line_b) : 0u;
+    }
+    auto load_line = [&](int d) {
+        if constexpr (PRE) {
+            // a step past the scan reads the next block or past the buffer
+            // (0); its weights are never used
+#pragma unroll
+            for (int v = 0; v < NV; ++v) pbuf[d][v] = __builtin_amdgcn_raw_buffer_load_b128(wpr, po + 16u * v, 0, 0);
+            po += dpo;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
+            const uint32_t nx = lo + dlo;
+            lo = nx < lo_min ? lo_min : (nx > lo_max ? lo_max : nx);
+        }
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -283,6 +373,28 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     read_ahead(0, 0, 0, (L - 1 - R) / K);
 
     auto step = [&](int s, int d, int qb1, int qb2) {
+        float hn[K];
+        if constexpr (PRE) {
+            asm volatile("" : "+v"(pbuf[d][0]));
+            float wv[3 * K];
+#pragma unroll
+            for (int e = 0; e < 3 * K; ++e) wv[e] = __uint_as_float(pbuf[d][e / 4][e % 4]);
+            // refill slot d only after it has been read
+#pragma unroll
+            for (int e = 0; e < 3 * K; ++e) asm volatile("" : "+v"(po) : "v"(wv[e]));
+            load_line(d);
+            float bv[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) bv[j] = __uint_as_float(__builtin_amdgcn_perm(bhr[j], blr[j], 0x0504000cu));
+            const float hl0 = row_prev(h[K - 1]);
+            const float hrK = row_next(h[0]);
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const float hl = j > 0 ? h[j - 1] : hl0;
+                const float hr = j < K - 1 ? h[j + 1] : hrK;
+                hn[j] = fmaf(wv[3 * j + 2], hr, fmaf(wv[3 * j], hl, fmaf(wv[3 * j + 1], h[j], bv[j])));
+            }
+        } else {
         asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
         float s0v[K], s1v[K], s2v[K], r[K];
 #pragma unroll
@@ -320,7 +432,6 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
         for (int j = 0; j < K; ++j) bv[j] = __uint_as_float(__builtin_amdgcn_perm(bhr[j], blr[j], 0x0504000cu));
         const float hl0 = row_prev(h[K - 1]);
         const float hrK = row_next(h[0]);
-        float hn[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const float hl = j > 0 ? h[j - 1] : hl0;
@@ -329,6 +440,7 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
             m = fmaf(s0v[j], hl, m);
             m = fmaf(s2v[j], hr, m);
             hn[j] = fmaf(m, r[j], bv[j]);
+        }
         }
 #pragma unroll
         for (int j = 0; j < K; ++j) h[j] = hn[j];
@@ -408,40 +520,67 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     }
 }
 
-template <int K, int R>
-hipError_t launch_kr(const void* x, const void* lam, const void* u, const void* w4, float eps,
-                     void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
-    constexpr int D = K * ((8 + K - 1) / K);
+// D: lines of taps in flight; with prepared weights a line takes KP
+// registers instead of 3 window words, so fewer are kept.
+template <int K, bool PRE> constexpr int depth() { return PRE ? K * ((5 + K - 1) / K) : K * ((8 + K - 1) / K); }
+
+template <int K, int R, bool PRE>
+hipError_t launch_kr(const void* x, const void* lam, const void* u, const void* w4, int64_t w4_bytes,
+                     float eps, void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
+    constexpr int D = depth<K, PRE>();
     const size_t lds = QuadLayout(static_cast<int>(L)).bytes;
-    auto kern = prop2d_quad_kernel<K, R, D>;
+    auto kern = prop2d_quad_kernel<K, R, D, PRE>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    const int64_t n = planes * L * L;
     kern<<<dim3(static_cast<unsigned>(planes)), dim3(64), lds, stream>>>(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(lam), static_cast<const uint16_t*>(u),
-        static_cast<const uint16_t*>(w4), static_cast<int>(12 * (n / o.cpg) * 2), eps,
+        static_cast<const uint16_t*>(w4), static_cast<int>(w4_bytes), eps,
         static_cast<uint16_t*>(y), static_cast<int>(planes), static_cast<int>(L), static_cast<int>(o.cpg));
     return hipGetLastError();
 }
 
-template <int K>
-hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, float eps,
-                    void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
+template <int K, bool PRE>
+hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, int64_t w4_bytes,
+                    float eps, void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
     switch ((L - 1) % K) {
-        case 0: return launch_kr<K, 0>(x, lam, u, w4, eps, y, planes, L, o, stream);
-        case 1: if constexpr (K > 1) return launch_kr<K, 1 % K>(x, lam, u, w4, eps, y, planes, L, o, stream);
+        case 0: return launch_kr<K, 0, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
+        case 1: if constexpr (K > 1) return launch_kr<K, 1 % K, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
                 [[fallthrough]];
-        case 2: if constexpr (K > 2) return launch_kr<K, 2 % K>(x, lam, u, w4, eps, y, planes, L, o, stream);
+        case 2: if constexpr (K > 2) return launch_kr<K, 2 % K, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
                 [[fallthrough]];
-        case 3: if constexpr (K > 3) return launch_kr<K, 3 % K>(x, lam, u, w4, eps, y, planes, L, o, stream);
+        case 3: if constexpr (K > 3) return launch_kr<K, 3 % K, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
                 [[fallthrough]];
-        default: if constexpr (K > 4) return launch_kr<K, 4 % K>(x, lam, u, w4, eps, y, planes, L, o, stream);
+        default: if constexpr (K > 4) return launch_kr<K, 4 % K, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
     }
     return hipErrorInvalidValue;
+}
+
+int quad_k(int64_t L) { return L <= 16 ? 1 : L <= 32 ? 2 : L <= 48 ? 3 : L <= 64 ? 4 : 5; }
+
+template <bool PRE>
+hipError_t launch_any(const void* x, const void* lam, const void* u, const void* w4, int64_t w4_bytes,
+                      float eps, void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
+    switch (quad_k(L)) {
+        case 1: return launch_k<1, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
+        case 2: return launch_k<2, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
+        case 3: return launch_k<3, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
+        case 4: return launch_k<4, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
+        default: return launch_k<5, PRE>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
+    }
+}
+
+template <int K>
+hipError_t launch_prepare(const void* w4, void* wp, float eps, int64_t tap_planes, int64_t L,
+                          hipStream_t stream) {
+    const int64_t total = 4 * tap_planes * L * 16 * K;
+    quad_prepare_kernel<K><<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, stream>>>(
+        static_cast<const uint16_t*>(w4), static_cast<float*>(wp), eps, static_cast<int>(tap_planes),
+        static_cast<int>(L));
+    return hipGetLastError();
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -461,11 +600,37 @@ bool prop2d_quad_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const
 hipError_t launch_prop2d_quad(const void* x, const void* lam, const void* u, const void* w4,
                               float eps, void* y, int64_t planes, int64_t L, const PropOpts& o,
                               hipStream_t stream) {
-    if (L <= 16) return launch_k<1>(x, lam, u, w4, eps, y, planes, L, o, stream);
-    if (L <= 32) return launch_k<2>(x, lam, u, w4, eps, y, planes, L, o, stream);
-    if (L <= 48) return launch_k<3>(x, lam, u, w4, eps, y, planes, L, o, stream);
-    if (L <= 64) return launch_k<4>(x, lam, u, w4, eps, y, planes, L, o, stream);
-    return launch_k<5>(x, lam, u, w4, eps, y, planes, L, o, stream);
+    const int64_t w4_bytes = 12 * (planes / o.cpg) * L * L * 2;
+    return launch_any<false>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
+}
+
+int64_t prop2d_quad_shared_workspace_bytes(int64_t planes, int64_t L, int64_t cpg) {
+    return 4 * (planes / cpg) * L * 16 * prepared_floats(quad_k(L)) * 4;
+}
+
+bool prop2d_quad_shared_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
+                                 const void* x, const void* lam, const void* u, const void* w4,
+                                 const void* y) {
+    if (o.cpg < 2) return false;
+    if (!prop2d_quad_eligible(dtype, planes, H, W, o, x, lam, u, w4, y)) return false;
+    return prop2d_quad_shared_workspace_bytes(planes, H, o.cpg) <= 0x7fffffff;
+}
+
+hipError_t launch_prop2d_quad_shared(const void* x, const void* lam, const void* u, const void* w4,
+                                     float eps, void* y, int64_t planes, int64_t L,
+                                     const PropOpts& o, void* ws, hipStream_t stream) {
+    const int64_t tap_planes = planes / o.cpg;
+    hipError_t e;
+    switch (quad_k(L)) {
+        case 1: e = launch_prepare<1>(w4, ws, eps, tap_planes, L, stream); break;
+        case 2: e = launch_prepare<2>(w4, ws, eps, tap_planes, L, stream); break;
+        case 3: e = launch_prepare<3>(w4, ws, eps, tap_planes, L, stream); break;
+        case 4: e = launch_prepare<4>(w4, ws, eps, tap_planes, L, stream); break;
+        default: e = launch_prepare<5>(w4, ws, eps, tap_planes, L, stream); break;
+    }
+    if (e != hipSuccess) return e;
+    return launch_any<true>(x, lam, u, ws, prop2d_quad_shared_workspace_bytes(planes, L, o.cpg), eps, y,
+                            planes, L, o, stream);
 }
 
 }  // namespace gspn

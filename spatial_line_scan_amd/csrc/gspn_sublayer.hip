@@ -192,9 +192,22 @@ hipError_t gemm(int dtype, const GemmShape& g, const void* A, const void* B, voi
     return blas_error(s);
 }
 
+// Bytes of the prepared-weight scratch the scan uses when its tap groups
+// share a normalisation (bf16 square planes with even sides up to 80, one
+// segment a scan; sized here whatever the segment count), else 0.
+int64_t shared_prep_bytes(int dtype, int64_t B, int64_t Cc, int64_t G, int64_t H, int64_t W) {
+    PropOpts o;
+    o.cpg = Cc / G;
+    const void* a = reinterpret_cast<const void*>(uintptr_t{256});
+    if (!prop2d_quad_shared_eligible(dtype, B * Cc, H, W, o, a, a, a, a, a)) return 0;
+    return prop2d_quad_shared_workspace_bytes(B * Cc, H, o.cpg);
+}
+
 struct SublayerLayout {
-    int64_t z, zt, lam, u, taps, yc, blas, total;
-    SublayerLayout(int64_t B, int64_t Cc, int64_t G, int64_t N, int64_t es) {
+    int64_t z, zt, lam, u, taps, yc, prep, blas, total;
+    SublayerLayout(int dtype, int64_t B, int64_t Cc, int64_t G, int64_t H, int64_t W) {
+        const int64_t N = H * W;
+        const int64_t es = dtype == 0 ? 4 : 2;
         const int64_t plane = align_up(B * Cc * N * es);
         z = 0;
         zt = z + plane;
@@ -202,7 +215,8 @@ struct SublayerLayout {
         u = lam + plane;
         taps = u + plane;
         yc = taps + align_up(12 * B * G * N * es);
-        blas = yc + plane;
+        prep = yc + plane;
+        blas = prep + align_up(shared_prep_bytes(dtype, B, Cc, G, H, W));
         total = blas + kBlasWorkspace;
     }
 };
@@ -211,7 +225,7 @@ struct SublayerLayout {
 
 int64_t latent_sublayer_workspace_bytes(int dtype, int64_t B, int64_t Cc, int64_t G, int64_t H,
                                         int64_t W) {
-    return SublayerLayout(B, Cc, G, H * W, dtype == 0 ? 4 : 2).total;
+    return SublayerLayout(dtype, B, Cc, G, H, W).total;
 }
 
 hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const void* w_param,
@@ -220,7 +234,7 @@ hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const v
                                   int64_t Cc, int64_t H, int64_t W, hipStream_t stream) {
     const int64_t N = H * W;
     const int64_t es = dtype == 0 ? 4 : 2;
-    const SublayerLayout lay(B, Cc, G, N, es);
+    const SublayerLayout lay(dtype, B, Cc, G, H, W);
     char* base = static_cast<char*>(ws);
     void* z = base + lay.z;
     void* zt = base + lay.zt;
@@ -241,6 +255,14 @@ hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const v
     PropOpts opts;
     opts.cpg = Cc / G;
     opts.k_chunk = k_chunk;
+    // the scan: shared tap groups are normalised once into the prep region
+    auto scan = [&]() {
+        if (lay.blas > lay.prep &&
+            prop2d_quad_shared_eligible(dtype, B * Cc, H, W, opts, z, lam, u, taps, yc))
+            return launch_prop2d_quad_shared(z, lam, u, taps, eps, yc, B * Cc, H, opts,
+                                             base + lay.prep, stream);
+        return launch_prop2d(z, lam, u, taps, eps, yc, dtype, B * Cc, H, W, opts, stream);
+    };
     if (conv1x1_eligible(dtype, B, Cc, H, W, C)) {
         // the parameter convolutions and P_up on the matrix cores: one launch
         // writes lambda, u and the row scans' taps from z, one the column
@@ -249,7 +271,7 @@ hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const v
         for (int d = 0; d < 4; ++d) taps4[d] = taps + d * B * 3 * G * N * es;
         e = launch_conv1x1_params(z, zt, w_param, B, Cc, G, H, W, lam, u, taps4, stream);
         if (e != hipSuccess) return e;
-        e = launch_prop2d(z, lam, u, taps, eps, yc, dtype, B * Cc, H, W, opts, stream);
+        e = scan();
         if (e != hipSuccess) return e;
         return launch_conv1x1_up(yc, p_up, B, Cc, C, H, W, y_tok, stream);
     }
@@ -283,7 +305,7 @@ hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const v
                    3 * G * N);
         if (e != hipSuccess) return e;
     }
-    e = launch_prop2d(z, lam, u, taps, eps, yc, dtype, B * Cc, H, W, opts, stream);
+    e = scan();
     if (e != hipSuccess) return e;
     // y[b] (N x C, row-major) = yc[b]^T P_up^T: column-major y^T = P_up yc[b]
     return gemm(dtype, {HIPBLAS_OP_T, HIPBLAS_OP_T, C, N, Cc, Cc, N, C, 0, Cc * N, N * C, bt}, p_up,

@@ -57,6 +57,11 @@ def lib():
         L.gspn_prop2d_4dir_ex.argtypes = [vp, vp, vp, vp, i64, i64, cf, vp, ci, i64, i64, i64,
                                           i64, vp]
         L.gspn_prop2d_4dir_ex.restype = ci
+        L.gspn_prop2d_4dir_ex_ws.argtypes = [vp, vp, vp, vp, i64, i64, cf, vp, vp, i64, ci, i64, i64,
+                                             i64, i64, vp]
+        L.gspn_prop2d_4dir_ex_ws.restype = ci
+        L.gspn_prop2d_4dir_ex_workspace.argtypes = [ci, i64, i64, i64, i64, i64]
+        L.gspn_prop2d_4dir_ex_workspace.restype = i64
         L.gspn_latent_sublayer.argtypes = [vp, vp, vp, vp, i64, i64, cf, vp, vp, i64, ci, i64,
                                            i64, i64, i64, i64, vp]
         L.gspn_latent_sublayer.restype = ci
@@ -173,11 +178,27 @@ def prop2d_4dir(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4: torch.T
     return out
 
 
+def prop2d_4dir_ex_workspace_bytes(dtype: torch.dtype, B: int, C: int, groups: int, H: int,
+                                   W: int) -> int:
+    """Scratch bytes prop2d_4dir_ex uses to normalise each tap group once
+    (0: none; every channel then normalises its group's taps)."""
+    code = FP32 if dtype == torch.float32 else BF16
+    n = lib().gspn_prop2d_4dir_ex_workspace(code, B, C, groups, H, W)
+    if n < 0:
+        raise ValueError("sizes not accepted by gspn_prop2d_4dir_ex")
+    return n
+
+
 def prop2d_4dir_ex(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4: torch.Tensor,
                    groups: int, k_chunk: int = 1, eps: float = 1e-6,
-                   out: torch.Tensor | None = None) -> torch.Tensor:
+                   out: torch.Tensor | None = None, workspace="auto") -> torch.Tensor:
     """prop2d_4dir with taps shared by `groups` contiguous channel groups and
-    each scan cut into k_chunk segments (include/gspn.h)."""
+    each scan cut into k_chunk segments (include/gspn.h).
+
+    workspace: "auto" allocates (with torch) the scratch that lets each tap
+    group be normalised once when the library would use it
+    (gspn_prop2d_4dir_ex_ws); a tensor is used as that scratch; None calls
+    gspn_prop2d_4dir_ex, which normalises the taps in every channel."""
     _same(x, lam, u, w4)
     if x.dim() != 4 or lam.shape != x.shape or u.shape != x.shape:
         raise ValueError("x, lam, u must share one [B, C, H, W] shape")
@@ -191,10 +212,27 @@ def prop2d_4dir_ex(x: torch.Tensor, lam: torch.Tensor, u: torch.Tensor, w4: torc
     _same(x, out)
     if out.shape != x.shape:
         raise ValueError("out must have x's shape")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        need = prop2d_4dir_ex_workspace_bytes(x.dtype, B, C, groups, H, W)
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=x.device) if need else None
+        use_ws = True
+    else:
+        use_ws = workspace is not None
+    if workspace is not None and (workspace.device != x.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on x's device")
     with torch.cuda.device(x.device):
-        _check(lib().gspn_prop2d_4dir_ex(_p(x), _p(lam), _p(u), _p(w4), int(groups), int(k_chunk),
-                                         float(eps), _p(out), _dtype_code(x), B, C, H, W,
-                                         _stream(x)))
+        if use_ws:
+            ws_ptr = ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0)
+            ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+            _check(lib().gspn_prop2d_4dir_ex_ws(_p(x), _p(lam), _p(u), _p(w4), int(groups),
+                                                int(k_chunk), float(eps), _p(out), ws_ptr, ws_bytes,
+                                                _dtype_code(x), B, C, H, W, _stream(x)))
+        else:
+            _check(lib().gspn_prop2d_4dir_ex(_p(x), _p(lam), _p(u), _p(w4), int(groups),
+                                             int(k_chunk), float(eps), _p(out), _dtype_code(x), B,
+                                             C, H, W, _stream(x)))
     return out
 
 

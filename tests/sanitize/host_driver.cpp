@@ -32,6 +32,17 @@ hipError_t launch_prop2d_backward(const void*, const void*, const void*, const v
                                   int64_t, const PropOpts&, hipStream_t) {
     ++g_launches; return hipSuccess;
 }
+hipError_t launch_prop2d_quad_shared(const void*, const void*, const void*, const void*, float, void*,
+                                     int64_t, int64_t, const PropOpts&, void*, hipStream_t) {
+    ++g_launches; return hipSuccess;
+}
+int64_t prop2d_quad_shared_workspace_bytes(int64_t planes, int64_t L, int64_t cpg) {
+    return 4 * (planes / cpg) * L * 16 * 16 * 4;
+}
+bool prop2d_quad_shared_eligible(int dtype, int64_t, int64_t H, int64_t W, const PropOpts& o, const void*,
+                                 const void*, const void*, const void*, const void*) {
+    return dtype == 1 && H == W && H % 2 == 0 && H <= 80 && o.cpg >= 2 && o.k_chunk == 1;
+}
 hipError_t launch_latent_sublayer(const void*, const void*, const void*, const void*, int64_t,
                                   int64_t, float, void*, void*, int, int64_t, int64_t, int64_t,
                                   int64_t, int64_t, hipStream_t) {
@@ -97,6 +108,21 @@ int main() {
     expect(gspn_prop2d_4dir_ex(P(0), P(1), P(2), P(3), big, 1, 1e-6f, M(5), 0, 2, 3, 5, 7, nullptr), GSPN_ERR_SHAPE, 0, "ex big groups");
     expect(gspn_prop2d_4dir_ex(P(0), P(1), P(2), P(3), 3, 0, 1e-6f, M(5), 0, 2, 3, 5, 7, nullptr), GSPN_ERR_VALUE, 0, "ex chunk");
     expect(gspn_prop2d_4dir_ex(P(0), P(1), P(2), P(3), 3, big, 1e-6f, M(5), 0, 2, 3, 5, 7, nullptr), GSPN_OK, 1, "ex huge chunk");
+    // gspn_prop2d_4dir_ex_ws: workspace used (bf16, square even side, shared taps) or not
+    const int64_t wse = gspn_prop2d_4dir_ex_workspace(1, 2, 4, 1, 6, 6);
+    if (wse <= 0) ++fails;
+    if (gspn_prop2d_4dir_ex_workspace(0, 2, 4, 1, 6, 6) != 0) ++fails;
+    if (gspn_prop2d_4dir_ex_workspace(1, 2, 4, 3, 6, 6) != -1) ++fails;
+    expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 1, 1, 1e-6f, M(5), M(6), wse, 1, 2, 4, 6, 6, nullptr),
+           GSPN_OK, 1, "ex_ws ok");
+    expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 1, 1, 1e-6f, M(5), M(6), wse - 1, 1, 2, 4, 6, 6,
+                                  nullptr), GSPN_ERR_SHAPE, 0, "ex_ws small");
+    expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 1, 1, 1e-6f, M(5), nullptr, wse, 1, 2, 4, 6, 6,
+                                  nullptr), GSPN_ERR_NULL, 0, "ex_ws null");
+    expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 1, 1, 1e-6f, M(5), M(3), wse, 1, 2, 4, 6, 6,
+                                  nullptr), GSPN_ERR_ALIAS, 0, "ex_ws alias");
+    expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 1, 1, 1e-6f, M(5), nullptr, 0, 0, 2, 4, 6, 6,
+                                  nullptr), GSPN_OK, 1, "ex_ws unused");
     // gspn_scan_dir and gspn_normalize_weights
     for (int dir = 0; dir < 4; ++dir)
         expect(gspn_scan_dir(P(0), P(1), P(2), P(3), 1, 1e-6f, M(5), 1, 0, 2, 3, 5, 7, dir, nullptr), GSPN_OK, 1, "scan ok");

@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gspn_abi_version() == 6
+    assert L.gspn_abi_version() == 7
     for s in range(10):
         assert L.gspn_status_str(s).decode().startswith("GSPN")
     assert "scratch" in L.gspn_status_str(SCRATCH).decode()
@@ -293,6 +293,33 @@ def test_noalloc_rejects_bad_arguments(L):
     ptrs = [P(j) for j in range(9)]
     ptrs[5] = P(4)
     assert exb_noalloc(L, ptrs=ptrs) == ALIAS                # gx over gy
+
+
+def test_ex_ws_workspace_query_and_rejections(L):
+    # bf16 square planes with even sides up to 80 and shared taps use the
+    # workspace (48 floats a lane-step are the most a direction keeps); other
+    # sizes run as gspn_prop2d_4dir_ex and need none
+    need = L.gspn_prop2d_4dir_ex_workspace(1, 32, 64, 1, 74, 74)
+    assert need == 4 * 32 * 74 * 16 * 16 * 4
+    assert L.gspn_prop2d_4dir_ex_workspace(1, 32, 64, 64, 74, 74) == 0      # no sharing
+    assert L.gspn_prop2d_4dir_ex_workspace(0, 32, 64, 1, 74, 74) == 0       # fp32
+    assert L.gspn_prop2d_4dir_ex_workspace(1, 4, 64, 1, 148, 148) == 0      # beyond 80
+    assert L.gspn_prop2d_4dir_ex_workspace(1, 2, 3, 2, 6, 6) == -1          # 2 does not divide 3
+    assert L.gspn_prop2d_4dir_ex_workspace(7, 2, 3, 1, 6, 6) == -1
+    n6 = L.gspn_prop2d_4dir_ex_workspace(1, 2, 4, 1, 6, 6)
+    assert n6 > 0
+
+    def exw(ws=P(6), nb=n6, groups=1, dt=1, H=6, W=6, ptrs=None):
+        p = list(ptrs) if ptrs else [P(i) for i in range(6)]
+        return L.gspn_prop2d_4dir_ex_ws(p[0], p[1], p[2], p[3], groups, 1, 1e-6, p[5], ws, nb, dt, 2, 4,
+                                        H, W, None)
+    assert exw(nb=n6 - 1) == SHAPE
+    assert exw(ws=None) == NULL
+    assert exw(ws=ctypes.c_void_p(A + 6 * STEP + 8)) == ALIGN
+    assert exw(ws=P(0)) == ALIAS
+    assert exw(ws=P(5)) == ALIAS
+    assert exw(groups=3) == SHAPE
+    assert exw(dt=9) == DTYPE
 
 
 def ex(L, groups=3, k=1, eps=1e-6, dt=0, B=2, C=3, H=5, W=7, y=None):

@@ -101,3 +101,82 @@ def test_ex_latent1k_sampled_planes(G, k):
         g = c // cpg
         r = oracle.prop2d_ex(sl(p["x"]), sl(p["lam"]), sl(p["u"]), w[:, b:b + 1, g:g + 1], 1, k)
         assert_close(_np(sl(y)), r, RTOL[wl.dtype], "plane (%d,%d)" % (b, c))
+
+
+# gspn_prop2d_4dir_ex_ws: bf16 square planes with even sides up to 80, one
+# segment a scan and at least 2 channels a group normalise each group's taps
+# once into the workspace; the sides cover every K (positions a lane) and
+# every (L - 1) mod K of the scan kernel
+SHARED_SIDES = [2, 4, 14, 16, 18, 30, 32, 34, 36, 46, 48, 50, 52, 62, 64, 66, 68, 70, 72, 74, 80]
+
+
+@pytest.mark.parametrize("L", SHARED_SIDES)
+@pytest.mark.parametrize("B,C,G", [(2, 4, 1), (1, 8, 4)])
+def test_ex_shared_weights_sides(L, B, C, G):
+    say("ex shared", L, "B", B, "C", C, "G", G)
+    assert gspn.prop2d_4dir_ex_workspace_bytes(torch.bfloat16, B, C, G, L, L) > 0
+    p = _problem(B, C, L, L, G, 500 + L + G, "bf16")
+    _run_check(p, G, 1, "bf16", "shared %dx%d G=%d" % (L, L, G))
+
+
+@pytest.mark.parametrize("L", [16, 50, 74])
+def test_ex_shared_weights_xcd_plane_order(L):
+    # planes a multiple of 8 groups: workgroups take planes in the order that
+    # keeps each tap group on one XCD; every plane is checked
+    say("ex shared xcd order", L)
+    B, C, G = 4, 16, 2
+    p = _problem(B, C, L, L, G, 700 + L, "bf16")
+    _run_check(p, G, 1, "bf16", "shared xcd order %dx%d" % (L, L))
+
+
+@pytest.mark.parametrize("L", [16, 74])
+def test_ex_shared_weights_deterministic_and_close_to_per_channel(L):
+    say("ex shared vs per-channel", L)
+    B, C, G = 4, 16, 1
+    p = _problem(B, C, L, L, G, 900 + L, "bf16")
+    args = (p["x"], p["lam"], p["u"], p["w"], G, 1)
+    y1 = gspn.prop2d_4dir_ex(*args)
+    y2 = gspn.prop2d_4dir_ex(*args)
+    y_pc = gspn.prop2d_4dir_ex(*args, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    # the two paths round the weights differently; both are within the bf16
+    # tolerance of the oracle, and of each other
+    assert_close(_np(y1), _np(y_pc), RTOL["bf16"], "shared vs per-channel %dx%d" % (L, L))
+    r = oracle.prop2d_ex(p["x"], p["lam"], p["u"], p["w"], G, 1)
+    assert_close(_np(y1), r, RTOL["bf16"], "shared %dx%d" % (L, L))
+
+
+def test_ex_shared_weights_clamp_and_saturation():
+    # logits near -20 (every sigmoid tiny: the clamp at eps acts), at +-800
+    # (saturated) and a large eps, through the prepared-weight kernel
+    say("ex shared clamp")
+    B, C, G, L = 2, 8, 2, 74
+    p = _problem(B, C, L, L, G, 1234, "bf16")
+    w = p["w"].float().reshape(4, B, G, 3, L * L)
+    w[:, 0] = -20.0 + 0.3 * w[:, 0]
+    w[0, 1, :, :, : L * L // 3] = -800.0
+    w[1, 1, :, 2, L * L // 2:] = 800.0
+    p["w"] = w.to(torch.bfloat16).reshape(p["w"].shape).contiguous()
+    for eps in (1e-6, 1e-3):
+        y = gspn.prop2d_4dir_ex(p["x"], p["lam"], p["u"], p["w"], G, 1, eps)
+        torch.cuda.synchronize()
+        r = oracle.prop2d_ex(p["x"], p["lam"], p["u"], p["w"], G, 1, eps)
+        assert_close(_np(y), r, RTOL["bf16"], "shared clamp eps %g" % eps)
+
+
+def test_ex_shared_weights_misaligned_buffers_fall_back():
+    # 2-byte aligned tensors cannot take the fast kernels: the call still
+    # succeeds with the workspace and matches the oracle
+    say("ex shared misaligned")
+    B, C, G, L = 1, 4, 1, 16
+    p = _problem(B, C, L, L, G, 77, "bf16")
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+    q = {k: shifted(v) for k, v in p.items()}
+    assert q["x"].data_ptr() % 4 == 2
+    _run_check(q, G, 1, "bf16", "misaligned shared")
