@@ -37,6 +37,16 @@ __device__ __forceinline__ words_t<NW> load_words(__amdgpu_buffer_rsrc_t r, uint
     else return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// The same at byte offset `off` + `soff` (soff uniform: a scalar offset).
+template <int NW>
+__device__ __forceinline__ words_t<NW> load_words_so(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+    static_assert(NW >= 1 && NW <= 4, "one load per window");
+    if constexpr (NW == 1) return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+    else if constexpr (NW == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+    else if constexpr (NW == 3) return __builtin_amdgcn_raw_buffer_load_b96(r, off, soff, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+}
+
 template <int NW>
 __device__ __forceinline__ uint32_t word(const words_t<NW>& w, int i) {
     if constexpr (NW == 1) return w;

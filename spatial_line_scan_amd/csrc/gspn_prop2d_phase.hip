@@ -1,5 +1,5 @@
-// Four-direction propagation of bf16 planes with even sides up to 160, one
-// wavefront per (b, c) plane in two phases (gfx950).  fp32 planes take the
+// Four-direction propagation of bf16 planes with sides up to 160, one
+// workgroup per (b, c) plane in two phases (gfx950).  fp32 planes take the
 // two-wavefront kernel: their 4-byte lambda x would not leave room for four
 // planes per CU.
 //
@@ -60,22 +60,26 @@ namespace {
 using namespace lane;
 
 // LDS layout in bytes (all offsets multiples of 16):
-//   [S dummy: 16][b dummy: 16][pad Lmax][S: H W][pad Lmax] fp32,
+//   [S dummy: 16][b dummy: 16][pad Lmax][S: H W][pad Lmax][side: Lmax] fp32,
 //   [pad][b_hi: H W][pad] u16, [pad][b_lo: H W][pad] u8
 // Slots past a line end all use the dummies: their S reads and writes go to
 // the S dummy, their b reads in the column scan to the b dummy (zero, never
 // written) and their b writes in the row scan to the pads before the b
 // arrays.  Their taps are all dropped, so no in-line position ever weighs
 // their (finite) states.
+// side: one line of fp32 where, with an odd number of lines, the backward
+// scan order puts its terms of the middle line (both orders reach it in the
+// same step); zeroed with S, added into S after the phase.
 struct PhaseLayout {
-    int s, bh, bl, bytes;
+    int s, side, bh, bl, bytes;
     static constexpr int dum = 0, bdum = 16;
     __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
     __host__ __device__ PhaseLayout(int H, int W) {
         const int lmax = H > W ? H : W;
         const int hw = H * W;
         s = a16(32 + 4 * lmax);
-        bh = a16(s + 4 * hw + 4 * lmax + 2 * lmax);
+        side = a16(s + 4 * hw + 4 * lmax);
+        bh = a16(side + 4 * lmax + 2 * lmax);
         bl = a16(bh + 2 * (hw + lmax) + lmax);
         bytes = a16(bl + hw + lmax);
     }
@@ -108,14 +112,21 @@ __device__ __forceinline__ lds_t<V>& lds_ref(uint32_t byte_off) {
 
 // T: bf16 bits (uint16_t).  Chunked: k_chunk > 1.  NH: lanes a scan order
 // takes: 32 (the two halves of one wavefront) or 64 (one wavefront each).
-template <typename T, int K, int D, bool Chunked, int NH>
+// Odd: H or W may be odd (then lines and planes start at any element; see
+// the window notes in phase()).
+template <typename T, int K, int D, bool Chunked, int NH, bool Odd>
 __global__ void __launch_bounds__(2 * NH)
 prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __restrict__ u,
                     const T* __restrict__ w4, int w4_bytes, float eps, T* __restrict__ y,
                     int planes, int H, int W, int cpg, int k_chunk) {
     static_assert(sizeof(T) == 2, "bf16 planes only");
+    static_assert(!Odd || D % 2 == 0, "odd lines: the window parity alternates with the ring slot");
     constexpr int ES = sizeof(T);
-    constexpr int NW = window_words<T, K>();
+    // words a window decodes from, and words loaded for it: with Odd a
+    // window is loaded from the even element at or below its first and
+    // shifted into place, which for even K takes one more word
+    constexpr int NW = Odd ? (K + 1) / 2 : window_words<T, K>();
+    constexpr int NWL = Odd && (K % 2 == 0) ? NW + 1 : NW;
     const int HW = H * W;
     const PhaseLayout lay(H, W);
     constexpr int NT = 2 * NH;           // threads of the workgroup
@@ -136,13 +147,18 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
     // [0, bh): the dummy words, S with its pads, and the pad before b_hi
     for (int f = tid; f < lay.bh / 16; f += NT) lds_ref<u32x4_t>(16u * f) = u32x4_t{0u, 0u, 0u, 0u};
 
-    const int words = HW / 2;     // HW is even: two pixels a dword
+    const int words = HW / 2;     // two pixels a dword (Odd: and a last pixel)
     // u for the end, in dword pairs, loaded now so that it arrives during
-    // the scans (a trailing odd dword is loaded at the end)
+    // the scans (a trailing odd dword is loaded at the end).  With Odd a
+    // plane may start at any element: the pairs are then 2-byte aligned,
+    // which global loads and stores allow.
     constexpr int kUPer = kTwo ? 12 : 24;
     const int pairs = words / 2;
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    const u32x2_t* u64p = reinterpret_cast<const u32x2_t*>(u + pix0);
+    // (the attribute is kept only on the named type: no template may carry
+    // it, or the compiler takes the 8-byte alignment back)
+    typedef uint32_t u32x2_u __attribute__((ext_vector_type(2), aligned(2)));
+    const u32x2_u* u64p = reinterpret_cast<const u32x2_u*>(u + pix0);
     u32x2_t ureg[kUPer];
 #pragma unroll
     for (int k = 0; k < kUPer; ++k) {
@@ -155,19 +171,21 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
     auto b_addr_hi = [&](int e) { return static_cast<uint32_t>(lay.bh + 2 * e); };
     auto b_addr_lo = [&](int e) { return static_cast<uint32_t>(lay.bl + e); };
 
-    // one resource per tap plane k, based k planes into the tap tensor
-    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T*>(x), 0, static_cast<int>(static_cast<int64_t>(planes) * HW * ES), kBufFlags);
-    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T*>(lam), 0, static_cast<int>(static_cast<int64_t>(planes) * HW * ES), kBufFlags);
+    // one resource per tap plane k, based k planes into the tap tensor (with
+    // Odd one, at the tensor, and the planes at scalar offsets).  Sizes are
+    // rounded up to whole dwords: an odd element count ends inside an aligned
+    // dword whose other half the windows never use.
+    const int xbytes = static_cast<int>((static_cast<int64_t>(planes) * HW * ES + 3) & ~int64_t{3});
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(x), 0, xbytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(lam), 0, xbytes, kBufFlags);
     __amdgpu_buffer_rsrc_t taps[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k)
-        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + static_cast<size_t>(k) * HW), 0,
-                                                    w4_bytes - k * HW * ES, kBufFlags);
+        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + (Odd ? 0 : static_cast<size_t>(k) * HW)),
+                                                    0, ((w4_bytes + 3) & ~3) - (Odd ? 0 : k * HW * ES), kBufFlags);
     const int tap_planes = planes / cpg;
-    const int par = (K * q) & 1;
-    const uint32_t win_b = static_cast<uint32_t>(K * q - par) * ES;
+    const int par = Odd ? 0 : (K * q) & 1;
+    const uint32_t win_b = Odd ? 0u : static_cast<uint32_t>(K * q - par) * ES;
     const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
     const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
 
@@ -198,16 +216,83 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
         uint32_t lo = static_cast<uint32_t>(((g * tap_planes + plane / cpg) * 3) * HW) * ES + win_b + lo0;
         // row scan: x and lambda of the current row, same window as the taps
         uint32_t xo = static_cast<uint32_t>(pix0) * ES + win_b + lo0;
-        words_t<NW> tbuf[D][3];
-        words_t<NW> xbuf[kRows ? D : 1], lbuf[kRows ? D : 1];
+        // Odd: a window starts at element E (its first position Kq on the
+        // line); it is loaded from element E & ~1 and shifted right by 16 bits
+        // when E is odd.  Along a scan E moves by +-L, so with L odd its
+        // parity alternates from step to step: slot d of the ring (steps of
+        // d's parity, D even) uses the shift and the offset increment of its
+        // parity, both fixed per lane.  Tap plane 2 lies 2 HW elements after
+        // plane 0 (same parity: a scalar offset); plane 1 lies HW after it,
+        // which with HW odd flips the parity (a scalar offset plus 4 bytes on
+        // the steps where plane 0's window starts odd).
+        uint32_t incE = dlo, incO = dlo, shE = 0, shO = 0, add1E = 0, add1O = 0, sh1E = 0, sh1O = 0;
+        uint32_t xincE = dlo, xincO = dlo, xshE = 0, xshO = 0;
+        int so1 = HW * ES, so2 = 2 * HW * ES;
+        if constexpr (Odd) {
+            const int lodd = L & 1, hodd = HW & 1;
+            const int line0 = fwd ? 0 : NL - 1;
+            const int dl = fwd ? L : -L;
+            const int e0 = ((g * tap_planes + plane / cpg) * 3) * HW + line0 * L + K * q;
+            const int p0 = e0 & 1, p1 = p0 ^ lodd;
+            lo = static_cast<uint32_t>(e0 - p0) * ES;
+            incE = static_cast<uint32_t>(2 * dl - 2 * lodd + 4 * lodd * p0);
+            incO = static_cast<uint32_t>(2 * dl - 2 * lodd + 4 * lodd * p1);
+            shE = 16u * p0;
+            shO = 16u * p1;
+            add1E = 4u * (p0 & hodd);
+            add1O = 4u * (p1 & hodd);
+            sh1E = shE ^ (16u * hodd);
+            sh1O = shO ^ (16u * hodd);
+            so1 = 2 * HW - 2 * hodd;
+            so2 = 4 * HW;
+            const int ex = static_cast<int>(pix0) + line0 * L + K * q;
+            const int px0 = ex & 1, px1 = px0 ^ lodd;
+            xo = static_cast<uint32_t>(ex - px0) * ES;
+            xincE = static_cast<uint32_t>(2 * dl - 2 * lodd + 4 * lodd * px0);
+            xincO = static_cast<uint32_t>(2 * dl - 2 * lodd + 4 * lodd * px1);
+            xshE = 16u * px0;
+            xshO = 16u * px1;
+        }
+        words_t<NWL> tbuf[D][3];
+        words_t<NWL> xbuf[kRows ? D : 1], lbuf[kRows ? D : 1];
         auto load_line = [&](int d) {
+            if constexpr (Odd) {
+                const bool od = (d & 1) != 0;
+                tbuf[d][0] = load_words_so<NWL>(taps[0], lo, 0);
+                tbuf[d][1] = load_words_so<NWL>(taps[0], lo + (od ? add1O : add1E), so1);
+                tbuf[d][2] = load_words_so<NWL>(taps[0], lo, so2);
+                lo += od ? incO : incE;
+                if constexpr (kRows) {
+                    xbuf[d] = load_words<NWL>(xs, xo);
+                    lbuf[d] = load_words<NWL>(ls, xo);
+                    xo += od ? xincO : xincE;
+                }
+            } else {
 #pragma unroll
-            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
-            lo += dlo;
-            if constexpr (kRows) {
-                xbuf[d] = load_words<NW>(xs, xo);
-                lbuf[d] = load_words<NW>(ls, xo);
-                xo += dlo;
+                for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
+                lo += dlo;
+                if constexpr (kRows) {
+                    xbuf[d] = load_words<NW>(xs, xo);
+                    lbuf[d] = load_words<NW>(ls, xo);
+                    xo += dlo;
+                }
+            }
+        };
+        // the NW words a window decodes from (Odd: shifted into place)
+        auto window = [&](const words_t<NWL>& w, uint32_t sh) -> words_t<NW> {
+            if constexpr (Odd) {
+                words_t<NW> r;
+#pragma unroll
+                for (int i = 0; i < NW; ++i) {
+                    const uint32_t lo_w = word<NWL>(w, i);
+                    const uint32_t hi_w = word<NWL>(w, i + 1 < NWL ? i + 1 : NWL - 1);
+                    const uint32_t v = __builtin_amdgcn_alignbit(hi_w, lo_w, sh);
+                    if constexpr (NW == 1) r = v;
+                    else r[i] = v;
+                }
+                return r;
+            } else {
+                return w;
             }
         };
 #pragma unroll
@@ -251,11 +336,25 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
             // bytes (hi.1, hi.0, lo.0, 0)
             return __uint_as_float(__builtin_amdgcn_perm(hi, lo8, 0x0504000cu));
         };
+        // Odd number of lines: both scan orders reach middle line m in step m;
+        // there the backward order reads and writes the side line instead
+        const bool mid = Odd && !fwd && (NL & 1);
+        const int m = NL / 2;
+        uint32_t sideJ[Odd ? K : 1];
+        if constexpr (Odd) {
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                sideJ[j] = valid[j] ? static_cast<uint32_t>(lay.side + 4 * (K * q + j)) : PhaseLayout::dum;
+        }
+        auto sum_addr = [&](int j, int st) -> uint32_t {
+            if constexpr (Odd) return (mid && st == m) ? sideJ[j] : aS[j];
+            else return aS[j];
+        };
         float h[K], acc[K], bv[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             h[j] = 0.0f;
-            acc[j] = lds_ref<float>(aS[j]);
+            acc[j] = lds_ref<float>(sum_addr(j, 0));
             if constexpr (!kRows) bv[j] = read_b(j);
         }
         int seg = NL, next_restart = NL;
@@ -267,17 +366,26 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
         auto step = [&](int s, int d) {
             asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
             if constexpr (kRows) asm volatile("" : "+v"(xbuf[d]), "+v"(lbuf[d]));
+            const bool od = (d & 1) != 0;
+            const words_t<NW> w0 = window(tbuf[d][0], od ? shO : shE);
+            const words_t<NW> w1 = window(tbuf[d][1], od ? sh1O : sh1E);
+            const words_t<NW> w2 = window(tbuf[d][2], od ? shO : shE);
+            words_t<NW> wx{}, wl{};
+            if constexpr (kRows) {
+                wx = window(xbuf[d], od ? xshO : xshE);
+                wl = window(lbuf[d], od ? xshO : xshE);
+            }
             float s0v[K], s1v[K], s2v[K], r[K];
 #pragma unroll
             for (int j = 0; j < K; ++j) {
                 if constexpr (kRows) {
                     // b = lambda x from the row's windows, also kept for the column scan
-                    bv[j] = window_elem<T, K, NW>(lbuf[d], j, sx[j], sx[j]) *
-                            window_elem<T, K, NW>(xbuf[d], j, sx[j], sx[j]);
+                    bv[j] = window_elem<T, K, NW>(wl, j, sx[j], sx[j]) *
+                            window_elem<T, K, NW>(wx, j, sx[j], sx[j]);
                 }
-                s0v[j] = window_elem<T, K, NW>(tbuf[d][0], j, st[0][j], st[0][j]) * kNegLog2e;
-                s1v[j] = window_elem<T, K, NW>(tbuf[d][1], j, st[1][j], st[1][j]) * kNegLog2e;
-                s2v[j] = window_elem<T, K, NW>(tbuf[d][2], j, st[2][j], st[2][j]) * kNegLog2e;
+                s0v[j] = window_elem<T, K, NW>(w0, j, st[0][j], st[0][j]) * kNegLog2e;
+                s1v[j] = window_elem<T, K, NW>(w1, j, st[1][j], st[1][j]) * kNegLog2e;
+                s2v[j] = window_elem<T, K, NW>(w2, j, st[2][j], st[2][j]) * kNegLog2e;
             }
             // breadth first over the 3 K taps: each dependent operation finds
             // its operand several instructions back
@@ -346,12 +454,14 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
             for (int j = 0; j < K; ++j) h[j] = hn[j];
 
 #pragma unroll
-            for (int j = 0; j < K; ++j) lds_ref<float>(aS[j]) = acc[j] + h[j];
+            for (int j = 0; j < K; ++j) lds_ref<float>(sum_addr(j, s)) = acc[j] + h[j];
             // Each pixel of the phase is updated once per scan order.  The
             // order that reaches it first does so by step NL / 2 - 1; the
             // other reads it one step ahead, at step NL / 2 - 1 or later.  So
             // one barrier there, between this step's writes and its
-            // read-ahead, orders every pair of updates (NL is even).
+            // read-ahead, orders every pair of updates (with NL odd the
+            // middle line, reached by both at step NL / 2, goes to the side
+            // line for the backward order).
             if constexpr (kTwo)
                 if (s == NL / 2 - 1) lds_barrier();
             // the next line, read after this step's writes
@@ -360,7 +470,7 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
                 aS[j] += dSj[j];
                 aH[j] += dHj[j];
                 aL[j] += dLj[j];
-                acc[j] = lds_ref<float>(aS[j]);
+                acc[j] = lds_ref<float>(sum_addr(j, s + 1));
                 if constexpr (!kRows) bv[j] = read_b(j);
             }
         };
@@ -374,23 +484,40 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
         for (int d = 0; d < D; ++d)
             if (s0 + d < NL) step(s0 + d, d);
     };
+    // with an odd number of lines, the backward order's terms of the middle
+    // line are added after the forward order's, and the side line cleared
+    auto fold = [&](bool rows) {
+        const int NL = rows ? H : W, L = rows ? W : H;
+        if (!(NL & 1)) return;
+        const int m = NL / 2;
+        for (int p = tid; p < L; p += NT) {
+            const uint32_t a = static_cast<uint32_t>(lay.s + 4 * (rows ? m * W + p : p * W + m));
+            lds_ref<float>(a) = lds_ref<float>(a) + lds_ref<float>(lay.side + 4 * p);
+            lds_ref<float>(lay.side + 4 * p) = 0.0f;
+        }
+        sync();
+    };
     phase(std::true_type{});
     sync();
+    if constexpr (Odd) fold(true);
     phase(std::false_type{});
     sync();
+    if constexpr (Odd) fold(false);
 
     // --------------------------------------------------------- y = u * S
     // (S is read as four floats per dword pair, 16-byte aligned since the
     // pair starts at an even dword)
     uint32_t* y32 = reinterpret_cast<uint32_t*>(y + pix0);
     const uint32_t* u32 = reinterpret_cast<const uint32_t*>(u + pix0);
-    u32x2_t* y64p = reinterpret_cast<u32x2_t*>(y + pix0);
+    u32x2_u* y64p = reinterpret_cast<u32x2_u*>(y + pix0);
     auto emit_word = [&](int f, uint32_t uv) -> uint32_t {
         const f32x2_t sv = lds_ref<f32x2_t>(lay.s + 8u * f);
         return pack_bf16x2(__uint_as_float(uv << 16) * sv.x, __uint_as_float(uv & 0xffff0000u) * sv.y);
     };
     auto emit_pair = [&](int f, u32x2_t uv) {
-        y64p[f] = u32x2_t{emit_word(2 * f, uv.x), emit_word(2 * f + 1, uv.y)};
+        const u32x2_t o = {emit_word(2 * f, uv.x), emit_word(2 * f + 1, uv.y)};
+        if constexpr (Odd) y64p[f] = o;
+        else reinterpret_cast<u32x2_t*>(y + pix0)[f] = o;
     };
 #pragma unroll
     for (int k = 0; k < kUPer; ++k) {
@@ -407,17 +534,28 @@ prop2d_phase_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
         for (int j = 0; j < 8; ++j)
             if (f0 + NT * j < pairs) emit_pair(f0 + NT * j, uv[j]);
     }
-    if ((words & 1) && tid == 0) y32[words - 1] = emit_word(words - 1, u32[words - 1]);
+    if constexpr (Odd) {
+        // the last HW mod 4 pixels one by one, 16 bits each (a plane may
+        // start at any element)
+        const int i = 4 * pairs + tid;
+        if (i < HW) {
+            const float v = __uint_as_float(static_cast<uint32_t>(u[pix0 + i]) << 16) *
+                            lds_ref<float>(lay.s + 4u * i);
+            y[pix0 + i] = static_cast<T>(pack_bf16x2(v, v) & 0xffffu);
+        }
+    } else {
+        if ((words & 1) && tid == 0) y32[words - 1] = emit_word(words - 1, u32[words - 1]);
+    }
 }
 
-template <int K, bool Chunked, int NH>
+template <int K, bool Chunked, int NH, bool Odd = false>
 hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, float eps,
                     void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                     hipStream_t stream) {
     using T = uint16_t;
     constexpr int D = 8;   // taps prefetched D steps ahead
     const size_t lds = PhaseLayout(static_cast<int>(H), static_cast<int>(W)).bytes;
-    auto kern = prop2d_phase_kernel<T, K, D, Chunked, NH>;
+    auto kern = prop2d_phase_kernel<T, K, D, Chunked, NH, Odd>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -452,6 +590,13 @@ hipError_t launch_c(const void* x, const void* lam, const void* u, const void* w
                     void* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                     hipStream_t stream) {
     const int64_t Lmax = H > W ? H : W;
+    // an odd side takes the two-wavefront form (its windows need the
+    // registers the one-wavefront form has no room for)
+    if ((H & 1) || (W & 1)) {
+        if (Lmax <= 64) return launch_k<1, Chunked, 64, true>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        if (Lmax <= 128) return launch_k<2, Chunked, 64, true>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+        return launch_k<3, Chunked, 64, true>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    }
     if (phase_two_waves(planes, H, W)) {
         if (Lmax <= 64) return launch_k<1, Chunked, 64>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
         if (Lmax <= 128) return launch_k<2, Chunked, 64>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
@@ -471,7 +616,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool prop2d_phase_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
                            const void* lam, const void* u, const void* w4, const void* y) {
     if (dtype != 1) return false;                         // bf16 planes only
-    if (H > 160 || W > 160 || (H & 1) || (W & 1)) return false;  // K <= 5 positions a lane; whole dwords per line
+    if (H > 160 || W > 160) return false;                 // K <= 5 positions a lane
     if (PhaseLayout(static_cast<int>(H), static_cast<int>(W)).bytes > kLdsBytes) return false;
     if (12 * planes * H * W * 2 > 0x7fffffff) return false;
     return aligned4(x) && aligned4(lam) && aligned4(u) && aligned4(w4) && aligned4(y);
