@@ -29,6 +29,14 @@ backward  : the gradient entry point (gspn_prop2d_4dir_backward) on the same
             `value`); algorithmic bytes = 31 values per pixel-channel (read x,
             lambda, u, gy and 12 taps, write gx, glambda, gu and 12 tap
             gradients)
+pixel_ordered_taps : what a caller holding the LR / RL taps in pixel order
+            ([3][H][W]) pays: a torch transpose of those 6 tap planes into the
+            library's line-major layout, then the call
+workloads : the other configurations, each timed the same way with its own
+            roofline: latent2k (4 x 64 x 148^2 bf16, forward and backward),
+            the same at 147^2 (odd side), base378 (8 x 64 x 27^2 fp32) with one
+            input set (warm: it fits the Infinity Cache) and rotated, wide256
+            (1 x 1024 x 256^2 fp32, forward and backward)
 backward_variants : gspn_prop2d_4dir_ex_backward on the same shape: shared
             taps (groups = 1) and per-channel taps, each with four-segment
             scans (k_chunk = 4); algorithmic bytes 7 + 24 G / C values per
@@ -50,8 +58,8 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "4-dir GSPN propagation GB/s & ms (B=32,C_c=64,74×74) + % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prop2d_latent1k_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "spatial_line_scan_amd", "csrc", f)
-                  for f in ("gspn_kernels.hip", "gspn_prop2d_phase.hip", "gspn_prop2d_pair.hip",
-                            "gspn_internal.h", "gspn_device.h", "gspn_lane.h")]
+                  for f in ("gspn_kernels.hip", "gspn_prop2d_quad.hip", "gspn_internal.h",
+                            "gspn_device.h", "gspn_lane.h")]
 BWD_VALUES_PER_PIXEL = 31
 
 
@@ -322,6 +330,89 @@ def backward_leg(wl, sets, args, dev):
                          "kernel_ms_min": round(float(np.min(kern)), 5)}}
 
 
+def shape_leg(args, dev, B, C, H, W, dtype, backward=False, rotate=True):
+    """gspn_prop2d_4dir (and, with backward, gspn_prop2d_4dir_backward) on a
+    B x C x H x W workload of the given storage type: inputs rotated over
+    sets of at least --rotate-bytes (rotate) or one set reused (warm, cache
+    resident when it fits); HIP-event kernel times and roofline per leg."""
+    import numpy as np
+    import torch
+
+    from spatial_line_scan_amd import gspn, inputs
+    from spatial_line_scan_amd.workloads import Workload
+
+    wl = Workload("shape", B, C, H, W, dtype, (0,))
+    base = inputs.problem_torch(B, C, H, W, 0, dtype, dev)
+    if backward:
+        base["gy"] = inputs.draw_torch(0, "gy", (B, C, H, W), dtype, dev)
+    nsets = max(1, int(np.ceil(args.rotate_bytes / wl.algorithmic_bytes))) if rotate else 1
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    outs = [torch.empty_like(base["x"]) for _ in range(nsets)]
+    torch.cuda.synchronize()
+
+    def fn(i):
+        st = sets[i % nsets]
+        gspn.prop2d_4dir(st["x"], st["lam"], st["u"], st["w"], out=outs[i % nsets])
+
+    wall, kavg, kmin = _timed(fn, args.steps, args.warmup, torch.cuda.current_stream(dev))
+    nbytes = wl.algorithmic_bytes
+    achieved = nbytes / (kavg * 1e-3) / 1e9
+    out = {"B": B, "C": C, "H": H, "W": W, "dtype": dtype,
+           "inputs": "rotated over %d sets" % nsets if rotate else "warm (one set)",
+           "forward": {"ms_per_step": round(wall * 1e3 / args.steps, 5),
+                       "value": round(nbytes / (wall / args.steps) / 1e9, 2), "unit": "GB/s",
+                       "algorithmic_bytes_per_step": nbytes,
+                       "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
+                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                    "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                                    "kernel_ms_avg": round(kavg, 5), "kernel_ms_min": round(kmin, 5)}}}
+    del outs
+    if backward:
+        out["backward"] = backward_leg(wl, sets, args, dev)
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def pixel_ordered_leg(wl, args, dev):
+    """The call a caller holding every direction's taps in pixel order
+    ([4][B][C][3][H][W]) makes: transpose the LR and RL tap planes to the
+    library's line-major layout (a torch copy into a preallocated tensor),
+    then gspn_prop2d_4dir.  Times the transpose, the call and both."""
+    import torch
+
+    from spatial_line_scan_amd import gspn, inputs
+
+    base = inputs.problem_torch(wl.B, wl.C, wl.H, wl.W, 0, wl.dtype, dev)
+    w_pix = base["w"].reshape(4, wl.B, wl.C, 3, wl.H, wl.W).clone()
+    w_lib = torch.empty_like(w_pix)
+    w_lib[:2].copy_(w_pix[:2])
+    y = torch.empty_like(base["x"])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def transpose(i):
+        w_lib[2:].copy_(w_pix[2:].transpose(-1, -2).reshape(2, wl.B, wl.C, 3, wl.H, wl.W))
+
+    def call(i):
+        gspn.prop2d_4dir(base["x"], base["lam"], base["u"], w_lib, out=y)
+
+    def both(i):
+        transpose(i)
+        call(i)
+
+    res = {}
+    for name, fn in (("transpose", transpose), ("call", call), ("transpose_and_call", both)):
+        wall, kavg, kmin = _timed(fn, args.steps, args.warmup, stream)
+        res[name + "_ms"] = round(kavg, 5)
+    res["transposed_bytes"] = 2 * 6 * wl.B * wl.C * wl.H * wl.W * wl.elem_bytes
+    res["note"] = ("one input set, no rotation; the transpose moves 6 of the 12 tap planes "
+                   "(read and write)")
+    del w_pix, w_lib, base
+    torch.cuda.empty_cache()
+    return res
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -346,6 +437,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-variants", action="store_true", help="skip the grouped / chunked legs")
     ap.add_argument("--no-sublayer", action="store_true", help="skip the latent sublayer legs")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads (latent2k, 147 x 147, base378, wide256) and the "
+                         "pixel-ordered tap leg")
     ap.add_argument("--sublayer-only", type=int, default=None, metavar="G",
                     help="run only the latent sublayer leg with G tap groups and print it "
                          "(for profiling its kernels on their own)")
@@ -480,6 +574,18 @@ def main():
         if not args.no_variants:
             print("bench: grouped / chunked backward", file=sys.stderr, flush=True)
             out["backward_variants"] = [ex_backward_leg(wl, args, dev, G, k) for G, k in ((1, 4), (wl.C, 4))]
+    if not args.no_workloads and wl.name == "latent1k":
+        print("bench: pixel-ordered taps", file=sys.stderr, flush=True)
+        out["pixel_ordered_taps"] = pixel_ordered_leg(wl, args, dev)
+        print("bench: other workloads", file=sys.stderr, flush=True)
+        l2, b3, wd = WORKLOADS["latent2k"], WORKLOADS["base378"], WORKLOADS["wide256"]
+        out["workloads"] = {
+            "latent2k": shape_leg(args, dev, l2.B, l2.C, l2.H, l2.W, l2.dtype, backward=True),
+            "latent2k_odd_147": shape_leg(args, dev, l2.B, l2.C, 147, 147, l2.dtype),
+            "base378_warm": shape_leg(args, dev, b3.B, b3.C, b3.H, b3.W, b3.dtype, rotate=False),
+            "base378_rotated": shape_leg(args, dev, b3.B, b3.C, b3.H, b3.W, b3.dtype),
+            "wide256": shape_leg(args, dev, wd.B, wd.C, wd.H, wd.W, wd.dtype, backward=True),
+        }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, sets[0], outs[0])

@@ -73,7 +73,8 @@ def test_backward_small_workloads(name):
 BWD_SHAPES = [(1, 1), (1, 2), (2, 1), (3, 5), (5, 3), (1, 74), (74, 1), (63, 64), (74, 74),
               (127, 33), (13, 148), (120, 120), (148, 148), (300, 5), (5, 300),
               (2, 2), (2, 96), (96, 2), (32, 34), (34, 32), (64, 66), (96, 96), (30, 66), (8, 74),
-              (98, 98), (128, 128), (130, 160), (160, 2), (2, 160), (158, 126), (96, 128), (162, 40)]
+              (98, 98), (128, 128), (130, 160), (160, 2), (2, 160), (158, 126), (96, 128), (162, 40),
+              (27, 27), (37, 37), (147, 147)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])

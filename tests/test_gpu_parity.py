@@ -57,7 +57,8 @@ def test_prop2d_small_workloads_all_seeds(name):
 # accumulates; columns in strips of 32).  The rest take the general kernel.
 EDGE_SHAPES = [(1, 1), (1, 2), (2, 1), (2, 2), (3, 5), (5, 3), (1, 74), (74, 1), (63, 64), (64, 65),
                (65, 63), (74, 74), (127, 33), (13, 148), (148, 148), (256, 7),
-               (98, 98), (128, 128), (130, 160), (160, 2), (2, 160), (158, 126), (96, 128), (162, 40)]
+               (98, 98), (128, 128), (130, 160), (160, 2), (2, 160), (158, 126), (96, 128), (162, 40),
+               (27, 27), (37, 37), (75, 75), (147, 147), (147, 146), (33, 147)]
 # fp32 only: the one-launch-per-direction kernel (bf16 planes this large are
 # rejected: no bf16 kernel holds their direction sum)
 WIDE_SHAPES = [(100, 100), (4, 256), (256, 4), (200, 100), (100, 196), (148, 152), (256, 256),
