@@ -374,6 +374,62 @@ def shape_leg(args, dev, B, C, H, W, dtype, backward=False, rotate=True):
     return out
 
 
+def scan_dir_leg(wl, args, dev):
+    """gspn_scan_dir on the workload's shape over rotated input sets.  One
+    direction alone (y = u h) reads x, lambda, u and that direction's three
+    tap planes and writes y: 7 values a pixel.  Timed for each direction with
+    raw taps, for top-down with pre-normalised taps, and for the four
+    directions as four calls into one output (top-down writes y, the other
+    three add to it and so also read it: 31 values a pixel)."""
+    import numpy as np
+    import torch
+
+    from spatial_line_scan_amd import gspn, inputs
+
+    B, C, H, W = wl.B, wl.C, wl.H, wl.W
+    base = inputs.problem_torch(B, C, H, W, 0, wl.dtype, dev)
+    base["w"] = base["w"].view(4, B, C, 3, H * W)
+    base["wn"] = (0.5 * torch.tanh(base["w"][0].float())).to(base["w"].dtype).contiguous()
+    one = 7 * wl.elem_bytes * wl.pixels
+    nsets = max(1, int(np.ceil(args.rotate_bytes / one)))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    outs = [torch.empty_like(base["x"]) for _ in range(nsets)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def leg(fn, nbytes):
+        wall, kavg, kmin = _timed(fn, args.steps, args.warmup, stream)
+        achieved = nbytes / (kavg * 1e-3) / 1e9
+        return {"ms_per_step": round(wall * 1e3 / args.steps, 5),
+                "value": round(nbytes / (wall / args.steps) / 1e9, 2), "unit": "GB/s",
+                "algorithmic_bytes_per_step": nbytes,
+                "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                             "kernel_ms_avg": round(kavg, 5), "kernel_ms_min": round(kmin, 5)}}
+
+    def one_dir(d, key="w"):
+        def fn(i):
+            st = sets[i % nsets]
+            w = st[key] if key == "wn" else st["w"][d]
+            gspn.scan_dir(st["x"], st["lam"], st["u"], w, d, w_is_raw=key == "w", out=outs[i % nsets])
+        return fn
+
+    def four(i):
+        st = sets[i % nsets]
+        for d in range(4):
+            gspn.scan_dir(st["x"], st["lam"], st["u"], st["w"][d], d, out=outs[i % nsets],
+                          accumulate=d > 0)
+
+    res = {"B": B, "C": C, "H": H, "W": W, "dtype": wl.dtype, "rotated_input_sets": nsets}
+    for d, name in enumerate(("top_down", "bottom_up", "left_right", "right_left")):
+        res[name] = leg(one_dir(d), one)
+    res["top_down_normalised_taps"] = leg(one_dir(0, "wn"), one)
+    res["four_calls_accumulated"] = leg(four, 31 * wl.elem_bytes * wl.pixels)
+    del sets, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def pixel_ordered_leg(wl, args, dev):
     """The call a caller holding every direction's taps in pixel order
     ([4][B][C][3][H][W]) makes: transpose the LR and RL tap planes to the
@@ -437,12 +493,15 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-variants", action="store_true", help="skip the grouped / chunked legs")
     ap.add_argument("--no-sublayer", action="store_true", help="skip the latent sublayer legs")
+    ap.add_argument("--no-scan-dir", action="store_true", help="skip the one-direction legs")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other workloads (latent2k, 147 x 147, base378, wide256) and the "
                          "pixel-ordered tap leg")
     ap.add_argument("--sublayer-only", type=int, default=None, metavar="G",
                     help="run only the latent sublayer leg with G tap groups and print it "
                          "(for profiling its kernels on their own)")
+    ap.add_argument("--scan-dir-only", action="store_true",
+                    help="run only the one-direction legs and print them")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only warmup + K backward launches and print their timing "
                          "(for profiling the backward kernel on its own)")
@@ -478,6 +537,9 @@ def main():
         return
     if args.sublayer_only is not None:
         print(json.dumps({"sublayer": sublayer_leg(args, dev, args.sublayer_only)}), flush=True)
+        return
+    if args.scan_dir_only:
+        print(json.dumps({"scan_dir": scan_dir_leg(wl, args, dev)}), flush=True)
         return
     print("bench: drawing %s inputs" % wl.name, file=sys.stderr, flush=True)
     base = inputs.problem_torch(wl.B, wl.C, wl.H, wl.W, 0, wl.dtype, dev)
@@ -574,6 +636,9 @@ def main():
         if not args.no_variants:
             print("bench: grouped / chunked backward", file=sys.stderr, flush=True)
             out["backward_variants"] = [ex_backward_leg(wl, args, dev, G, k) for G, k in ((1, 4), (wl.C, 4))]
+    if not args.no_scan_dir:
+        print("bench: one-direction scans", file=sys.stderr, flush=True)
+        out["scan_dir"] = scan_dir_leg(wl, args, dev)
     if not args.no_workloads and wl.name == "latent1k":
         print("bench: pixel-ordered taps", file=sys.stderr, flush=True)
         out["pixel_ordered_taps"] = pixel_ordered_leg(wl, args, dev)

@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["gspn_host.cpp", "gspn_kernels.hip", "gspn_prop2d_pair.hip", "gspn_prop2d_phase.hip", "gspn_prop2d_quad.hip", "gspn_prop2d_duo.hip",
            "gspn_backward.hip", "gspn_backward_pair.hip", "gspn_sublayer.hip", "gspn_conv1x1.hip",
-           "gspn_prop2d_wide.hip", "gspn_backward_wide.hip", "gspn_noalloc.hip"]
+           "gspn_prop2d_wide.hip", "gspn_backward_wide.hip", "gspn_noalloc.hip",
+           "gspn_scan_dir.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -35,6 +35,13 @@ hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const vo
                          float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                          const PropOpts& opts, hipStream_t stream);
 
+// Fast path of gspn_scan_dir: one wavefront per plane, lambda x and the
+// hidden state in LDS (gspn_scan_dir.hip).
+bool scan_dir_fast_eligible(int64_t H, int64_t W, int dir);
+hipError_t launch_scan_dir_fast(const void* x, const void* lam, const void* u, const void* w,
+                                int w_is_raw, float eps, void* y, int accumulate, int dtype,
+                                int64_t planes, int64_t H, int64_t W, int dir, hipStream_t stream);
+
 // Fast path of gspn_prop2d_4dir: two wavefronts per plane (gspn_prop2d_pair.hip).
 bool prop2d_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
                           const void* lam, const void* u, const void* w4, const void* y);

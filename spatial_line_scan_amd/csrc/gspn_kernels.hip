@@ -238,6 +238,9 @@ hipError_t launch_normalize(const void* w_raw, void* w_norm, int dtype, int64_t 
 hipError_t launch_scan_dir(const void* x, const void* lam, const void* u, const void* w,
                            int w_is_raw, float eps, void* y, int accumulate, int dtype,
                            int64_t planes, int64_t H, int64_t W, int dir, hipStream_t stream) {
+    if (scan_dir_fast_eligible(H, W, dir))
+        return launch_scan_dir_fast(x, lam, u, w, w_is_raw, eps, y, accumulate, dtype, planes, H,
+                                    W, dir, stream);
     return dtype == 0 ? scan_dir_t<float>(x, lam, u, w, w_is_raw, eps, y, accumulate, planes, H,
                                           W, dir, stream)
                       : scan_dir_t<uint16_t>(x, lam, u, w, w_is_raw, eps, y, accumulate,

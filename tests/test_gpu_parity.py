@@ -242,8 +242,16 @@ def test_prop2d_writes_into_given_output_and_rejects_big_bf16_planes():
 
 # ------------------------------------------------------------------ scan_dir
 
+# Planes whose lambda x fits in LDS as fp32 (up to 40956 pixels) take the
+# one-wavefront kernel for lines up to 256 (K = 1 .. 4 positions a lane:
+# lines of 1..64, 65..128, 129..192, 193..256); longer lines and larger planes
+# take the general kernel: (1, 300) rows, (210, 210) every direction.
+SCAN_DIR_SHAPES = [(1, 1), (7, 1), (1, 9), (16, 16), (27, 27), (33, 70), (74, 74), (65, 129),
+                   (129, 65), (190, 200), (256, 40), (3, 193), (1, 300), (210, 210)]
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("H,W", [(1, 1), (7, 1), (1, 9), (16, 16), (27, 27), (33, 70), (74, 74)])
+@pytest.mark.parametrize("H,W", SCAN_DIR_SHAPES)
 def test_scan_dir_raw_and_normalised(H, W, dtype):
     B, C = 2, 3
     p = _problem(B, C, H, W, 5 + H * W, dtype)
@@ -260,6 +268,39 @@ def test_scan_dir_raw_and_normalised(H, W, dtype):
         torch.cuda.synchronize()
         r = oracle.scan_dir(p["x"], p["lam"], p["u"], wn, d, w_is_raw=False)
         assert_close(_np(y), r, RTOL[dtype], "normalised dir %d" % d)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_scan_dir_latent1k_sampled_planes(dtype):
+    """B=32, C=64, 74x74 (the latent1k shape): every direction, raw and
+    pre-normalised taps, and an accumulated four-direction sum, checked on
+    sampled planes."""
+    B, C, H, W = 32, 64, 74, 74
+    p = _problem(B, C, H, W, 4242, dtype)
+    w4 = p["w"].view(4, B, C, 3, H * W)
+    planes = _sampled_planes(B, C)
+    acc = torch.zeros_like(p["x"])
+    for d in range(4):
+        wd = w4[d].contiguous()
+        wn = (0.5 * torch.tanh(wd.float())).to(wd.dtype).contiguous()
+        say("scan_dir latent1k", d, dtype)
+        y_raw = gspn.scan_dir(p["x"], p["lam"], p["u"], wd, d)
+        y_nrm = gspn.scan_dir(p["x"], p["lam"], p["u"], wn, d, w_is_raw=False)
+        gspn.scan_dir(p["x"], p["lam"], p["u"], wd, d, out=acc, accumulate=True)
+        torch.cuda.synchronize()
+        for b, c in planes:
+            sl = (slice(b, b + 1), slice(c, c + 1))
+            args = [p[k][sl] for k in ("x", "lam", "u")]
+            r = oracle.scan_dir(*args, wd[sl], d, w_is_raw=True)
+            assert_close(_np(y_raw[sl]), r, RTOL[dtype], "raw dir %d plane %d,%d" % (d, b, c))
+            r = oracle.scan_dir(*args, wn[sl], d, w_is_raw=False)
+            assert_close(_np(y_nrm[sl]), r, RTOL[dtype], "normalised dir %d plane %d,%d" % (d, b, c))
+    if dtype == "fp32":
+        for b, c in planes:
+            sl = (slice(b, b + 1), slice(c, c + 1))
+            r = oracle.prop2d(*[p[k][sl] for k in ("x", "lam", "u")],
+                              w4[:, b:b + 1, c:c + 1].contiguous())
+            assert_close(_np(acc[sl]), r, RTOL[dtype], "accumulated plane %d,%d" % (b, c))
 
 
 def test_scan_dir_accumulate_sums_to_prop2d():
