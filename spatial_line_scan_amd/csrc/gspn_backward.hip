@@ -243,8 +243,12 @@ int64_t plane_kernel_workspace_bytes(int64_t planes, int64_t H, int64_t W) {
 }
 
 // Per-channel fp32 tap gradients of channels that share taps, [4][planes][3][H W].
+// Channels sharing taps: their fp32 tap gradients (or partial sums of tap
+// products), then the group's normalised weights (pair kernel).
 int64_t group_grad_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg) {
-    return cpg > 1 ? (12 * planes * H * W * 4 + 255) & ~static_cast<int64_t>(255) : 0;
+    return cpg > 1 ? ((12 * planes * H * W * 4 + 255) & ~static_cast<int64_t>(255)) +
+                         prop2d_backward_pair_shared_weights_bytes(planes, H, W, cpg)
+                   : 0;
 }
 
 // Tap gradient of each group: the sum over its channels, in channel order.
@@ -328,6 +332,15 @@ hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u,
                              ? prop2d_backward_pair_workspace_bytes(planes, H, W) : 0;
     const int64_t avail = ws ? (general > pair ? general : pair) : 0;
     if (prop2d_backward_pair_eligible(dtype, planes, H, W, ptrs, 9, rest)) {
+        if (grouped) {
+            // partial sums at the start of the workspace, the weights after
+            // the per-channel region
+            float* part = static_cast<float*>(ws);
+            float* wpre = reinterpret_cast<float*>(
+                static_cast<char*>(ws) + ((12 * planes * H * W * 4 + 255) & ~static_cast<int64_t>(255)));
+            return launch_prop2d_backward_pair_shared(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, part, wpre,
+                                                      rest, dtype, planes, H, W, o, stream);
+        }
         e = launch_prop2d_backward_pair(x, lam, u, w4, gy, eps, gx, glam, gu, gdst, grouped, rest,
                                         dtype, planes, H, W, o, stream);
     } else if (prop2d_backward_wide_eligible(dtype, planes, H, W, ptrs, 9, rest, avail)) {

@@ -43,6 +43,7 @@
 #include "gspn_internal.h"
 #include "gspn_lane.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace gspn {
@@ -85,8 +86,9 @@ struct PairBwdLayout {
                                       // array; tap-gradient staging lines
     static constexpr int dum = 0, ldum = 8;
     __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
-    // gsize: bytes of a staged tap gradient
-    __host__ __device__ PairBwdLayout(int NL, int L, bool narrow, int gsize) {
+    // gsize: bytes of a staged tap gradient; nstage: staging sets (two when
+    // the workgroup's planes add their tap gradients)
+    __host__ __device__ PairBwdLayout(int NL, int L, bool narrow, int gsize, int nstage = 1) {
         constexpr int nh = 64;   // lanes a direction takes
         const int w = narrow ? 2 : 4;
         a = a16(32 + 2 * w * L);   // 16 dummy bytes per wavefront
@@ -99,7 +101,7 @@ struct PairBwdLayout {
             end = lb + (NL + 2) * L;
         }
         stage = a16(end);
-        bytes = stage + 6 * nh * ((L + nh - 1) / nh) * gsize;   // K = ceil(L / nh) slots a lane
+        bytes = stage + nstage * 6 * nh * ((L + nh - 1) / nh) * gsize;   // K = ceil(L / nh) slots a lane
     }
 };
 
@@ -173,8 +175,17 @@ __device__ __forceinline__ f32x2_t load_pair(const T* p, size_t e) {
 // are written per channel, as GT, to gwd ([4][planes][3][..][..], gw_bytes).
 // Chunked: k_chunk > 1.  A wavefront per direction; they meet only between
 // passes.
-template <typename T, typename GT, int K, int D, bool Cols, bool Chunked>
-__global__ void __launch_bounds__(128)
+// Pre (channels sharing taps): the workgroup holds cc planes of one tap
+// group, a wavefront pair each.  The weights come normalised in fp32 from
+// wpre ([4][planes / cpg][3][..][..], wpre_bytes), so no step evaluates a
+// transcendental, and the adjoint produces the tap products
+// e_k(i, p) = g_i[p] h_{i-1}[p+k-1] in place of the tap gradients: the cc
+// planes' products of a line are added on chip in plane order, and the sum
+// goes to gwd as fp32, one plane of partial sums per workgroup
+// ([4][planes / cc][3][..][..]).  The normalisation's Jacobian is applied
+// once per group afterwards.
+template <typename T, typename GT, int K, int D, bool Cols, bool Chunked, bool Pre, int CC>
+__global__ void __launch_bounds__(128 * CC)
 prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml,
                             const T* __restrict__ ul, const T* __restrict__ gyl,
                             const T* __restrict__ w4, int w4_bytes, GT* __restrict__ gwd,
@@ -183,23 +194,39 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                             float* __restrict__ s_ws, float* __restrict__ g_ws,
                             const T* __restrict__ x, const T* __restrict__ lam,
                             const T* __restrict__ gy, T* __restrict__ gx, T* __restrict__ glam,
-                            T* __restrict__ gu) {
+                            T* __restrict__ gu, const float* __restrict__ wpre, int wpre_bytes) {
+    static_assert(!Pre || sizeof(GT) == 4, "partial sums of tap products are fp32");
+    static_assert(CC == 1 || Pre, "planes are added only with prepared weights");
+    constexpr int cc = CC;
     constexpr int ES = sizeof(T);
     constexpr int NW = window_words<T, K>();
+    constexpr int TW = Pre ? K : NW;        // words of a tap window: fp32 weights or raw taps
     constexpr bool kNarrow = ES == 2;
     constexpr int VW = kNarrow ? 2 : 4;     // bytes of a value in the A / B array
     const int HW = NL * L;
     constexpr int GS = sizeof(GT);
-    const PairBwdLayout lay(NL, L, kNarrow, GS);
-    constexpr int NT = 128;                 // threads of the workgroup
-    const int tid = threadIdx.x;
+    PairBwdLayout lay(NL, L, kNarrow, GS, CC > 1 ? 2 : 1);
+    constexpr int NT = 128;                 // threads of a plane's wavefront pair
+    const int pslot = Pre ? static_cast<int>(threadIdx.x >> 7) : 0;   // the workgroup's plane
+    const int tid = Pre ? static_cast<int>(threadIdx.x & 127) : static_cast<int>(threadIdx.x);
     const int lane = tid & 63;
     const int half = tid >> 6;              // the wavefront: its direction
     const int q = lane;
     const bool fwd = half == 0;
-    // orders the LDS accesses of the two wavefronts
+    // each plane of the workgroup has its own copy of the layout
+    const int pstride = lay.bytes;
+    const uint32_t stage0 = static_cast<uint32_t>(lay.stage);   // plane 0's staging
+    {
+        const int pb = pslot * pstride;
+        lay.a += pb;
+        lay.b += pb;
+        lay.la += pb;
+        lay.lb += pb;
+        lay.stage += pb;
+    }
+    // orders the LDS accesses of the workgroup's wavefronts
     auto sync = [&]() { lds_barrier(); };
-    const int plane = blockIdx.x;
+    const int plane = Pre ? static_cast<int>(blockIdx.x) * cc + pslot : static_cast<int>(blockIdx.x);
     const size_t pix0 = static_cast<size_t>(plane) * HW;
 
     // each wavefront zeroes its own dummy words before it uses them: the
@@ -207,7 +234,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     // only by dropped taps) then follow that wavefront's program order alone,
     // so even the signs of the zero tap gradients they touch are the same
     // from run to run
-    const uint32_t dum0 = 16u * half;
+    const uint32_t dum0 = static_cast<uint32_t>(pslot * pstride) + 16u * half;
     if (lane < 4) lds_at<float>(dum0 + 4u * lane) = 0.0f;
     // zero lines: h before a scan's first line
     for (int f = tid; f < L; f += NT) {
@@ -273,6 +300,21 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
     const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
     const uint32_t tap_b = static_cast<uint32_t>(((dir0 + half) * (planes / cpg) + plane / cpg) * 3 * HW) * ES;
+    // the window of this lane on line 0 of its direction's taps, and the
+    // bytes of a line: raw taps, or fp32 weights (Pre)
+    __amdgpu_buffer_rsrc_t trs[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        if constexpr (Pre)
+            trs[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wpre + static_cast<size_t>(k) * HW), 0,
+                                                       wpre_bytes - k * HW * 4, kBufFlags);
+        else
+            trs[k] = taps[k];
+    }
+    const uint32_t t_base = Pre ? static_cast<uint32_t>(((dir0 + half) * (planes / cpg) + plane / cpg) * 3 * HW) * 4u +
+                                      static_cast<uint32_t>(K * q) * 4u
+                                : tap_b + win_b;
+    const uint32_t t_line = static_cast<uint32_t>(L) * (Pre ? 4u : static_cast<uint32_t>(ES));
     // segments of a chunked scan; a segment's first line reads no line before it
     const int seg = Chunked ? (NL + k_chunk - 1) / k_chunk : NL;
     const uint32_t line_b = static_cast<uint32_t>(L) * ES;
@@ -373,15 +415,17 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     {
         const uint32_t lo0 = fwd ? 0u : static_cast<uint32_t>(NL - 1) * line_b;
         const uint32_t dlo = fwd ? line_b : 0u - line_b;
-        uint32_t lo = tap_b + win_b + lo0;
+        const uint32_t dto = fwd ? t_line : 0u - t_line;
+        uint32_t lo = t_base + (fwd ? 0u : static_cast<uint32_t>(NL - 1) * t_line);
         uint32_t xo = static_cast<uint32_t>(pix0) * ES + win_b + lo0;
-        words_t<NW> tbuf[D][3], xbuf[D], lbuf[D];
+        words_t<TW> tbuf[D][3];
+        words_t<NW> xbuf[D], lbuf[D];
         auto load_line = [&](int d) {
 #pragma unroll
-            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
+            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<TW>(trs[k], lo);
             xbuf[d] = load_words<NW>(xs, xo);
             lbuf[d] = load_words<NW>(ls, xo);
-            lo += dlo;
+            lo += dto;
             xo += dlo;
         };
 #pragma unroll
@@ -411,12 +455,23 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         auto step = [&](int s, int d) {
             asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
             asm volatile("" : "+v"(xbuf[d]), "+v"(lbuf[d]));
+            // Pre: s0..s2 are the normalised weights and r is 1
             float s0[K], s1[K], s2[K], t[K], r[K], b[K];
 #pragma unroll
             for (int j = 0; j < K; ++j)
                 b[j] = window_elem<T, K, NW>(lbuf[d], j, sx[j], sx[j]) *
                        window_elem<T, K, NW>(xbuf[d], j, sx[j], sx[j]);
-            normalise(tbuf[d], s0, s1, s2, t, r);
+            if constexpr (Pre) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    s0[j] = __uint_as_float(word<TW>(tbuf[d][0], j));
+                    s1[j] = __uint_as_float(word<TW>(tbuf[d][1], j));
+                    s2[j] = __uint_as_float(word<TW>(tbuf[d][2], j));
+                    t[j] = r[j] = 1.0f;
+                }
+            } else {
+                normalise(tbuf[d], s0, s1, s2, t, r);
+            }
 #pragma unroll
             for (int j = 0; j < K; ++j)
                 asm volatile("" : "+v"(lo), "+v"(xo) : "v"(s0[j]), "v"(s1[j]), "v"(s2[j]), "v"(r[j]), "v"(b[j]));
@@ -437,13 +492,14 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 float m = s1[j] * h[j];
                 m = fmaf(s0[j], hl, m);
                 m = fmaf(s2[j], hr, m);
-                hn[j] = fmaf(m, r[j], b[j]);
+                hn[j] = Pre ? m + b[j] : fmaf(m, r[j], b[j]);
             }
             // fp32 slots past the line end hold 0 (their windows read the next
-            // line or plane; bf16 ones decode to 0 and stay 0)
+            // line or plane; bf16 ones decode to 0 and stay 0; fp32 weights
+            // past a line's end are the next line's, so Pre zeroes them too)
 #pragma unroll
             for (int j = 0; j < K; ++j) {
-                if constexpr (!kB16) hn[j] = valid[j] ? hn[j] : 0.0f;
+                if constexpr (!kB16 || Pre) hn[j] = valid[j] ? hn[j] : 0.0f;
                 h[j] = hn[j];
                 put(aH[j], aL[j], hn[j]);
                 aH[j] += dH[j];
@@ -478,15 +534,17 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         const int i0 = fwd ? NL - 1 : 0;
         const uint32_t lo0 = static_cast<uint32_t>(i0) * line_b;
         const uint32_t dlo = fwd ? 0u - line_b : line_b;
-        uint32_t lo = tap_b + win_b + lo0;
+        const uint32_t dto = fwd ? 0u - t_line : t_line;
+        uint32_t lo = t_base + static_cast<uint32_t>(i0) * t_line;
         uint32_t uo = static_cast<uint32_t>(pix0) * ES + win_b + lo0;
-        words_t<NW> tbuf[D][3], ubuf[D], gbuf[D];
+        words_t<TW> tbuf[D][3];
+        words_t<NW> ubuf[D], gbuf[D];
         auto load_line = [&](int d) {
 #pragma unroll
-            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
+            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<TW>(trs[k], lo);
             ubuf[d] = load_words<NW>(us, uo);
             gbuf[d] = load_words<NW>(gs, uo);
-            lo += dlo;
+            lo += dto;
             uo += dlo;
         };
 #pragma unroll
@@ -501,25 +559,35 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         constexpr int NR = (3 * K * GS + 3) / 4; // ceil(3 * SL * GS / 4 / 64)
         constexpr int kLines = 3;
         const int per_line = L * GS / 4;
+        // Pre, several planes: the workgroup's planes of a direction each
+        // write a share of its three lines, dwords f = share + lane + 64 t,
+        // adding that dword of every plane's staging (plane stride pstride)
+        constexpr bool summed = CC > 1;
+        const int share = summed ? (kLines * per_line + cc - 1) / cc : kLines * per_line;
+        const int f0 = summed ? pslot * share : 0;
+        // partial-sum planes (Pre) or per-channel planes, and this one's index
+        const int out_planes = Pre ? planes / cc : planes;
+        const int out_plane = Pre ? static_cast<int>(blockIdx.x) : plane;
         uint32_t rd[NR], go[NR], gd[NR];
 #pragma unroll
         for (int t = 0; t < NR; ++t) {
-            const int f = lane + 64 * t;
-            rd[t] = lay.stage;
+            const int f = f0 + lane + 64 * t;
+            rd[t] = summed ? stage0 : lay.stage;
             go[t] = kDrop;
             gd[t] = 0;
-            if (f < kLines * per_line) {
+            if (lane + 64 * t < share && f < kLines * per_line) {
                 const int hk = 3 * half + f / per_line;
                 const int m = f - (f / per_line) * per_line;
                 const int h = hk / 3, k = hk - 3 * h;
                 const int start = h == 0 ? NL - 1 : 0;      // first adjoint line of that wavefront
-                rd[t] = lay.stage + hk * SL * GS + 4 * m;
-                go[t] = static_cast<uint32_t>((((dir0 + h) * planes + plane) * 3 + k) * HW * GS +
+                rd[t] = (summed ? stage0 : static_cast<uint32_t>(lay.stage)) + hk * SL * GS + 4 * m;
+                go[t] = static_cast<uint32_t>((((dir0 + h) * out_planes + out_plane) * 3 + k) * HW * GS +
                                               start * L * GS + 4 * m);
                 gd[t] = h == 0 ? 0u - static_cast<uint32_t>(L * GS) : static_cast<uint32_t>(L * GS);
             }
         }
         const uint32_t my_stage = lay.stage + 3 * half * SL * GS;
+        const uint32_t set_bytes = 6u * SL * GS;    // one staging set of a plane
         // adjoint step of the next restart line: its taps read nothing (tap
         // gradient 0) and the line before it receives no adjoint term from it
         int next_restart = fwd ? (NL - 1) - ((NL - 1) / seg) * seg : seg - 1;
@@ -549,12 +617,23 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         auto step = [&](int s, int d) {
             asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
             asm volatile("" : "+v"(ubuf[d]), "+v"(gbuf[d]));
+            // Pre: s0..s2 are the normalised weights and r is 1
             float s0[K], s1[K], s2[K], t[K], r[K], ugy[K];
 #pragma unroll
             for (int j = 0; j < K; ++j)
                 ugy[j] = window_elem<T, K, NW>(ubuf[d], j, sx[j], sx[j]) *
                          window_elem<T, K, NW>(gbuf[d], j, sx[j], sx[j]);
-            normalise(tbuf[d], s0, s1, s2, t, r);
+            if constexpr (Pre) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    s0[j] = __uint_as_float(word<TW>(tbuf[d][0], j));
+                    s1[j] = __uint_as_float(word<TW>(tbuf[d][1], j));
+                    s2[j] = __uint_as_float(word<TW>(tbuf[d][2], j));
+                    t[j] = r[j] = 1.0f;
+                }
+            } else {
+                normalise(tbuf[d], s0, s1, s2, t, r);
+            }
 #pragma unroll
             for (int j = 0; j < K; ++j)
                 asm volatile("" : "+v"(lo), "+v"(uo) : "v"(s0[j]), "v"(s1[j]), "v"(s2[j]), "v"(r[j]), "v"(ugy[j]));
@@ -574,7 +653,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             for (int j = 0; j < K; ++j) {
                 g[j] += j < K - 1 ? P0[j + 1] : P0n;
                 g[j] += j > 0 ? P2[j - 1] : P2p;
-                if constexpr (!kB16) g[j] = valid[j] ? g[j] : 0.0f;
+                if constexpr (!kB16 || Pre) g[j] = valid[j] ? g[j] : 0.0f;
             }
 
             // tap gradients of line i
@@ -593,6 +672,16 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 const float hl = j > 0 ? hp[j - 1] : hl0;
                 const float hr = j < K - 1 ? hp[j + 1] : hrK;
                 const float e0 = g[j] * hl, e1 = g[j] * hp[j], e2 = g[j] * hr;
+                if constexpr (Pre) {
+                    // the tap products; the Jacobian comes after the group sum
+                    gz0[j] = e0;
+                    gz1[j] = e1;
+                    gz2[j] = e2;
+                    w0p[j] = s0[j];
+                    w1p[j] = s1[j];
+                    w2p[j] = s2[j];
+                    continue;
+                }
                 const float wn0 = s0[j] * r[j], wn1 = s1[j] * r[j], wn2 = s2[j] * r[j];
                 float n0 = e0, n1 = e1, n2 = e2;
                 if (t[j] > eps) {
@@ -609,17 +698,42 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 w1p[j] = wn1;
                 w2p[j] = wn2;
             }
-            stage_put<GT, K>(my_stage, q, gz0);
-            stage_put<GT, K>(my_stage + SL * GS, q, gz1);
-            stage_put<GT, K>(my_stage + 2 * SL * GS, q, gz2);
-            // the staging lines are written with 16- and 32-bit stores and read
-            // back as dwords: keep the compiler from moving the reads above
-            // the writes (the LDS then executes them in program order)
-            asm volatile("" ::: "memory");
+            if constexpr (summed) {
+                // staging sets alternate by step: a set is rewritten two steps
+                // later, after every wavefront has passed the barrier between
+                const uint32_t set = static_cast<uint32_t>(s & 1) * set_bytes;
+                stage_put<GT, K>(my_stage + set, q, gz0);
+                stage_put<GT, K>(my_stage + set + SL * GS, q, gz1);
+                stage_put<GT, K>(my_stage + set + 2 * SL * GS, q, gz2);
+                sync();
+                // this wavefront's share is at most 3 K 64 / CC dwords
+                constexpr int NRS = (3 * K + CC - 1) / CC;
+                static_assert(NRS <= NR, "a share fits the read-back slots");
 #pragma unroll
-            for (int t = 0; t < NR; ++t) {
-                __builtin_amdgcn_raw_buffer_store_b32(lds_at<uint32_t>(rd[t]), gws, go[t], 0, 0);
-                go[t] += gd[t];
+                for (int t = 0; t < NRS; ++t) {
+                    float v[CC];
+#pragma unroll
+                    for (int c = 0; c < CC; ++c)
+                        v[c] = lds_at<float>(rd[t] + set + static_cast<uint32_t>(c * pstride));
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < CC; ++c) acc += v[c];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), gws, go[t], 0, 0);
+                    go[t] += gd[t];
+                }
+            } else {
+                stage_put<GT, K>(my_stage, q, gz0);
+                stage_put<GT, K>(my_stage + SL * GS, q, gz1);
+                stage_put<GT, K>(my_stage + 2 * SL * GS, q, gz2);
+                // the staging lines are written with 16- and 32-bit stores and
+                // read back as dwords: keep the compiler from moving the reads
+                // above the writes (the LDS then executes them in program order)
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int t = 0; t < NR; ++t) {
+                    __builtin_amdgcn_raw_buffer_store_b32(lds_at<uint32_t>(rd[t]), gws, go[t], 0, 0);
+                    go[t] += gd[t];
+                }
             }
 
 #pragma unroll
@@ -739,25 +853,38 @@ struct PassArgs {
     float *s_ws, *g_ws;
     const T *x, *lam, *gy;          // pixel order (column pair's outputs)
     T *gx, *glam, *gu;
+    const float* wpre = nullptr;    // Pre: normalised fp32 weights
+    int wpre_bytes = 0;
+    int cc = 1;                     // Pre: planes a workgroup
 };
 
-template <typename T, typename GT, int K, bool Cols, bool Chunked>
-hipError_t launch_pass(const PassArgs<T, GT>& a, hipStream_t stream) {
+template <typename T, typename GT, int K, bool Cols, bool Chunked, bool Pre, int CC>
+hipError_t launch_pass_cc(const PassArgs<T, GT>& a, hipStream_t stream) {
     constexpr int D = 4;   // lines prefetched ahead (the steps are long; a deeper unroll outgrows the instruction cache)
-    const size_t lds = PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L), sizeof(T) == 2,
-                                     sizeof(GT)).bytes;
-    auto kern = prop2d_backward_pair_kernel<T, GT, K, D, Cols, Chunked>;
+    constexpr int cc = CC;
+    const size_t lds = cc * static_cast<size_t>(PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L),
+                                                              sizeof(T) == 2, sizeof(GT), cc > 1 ? 2 : 1).bytes);
+    auto kern = prop2d_backward_pair_kernel<T, GT, K, D, Cols, Chunked, Pre, CC>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    kern<<<dim3(static_cast<unsigned>(a.planes)), dim3(128), lds, stream>>>(
+    kern<<<dim3(static_cast<unsigned>(a.planes / cc)), dim3(128 * cc), lds, stream>>>(
         a.xl, a.ll, a.ul, a.gl, a.w4, a.w4_bytes, a.gwd, a.gw_bytes, a.cpg, a.k_chunk, a.eps,
         static_cast<int>(a.planes), static_cast<int>(a.NL), static_cast<int>(a.L), a.dir0, a.s_ws,
-        a.g_ws, a.x, a.lam, a.gy, a.gx, a.glam, a.gu);
+        a.g_ws, a.x, a.lam, a.gy, a.gx, a.glam, a.gu, a.wpre, a.wpre_bytes);
     return hipGetLastError();
+}
+
+template <typename T, typename GT, int K, bool Cols, bool Chunked, bool Pre>
+hipError_t launch_pass(const PassArgs<T, GT>& a, hipStream_t stream) {
+    if constexpr (Pre) {
+        if (a.cc == 4) return launch_pass_cc<T, GT, K, Cols, Chunked, true, 4>(a, stream);
+        if (a.cc == 2) return launch_pass_cc<T, GT, K, Cols, Chunked, true, 2>(a, stream);
+    }
+    return launch_pass_cc<T, GT, K, Cols, Chunked, Pre, 1>(a, stream);
 }
 
 // K = ceil(L / 64) positions a lane.  A wavefront per direction needs no
@@ -765,21 +892,23 @@ hipError_t launch_pass(const PassArgs<T, GT>& a, hipStream_t stream) {
 // wavefronts a SIMD hide more of each other's latency than the halves of
 // one wavefront (K = ceil(L / 32)) saved in idle slots: latent1k 0.480 ms
 // against 0.505, 148 x 148 (one plane per CU) 0.42 against 0.58.
-template <typename T, typename GT, bool Cols>
+template <typename T, typename GT, bool Cols, bool Pre>
 hipError_t launch_pass_k(const PassArgs<T, GT>& a, hipStream_t stream) {
     const bool ch = a.k_chunk > 1;
     if (a.L <= 64)
-        return ch ? launch_pass<T, GT, 1, Cols, true>(a, stream) : launch_pass<T, GT, 1, Cols, false>(a, stream);
+        return ch ? launch_pass<T, GT, 1, Cols, true, Pre>(a, stream) : launch_pass<T, GT, 1, Cols, false, Pre>(a, stream);
     if (a.L <= 128)
-        return ch ? launch_pass<T, GT, 2, Cols, true>(a, stream) : launch_pass<T, GT, 2, Cols, false>(a, stream);
-    return ch ? launch_pass<T, GT, 3, Cols, true>(a, stream) : launch_pass<T, GT, 3, Cols, false>(a, stream);
+        return ch ? launch_pass<T, GT, 2, Cols, true, Pre>(a, stream) : launch_pass<T, GT, 2, Cols, false, Pre>(a, stream);
+    return ch ? launch_pass<T, GT, 3, Cols, true, Pre>(a, stream) : launch_pass<T, GT, 3, Cols, false, Pre>(a, stream);
 }
 
-template <typename T, typename GT>
+// gwd_: per-channel tap gradients as GT, or (Pre) the fp32 partial sums of
+// the tap products, one plane per cc planes; wpre: the normalised weights.
+template <typename T, typename GT, bool Pre>
 hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, const void* w4_,
                            const void* gy_, float eps, void* gx_, void* glam_, void* gu_, void* gwd_,
                            void* ws_, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
-                           hipStream_t stream) {
+                           hipStream_t stream, const float* wpre = nullptr, int cc = 1) {
     char* ws = static_cast<char*>(ws_);
     const PairBwdWs lay(planes, H, W, sizeof(T));
     T* xt = reinterpret_cast<T*>(ws + lay.xt);
@@ -794,7 +923,10 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
     a.w4 = static_cast<const T*>(w4_);
     a.w4_bytes = static_cast<int>(12 * (planes / o.cpg) * H * W * sizeof(T));
     a.gwd = static_cast<GT*>(gwd_);
-    a.gw_bytes = static_cast<int>(12 * planes * H * W * sizeof(GT));
+    a.gw_bytes = static_cast<int>(12 * (planes / cc) * H * W * sizeof(GT));
+    a.wpre = wpre;
+    a.wpre_bytes = static_cast<int>(12 * (planes / o.cpg) * H * W * 4);
+    a.cc = cc;
     a.cpg = static_cast<int>(o.cpg);
     a.k_chunk = static_cast<int>(o.k_chunk);
     a.eps = eps;
@@ -812,7 +944,7 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
     a.gu = static_cast<T*>(gu_);
 
     // row pair on the inputs as they are: taps and gradients of directions 0, 1
-    hipError_t e = launch_pass_k<T, GT, false>(a, stream);
+    hipError_t e = launch_pass_k<T, GT, false, Pre>(a, stream);
     if (e != hipSuccess) return e;
     const size_t tlds = static_cast<size_t>(H * W) * sizeof(T);
     if (tlds > 64 * 1024 &&
@@ -830,7 +962,95 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
     a.NL = W;
     a.L = H;
     a.dir0 = 2;
-    return launch_pass_k<T, GT, true>(a, stream);
+    return launch_pass_k<T, GT, true, Pre>(a, stream);
+}
+
+// Normalised weights of every tap group, fp32, in the taps' layout
+// ([4][groups][3][NL][L], line-major per direction): one thread per (direction,
+// group, position); taps whose source lies off the line get 0.
+template <typename T>
+__global__ void __launch_bounds__(256)
+shared_weights_kernel(const T* __restrict__ w4, float* __restrict__ wn, int64_t tplanes, int H, int W,
+                      float eps) {
+    const int64_t HW = static_cast<int64_t>(H) * W;
+    const int64_t per_dir = tplanes * HW;
+    const int64_t total = 4 * per_dir;
+    for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < total; idx += static_cast<int64_t>(gridDim.x) * 256) {
+        const int dir = static_cast<int>(idx / per_dir);
+        const int64_t rem = idx - dir * per_dir;
+        const int64_t tp = rem / HW;
+        const int64_t t = rem - tp * HW;
+        const int L = dir < 2 ? W : H;
+        const int p = static_cast<int>(t % L);
+        const size_t base = static_cast<size_t>((dir * tplanes + tp) * 3 * HW + t);
+        float w0, w1, w2;
+        normalize3(load_elem(w4, base), load_elem(w4, base + HW), load_elem(w4, base + 2 * HW), p > 0,
+                   p < L - 1, eps, w0, w1, w2);
+        wn[base] = w0;
+        wn[base + HW] = w1;
+        wn[base + 2 * HW] = w2;
+    }
+}
+
+// Tap gradients of every tap group from the partial sums of the tap
+// products (part: [4][groups][nch][3][NL][L], nch partial planes a group,
+// added in order), through the normalisation's Jacobian: with s = sigmoid(z),
+// T = sum s, r = 1 / max(T, eps), wn = s r and e the summed products,
+//   T > eps: gs_m = r sum_{k != m} wn_k (e_m - e_k), else gs_m = r e_m;
+//   gz_m = gs_m s_m (1 - s_m); dropped taps have s = 0 and get 0.
+template <typename T>
+__global__ void __launch_bounds__(256)
+shared_tap_grad_kernel(const float* __restrict__ part, const T* __restrict__ w4, T* __restrict__ gw4,
+                       int64_t tplanes, int nch, int H, int W, float eps) {
+    const int64_t HW = static_cast<int64_t>(H) * W;
+    const int64_t per_dir = tplanes * HW;
+    const int64_t total = 4 * per_dir;
+    for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < total; idx += static_cast<int64_t>(gridDim.x) * 256) {
+        const int dir = static_cast<int>(idx / per_dir);
+        const int64_t rem = idx - dir * per_dir;
+        const int64_t tp = rem / HW;
+        const int64_t t = rem - tp * HW;
+        const int L = dir < 2 ? W : H;
+        const int p = static_cast<int>(t % L);
+        const size_t base = static_cast<size_t>((dir * tplanes + tp) * 3 * HW + t);
+        const float* pp = part + static_cast<size_t>((dir * tplanes + tp) * nch) * 3 * HW + t;
+        float e0 = 0.0f, e1 = 0.0f, e2 = 0.0f;
+        for (int j = 0; j < nch; ++j) {
+            e0 += pp[0];
+            e1 += pp[HW];
+            e2 += pp[2 * HW];
+            pp += 3 * HW;
+        }
+        const float s0 = p > 0 ? sigmoid_hw(load_elem(w4, base)) : 0.0f;
+        const float s1 = sigmoid_hw(load_elem(w4, base + HW));
+        const float s2 = p < L - 1 ? sigmoid_hw(load_elem(w4, base + 2 * HW)) : 0.0f;
+        const float tt = (s0 + s1) + s2;
+        const float r = __builtin_amdgcn_rcpf(fmaxf(tt, eps));
+        const float wn0 = s0 * r, wn1 = s1 * r, wn2 = s2 * r;
+        float n0 = e0, n1 = e1, n2 = e2;
+        if (tt > eps) {
+            const float d01 = e0 - e1, d02 = e0 - e2, d12 = e1 - e2;
+            n0 = fmaf(wn1, d01, wn2 * d02);
+            n1 = fmaf(wn2, d12, -(wn0 * d01));
+            n2 = -fmaf(wn0, d02, wn1 * d12);
+        }
+        store_elem(gw4, base, n0 * (r * fmaf(-s0, s0, s0)));
+        store_elem(gw4, base + HW, n1 * (r * fmaf(-s1, s1, s1)));
+        store_elem(gw4, base + 2 * HW, n2 * (r * fmaf(-s2, s2, s2)));
+    }
+}
+
+// Planes a workgroup for channels that share taps: 4, 2 or 1, a divisor of
+// the channels a group whose layouts (two staging sets) fit in LDS together,
+// for the row and the column launch.
+int shared_planes_per_group(int64_t cpg, int64_t H, int64_t W, bool narrow) {
+    for (int cc = 4; cc > 1; cc /= 2) {
+        if (cpg % cc != 0) continue;
+        const int64_t rows = PairBwdLayout(static_cast<int>(H), static_cast<int>(W), narrow, 4, 2).bytes;
+        const int64_t cols = PairBwdLayout(static_cast<int>(W), static_cast<int>(H), narrow, 4, 2).bytes;
+        if (cc * rows <= kLdsBytes && cc * cols <= kLdsBytes) return cc;
+    }
+    return 1;
 }
 
 }  // namespace
@@ -873,19 +1093,57 @@ bool prop2d_backward_pair_eligible(int dtype, int64_t planes, int64_t H, int64_t
     return (reinterpret_cast<uintptr_t>(ws) & 15u) == 0;
 }
 
+int64_t prop2d_backward_pair_shared_weights_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg) {
+    return (12 * (planes / cpg) * H * W * 4 + 255) & ~static_cast<int64_t>(255);
+}
+
+hipError_t launch_prop2d_backward_pair_shared(const void* x, const void* lam, const void* u,
+                                              const void* w4, const void* gy, float eps, void* gx,
+                                              void* glam, void* gu, void* gw4, float* part, float* wpre,
+                                              void* ws, int dtype, int64_t planes, int64_t H,
+                                              int64_t W, const PropOpts& o, hipStream_t stream) {
+    const int64_t tplanes = planes / o.cpg;
+    const int64_t n = 4 * tplanes * H * W;
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 256 * 64));
+    const int cc = shared_planes_per_group(o.cpg, H, W, dtype == 1);
+    hipError_t e;
+    if (dtype == 0) {
+        shared_weights_kernel<float><<<dim3(blocks), dim3(256), 0, stream>>>(
+            static_cast<const float*>(w4), wpre, tplanes, static_cast<int>(H), static_cast<int>(W), eps);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = backward_pair_t<float, float, true>(x, lam, u, w4, gy, eps, gx, glam, gu, part, ws, planes, H, W, o,
+                                                stream, wpre, cc);
+        if (e != hipSuccess) return e;
+        shared_tap_grad_kernel<float><<<dim3(blocks), dim3(256), 0, stream>>>(
+            part, static_cast<const float*>(w4), static_cast<float*>(gw4), tplanes,
+            static_cast<int>(o.cpg / cc), static_cast<int>(H), static_cast<int>(W), eps);
+    } else {
+        shared_weights_kernel<uint16_t><<<dim3(blocks), dim3(256), 0, stream>>>(
+            static_cast<const uint16_t*>(w4), wpre, tplanes, static_cast<int>(H), static_cast<int>(W), eps);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = backward_pair_t<uint16_t, float, true>(x, lam, u, w4, gy, eps, gx, glam, gu, part, ws, planes, H, W,
+                                                   o, stream, wpre, cc);
+        if (e != hipSuccess) return e;
+        shared_tap_grad_kernel<uint16_t><<<dim3(blocks), dim3(256), 0, stream>>>(
+            part, static_cast<const uint16_t*>(w4), static_cast<uint16_t*>(gw4), tplanes,
+            static_cast<int>(o.cpg / cc), static_cast<int>(H), static_cast<int>(W), eps);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_prop2d_backward_pair(const void* x, const void* lam, const void* u,
                                        const void* w4, const void* gy, float eps, void* gx,
                                        void* glam, void* gu, void* gwd, bool gw_fp32, void* ws,
                                        int dtype, int64_t planes, int64_t H, int64_t W,
                                        const PropOpts& o, hipStream_t stream) {
     if (dtype == 0)
-        return backward_pair_t<float, float>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes, H, W,
-                                             o, stream);
+        return backward_pair_t<float, float, false>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes, H,
+                                                    W, o, stream);
     if (gw_fp32)
-        return backward_pair_t<uint16_t, float>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes, H,
-                                                W, o, stream);
-    return backward_pair_t<uint16_t, uint16_t>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes, H,
-                                               W, o, stream);
+        return backward_pair_t<uint16_t, float, false>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes,
+                                                       H, W, o, stream);
+    return backward_pair_t<uint16_t, uint16_t, false>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes,
+                                                      H, W, o, stream);
 }
 
 }  // namespace gspn

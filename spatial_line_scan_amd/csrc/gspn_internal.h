@@ -113,6 +113,17 @@ hipError_t launch_prop2d_backward_pair(const void* x, const void* lam, const voi
                                        void* glam, void* gu, void* gwd, bool gw_fp32, void* ws,
                                        int dtype, int64_t planes, int64_t H, int64_t W,
                                        const PropOpts& opts, hipStream_t stream);
+// Channels sharing taps (cpg > 1) on the pair kernel: the taps are
+// normalised once per group into wpre (prop2d_backward_pair_shared_weights_bytes
+// bytes), the pair kernel sums its planes' tap products on chip into part
+// (up to 12 planes H W fp32) and a last kernel applies the normalisation's
+// Jacobian per group into gw4 (storage type).  ws as for the pair kernel.
+int64_t prop2d_backward_pair_shared_weights_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg);
+hipError_t launch_prop2d_backward_pair_shared(const void* x, const void* lam, const void* u,
+                                              const void* w4, const void* gy, float eps, void* gx,
+                                              void* glam, void* gu, void* gw4, float* part, float* wpre,
+                                              void* ws, int dtype, int64_t planes, int64_t H,
+                                              int64_t W, const PropOpts& opts, hipStream_t stream);
 // Longest line the backward's LDS lines allow.
 int64_t prop2d_backward_max_line();
 

@@ -230,12 +230,15 @@ def exb(L, groups=3, k=1, ws=None, ws_bytes=0, dt=0, B=2, C=3, H=5, W=7, ptrs=No
 
 
 def test_ex_backward_workspace_query(L):
-    # shared taps add 48 bytes of fp32 tap gradients per pixel-channel
+    # shared taps add 48 bytes of fp32 tap gradients (or partial sums of tap
+    # products) per pixel-channel and 48 bytes of normalised weights per
+    # pixel-group, each region rounded up to 256 bytes
+    r256 = lambda v: (v + 255) // 256 * 256
     assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 3, 5, 7) == 0
-    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 1, 5, 7) == (12 * 2 * 3 * 35 * 4 + 255) // 256 * 256
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 1, 5, 7) == r256(12 * 2 * 3 * 35 * 4) + r256(12 * 2 * 35 * 4)
     n = 32 * 64 * 74 * 74
     assert L.gspn_prop2d_4dir_ex_backward_workspace(32, 64, 64, 74, 74) == 6 * 4 * n
-    assert L.gspn_prop2d_4dir_ex_backward_workspace(32, 64, 1, 74, 74) == 6 * 4 * n + 48 * n
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(32, 64, 1, 74, 74) == 6 * 4 * n + 48 * n + r256(48 * n // 64)
     assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 2, 5, 7) == -1       # 2 does not divide 3
     assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 0, 5, 7) == -1
 
