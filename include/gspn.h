@@ -212,14 +212,18 @@ int64_t gspn_prop2d_4dir_ex_workspace(int dtype, int64_t B, int64_t C, int64_t g
  *   x, lam, u, gy, gx, glam, gu : [B][C][H][W];  w_raw4, gw4 : [4][B][C][3][..][..].
  *   workspace : scratch of at least
  *               gspn_prop2d_4dir_backward_workspace(B, C, H, W) bytes, 4-byte
- *               aligned (16-byte alignment lets even-sided planes up to 96
- *               take the fast kernels); contents on return are unspecified.
- *               Planes with even H and W up to 96 need it for transposed
- *               copies of x, lam, u, gy and two fp32 partial sums per
- *               pixel-channel (sized for fp32 storage).  Otherwise it holds
- *               three fp32 planes per (b, c) once they no longer fit in LDS
- *               (above about 115 x 115); below that the size is 0 and NULL is
- *               allowed.
+ *               aligned (16-byte alignment lets the fast kernels run);
+ *               contents on return are unspecified.  Sizes are for fp32
+ *               storage.  Planes with even H and W up to 160 need it for
+ *               transposed copies of x, lam, u, gy and two fp32 partial sums
+ *               per pixel-channel.  A plane with an odd side whose sides,
+ *               padded to even, are at most 160 also holds padded copies of the
+ *               inputs, outputs, taps and tap gradients there, and is run as
+ *               the padded plane (the padding is exact: the added row and
+ *               column start at 0 and no real position reads them).  Other
+ *               planes need three fp32 planes per (b, c) once those no longer
+ *               fit in LDS (above about 115 x 115); below that the size is 0
+ *               and NULL is allowed.
  *   Outputs must not overlap inputs, each other or the workspace.  Lines up
  *   to 5851 (H and W).  bf16 gradients are rounded to nearest even.  The
  *   result is bitwise reproducible from run to run.
@@ -249,8 +253,11 @@ int64_t gspn_prop2d_4dir_backward_workspace(int64_t B, int64_t C, int64_t H, int
  *   workspace : at least gspn_prop2d_4dir_ex_backward_workspace(B, C, groups,
  *               H, W) bytes, 4-byte aligned (16 for the fast kernels).  On top
  *               of what gspn_prop2d_4dir_backward needs, channels that share
- *               taps (groups < C) keep their fp32 tap gradients there before
- *               they are summed: 48 bytes per pixel-channel.
+ *               taps (groups < C) keep fp32 tap gradients or partial sums of
+ *               tap products there (48 bytes per pixel-channel) and their
+ *               group's normalised taps (48 bytes per pixel-group).  A chunked
+ *               scan whose k_chunk divides an odd side runs that plane
+ *               unpadded.
  * Other arguments, layouts, errors and determinism as
  * gspn_prop2d_4dir_backward, which is this call with groups = C, k_chunk = 1.
  */

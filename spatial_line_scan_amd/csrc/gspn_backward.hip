@@ -304,13 +304,205 @@ group_sum4_kernel(const float* __restrict__ gwc, T* __restrict__ gw4, int64_t n_
     }
 }
 
-}  // namespace
+// ------------------------------------------------------------ odd sides
+// A plane with an odd side is run as the plane one row and/or column larger,
+// which the pair kernel takes.  The copy adds a zero row below and a zero
+// column to the right of x, lambda, u and gy; in every direction's taps the
+// added line's taps are 0 and so are those of the added position of each
+// line, and the tap that reaches from a line's last position to the added
+// one gets logit -inf, whose sigmoid is exactly 0.  Then every real
+// position's weights are the ones of the plane as it is, the added positions
+// never reach a real one (weight 0 times a finite value), a scan that starts
+// on the added line gives the first real line h = lambda x exactly as the
+// plane's own first line, and with gy = 0 there the adjoint carries nothing
+// out of it; the tap gradient of the -inf tap is 0 (s (1 - s) = 0), as for a
+// dropped tap.  So the real part of the padded gradients is the gradient of
+// the plane.  A chunked scan keeps its segments as long as ceil(NL / k) does
+// not change with the added line (not when k divides an odd NL).
 
-int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg) {
+// Division of n < 2^31 by a fixed d (1 <= d < 2^31): q = (umulhi(n, m) + n) >> s
+// with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1 (the
+// round-up method of Granlund and Montgomery, "Division by invariant
+// integers using multiplication").
+struct FastDiv {
+    uint32_t d, m, s;
+    FastDiv() = default;
+    explicit FastDiv(uint32_t div) : d(div), s(0) {
+        while ((1ull << s) < div) ++s;
+        m = static_cast<uint32_t>(((1ull << 32) * ((1ull << s) - div)) / div + 1);
+    }
+    __device__ __forceinline__ uint32_t div(uint32_t n) const { return (__umulhi(n, m) + n) >> s; }
+};
+
+// Up to four line-plane tensors ([n][NL][L]) and their padded copies
+// ([n][NLp][Lp]); blockIdx.y picks the tensor.  One thread per padded
+// element.  taps: plane j is tap j % 3 of its position, and tap 2 of each
+// line's last real position gets neg_inf when the line was lengthened.
+template <typename T>
+struct PadArgs {
+    const T* src[4];
+    T* dst[4];
+    int n, NL, L, NLp, Lp;
+    FastDiv per_plane, per_line;     // NLp * Lp, Lp
+    bool taps;
+    T neg_inf;
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+pad_lines_kernel(PadArgs<T> a) {
+    const uint32_t total = static_cast<uint32_t>(a.n) * a.per_plane.d;
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t pl = a.per_plane.div(i);
+    const uint32_t e = i - pl * a.per_plane.d;
+    const uint32_t line = a.per_line.div(e);
+    const uint32_t p = e - line * a.per_line.d;
+    const T* src = a.src[blockIdx.y];
+    T v = T(0);
+    if (line < static_cast<uint32_t>(a.NL) && p < static_cast<uint32_t>(a.L))
+        v = (a.taps && pl % 3 == 2 && p == static_cast<uint32_t>(a.L - 1) && a.Lp > a.L)
+                ? a.neg_inf
+                : src[(static_cast<int64_t>(pl) * a.NL + line) * a.L + p];
+    a.dst[blockIdx.y][i] = v;
+}
+
+// The real lines of padded copies: dst[y] ([n][NL][L]) from src[y]
+// ([n][NLp][Lp]); one thread per real element.
+template <typename T>
+struct CropArgs {
+    const T* src[4];
+    T* dst[4];
+    int n, NL, L, NLp, Lp;
+    FastDiv per_plane, per_line;     // NL * L, L
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+crop_lines_kernel(CropArgs<T> a) {
+    const uint32_t total = static_cast<uint32_t>(a.n) * a.per_plane.d;
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t pl = a.per_plane.div(i);
+    const uint32_t e = i - pl * a.per_plane.d;
+    const uint32_t line = a.per_line.div(e);
+    const uint32_t p = e - line * a.per_line.d;
+    a.dst[blockIdx.y][i] = a.src[blockIdx.y][(static_cast<int64_t>(pl) * a.NLp + line) * a.Lp + p];
+}
+
+// The padded problem: inputs and taps copied in, the pair path run on it,
+// the real part of the gradients copied out.  buf: padded x, lambda, u, gy,
+// gx, glambda, gu, taps, tap gradients.
+template <typename T>
+hipError_t run_padded(const void* x, const void* lam, const void* u, const void* w4, const void* gy,
+                      float eps, void* gx, void* glam, void* gu, void* gw4, void* ws, void* const* buf,
+                      int dtype, int64_t planes, int64_t H, int64_t W, int64_t Hp, int64_t Wp,
+                      const PropOpts& o, hipStream_t stream) {
+    const int64_t tp = planes / o.cpg;
+    const int64_t HW = H * W, HWp = Hp * Wp;
+    auto blocks = [](int64_t n, int ny) { return dim3(static_cast<unsigned>((n + 255) / 256), ny); };
+    T neg_inf;
+    if constexpr (sizeof(T) == 4) neg_inf = -__builtin_inff();
+    else neg_inf = static_cast<T>(0xff80u);   // bf16 -inf
+    hipError_t e;
+    {   // x, lambda, u, gy: lines are rows
+        PadArgs<T> a{};
+        const void* in[4] = {x, lam, u, gy};
+        for (int i = 0; i < 4; ++i) {
+            a.src[i] = static_cast<const T*>(in[i]);
+            a.dst[i] = static_cast<T*>(buf[i]);
+        }
+        a.n = static_cast<int>(planes);
+        a.NL = static_cast<int>(H); a.L = static_cast<int>(W); a.NLp = static_cast<int>(Hp); a.Lp = static_cast<int>(Wp);
+        a.per_plane = FastDiv(static_cast<uint32_t>(HWp));
+        a.per_line = FastDiv(static_cast<uint32_t>(Wp));
+        a.taps = false;
+        a.neg_inf = neg_inf;
+        pad_lines_kernel<T><<<blocks(planes * HWp, 4), dim3(256), 0, stream>>>(a);
+    }
+    // taps: the row directions' 6 tp planes (lines are rows), then the column
+    // directions' (lines are columns)
+    for (int part = 0; part < 2; ++part) {
+        PadArgs<T> a{};
+        a.src[0] = static_cast<const T*>(w4) + part * 6 * tp * HW;
+        a.dst[0] = static_cast<T*>(buf[7]) + part * 6 * tp * HWp;
+        a.n = static_cast<int>(6 * tp);
+        a.NL = static_cast<int>(part ? W : H); a.L = static_cast<int>(part ? H : W);
+        a.NLp = static_cast<int>(part ? Wp : Hp); a.Lp = static_cast<int>(part ? Hp : Wp);
+        a.per_plane = FastDiv(static_cast<uint32_t>(HWp));
+        a.per_line = FastDiv(static_cast<uint32_t>(a.Lp));
+        a.taps = true;
+        a.neg_inf = neg_inf;
+        pad_lines_kernel<T><<<blocks(6 * tp * HWp, 1), dim3(256), 0, stream>>>(a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_prop2d_backward(buf[0], buf[1], buf[2], buf[7], buf[3], eps, buf[4], buf[5], buf[6], buf[8], ws,
+                               dtype, planes, Hp, Wp, o, stream);
+    if (e != hipSuccess) return e;
+    {
+        CropArgs<T> a{};
+        void* out[3] = {gx, glam, gu};
+        for (int i = 0; i < 3; ++i) {
+            a.src[i] = static_cast<const T*>(buf[4 + i]);
+            a.dst[i] = static_cast<T*>(out[i]);
+        }
+        a.n = static_cast<int>(planes);
+        a.NL = static_cast<int>(H); a.L = static_cast<int>(W); a.NLp = static_cast<int>(Hp); a.Lp = static_cast<int>(Wp);
+        a.per_plane = FastDiv(static_cast<uint32_t>(HW));
+        a.per_line = FastDiv(static_cast<uint32_t>(W));
+        crop_lines_kernel<T><<<blocks(planes * HW, 3), dim3(256), 0, stream>>>(a);
+    }
+    for (int part = 0; part < 2; ++part) {
+        CropArgs<T> a{};
+        a.src[0] = static_cast<const T*>(buf[8]) + part * 6 * tp * HWp;
+        a.dst[0] = static_cast<T*>(gw4) + part * 6 * tp * HW;
+        a.n = static_cast<int>(6 * tp);
+        a.NL = static_cast<int>(part ? W : H); a.L = static_cast<int>(part ? H : W);
+        a.NLp = static_cast<int>(part ? Wp : Hp); a.Lp = static_cast<int>(part ? Hp : Wp);
+        a.per_plane = FastDiv(static_cast<uint32_t>(HW));
+        a.per_line = FastDiv(static_cast<uint32_t>(a.L));
+        crop_lines_kernel<T><<<blocks(6 * tp * HW, 1), dim3(256), 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+int64_t a256(int64_t v) { return (v + 255) & ~static_cast<int64_t>(255); }
+
+// Bytes of the padded copies (storage up to 4 bytes): x, lambda, u, gy, gx,
+// glambda, gu and the taps and their gradients.
+int64_t padded_copy_bytes(int64_t planes, int64_t Hp, int64_t Wp, int64_t cpg) {
+    const int64_t n = planes * Hp * Wp * 4;
+    return 7 * a256(n) + 2 * a256(12 * (planes / cpg) * Hp * Wp * 4);
+}
+
+bool odd_shape(int64_t H, int64_t W) { return (H & 1) || (W & 1); }
+
+// Whether the padded plane takes the pair kernel (workspace sizing).
+bool padded_pair_shape(int64_t planes, int64_t H, int64_t W) {
+    return odd_shape(H, W) && prop2d_backward_pair_shape(planes, H + (H & 1), W + (W & 1));
+}
+
+int64_t direct_workspace_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg) {
     const int64_t general = plane_kernel_workspace_bytes(planes, H, W);
     const int64_t pair = prop2d_backward_pair_shape(planes, H, W)
                              ? prop2d_backward_pair_workspace_bytes(planes, H, W) : 0;
     return group_grad_bytes(planes, H, W, cpg) + (general > pair ? general : pair);
+}
+
+// ceil(NL / k) with the added line.
+bool segments_keep(int64_t NL, int64_t k) {
+    if (!(NL & 1) || k <= 1) return true;
+    return (NL + 1 + k - 1) / k == (NL + k - 1) / k;
+}
+
+}  // namespace
+
+int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg) {
+    const int64_t direct = direct_workspace_bytes(planes, H, W, cpg);
+    if (!padded_pair_shape(planes, H, W)) return direct;
+    const int64_t Hp = H + (H & 1), Wp = W + (W & 1);
+    const int64_t padded = direct_workspace_bytes(planes, Hp, Wp, cpg) + padded_copy_bytes(planes, Hp, Wp, cpg);
+    return padded > direct ? padded : direct;
 }
 
 int64_t prop2d_backward_max_line() { return kLdsBytes / 4 / 7; }
@@ -319,6 +511,23 @@ hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u,
                                   const void* gy, float eps, void* gx, void* glam, void* gu,
                                   void* gw4, void* ws, int dtype, int64_t planes, int64_t H,
                                   int64_t W, const PropOpts& o, hipStream_t stream) {
+    if (ws && padded_pair_shape(planes, H, W) && segments_keep(H, o.k_chunk) && segments_keep(W, o.k_chunk)) {
+        const int64_t Hp = H + (H & 1), Wp = W + (W & 1);
+        const int64_t n = planes * Hp * Wp, nt = 12 * (planes / o.cpg) * Hp * Wp;
+        char* p = static_cast<char*>(ws) + direct_workspace_bytes(planes, Hp, Wp, o.cpg);
+        void* buf[9];
+        for (int i = 0; i < 7; ++i) {
+            buf[i] = p;
+            p += a256(n * 4);
+        }
+        buf[7] = p;                      // taps
+        p += a256(nt * 4);
+        buf[8] = p;                      // tap gradients
+        return dtype == 0 ? run_padded<float>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, buf, dtype, planes,
+                                              H, W, Hp, Wp, o, stream)
+                          : run_padded<uint16_t>(x, lam, u, w4, gy, eps, gx, glam, gu, gw4, ws, buf, dtype,
+                                                 planes, H, W, Hp, Wp, o, stream);
+    }
     // channels that share taps write their own fp32 tap gradients first, at
     // the start of the workspace; the kernels' own scratch follows
     const bool grouped = o.cpg > 1;

@@ -155,7 +155,32 @@ def test_aliasing(L):
     assert norm(L, dst=P(3)) == ALIAS
 
 
-def bwd(L, ptrs=None, eps=1e-6, ws=None, ws_bytes=0, dt=0, B=2, C=3, H=5, W=7):
+# Backward workspace layout (fp32-sized regions, each rounded up to 256 bytes):
+# the pair kernel's transposed x, lambda, u, gy and two fp32 sums; with shared
+# taps first the per-channel fp32 tap gradients or partial sums and the
+# group's normalised taps; planes with an odd side add padded copies of the
+# seven planes per pixel-channel and of the taps and tap gradients.
+def r256(v):
+    return (v + 255) // 256 * 256
+
+
+def pair_ws(planes, H, W):
+    return 6 * r256(planes * H * W * 4)
+
+
+def group_ws(planes, H, W, cpg):
+    return r256(12 * planes * H * W * 4) + r256(12 * (planes // cpg) * H * W * 4) if cpg > 1 else 0
+
+
+def padded_ws(planes, H, W, cpg=1):
+    Hp, Wp = H + H % 2, W + W % 2
+    return (group_ws(planes, Hp, Wp, cpg) + pair_ws(planes, Hp, Wp) + 7 * r256(planes * Hp * Wp * 4) +
+            2 * r256(12 * (planes // cpg) * Hp * Wp * 4))
+
+
+# the argument checks below run on a 3 x 170 plane: too long a line for the
+# pair kernel, padded or not, and small enough for LDS, so no workspace
+def bwd(L, ptrs=None, eps=1e-6, ws=None, ws_bytes=0, dt=0, B=2, C=3, H=3, W=170):
     p = list(ptrs) if ptrs else [P(i) for i in range(9)]
     return L.gspn_prop2d_4dir_backward(p[0], p[1], p[2], p[3], p[4], eps, p[5], p[6], p[7], p[8],
                                        ws, ws_bytes, dt, B, C, H, W, None)
@@ -170,11 +195,16 @@ def test_backward_workspace_query(L):
     assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 2, 96) == 6 * 768    # 256-byte regions
     assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 120, 120) == 6 * 4 * 2 * 3 * 120 * 120
     assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 148, 148) == 6 * ((148 * 148 * 4 + 255) // 256 * 256)
+    # odd sides: the padded plane's workspace plus the padded copies
+    assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 5, 7) == padded_ws(6, 5, 7)
+    assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 115, 115) == padded_ws(1, 115, 115)
+    assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 121, 121) == padded_ws(6, 121, 121)
+    assert L.gspn_prop2d_4dir_backward_workspace(4, 64, 147, 147) == padded_ws(256, 147, 147)
+    assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 159, 2) == padded_ws(1, 159, 2)
     # otherwise 7 LDS lines plus three fp32 planes fit in 160 KiB up to about 115 x 115
-    assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 115, 115) == 0
-    assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 95, 96) == 0
+    assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 3, 170) == 0
+    assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 161, 2) == 0
     assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 170, 170) == 2 * 3 * 3 * 170 * 170 * 4
-    assert L.gspn_prop2d_4dir_backward_workspace(2, 3, 121, 121) == 2 * 3 * 3 * 121 * 121 * 4
     assert L.gspn_prop2d_4dir_backward_workspace(1, 1, 5852, 2) == -1      # line too long
     assert L.gspn_prop2d_4dir_backward_workspace(0, 1, 4, 4) == -1
     assert L.gspn_prop2d_4dir_backward_workspace(1, 1 << 18, 64, 64) == -1
@@ -194,6 +224,7 @@ def test_backward_rejects_bad_arguments(L):
     ptrs = [P(j) for j in range(9)]
     ptrs[0] = ctypes.c_void_p(A + 2)
     assert bwd(L, ptrs) == ALIGN
+    assert bwd(L, H=5, W=7) == NULL                          # padded odd planes need a workspace
     ptrs = [P(j) for j in range(9)]
     ptrs[8] = ctypes.c_void_p(A + 8 * STEP + 1)
     assert bwd(L, ptrs, dt=1) == ALIGN
@@ -223,7 +254,7 @@ def test_backward_workspace_checks(L):
     assert bwd(L, ws_bytes=-1) == SHAPE
 
 
-def exb(L, groups=3, k=1, ws=None, ws_bytes=0, dt=0, B=2, C=3, H=5, W=7, ptrs=None):
+def exb(L, groups=3, k=1, ws=None, ws_bytes=0, dt=0, B=2, C=3, H=3, W=170, ptrs=None):
     p = list(ptrs) if ptrs else [P(i) for i in range(9)]
     return L.gspn_prop2d_4dir_ex_backward(p[0], p[1], p[2], p[3], groups, k, p[4], 1e-6, p[5], p[6],
                                           p[7], p[8], ws, ws_bytes, dt, B, C, H, W, None)
@@ -233,9 +264,10 @@ def test_ex_backward_workspace_query(L):
     # shared taps add 48 bytes of fp32 tap gradients (or partial sums of tap
     # products) per pixel-channel and 48 bytes of normalised weights per
     # pixel-group, each region rounded up to 256 bytes
-    r256 = lambda v: (v + 255) // 256 * 256
-    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 3, 5, 7) == 0
-    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 1, 5, 7) == r256(12 * 2 * 3 * 35 * 4) + r256(12 * 2 * 35 * 4)
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 3, 3, 170) == 0
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 1, 3, 170) == group_ws(6, 3, 170, 3)
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 3, 5, 7) == padded_ws(6, 5, 7)
+    assert L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 1, 5, 7) == padded_ws(6, 5, 7, 3)
     n = 32 * 64 * 74 * 74
     assert L.gspn_prop2d_4dir_ex_backward_workspace(32, 64, 64, 74, 74) == 6 * 4 * n
     assert L.gspn_prop2d_4dir_ex_backward_workspace(32, 64, 1, 74, 74) == 6 * 4 * n + 48 * n + r256(48 * n // 64)
@@ -249,18 +281,18 @@ def test_ex_backward_rejects_bad_arguments(L):
     assert exb(L, k=0) == VALUE
     assert exb(L, dt=2) == DTYPE
     assert exb(L, groups=1) == NULL                          # shared taps need a workspace
-    need = L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 1, 5, 7)
+    need = L.gspn_prop2d_4dir_ex_backward_workspace(2, 3, 1, 3, 170)
     assert exb(L, groups=1, ws=P(10), ws_bytes=need - 4) == SHAPE
     assert exb(L, groups=1, ws=P(0), ws_bytes=need) == ALIAS      # over x
     ptrs = [P(j) for j in range(9)]
     ptrs[8] = P(3)
     assert exb(L, ptrs=ptrs) == ALIAS                        # gw4 over w_raw4
     ptrs = [P(j) for j in range(9)]
-    ptrs[8] = ctypes.c_void_p(A + 3 * STEP + 12 * 2 * 1 * 35 * 4 - 4)
+    ptrs[8] = ctypes.c_void_p(A + 3 * STEP + 12 * 2 * 1 * 510 * 4 - 4)
     assert exb(L, groups=1, ptrs=ptrs, ws=P(10), ws_bytes=need) == ALIAS   # last word of 1-group taps
 
 
-def exb_noalloc(L, groups=3, k=1, dt=0, B=2, C=3, H=5, W=7, ptrs=None):
+def exb_noalloc(L, groups=3, k=1, dt=0, B=2, C=3, H=3, W=170, ptrs=None):
     p = list(ptrs) if ptrs else [P(i) for i in range(9)]
     return L.gspn_prop2d_4dir_ex_backward_noalloc(p[0], p[1], p[2], p[3], groups, k, p[4], 1e-6,
                                                   p[5], p[6], p[7], p[8], dt, B, C, H, W, None)
