@@ -646,9 +646,9 @@ def main():
         l2, b3, wd = WORKLOADS["latent2k"], WORKLOADS["base378"], WORKLOADS["wide256"]
         out["workloads"] = {
             "latent2k": shape_leg(args, dev, l2.B, l2.C, l2.H, l2.W, l2.dtype, backward=True),
-            "latent2k_odd_147": shape_leg(args, dev, l2.B, l2.C, 147, 147, l2.dtype),
+            "latent2k_odd_147": shape_leg(args, dev, l2.B, l2.C, 147, 147, l2.dtype, backward=True),
             "base378_warm": shape_leg(args, dev, b3.B, b3.C, b3.H, b3.W, b3.dtype, rotate=False),
-            "base378_rotated": shape_leg(args, dev, b3.B, b3.C, b3.H, b3.W, b3.dtype),
+            "base378_rotated": shape_leg(args, dev, b3.B, b3.C, b3.H, b3.W, b3.dtype, backward=True),
             "wide256": shape_leg(args, dev, wd.B, wd.C, wd.H, wd.W, wd.dtype, backward=True),
         }
     if not args.no_cpu_baseline:
