@@ -502,6 +502,9 @@ def main():
                          "(for profiling its kernels on their own)")
     ap.add_argument("--scan-dir-only", action="store_true",
                     help="run only the one-direction legs and print them")
+    ap.add_argument("--shape-only", default=None, metavar="B,C,H,W,DTYPE",
+                    help="run only the forward and backward legs on one B x C x H x W grid "
+                         "(dtype fp32 or bf16) and print them (for profiling)")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only warmup + K backward launches and print their timing "
                          "(for profiling the backward kernel on its own)")
@@ -537,6 +540,11 @@ def main():
         return
     if args.sublayer_only is not None:
         print(json.dumps({"sublayer": sublayer_leg(args, dev, args.sublayer_only)}), flush=True)
+        return
+    if args.shape_only:
+        f = args.shape_only.split(",")
+        B, C, H, W = (int(v) for v in f[:4])
+        print(json.dumps({"shape": shape_leg(args, dev, B, C, H, W, f[4], backward=True)}), flush=True)
         return
     if args.scan_dir_only:
         print(json.dumps({"scan_dir": scan_dir_leg(wl, args, dev)}), flush=True)
