@@ -335,18 +335,24 @@ struct FastDiv {
 };
 
 // Up to four line-plane tensors ([n][NL][L]) and their padded copies
-// ([n][NLp][Lp]); blockIdx.y picks the tensor.  One thread per padded
-// element.  taps: plane j is tap j % 3 of its position, and tap 2 of each
-// line's last real position gets neg_inf when the line was lengthened.
+// ([n][NLp][Lp], Lp even); blockIdx.y picks the tensor.  One thread per
+// element pair of the padded copies (a 4- or 8-byte store: padded lines
+// start on even elements).  taps: plane j is tap j % 3 of its position, and
+// tap 2 of each line's last real position gets neg_inf when the line was
+// lengthened.
 template <typename T>
 struct PadArgs {
     const T* src[4];
     T* dst[4];
     int n, NL, L, NLp, Lp;
-    FastDiv per_plane, per_line;     // NLp * Lp, Lp
+    FastDiv per_plane, per_line;     // NLp * Lp / 2, Lp / 2 (pairs)
     bool taps;
     T neg_inf;
 };
+
+template <typename T> struct Pair2;
+template <> struct Pair2<float> { typedef float __attribute__((ext_vector_type(2))) type; };
+template <> struct Pair2<uint16_t> { typedef uint16_t __attribute__((ext_vector_type(2))) type; };
 
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -357,24 +363,30 @@ pad_lines_kernel(PadArgs<T> a) {
     const uint32_t pl = a.per_plane.div(i);
     const uint32_t e = i - pl * a.per_plane.d;
     const uint32_t line = a.per_line.div(e);
-    const uint32_t p = e - line * a.per_line.d;
-    const T* src = a.src[blockIdx.y];
-    T v = T(0);
-    if (line < static_cast<uint32_t>(a.NL) && p < static_cast<uint32_t>(a.L))
-        v = (a.taps && pl % 3 == 2 && p == static_cast<uint32_t>(a.L - 1) && a.Lp > a.L)
-                ? a.neg_inf
-                : src[(static_cast<int64_t>(pl) * a.NL + line) * a.L + p];
-    a.dst[blockIdx.y][i] = v;
+    const uint32_t p0 = 2 * (e - line * a.per_line.d);
+    const T* src = a.src[blockIdx.y] + (static_cast<int64_t>(pl) * a.NL + line) * a.L;
+    const bool real_line = line < static_cast<uint32_t>(a.NL);
+    T v[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t p = p0 + j;
+        v[j] = T(0);
+        if (real_line && p < static_cast<uint32_t>(a.L))
+            v[j] = (a.taps && pl % 3 == 2 && p == static_cast<uint32_t>(a.L - 1) && a.Lp > a.L) ? a.neg_inf : src[p];
+    }
+    typedef typename Pair2<T>::type P2;
+    reinterpret_cast<P2*>(a.dst[blockIdx.y])[i] = P2{v[0], v[1]};
 }
 
 // The real lines of padded copies: dst[y] ([n][NL][L]) from src[y]
-// ([n][NLp][Lp]); one thread per real element.
+// ([n][NLp][Lp]); one thread per element pair of the padded copy (an
+// aligned 4- or 8-byte load), storing its real elements.
 template <typename T>
 struct CropArgs {
     const T* src[4];
     T* dst[4];
     int n, NL, L, NLp, Lp;
-    FastDiv per_plane, per_line;     // NL * L, L
+    FastDiv per_plane, per_line;     // NLp * Lp / 2, Lp / 2 (pairs)
 };
 
 template <typename T>
@@ -386,8 +398,13 @@ crop_lines_kernel(CropArgs<T> a) {
     const uint32_t pl = a.per_plane.div(i);
     const uint32_t e = i - pl * a.per_plane.d;
     const uint32_t line = a.per_line.div(e);
-    const uint32_t p = e - line * a.per_line.d;
-    a.dst[blockIdx.y][i] = a.src[blockIdx.y][(static_cast<int64_t>(pl) * a.NLp + line) * a.Lp + p];
+    if (line >= static_cast<uint32_t>(a.NL)) return;
+    const uint32_t p0 = 2 * (e - line * a.per_line.d);
+    typedef typename Pair2<T>::type P2;
+    const P2 v = reinterpret_cast<const P2*>(a.src[blockIdx.y])[i];
+    T* dst = a.dst[blockIdx.y] + (static_cast<int64_t>(pl) * a.NL + line) * a.L;
+    if (p0 < static_cast<uint32_t>(a.L)) dst[p0] = v.x;
+    if (p0 + 1 < static_cast<uint32_t>(a.L)) dst[p0 + 1] = v.y;
 }
 
 // The padded problem: inputs and taps copied in, the pair path run on it,
@@ -414,11 +431,11 @@ hipError_t run_padded(const void* x, const void* lam, const void* u, const void*
         }
         a.n = static_cast<int>(planes);
         a.NL = static_cast<int>(H); a.L = static_cast<int>(W); a.NLp = static_cast<int>(Hp); a.Lp = static_cast<int>(Wp);
-        a.per_plane = FastDiv(static_cast<uint32_t>(HWp));
-        a.per_line = FastDiv(static_cast<uint32_t>(Wp));
+        a.per_plane = FastDiv(static_cast<uint32_t>(HWp / 2));
+        a.per_line = FastDiv(static_cast<uint32_t>(Wp / 2));
         a.taps = false;
         a.neg_inf = neg_inf;
-        pad_lines_kernel<T><<<blocks(planes * HWp, 4), dim3(256), 0, stream>>>(a);
+        pad_lines_kernel<T><<<blocks(planes * HWp / 2, 4), dim3(256), 0, stream>>>(a);
     }
     // taps: the row directions' 6 tp planes (lines are rows), then the column
     // directions' (lines are columns)
@@ -429,11 +446,11 @@ hipError_t run_padded(const void* x, const void* lam, const void* u, const void*
         a.n = static_cast<int>(6 * tp);
         a.NL = static_cast<int>(part ? W : H); a.L = static_cast<int>(part ? H : W);
         a.NLp = static_cast<int>(part ? Wp : Hp); a.Lp = static_cast<int>(part ? Hp : Wp);
-        a.per_plane = FastDiv(static_cast<uint32_t>(HWp));
-        a.per_line = FastDiv(static_cast<uint32_t>(a.Lp));
+        a.per_plane = FastDiv(static_cast<uint32_t>(HWp / 2));
+        a.per_line = FastDiv(static_cast<uint32_t>(a.Lp / 2));
         a.taps = true;
         a.neg_inf = neg_inf;
-        pad_lines_kernel<T><<<blocks(6 * tp * HWp, 1), dim3(256), 0, stream>>>(a);
+        pad_lines_kernel<T><<<blocks(6 * tp * HWp / 2, 1), dim3(256), 0, stream>>>(a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = launch_prop2d_backward(buf[0], buf[1], buf[2], buf[7], buf[3], eps, buf[4], buf[5], buf[6], buf[8], ws,
@@ -448,9 +465,9 @@ hipError_t run_padded(const void* x, const void* lam, const void* u, const void*
         }
         a.n = static_cast<int>(planes);
         a.NL = static_cast<int>(H); a.L = static_cast<int>(W); a.NLp = static_cast<int>(Hp); a.Lp = static_cast<int>(Wp);
-        a.per_plane = FastDiv(static_cast<uint32_t>(HW));
-        a.per_line = FastDiv(static_cast<uint32_t>(W));
-        crop_lines_kernel<T><<<blocks(planes * HW, 3), dim3(256), 0, stream>>>(a);
+        a.per_plane = FastDiv(static_cast<uint32_t>(HWp / 2));
+        a.per_line = FastDiv(static_cast<uint32_t>(Wp / 2));
+        crop_lines_kernel<T><<<blocks(planes * HWp / 2, 3), dim3(256), 0, stream>>>(a);
     }
     for (int part = 0; part < 2; ++part) {
         CropArgs<T> a{};
@@ -459,9 +476,9 @@ hipError_t run_padded(const void* x, const void* lam, const void* u, const void*
         a.n = static_cast<int>(6 * tp);
         a.NL = static_cast<int>(part ? W : H); a.L = static_cast<int>(part ? H : W);
         a.NLp = static_cast<int>(part ? Wp : Hp); a.Lp = static_cast<int>(part ? Hp : Wp);
-        a.per_plane = FastDiv(static_cast<uint32_t>(HW));
-        a.per_line = FastDiv(static_cast<uint32_t>(a.L));
-        crop_lines_kernel<T><<<blocks(6 * tp * HW, 1), dim3(256), 0, stream>>>(a);
+        a.per_plane = FastDiv(static_cast<uint32_t>(HWp / 2));
+        a.per_line = FastDiv(static_cast<uint32_t>(a.Lp / 2));
+        crop_lines_kernel<T><<<blocks(6 * tp * HWp / 2, 1), dim3(256), 0, stream>>>(a);
     }
     return hipGetLastError();
 }
