@@ -242,12 +242,17 @@ def test_prop2d_writes_into_given_output_and_rejects_big_bf16_planes():
 
 # ------------------------------------------------------------------ scan_dir
 
-# Planes whose lambda x fits in LDS as fp32 (up to 40956 pixels) take the
-# one-wavefront kernel for lines up to 256 (K = 1 .. 4 positions a lane:
-# lines of 1..64, 65..128, 129..192, 193..256); longer lines and larger planes
-# take the general kernel: (1, 300) rows, (210, 210) every direction.
-SCAN_DIR_SHAPES = [(1, 1), (7, 1), (1, 9), (16, 16), (27, 27), (33, 70), (74, 74), (65, 129),
-                   (129, 65), (190, 200), (256, 40), (3, 193), (1, 300), (210, 210)]
+# One wavefront a plane, lines up to 256 (K = 1 .. 4 positions a lane).
+# Rows (top-down, bottom-up) stream, with whole-window loads where K divides
+# the row and windows are whole dwords (74, 70, 200; fp32 also 27, 129).
+# Columns stage lambda x one strip of 64 (bf16) or 32 (fp32) columns at a
+# time in LDS, transposed (one strip at 16, 27, 33; a partial last strip at
+# 70, 74, 129, 193, 200, 210; bf16 odd W moves one element a lane, W a
+# multiple of 4 or 8 wider vectors).  Longer lines take the general kernel:
+# (1, 300) rows.
+SCAN_DIR_SHAPES = [(1, 1), (7, 1), (1, 9), (2, 2), (16, 16), (27, 27), (33, 70), (74, 74), (65, 129),
+                   (129, 65), (190, 200), (256, 40), (3, 193), (1, 300), (210, 210), (128, 34),
+                   (64, 48)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
