@@ -84,13 +84,15 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
-    """Time the fp64 oracle on whole planes of the workload, single-threaded.
+    """Time the fp64 oracle on whole planes of the workload, single-threaded,
+    pinned to one host core; the median of three runs of a third of the
+    budget each.
 
-    The planes are those of the first rotated input set, in order, until the
-    time budget is spent; when the whole workload takes less than the budget
-    it is run again (whole passes) until the budget is reached.  The GPU
-    output of the first pass's planes from the timed steps is compared with
-    the oracle's as a by-product.
+    The planes are those of the first rotated input set, in order, until a
+    run's time is spent (whole passes again when the workload takes less);
+    the next run continues where the last stopped.  The GPU output of the
+    first pass's planes from the timed steps is compared with the oracle's
+    as a by-product.
     """
     import ctypes
 
@@ -107,35 +109,49 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
     X, LAM, U, Wt = (f64(gpu_inputs[k]) for k in ("x", "lam", "u", "w"))
     Wt = Wt.reshape(4, wl.B, wl.C, 3 * n)
     Y = f64(gpu_out)
-    planes, spent, all_ok, details = 0, 0.0, True, []
+    planes, all_ok, details = 0, True, []
     order = [(b, c) for b in range(wl.B) for c in range(wl.C)]
-    while spent < budget_s:
-        b, c = order[planes % len(order)]
-        arrs = [np.ascontiguousarray(a[b, c]) for a in (X, LAM, U)]
-        arrs.append(np.ascontiguousarray(Wt[:, b, c]))
-        y = np.empty_like(arrs[0])
-        t0 = time.perf_counter()
-        rc = lib.gspn_oracle_prop2d(*(a.ctypes.data_as(dp) for a in arrs), 1e-6,
-                                    y.ctypes.data_as(dp), 1, 1, wl.H, wl.W)
-        spent += time.perf_counter() - t0
-        if rc != 0:
-            raise MemoryError("oracle failed")
-        if planes < len(order):
-            ok, msg = compare(Y[b, c], y, RTOL[wl.dtype])
-            all_ok &= ok
-            if len(details) < 2 or not ok:
-                details.append("(%d,%d): %s" % (b, c, msg))
-        planes += 1
-    bytes_done = 16 * wl.elem_bytes * n * planes
+    per_plane_bytes = 16 * wl.elem_bytes * n
+    old_affinity = os.sched_getaffinity(0)
+    core = max(old_affinity)
+    os.sched_setaffinity(0, {core})
+    rates, total_spent = [], 0.0
+    try:
+        for _ in range(3):
+            spent, done = 0.0, 0
+            while spent < budget_s / 3:
+                b, c = order[planes % len(order)]
+                arrs = [np.ascontiguousarray(a[b, c]) for a in (X, LAM, U)]
+                arrs.append(np.ascontiguousarray(Wt[:, b, c]))
+                y = np.empty_like(arrs[0])
+                t0 = time.perf_counter()
+                rc = lib.gspn_oracle_prop2d(*(a.ctypes.data_as(dp) for a in arrs), 1e-6,
+                                            y.ctypes.data_as(dp), 1, 1, wl.H, wl.W)
+                spent += time.perf_counter() - t0
+                if rc != 0:
+                    raise MemoryError("oracle failed")
+                if planes < len(order):
+                    ok, msg = compare(Y[b, c], y, RTOL[wl.dtype])
+                    all_ok &= ok
+                    if len(details) < 2 or not ok:
+                        details.append("(%d,%d): %s" % (b, c, msg))
+                planes += 1
+                done += 1
+            rates.append(done * per_plane_bytes / spent / 1e9)
+            total_spent += spent
+    finally:
+        os.sched_setaffinity(0, old_affinity)
     return {
-        "value": bytes_done / spent / 1e9,
+        "value": float(np.median(rates)),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": "%d planes (%.1f passes over the %d planes, %dx%d, %s values, of the timed "
-                  "inputs), fp64 C loop, %.1f s" % (planes, planes / len(order), len(order), wl.H,
-                                                  wl.W, wl.dtype, spent),
-        "seconds": spent,
+                  "inputs), fp64 C loop on host core %d, three runs of %.1f s, median" % (
+                      planes, planes / len(order), len(order), wl.H, wl.W, wl.dtype, core,
+                      budget_s / 3),
+        "runs_GBps": [round(r, 4) for r in rates],
+        "seconds": total_spent,
         "cpu": _cpu_model(),
         "host_cores_visible": os.cpu_count(),
         "gpu_output_matches_oracle_on_sample": bool(all_ok),
