@@ -643,7 +643,12 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel_ms_avg": round(kern_avg, 5),
+                     "traffic": traffic,
+                     "traffic_source": ("profiles/prop2d_latent1k_traffic.json: rocprofv3 FETCH_SIZE and "
+                                        "WRITE_SIZE taken on this kernel source (source hash matched), "
+                                        "scaled by a 1 GiB copy's reading; not counted in this run"
+                                        if traffic is not None else None),
+                     "kernel_ms_avg": round(kern_avg, 5),
                      "kernel_ms_min": round(float(np.min(kern_ms)), 5)},
         "calibration": {"torch_copy_GBps": round(copy_gbps, 1),
                         "frac_of_copy": round(achieved / copy_gbps, 4)},
