@@ -251,9 +251,10 @@ hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const vo
                          float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                          const PropOpts& o, hipStream_t stream) {
     // square bf16 planes: one wavefront a plane up to 80, except when there
-    // are too few planes to fill the CUs, where two wavefronts a plane finish
-    // sooner (sides 66..80: 128 and 256 planes of 74 x 74 take 0.029 ms
-    // against 0.037); two wavefronts a plane for sides 82..96
+    // are too few planes to fill the CUs, where a wavefront a direction
+    // finishes sooner (sides 66..80: 128 planes of 74 x 74 take 0.025 ms
+    // against 0.037); two wavefronts a plane for sides 82..96, four for
+    // 98..150
     const bool few = planes <= kFewPlanes && H > 64;
     if (!few && prop2d_quad_eligible(dtype, planes, H, W, o, x, lam, u, w4, y))
         return launch_prop2d_quad(x, lam, u, w4, eps, y, planes, H, o, stream);

@@ -121,9 +121,12 @@ def test_prop2d_quad_sides(L):
 
 
 # square bf16 planes with even sides 66..80 and at most 256 planes, and sides
-# 82..96, take the kernel with two wavefronts a plane (rows in one, columns in
-# the other, 32 lanes a direction, K = 3); the sides cover every (L - 1) mod 3
-DUO_SIDES = [66, 68, 70, 74, 80, 82, 84, 86, 90, 94, 96]
+# 82..150, take the kernel that runs the row and the column scans in different
+# wavefronts: a wavefront a direction (64 lanes, K = 2 up to 128, 3 up to 150)
+# at 66..80 and 98..150, two wavefronts a plane (32 lanes a direction, K = 3)
+# at 82..96; the sides cover every (L - 1) mod K an even side has
+DUO_SIDES = [66, 68, 70, 74, 80, 82, 84, 86, 90, 94, 96, 98, 100, 112, 126, 128, 130, 132, 134, 136,
+             138, 148, 150]
 
 
 @pytest.mark.parametrize("L", DUO_SIDES)
