@@ -49,7 +49,7 @@ def test_prop2d_small_workloads_all_seeds(name):
 
 # Forward dispatch.  bf16: square planes with even sides up to 80 take the
 # four-directions-a-wavefront kernel (K = 1..5 positions a lane in 16-lane
-# rows), except that sides 66..80 with at most 256 planes, and sides 82..96,
+# rows), except that sides 66..80 with at most 512 planes, and sides 82..96,
 # take the two-wavefronts-a-plane kernel (K = 1..3 over 32 lanes); other
 # planes with even sides up to 160 take the rows-then-columns phase kernel.
 # fp32: planes up to 96 the two-wavefront pair kernel, planes with sides up
@@ -104,7 +104,7 @@ def test_prop2d_phase_one_wave_form(H, W):
 # square bf16 planes with even sides up to 80 take the kernel that scans the
 # four directions at once (16 lanes a direction, K = 1 .. 5 positions a lane);
 # sides cover every K and every value of (L - 1) mod K it is built for.  Sides
-# above 64 take it only with more than 256 planes.
+# above 64 take it only with more than 512 planes.
 QUAD_SIDES = [2, 4, 6, 14, 16, 18, 30, 32, 34, 36, 38, 46, 48, 50, 52, 62, 64, 66, 68, 70, 72, 74,
               76, 78, 80]
 
@@ -112,7 +112,7 @@ QUAD_SIDES = [2, 4, 6, 14, 16, 18, 30, 32, 34, 36, 38, 46, 48, 50, 52, 62, 64, 6
 @pytest.mark.parametrize("L", QUAD_SIDES)
 def test_prop2d_quad_sides(L):
     say("prop2d quad", L)
-    B, C = (3, 5) if L <= 64 else (3, 90)
+    B, C = (3, 5) if L <= 64 else (6, 90)
     p = _problem(B, C, L, L, 101 + L, "bf16")
     y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
     torch.cuda.synchronize()
@@ -120,7 +120,7 @@ def test_prop2d_quad_sides(L):
                  "%dx%d bf16" % (L, L))
 
 
-# square bf16 planes with even sides 66..80 and at most 256 planes, and sides
+# square bf16 planes with even sides 66..80 and at most 512 planes, and sides
 # 82..150, take the kernel that runs the row and the column scans in different
 # wavefronts: a wavefront a direction (64 lanes, K = 2 up to 128, 3 up to 150)
 # at 66..80 and 98..150, two wavefronts a plane (32 lanes a direction, K = 3)
@@ -142,10 +142,10 @@ def test_prop2d_duo_sides(L):
 def test_prop2d_duo_and_quad_agree_bitwise():
     # both kernels add each pixel's four directional terms in step order (the
     # terms of a step's meeting pixels after the scan), so the plane a small
-    # launch computes with two wavefronts equals the one a full launch computes
-    # with one
+    # launch computes with a wavefront a direction equals the one a full
+    # launch computes with one wavefront a plane
     say("prop2d duo vs quad 74x74")
-    p = _problem(4, 80, 74, 74, 77, "bf16")            # 320 planes: the quad kernel
+    p = _problem(8, 80, 74, 74, 77, "bf16")            # 640 planes: the quad kernel
     y_all = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
     sl = lambda t: t[1:2].contiguous()                   # 80 planes: the duo kernel
     y_one = gspn.prop2d_4dir(sl(p["x"]), sl(p["lam"]), sl(p["u"]), p["w"][:, 1:2].contiguous())
