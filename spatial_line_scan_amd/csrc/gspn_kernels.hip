@@ -254,7 +254,7 @@ hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const vo
     // are too few planes to fill the CUs, where a wavefront a direction
     // finishes sooner (sides 66..80: 128 planes of 74 x 74 take 0.025 ms
     // against 0.037); two wavefronts a plane for sides 82..96, four for
-    // 98..150
+    // 98..150 and odd 97..149
     const bool few = planes <= kFewPlanes && H > 64;
     if (!few && prop2d_quad_eligible(dtype, planes, H, W, o, x, lam, u, w4, y))
         return launch_prop2d_quad(x, lam, u, w4, eps, y, planes, H, o, stream);

@@ -1,5 +1,5 @@
-// Four-direction propagation of square bf16 planes with even sides 66..150,
-// all four directions in the same step, with the two row scans and the two
+// Four-direction propagation of square bf16 planes with even sides 66..150
+// and odd sides 97..149, all four directions in the same step, with the two row scans and the two
 // column scans in different wavefronts of one workgroup (gfx950).
 //
 // Operator: "Scaling Parallel Sequence Models to Foundation-Scale Vision
@@ -15,7 +15,7 @@
 //     last lane receives from the other half only meets a dropped tap
 //     (weight exactly 0).
 //   - 64 lanes a direction (four wavefronts a plane): top-down, bottom-up,
-//     left-right, right-left.
+//     left-right, right-left.  The only form for odd sides.
 // Lane q holds positions Kq .. Kq+K-1 of its line; the neighbour exchange is
 // one whole-wavefront DPP shift each way.
 //
@@ -45,8 +45,11 @@
 // (s, L-1-s), (L-1-s, s) and (L-1-s, L-1-s); there the column scan adds its
 // state into a side word indexed by the step, and the side words are added
 // into the diagonals after the scan.  Row scans never meet each other
-// (L even), nor do column scans.  Each pixel's four terms are therefore
-// summed in a fixed order and the result is bitwise reproducible.
+// (L even), nor do column scans.  With L odd the two row scans both reach
+// the middle row m = (L-1)/2 at step m (and the column scans the middle
+// column): there the bottom-up and right-left scans write their terms into
+// separate mid lines, added in after the scan.  Each pixel's four terms are
+// therefore summed in a fixed order and the result is bitwise reproducible.
 //
 // Slots past the end of a line (positions >= L) read and write dummy words,
 // decode every tap to -2^127 (weight exactly 0) and hold h = 0; lanes whose
@@ -67,27 +70,34 @@ using namespace lane;
 // (the pad), one row after it (side), and for b the neighbouring arrays or
 // b_lo's spare row.  b_hi and b_lo have 8 spare entries for the second half
 // of the plane's last 16-byte chunk when L L is not a multiple of 8.
+// mid fp32 [2][L]: with L odd, where the bottom-up scan puts its terms of the
+// middle row and the right-left scan its terms of the middle column (each
+// pair of scans reaches its middle line in the same step); added into S
+// after the scan.
 struct DuoLayout {
-    int s, side, bh, bl, bytes;
+    int s, side, mid, bh, bl, bytes;
     static constexpr int sdum = 0, bdum = 16;
     __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
     __host__ __device__ explicit DuoLayout(int L) {
         const int n = L * L;
         s = a16(32 + 4 * L);
         side = a16(s + 4 * n);
-        bh = a16(side + 16 * L);
+        mid = a16(side + 16 * L);
+        bh = a16(mid + 8 * L);
         bl = a16(bh + 2 * (n + 8));
         bytes = a16(bl + n + L + 8);
     }
 };
 
 constexpr int kMaxSide = 150;       // the layout's LDS at 150 x 150: 157 KB
+constexpr int kMinOddSide = 97;     // odd sides: a wavefront a direction, 97..149
 // 16-byte chunks of a plane's bf16 values a thread loads at once (a 96 x 96
 // plane in one batch)
 constexpr int kBatch = 9;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_u __attribute__((ext_vector_type(4), aligned(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <typename V> using lds_t = __attribute__((address_space(3))) V;
 
@@ -170,12 +180,19 @@ __device__ __forceinline__ void fill_plane(const DuoLayout& lay, int tid, int nc
 // LANES: lanes a direction (32: a wavefront holds both scans of the pair,
 // one per half; 64: a wavefront per scan, `half` says which).  NT: threads
 // of the workgroup.
-template <int K, int R, int D, bool ROWS, int LANES, int NT>
+// Odd: L odd (lines and planes start at any element; see the window notes
+// below), a wavefront a direction.
+template <int K, int R, int D, bool ROWS, int LANES, int NT, bool Odd>
 __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay, int tid, int lane,
                                           int wave_half, int nchunk, __amdgpu_buffer_rsrc_t xs,
                                           __amdgpu_buffer_rsrc_t ls, uint32_t plane_b) {
     static_assert(D % K == 0, "blocks of whole slot cycles");
-    constexpr int NW = window_words<uint16_t, K>();
+    static_assert(!Odd || (D % 2 == 0 && LANES == 64), "odd lines: window parity alternates with the ring slot");
+    // words a window decodes from, and words loaded for it: with Odd a window
+    // is loaded from the even element at or below its first and shifted into
+    // place, which for even K takes one more word
+    constexpr int NW = Odd ? (K + 1) / 2 : window_words<uint16_t, K>();
+    constexpr int NWL = Odd && (K % 2 == 0) ? NW + 1 : NW;
     const int L = a.L;
     const int n = L * L;
     const int half = LANES == 32 ? lane >> 5 : wave_half;
@@ -190,7 +207,7 @@ __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay
     for (int k = 0; k < 3; ++k)
         taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.w4) + static_cast<size_t>(k) * n,
                                                     0, a.w4_bytes - k * n * 2, kBufFlags);
-    const int par = (K * q) & 1;
+    const int par = Odd ? 0 : (K * q) & 1;
     const bool lane_live = K * q < L;
     const uint32_t line_b = static_cast<uint32_t>(L) * 2u;
     const uint32_t tap_base =
@@ -200,12 +217,67 @@ __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay
     const uint32_t lo_max = lane_live ? tap_base + static_cast<uint32_t>(L - 1) * line_b : 0x80000000u;
     uint32_t lo = fwd ? lo_min : lo_max;
     const uint32_t dlo = lane_live ? (fwd ? line_b : 0u - line_b) : 0u;
-    words_t<NW> tbuf[D][3];
+    // Odd: a window starts at element E (its first position Kq on the line);
+    // it is loaded from element E & ~1 and shifted right by 16 bits when E is
+    // odd.  Along a scan E moves by +-L, so its parity alternates from step to
+    // step: ring slot d (steps of d's parity, D even) uses the shift and the
+    // offset increment of its parity.  Tap plane 2 lies 2 n elements after
+    // plane 0 (same parity: a scalar offset); plane 1 lies n after it, which
+    // with n odd flips the parity (a scalar offset plus 4 bytes on the steps
+    // where plane 0's window starts odd).  Reads past a scan's end run on
+    // into the next lines or past the tensor (0); they are never used.
+    __amdgpu_buffer_rsrc_t tall = taps[0];
+    uint32_t incE = 0, incO = 0, shE = 0, shO = 0, add1E = 0, add1O = 0, sh1E = 0, sh1O = 0;
+    int so1 = 0, so2 = 0;
+    if constexpr (Odd) {
+        tall = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.w4), 0, (a.w4_bytes + 3) & ~3, kBufFlags);
+        const int line0 = fwd ? 0 : L - 1;
+        const int dl = fwd ? L : -L;
+        const int e0 = ((g * tap_planes + a.plane / a.cpg) * 3) * n + line0 * L + K * q;
+        const int p0 = e0 & 1, p1 = p0 ^ 1;
+        lo = static_cast<uint32_t>(e0 - p0) * 2u;
+        incE = static_cast<uint32_t>(2 * dl - 2 + 4 * p0);
+        incO = static_cast<uint32_t>(2 * dl - 2 + 4 * p1);
+        shE = 16u * p0;
+        shO = 16u * p1;
+        add1E = 4u * p0;
+        add1O = 4u * p1;
+        sh1E = shE ^ 16u;
+        sh1O = shO ^ 16u;
+        so1 = 2 * n - 2;
+        so2 = 4 * n;
+    }
+    words_t<NWL> tbuf[D][3];
     auto load_line = [&](int d) {
+        if constexpr (Odd) {
+            const bool od = (d & 1) != 0;
+            tbuf[d][0] = load_words_so<NWL>(tall, lo, 0);
+            tbuf[d][1] = load_words_so<NWL>(tall, lo + (od ? add1O : add1E), so1);
+            tbuf[d][2] = load_words_so<NWL>(tall, lo, so2);
+            lo += od ? incO : incE;
+        } else {
 #pragma unroll
-        for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
-        const uint32_t nx = lo + dlo;
-        lo = nx < lo_min ? lo_min : (nx > lo_max ? lo_max : nx);
+            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
+            const uint32_t nx = lo + dlo;
+            lo = nx < lo_min ? lo_min : (nx > lo_max ? lo_max : nx);
+        }
+    };
+    // the NW words a window decodes from (Odd: shifted into place)
+    auto window = [&](const words_t<NWL>& w, uint32_t sh) -> words_t<NW> {
+        if constexpr (Odd) {
+            words_t<NW> rv;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const uint32_t lo_w = word<NWL>(w, i);
+                const uint32_t hi_w = word<NWL>(w, i + 1 < NWL ? i + 1 : NWL - 1);
+                const uint32_t v = __builtin_amdgcn_alignbit(hi_w, lo_w, sh);
+                if constexpr (NW == 1) rv = v;
+                else rv[i] = v;
+            }
+            return rv;
+        } else {
+            return w;
+        }
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -239,6 +311,21 @@ __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay
         sel[1][j] = valid ? s_in : kSelDropped;
         sel[2][j] = (valid && p < L - 1) ? s_in : kSelDropped;
     }
+    // Odd: the backward scan of the pair (bottom-up, right-left) puts its
+    // terms of the middle line (step m) into the mid lines
+    const bool mid_scan = Odd && !fwd;
+    const int m = L / 2;
+    uint32_t aM[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int p = K * q + j;
+        aM[j] = p < L ? static_cast<uint32_t>(lay.mid + 4 * (ROWS ? 0 : L) + 4 * p) : DuoLayout::sdum;
+    }
+    // the S word of slot j at step s (the mid line at the middle step)
+    auto base = [&](int j, int s) -> uint32_t {
+        if constexpr (Odd) return (mid_scan && s == m) ? aM[j] : aS[j];
+        else return aS[j];
+    };
     // column slots that meet a row scan go to side words
     const uint32_t side1 = static_cast<uint32_t>(lay.side + 4 * L * (g == 3 ? 1 : 0));
     const uint32_t side2 = static_cast<uint32_t>(lay.side + 4 * L * (g == 3 ? 3 : 2));
@@ -260,7 +347,7 @@ __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay
             const uint32_t q1 = static_cast<uint32_t>(qb1 + t / K);
             const uint32_t q2 =
                 static_cast<uint32_t>(qb2 + (R - t >= 0 ? (R - t) / K : -((t - R + K - 1) / K)));
-            uint32_t m1 = aS[j1], m2 = aS[j2];
+            uint32_t m1 = base(j1, s), m2 = base(j2, s);
             m1 = key == q1 ? side1 + 4u * s : m1;
             if (j2 == j1) m2 = m1;
             m2 = key == q2 ? side2 + 4u * s : m2;
@@ -270,8 +357,8 @@ __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay
         }
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            uint32_t ad = aS[j];
-            if constexpr (!ROWS) ad = j == j1 ? ra1 : (j == j2 ? ra2 : aS[j]);
+            uint32_t ad = base(j, s);
+            if constexpr (!ROWS) ad = j == j1 ? ra1 : (j == j2 ? ra2 : ad);
             acc[j] = lds_ref<float>(ad);
         }
     };
@@ -290,11 +377,15 @@ __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay
     // decode and exponentials, then the sigmoids, their sum and its inverse
     auto weights_a = [&](int d) {
         asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
+        const bool od = (d & 1) != 0;
+        const words_t<NW> w0 = window(tbuf[d][0], od ? shO : shE);
+        const words_t<NW> w1 = window(tbuf[d][1], od ? sh1O : sh1E);
+        const words_t<NW> w2 = window(tbuf[d][2], od ? shO : shE);
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            s0v[j] = window_elem<uint16_t, K, NW>(tbuf[d][0], j, sel[0][j], sel[0][j]) * kNegLog2e;
-            s1v[j] = window_elem<uint16_t, K, NW>(tbuf[d][1], j, sel[1][j], sel[1][j]) * kNegLog2e;
-            s2v[j] = window_elem<uint16_t, K, NW>(tbuf[d][2], j, sel[2][j], sel[2][j]) * kNegLog2e;
+            s0v[j] = window_elem<uint16_t, K, NW>(w0, j, sel[0][j], sel[0][j]) * kNegLog2e;
+            s1v[j] = window_elem<uint16_t, K, NW>(w1, j, sel[1][j], sel[1][j]) * kNegLog2e;
+            s2v[j] = window_elem<uint16_t, K, NW>(w2, j, sel[2][j], sel[2][j]) * kNegLog2e;
         }
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -362,8 +453,8 @@ __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay
         const int j2 = ((R - t) % K + K) % K;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            uint32_t ad = aS[j];
-            if constexpr (!ROWS) ad = j == j1 ? ra1 : (j == j2 ? ra2 : aS[j]);
+            uint32_t ad = base(j, s);
+            if constexpr (!ROWS) ad = j == j1 ? ra1 : (j == j2 ? ra2 : ad);
             lds_ref<float>(ad) = acc[j] + h[j];
         }
         // the pins keep each address one add a step instead of base +
@@ -394,7 +485,7 @@ __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay
     }
 }
 
-template <int K, int R, int D, int LANES>
+template <int K, int R, int D, int LANES, bool Odd>
 __global__ void __launch_bounds__(LANES == 32 ? 128 : 256)
 prop2d_duo_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
                   const uint16_t* __restrict__ u, const uint16_t* __restrict__ w4, int w4_bytes,
@@ -408,7 +499,12 @@ prop2d_duo_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ l
     const int plane = blockIdx.x;
     const uint32_t plane_b = static_cast<uint32_t>(plane) * static_cast<uint32_t>(n) * 2u;
     const int nchunk = (2 * n + 15) / 16;   // 16-byte chunks of a plane's bf16 values
-    const int span = static_cast<int>(static_cast<int64_t>(planes) * n * 2);
+    // Odd L: planes start at any element, so a plane's 16-byte chunks are not
+    // dword aligned; a dword that straddles a buffer's end reads as 0, so the
+    // bound reaches past the dword holding the last element (2 bytes at most
+    // past the tensor, never used)
+    const int bytes = static_cast<int>(static_cast<int64_t>(planes) * n * 2);
+    const int span = Odd ? ((bytes + 2 + 3) & ~3) : bytes;
 
     // ------------------------------------------------ u: the first batch, prefetched for the end
     const __amdgpu_buffer_rsrc_t us = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(u), 0, span, kBufFlags);
@@ -429,14 +525,16 @@ prop2d_duo_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ l
     const bool rows = LANES == 32 ? wave == 0 : wave < 2;
     const int wave_half = LANES == 32 ? 0 : (wave & 1);
     if (rows)
-        scan_pair<K, R, D, true, LANES, NT>(a, lay, tid, lane, wave_half, nchunk, xs, ls, plane_b);
+        scan_pair<K, R, D, true, LANES, NT, Odd>(a, lay, tid, lane, wave_half, nchunk, xs, ls, plane_b);
     else
-        scan_pair<K, R, D, false, LANES, NT>(a, lay, tid, lane, wave_half, nchunk, xs, ls, plane_b);
+        scan_pair<K, R, D, false, LANES, NT, Odd>(a, lay, tid, lane, wave_half, nchunk, xs, ls, plane_b);
     block_lds_barrier();
 
     // ------------------------------------------------ meeting pixels
     // (t, t) += LR's side word of step t + RL's of step L-1-t;
-    // (t, L-1-t) += RL's of step t + LR's of step L-1-t
+    // (t, L-1-t) += RL's of step t + LR's of step L-1-t.
+    // Odd L: the middle row and column get the mid lines; of their pixels
+    // only (m, m) is also on a diagonal, and its thread adds both.
     for (int t = tid; t < L; t += NT) {
         const uint32_t sd = static_cast<uint32_t>(lay.s + 4 * (t * L + t));
         const uint32_t sa = static_cast<uint32_t>(lay.s + 4 * (t * L + L - 1 - t));
@@ -446,6 +544,19 @@ prop2d_duo_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ l
         const float a1 = lds_ref<float>(lay.side + 4 * (2 * L + L - 1 - t));
         lds_ref<float>(sd) = (lds_ref<float>(sd) + d0) + d1;
         lds_ref<float>(sa) = (lds_ref<float>(sa) + a0) + a1;
+        if constexpr (Odd) {
+            const int m = L / 2;
+            const float mr = lds_ref<float>(lay.mid + 4 * t);
+            const float mc = lds_ref<float>(lay.mid + 4 * (L + t));
+            if (t == m) {
+                lds_ref<float>(sd) = (lds_ref<float>(sd) + mr) + mc;
+            } else {
+                const uint32_t sr = static_cast<uint32_t>(lay.s + 4 * (m * L + t));
+                const uint32_t sc = static_cast<uint32_t>(lay.s + 4 * (t * L + m));
+                lds_ref<float>(sr) = lds_ref<float>(sr) + mr;
+                lds_ref<float>(sc) = lds_ref<float>(sc) + mc;
+            }
+        }
     }
     block_lds_barrier();
 
@@ -473,23 +584,39 @@ prop2d_duo_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ l
             o[2] = pack_bf16x2(bf_lo(uv[k][2]) * sb[0], bf_hi(uv[k][2]) * sb[1]);
             o[3] = pack_bf16x2(bf_lo(uv[k][3]) * sb[2], bf_hi(uv[k][3]) * sb[3]);
             const uint32_t yo = plane_b + 16u * static_cast<uint32_t>(f);
-            if (f < nfull)
+            if constexpr (Odd) {
+                // planes start at any element: whole chunks as one unaligned
+                // store, the last one element by element (never into the next
+                // plane, which another workgroup writes)
+                uint16_t* yp = y + static_cast<size_t>(plane) * n + 8 * f;
+                if (f < nfull) {
+                    *reinterpret_cast<u32x4_u*>(yp) = o;
+                } else {
+                    const int rest = n - 8 * f;
+#pragma unroll
+                    for (int e = 0; e < 7; ++e)
+                        if (e < rest) yp[e] = static_cast<uint16_t>(o[e >> 1] >> (16 * (e & 1)));
+                }
+            } else if (f < nfull) {
                 __builtin_amdgcn_raw_buffer_store_b128(o, ys, yo, 0, 0);
-            else  // a plane of L L = 4 mod 8 values ends half way into its last chunk
+            } else {  // a plane of L L = 4 mod 8 values ends half way into its last chunk
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{o[0], o[1]}, ys, yo, 0, 0);
+            }
         }
     }
     }
 }
 
-template <int K, int R, int LANES>
+template <int K, int R, int LANES, bool Odd>
 hipError_t launch_kr(const void* x, const void* lam, const void* u, const void* w4, float eps,
                      void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
     // lines of taps in flight: a multiple of K, at least 8 up to K = 3 (the
-    // ring of 3-dword windows stays within the registers for K = 4, 5)
-    constexpr int D = K <= 3 ? K * ((8 + K - 1) / K) : K;
+    // ring of 3-dword windows stays within the registers for K = 4, 5); odd
+    // L: also even
+    constexpr int DM = Odd && (K % 2) ? 2 * K : K;
+    constexpr int D = K <= 3 ? DM * ((8 + DM - 1) / DM) : DM;
     const size_t lds = DuoLayout(static_cast<int>(L)).bytes;
-    auto kern = prop2d_duo_kernel<K, R, D, LANES>;
+    auto kern = prop2d_duo_kernel<K, R, D, LANES, Odd>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -504,12 +631,12 @@ hipError_t launch_kr(const void* x, const void* lam, const void* u, const void* 
     return hipGetLastError();
 }
 
-template <int K, int LANES, int R = K - 1>
+template <int K, int LANES, bool Odd = false, int R = K - 1>
 hipError_t launch_k(const void* x, const void* lam, const void* u, const void* w4, float eps,
                     void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
     // R = (L - 1) mod K
-    if ((L - 1) % K == R) return launch_kr<K, R, LANES>(x, lam, u, w4, eps, y, planes, L, o, stream);
-    if constexpr (R > 0) return launch_k<K, LANES, R - 1>(x, lam, u, w4, eps, y, planes, L, o, stream);
+    if ((L - 1) % K == R) return launch_kr<K, R, LANES, Odd>(x, lam, u, w4, eps, y, planes, L, o, stream);
+    if constexpr (R > 0) return launch_k<K, LANES, Odd, R - 1>(x, lam, u, w4, eps, y, planes, L, o, stream);
     return hipErrorInvalidValue;
 }
 
@@ -520,7 +647,8 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool prop2d_duo_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                          const void* x, const void* lam, const void* u, const void* w4,
                          const void* y) {
-    if (dtype != 1 || H != W || (H & 1) || H <= 64 || H > kMaxSide) return false;
+    if (dtype != 1 || H != W || H <= 64 || H > kMaxSide) return false;
+    if ((H & 1) && H < kMinOddSide) return false;
     if (o.k_chunk != 1) return false;
     if (DuoLayout(static_cast<int>(H)).bytes > kLdsBytes) return false;
     if (12 * planes * H * W * 2 > 0x7fffffff) return false;
@@ -536,6 +664,9 @@ hipError_t launch_prop2d_duo(const void* x, const void* lam, const void* u, cons
     // lanes a direction, K = 3, 96 slots a line) for sides 82..96, where
     // their fuller lines win (96 x 96: 0.041 ms against 0.045 with 64 lanes,
     // 256 planes).
+    if (L & 1)
+        return L <= 128 ? launch_k<2, 64, true>(x, lam, u, w4, eps, y, planes, L, o, stream)
+                        : launch_k<3, 64, true>(x, lam, u, w4, eps, y, planes, L, o, stream);
     if (L <= 80) return launch_k<2, 64>(x, lam, u, w4, eps, y, planes, L, o, stream);
     if (L <= 96) return launch_k<3, 32>(x, lam, u, w4, eps, y, planes, L, o, stream);
     if (L <= 128) return launch_k<2, 64>(x, lam, u, w4, eps, y, planes, L, o, stream);

@@ -49,9 +49,10 @@ def test_prop2d_small_workloads_all_seeds(name):
 
 # Forward dispatch.  bf16: square planes with even sides up to 80 take the
 # four-directions-a-wavefront kernel (K = 1..5 positions a lane in 16-lane
-# rows), except that sides 66..80 with at most 512 planes, and sides 82..96,
-# take the two-wavefronts-a-plane kernel (K = 1..3 over 32 lanes); other
-# planes with even sides up to 160 take the rows-then-columns phase kernel.
+# rows), except that sides 66..80 with at most 512 planes, even sides
+# 82..150 and odd sides 97..149 take the kernel with the row and column
+# scans in different wavefronts; other planes with sides up to 160 take the
+# rows-then-columns phase kernel.
 # fp32: planes up to 96 the two-wavefront pair kernel, planes with sides up
 # to 256 that are multiples of 4 the one-launch-per-direction kernel (y
 # accumulates; columns in strips of 32).  The rest take the general kernel.
@@ -124,9 +125,12 @@ def test_prop2d_quad_sides(L):
 # 82..150, take the kernel that runs the row and the column scans in different
 # wavefronts: a wavefront a direction (64 lanes, K = 2 up to 128, 3 up to 150)
 # at 66..80 and 98..150, two wavefronts a plane (32 lanes a direction, K = 3)
-# at 82..96; the sides cover every (L - 1) mod K an even side has
+# at 82..96; the sides cover every (L - 1) mod K an even side has.  Odd sides
+# 97..149 take its wavefront-a-direction form (every (L - 1) mod K an odd
+# side has; planes start at even and odd elements, the middle row and column
+# are met by both scans of a pair).
 DUO_SIDES = [66, 68, 70, 74, 80, 82, 84, 86, 90, 94, 96, 98, 100, 112, 126, 128, 130, 132, 134, 136,
-             138, 148, 150]
+             138, 148, 150, 97, 99, 101, 115, 127, 129, 131, 133, 147, 149]
 
 
 @pytest.mark.parametrize("L", DUO_SIDES)
@@ -137,6 +141,21 @@ def test_prop2d_duo_sides(L):
     torch.cuda.synchronize()
     assert_close(_np(y), oracle.prop2d(p["x"], p["lam"], p["u"], p["w"]), RTOL["bf16"],
                  "%dx%d bf16" % (L, L))
+
+
+@pytest.mark.parametrize("L,B,C", [(147, 4, 71), (99, 3, 101)])
+def test_prop2d_duo_odd_many_planes(L, B, C):
+    # more planes than the CUs hold at once, an odd count: planes at every
+    # element parity, the last one ending inside a dword of the tensor
+    say("prop2d duo odd planes", L, B, C)
+    p = _problem(B, C, L, L, 5 + L, "bf16")
+    y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    for (b, c) in _sampled_planes(B, C, k=8):
+        sl = lambda t: t[b:b + 1, c:c + 1]
+        r = oracle.prop2d(sl(p["x"]), sl(p["lam"]), sl(p["u"]), p["w"][:, b:b + 1, c:c + 1])
+        assert_close(_np(sl(y)), r, RTOL["bf16"], "%dx%d plane (%d,%d)" % (L, L, b, c))
 
 
 def test_prop2d_duo_and_quad_agree_bitwise():
