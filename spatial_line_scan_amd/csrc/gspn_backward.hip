@@ -528,7 +528,17 @@ hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u,
                                   const void* gy, float eps, void* gx, void* glam, void* gu,
                                   void* gw4, void* ws, int dtype, int64_t planes, int64_t H,
                                   int64_t W, const PropOpts& o, hipStream_t stream) {
-    if (ws && padded_pair_shape(planes, H, W) && segments_keep(H, o.k_chunk) && segments_keep(W, o.k_chunk)) {
+    // square bf16 planes of odd side with per-channel taps take the pair
+    // kernel's odd form directly; other odd shapes that fit it padded run
+    // padded
+    const bool odd = odd_shape(H, W);
+    const void* ptrs0[] = {x, lam, u, w4, gy, gx, glam, gu, gw4};
+    const bool odd_direct =
+        odd && dtype == 1 && o.cpg == 1 && ws &&
+        prop2d_backward_pair_eligible(dtype, planes, H, W, ptrs0, 9,
+                                      static_cast<char*>(ws) + group_grad_bytes(planes, H, W, o.cpg));
+    if (!odd_direct && ws && padded_pair_shape(planes, H, W) && segments_keep(H, o.k_chunk) &&
+        segments_keep(W, o.k_chunk)) {
         const int64_t Hp = H + (H & 1), Wp = W + (W & 1);
         const int64_t n = planes * Hp * Wp, nt = 12 * (planes / o.cpg) * Hp * Wp;
         char* p = static_cast<char*>(ws) + direct_workspace_bytes(planes, Hp, Wp, o.cpg);
@@ -557,7 +567,7 @@ hipError_t launch_prop2d_backward(const void* x, const void* lam, const void* u,
     const int64_t pair = prop2d_backward_pair_shape(planes, H, W)
                              ? prop2d_backward_pair_workspace_bytes(planes, H, W) : 0;
     const int64_t avail = ws ? (general > pair ? general : pair) : 0;
-    if (prop2d_backward_pair_eligible(dtype, planes, H, W, ptrs, 9, rest)) {
+    if (!(odd && grouped) && prop2d_backward_pair_eligible(dtype, planes, H, W, ptrs, 9, rest)) {
         if (grouped) {
             // partial sums at the start of the workspace, the weights after
             // the per-channel region

@@ -167,6 +167,42 @@ __device__ __forceinline__ f32x2_t load_pair(const T* p, size_t e) {
     }
 }
 
+// Odd line lengths (bf16): a window of K elements starting at element E is
+// loaded from the even element at or below E and shifted right by 16 bits
+// when E is odd.  Along a scan E moves by +-L, so with L odd its parity
+// alternates from line to line, and a ring of D (even) prefetched lines
+// gives every slot a fixed parity.  A stream's state: the byte offset of
+// the next load, the increments after a load of even and of odd parity (in
+// the slot order of the scan's first line), and the shift of even slots.
+struct OddStream {
+    uint32_t off, incE, incO, shE;
+};
+__device__ __forceinline__ OddStream odd_stream(int e0, int dl) {
+    const int p0 = e0 & 1;
+    return {static_cast<uint32_t>(e0 - p0) * 2u, static_cast<uint32_t>(2 * dl - 2 + 4 * p0),
+            static_cast<uint32_t>(2 * dl - 2 + 4 * (p0 ^ 1)), 16u * static_cast<uint32_t>(p0)};
+}
+// The NW words a window decodes from: with Odd, the NWL loaded words shifted
+// right by sh bits (0 or 16).
+template <bool Odd, int NW, int NWL>
+__device__ __forceinline__ words_t<NW> odd_window(const words_t<NWL>& w, uint32_t sh) {
+    if constexpr (!Odd) {
+        return w;
+    } else {
+        words_t<NW> rv;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const uint32_t v = __builtin_amdgcn_alignbit(word<NWL>(w, i + 1 < NWL ? i + 1 : NWL - 1),
+                                                         word<NWL>(w, i), sh);
+            if constexpr (NW == 1) rv = v;
+            else rv[i] = v;
+        }
+        return rv;
+    }
+}
+// Two bf16 values at any element (a 4-byte load at 2-byte alignment).
+typedef uint32_t u32_u __attribute__((aligned(2)));
+
 // Cols = false: the row pair (NL = H, L = W), inputs as they are; writes S and
 // G of the pair to s_ws, g_ws ([planes][H][W] fp32).
 // Cols = true: the column pair (NL = W, L = H), inputs transposed; adds the
@@ -184,7 +220,12 @@ __device__ __forceinline__ f32x2_t load_pair(const T* p, size_t e) {
 // goes to gwd as fp32, one plane of partial sums per workgroup
 // ([4][planes / cc][3][..][..]).  The normalisation's Jacobian is applied
 // once per group afterwards.
-template <typename T, typename GT, int K, int D, bool Cols, bool Chunked, bool Pre, int CC>
+// Odd (bf16, per-channel taps, square planes of odd side): lines and planes
+// start at any element (windows as OddStream describes); tap gradients go
+// out one element a lane per store; S and G of the row pair are kept at a
+// plane stride of HW rounded up to 4; the column pair's outputs are written
+// in pixel pairs of unaligned dwords, a plane's odd last pixel alone.
+template <typename T, typename GT, int K, int D, bool Cols, bool Chunked, bool Pre, int CC, bool Odd>
 __global__ void __launch_bounds__(128 * CC)
 prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml,
                             const T* __restrict__ ul, const T* __restrict__ gyl,
@@ -197,13 +238,20 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                             T* __restrict__ gu, const float* __restrict__ wpre, int wpre_bytes) {
     static_assert(!Pre || sizeof(GT) == 4, "partial sums of tap products are fp32");
     static_assert(CC == 1 || Pre, "planes are added only with prepared weights");
+    static_assert(!Odd || (sizeof(T) == 2 && sizeof(GT) == 2 && !Pre && D % 2 == 0),
+                  "odd lines: bf16, per-channel taps, slots of fixed parity");
     constexpr int cc = CC;
     constexpr int ES = sizeof(T);
-    constexpr int NW = window_words<T, K>();
-    constexpr int TW = Pre ? K : NW;        // words of a tap window: fp32 weights or raw taps
+    // words a window decodes from, and words loaded for it (Odd: one more
+    // for even K, which the shift needs)
+    constexpr int NW = Odd ? (K + 1) / 2 : window_words<T, K>();
+    constexpr int NWL = Odd && (K % 2 == 0) ? NW + 1 : NW;
+    constexpr int TW = Pre ? K : NWL;       // words loaded for a tap window: fp32 weights or raw taps
     constexpr bool kNarrow = ES == 2;
     constexpr int VW = kNarrow ? 2 : 4;     // bytes of a value in the A / B array
     const int HW = NL * L;
+    // plane stride of the row pair's S and G (fp32, workspace)
+    const int HWa = Odd ? (HW + 3) & ~3 : HW;
     constexpr int GS = sizeof(GT);
     PairBwdLayout lay(NL, L, kNarrow, GS, CC > 1 ? 2 : 1);
     constexpr int NT = 128;                 // threads of a plane's wavefront pair
@@ -283,7 +331,9 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         }
     };
 
-    const int in_bytes = planes * HW * ES;
+    // (Odd: windows are dword-aligned loads, so the bound is rounded up to
+    // whole dwords)
+    const int in_bytes = Odd ? (planes * HW * ES + 3) & ~3 : planes * HW * ES;
     const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xl), 0, in_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(laml), 0, in_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t us = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(ul), 0, in_bytes, kBufFlags);
@@ -295,7 +345,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + static_cast<size_t>(k) * HW), 0,
                                                     w4_bytes - k * HW * ES, kBufFlags);
     }
-    const int par = ES == 2 ? ((K * q) & 1) : 0;
+    const int par = (ES == 2 && !Odd) ? ((K * q) & 1) : 0;
     const uint32_t win_b = static_cast<uint32_t>(K * q - par) * ES;
     const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
     const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
@@ -315,6 +365,14 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                                       static_cast<uint32_t>(K * q) * 4u
                                 : tap_b + win_b;
     const uint32_t t_line = static_cast<uint32_t>(L) * (Pre ? 4u : static_cast<uint32_t>(ES));
+    // Odd: one resource over all taps; planes 1 and 2 of a tap triple at
+    // scalar offsets (plane 1 flips the parity: 4 more bytes when the
+    // window starts odd, the other shift)
+    const __amdgpu_buffer_rsrc_t tall =
+        Odd ? __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4), 0, (w4_bytes + 3) & ~3, kBufFlags) : taps[0];
+    const int so1 = 2 * HW - 2, so2 = 4 * HW;
+    const int tap_e = ((dir0 + half) * (planes / cpg) + plane / cpg) * 3 * HW + K * q;   // element of line 0
+    const int pix_e = static_cast<int>(pix0) + K * q;
     // segments of a chunked scan; a segment's first line reads no line before it
     const int seg = Chunked ? (NL + k_chunk - 1) / k_chunk : NL;
     const uint32_t line_b = static_cast<uint32_t>(L) * ES;
@@ -411,6 +469,61 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         }
     };
 
+    // The same for Odd planes: pixel pairs (e, e+1) of the plane in pixel
+    // order, e even, (e+1) on the next row when e ends a row; the row pair's
+    // sums at plane stride HWa; m0, m1 and the outputs at any element, read
+    // and written as unaligned dwords, except a plane's odd last pixel (read
+    // as the high half of the dword before it, written alone).
+    auto column_pass_odd = [&](const float* part, const T* m0, const T* m1, T* out0, T* out1,
+                               auto two_tag) {
+        constexpr bool kTwo = decltype(two_tag)::value;
+        constexpr int U = 16;
+        const int W = NL, H = L, npairs = (HW + 1) / 2;
+        const float invW = 1.0f / static_cast<float>(W);
+        const f32x2_t* pp = reinterpret_cast<const f32x2_t*>(part + static_cast<size_t>(plane) * HWa);
+        auto load2 = [&](const T* m, int e, bool single) -> f32x2_t {
+            const uint32_t w = *reinterpret_cast<const u32_u*>(m + pix0 + e - (single ? 1 : 0));
+            const float hi = __uint_as_float(w & 0xffff0000u);
+            return f32x2_t{single ? hi : __uint_as_float(w << 16), hi};
+        };
+        for (int base = 0; base < npairs; base += NT * U) {
+            f32x2_t pv[U], a[U], b[U];
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                // clamped to the last pair: in bounds, the value is not used
+                const int e2 = min(base + NT * k + tid, npairs - 1);
+                const bool single = 2 * e2 + 1 == HW;
+                pv[k] = pp[e2];
+                a[k] = load2(m0, 2 * e2, single);
+                if constexpr (kTwo) b[k] = load2(m1, 2 * e2, single);
+            }
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const int e2 = base + NT * k + tid;
+                if (e2 < npairs) {
+                    const int e = 2 * e2;
+                    const bool single = e + 1 == HW;
+                    const int r = static_cast<int>((static_cast<float>(e) + 0.5f) * invW);
+                    const int c = e - r * W;
+                    const bool wrap = c + 1 == W;
+                    const uint32_t i0 = c * H + r;
+                    const uint32_t i1 = wrap ? static_cast<uint32_t>(r + 1) : i0 + H;
+                    const float v0 = pv[k].x + (get(lay.a + VW * i0, lay.la + i0) + get(lay.b + VW * i0, lay.lb + i0));
+                    const float v1 = pv[k].y + (get(lay.a + VW * i1, lay.la + i1) + get(lay.b + VW * i1, lay.lb + i1));
+                    const uint32_t o0 = pack_bf16x2(a[k].x * v0, a[k].y * v1);
+                    const uint32_t o1 = kTwo ? pack_bf16x2(b[k].x * v0, b[k].y * v1) : 0u;
+                    if (!single) {
+                        *reinterpret_cast<u32_u*>(out0 + pix0 + e) = o0;
+                        if constexpr (kTwo) *reinterpret_cast<u32_u*>(out1 + pix0 + e) = o1;
+                    } else {
+                        out0[pix0 + e] = static_cast<T>(o0 & 0xffffu);
+                        if constexpr (kTwo) out1[pix0 + e] = static_cast<T>(o1 & 0xffffu);
+                    }
+                }
+            }
+        }
+    };
+
     // ------------------------------------------------------------ forward
     {
         const uint32_t lo0 = fwd ? 0u : static_cast<uint32_t>(NL - 1) * line_b;
@@ -418,15 +531,34 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         const uint32_t dto = fwd ? t_line : 0u - t_line;
         uint32_t lo = t_base + (fwd ? 0u : static_cast<uint32_t>(NL - 1) * t_line);
         uint32_t xo = static_cast<uint32_t>(pix0) * ES + win_b + lo0;
+        const int i0f = fwd ? 0 : NL - 1;
+        const OddStream ot = odd_stream(tap_e + i0f * L, fwd ? L : -L);
+        const OddStream ox = odd_stream(pix_e + i0f * L, fwd ? L : -L);
+        if constexpr (Odd) {
+            lo = ot.off;
+            xo = ox.off;
+        }
         words_t<TW> tbuf[D][3];
-        words_t<NW> xbuf[D], lbuf[D];
+        words_t<NWL> xbuf[D], lbuf[D];
         auto load_line = [&](int d) {
+            if constexpr (Odd) {
+                const bool od = (d & 1) != 0;
+                const uint32_t sh = od ? ot.shE ^ 16u : ot.shE;   // 16 x the window start's parity
+                tbuf[d][0] = load_words_so<TW>(tall, lo, 0);
+                tbuf[d][1] = load_words_so<TW>(tall, lo + (sh >> 2), so1);
+                tbuf[d][2] = load_words_so<TW>(tall, lo, so2);
+                xbuf[d] = load_words<NWL>(xs, xo);
+                lbuf[d] = load_words<NWL>(ls, xo);
+                lo += od ? ot.incO : ot.incE;
+                xo += od ? ox.incO : ox.incE;
+            } else {
 #pragma unroll
-            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<TW>(trs[k], lo);
-            xbuf[d] = load_words<NW>(xs, xo);
-            lbuf[d] = load_words<NW>(ls, xo);
-            lo += dto;
-            xo += dlo;
+                for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<TW>(trs[k], lo);
+                xbuf[d] = load_words<NW>(xs, xo);
+                lbuf[d] = load_words<NW>(ls, xo);
+                lo += dto;
+                xo += dlo;
+            }
         };
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -457,10 +589,15 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             asm volatile("" : "+v"(xbuf[d]), "+v"(lbuf[d]));
             // Pre: s0..s2 are the normalised weights and r is 1
             float s0[K], s1[K], s2[K], t[K], r[K], b[K];
+            const bool od = (d & 1) != 0;
+            {
+                const uint32_t sh = od ? ox.shE ^ 16u : ox.shE;
+                const words_t<NW> xw = odd_window<Odd, NW, NWL>(xbuf[d], sh);
+                const words_t<NW> lw = odd_window<Odd, NW, NWL>(lbuf[d], sh);
 #pragma unroll
-            for (int j = 0; j < K; ++j)
-                b[j] = window_elem<T, K, NW>(lbuf[d], j, sx[j], sx[j]) *
-                       window_elem<T, K, NW>(xbuf[d], j, sx[j], sx[j]);
+                for (int j = 0; j < K; ++j)
+                    b[j] = window_elem<T, K, NW>(lw, j, sx[j], sx[j]) * window_elem<T, K, NW>(xw, j, sx[j], sx[j]);
+            }
             if constexpr (Pre) {
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
@@ -470,7 +607,11 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                     t[j] = r[j] = 1.0f;
                 }
             } else {
-                normalise(tbuf[d], s0, s1, s2, t, r);
+                const uint32_t sh = od ? ot.shE ^ 16u : ot.shE;
+                const words_t<NW> tw[3] = {odd_window<Odd, NW, TW>(tbuf[d][0], sh),
+                                           odd_window<Odd, NW, TW>(tbuf[d][1], sh ^ 16u),
+                                           odd_window<Odd, NW, TW>(tbuf[d][2], sh)};
+                normalise(tw, s0, s1, s2, t, r);
             }
 #pragma unroll
             for (int j = 0; j < K; ++j)
@@ -521,8 +662,10 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     // (line-major order is pixel order for the row pair; for the column pair
     // pixel (r, c) is position r of line c)
     if constexpr (!Cols) {
-        f32x4_t* sp = reinterpret_cast<f32x4_t*>(s_ws + pix0);
-        for (int e = tid; e < HW / 4; e += NT) sp[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
+        f32x4_t* sp = reinterpret_cast<f32x4_t*>(s_ws + static_cast<size_t>(plane) * HWa);
+        for (int e = tid; e < HWa / 4; e += NT) sp[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
+    } else if constexpr (Odd) {
+        column_pass_odd(s_ws, gy, gy, gu, gu, std::false_type{});
     } else {
         column_pass(s_ws, gy, gy, gu, gu, std::false_type{});
     }
@@ -537,15 +680,33 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         const uint32_t dto = fwd ? 0u - t_line : t_line;
         uint32_t lo = t_base + static_cast<uint32_t>(i0) * t_line;
         uint32_t uo = static_cast<uint32_t>(pix0) * ES + win_b + lo0;
+        const OddStream ot = odd_stream(tap_e + i0 * L, fwd ? -L : L);
+        const OddStream ou = odd_stream(pix_e + i0 * L, fwd ? -L : L);
+        if constexpr (Odd) {
+            lo = ot.off;
+            uo = ou.off;
+        }
         words_t<TW> tbuf[D][3];
-        words_t<NW> ubuf[D], gbuf[D];
+        words_t<NWL> ubuf[D], gbuf[D];
         auto load_line = [&](int d) {
+            if constexpr (Odd) {
+                const bool od = (d & 1) != 0;
+                const uint32_t sh = od ? ot.shE ^ 16u : ot.shE;
+                tbuf[d][0] = load_words_so<TW>(tall, lo, 0);
+                tbuf[d][1] = load_words_so<TW>(tall, lo + (sh >> 2), so1);
+                tbuf[d][2] = load_words_so<TW>(tall, lo, so2);
+                ubuf[d] = load_words<NWL>(us, uo);
+                gbuf[d] = load_words<NWL>(gs, uo);
+                lo += od ? ot.incO : ot.incE;
+                uo += od ? ou.incO : ou.incE;
+            } else {
 #pragma unroll
-            for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<TW>(trs[k], lo);
-            ubuf[d] = load_words<NW>(us, uo);
-            gbuf[d] = load_words<NW>(gs, uo);
-            lo += dto;
-            uo += dlo;
+                for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<TW>(trs[k], lo);
+                ubuf[d] = load_words<NW>(us, uo);
+                gbuf[d] = load_words<NW>(gs, uo);
+                lo += dto;
+                uo += dlo;
+            }
         };
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -568,6 +729,26 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
         // partial-sum planes (Pre) or per-channel planes, and this one's index
         const int out_planes = Pre ? planes / cc : planes;
         const int out_plane = Pre ? static_cast<int>(blockIdx.x) : plane;
+        // Odd: the three lines' 3 L elements, element f = lane + 64 t, one a
+        // lane per 2-byte store (lines start at any element)
+        constexpr int NR16 = Odd ? 3 * K : 1;
+        uint32_t rd16[NR16], go16[NR16], gd16[NR16];
+        if constexpr (Odd) {
+#pragma unroll
+            for (int t = 0; t < NR16; ++t) {
+                const int f = lane + 64 * t;
+                rd16[t] = lay.stage;
+                go16[t] = kDrop;
+                gd16[t] = 0;
+                if (f < 3 * L) {
+                    const int k = f / L, m = f - (f / L) * L;
+                    const int start = half == 0 ? NL - 1 : 0;
+                    rd16[t] = static_cast<uint32_t>(lay.stage + (3 * half + k) * SL * GS + 2 * m);
+                    go16[t] = static_cast<uint32_t>(((((dir0 + half) * planes + plane) * 3 + k) * HW + start * L + m) * 2);
+                    gd16[t] = half == 0 ? 0u - static_cast<uint32_t>(2 * L) : static_cast<uint32_t>(2 * L);
+                }
+            }
+        }
         uint32_t rd[NR], go[NR], gd[NR];
 #pragma unroll
         for (int t = 0; t < NR; ++t) {
@@ -619,10 +800,15 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             asm volatile("" : "+v"(ubuf[d]), "+v"(gbuf[d]));
             // Pre: s0..s2 are the normalised weights and r is 1
             float s0[K], s1[K], s2[K], t[K], r[K], ugy[K];
+            const bool od = (d & 1) != 0;
+            {
+                const uint32_t sh = od ? ou.shE ^ 16u : ou.shE;
+                const words_t<NW> uw = odd_window<Odd, NW, NWL>(ubuf[d], sh);
+                const words_t<NW> gw = odd_window<Odd, NW, NWL>(gbuf[d], sh);
 #pragma unroll
-            for (int j = 0; j < K; ++j)
-                ugy[j] = window_elem<T, K, NW>(ubuf[d], j, sx[j], sx[j]) *
-                         window_elem<T, K, NW>(gbuf[d], j, sx[j], sx[j]);
+                for (int j = 0; j < K; ++j)
+                    ugy[j] = window_elem<T, K, NW>(uw, j, sx[j], sx[j]) * window_elem<T, K, NW>(gw, j, sx[j], sx[j]);
+            }
             if constexpr (Pre) {
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
@@ -632,7 +818,11 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                     t[j] = r[j] = 1.0f;
                 }
             } else {
-                normalise(tbuf[d], s0, s1, s2, t, r);
+                const uint32_t sh = od ? ot.shE ^ 16u : ot.shE;
+                const words_t<NW> tw[3] = {odd_window<Odd, NW, TW>(tbuf[d][0], sh),
+                                           odd_window<Odd, NW, TW>(tbuf[d][1], sh ^ 16u),
+                                           odd_window<Odd, NW, TW>(tbuf[d][2], sh)};
+                normalise(tw, s0, s1, s2, t, r);
             }
 #pragma unroll
             for (int j = 0; j < K; ++j)
@@ -729,10 +919,18 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                 // read back as dwords: keep the compiler from moving the reads
                 // above the writes (the LDS then executes them in program order)
                 asm volatile("" ::: "memory");
+                if constexpr (Odd) {
 #pragma unroll
-                for (int t = 0; t < NR; ++t) {
-                    __builtin_amdgcn_raw_buffer_store_b32(lds_at<uint32_t>(rd[t]), gws, go[t], 0, 0);
-                    go[t] += gd[t];
+                    for (int t = 0; t < NR16; ++t) {
+                        __builtin_amdgcn_raw_buffer_store_b16(lds_at<uint16_t>(rd16[t]), gws, go16[t], 0, 0);
+                        go16[t] += gd16[t];
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < NR; ++t) {
+                        __builtin_amdgcn_raw_buffer_store_b32(lds_at<uint32_t>(rd[t]), gws, go[t], 0, 0);
+                        go[t] += gd[t];
+                    }
                 }
             }
 
@@ -760,8 +958,10 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
 
     // --------------------------------------------------------- G = g_a + g_b
     if constexpr (!Cols) {
-        f32x4_t* gp4 = reinterpret_cast<f32x4_t*>(g_ws + pix0);
-        for (int e = tid; e < HW / 4; e += NT) gp4[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
+        f32x4_t* gp4 = reinterpret_cast<f32x4_t*>(g_ws + static_cast<size_t>(plane) * HWa);
+        for (int e = tid; e < HWa / 4; e += NT) gp4[e] = get4(lay.a, lay.la, e) + get4(lay.b, lay.lb, e);
+    } else if constexpr (Odd) {
+        column_pass_odd(g_ws, lam, x, gx, glam, std::true_type{});
     } else {
         column_pass(g_ws, lam, x, gx, glam, std::true_type{});
     }
@@ -821,20 +1021,84 @@ transpose4_kernel(const T* __restrict__ a0, const T* __restrict__ a1, const T* _
     }
 }
 
+// x, lambda, u, gy of every bf16 plane transposed ([H][W] -> [W][H]) when
+// H W is odd, so that planes start at any element; one workgroup per
+// (plane, tensor).  The plane is read as the dwords from the even element at
+// or below its first, staged in LDS element by element, and written as the
+// dwords of the same span, a plane's first or last element alone when its
+// dword is shared with the next plane.
+__global__ void __launch_bounds__(256)
+transpose4_odd_kernel(const uint16_t* __restrict__ a0, const uint16_t* __restrict__ a1,
+                      const uint16_t* __restrict__ a2, const uint16_t* __restrict__ a3,
+                      uint16_t* __restrict__ t0, uint16_t* __restrict__ t1, uint16_t* __restrict__ t2,
+                      uint16_t* __restrict__ t3, int H, int W, int in_bytes) {
+    const int which = blockIdx.y;
+    const uint16_t* src = which == 0 ? a0 : which == 1 ? a1 : which == 2 ? a2 : a3;
+    uint16_t* dst = which == 0 ? t0 : which == 1 ? t1 : which == 2 ? t2 : t3;
+    const int HW = H * W;
+    const int base = static_cast<int>(blockIdx.x) * HW;
+    const int par = base & 1;
+    const int nw = (par + HW + 1) / 2;   // dwords of the span
+    // (a dword that straddles a buffer's end reads as 0: the bound is
+    // rounded up to whole dwords)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, (in_bytes + 3) & ~3, kBufFlags);
+    const uint32_t off0 = static_cast<uint32_t>(base - par) * 2u;
+    const int tid = static_cast<int>(threadIdx.x);
+    for (int q0 = 0; q0 < nw; q0 += 8 * 256) {
+        uint32_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = q0 + 256 * j + tid;
+            v[j] = t < nw ? __builtin_amdgcn_raw_buffer_load_b32(rs, off0 + 4u * t, 0, 0) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = q0 + 256 * j + tid;
+            const int g = 2 * t - par;
+            if (t < nw) {
+                if (g >= 0) lds_at<uint16_t>(2u * g) = static_cast<uint16_t>(v[j]);
+                if (g + 1 < HW) lds_at<uint16_t>(2u * (g + 1)) = static_cast<uint16_t>(v[j] >> 16);
+            }
+        }
+    }
+    __syncthreads();
+    // output element o = c H + r holds input element r W + c
+    const float invH = 1.0f / static_cast<float>(H);
+    auto in_of = [&](int o) -> uint32_t {
+        const int c = static_cast<int>((static_cast<float>(o) + 0.5f) * invH);
+        const int r = o - c * H;
+        return 2u * static_cast<uint32_t>(r * W + c);
+    };
+    uint16_t* d0 = dst + (base - par);
+    for (int t = tid; t < nw; t += 256) {
+        const int o0 = 2 * t - par, o1 = o0 + 1;
+        const uint32_t lo = o0 >= 0 ? lds_at<uint16_t>(in_of(o0)) : 0u;
+        const uint32_t hi = o1 < HW ? lds_at<uint16_t>(in_of(o1)) : 0u;
+        if (o0 >= 0 && o1 < HW)
+            *reinterpret_cast<uint32_t*>(d0 + 2 * t) = lo | (hi << 16);
+        else if (o0 >= 0)
+            d0[2 * t] = static_cast<uint16_t>(lo);
+        else
+            d0[2 * t + 1] = static_cast<uint16_t>(hi);
+    }
+}
+
 // Workspace regions (bytes, 256-aligned): x, lambda, u, gy transposed, then
-// S and G of the row pair in fp32.
+// S and G of the row pair in fp32 (a plane every H W rounded up to 4).
 struct PairBwdWs {
     int64_t xt, lt, ut, gt, s, g, bytes;
     PairBwdWs(int64_t planes, int64_t H, int64_t W, int64_t es) {
         auto a256 = [](int64_t v) { return (v + 255) & ~static_cast<int64_t>(255); };
         const int64_t n = planes * H * W;
+        const int64_t na = planes * ((H * W + 3) & ~static_cast<int64_t>(3));
         xt = 0;
         lt = a256(xt + n * es);
         ut = a256(lt + n * es);
         gt = a256(ut + n * es);
         s = a256(gt + n * es);
-        g = a256(s + n * 4);
-        bytes = a256(g + n * 4);
+        g = a256(s + na * 4);
+        bytes = a256(g + na * 4);
     }
 };
 
@@ -858,13 +1122,13 @@ struct PassArgs {
     int cc = 1;                     // Pre: planes a workgroup
 };
 
-template <typename T, typename GT, int K, bool Cols, bool Chunked, bool Pre, int CC>
+template <typename T, typename GT, int K, bool Cols, bool Chunked, bool Pre, int CC, bool Odd>
 hipError_t launch_pass_cc(const PassArgs<T, GT>& a, hipStream_t stream) {
     constexpr int D = 4;   // lines prefetched ahead (the steps are long; a deeper unroll outgrows the instruction cache)
     constexpr int cc = CC;
     const size_t lds = cc * static_cast<size_t>(PairBwdLayout(static_cast<int>(a.NL), static_cast<int>(a.L),
                                                               sizeof(T) == 2, sizeof(GT), cc > 1 ? 2 : 1).bytes);
-    auto kern = prop2d_backward_pair_kernel<T, GT, K, D, Cols, Chunked, Pre, CC>;
+    auto kern = prop2d_backward_pair_kernel<T, GT, K, D, Cols, Chunked, Pre, CC, Odd>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -878,13 +1142,13 @@ hipError_t launch_pass_cc(const PassArgs<T, GT>& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename T, typename GT, int K, bool Cols, bool Chunked, bool Pre>
+template <typename T, typename GT, int K, bool Cols, bool Chunked, bool Pre, bool Odd>
 hipError_t launch_pass(const PassArgs<T, GT>& a, hipStream_t stream) {
     if constexpr (Pre) {
-        if (a.cc == 4) return launch_pass_cc<T, GT, K, Cols, Chunked, true, 4>(a, stream);
-        if (a.cc == 2) return launch_pass_cc<T, GT, K, Cols, Chunked, true, 2>(a, stream);
+        if (a.cc == 4) return launch_pass_cc<T, GT, K, Cols, Chunked, true, 4, false>(a, stream);
+        if (a.cc == 2) return launch_pass_cc<T, GT, K, Cols, Chunked, true, 2, false>(a, stream);
     }
-    return launch_pass_cc<T, GT, K, Cols, Chunked, Pre, 1>(a, stream);
+    return launch_pass_cc<T, GT, K, Cols, Chunked, Pre, 1, Odd>(a, stream);
 }
 
 // K = ceil(L / 64) positions a lane.  A wavefront per direction needs no
@@ -892,19 +1156,23 @@ hipError_t launch_pass(const PassArgs<T, GT>& a, hipStream_t stream) {
 // wavefronts a SIMD hide more of each other's latency than the halves of
 // one wavefront (K = ceil(L / 32)) saved in idle slots: latent1k 0.480 ms
 // against 0.505, 148 x 148 (one plane per CU) 0.42 against 0.58.
-template <typename T, typename GT, bool Cols, bool Pre>
+template <typename T, typename GT, bool Cols, bool Pre, bool Odd>
 hipError_t launch_pass_k(const PassArgs<T, GT>& a, hipStream_t stream) {
     const bool ch = a.k_chunk > 1;
     if (a.L <= 64)
-        return ch ? launch_pass<T, GT, 1, Cols, true, Pre>(a, stream) : launch_pass<T, GT, 1, Cols, false, Pre>(a, stream);
+        return ch ? launch_pass<T, GT, 1, Cols, true, Pre, Odd>(a, stream)
+                  : launch_pass<T, GT, 1, Cols, false, Pre, Odd>(a, stream);
     if (a.L <= 128)
-        return ch ? launch_pass<T, GT, 2, Cols, true, Pre>(a, stream) : launch_pass<T, GT, 2, Cols, false, Pre>(a, stream);
-    return ch ? launch_pass<T, GT, 3, Cols, true, Pre>(a, stream) : launch_pass<T, GT, 3, Cols, false, Pre>(a, stream);
+        return ch ? launch_pass<T, GT, 2, Cols, true, Pre, Odd>(a, stream)
+                  : launch_pass<T, GT, 2, Cols, false, Pre, Odd>(a, stream);
+    return ch ? launch_pass<T, GT, 3, Cols, true, Pre, Odd>(a, stream)
+              : launch_pass<T, GT, 3, Cols, false, Pre, Odd>(a, stream);
 }
 
 // gwd_: per-channel tap gradients as GT, or (Pre) the fp32 partial sums of
 // the tap products, one plane per cc planes; wpre: the normalised weights.
-template <typename T, typename GT, bool Pre>
+// Odd: square bf16 planes of odd side (per-channel taps).
+template <typename T, typename GT, bool Pre, bool Odd = false>
 hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, const void* w4_,
                            const void* gy_, float eps, void* gx_, void* glam_, void* gu_, void* gwd_,
                            void* ws_, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
@@ -944,15 +1212,25 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
     a.gu = static_cast<T*>(gu_);
 
     // row pair on the inputs as they are: taps and gradients of directions 0, 1
-    hipError_t e = launch_pass_k<T, GT, false, Pre>(a, stream);
+    hipError_t e = launch_pass_k<T, GT, false, Pre, Odd>(a, stream);
     if (e != hipSuccess) return e;
     const size_t tlds = static_cast<size_t>(H * W) * sizeof(T);
-    if (tlds > 64 * 1024 &&
-        (e = hipFuncSetAttribute(reinterpret_cast<const void*>(transpose4_kernel<T>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(tlds))) != hipSuccess)
-        return e;
-    transpose4_kernel<T><<<dim3(static_cast<unsigned>(planes), 4), dim3(256), tlds, stream>>>(
-        a.x, a.lam, a.ul, a.gy, xt, lt, ut, gt, static_cast<int>(H), static_cast<int>(W));
+    if constexpr (Odd) {
+        if (tlds > 64 * 1024 &&
+            (e = hipFuncSetAttribute(reinterpret_cast<const void*>(transpose4_odd_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(tlds))) != hipSuccess)
+            return e;
+        transpose4_odd_kernel<<<dim3(static_cast<unsigned>(planes), 4), dim3(256), tlds, stream>>>(
+            a.x, a.lam, a.ul, a.gy, xt, lt, ut, gt, static_cast<int>(H), static_cast<int>(W),
+            static_cast<int>(planes * H * W * 2));
+    } else {
+        if (tlds > 64 * 1024 &&
+            (e = hipFuncSetAttribute(reinterpret_cast<const void*>(transpose4_kernel<T>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(tlds))) != hipSuccess)
+            return e;
+        transpose4_kernel<T><<<dim3(static_cast<unsigned>(planes), 4), dim3(256), tlds, stream>>>(
+            a.x, a.lam, a.ul, a.gy, xt, lt, ut, gt, static_cast<int>(H), static_cast<int>(W));
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // column pair on the transposed copies: directions 2, 3, then the outputs
     a.xl = xt;
@@ -962,7 +1240,7 @@ hipError_t backward_pair_t(const void* x_, const void* lam_, const void* u_, con
     a.NL = W;
     a.L = H;
     a.dir0 = 2;
-    return launch_pass_k<T, GT, true, Pre>(a, stream);
+    return launch_pass_k<T, GT, true, Pre, Odd>(a, stream);
 }
 
 // Normalised weights of every tap group, fp32, in the taps' layout
@@ -1063,7 +1341,9 @@ namespace {
 // for both the row and the column launch.
 bool pair_fits(int64_t planes, int64_t H, int64_t W, bool narrow) {
     const int64_t side = narrow ? 160 : 128;
-    if (H < 2 || W < 2 || H > side || W > side || (H & 1) || (W & 1)) return false;
+    if (H < 2 || W < 2 || H > side || W > side) return false;
+    // odd sides: square bf16 planes (the kernel's odd form)
+    if (((H & 1) || (W & 1)) && !(narrow && H == W && H >= 3)) return false;
     if (PairBwdLayout(static_cast<int>(H), static_cast<int>(W), narrow, 4).bytes > kLdsBytes ||
         PairBwdLayout(static_cast<int>(W), static_cast<int>(H), narrow, 4).bytes > kLdsBytes)
         return false;
@@ -1142,6 +1422,9 @@ hipError_t launch_prop2d_backward_pair(const void* x, const void* lam, const voi
     if (gw_fp32)
         return backward_pair_t<uint16_t, float, false>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes,
                                                        H, W, o, stream);
+    if (H & 1)
+        return backward_pair_t<uint16_t, uint16_t, false, true>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws,
+                                                                planes, H, W, o, stream);
     return backward_pair_t<uint16_t, uint16_t, false>(x, lam, u, w4, gy, eps, gx, glam, gu, gwd, ws, planes,
                                                       H, W, o, stream);
 }

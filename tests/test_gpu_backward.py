@@ -67,14 +67,18 @@ def test_backward_small_workloads(name):
 
 # Even sides take the one-wavefront-per-direction-pair kernel up to 160 in
 # bf16 and 128 in fp32 (its lines cover 1 to 5 positions per lane; the two
-# launches of a plane can differ); fp32 planes whose sums leave LDS (above
-# about 13K pixels) with sides up to 256, multiples of 4, the wide kernel
-# ((120, 120) and (148, 148) in fp32); the rest the general kernel.
+# launches of a plane can differ), and so do square bf16 planes of odd side
+# 3..159 (its odd form: 1, 2 or 3 positions a lane; planes start at even
+# and odd elements); other odd shapes that fit it padded run padded; fp32
+# planes whose sums leave LDS (above about 13K pixels) with sides up to 256,
+# multiples of 4, the wide kernel ((120, 120) and (148, 148) in fp32); the
+# rest the general kernel.
 BWD_SHAPES = [(1, 1), (1, 2), (2, 1), (3, 5), (5, 3), (1, 74), (74, 1), (63, 64), (74, 74),
               (127, 33), (13, 148), (120, 120), (148, 148), (300, 5), (5, 300),
               (2, 2), (2, 96), (96, 2), (32, 34), (34, 32), (64, 66), (96, 96), (30, 66), (8, 74),
               (98, 98), (128, 128), (130, 160), (160, 2), (2, 160), (158, 126), (96, 128), (162, 40),
-              (27, 27), (37, 37), (147, 147)]
+              (27, 27), (37, 37), (147, 147), (3, 3), (5, 5), (63, 63), (65, 65), (97, 97),
+              (127, 127), (129, 129), (159, 159)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -83,6 +87,25 @@ def test_backward_edge_shapes(H, W, dtype):
     say("backward edge", H, W, dtype)
     p = _problem(2, 3, H, W, 21 + H + 5 * W, dtype)
     _check(_run(p), _oracle(p), dtype, "%dx%d %s" % (H, W, dtype))
+
+
+@pytest.mark.parametrize("L,B,C", [(147, 4, 33), (65, 3, 67)])
+def test_backward_odd_many_planes(L, B, C):
+    # the odd form over more planes than the CUs hold at once, an odd count
+    # (planes at both element parities); the oracle recomputes sampled planes
+    say("backward odd planes", L, B, C)
+    p = _problem(B, C, L, L, 9 + L, "bf16")
+    got = _run(p)
+    for t in got:
+        assert bool(torch.isfinite(t).all())
+    w = p["w"].view(4, B, C, 3, -1)
+    gw = got[3].view(4, B, C, 3, -1)
+    for (b, c) in [(0, 0), (0, 1), (B - 1, C - 1), (1, C // 2), (B - 1, 0)]:
+        sl = lambda t: t[b:b + 1, c:c + 1]
+        ref = oracle.prop2d_backward(sl(p["x"]), sl(p["lam"]), sl(p["u"]), w[:, b:b + 1, c:c + 1],
+                                     sl(p["gy"]))
+        mine = (sl(got[0]), sl(got[1]), sl(got[2]), gw[:, b:b + 1, c:c + 1])
+        _check(mine, ref, "bf16", "%dx%d plane (%d,%d)" % (L, L, b, c))
 
 
 # fp32 only: the one-wavefront-per-plane kernel for planes whose sums leave
