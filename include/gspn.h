@@ -216,11 +216,13 @@ int64_t gspn_prop2d_4dir_ex_workspace(int dtype, int64_t B, int64_t C, int64_t g
  *               contents on return are unspecified.  Sizes are for fp32
  *               storage.  Planes with even H and W up to 160 need it for
  *               transposed copies of x, lam, u, gy and two fp32 partial sums
- *               per pixel-channel.  A plane with an odd side whose sides,
- *               padded to even, are at most 160 also holds padded copies of the
- *               inputs, outputs, taps and tap gradients there, and is run as
- *               the padded plane (the padding is exact: the added row and
- *               column start at 0 and no real position reads them).  Other
+ *               per pixel-channel, and so do bf16 planes with H = W odd, up to
+ *               159.  Another plane with an odd side whose sides, padded to
+ *               even, are at most 160 (fp32, or H != W) also holds padded
+ *               copies of the inputs, outputs, taps and tap gradients there,
+ *               and is run as the padded plane (the padding is exact: the
+ *               added row and column start at 0 and no real position reads
+ *               them); the size covers that for every odd side.  Other
  *               planes need three fp32 planes per (b, c) once those no longer
  *               fit in LDS (above about 115 x 115); below that the size is 0
  *               and NULL is allowed.
@@ -255,8 +257,9 @@ int64_t gspn_prop2d_4dir_backward_workspace(int64_t B, int64_t C, int64_t H, int
  *               of what gspn_prop2d_4dir_backward needs, channels that share
  *               taps (groups < C) keep fp32 tap gradients or partial sums of
  *               tap products there (48 bytes per pixel-channel) and their
- *               group's normalised taps (48 bytes per pixel-group).  A chunked
- *               scan whose k_chunk divides an odd side runs that plane
+ *               group's normalised taps (48 bytes per pixel-group).  Shared
+ *               taps with an odd side run padded as above, except a chunked
+ *               scan whose k_chunk divides an odd side, which runs that plane
  *               unpadded.
  * Other arguments, layouts, errors and determinism as
  * gspn_prop2d_4dir_backward, which is this call with groups = C, k_chunk = 1.
