@@ -86,11 +86,14 @@ EPS = {"deep": 1e-6, "eps": 1e-3}
 #   148 x 148, 40 x 30 bf16, few     phase kernel, two wavefronts a plane
 #   74 x 74, 9 x 11 fp32             two-wavefront fp32 kernel
 #   120 x 120, 256 x 252 fp32        wide fp32 kernel (y accumulates)
-#   27 x 27, 37 x 35 bf16            general kernel (odd sides)
+#   27 x 27, 37 x 35 bf16            phase kernel, odd sides
+#   74 x 74, 90 x 90 bf16, few       row and column scans in different wavefronts
+#   147 x 147, 99 x 99 bf16          the same, odd form (K = 3, 2)
 FWD_CASES = [(74, 74, "bf16", 8, 128), (30, 66, "bf16", 8, 128), (148, 148, "bf16", 1, 8),
              (40, 30, "bf16", 2, 4), (74, 74, "fp32", 1, 8), (9, 11, "fp32", 1, 4),
              (120, 120, "fp32", 1, 4), (256, 252, "fp32", 1, 4), (27, 27, "bf16", 2, 4),
-             (37, 35, "bf16", 1, 4), (74, 74, "bf16", 2, 4), (90, 90, "bf16", 1, 4)]
+             (37, 35, "bf16", 1, 4), (74, 74, "bf16", 2, 4), (90, 90, "bf16", 1, 4),
+             (147, 147, "bf16", 1, 5), (99, 99, "bf16", 1, 5)]
 
 
 def _sampled(B, C):
@@ -130,9 +133,11 @@ def test_forward_edge_logits_groups_chunks(G, k, mode):
 
 
 # backward: 74 x 74 (bf16 and fp32) the pair kernel, 148 x 152 fp32 the wide
-# kernel, 27 x 27 / 9 x 11 the general kernel
+# kernel, 27 x 27, 65 x 65 and 147 x 147 bf16 the pair kernel's odd form,
+# 9 x 11 fp32 the pair kernel on the padded plane
 BWD_CASES = [(74, 74, "bf16", 2, 4), (74, 74, "fp32", 1, 4), (148, 152, "fp32", 1, 4),
-             (27, 27, "bf16", 1, 4), (9, 11, "fp32", 1, 4)]
+             (27, 27, "bf16", 1, 4), (9, 11, "fp32", 1, 4), (65, 65, "bf16", 1, 5),
+             (147, 147, "bf16", 1, 5)]
 
 
 @pytest.mark.parametrize("mode", ["deep", "eps"])
@@ -191,7 +196,8 @@ def test_scan_dir_edge_logits_and_accumulate(dtype, mode):
 # taps) must leave plane p exactly as the oracle computes it.
 CONFINE_CASES = [(74, 74, "bf16", 8, 128), (30, 66, "bf16", 8, 128), (40, 30, "bf16", 1, 4),
                  (74, 74, "fp32", 1, 4), (120, 120, "fp32", 1, 4), (27, 27, "bf16", 1, 4),
-                 (74, 74, "bf16", 1, 4), (90, 90, "bf16", 1, 4)]
+                 (74, 74, "bf16", 1, 4), (90, 90, "bf16", 1, 4), (147, 147, "bf16", 1, 4),
+                 (99, 99, "bf16", 1, 4)]
 
 
 @pytest.mark.parametrize("H,W,dtype,B,C", CONFINE_CASES)
@@ -222,10 +228,12 @@ def test_nonfinite_values_stay_in_their_plane(H, W, dtype, B, C):
         assert_close(_np(sl2(y)), r2, RTOL[dtype], "plane (0,2) after a non-finite plane")
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_backward_nonfinite_values_stay_in_their_plane(dtype):
-    B, C, H, W = 1, 4, 74, 74
-    say("backward confinement", dtype)
+# (bf16 147 x 147 and 27 x 27: the pair kernel's odd form, whose windows and
+# transposes read dwords that a plane shares with its neighbours)
+@pytest.mark.parametrize("dtype,L", [("fp32", 74), ("bf16", 74), ("bf16", 147), ("bf16", 27)])
+def test_backward_nonfinite_values_stay_in_their_plane(dtype, L):
+    B, C, H, W = 1, 4, L, L
+    say("backward confinement", dtype, L)
     p = inputs.problem_torch(B, C, H, W, 43, dtype, DEV)
     gy = inputs.draw_torch(43, "gy", (B, C, H, W), dtype, DEV)
     x, lam, u = p["x"].clone(), p["lam"].clone(), p["u"].clone()
