@@ -167,6 +167,20 @@ __device__ __forceinline__ f32x2_t load_pair(const T* p, size_t e) {
     }
 }
 
+// A buffer resource whose fields the compiler is told are uniform.  Values
+// computed from the kernel's arguments can still be taken as varying across
+// the wavefront when the compiler places their computation inside a loop
+// with a per-lane trip count (the plane's zeroing loops); a resource held in
+// vector registers then costs a loop over the distinct values on every load.
+template <typename P>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const P* p, int num_records) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+    const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((hi << 32) | lo), 0,
+                                             __builtin_amdgcn_readfirstlane(num_records), kBufFlags);
+}
+
 // Odd line lengths (bf16): a window of K elements starting at element E is
 // loaded from the even element at or below E and shifted right by 16 bits
 // when E is odd.  Along a scan E moves by +-L, so with L odd its parity
@@ -334,16 +348,15 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     // (Odd: windows are dword-aligned loads, so the bound is rounded up to
     // whole dwords)
     const int in_bytes = Odd ? (planes * HW * ES + 3) & ~3 : planes * HW * ES;
-    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xl), 0, in_bytes, kBufFlags);
-    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(laml), 0, in_bytes, kBufFlags);
-    const __amdgpu_buffer_rsrc_t us = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(ul), 0, in_bytes, kBufFlags);
-    const __amdgpu_buffer_rsrc_t gs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(gyl), 0, in_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t xs = uniform_rsrc(xl, in_bytes);
+    const __amdgpu_buffer_rsrc_t ls = uniform_rsrc(laml, in_bytes);
+    const __amdgpu_buffer_rsrc_t us = uniform_rsrc(ul, in_bytes);
+    const __amdgpu_buffer_rsrc_t gs = uniform_rsrc(gyl, in_bytes);
     __amdgpu_buffer_rsrc_t taps[3];
-    const __amdgpu_buffer_rsrc_t gws = __builtin_amdgcn_make_buffer_rsrc(gwd, 0, gw_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t gws = uniform_rsrc(gwd, gw_bytes);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + static_cast<size_t>(k) * HW), 0,
-                                                    w4_bytes - k * HW * ES, kBufFlags);
+        taps[k] = uniform_rsrc(w4 + static_cast<size_t>(k) * HW, w4_bytes - k * HW * ES);
     }
     const int par = (ES == 2 && !Odd) ? ((K * q) & 1) : 0;
     const uint32_t win_b = static_cast<uint32_t>(K * q - par) * ES;
@@ -356,8 +369,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         if constexpr (Pre)
-            trs[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wpre + static_cast<size_t>(k) * HW), 0,
-                                                       wpre_bytes - k * HW * 4, kBufFlags);
+            trs[k] = uniform_rsrc(wpre + static_cast<size_t>(k) * HW, wpre_bytes - k * HW * 4);
         else
             trs[k] = taps[k];
     }
@@ -369,7 +381,7 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     // scalar offsets (plane 1 flips the parity: 4 more bytes when the
     // window starts odd, the other shift)
     const __amdgpu_buffer_rsrc_t tall =
-        Odd ? __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4), 0, (w4_bytes + 3) & ~3, kBufFlags) : taps[0];
+        Odd ? uniform_rsrc(w4, (w4_bytes + 3) & ~3) : taps[0];
     const int so1 = 2 * HW - 2, so2 = 4 * HW;
     const int tap_e = ((dir0 + half) * (planes / cpg) + plane / cpg) * 3 * HW + K * q;   // element of line 0
     const int pix_e = static_cast<int>(pix0) + K * q;
