@@ -10,7 +10,9 @@ steps do not hit the 256 MB Infinity Cache.  Prints one JSON line.
 value     : algorithmic GB/s = 16 values per pixel-channel (read x, lambda, u
             and 4 x 3 taps, write y) x bytes per value / wall time per step
 roofline  : the same bytes / average kernel duration (HIP events on the
-            launch stream), against the MI355X HBM peak of 8 TB/s; `traffic`
+            launch stream around the K back-to-back launches, divided by K;
+            the minimum from events around single launches), against the
+            MI355X HBM peak of 8 TB/s; `traffic`
             is the measured HBM bytes per launch from the committed rocprofv3
             counter summary when it was taken on the current kernel source
 cpu_baseline : the fp64 C oracle on the host, single thread, on a bounded
@@ -159,9 +161,32 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
     }
 
 
-def _timed(fn, steps, warmup, stream):
-    """Wall time of `steps` calls and their per-call HIP-event durations."""
+def _events(fn, steps, stream):
+    """Kernel time per call from HIP events on the launch stream: the average
+    is one event pair around `steps` back-to-back calls (each call is that
+    path's launches only), divided by `steps`; the minimum is over event pairs
+    around single calls, which also hold each pair's own overhead."""
     import numpy as np
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    avg = a.elapsed_time(b) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(avg), float(np.min([x.elapsed_time(y) for x, y in ev]))
+
+
+def _timed(fn, steps, warmup, stream):
+    """Wall time of `steps` calls and their HIP-event kernel times (_events)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -171,15 +196,8 @@ def _timed(fn, steps, warmup, stream):
         fn(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        fn(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    kern = [a.elapsed_time(b) for a, b in ev]
-    return wall, float(np.mean(kern)), float(np.min(kern))
+    kavg, kmin = _events(fn, steps, stream)
+    return wall, kavg, kmin
 
 
 def variant_leg(wl, args, dev, G, k):
@@ -289,7 +307,7 @@ def sublayer_leg(args, dev, G, B=32, C=1152, Cc=64, H=74, W=74):
 
 def backward_leg(wl, sets, args, dev):
     """Warmup + K backward launches over the rotated sets: wall time and
-    per-launch HIP-event durations on the launch stream."""
+    HIP-event kernel times on the launch stream (_events)."""
     import numpy as np
     import torch
 
@@ -325,15 +343,7 @@ def backward_leg(wl, sets, args, dev):
         bstep(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        bstep(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    kern = [a.elapsed_time(b) for a, b in ev]
-    kavg = float(np.mean(kern))
+    kavg, kmin = _events(bstep, args.steps, stream)
     nbytes = BWD_VALUES_PER_PIXEL * wl.elem_bytes * wl.pixels
     achieved = nbytes / (kavg * 1e-3) / 1e9
     del grads, ws
@@ -343,7 +353,7 @@ def backward_leg(wl, sets, args, dev):
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                          "kernel_ms_avg": round(kavg, 5),
-                         "kernel_ms_min": round(float(np.min(kern)), 5)}}
+                         "kernel_ms_min": round(kmin, 5)}}
 
 
 def shape_leg(args, dev, B, C, H, W, dtype, backward=False, rotate=True):
@@ -595,16 +605,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-launch kernel durations, HIP events on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kern_avg = float(np.mean(kern_ms))
+    # kernel time per launch, HIP events on the launch stream (a step is one
+    # launch of the four-direction kernel)
+    kern_avg, kern_min = _events(step, args.steps, stream)
 
     # calibration: a plain device copy of ~1 GB through the same HBM
     cal = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -649,7 +652,7 @@ def main():
                                         "scaled by a 1 GiB copy's reading; not counted in this run"
                                         if traffic is not None else None),
                      "kernel_ms_avg": round(kern_avg, 5),
-                     "kernel_ms_min": round(float(np.min(kern_ms)), 5)},
+                     "kernel_ms_min": round(kern_min, 5)},
         "calibration": {"torch_copy_GBps": round(copy_gbps, 1),
                         "frac_of_copy": round(achieved / copy_gbps, 4)},
     }
