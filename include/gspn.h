@@ -138,6 +138,10 @@ int gspn_scan_dir(const void* x, const void* lam, const void* u, const void* w,
  *   x, lam, u, y : [B][C][H][W];  w_raw4 : [4][B][C][3][..][..] logits.
  *   y must not overlap any input.  The result is bitwise reproducible
  *   from run to run.
+ *   bf16 planes whose fp32 direction sum does not fit on chip (H W above
+ *   40960 - 2 max(H, W) pixels, about 200 x 200) return GSPN_ERR_SHAPE here:
+ *   gspn_prop2d_4dir_ex_ws with groups = C takes them, keeping the sum in its
+ *   workspace (fp32 output is its own accumulator and has no such limit).
  */
 int gspn_prop2d_4dir(const void* x, const void* lam, const void* u,
                      const void* w_raw4, float eps, void* y, int dtype,
@@ -179,7 +183,11 @@ int gspn_prop2d_4dir_ex(const void* x, const void* lam, const void* u,
  *   workspace : at least gspn_prop2d_4dir_ex_workspace(...) bytes, 16-byte
  *               aligned, not overlapping any argument; contents on return
  *               unspecified.  When that size is 0 the workspace is not used
- *               (may be NULL) and the call is gspn_prop2d_4dir_ex.
+ *               (may be NULL) and the call is gspn_prop2d_4dir_ex.  bf16
+ *               planes too large for gspn_prop2d_4dir_ex (see
+ *               gspn_prop2d_4dir) keep their fp32 direction sum here, 4 bytes
+ *               per pixel-channel (any groups and k_chunk), and are accepted
+ *               only by this call.
  * Other arguments, layouts and errors as gspn_prop2d_4dir_ex, plus
  * GSPN_ERR_SHAPE for a workspace smaller than needed.
  */
@@ -190,8 +198,9 @@ int gspn_prop2d_4dir_ex_ws(const void* x, const void* lam, const void* u, const 
 
 /* Workspace bytes gspn_prop2d_4dir_ex_ws uses for these sizes: 0 where it
  * runs as gspn_prop2d_4dir_ex (today: all but bf16 square planes with even
- * sides up to 80, one segment a scan and at least 2 channels a group), or -1
- * if the sizes are not accepted. */
+ * sides up to 80, one segment a scan and at least 2 channels a group, and
+ * bf16 planes whose direction sum does not fit on chip), or -1 if the sizes
+ * are not accepted. */
 int64_t gspn_prop2d_4dir_ex_workspace(int dtype, int64_t B, int64_t C, int64_t groups, int64_t H,
                                       int64_t W);
 

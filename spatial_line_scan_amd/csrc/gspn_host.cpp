@@ -48,6 +48,9 @@ int launch_status(hipError_t e) { return e == hipSuccess ? GSPN_OK : GSPN_ERR_HI
 // Workspace the grouped forward uses to normalise each group's taps once
 // (0: the taps are normalised by every channel as it scans).
 int64_t shared_workspace(int dtype, int64_t B, int64_t C, int64_t groups, int64_t H, int64_t W) {
+    // bf16 planes whose direction sum leaves LDS: an fp32 accumulator plane
+    // per (b, c)
+    if (int64_t acc = gspn::prop2d_global_acc_bytes(dtype, B * C, H, W)) return acc;
     gspn::PropOpts o;
     o.cpg = C / groups;
     // the eligibility test reads only alignment from these
@@ -62,7 +65,9 @@ int ex_forward(const void* x, const void* lam, const void* u, const void* w_raw4
                bool with_ws, int dtype, int64_t B, int64_t C, int64_t H, int64_t W, void* stream) {
     if (!valid_dtype(dtype)) return GSPN_ERR_DTYPE;
     if (int s = check_dims(B, C, H, W, 12)) return s;
-    if (H * W > gspn::prop2d_max_plane(dtype, H, W)) return GSPN_ERR_SHAPE;
+    // bf16 planes above the LDS direction sum need the workspace's accumulator
+    const bool global_acc = H * W > gspn::prop2d_max_plane(dtype, H, W);
+    if (global_acc && !with_ws) return GSPN_ERR_SHAPE;
     if (groups < 1 || groups > C || C % groups != 0) return GSPN_ERR_SHAPE;
     if (k_chunk < 1) return GSPN_ERR_VALUE;
     if (!valid_eps(eps)) return GSPN_ERR_VALUE;
@@ -88,6 +93,10 @@ int ex_forward(const void* x, const void* lam, const void* u, const void* w_raw4
             overlap(workspace, need, u, n) || overlap(workspace, need, w_raw4, taps) ||
             overlap(workspace, need, y, n))
             return GSPN_ERR_ALIAS;
+        if (global_acc)
+            return launch_status(gspn::launch_prop2d_global_acc(x, lam, u, w_raw4, eps, y, B * C, H, W, opts,
+                                                                static_cast<float*>(workspace),
+                                                                static_cast<hipStream_t>(stream)));
         // buffers the fast kernels cannot address (2-byte aligned) take the
         // path that normalises per channel
         if (gspn::prop2d_quad_shared_eligible(dtype, B * C, H, W, opts, x, lam, u, w_raw4, y))
@@ -242,7 +251,6 @@ int gspn_prop2d_4dir_ex_ws(const void* x, const void* lam, const void* u, const 
 int64_t gspn_prop2d_4dir_ex_workspace(int dtype, int64_t B, int64_t C, int64_t groups, int64_t H,
                                       int64_t W) {
     if (!valid_dtype(dtype) || check_dims(B, C, H, W, 12) != GSPN_OK) return -1;
-    if (H * W > gspn::prop2d_max_plane(dtype, H, W)) return -1;
     if (groups < 1 || groups > C || C % groups != 0) return -1;
     return shared_workspace(dtype, B, C, groups, H, W);
 }

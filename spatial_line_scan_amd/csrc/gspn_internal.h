@@ -174,4 +174,12 @@ hipError_t noalloc_scratch(void** out);
 // Largest plane (H * W pixels) gspn_prop2d_4dir accepts for an element type.
 int64_t prop2d_max_plane(int dtype, int64_t H, int64_t W);
 
+// bf16 planes above that size: the bytes of an fp32 accumulator plane per
+// (b, c) (0 for planes that need none), and the four-direction forward that
+// keeps the direction sum there.
+int64_t prop2d_global_acc_bytes(int dtype, int64_t planes, int64_t H, int64_t W);
+hipError_t launch_prop2d_global_acc(const void* x, const void* lam, const void* u, const void* w4,
+                                    float eps, void* y, int64_t planes, int64_t H, int64_t W,
+                                    const PropOpts& o, float* acc, hipStream_t stream);
+
 }  // namespace gspn

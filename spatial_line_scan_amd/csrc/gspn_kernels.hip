@@ -116,12 +116,14 @@ scan_dir_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __r
 }
 
 // Four directions of one plane per workgroup.  The sum of the directional
-// states is kept in `acc`: LDS when it fits, otherwise the fp32 output itself.
+// states is kept in `acc`: LDS when it fits, otherwise the fp32 output itself
+// or, for bf16 output, the fp32 plane of `accg` (a workspace of one float per
+// pixel-channel).
 template <typename T, bool kAccInLds>
 __global__ void __launch_bounds__(kThreads)
 prop2d_plane_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __restrict__ u,
                     const T* __restrict__ w4, float eps, T* __restrict__ y, int64_t planes, int H,
-                    int W, int64_t cpg, int k_chunk) {
+                    int W, int64_t cpg, int k_chunk, float* __restrict__ accg) {
     extern __shared__ float lds[];
     const int Lmax = H > W ? H : W;
     const size_t npix = static_cast<size_t>(H) * W;
@@ -129,9 +131,10 @@ prop2d_plane_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T*
     float* acc;
     if constexpr (kAccInLds) {
         acc = lds + 2 * Lmax;
-    } else {
-        static_assert(sizeof(T) == sizeof(float), "global accumulation needs fp32 output");
+    } else if constexpr (sizeof(T) == sizeof(float)) {
         acc = reinterpret_cast<float*>(y + plane * npix);
+    } else {
+        acc = accg + plane * npix;
     }
     // tap plane of this plane: its channel group's
     const size_t tap_planes = static_cast<size_t>(planes / cpg);
@@ -208,7 +211,7 @@ hipError_t prop2d_t(const void* x, const void* lam, const void* u, const void* w
         prop2d_plane_kernel<T, true><<<grid, dim3(kThreads), lds_acc, stream>>>(
             static_cast<const T*>(x), static_cast<const T*>(lam), static_cast<const T*>(u),
             static_cast<const T*>(w4), eps, static_cast<T*>(y), planes, static_cast<int>(H),
-            static_cast<int>(W), o.cpg, static_cast<int>(o.k_chunk));
+            static_cast<int>(W), o.cpg, static_cast<int>(o.k_chunk), nullptr);
     } else {
         if constexpr (sizeof(T) != sizeof(float)) {
             return hipErrorInvalidValue;  // rejected earlier by prop2d_max_plane
@@ -219,7 +222,7 @@ hipError_t prop2d_t(const void* x, const void* lam, const void* u, const void* w
             prop2d_plane_kernel<T, false><<<grid, dim3(kThreads), lds, stream>>>(
                 static_cast<const T*>(x), static_cast<const T*>(lam), static_cast<const T*>(u),
                 static_cast<const T*>(w4), eps, static_cast<T*>(y), planes,
-                static_cast<int>(H), static_cast<int>(W), o.cpg, static_cast<int>(o.k_chunk));
+                static_cast<int>(H), static_cast<int>(W), o.cpg, static_cast<int>(o.k_chunk), nullptr);
         }
     }
     return hipGetLastError();
@@ -273,6 +276,24 @@ hipError_t launch_prop2d(const void* x, const void* lam, const void* u, const vo
 int64_t prop2d_max_plane(int dtype, int64_t H, int64_t W) {
     if (dtype == 0) return INT64_MAX;  // fp32 output doubles as the accumulator
     return kLdsBytes / static_cast<int64_t>(sizeof(float)) - 2 * std::max(H, W);
+}
+
+int64_t prop2d_global_acc_bytes(int dtype, int64_t planes, int64_t H, int64_t W) {
+    if (dtype != 1 || H * W <= prop2d_max_plane(dtype, H, W)) return 0;
+    return (planes * H * W * static_cast<int64_t>(sizeof(float)) + 255) & ~static_cast<int64_t>(255);
+}
+
+hipError_t launch_prop2d_global_acc(const void* x, const void* lam, const void* u, const void* w4,
+                                    float eps, void* y, int64_t planes, int64_t H, int64_t W,
+                                    const PropOpts& o, float* acc, hipStream_t stream) {
+    const size_t lds = 2 * std::max(H, W) * sizeof(float);
+    hipError_t e = allow_lds(prop2d_plane_kernel<uint16_t, false>, lds);
+    if (e != hipSuccess) return e;
+    prop2d_plane_kernel<uint16_t, false><<<dim3(static_cast<unsigned>(planes)), dim3(kThreads), lds, stream>>>(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(lam), static_cast<const uint16_t*>(u),
+        static_cast<const uint16_t*>(w4), eps, static_cast<uint16_t*>(y), planes, static_cast<int>(H),
+        static_cast<int>(W), o.cpg, static_cast<int>(o.k_chunk), acc);
+    return hipGetLastError();
 }
 
 }  // namespace gspn

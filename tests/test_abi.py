@@ -101,7 +101,24 @@ def test_element_count_limit_counts_all_taps(L):
 
 
 def test_bf16_plane_limit(L):
-    assert prop(L, dt=1, B=1, C=1, H=256, W=256) == SHAPE   # accumulator does not fit on chip
+    # the plain call has no room for a bf16 plane whose fp32 direction sum
+    # leaves LDS (above 160 KiB / 4 - 2 max(H, W) pixels); the workspace call
+    # takes it with an fp32 accumulator plane per (b, c)
+    assert prop(L, dt=1, B=1, C=1, H=256, W=256) == SHAPE
+    assert L.gspn_prop2d_4dir_ex_workspace(1, 1, 2, 2, 200, 200) == 0       # fits: 40000 <= 40560
+    need = L.gspn_prop2d_4dir_ex_workspace(1, 1, 2, 2, 202, 202)           # 40804 > 40556
+    assert need == (2 * 202 * 202 * 4 + 255) // 256 * 256
+    big = L.gspn_prop2d_4dir_ex_workspace(1, 3, 4, 2, 256, 256)             # any grouping
+    assert big == 12 * 256 * 256 * 4
+    assert L.gspn_prop2d_4dir_ex_workspace(0, 1, 2, 2, 256, 256) == 0       # fp32: y accumulates
+
+    def exw(ws=P(6), nb=big, dt=1):
+        return L.gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 2, 1, 1e-6, P(5), ws, nb, dt, 3, 4,
+                                        256, 256, None)
+    assert exw(nb=big - 1) == SHAPE
+    assert exw(ws=None) == NULL
+    assert exw(ws=ctypes.c_void_p(A + 6 * STEP + 8)) == ALIGN
+    assert exw(ws=P(5)) == ALIAS
 
 
 @pytest.mark.parametrize("eps", [0.0, -1e-6, float("nan"), float("inf")])

@@ -61,6 +61,25 @@ def test_ex_groups_and_chunks(H, W, G, k, dtype):
     _run_check(p, G, k, dtype, "%dx%d G=%d k=%d %s" % (H, W, G, k, dtype))
 
 
+# bf16 planes whose fp32 direction sum does not fit in LDS (above about
+# 40,500 pixels) run with an fp32 accumulator plane per (b, c) in the
+# workspace (gspn_prop2d_4dir_ex_ws; the binding allocates it); the plain
+# call refuses them
+@pytest.mark.parametrize("H,W", [(202, 202), (256, 256), (203, 201), (256, 170)])
+@pytest.mark.parametrize("G,k", [(3, 1), (1, 4)])
+def test_ex_bf16_planes_beyond_lds(H, W, G, k):
+    say("ex bf16 beyond LDS", H, W, G, k)
+    p = _problem(1, 3, H, W, G, 17 + H + W + k, "bf16")
+    assert gspn.prop2d_4dir_ex_workspace_bytes(torch.bfloat16, 1, 3, G, H, W) == 3 * H * W * 4 + (-(3 * H * W * 4)) % 256
+    y = _run_check(p, G, k, "bf16", "%dx%d bf16 G=%d k=%d" % (H, W, G, k))
+    y2 = gspn.prop2d_4dir_ex(p["x"], p["lam"], p["u"], p["w"], G, k)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    if G == 3 and k == 1:
+        with pytest.raises(Exception):
+            gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
+
+
 @pytest.mark.parametrize("H,W", [(7, 9), (10, 4), (75, 73)])
 @pytest.mark.parametrize("k", [2, 3, 4, 7])
 def test_ex_ragged_segments(H, W, k):
