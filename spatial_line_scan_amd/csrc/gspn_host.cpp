@@ -93,10 +93,15 @@ int ex_forward(const void* x, const void* lam, const void* u, const void* w_raw4
             overlap(workspace, need, u, n) || overlap(workspace, need, w_raw4, taps) ||
             overlap(workspace, need, y, n))
             return GSPN_ERR_ALIAS;
-        if (global_acc)
+        if (global_acc) {
+            float* acc = static_cast<float*>(workspace);
+            const hipStream_t st = static_cast<hipStream_t>(stream);
+            if (gspn::prop2d_wide_bf16_eligible(B * C, H, W, x, lam, u, w_raw4, y, acc))
+                return launch_status(gspn::launch_prop2d_wide_bf16(x, lam, u, w_raw4, eps, y, B * C, H, W, opts,
+                                                                   acc, st));
             return launch_status(gspn::launch_prop2d_global_acc(x, lam, u, w_raw4, eps, y, B * C, H, W, opts,
-                                                                static_cast<float*>(workspace),
-                                                                static_cast<hipStream_t>(stream)));
+                                                                acc, st));
+        }
         // buffers the fast kernels cannot address (2-byte aligned) take the
         // path that normalises per channel
         if (gspn::prop2d_quad_shared_eligible(dtype, B * C, H, W, opts, x, lam, u, w_raw4, y))

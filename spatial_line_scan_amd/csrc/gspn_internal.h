@@ -51,13 +51,21 @@ hipError_t launch_prop2d_pair(const void* x, const void* lam, const void* u, con
                               float eps, void* y, int dtype, int64_t planes, int64_t H, int64_t W,
                               const PropOpts& opts, hipStream_t stream);
 
-// Large fp32 planes (sides up to 256, multiples of 4): one launch per
-// direction with y as the accumulator (gspn_prop2d_wide.hip).
+// Large fp32 planes (sides up to 256, multiples of 4): one launch, one
+// wavefront a plane, a pass per direction with y as the accumulator
+// (gspn_prop2d_wide.hip).
 bool prop2d_wide_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
                           const void* lam, const void* u, const void* w4, const void* y);
 hipError_t launch_prop2d_wide(const void* x, const void* lam, const void* u, const void* w4,
                               float eps, void* y, int64_t planes, int64_t H, int64_t W,
                               const PropOpts& opts, hipStream_t stream);
+// The same for bf16 planes with sides 196..256 (multiples of 4), the
+// direction sum in acc (fp32, one plane per (b, c)).
+bool prop2d_wide_bf16_eligible(int64_t planes, int64_t H, int64_t W, const void* x, const void* lam,
+                               const void* u, const void* w4, const void* y, const void* acc);
+hipError_t launch_prop2d_wide_bf16(const void* x, const void* lam, const void* u, const void* w4,
+                                   float eps, void* y, int64_t planes, int64_t H, int64_t W,
+                                   const PropOpts& opts, float* acc, hipStream_t stream);
 
 // Fast path for bf16 planes: one wavefront per plane, rows then columns,
 // lambda x and the direction sum on chip (gspn_prop2d_phase.hip).

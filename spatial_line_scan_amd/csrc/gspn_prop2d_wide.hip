@@ -1,21 +1,23 @@
-// Four-direction propagation of large fp32 planes (sides up to 256, a
-// multiple of 4), gfx950.
+// Four-direction propagation of large planes (sides up to 256, a multiple
+// of 4): fp32, and bf16 planes whose direction sum does not fit on chip
+// (sides 196..256, four positions a lane), gfx950.
 //
 // Operator: "Scaling Parallel Sequence Models to Foundation-Scale Vision
 // Encoders", §3 line-scan recurrence, §4.1 all steps of a scan in one launch,
 // §5.1 fused normalisation (sigmoid, local sum, clamp, divide); reading
 // notes, method / overall framework.
 //
-// A plane's direction sum does not fit in LDS, so the fp32 output y is the
-// accumulator.  One launch, one wavefront per (b, c) plane, which runs four
+// A plane's direction sum does not fit in LDS, so it is kept in global
+// memory: in the fp32 output y itself, or for bf16 in an fp32 plane of the
+// caller's workspace (acc), from which the last pass writes y.  One launch, one wavefront per (b, c) plane, which runs four
 // passes over its plane in turn (ordered by workgroup-scope fences: a pass
 // reads y that other lanes wrote in the previous one); lane l holds
 // positions K l .. K l + K - 1 of the current line (K = ceil(L / 64)), and
 // the neighbour exchange is one wave-wide DPP shift each way:
-//   TD  y = h_TD            rows top-down
-//   BU  y = y + h_BU        rows bottom-up
-//   LR  y = y + h_LR        columns left-right
-//   RL  y = u (y + h_RL)    columns right-left
+//   TD  acc = h_TD                rows top-down
+//   BU  acc = acc + h_BU          rows bottom-up
+//   LR  acc = acc + h_LR          columns left-right
+//   RL  y = u (acc + h_RL)        columns right-left
 // so the four terms of a pixel are summed in the fixed order TD, BU, LR, RL.
 // Every direction's taps are line-major, so a tap window is contiguous in
 // both kinds of pass, and taps are prefetched D lines ahead.
@@ -68,14 +70,31 @@ __device__ __forceinline__ void pass_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Element j of a window of K consecutive values (fp32 words, or bf16 pairs
+// from an even element) as fp32.
+template <typename T, int KW>
+__device__ __forceinline__ float wide_elem(const words_t<KW>& w, int j) {
+    if constexpr (sizeof(T) == 4) {
+        return __uint_as_float(word<KW>(w, j));
+    } else {
+        const uint32_t v = word<KW>(w, j >> 1);
+        return __uint_as_float((j & 1) ? (v & 0xffff0000u) : (v << 16));
+    }
+}
+
 // One direction's pass over plane blockIdx.x; strip is the column passes' LDS.
-template <int K, int D, int Dir, bool Chunked>
-__device__ __forceinline__ void wide_pass(const float* __restrict__ x, const float* __restrict__ lam,
-                                          const float* __restrict__ u, const float* __restrict__ w4,
-                                          float eps, float* __restrict__ y, int planes, int H, int W,
-                                          int cpg, int k_chunk, float* strip) {
+// T: storage type of x, lambda, u, the taps and y; acc: the fp32 direction
+// sum (y itself for fp32).
+template <typename T, int K, int D, int Dir, bool Chunked>
+__device__ __forceinline__ void wide_pass(const T* __restrict__ x, const T* __restrict__ lam,
+                                          const T* __restrict__ u, const T* __restrict__ w4,
+                                          float eps, float* __restrict__ y, T* __restrict__ yout,
+                                          int planes, int H, int W, int cpg, int k_chunk, float* strip) {
     constexpr bool kRows = Dir < 2;
     constexpr bool kFwd = Dir == 0 || Dir == 2;
+    constexpr int ES = sizeof(T);
+    static_assert(ES == 4 || K % 2 == 0, "bf16 windows of whole dwords");
+    constexpr int KW = ES == 4 ? K : K / 2;   // dwords of a lane's window
     static_assert(kSW % D == 0 && 4 % D == 0, "strip steps stay aligned to the prefetch ring");
     const int HW = H * W;
     const int NL = kRows ? H : W;
@@ -85,16 +104,17 @@ __device__ __forceinline__ void wide_pass(const float* __restrict__ x, const flo
     const size_t pix0 = static_cast<size_t>(plane) * HW;
     // one buffer resource per plane (offsets within a plane; loads past its
     // end return 0), so the tensors themselves may exceed 2 GiB
-    const int plane_bytes = HW * 4;
-    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(x + pix0), 0, plane_bytes, kBufFlags);
-    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lam + pix0), 0, plane_bytes, kBufFlags);
-    const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(y + pix0, 0, plane_bytes, kBufFlags);
+    const int plane_bytes = HW * ES;
+    const int acc_bytes = HW * 4;
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(x + pix0), 0, plane_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(lam + pix0), 0, plane_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(y + pix0, 0, acc_bytes, kBufFlags);
     __amdgpu_buffer_rsrc_t taps[3];
     const int tap_planes = planes / cpg;
     const size_t tap0 = (static_cast<size_t>(Dir) * tap_planes + plane / cpg) * 3 * HW;
 #pragma unroll
     for (int k = 0; k < 3; ++k)
-        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w4 + tap0 + static_cast<size_t>(k) * HW), 0,
+        taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(w4 + tap0 + static_cast<size_t>(k) * HW), 0,
                                                     plane_bytes, kBufFlags);
 
     float c0[K], c1[K], c2[K];
@@ -113,20 +133,23 @@ __device__ __forceinline__ void wide_pass(const float* __restrict__ x, const flo
     auto restarts = [&](int i) {
         return kFwd ? i % seg == 0 : (i == NL - 1 || (i + 1) % seg == 0);
     };
-    const uint32_t win = static_cast<uint32_t>(K * lane) * 4;   // byte offset of the lane's window
+    // byte offsets of the lane's window: storage type, and the fp32 sum
+    const uint32_t win = static_cast<uint32_t>(K * lane) * ES;
+    const uint32_t wina = static_cast<uint32_t>(K * lane) * 4;
 
     // ---- prefetch ring: taps (and for rows x, lambda, y) of line line_of(s)
-    words_t<K> tbuf[D][3], xbuf[kRows ? D : 1], lbuf[kRows ? D : 1], ybuf[kRows ? D : 1];
+    words_t<KW> tbuf[D][3], xbuf[kRows ? D : 1], lbuf[kRows ? D : 1];
+    words_t<K> ybuf[kRows ? D : 1];
     auto load_line = [&](int s, int d) {
         const int i = line_of(s < NL ? s : NL - 1);
-        const uint32_t lo = static_cast<uint32_t>(i * L) * 4 + win;
+        const uint32_t lo = static_cast<uint32_t>(i * L) * ES + win;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<K>(taps[k], lo);
+        for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<KW>(taps[k], lo);
         if constexpr (kRows) {
-            const uint32_t xo = static_cast<uint32_t>(i * W) * 4 + win;
-            xbuf[d] = load_words<K>(xs, xo);
-            lbuf[d] = load_words<K>(ls, xo);
-            if constexpr (Dir == 1) ybuf[d] = load_words<K>(ys, xo);
+            const uint32_t xo = static_cast<uint32_t>(i * W) * ES + win;
+            xbuf[d] = load_words<KW>(xs, xo);
+            lbuf[d] = load_words<KW>(ls, xo);
+            if constexpr (Dir == 1) ybuf[d] = load_words<K>(ys, static_cast<uint32_t>(i * W) * 4 + wina);
         }
     };
 #pragma unroll
@@ -142,9 +165,9 @@ __device__ __forceinline__ void wide_pass(const float* __restrict__ x, const flo
         float s0[K], s1[K], s2[K], r[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            s0[j] = __builtin_amdgcn_exp2f(__uint_as_float(word<K>(tbuf[d][0], j)) * kNegLog2e);
-            s1[j] = __builtin_amdgcn_exp2f(__uint_as_float(word<K>(tbuf[d][1], j)) * kNegLog2e);
-            s2[j] = __builtin_amdgcn_exp2f(__uint_as_float(word<K>(tbuf[d][2], j)) * kNegLog2e);
+            s0[j] = __builtin_amdgcn_exp2f(wide_elem<T, KW>(tbuf[d][0], j) * kNegLog2e);
+            s1[j] = __builtin_amdgcn_exp2f(wide_elem<T, KW>(tbuf[d][1], j) * kNegLog2e);
+            s2[j] = __builtin_amdgcn_exp2f(wide_elem<T, KW>(tbuf[d][2], j) * kNegLog2e);
         }
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -180,7 +203,7 @@ __device__ __forceinline__ void wide_pass(const float* __restrict__ x, const flo
                     float b[K], hn[K];
 #pragma unroll
                     for (int j = 0; j < K; ++j)
-                        b[j] = __uint_as_float(word<K>(lbuf[d], j)) * __uint_as_float(word<K>(xbuf[d], j));
+                        b[j] = wide_elem<T, KW>(lbuf[d], j) * wide_elem<T, KW>(xbuf[d], j);
                     float yv[K];
                     if constexpr (Dir == 1) {
 #pragma unroll
@@ -200,13 +223,22 @@ __device__ __forceinline__ void wide_pass(const float* __restrict__ x, const flo
         // strips of kSW columns: LR takes them left to right, RL right to left
         const int pitch = strip_pitch(H);
         float* bs = strip;                          // [column][row]: b = lambda x, then h
-        const int T = (W + kSW - 1) / kSW;
+        const int nstrips = (W + kSW - 1) / kSW;
         const int units = H * kCQ;                  // (row, 4-column chunk) pairs of a strip
         const __amdgpu_buffer_rsrc_t us =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(u + pix0), 0, plane_bytes, kBufFlags);
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(u + pix0), 0, plane_bytes, kBufFlags);
+        // four consecutive values of a storage-type plane at element e
+        auto load4 = [&](__amdgpu_buffer_rsrc_t r, int e) -> f32x4_t {
+            if constexpr (ES == 4) {
+                return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<uint32_t>(e) * 4, 0, 0));
+            } else {
+                const words_t<2> v = load_words<2>(r, static_cast<uint32_t>(e) * 2);
+                return f32x4_t{wide_elem<T, 2>(v, 0), wide_elem<T, 2>(v, 1), wide_elem<T, 2>(v, 2), wide_elem<T, 2>(v, 3)};
+            }
+        };
         int s = 0;                                  // scan step
-        for (int tt = 0; tt < T; ++tt) {
-            const int t = kFwd ? tt : T - 1 - tt;
+        for (int tt = 0; tt < nstrips; ++tt) {
+            const int t = kFwd ? tt : nstrips - 1 - tt;
             const int cb = t * kSW;                 // first column of the strip
             const int width = W - cb < kSW ? W - cb : kSW;   // a multiple of 4
             // b of the strip: unit f = row f / kCQ, columns cb + 4 (f % kCQ) ..
@@ -218,9 +250,8 @@ __device__ __forceinline__ void wide_pass(const float* __restrict__ x, const flo
                     const int row = f / kCQ, cq = 4 * (f % kCQ);
                     xv[a] = lv[a] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
                     if (f < units && cq < width) {
-                        const uint32_t o = static_cast<uint32_t>(row * W + cb + cq) * 4;
-                        xv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0));
-                        lv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ls, o, 0, 0));
+                        xv[a] = load4(xs, row * W + cb + cq);
+                        lv[a] = load4(ls, row * W + cb + cq);
                     }
                 }
 #pragma unroll
@@ -268,8 +299,7 @@ __device__ __forceinline__ void wide_pass(const float* __restrict__ x, const flo
                     if (f < units && cq < width) {
                         const uint32_t o = static_cast<uint32_t>(row * W + cb + cq) * 4;
                         yv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ys, o, 0, 0));
-                        if constexpr (Dir == 3)
-                            uv[a] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(us, o, 0, 0));
+                        if constexpr (Dir == 3) uv[a] = load4(us, row * W + cb + cq);
                     }
                 }
 #pragma unroll
@@ -281,7 +311,14 @@ __device__ __forceinline__ void wide_pass(const float* __restrict__ x, const flo
 #pragma unroll
                         for (int e = 0; e < 4; ++e) v[e] = yv[a][e] + bs[(cq + e) * pitch + row];
                         if constexpr (Dir == 3) v = v * uv[a];
-                        *reinterpret_cast<f32x4_t*>(y + pix0 + static_cast<size_t>(row) * W + cb + cq) = v;
+                        const size_t e = pix0 + static_cast<size_t>(row) * W + cb + cq;
+                        if constexpr (Dir == 3 && ES == 2) {
+                            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                            *reinterpret_cast<u32x2_t*>(yout + e) =
+                                u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        } else {
+                            *reinterpret_cast<f32x4_t*>(y + e) = v;
+                        }
                     }
                 }
             }
@@ -292,26 +329,26 @@ __device__ __forceinline__ void wide_pass(const float* __restrict__ x, const flo
 
 // The four passes of one plane, in the summation order TD, BU, LR, RL; KR
 // and KC are the positions a lane holds on a row and on a column.
-template <int KR, int KC, bool Chunked>
+template <typename T, int KR, int KC, bool Chunked>
 __global__ void __launch_bounds__(64)
-prop2d_wide_kernel(const float* __restrict__ x, const float* __restrict__ lam,
-                   const float* __restrict__ u, const float* __restrict__ w4, float eps,
-                   float* __restrict__ y, int planes, int H, int W, int cpg, int k_chunk) {
+prop2d_wide_kernel(const T* __restrict__ x, const T* __restrict__ lam, const T* __restrict__ u,
+                   const T* __restrict__ w4, float eps, float* __restrict__ y, T* __restrict__ yout,
+                   int planes, int H, int W, int cpg, int k_chunk) {
     extern __shared__ __attribute__((aligned(16))) float strip[];
     constexpr int D = 4;
-    wide_pass<KR, D, 0, Chunked>(x, lam, u, w4, eps, y, planes, H, W, cpg, k_chunk, strip);
+    wide_pass<T, KR, D, 0, Chunked>(x, lam, u, w4, eps, y, yout, planes, H, W, cpg, k_chunk, strip);
     pass_sync();
-    wide_pass<KR, D, 1, Chunked>(x, lam, u, w4, eps, y, planes, H, W, cpg, k_chunk, strip);
+    wide_pass<T, KR, D, 1, Chunked>(x, lam, u, w4, eps, y, yout, planes, H, W, cpg, k_chunk, strip);
     pass_sync();
-    wide_pass<KC, D, 2, Chunked>(x, lam, u, w4, eps, y, planes, H, W, cpg, k_chunk, strip);
+    wide_pass<T, KC, D, 2, Chunked>(x, lam, u, w4, eps, y, yout, planes, H, W, cpg, k_chunk, strip);
     pass_sync();
-    wide_pass<KC, D, 3, Chunked>(x, lam, u, w4, eps, y, planes, H, W, cpg, k_chunk, strip);
+    wide_pass<T, KC, D, 3, Chunked>(x, lam, u, w4, eps, y, yout, planes, H, W, cpg, k_chunk, strip);
 }
 
-template <int KR, int KC>
-hipError_t launch_k(const float* x, const float* lam, const float* u, const float* w4, float eps,
-                    float* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
-                    hipStream_t stream) {
+// y: the fp32 direction sum (the output itself for fp32); yout: the output.
+template <typename T, int KR, int KC>
+hipError_t launch_k(const T* x, const T* lam, const T* u, const T* w4, float eps, float* y, T* yout,
+                    int64_t planes, int64_t H, int64_t W, const PropOpts& o, hipStream_t stream) {
     const size_t lds = kSW * static_cast<size_t>(strip_pitch(static_cast<int>(H))) * 4;
     auto run = [&](auto kern) -> hipError_t {
         if (lds > 64 * 1024) {
@@ -320,11 +357,11 @@ hipError_t launch_k(const float* x, const float* lam, const float* u, const floa
             if (e != hipSuccess) return e;
         }
         kern<<<dim3(static_cast<unsigned>(planes)), dim3(64), lds, stream>>>(
-            x, lam, u, w4, eps, y, static_cast<int>(planes), static_cast<int>(H),
+            x, lam, u, w4, eps, y, yout, static_cast<int>(planes), static_cast<int>(H),
             static_cast<int>(W), static_cast<int>(o.cpg), static_cast<int>(o.k_chunk));
         return hipGetLastError();
     };
-    return o.k_chunk > 1 ? run(prop2d_wide_kernel<KR, KC, true>) : run(prop2d_wide_kernel<KR, KC, false>);
+    return o.k_chunk > 1 ? run(prop2d_wide_kernel<T, KR, KC, true>) : run(prop2d_wide_kernel<T, KR, KC, false>);
 }
 
 // K = ceil(L / 64) positions a lane, L up to 256
@@ -332,15 +369,39 @@ template <int KR>
 hipError_t launch_kc(const float* x, const float* lam, const float* u, const float* w4, float eps,
                      float* y, int64_t planes, int64_t H, int64_t W, const PropOpts& o,
                      hipStream_t stream) {
-    if (H <= 64) return launch_k<KR, 1>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    if (H <= 128) return launch_k<KR, 2>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    if (H <= 192) return launch_k<KR, 3>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
-    return launch_k<KR, 4>(x, lam, u, w4, eps, y, planes, H, W, o, stream);
+    if (H <= 64) return launch_k<float, KR, 1>(x, lam, u, w4, eps, y, y, planes, H, W, o, stream);
+    if (H <= 128) return launch_k<float, KR, 2>(x, lam, u, w4, eps, y, y, planes, H, W, o, stream);
+    if (H <= 192) return launch_k<float, KR, 3>(x, lam, u, w4, eps, y, y, planes, H, W, o, stream);
+    return launch_k<float, KR, 4>(x, lam, u, w4, eps, y, y, planes, H, W, o, stream);
 }
+
+// bf16 planes take this kernel only when their direction sum leaves LDS
+// (above about 40,500 pixels, so both sides above 158): K = 4 on both lines
+// (sides 196..256, multiples of 4); other sizes take the general kernel
+bool wide_bf16_side(int64_t L) { return L > 192 && L <= kMaxSideWide; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
+
+bool prop2d_wide_bf16_eligible(int64_t planes, int64_t H, int64_t W, const void* x, const void* lam,
+                               const void* u, const void* w4, const void* y, const void* acc) {
+    if ((H & 3) || (W & 3) || !wide_bf16_side(H) || !wide_bf16_side(W)) return false;
+    if (planes > 0x7fffffff || 12 * H * W * 2 > 0x7fffffff) return false;
+    return aligned16(x) && aligned16(lam) && aligned16(u) && aligned16(w4) && aligned16(y) && aligned16(acc);
+}
+
+hipError_t launch_prop2d_wide_bf16(const void* x_, const void* lam_, const void* u_, const void* w4_,
+                                   float eps, void* y_, int64_t planes, int64_t H, int64_t W,
+                                   const PropOpts& o, float* acc, hipStream_t stream) {
+    const uint16_t* x = static_cast<const uint16_t*>(x_);
+    const uint16_t* lam = static_cast<const uint16_t*>(lam_);
+    const uint16_t* u = static_cast<const uint16_t*>(u_);
+    const uint16_t* w4 = static_cast<const uint16_t*>(w4_);
+    uint16_t* y = static_cast<uint16_t*>(y_);
+    if (!wide_bf16_side(H) || !wide_bf16_side(W)) return hipErrorInvalidValue;
+    return launch_k<uint16_t, 4, 4>(x, lam, u, w4, eps, acc, y, planes, H, W, o, stream);
+}
 
 bool prop2d_wide_eligible(int dtype, int64_t planes, int64_t H, int64_t W, const void* x,
                           const void* lam, const void* u, const void* w4, const void* y) {

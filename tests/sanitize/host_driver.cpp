@@ -51,6 +51,21 @@ hipError_t launch_latent_sublayer(const void*, const void*, const void*, const v
 // size queries: the forms the kernels' own give (within the bounds the host
 // layer checks first)
 int64_t prop2d_max_plane(int dtype, int64_t, int64_t) { return dtype == 0 ? (int64_t{1} << 62) : 40000; }
+int64_t prop2d_global_acc_bytes(int dtype, int64_t planes, int64_t H, int64_t W) {
+    return (dtype == 1 && H * W > 40000) ? ((planes * H * W * 4 + 255) & ~int64_t{255}) : 0;
+}
+hipError_t launch_prop2d_global_acc(const void*, const void*, const void*, const void*, float, void*, int64_t,
+                                    int64_t, int64_t, const PropOpts&, float*, hipStream_t) {
+    ++g_launches; return hipSuccess;
+}
+bool prop2d_wide_bf16_eligible(int64_t, int64_t H, int64_t W, const void*, const void*, const void*,
+                               const void*, const void*, const void*) {
+    return H % 4 == 0 && W % 4 == 0 && H > 192 && W > 192 && H <= 256 && W <= 256;
+}
+hipError_t launch_prop2d_wide_bf16(const void*, const void*, const void*, const void*, float, void*, int64_t,
+                                   int64_t, int64_t, const PropOpts&, float*, hipStream_t) {
+    ++g_launches; return hipSuccess;
+}
 int64_t prop2d_backward_max_line() { return 8192; }
 int64_t prop2d_backward_workspace_bytes(int64_t planes, int64_t H, int64_t W, int64_t cpg) {
     return 24 * planes * H * W + (cpg > 1 ? 48 * planes * H * W : 0);
@@ -123,6 +138,19 @@ int main() {
                                   nullptr), GSPN_ERR_ALIAS, 0, "ex_ws alias");
     expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 1, 1, 1e-6f, M(5), nullptr, 0, 0, 2, 4, 6, 6,
                                   nullptr), GSPN_OK, 1, "ex_ws unused");
+    // bf16 planes beyond the on-chip sum: only with the workspace's accumulator
+    const int64_t wacc = gspn_prop2d_4dir_ex_workspace(1, 2, 4, 4, 256, 256);
+    if (wacc != 8 * 256 * 256 * 4) ++fails;
+    expect(gspn_prop2d_4dir(P(0), P(1), P(2), P(3), 1e-6f, M(5), 1, 2, 4, 256, 256, nullptr), GSPN_ERR_SHAPE, 0,
+           "prop bf16 beyond LDS");
+    expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 4, 1, 1e-6f, M(5), M(6), wacc, 1, 2, 4, 256, 256,
+                                  nullptr), GSPN_OK, 1, "ex_ws bf16 beyond LDS");
+    expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 2, 3, 1e-6f, M(5), M(6), wacc, 1, 2, 4, 203, 201,
+                                  nullptr), GSPN_OK, 1, "ex_ws bf16 beyond LDS, general");
+    expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 4, 1, 1e-6f, M(5), M(6), wacc - 1, 1, 2, 4, 256, 256,
+                                  nullptr), GSPN_ERR_SHAPE, 0, "ex_ws bf16 beyond LDS, small");
+    expect(gspn_prop2d_4dir_ex_ws(P(0), P(1), P(2), P(3), 4, 1, 1e-6f, M(5), nullptr, wacc, 1, 2, 4, 256, 256,
+                                  nullptr), GSPN_ERR_NULL, 0, "ex_ws bf16 beyond LDS, null");
     // gspn_scan_dir and gspn_normalize_weights
     for (int dir = 0; dir < 4; ++dir)
         expect(gspn_scan_dir(P(0), P(1), P(2), P(3), 1, 1e-6f, M(5), 1, 0, 2, 3, 5, 7, dir, nullptr), GSPN_OK, 1, "scan ok");

@@ -63,9 +63,12 @@ def test_ex_groups_and_chunks(H, W, G, k, dtype):
 
 # bf16 planes whose fp32 direction sum does not fit in LDS (above about
 # 40,500 pixels) run with an fp32 accumulator plane per (b, c) in the
-# workspace (gspn_prop2d_4dir_ex_ws; the binding allocates it); the plain
-# call refuses them
-@pytest.mark.parametrize("H,W", [(202, 202), (256, 256), (203, 201), (256, 170)])
+# workspace (gspn_prop2d_4dir_ex_ws; the binding allocates it): sides
+# 196..256 that are multiples of 4 in the one-wavefront-a-plane kernel
+# (202 x 202 is not: the general kernel), the rest in the general kernel;
+# the plain call refuses them
+@pytest.mark.parametrize("H,W", [(204, 204), (256, 256), (244, 200), (202, 202), (203, 201),
+                                 (256, 170)])
 @pytest.mark.parametrize("G,k", [(3, 1), (1, 4)])
 def test_ex_bf16_planes_beyond_lds(H, W, G, k):
     say("ex bf16 beyond LDS", H, W, G, k)
