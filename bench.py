@@ -374,17 +374,25 @@ def shape_leg(args, dev, B, C, H, W, dtype, backward=False, rotate=True):
     nsets = max(1, int(np.ceil(args.rotate_bytes / wl.algorithmic_bytes))) if rotate else 1
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
     outs = [torch.empty_like(base["x"]) for _ in range(nsets)]
+    # bf16 planes whose direction sum leaves LDS run only with a workspace
+    # (gspn_prop2d_4dir_ex_ws, groups = C), allocated before the timed region
+    need = gspn.prop2d_4dir_ex_workspace_bytes(base["x"].dtype, B, C, C, H, W)
+    ws = torch.empty(need // 4, dtype=torch.float32, device=dev) if need else None
     torch.cuda.synchronize()
 
     def fn(i):
         st = sets[i % nsets]
-        gspn.prop2d_4dir(st["x"], st["lam"], st["u"], st["w"], out=outs[i % nsets])
+        if ws is None:
+            gspn.prop2d_4dir(st["x"], st["lam"], st["u"], st["w"], out=outs[i % nsets])
+        else:
+            gspn.prop2d_4dir_ex(st["x"], st["lam"], st["u"], st["w"], C, 1, out=outs[i % nsets], workspace=ws)
 
     wall, kavg, kmin = _timed(fn, args.steps, args.warmup, torch.cuda.current_stream(dev))
     nbytes = wl.algorithmic_bytes
     achieved = nbytes / (kavg * 1e-3) / 1e9
     out = {"B": B, "C": C, "H": H, "W": W, "dtype": dtype,
            "inputs": "rotated over %d sets" % nsets if rotate else "warm (one set)",
+           "forward_workspace_bytes": need,
            "forward": {"ms_per_step": round(wall * 1e3 / args.steps, 5),
                        "value": round(nbytes / (wall / args.steps) / 1e9, 2), "unit": "GB/s",
                        "algorithmic_bytes_per_step": nbytes,
@@ -392,7 +400,7 @@ def shape_leg(args, dev, B, C, H, W, dtype, backward=False, rotate=True):
                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
                                     "kernel_ms_avg": round(kavg, 5), "kernel_ms_min": round(kmin, 5)}}}
-    del outs
+    del outs, ws
     if backward:
         out["backward"] = backward_leg(wl, sets, args, dev)
     del sets
