@@ -21,6 +21,14 @@ __device__ __forceinline__ float from_next(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x130, 0xf, 0xf, true));
 }
 
+// The middle one of three unsigned values, as one v_med3_u32 (clamping a
+// look-ahead offset to a plane's first and last lines).
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // NW (1..4) consecutive dwords as one value, so that a prefetched window
 // stays one register tuple from its load to its use.
 template <int NW> struct Words { using type = uint32_t __attribute__((ext_vector_type(NW))); };

@@ -259,7 +259,7 @@ __device__ __forceinline__ void scan_pair(const DuoArgs& a, const DuoLayout& lay
 #pragma unroll
             for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
             const uint32_t nx = lo + dlo;
-            lo = nx < lo_min ? lo_min : (nx > lo_max ? lo_max : nx);
+            lo = umed3(nx, lo_min, lo_max);
         }
     };
     // the NW words a window decodes from (Odd: shifted into place)

@@ -44,6 +44,13 @@
 // adds in program order, so every pixel's four terms are summed in a fixed
 // order and the result is bitwise reproducible.
 //
+// Grid.  The launch has as many workgroups as the CUs keep resident at once
+// (four 74 x 74 planes a CU), each walking planes blockIdx.x + i gridDim.x:
+// a workgroup issues its next plane's x, lambda and first tap lines as soon
+// as the current plane's scan ends, so they arrive while it adds the meeting
+// pixels' side words and writes y, instead of every workgroup of a second
+// round waiting for them at once.
+//
 // Slots past the end of a line (positions >= L) read and write dummy words,
 // decode every tap to -2^127 (weight exactly 0) and hold h = 0; lanes whose
 // whole window lies past the line load nothing (an offset past the buffer).
@@ -52,6 +59,7 @@
 #include "gspn_internal.h"
 #include "gspn_lane.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace gspn {
@@ -190,14 +198,21 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     // the plane of workgroup i is chosen so that XCD x walks tap planes x,
     // x + 8, ... and every channel of a tap group reads its weights through
     // one L2.  Any plane order gives the same results.
-    int plane = blockIdx.x;
-    if constexpr (PRE) {
-        if (planes % (8 * cpg) == 0) {
-            const int x8 = plane & 7, sl = plane >> 3;
-            plane = ((sl / cpg) * 8 + x8) * cpg + sl % cpg;
+    // A workgroup scans planes v = blockIdx.x, blockIdx.x + gridDim.x, ...
+    // (the grid holds at most as many workgroups as the CUs keep resident):
+    // the next plane's x, lambda and first tap lines are loaded while the
+    // current plane's sums are finished and written out.  gridDim.x is a
+    // multiple of 8 or the whole plane count, so v and blockIdx.x share an
+    // XCD.
+    auto plane_of = [&](int v) -> int {
+        if constexpr (PRE) {
+            if (planes % (8 * cpg) == 0) {
+                const int x8 = v & 7, sl = v >> 3;
+                return ((sl / cpg) * 8 + x8) * cpg + sl % cpg;
+            }
         }
-    }
-    const uint32_t plane_b = static_cast<uint32_t>(plane) * static_cast<uint32_t>(n) * 2u;
+        return v;
+    };
     const int nchunk = (2 * n + 15) / 16;  // 16-byte chunks of a plane's bf16 values
 
     // ------------------------------------------------ u, prefetched for the end
@@ -206,12 +221,6 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     const __amdgpu_buffer_rsrc_t us = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(u), 0, static_cast<int>(static_cast<int64_t>(planes) * n * 2), kBufFlags);
     u32x4_t uv[kU];
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-        const int f = lane + 64 * k;
-        uv[k] = f < nchunk ? __builtin_amdgcn_raw_buffer_load_b128(us, plane_b + 16u * static_cast<uint32_t>(f), 0, 0)
-                           : u32x4_t{0u, 0u, 0u, 0u};
-    }
 
     // ------------------------------------------------ x and lambda, all at once
     const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
@@ -219,13 +228,6 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(lam), 0, static_cast<int>(static_cast<int64_t>(planes) * n * 2), kBufFlags);
     u32x4_t xv[kU], lv[kU];
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-        const int f = lane + 64 * k;
-        const uint32_t off = plane_b + 16u * static_cast<uint32_t>(f);
-        xv[k] = f < nchunk ? __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0) : u32x4_t{0u, 0u, 0u, 0u};
-        lv[k] = f < nchunk ? __builtin_amdgcn_raw_buffer_load_b128(ls, off, 0, 0) : u32x4_t{0u, 0u, 0u, 0u};
-    }
 
     // ------------------------------------------------ taps: first D lines
     const int tap_planes = planes / cpg;
@@ -242,22 +244,27 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w4), 0, w4_bytes, kBufFlags);
     uint32_t po = 0;
     constexpr uint32_t dpo = 16u * KP * 4u;
-    if constexpr (PRE) {
-        po = (static_cast<uint32_t>(g * tap_planes + plane / cpg) * static_cast<uint32_t>(L) * 16u +
-              static_cast<uint32_t>(q)) * (KP * 4u);
-    } else {
+    if constexpr (!PRE) {
 #pragma unroll
         for (int k = 0; k < 3; ++k)
             taps[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w4) + static_cast<size_t>(k) * n,
                                                         0, w4_bytes - k * n * 2, kBufFlags);
-        const uint32_t tap_base =
-            static_cast<uint32_t>((g * tap_planes + plane / cpg) * 3) * static_cast<uint32_t>(n) * 2u +
-            static_cast<uint32_t>(K * q - par) * 2u;
-        lo_min = lane_live ? tap_base : 0x80000000u;
-        lo_max = lane_live ? tap_base + static_cast<uint32_t>(L - 1) * line_b : 0x80000000u;
-        lo = fwd ? lo_min : lo_max;
-        dlo = lane_live ? (fwd ? line_b : 0u - line_b) : 0u;
     }
+    // a plane's first tap line of this lane's direction
+    auto tap_start = [&](int plane) {
+        if constexpr (PRE) {
+            po = (static_cast<uint32_t>(g * tap_planes + plane / cpg) * static_cast<uint32_t>(L) * 16u +
+                  static_cast<uint32_t>(q)) * (KP * 4u);
+        } else {
+            const uint32_t tap_base =
+                static_cast<uint32_t>((g * tap_planes + plane / cpg) * 3) * static_cast<uint32_t>(n) * 2u +
+                static_cast<uint32_t>(K * q - par) * 2u;
+            lo_min = lane_live ? tap_base : 0x80000000u;
+            lo_max = lane_live ? tap_base + static_cast<uint32_t>(L - 1) * line_b : 0x80000000u;
+            lo = fwd ? lo_min : lo_max;
+            dlo = lane_live ? (fwd ? line_b : 0u - line_b) : 0u;
+        }
+    };
     auto load_line = [&](int d) {
         if constexpr (PRE) {
             // a step past the scan reads the next block or past the buffer
@@ -269,120 +276,191 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
 #pragma unroll
             for (int k = 0; k < 3; ++k) tbuf[d][k] = load_words<NW>(taps[k], lo);
             const uint32_t nx = lo + dlo;
-            lo = nx < lo_min ? lo_min : (nx > lo_max ? lo_max : nx);
+            lo = umed3(nx, lo_min, lo_max);
         }
     };
+    // x, lambda and the first D tap lines of a plane
+    auto issue_plane = [&](int plane) {
+        const uint32_t pb = static_cast<uint32_t>(plane) * static_cast<uint32_t>(n) * 2u;
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        load_line(d);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // ------------------------------------------------ zero S, side, dummies
-    for (int f = lane; f < lay.bh / 16; f += 64) lds_ref<u32x4_t>(16u * f) = u32x4_t{0u, 0u, 0u, 0u};
-
-    // ------------------------------------------------ b = lambda x into LDS
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-        const int f = lane + 64 * k;
-        if (f < nchunk) {
-            uint32_t bb[8];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                bb[2 * m] = __float_as_uint(bf_lo(lv[k][m]) * bf_lo(xv[k][m]));
-                bb[2 * m + 1] = __float_as_uint(bf_hi(lv[k][m]) * bf_hi(xv[k][m]));
-            }
-            u32x4_t hi;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) hi[m] = __builtin_amdgcn_perm(bb[2 * m + 1], bb[2 * m], 0x07060302u);
-            u32x2_t lo8;
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const uint32_t t01 = __builtin_amdgcn_perm(bb[4 * m + 1], bb[4 * m], 0x0c0c0501u);
-                const uint32_t t23 = __builtin_amdgcn_perm(bb[4 * m + 3], bb[4 * m + 2], 0x05010c0cu);
-                lo8[m] = t01 | t23;
-            }
-            lds_ref<u32x4_t>(lay.bh + 16u * f) = hi;
-            lds_ref<u32x2_t>(lay.bl + 8u * f) = lo8;
+        for (int k = 0; k < kU; ++k) {
+            const int f = lane + 64 * k;
+            const uint32_t off = pb + 16u * static_cast<uint32_t>(f);
+            xv[k] = f < nchunk ? __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0) : u32x4_t{0u, 0u, 0u, 0u};
+            lv[k] = f < nchunk ? __builtin_amdgcn_raw_buffer_load_b128(ls, off, 0, 0) : u32x4_t{0u, 0u, 0u, 0u};
         }
-    }
-    lds_order();
-
-    // ------------------------------------------------ per-slot constants
-    const int i0 = fwd ? 0 : L - 1;
-    const int de = rows ? (fwd ? L : -L) : (fwd ? 1 : -1);
-    uint32_t aS[K], aH[K], aL[K];
-    int dSj[K], dHj[K], dLj[K];
-    uint32_t sel[3][K];
-    const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
-    const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
+        tap_start(plane);
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-        const int p = K * q + j;
-        const bool valid = p < L;
-        const int e = rows ? i0 * L + p : p * L + i0;
-        aS[j] = valid ? static_cast<uint32_t>(lay.s + 4 * e) : QuadLayout::sdum;
-        aH[j] = valid ? static_cast<uint32_t>(lay.bh + 2 * e) : QuadLayout::bdum;
-        aL[j] = valid ? static_cast<uint32_t>(lay.bl + e) : QuadLayout::bdum;
-        dSj[j] = valid ? 4 * de : 0;
-        dHj[j] = valid ? 2 * de : 0;
-        dLj[j] = valid ? de : 0;
-        const uint32_t s_in = (j & 1) ? sel_odd : sel_even;
-        sel[0][j] = (valid && p > 0) ? s_in : kSelDropped;
-        sel[1][j] = valid ? s_in : kSelDropped;
-        sel[2][j] = (valid && p < L - 1) ? s_in : kSelDropped;
-    }
-    // column slots that meet a row scan: key q for the column rows, none else
-    const uint32_t key = rows ? 0xffu : static_cast<uint32_t>(q);
-    const uint32_t side1 = static_cast<uint32_t>(lay.side + 4 * L * (g == 3 ? 1 : 0));
-    const uint32_t side2 = static_cast<uint32_t>(lay.side + 4 * L * (g == 3 ? 3 : 2));
-
-    float h[K], acc[K];
-    uint32_t bhr[K], blr[K];
-    uint32_t ra1 = 0, ra2 = 0;   // addresses of this step's two meeting slots
-
-    // S address of slot j at step s, for a step whose meeting slots are j1
-    // (row s, lanes q1) and j2 (row L-1-s, lanes q2)
-    auto meet_addr = [&](int j, int j1, int j2, uint32_t q1, uint32_t q2, int s) -> uint32_t {
-        uint32_t a = aS[j];
-        if (j == j1) a = key == q1 ? side1 + 4u * s : a;
-        if (j == j2) a = key == q2 ? side2 + 4u * s : a;
-        return a;
+        for (int d = 0; d < D; ++d) {
+            load_line(d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
-    // Meeting slots of step s = s0 + t of a block starting at s0 (a multiple
-    // of K; t a compile-time value): rows s (slot t mod K, lanes q1) and
-    // L-1-s (slot (R - t) mod K, lanes q2), with q1 = s0 / K + t / K and q2 =
-    // (L-1-R-s0) / K + floor((R - t) / K).
-    auto read_ahead = [&](int t, int s, int qb1, int qb2) {
-        const int j1 = t % K;
-        const int j2 = ((R - t) % K + K) % K;
-        const uint32_t q1 = static_cast<uint32_t>(qb1 + t / K);
-        const uint32_t q2 = static_cast<uint32_t>(qb2 + (R - t >= 0 ? (R - t) / K : -((t - R + K - 1) / K)));
-        ra1 = meet_addr(j1, j1, j2, q1, q2, s);
-        ra2 = meet_addr(j2, j1, j2, q1, q2, s);
+    issue_plane(plane_of(static_cast<int>(blockIdx.x)));
+
+    for (int v = static_cast<int>(blockIdx.x); v < planes; v += static_cast<int>(gridDim.x)) {
+        const int plane = plane_of(v);
+        const uint32_t plane_b = static_cast<uint32_t>(plane) * static_cast<uint32_t>(n) * 2u;
+        // ------------------------------------------------ u, for the end
+        // (it arrives while the plane is scanned; kU 16-byte chunks a lane)
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+            const int f = lane + 64 * k;
+            uv[k] = f < nchunk ? __builtin_amdgcn_raw_buffer_load_b128(us, plane_b + 16u * static_cast<uint32_t>(f), 0, 0)
+                               : u32x4_t{0u, 0u, 0u, 0u};
+        }
+
+        // ------------------------------------------------ zero S, side, dummies
+        // (after the previous plane's last reads of S)
+        lds_order();
+        for (int f = lane; f < lay.bh / 16; f += 64) lds_ref<u32x4_t>(16u * f) = u32x4_t{0u, 0u, 0u, 0u};
+
+        // ------------------------------------------------ b = lambda x into LDS
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+            const int f = lane + 64 * k;
+            if (f < nchunk) {
+                uint32_t bb[8];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    bb[2 * m] = __float_as_uint(bf_lo(lv[k][m]) * bf_lo(xv[k][m]));
+                    bb[2 * m + 1] = __float_as_uint(bf_hi(lv[k][m]) * bf_hi(xv[k][m]));
+                }
+                u32x4_t hi;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) hi[m] = __builtin_amdgcn_perm(bb[2 * m + 1], bb[2 * m], 0x07060302u);
+                u32x2_t lo8;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const uint32_t t01 = __builtin_amdgcn_perm(bb[4 * m + 1], bb[4 * m], 0x0c0c0501u);
+                    const uint32_t t23 = __builtin_amdgcn_perm(bb[4 * m + 3], bb[4 * m + 2], 0x05010c0cu);
+                    lo8[m] = t01 | t23;
+                }
+                lds_ref<u32x4_t>(lay.bh + 16u * f) = hi;
+                lds_ref<u32x2_t>(lay.bl + 8u * f) = lo8;
+            }
+        }
+        lds_order();
+
+        // ------------------------------------------------ per-slot constants
+        const int i0 = fwd ? 0 : L - 1;
+        const int de = rows ? (fwd ? L : -L) : (fwd ? 1 : -1);
+        uint32_t aS[K], aH[K], aL[K];
+        int dSj[K], dHj[K], dLj[K];
+        uint32_t sel[3][K];
+        const uint32_t sel_even = par ? 0x03020c0cu : 0x01000c0cu;
+        const uint32_t sel_odd = par ? 0x05040c0cu : 0x03020c0cu;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            const uint32_t a = j == j1 ? ra1 : (j == j2 ? ra2 : aS[j]);
-            acc[j] = lds_ref<float>(a);
-            bhr[j] = lds_ref<uint16_t>(aH[j]);
-            blr[j] = lds_ref<uint8_t>(aL[j]);
+            const int p = K * q + j;
+            const bool valid = p < L;
+            const int e = rows ? i0 * L + p : p * L + i0;
+            aS[j] = valid ? static_cast<uint32_t>(lay.s + 4 * e) : QuadLayout::sdum;
+            aH[j] = valid ? static_cast<uint32_t>(lay.bh + 2 * e) : QuadLayout::bdum;
+            aL[j] = valid ? static_cast<uint32_t>(lay.bl + e) : QuadLayout::bdum;
+            dSj[j] = valid ? 4 * de : 0;
+            dHj[j] = valid ? 2 * de : 0;
+            dLj[j] = valid ? de : 0;
+            const uint32_t s_in = (j & 1) ? sel_odd : sel_even;
+            sel[0][j] = (valid && p > 0) ? s_in : kSelDropped;
+            sel[1][j] = valid ? s_in : kSelDropped;
+            sel[2][j] = (valid && p < L - 1) ? s_in : kSelDropped;
         }
-    };
-#pragma unroll
-    for (int j = 0; j < K; ++j) h[j] = 0.0f;
-    read_ahead(0, 0, 0, (L - 1 - R) / K);
+        // column slots that meet a row scan: key q for the column rows, none else
+        const uint32_t key = rows ? 0xffu : static_cast<uint32_t>(q);
+        const uint32_t side1 = static_cast<uint32_t>(lay.side + 4 * L * (g == 3 ? 1 : 0));
+        const uint32_t side2 = static_cast<uint32_t>(lay.side + 4 * L * (g == 3 ? 3 : 2));
 
-    auto step = [&](int s, int d, int qb1, int qb2) {
-        float hn[K];
-        if constexpr (PRE) {
-            asm volatile("" : "+v"(pbuf[d][0]));
-            float wv[3 * K];
+        float h[K], acc[K];
+        uint32_t bhr[K], blr[K];
+        uint32_t ra1 = 0, ra2 = 0;   // addresses of this step's two meeting slots
+
+        // S address of slot j at step s, for a step whose meeting slots are j1
+        // (row s, lanes q1) and j2 (row L-1-s, lanes q2)
+        auto meet_addr = [&](int j, int j1, int j2, uint32_t q1, uint32_t q2, int s) -> uint32_t {
+            uint32_t a = aS[j];
+            if (j == j1) a = key == q1 ? side1 + 4u * s : a;
+            if (j == j2) a = key == q2 ? side2 + 4u * s : a;
+            return a;
+        };
+        // Meeting slots of step s = s0 + t of a block starting at s0 (a multiple
+        // of K; t a compile-time value): rows s (slot t mod K, lanes q1) and
+        // L-1-s (slot (R - t) mod K, lanes q2), with q1 = s0 / K + t / K and q2 =
+        // (L-1-R-s0) / K + floor((R - t) / K).
+        auto read_ahead = [&](int t, int s, int qb1, int qb2) {
+            const int j1 = t % K;
+            const int j2 = ((R - t) % K + K) % K;
+            const uint32_t q1 = static_cast<uint32_t>(qb1 + t / K);
+            const uint32_t q2 = static_cast<uint32_t>(qb2 + (R - t >= 0 ? (R - t) / K : -((t - R + K - 1) / K)));
+            ra1 = meet_addr(j1, j1, j2, q1, q2, s);
+            ra2 = meet_addr(j2, j1, j2, q1, q2, s);
 #pragma unroll
-            for (int e = 0; e < 3 * K; ++e) wv[e] = __uint_as_float(pbuf[d][e / 4][e % 4]);
-            // refill slot d only after it has been read
+            for (int j = 0; j < K; ++j) {
+                const uint32_t a = j == j1 ? ra1 : (j == j2 ? ra2 : aS[j]);
+                acc[j] = lds_ref<float>(a);
+                bhr[j] = lds_ref<uint16_t>(aH[j]);
+                blr[j] = lds_ref<uint8_t>(aL[j]);
+            }
+        };
 #pragma unroll
-            for (int e = 0; e < 3 * K; ++e) asm volatile("" : "+v"(po) : "v"(wv[e]));
+        for (int j = 0; j < K; ++j) h[j] = 0.0f;
+        read_ahead(0, 0, 0, (L - 1 - R) / K);
+
+        auto step = [&](int s, int d, int qb1, int qb2) {
+            float hn[K];
+            if constexpr (PRE) {
+                asm volatile("" : "+v"(pbuf[d][0]));
+                float wv[3 * K];
+#pragma unroll
+                for (int e = 0; e < 3 * K; ++e) wv[e] = __uint_as_float(pbuf[d][e / 4][e % 4]);
+                // refill slot d only after it has been read
+#pragma unroll
+                for (int e = 0; e < 3 * K; ++e) asm volatile("" : "+v"(po) : "v"(wv[e]));
+                load_line(d);
+                float bv[K];
+#pragma unroll
+                for (int j = 0; j < K; ++j) bv[j] = __uint_as_float(__builtin_amdgcn_perm(bhr[j], blr[j], 0x0504000cu));
+                const float hl0 = row_prev(h[K - 1]);
+                const float hrK = row_next(h[0]);
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    const float hl = j > 0 ? h[j - 1] : hl0;
+                    const float hr = j < K - 1 ? h[j + 1] : hrK;
+                    hn[j] = fmaf(wv[3 * j + 2], hr, fmaf(wv[3 * j], hl, fmaf(wv[3 * j + 1], h[j], bv[j])));
+                }
+            } else {
+            asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
+            float s0v[K], s1v[K], s2v[K], r[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                s0v[j] = window_elem<uint16_t, K, NW>(tbuf[d][0], j, sel[0][j], sel[0][j]) * kNegLog2e;
+                s1v[j] = window_elem<uint16_t, K, NW>(tbuf[d][1], j, sel[1][j], sel[1][j]) * kNegLog2e;
+                s2v[j] = window_elem<uint16_t, K, NW>(tbuf[d][2], j, sel[2][j], sel[2][j]) * kNegLog2e;
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                s0v[j] = __builtin_amdgcn_exp2f(s0v[j]);
+                s1v[j] = __builtin_amdgcn_exp2f(s1v[j]);
+                s2v[j] = __builtin_amdgcn_exp2f(s2v[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                s0v[j] = __builtin_amdgcn_rcpf(s0v[j] + 1.0f);
+                s1v[j] = __builtin_amdgcn_rcpf(s1v[j] + 1.0f);
+                s2v[j] = __builtin_amdgcn_rcpf(s2v[j] + 1.0f);
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) r[j] = s0v[j] + s1v[j];
+#pragma unroll
+            for (int j = 0; j < K; ++j) r[j] = fmaxf(r[j] + s2v[j], eps);
+#pragma unroll
+            for (int j = 0; j < K; ++j) r[j] = __builtin_amdgcn_rcpf(r[j]);
+            // refill slot d only after it has been decoded
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                asm volatile("" : "+v"(lo) : "v"(s0v[j]), "v"(s1v[j]), "v"(s2v[j]), "v"(r[j]));
             load_line(d);
+
             float bv[K];
 #pragma unroll
             for (int j = 0; j < K; ++j) bv[j] = __uint_as_float(__builtin_amdgcn_perm(bhr[j], blr[j], 0x0504000cu));
@@ -392,132 +470,132 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
             for (int j = 0; j < K; ++j) {
                 const float hl = j > 0 ? h[j - 1] : hl0;
                 const float hr = j < K - 1 ? h[j + 1] : hrK;
-                hn[j] = fmaf(wv[3 * j + 2], hr, fmaf(wv[3 * j], hl, fmaf(wv[3 * j + 1], h[j], bv[j])));
+                float m = s1v[j] * h[j];
+                m = fmaf(s0v[j], hl, m);
+                m = fmaf(s2v[j], hr, m);
+                hn[j] = fmaf(m, r[j], bv[j]);
             }
-        } else {
-        asm volatile("" : "+v"(tbuf[d][0]), "+v"(tbuf[d][1]), "+v"(tbuf[d][2]));
-        float s0v[K], s1v[K], s2v[K], r[K];
+            }
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            s0v[j] = window_elem<uint16_t, K, NW>(tbuf[d][0], j, sel[0][j], sel[0][j]) * kNegLog2e;
-            s1v[j] = window_elem<uint16_t, K, NW>(tbuf[d][1], j, sel[1][j], sel[1][j]) * kNegLog2e;
-            s2v[j] = window_elem<uint16_t, K, NW>(tbuf[d][2], j, sel[2][j], sel[2][j]) * kNegLog2e;
-        }
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-            s0v[j] = __builtin_amdgcn_exp2f(s0v[j]);
-            s1v[j] = __builtin_amdgcn_exp2f(s1v[j]);
-            s2v[j] = __builtin_amdgcn_exp2f(s2v[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-            s0v[j] = __builtin_amdgcn_rcpf(s0v[j] + 1.0f);
-            s1v[j] = __builtin_amdgcn_rcpf(s1v[j] + 1.0f);
-            s2v[j] = __builtin_amdgcn_rcpf(s2v[j] + 1.0f);
-        }
-#pragma unroll
-        for (int j = 0; j < K; ++j) r[j] = s0v[j] + s1v[j];
-#pragma unroll
-        for (int j = 0; j < K; ++j) r[j] = fmaxf(r[j] + s2v[j], eps);
-#pragma unroll
-        for (int j = 0; j < K; ++j) r[j] = __builtin_amdgcn_rcpf(r[j]);
-        // refill slot d only after it has been decoded
-#pragma unroll
-        for (int j = 0; j < K; ++j)
-            asm volatile("" : "+v"(lo) : "v"(s0v[j]), "v"(s1v[j]), "v"(s2v[j]), "v"(r[j]));
-        load_line(d);
+            for (int j = 0; j < K; ++j) h[j] = hn[j];
 
-        float bv[K];
+            const int t = d % K;
+            const int j1 = t;
+            const int j2 = ((R - t) % K + K) % K;
 #pragma unroll
-        for (int j = 0; j < K; ++j) bv[j] = __uint_as_float(__builtin_amdgcn_perm(bhr[j], blr[j], 0x0504000cu));
-        const float hl0 = row_prev(h[K - 1]);
-        const float hrK = row_next(h[0]);
+            for (int j = 0; j < K; ++j) {
+                const uint32_t a = j == j1 ? ra1 : (j == j2 ? ra2 : aS[j]);
+                lds_ref<float>(a) = acc[j] + h[j];
+            }
+            // the next step's pixels, read after this step's writes (the pins keep
+            // each address one add a step instead of base + multiple of the step)
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            const float hl = j > 0 ? h[j - 1] : hl0;
-            const float hr = j < K - 1 ? h[j + 1] : hrK;
-            float m = s1v[j] * h[j];
-            m = fmaf(s0v[j], hl, m);
-            m = fmaf(s2v[j], hr, m);
-            hn[j] = fmaf(m, r[j], bv[j]);
-        }
-        }
-#pragma unroll
-        for (int j = 0; j < K; ++j) h[j] = hn[j];
+            for (int j = 0; j < K; ++j) {
+                aS[j] += dSj[j];
+                aH[j] += dHj[j];
+                aL[j] += dLj[j];
+                asm volatile("" : "+v"(aS[j]), "+v"(aH[j]), "+v"(aL[j]));
+            }
+            read_ahead(d + 1, s + 1, qb1, qb2);
+        };
 
-        const int t = d % K;
-        const int j1 = t;
-        const int j2 = ((R - t) % K + K) % K;
+        int s0 = 0;
+        for (; s0 + D <= L; s0 += D) {
+            const int qb1 = s0 / K, qb2 = (L - 1 - R - s0) / K;
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            const uint32_t a = j == j1 ? ra1 : (j == j2 ? ra2 : aS[j]);
-            lds_ref<float>(a) = acc[j] + h[j];
+            for (int d = 0; d < D; ++d) step(s0 + d, d, qb1, qb2);
         }
-        // the next step's pixels, read after this step's writes (the pins keep
-        // each address one add a step instead of base + multiple of the step)
+        {
+            const int qb1 = s0 / K, qb2 = (L - 1 - R - s0) / K;
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            aS[j] += dSj[j];
-            aH[j] += dHj[j];
-            aL[j] += dLj[j];
-            asm volatile("" : "+v"(aS[j]), "+v"(aH[j]), "+v"(aL[j]));
+            for (int d = 0; d < D; ++d)
+                if (s0 + d < L) step(s0 + d, d, qb1, qb2);
         }
-        read_ahead(d + 1, s + 1, qb1, qb2);
-    };
+        // the next plane's inputs and first tap lines, while this one finishes
+        if (v + static_cast<int>(gridDim.x) < planes) issue_plane(plane_of(v + static_cast<int>(gridDim.x)));
+        lds_order();
 
-    int s0 = 0;
-    for (; s0 + D <= L; s0 += D) {
-        const int qb1 = s0 / K, qb2 = (L - 1 - R - s0) / K;
-#pragma unroll
-        for (int d = 0; d < D; ++d) step(s0 + d, d, qb1, qb2);
-    }
-    {
-        const int qb1 = s0 / K, qb2 = (L - 1 - R - s0) / K;
-#pragma unroll
-        for (int d = 0; d < D; ++d)
-            if (s0 + d < L) step(s0 + d, d, qb1, qb2);
-    }
-    lds_order();
+        // ------------------------------------------------ meeting pixels
+        // (t, t) += LR's side word of step t + RL's of step L-1-t;
+        // (t, L-1-t) += RL's of step t + LR's of step L-1-t
+        for (int t = lane; t < L; t += 64) {
+            const uint32_t sd = static_cast<uint32_t>(lay.s + 4 * (t * L + t));
+            const uint32_t sa = static_cast<uint32_t>(lay.s + 4 * (t * L + L - 1 - t));
+            const float d0 = lds_ref<float>(lay.side + 4 * t);                    // LR, row = col = t
+            const float d1 = lds_ref<float>(lay.side + 4 * (3 * L + L - 1 - t));  // RL at step L-1-t
+            const float a0 = lds_ref<float>(lay.side + 4 * (L + t));              // RL, (t, L-1-t)
+            const float a1 = lds_ref<float>(lay.side + 4 * (2 * L + L - 1 - t));  // LR at step L-1-t
+            lds_ref<float>(sd) = (lds_ref<float>(sd) + d0) + d1;
+            lds_ref<float>(sa) = (lds_ref<float>(sa) + a0) + a1;
+        }
+        lds_order();
 
-    // ------------------------------------------------ meeting pixels
-    // (t, t) += LR's side word of step t + RL's of step L-1-t;
-    // (t, L-1-t) += RL's of step t + LR's of step L-1-t
-    for (int t = lane; t < L; t += 64) {
-        const uint32_t sd = static_cast<uint32_t>(lay.s + 4 * (t * L + t));
-        const uint32_t sa = static_cast<uint32_t>(lay.s + 4 * (t * L + L - 1 - t));
-        const float d0 = lds_ref<float>(lay.side + 4 * t);                    // LR, row = col = t
-        const float d1 = lds_ref<float>(lay.side + 4 * (3 * L + L - 1 - t));  // RL at step L-1-t
-        const float a0 = lds_ref<float>(lay.side + 4 * (L + t));              // RL, (t, L-1-t)
-        const float a1 = lds_ref<float>(lay.side + 4 * (2 * L + L - 1 - t));  // LR at step L-1-t
-        lds_ref<float>(sd) = (lds_ref<float>(sd) + d0) + d1;
-        lds_ref<float>(sa) = (lds_ref<float>(sa) + a0) + a1;
-    }
-    lds_order();
-
-    // ------------------------------------------------ y = u * S
-    {
-        const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
-            y, 0, static_cast<int>(static_cast<int64_t>(planes) * n * 2), kBufFlags);
-        const int nfull = (2 * n) / 16;   // whole chunks of the plane
+        // ------------------------------------------------ y = u * S
+        {
+            const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
+                y, 0, static_cast<int>(static_cast<int64_t>(planes) * n * 2), kBufFlags);
+            const int nfull = (2 * n) / 16;   // whole chunks of the plane
 #pragma unroll
-        for (int k = 0; k < kU; ++k) {
-            const int f = lane + 64 * k;
-            if (f < nchunk) {
-                const f32x4_t sa = lds_ref<f32x4_t>(lay.s + 32u * f);
-                const f32x4_t sb = lds_ref<f32x4_t>(lay.s + 32u * f + 16u);
-                u32x4_t o;
-                o[0] = pack_bf16x2(bf_lo(uv[k][0]) * sa[0], bf_hi(uv[k][0]) * sa[1]);
-                o[1] = pack_bf16x2(bf_lo(uv[k][1]) * sa[2], bf_hi(uv[k][1]) * sa[3]);
-                o[2] = pack_bf16x2(bf_lo(uv[k][2]) * sb[0], bf_hi(uv[k][2]) * sb[1]);
-                o[3] = pack_bf16x2(bf_lo(uv[k][3]) * sb[2], bf_hi(uv[k][3]) * sb[3]);
-                const uint32_t yo = plane_b + 16u * static_cast<uint32_t>(f);
-                if (f < nfull)
-                    __builtin_amdgcn_raw_buffer_store_b128(o, ys, yo, 0, 0);
-                else  // a plane of L L = 4 mod 8 values ends half way into its last chunk
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{o[0], o[1]}, ys, yo, 0, 0);
+            for (int k = 0; k < kU; ++k) {
+                const int f = lane + 64 * k;
+                if (f < nchunk) {
+                    const f32x4_t sa = lds_ref<f32x4_t>(lay.s + 32u * f);
+                    const f32x4_t sb = lds_ref<f32x4_t>(lay.s + 32u * f + 16u);
+                    u32x4_t o;
+                    o[0] = pack_bf16x2(bf_lo(uv[k][0]) * sa[0], bf_hi(uv[k][0]) * sa[1]);
+                    o[1] = pack_bf16x2(bf_lo(uv[k][1]) * sa[2], bf_hi(uv[k][1]) * sa[3]);
+                    o[2] = pack_bf16x2(bf_lo(uv[k][2]) * sb[0], bf_hi(uv[k][2]) * sb[1]);
+                    o[3] = pack_bf16x2(bf_lo(uv[k][3]) * sb[2], bf_hi(uv[k][3]) * sb[3]);
+                    const uint32_t yo = plane_b + 16u * static_cast<uint32_t>(f);
+                    if (f < nfull)
+                        __builtin_amdgcn_raw_buffer_store_b128(o, ys, yo, 0, 0);
+                    else  // a plane of L L = 4 mod 8 values ends half way into its last chunk
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{o[0], o[1]}, ys, yo, 0, 0);
+                }
             }
         }
-    }
+    }  // planes of this workgroup
+}
+
+// CUs of the current device, queried once per device.
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];
+hipError_t g_cus_err[kMaxDevices];
+std::once_flag g_cus_once[kMaxDevices];
+
+hipError_t device_cus(int* out) {
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_cus_once[dev], [dev] {
+        g_cus_err[dev] = hipDeviceGetAttribute(&g_cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    });
+    if (g_cus_err[dev] != hipSuccess) return g_cus_err[dev];
+    *out = g_cus[dev] > 0 ? g_cus[dev] : 1;
+    return hipSuccess;
+}
+
+// Workgroups of 64 threads with `lds` bytes of LDS each that the device
+// keeps resident at once: its CUs times the smaller of the kernel's own
+// limit per CU (registers; queried once per kernel) and the LDS limit.
+template <typename F>
+hipError_t resident_workgroups(F* kern, size_t lds, int64_t* out) {
+    static std::once_flag once;
+    static int per_cu = 0;
+    static hipError_t err = hipSuccess;
+    std::call_once(once, [kern] {
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), 64, 0);
+    });
+    if (err != hipSuccess) return err;
+    int cus = 1;
+    const hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    int64_t w = per_cu > 0 ? per_cu : 1;
+    const int64_t by_lds = lds > 0 ? static_cast<int64_t>(kLdsBytes / static_cast<int64_t>(lds)) : w;
+    w = by_lds < w ? (by_lds > 0 ? by_lds : 1) : w;
+    *out = w * cus;
+    return hipSuccess;
 }
 
 // D: lines of taps in flight; with prepared weights a line takes KP
@@ -531,12 +609,19 @@ hipError_t launch_kr(const void* x, const void* lam, const void* u, const void* 
     const size_t lds = QuadLayout(static_cast<int>(L)).bytes;
     auto kern = prop2d_quad_kernel<K, R, D, PRE>;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(lds));
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    kern<<<dim3(static_cast<unsigned>(planes)), dim3(64), lds, stream>>>(
+    // as many workgroups as the CUs keep resident at once (each walks its
+    // share of the planes), or one a plane when there are fewer planes
+    int64_t slots = 0;
+    const hipError_t e = resident_workgroups(kern, lds, &slots);
+    if (e != hipSuccess) return e;
+    // a multiple of 8 (whole rounds of the XCDs) below the plane count
+    const int64_t grid = planes <= slots ? planes : (slots & ~int64_t{7}) > 0 ? (slots & ~int64_t{7}) : slots;
+    kern<<<dim3(static_cast<unsigned>(grid)), dim3(64), lds, stream>>>(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(lam), static_cast<const uint16_t*>(u),
         static_cast<const uint16_t*>(w4), static_cast<int>(w4_bytes), eps,
         static_cast<uint16_t*>(y), static_cast<int>(planes), static_cast<int>(L), static_cast<int>(o.cpg));
