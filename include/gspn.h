@@ -327,15 +327,18 @@ int64_t gspn_noalloc_scratch_bytes(void);
  *             latent, its parameters, the scan output and the GEMM library's
  *             scratch; contents on return are unspecified.
  *   All pointers 16-byte aligned; y_tok and workspace must not overlap any
- *   input or each other.  The projections run in hipBLASLt (fp32
- *   accumulation; bf16 storage rounds every intermediate to bf16).  Per
- *   shape the GEMM algorithm is the library heuristic's first candidate that
- *   succeeds and fits the scratch: nothing is timed, the call never waits
- *   on the stream, and every process runs the same kernels, so results
- *   repeat bitwise.  The first call on a device creates that device's
- *   hipBLASLt handle, and the first call for a shape queries the heuristic;
- *   both are remembered for the process (so make those first calls outside
- *   stream capture).  Errors as gspn_prop2d_4dir_ex, plus
+ *   input or each other.  The projections accumulate in fp32; bf16 storage
+ *   rounds every intermediate to bf16.  In bf16 they run on this library's
+ *   matrix-core kernels where the shape fits them (P_down: Cc of 32 or 64
+ *   and C a multiple of 128 up to 1280; the parameter convolutions and
+ *   P_up: Cc a multiple of 8 up to 64, sides up to 96; H W a multiple of 4),
+ *   else in hipBLASLt.  Per shape the hipBLASLt algorithm is the library
+ *   heuristic's first candidate that succeeds and fits the scratch: nothing
+ *   is timed, the call never waits on the stream, and every process runs
+ *   the same kernels, so results repeat bitwise.  The first hipBLASLt call
+ *   on a device creates that device's handle, and the first call for a
+ *   shape queries the heuristic; both are remembered for the process (so
+ *   make those first calls outside stream capture).  Errors as gspn_prop2d_4dir_ex, plus
  *   GSPN_ERR_SHAPE for a workspace that is too small or C outside
  *   [1, 65536].
  */

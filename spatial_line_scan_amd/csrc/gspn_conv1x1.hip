@@ -1,5 +1,6 @@
 // 1x1 convolutions of the latent sublayer on the matrix cores (gfx950, bf16
-// storage, fp32 accumulation).
+// storage, fp32 accumulation).  P_down (tokens to latent, inner dimension C)
+// has a kernel of its own, described above pdown_kernel; the rest:
 //
 // "Scaling Parallel Sequence Models to Foundation-Scale Vision Encoders",
 // §5.1 (propagation in a compressed latent); reading notes, key design 1: the
@@ -37,6 +38,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 enum { kRowMajor = 0, kTokenMajor = 1 };
 
@@ -280,6 +282,127 @@ transpose_plane_kernel(const uint16_t* __restrict__ z, uint16_t* __restrict__ zt
     }
 }
 
+// P_down: z[b][ch][n] = sum_c p_down[ch][c] x[b][n][c] for the tokens of the
+// whole batch, t = b N + n (token-major input, C channels contiguous; planar
+// latent output).  Its time is the reading of the tokens (404 MB at the 1K
+// shape against 22 MB written and about 26 GFLOP), so the kernel is built
+// to read them as a plain copy would:
+//   - a workgroup of 8 wavefronts takes 32-token tiles blockIdx.x,
+//     blockIdx.x + gridDim.x, ...; a tile is one contiguous block of 64 C
+//     bytes, which the workgroup reads with consecutive 16-byte loads (a
+//     tile ahead, into registers) and writes into LDS, token rows padded to
+//     2 C + 16 bytes;
+//   - wavefront w multiplies channels C w / 8 .. C (w + 1) / 8 of the tile: in
+//     k-step s (KS = C / 128 of them, v_mfma_f32_32x32x16_bf16) lane (q, h)
+//     reads channels C w / 8 + 16 s + 8 h .. + 7 of token q from LDS, and its
+//     p_down operands, the same channels of latent channel 32 nt + q, stay in
+//     registers;
+//   - each wavefront's 32 x Cc partial sums go to LDS, and the workgroup adds
+//     the 8 partials of each output in wavefront order and writes four
+//     consecutive tokens of a channel a thread (8-byte stores; N % 4 == 0, so
+//     they never straddle two images).
+// Every output is one fp32 sum in a fixed order, rounded once to bf16, so
+// repeated calls are bitwise equal.
+constexpr int kDownWaves = 8;
+constexpr int kDownPitch = 36;          // floats a channel row of a partial (32 tokens + pad)
+
+template <int NT, int KS>
+__global__ void __launch_bounds__(64 * kDownWaves)
+pdown_kernel(const uint16_t* __restrict__ x, int x_bytes, const uint16_t* __restrict__ pd,
+             uint16_t* __restrict__ z, int N, int tokens, int tiles) {
+    extern __shared__ __attribute__((aligned(16))) u32x4_t lds4[];
+    constexpr int C = 128 * KS;
+    constexpr int CC = 32 * NT;
+    constexpr int ROW = C / 8 + 1;                 // 16-byte units a padded token row
+    constexpr int UNITS = 32 * C / 8;              // 16-byte units of a tile
+    constexpr int PER = (UNITS + 64 * kDownWaves - 1) / (64 * kDownWaves);   // a thread's loads
+    constexpr int PW = CC * kDownPitch;            // floats of one wavefront's partial
+    u32x4_t* tile_lds = lds4;                      // [32][ROW]
+    float* part = reinterpret_cast<float*>(lds4 + 32 * ROW);   // [8 waves][CC][kDownPitch]
+    const int tid = threadIdx.x;
+    const int l = tid & 63, w = tid >> 6;
+    const int q = l & 31, hk = l >> 5;
+    const int u0 = 2 * KS * w + hk;                // 16-byte unit of this lane's k-step 0 in a row
+
+    // p_down operands of this wavefront: latent channel 32 nt + q, k-step s
+    u32x4_t bw[NT][KS];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int s4 = 0; s4 < KS; ++s4)
+            bw[nt][s4] = *reinterpret_cast<const u32x4_t*>(pd + static_cast<int64_t>(32 * nt + q) * C + 8 * (u0 + 2 * s4));
+
+    const __amdgpu_buffer_rsrc_t xs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, x_bytes, lane::kBufFlags);
+    // unit f = tid + 512 k of tile t; tiles past the last read past the buffer
+    // (which ends below 2^31 bytes): zeros, never used
+    u32x4_t tv[PER];
+    auto issue = [&](int t) {
+        const uint32_t base = t < tiles ? static_cast<uint32_t>(t) * (64u * C) : 0x80000000u;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int f = tid + 64 * kDownWaves * k;
+            tv[k] = (UNITS % (64 * kDownWaves) == 0 || f < UNITS)
+                        ? __builtin_amdgcn_raw_buffer_load_b128(xs, base + 16u * static_cast<uint32_t>(f), 0, 0)
+                        : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    const int G = static_cast<int>(gridDim.x);
+    int t = static_cast<int>(blockIdx.x);
+    issue(t);
+    for (; t < tiles; t += G) {
+        // every thread has read the previous tile's operands and partials
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int f = tid + 64 * kDownWaves * k;
+            if (UNITS % (64 * kDownWaves) == 0 || f < UNITS) tile_lds[(f / (C / 8)) * ROW + f % (C / 8)] = tv[k];
+        }
+        issue(t + G);
+        __syncthreads();
+        f32x16_t acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16_t{};
+#pragma unroll
+        for (int s4 = 0; s4 < KS; ++s4) {
+            const u32x4_t a = tile_lds[q * ROW + u0 + 2 * s4];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                  __builtin_bit_cast(bf16x8_t, bw[nt][s4]),
+                                                                  acc[nt], 0, 0, 0);
+        }
+        // D row 8 g + 4 hk + r (token), column q (latent channel 32 nt + q)
+        float* mine = part + w * PW;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4_t*>(mine + (32 * nt + q) * kDownPitch + 8 * g + 4 * hk) =
+                    f32x4_t{acc[nt][4 * g], acc[nt][4 * g + 1], acc[nt][4 * g + 2], acc[nt][4 * g + 3]};
+        __syncthreads();
+        // outputs: channel ch = i / 8, tokens 4 (i % 8) .. + 3 of the tile
+        for (int i = tid; i < CC * 8; i += 64 * kDownWaves) {
+            const int ch = i >> 3, j = i & 7;
+            f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + ch * kDownPitch + 4 * j);
+#pragma unroll
+            for (int ww = 1; ww < kDownWaves; ++ww)
+                v += *reinterpret_cast<const f32x4_t*>(part + ww * PW + ch * kDownPitch + 4 * j);
+            const int tk = 32 * t + 4 * j;
+            if (tk < tokens) {
+                const int b = tk / N, n = tk - b * N;
+                *reinterpret_cast<u32x2_t*>(z + (static_cast<int64_t>(b) * CC + ch) * N + n) =
+                    u32x2_t{lane::pack_bf16x2(v[0], v[1]), lane::pack_bf16x2(v[2], v[3])};
+            }
+        }
+    }
+}
+
+// LDS of the P_down kernel: the padded tile and the wavefronts' partials.
+size_t pdown_lds_bytes(int64_t C, int64_t Cc) {
+    return static_cast<size_t>(32 * (C / 8 + 1)) * 16 + static_cast<size_t>(kDownWaves) * Cc * kDownPitch * 4;
+}
+
 template <int Mode>
 hipError_t launch(const void* in, int64_t B, int64_t K, int64_t N, const void* wm, int64_t M,
                   const Segs& segs, void* yt, hipStream_t stream) {
@@ -312,6 +435,25 @@ Segs make_segs(int n, const int64_t* start, void* const* base, const int64_t* bs
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// P_down instances: k-steps a lane KS = C / 128 up to 10 (C up to 1280), Cc
+// of 64 (two 32-channel tiles) or 32
+constexpr int kMaxDownKS = 10;
+
+template <int NT, int KS = 1, typename Go>
+hipError_t dispatch_down_ks(Go& go, int ks) {
+    if constexpr (KS > kMaxDownKS) {
+        return hipErrorInvalidValue;
+    } else {
+        if (ks == KS) return go(pdown_kernel<NT, KS>);
+        return dispatch_down_ks<NT, KS + 1>(go, ks);
+    }
+}
+
+template <typename Go>
+hipError_t dispatch_down(Go& go, bool two, int ks) {
+    return two ? dispatch_down_ks<2>(go, ks) : dispatch_down_ks<1>(go, ks);
+}
 
 }  // namespace
 
@@ -350,6 +492,40 @@ hipError_t launch_conv1x1_params(const void* z, void* zt, const void* w_param, i
     const int64_t bs[4] = {tg * N, tg * N, 0, 0};
     return launch<kRowMajor>(zt, B, Cc, N, wcol, 2 * tg, make_segs(2, start, base, bs), nullptr,
                              stream);
+}
+
+bool conv1x1_down_eligible(int dtype, int64_t B, int64_t Cc, int64_t H, int64_t W, int64_t C) {
+    const int64_t N = H * W;
+    return dtype == 1 && (Cc == 32 || Cc == 64) && C % 128 == 0 && C >= 128 && C <= 128 * kMaxDownKS &&
+           N % 4 == 0 && B * N * C * 2 + 64 <= 0x7fffffff &&
+           static_cast<int64_t>(pdown_lds_bytes(C, Cc)) <= kLdsBytes;
+}
+
+hipError_t launch_conv1x1_down(const void* x_tok, const void* p_down, int64_t B, int64_t C,
+                               int64_t Cc, int64_t H, int64_t W, void* z, hipStream_t stream) {
+    if (!aligned16(p_down) || !aligned16(x_tok) || !aligned16(z)) return hipErrorInvalidValue;
+    const int64_t N = H * W;
+    const int64_t tokens = B * N;
+    const int64_t tiles = (tokens + 31) / 32;
+    const size_t lds = pdown_lds_bytes(C, Cc);
+    int cus = 1;
+    hipError_t e = device_cu_count(&cus);
+    if (e != hipSuccess) return e;
+    const int64_t grid = tiles < cus ? tiles : cus;
+    auto go = [&](auto kern) -> hipError_t {
+        if (lds > 64 * 1024) {
+            const hipError_t fe = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                      static_cast<int>(lds));
+            if (fe != hipSuccess) return fe;
+        }
+        kern<<<dim3(static_cast<unsigned>(grid)), dim3(64 * kDownWaves), lds, stream>>>(
+            static_cast<const uint16_t*>(x_tok), static_cast<int>(tokens * C * 2),
+            static_cast<const uint16_t*>(p_down), static_cast<uint16_t*>(z), static_cast<int>(N),
+            static_cast<int>(tokens), static_cast<int>(tiles));
+        return hipGetLastError();
+    };
+    return dispatch_down(go, Cc == 64, static_cast<int>(C / 128));
 }
 
 hipError_t launch_conv1x1_up(const void* yc, const void* p_up, int64_t B, int64_t Cc, int64_t C,

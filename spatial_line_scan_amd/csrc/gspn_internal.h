@@ -170,6 +170,13 @@ bool conv1x1_eligible(int dtype, int64_t B, int64_t K, int64_t H, int64_t W, int
 hipError_t launch_conv1x1_params(const void* z, void* zt, const void* w_param, int64_t B,
                                  int64_t Cc, int64_t G, int64_t H, int64_t W, void* lam, void* u,
                                  void* const* taps4, hipStream_t stream);
+// z [B][Cc][H W] = P_down applied to the tokens x_tok [B][H W][C] (bf16, Cc
+// of 32 or 64, C a multiple of 128 up to 1280, H W a multiple of 4).
+bool conv1x1_down_eligible(int dtype, int64_t B, int64_t Cc, int64_t H, int64_t W, int64_t C);
+hipError_t launch_conv1x1_down(const void* x_tok, const void* p_down, int64_t B, int64_t C,
+                               int64_t Cc, int64_t H, int64_t W, void* z, hipStream_t stream);
+// CUs of the current device (queried once per device).
+hipError_t device_cu_count(int* out);
 // y_tok [B][H W][C] = P_up applied to the planar latent yc [B][Cc][H W].
 hipError_t launch_conv1x1_up(const void* yc, const void* p_up, int64_t B, int64_t Cc, int64_t C,
                              int64_t H, int64_t W, void* y_tok, hipStream_t stream);

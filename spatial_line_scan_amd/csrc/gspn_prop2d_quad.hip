@@ -557,25 +557,6 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     }  // planes of this workgroup
 }
 
-// CUs of the current device, queried once per device.
-constexpr int kMaxDevices = 64;
-int g_cus[kMaxDevices];
-hipError_t g_cus_err[kMaxDevices];
-std::once_flag g_cus_once[kMaxDevices];
-
-hipError_t device_cus(int* out) {
-    int dev = 0;
-    const hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::call_once(g_cus_once[dev], [dev] {
-        g_cus_err[dev] = hipDeviceGetAttribute(&g_cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
-    });
-    if (g_cus_err[dev] != hipSuccess) return g_cus_err[dev];
-    *out = g_cus[dev] > 0 ? g_cus[dev] : 1;
-    return hipSuccess;
-}
-
 // Workgroups of 64 threads with `lds` bytes of LDS each that the device
 // keeps resident at once: its CUs times the smaller of the kernel's own
 // limit per CU (registers; queried once per kernel) and the LDS limit.
@@ -589,7 +570,7 @@ hipError_t resident_workgroups(F* kern, size_t lds, int64_t* out) {
     });
     if (err != hipSuccess) return err;
     int cus = 1;
-    const hipError_t e = device_cus(&cus);
+    const hipError_t e = device_cu_count(&cus);
     if (e != hipSuccess) return e;
     int64_t w = per_cu > 0 ? per_cu : 1;
     const int64_t by_lds = lds > 0 ? static_cast<int64_t>(kLdsBytes / static_cast<int64_t>(lds)) : w;

@@ -19,9 +19,10 @@
 //        kernels read them, because their GEMM reads the transposed latent)
 //     --four-direction scan-->    yc [B][Cc][H][W]
 //     --GEMM (P_up)-->            tokens y [B][N][C]
-// The 1x1 convolutions are plain GEMMs and run in hipBLASLt; the scan and
-// the transposes are this library's kernels.  Every intermediate lives in
-// the caller's workspace.
+// The 1x1 convolutions are plain GEMMs: in bf16 they run on this library's
+// matrix-core kernels where the shape fits them (gspn_conv1x1.hip), else in
+// hipBLASLt; the scan and the transposes are this library's kernels.  Every
+// intermediate lives in the caller's workspace.
 #include <hipblaslt/hipblaslt.h>
 
 #include <map>
@@ -248,9 +249,13 @@ hipError_t launch_latent_sublayer(const void* x_tok, const void* p_down, const v
     hipError_t e;
 
     // z[b] (Cc x N, row-major) = P_down x[b]^T, i.e. z[b]^T = x[b] P_down^T with
-    // x[b] the N x C token matrix
-    e = gemm(dtype, {HIPBLAS_OP_T, HIPBLAS_OP_N, N, Cc, C, C, C, N, N * C, 0, Cc * N, bt}, x_tok,
-             p_down, z, bws, stream);
+    // x[b] the N x C token matrix: on the matrix cores where the shape fits
+    // the token-streaming kernel, else in hipBLASLt
+    if (conv1x1_down_eligible(dtype, B, Cc, H, W, C))
+        e = launch_conv1x1_down(x_tok, p_down, B, C, Cc, H, W, z, stream);
+    else
+        e = gemm(dtype, {HIPBLAS_OP_T, HIPBLAS_OP_N, N, Cc, C, C, C, N, N * C, 0, Cc * N, bt}, x_tok,
+                 p_down, z, bws, stream);
     if (e != hipSuccess) return e;
     PropOpts opts;
     opts.cpg = Cc / G;

@@ -59,6 +59,19 @@ def test_sublayer_small(B, C, Cc, G, H, W, k, dtype):
     _run(B, C, Cc, G, H, W, k, dtype, 5 + B + C + G + k)
 
 
+# The matrix-core P_down (bf16, Cc of 32 or 64, C a multiple of 128 up to
+# 1280): one to ten k-steps a lane (C / 128), 32-token tiles that span
+# two or more images (H W not a multiple of 32, and below 32), a ragged last
+# tile, and a batch of fewer tiles than CUs
+@pytest.mark.parametrize("B,C,Cc,G,H,W", [
+    (3, 128, 32, 32, 10, 10), (2, 256, 64, 4, 9, 12), (5, 384, 64, 64, 6, 6),
+    (2, 640, 32, 1, 12, 12), (3, 1280, 64, 2, 4, 4), (1, 896, 32, 8, 14, 10),
+    (2, 1536, 64, 64, 6, 6)])   # C past the matrix-core form: hipBLASLt
+def test_sublayer_matrix_core_p_down(B, C, Cc, G, H, W):
+    say("sublayer p_down", B, C, Cc, G, H, W)
+    _run(B, C, Cc, G, H, W, 1, "bf16", 40 + B + C + G)
+
+
 @pytest.mark.parametrize("G", [64, 1])
 def test_sublayer_latent1k_sampled_batches(G):
     """The pages' 1K sublayer shape: B=32 images of 74 x 74 tokens, C=1152
