@@ -74,18 +74,23 @@ using namespace lane;
 // (the pad), one row after it (side), and for b the neighbouring arrays or
 // b_lo's spare row.
 // b_hi and b_lo have 8 spare entries for the second half of the plane's last
-// 16-byte chunk when L L is not a multiple of 8.
+// 16-byte chunk when L L is not a multiple of 8.  A workgroup of several
+// planes gives each its own copy, `bytes` apart; the offsets below include
+// the copy's base.
 struct QuadLayout {
-    int s, side, bh, bl, bytes;
-    static constexpr int sdum = 0, bdum = 16;
+    int base, sdum, bdum, s, side, bh, bl, bytes;
     __host__ __device__ static int a16(int v) { return (v + 15) & ~15; }
-    __host__ __device__ explicit QuadLayout(int L) {
+    __host__ __device__ explicit QuadLayout(int L, int copy = 0) {
         const int n = L * L;
-        s = a16(32 + 4 * L);
+        bytes = a16(a16(a16(a16(32 + 4 * L) + 4 * n) + 16 * L) + 2 * (n + 8)) + n + L + 8;
+        bytes = a16(bytes);
+        base = copy * bytes;
+        sdum = base;
+        bdum = base + 16;
+        s = base + a16(32 + 4 * L);
         side = a16(s + 4 * n);
         bh = a16(side + 16 * L);
         bl = a16(bh + 2 * (n + 8));
-        bytes = a16(bl + n + L + 8);
     }
 };
 
@@ -178,8 +183,9 @@ quad_prepare_kernel(const uint16_t* __restrict__ w4, float* __restrict__ wp, flo
 
 // PRE: w4 holds the weights quad_prepare_kernel wrote (fp32, normalised, in
 // scan order, KP a lane a line) instead of raw bf16 taps.
-template <int K, int R, int D, bool PRE>
-__global__ void __launch_bounds__(64)
+// WPB: planes (wavefronts) a workgroup, 1 or (with prepared weights) 4.
+template <int K, int R, int D, bool PRE, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
 prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
                    const uint16_t* __restrict__ u, const uint16_t* __restrict__ w4, int w4_bytes,
                    float eps, uint16_t* __restrict__ y, int planes, int L, int cpg) {
@@ -187,31 +193,36 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     constexpr int NW = window_words<uint16_t, K>();
     constexpr int KP = prepared_floats(K);
     constexpr int NV = KP / 4;
+    static_assert(WPB == 1 || (WPB == 4 && PRE), "four planes a workgroup share prepared weights");
     const int n = L * L;
-    const QuadLayout lay(L);
-    const int lane = threadIdx.x;
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int wave = static_cast<int>(threadIdx.x) >> 6;
+    const QuadLayout lay(L, wave);
     const int g = lane >> 4;             // 0 TD, 1 BU, 2 LR, 3 RL
     const int q = lane & 15;
     const bool rows = g < 2;
     const bool fwd = (g & 1) == 0;
-    // With shared taps, consecutive workgroups go to the 8 XCDs in turn;
-    // the plane of workgroup i is chosen so that XCD x walks tap planes x,
-    // x + 8, ... and every channel of a tap group reads its weights through
-    // one L2.  Any plane order gives the same results.
-    // A workgroup scans planes v = blockIdx.x, blockIdx.x + gridDim.x, ...
-    // (the grid holds at most as many workgroups as the CUs keep resident):
-    // the next plane's x, lambda and first tap lines are loaded while the
-    // current plane's sums are finished and written out.  gridDim.x is a
-    // multiple of 8 or the whole plane count, so v and blockIdx.x share an
-    // XCD.
+    // A workgroup takes plane slots v = blockIdx.x, blockIdx.x + gridDim.x,
+    // ... (the grid holds at most as many workgroups as the CUs keep
+    // resident): the next slot's x, lambda and first tap lines are loaded
+    // while the current plane's sums are finished and written out.  gridDim.x
+    // is a multiple of 8 or the whole slot count, so v and blockIdx.x share an
+    // XCD.  A slot is WPB consecutive planes, one a wavefront.
+    // With shared taps, consecutive workgroups go to the 8 XCDs in turn, and
+    // slot v is chosen so that XCD x walks tap groups x, x + 8, ...: every
+    // channel of a group reads its weights through one L2, and the
+    // wavefronts of a workgroup (channels of one group, at about the same
+    // step) through one L1.  Any plane order gives the same results.
+    const int slots = (planes + WPB - 1) / WPB;
     auto plane_of = [&](int v) -> int {
         if constexpr (PRE) {
-            if (planes % (8 * cpg) == 0) {
+            const int spg = cpg / WPB;     // slots a tap group
+            if (cpg % WPB == 0 && planes % (8 * cpg) == 0) {
                 const int x8 = v & 7, sl = v >> 3;
-                return ((sl / cpg) * 8 + x8) * cpg + sl % cpg;
+                return (((sl / spg) * 8 + x8) * spg + sl % spg) * WPB + wave;
             }
         }
-        return v;
+        return v * WPB + wave;
     };
     const int nchunk = (2 * n + 15) / 16;  // 16-byte chunks of a plane's bf16 values
 
@@ -298,8 +309,9 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     };
     issue_plane(plane_of(static_cast<int>(blockIdx.x)));
 
-    for (int v = static_cast<int>(blockIdx.x); v < planes; v += static_cast<int>(gridDim.x)) {
+    for (int v = static_cast<int>(blockIdx.x); v < slots; v += static_cast<int>(gridDim.x)) {
         const int plane = plane_of(v);
+        if (plane >= planes) continue;     // the last slot's spare wavefronts (no barrier anywhere)
         const uint32_t plane_b = static_cast<uint32_t>(plane) * static_cast<uint32_t>(n) * 2u;
         // ------------------------------------------------ u, for the end
         // (it arrives while the plane is scanned; kU 16-byte chunks a lane)
@@ -313,7 +325,8 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
         // ------------------------------------------------ zero S, side, dummies
         // (after the previous plane's last reads of S)
         lds_order();
-        for (int f = lane; f < lay.bh / 16; f += 64) lds_ref<u32x4_t>(16u * f) = u32x4_t{0u, 0u, 0u, 0u};
+        for (int f = lane; f < (lay.bh - lay.base) / 16; f += 64)
+            lds_ref<u32x4_t>(static_cast<uint32_t>(lay.base) + 16u * f) = u32x4_t{0u, 0u, 0u, 0u};
 
         // ------------------------------------------------ b = lambda x into LDS
 #pragma unroll
@@ -355,9 +368,9 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
             const int p = K * q + j;
             const bool valid = p < L;
             const int e = rows ? i0 * L + p : p * L + i0;
-            aS[j] = valid ? static_cast<uint32_t>(lay.s + 4 * e) : QuadLayout::sdum;
-            aH[j] = valid ? static_cast<uint32_t>(lay.bh + 2 * e) : QuadLayout::bdum;
-            aL[j] = valid ? static_cast<uint32_t>(lay.bl + e) : QuadLayout::bdum;
+            aS[j] = valid ? static_cast<uint32_t>(lay.s + 4 * e) : static_cast<uint32_t>(lay.sdum);
+            aH[j] = valid ? static_cast<uint32_t>(lay.bh + 2 * e) : static_cast<uint32_t>(lay.bdum);
+            aL[j] = valid ? static_cast<uint32_t>(lay.bl + e) : static_cast<uint32_t>(lay.bdum);
             dSj[j] = valid ? 4 * de : 0;
             dHj[j] = valid ? 2 * de : 0;
             dLj[j] = valid ? de : 0;
@@ -512,7 +525,7 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
                 if (s0 + d < L) step(s0 + d, d, qb1, qb2);
         }
         // the next plane's inputs and first tap lines, while this one finishes
-        if (v + static_cast<int>(gridDim.x) < planes) issue_plane(plane_of(v + static_cast<int>(gridDim.x)));
+        if (v + static_cast<int>(gridDim.x) < slots) issue_plane(plane_of(v + static_cast<int>(gridDim.x)));
         lds_order();
 
         // ------------------------------------------------ meeting pixels
@@ -557,16 +570,16 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     }  // planes of this workgroup
 }
 
-// Workgroups of 64 threads with `lds` bytes of LDS each that the device
-// keeps resident at once: its CUs times the smaller of the kernel's own
-// limit per CU (registers; queried once per kernel) and the LDS limit.
+// Workgroups of `threads` threads with `lds` bytes of LDS each that the
+// device keeps resident at once: its CUs times the smaller of the kernel's
+// own limit per CU (registers; queried once per kernel) and the LDS limit.
 template <typename F>
-hipError_t resident_workgroups(F* kern, size_t lds, int64_t* out) {
+hipError_t resident_workgroups(F* kern, int threads, size_t lds, int64_t* out) {
     static std::once_flag once;
     static int per_cu = 0;
     static hipError_t err = hipSuccess;
-    std::call_once(once, [kern] {
-        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), 64, 0);
+    std::call_once(once, [kern, threads] {
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), threads, 0);
     });
     if (err != hipSuccess) return err;
     int cus = 1;
@@ -583,12 +596,12 @@ hipError_t resident_workgroups(F* kern, size_t lds, int64_t* out) {
 // registers instead of 3 window words, so fewer are kept.
 template <int K, bool PRE> constexpr int depth() { return PRE ? K * ((5 + K - 1) / K) : K * ((8 + K - 1) / K); }
 
-template <int K, int R, bool PRE>
-hipError_t launch_kr(const void* x, const void* lam, const void* u, const void* w4, int64_t w4_bytes,
-                     float eps, void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
+template <int K, int R, bool PRE, int WPB>
+hipError_t launch_krw(const void* x, const void* lam, const void* u, const void* w4, int64_t w4_bytes,
+                      float eps, void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
     constexpr int D = depth<K, PRE>();
-    const size_t lds = QuadLayout(static_cast<int>(L)).bytes;
-    auto kern = prop2d_quad_kernel<K, R, D, PRE>;
+    const size_t lds = static_cast<size_t>(WPB) * QuadLayout(static_cast<int>(L)).bytes;
+    auto kern = prop2d_quad_kernel<K, R, D, PRE, WPB>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -596,17 +609,31 @@ hipError_t launch_kr(const void* x, const void* lam, const void* u, const void* 
         if (e != hipSuccess) return e;
     }
     // as many workgroups as the CUs keep resident at once (each walks its
-    // share of the planes), or one a plane when there are fewer planes
-    int64_t slots = 0;
-    const hipError_t e = resident_workgroups(kern, lds, &slots);
+    // share of the plane slots), or one a slot when there are fewer slots
+    int64_t resident = 0;
+    const hipError_t e = resident_workgroups(kern, 64 * WPB, lds, &resident);
     if (e != hipSuccess) return e;
-    // a multiple of 8 (whole rounds of the XCDs) below the plane count
-    const int64_t grid = planes <= slots ? planes : (slots & ~int64_t{7}) > 0 ? (slots & ~int64_t{7}) : slots;
-    kern<<<dim3(static_cast<unsigned>(grid)), dim3(64), lds, stream>>>(
+    const int64_t slots = (planes + WPB - 1) / WPB;
+    // a multiple of 8 (whole rounds of the XCDs) below the slot count
+    const int64_t grid = slots <= resident ? slots : (resident & ~int64_t{7}) > 0 ? (resident & ~int64_t{7}) : resident;
+    kern<<<dim3(static_cast<unsigned>(grid)), dim3(64 * WPB), lds, stream>>>(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(lam), static_cast<const uint16_t*>(u),
         static_cast<const uint16_t*>(w4), static_cast<int>(w4_bytes), eps,
         static_cast<uint16_t*>(y), static_cast<int>(planes), static_cast<int>(L), static_cast<int>(o.cpg));
     return hipGetLastError();
+}
+
+// With prepared weights, four channels of one tap group a workgroup when
+// their four layouts fit in LDS (the weights they read at the same steps
+// then come through one L1).
+template <int K, int R, bool PRE>
+hipError_t launch_kr(const void* x, const void* lam, const void* u, const void* w4, int64_t w4_bytes,
+                     float eps, void* y, int64_t planes, int64_t L, const PropOpts& o, hipStream_t stream) {
+    if constexpr (PRE) {
+        if (o.cpg % 4 == 0 && 4 * static_cast<int64_t>(QuadLayout(static_cast<int>(L)).bytes) <= kLdsBytes)
+            return launch_krw<K, R, PRE, 4>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
+    }
+    return launch_krw<K, R, PRE, 1>(x, lam, u, w4, w4_bytes, eps, y, planes, L, o, stream);
 }
 
 template <int K, bool PRE>
