@@ -53,6 +53,7 @@ using namespace lane;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <typename V> using lds_t = __attribute__((address_space(3))) V;
 
 template <typename V>
@@ -333,7 +334,6 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
     // four consecutive values from array offset (in values) e4 * 4
     auto get4 = [&](int base, int lbase, int e4) -> f32x4_t {
         if constexpr (kNarrow) {
-            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
             const u32x2_t hi = lds_at<u32x2_t>(base + 8u * e4);
             const uint32_t lo = lds_at<uint32_t>(lbase + 4u * e4);
             return f32x4_t{__uint_as_float(__builtin_amdgcn_perm(hi.x, lo, 0x0504000cu)),
@@ -780,6 +780,21 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
             }
         }
         const uint32_t my_stage = lay.stage + 3 * half * SL * GS;
+        // K <= 2 on even lines, one plane a workgroup: a lane's K positions of
+        // a tap's line are one aligned K GS-byte word of the tap-gradient
+        // plane, so the line goes out with one store a lane and tap (taps 1
+        // and 2 at scalar offsets of one and two planes) instead of through
+        // the staging lines.  Lanes past the line's end store past the buffer
+        // (dropped).
+        constexpr bool kDirect = !summed && !Odd && K <= 2;
+        const uint32_t d_off0 = K * q < L ? static_cast<uint32_t>((((dir0 + half) * out_planes + out_plane) * 3) * HW * GS +
+                                                                  i0 * L * GS + K * q * GS)
+                                          : 0x80000000u;
+        const uint32_t d_step = K * q < L ? (fwd ? 0u - static_cast<uint32_t>(L * GS) : static_cast<uint32_t>(L * GS)) : 0u;
+        uint32_t d_off = d_off0;
+        // bytes between a triple's tap planes (read through readfirstlane so
+        // that the compiler keeps the scalar offsets in scalar registers)
+        const int d_tap = __builtin_amdgcn_readfirstlane(HW * GS);
         const uint32_t set_bytes = 6u * SL * GS;    // one staging set of a plane
         // adjoint step of the next restart line: its taps read nothing (tap
         // gradient 0) and the line before it receives no adjoint term from it
@@ -923,6 +938,23 @@ prop2d_backward_pair_kernel(const T* __restrict__ xl, const T* __restrict__ laml
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), gws, go[t], 0, 0);
                     go[t] += gd[t];
                 }
+            } else if constexpr (kDirect) {
+                const float* gzs[3] = {gz0, gz1, gz2};
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    const float* v = gzs[k];
+                    if constexpr (GS == 4 && K == 2)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            u32x2_t{__float_as_uint(v[0]), __float_as_uint(v[1])}, gws, d_off, k * d_tap, 0);
+                    else if constexpr (GS == 4)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), gws, d_off, k * d_tap, 0);
+                    else if constexpr (K == 2)
+                        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[0], v[1]), gws, d_off, k * d_tap, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pack_bf16x2(v[0], v[0])), gws,
+                                                              d_off, k * d_tap, 0);
+                }
+                d_off += d_step;
             } else {
                 stage_put<GT, K>(my_stage, q, gz0);
                 stage_put<GT, K>(my_stage + SL * GS, q, gz1);
