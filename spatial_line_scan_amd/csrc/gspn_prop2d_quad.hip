@@ -195,8 +195,8 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     constexpr int NV = KP / 4;
     static_assert(WPB == 1 || (WPB == 4 && PRE), "four planes a workgroup share prepared weights");
     const int n = L * L;
-    const int lane = static_cast<int>(threadIdx.x) & 63;
-    const int wave = static_cast<int>(threadIdx.x) >> 6;
+    const int lane = WPB == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) & 63;
+    const int wave = WPB == 1 ? 0 : static_cast<int>(threadIdx.x) >> 6;
     const QuadLayout lay(L, wave);
     const int g = lane >> 4;             // 0 TD, 1 BU, 2 LR, 3 RL
     const int q = lane & 15;
@@ -311,7 +311,9 @@ prop2d_quad_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
 
     for (int v = static_cast<int>(blockIdx.x); v < slots; v += static_cast<int>(gridDim.x)) {
         const int plane = plane_of(v);
-        if (plane >= planes) continue;     // the last slot's spare wavefronts (no barrier anywhere)
+        if constexpr (WPB > 1) {
+            if (plane >= planes) continue;   // the last slot's spare wavefronts (no barrier anywhere)
+        }
         const uint32_t plane_b = static_cast<uint32_t>(plane) * static_cast<uint32_t>(n) * 2u;
         // ------------------------------------------------ u, for the end
         // (it arrives while the plane is scanned; kU 16-byte chunks a lane)
