@@ -10,8 +10,9 @@ steps do not hit the 256 MB Infinity Cache.  Prints one JSON line.
 value     : algorithmic GB/s = 16 values per pixel-channel (read x, lambda, u
             and 4 x 3 taps, write y) x bytes per value / wall time per step
 roofline  : the same bytes / average kernel duration (HIP events on the
-            launch stream around the K back-to-back launches, divided by K;
-            the minimum from events around single launches), against the
+            launch stream at the two ends of the timed region, the same K
+            back-to-back launches the wall clock times, divided by K; the
+            minimum from events around single launches), against the
             MI355X HBM peak of 8 TB/s; `traffic`
             is the measured HBM bytes per launch from the committed rocprofv3
             counter summary when it was taken on the current kernel source
@@ -161,20 +162,29 @@ def cpu_baseline(wl, budget_s: float, gpu_inputs: dict, gpu_out):
     }
 
 
-def _events(fn, steps, stream):
-    """Kernel time per call from HIP events on the launch stream: the average
-    is one event pair around `steps` back-to-back calls (each call is that
-    path's launches only), divided by `steps`; the minimum is over event pairs
-    around single calls, which also hold each pair's own overhead."""
-    import numpy as np
+def _region(fn, steps, stream):
+    """One timed region of `steps` back-to-back calls: its wall time, and its
+    kernel time per call from a pair of HIP events recorded on the launch
+    stream at the region's two ends (inside the wall clock), divided by
+    `steps`."""
     import torch
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     a.record(stream)
     for i in range(steps):
         fn(i)
     b.record(stream)
     torch.cuda.synchronize()
-    avg = a.elapsed_time(b) / steps
+    wall = time.perf_counter() - t0
+    return wall, float(a.elapsed_time(b)) / steps
+
+
+def _single_min(fn, steps, stream):
+    """The fastest single call, from event pairs around each of `steps`
+    calls (each pair's own overhead included)."""
+    import numpy as np
+    import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     for i in range(steps):
@@ -182,22 +192,18 @@ def _events(fn, steps, stream):
         fn(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    return float(avg), float(np.min([x.elapsed_time(y) for x, y in ev]))
+    return float(np.min([x.elapsed_time(y) for x, y in ev]))
 
 
 def _timed(fn, steps, warmup, stream):
-    """Wall time of `steps` calls and their HIP-event kernel times (_events)."""
+    """Wall time of `steps` calls, their kernel time per call from HIP events
+    around the same calls, and the fastest single call."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        fn(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kavg, kmin = _events(fn, steps, stream)
-    return wall, kavg, kmin
+    wall, kavg = _region(fn, steps, stream)
+    return wall, kavg, _single_min(fn, steps, stream)
 
 
 def variant_leg(wl, args, dev, G, k):
@@ -307,7 +313,7 @@ def sublayer_leg(args, dev, G, B=32, C=1152, Cc=64, H=74, W=74):
 
 def backward_leg(wl, sets, args, dev):
     """Warmup + K backward launches over the rotated sets: wall time and
-    HIP-event kernel times on the launch stream (_events)."""
+    HIP-event kernel times on the launch stream (_region, _single_min)."""
     import numpy as np
     import torch
 
@@ -338,12 +344,8 @@ def backward_leg(wl, sets, args, dev):
     for i in range(args.warmup):
         bstep(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        bstep(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kavg, kmin = _events(bstep, args.steps, stream)
+    wall, kavg = _region(bstep, args.steps, stream)
+    kmin = _single_min(bstep, args.steps, stream)
     nbytes = BWD_VALUES_PER_PIXEL * wl.elem_bytes * wl.pixels
     achieved = nbytes / (kavg * 1e-3) / 1e9
     del grads, ws
@@ -604,18 +606,12 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # wall time of exactly K steps
+    # exactly K steps: their wall time, and their kernel time per launch from
+    # HIP events on the launch stream at the two ends of the same region (a
+    # step is one launch of the four-direction kernel)
     stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # kernel time per launch, HIP events on the launch stream (a step is one
-    # launch of the four-direction kernel)
-    kern_avg, kern_min = _events(step, args.steps, stream)
+    wall, kern_avg = _region(step, args.steps, stream)
+    kern_min = _single_min(step, args.steps, stream)
 
     # calibration: a plain device copy of ~1 GB through the same HBM
     cal = torch.empty(1 << 28, dtype=torch.float32, device=dev)
