@@ -191,6 +191,25 @@ def test_prop2d_quad_planes_beyond_one_round(L, B, C):
         assert_close(_np(sl(y)), r, RTOL["bf16"], "%dx%d plane (%d,%d)" % (L, L, b, c))
 
 
+@pytest.mark.parametrize("L,B,C", [(74, 3, 370), (80, 2, 410), (34, 5, 1000), (74, 2, 1100)])
+def test_prop2d_quad_persistent_grid_matches_single_rounds(L, B, C):
+    # A launch of more planes than the CUs keep resident walks the planes
+    # with a resident-sized grid (a workgroup takes planes blockIdx.x,
+    # blockIdx.x + gridDim.x, ..., the next one's inputs loading while it
+    # finishes the current one).  Every plane of it must equal the same plane
+    # from a launch of one image (C planes, one round: the same kernel, or
+    # the wavefront-a-direction kernel, which sums in the same order).
+    say("prop2d persistent vs single rounds", L, B, C)
+    p = _problem(B, C, L, L, 11 + L + C, "bf16")
+    y = gspn.prop2d_4dir(p["x"], p["lam"], p["u"], p["w"])
+    parts = []
+    for b in range(B):
+        sl = lambda t: t[b:b + 1].contiguous()
+        parts.append(gspn.prop2d_4dir(sl(p["x"]), sl(p["lam"]), sl(p["u"]), p["w"][:, b:b + 1].contiguous()))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), torch.cat(parts).view(torch.int16))
+
+
 @pytest.mark.parametrize("H,W", WIDE_SHAPES)
 def test_prop2d_wide_fp32_shapes(H, W):
     say("prop2d wide", H, W)
