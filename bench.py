@@ -12,7 +12,8 @@ value     : algorithmic GB/s = 16 values per pixel-channel (read x, lambda, u
 roofline  : the same bytes / average kernel duration (HIP events on the
             launch stream at the two ends of the timed region, the same K
             back-to-back launches the wall clock times, divided by K; the
-            minimum from events around single launches), against the
+            minimum and median of 100 single launches from events around
+            each), against the
             MI355X HBM peak of 8 TB/s; `traffic`
             is the measured HBM bytes per launch from the committed rocprofv3
             counter summary when it was taken on the current kernel source
@@ -180,19 +181,26 @@ def _region(fn, steps, stream):
     return wall, float(a.elapsed_time(b)) / steps
 
 
-def _single_min(fn, steps, stream):
-    """The fastest single call, from event pairs around each of `steps`
-    calls (each pair's own overhead included)."""
+def _single_calls(fn, n, stream):
+    """Event pairs around each of n single calls (each pair's own overhead
+    included): the fastest and the median call, in ms."""
     import numpy as np
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for i in range(steps):
+          for _ in range(n)]
+    for i in range(n):
         ev[i][0].record(stream)
         fn(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    return float(np.min([x.elapsed_time(y) for x, y in ev]))
+    t = [x.elapsed_time(y) for x, y in ev]
+    return float(np.min(t)), float(np.median(t))
+
+
+def _single_min(fn, steps, stream):
+    """The fastest single call, from event pairs around each of `steps`
+    calls (each pair's own overhead included)."""
+    return _single_calls(fn, steps, stream)[0]
 
 
 def _timed(fn, steps, warmup, stream):
@@ -611,7 +619,9 @@ def main():
     # step is one launch of the four-direction kernel)
     stream = torch.cuda.current_stream(dev)
     wall, kern_avg = _region(step, args.steps, stream)
-    kern_min = _single_min(step, args.steps, stream)
+    # single launches, an event pair around each: the fastest and the median
+    # of 100 (or K if more)
+    kern_min, kern_median = _single_calls(step, max(100, args.steps), stream)
 
     # calibration: a plain device copy of ~1 GB through the same HBM
     cal = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -656,7 +666,8 @@ def main():
                                         "scaled by a 1 GiB copy's reading; not counted in this run"
                                         if traffic is not None else None),
                      "kernel_ms_avg": round(kern_avg, 5),
-                     "kernel_ms_min": round(kern_min, 5)},
+                     "kernel_ms_min": round(kern_min, 5),
+                     "kernel_ms_median_single": round(kern_median, 5)},
         "calibration": {"torch_copy_GBps": round(copy_gbps, 1),
                         "frac_of_copy": round(achieved / copy_gbps, 4)},
     }
